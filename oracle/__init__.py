@@ -1,0 +1,179 @@
+"""fp64 CPU oracle for the Gated DeltaNet token mixer (ctypes over liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path. It shares no code with
+the HIP library; both sides are fed the same raw draws from the input generator.
+
+Every function follows the reading notes of "On the Design of Qwen3.8-Next
+Architecture", section 2.1.1: eqs. (1)-(5) for the recurrence, eqs. (6)-(10) for
+the pre-processing and gates, eq. (11) (without W_o) for the output gate; the
+C source states the passage per function.
+
+Parity status: the recurrence, conv, SiLU, L2Norm, gates and output gate are all
+pinned by the CPU tests (closed forms, invariants, exact-rational brute force,
+library routines). The conventions the pages leave open (conv tap order, the
+epsilons, RMSNorm scope) are pinned only by the stated readings.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+L2_EPS = 1e-6
+RMS_EPS = 1e-6
+CONV_K = 4
+
+_lib = None
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.gdn_oracle_short_conv.argtypes = [_dp, _dp, ctypes.c_int, _ip, ctypes.c_int,
+                                              ctypes.c_int, _dp]
+        lib.gdn_oracle_silu.argtypes = [_dp, ctypes.c_long, _dp]
+        lib.gdn_oracle_l2norm.argtypes = [_dp, ctypes.c_long, ctypes.c_int, ctypes.c_double, _dp]
+        lib.gdn_oracle_gates.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_int,
+                                         _dp, _dp, _dp]
+        lib.gdn_oracle_recurrence.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _dp, _dp, ctypes.c_int]
+        lib.gdn_oracle_recurrence.restype = ctypes.c_int
+        lib.gdn_oracle_output_gate.argtypes = [_dp, _dp, _dp, ctypes.c_long, ctypes.c_int,
+                                               ctypes.c_double, _dp]
+        _lib = lib
+    return _lib
+
+
+def _d(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# ------------------------------------------------------------------ eqs. 6-8
+def short_conv(x, w, cu_seqlens):
+    """x: [ntok, C]; w: [C, K] (tap K-1 = current token); zero history per sequence."""
+    x = _d(x)
+    w = _d(w)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ntok, C = x.shape
+    u = np.empty_like(x)
+    _load().gdn_oracle_short_conv(_p(x), _p(w), w.shape[1], cu.ctypes.data_as(_ip),
+                                  len(cu) - 1, C, _p(u))
+    return u
+
+
+def silu(u):
+    u = _d(u)
+    a = np.empty_like(u)
+    _load().gdn_oracle_silu(_p(u), u.size, _p(a))
+    return a
+
+
+def l2norm(a, eps=L2_EPS):
+    a = _d(a)
+    d = a.shape[-1]
+    out = np.empty_like(a)
+    _load().gdn_oracle_l2norm(_p(a), a.size // d, d, eps, _p(out))
+    return out
+
+
+# ------------------------------------------------------------------ eqs. 9-10
+def gates(a_raw, b_raw, A_log, dt_bias):
+    """Returns (g = log alpha, alpha, beta), each shaped like a_raw ([..., H])."""
+    a_raw = _d(a_raw)
+    b_raw = _d(b_raw)
+    H = a_raw.shape[-1]
+    g = np.empty_like(a_raw)
+    al = np.empty_like(a_raw)
+    be = np.empty_like(a_raw)
+    _load().gdn_oracle_gates(_p(a_raw), _p(b_raw), _p(_d(A_log)), _p(_d(dt_bias)),
+                             a_raw.size // H, H, _p(g), _p(al), _p(be))
+    return g, al, be
+
+
+# ------------------------------------------------------------------ eqs. 1-5
+def recurrence(q, k, v, alpha, beta, S0=None, cu_seqlens=None, closed_form=False, nthreads=None):
+    """Token-by-token gated delta rule. q,k: [ntok,H,dk]; v: [ntok,H,dv]; alpha,beta: [ntok,H];
+    S0: [nseq,H,dk,dv] or None. Returns (y [ntok,H,dv], S_T [nseq,H,dk,dv])."""
+    q = _d(q)
+    k = _d(k)
+    v = _d(v)
+    alpha = _d(alpha)
+    beta = _d(beta)
+    ntok, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = [0, ntok]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    nseq = len(cu) - 1
+    s0 = None if S0 is None else _d(S0)
+    y = np.zeros((ntok, H, dv))
+    ST = np.zeros((nseq, H, dk, dv))
+    _load().gdn_oracle_recurrence(_p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(s0),
+                                  cu.ctypes.data_as(_ip), nseq, H, dk, dv, int(closed_form),
+                                  _p(y), _p(ST), nthreads or default_threads())
+    return y, ST
+
+
+# ------------------------------------------------------------------ eq. 11 without W_o
+def output_gate(y, z, w, eps=RMS_EPS):
+    """o = sigmoid(z) * (1 + w) * y / sqrt(mean(y^2) + eps) over the last axis."""
+    y = _d(y)
+    z = _d(z)
+    dv = y.shape[-1]
+    o = np.empty_like(y)
+    _load().gdn_oracle_output_gate(_p(y), _p(z), _p(_d(w)), y.size // dv, dv, eps, _p(o))
+    return o
+
+
+# ------------------------------------------------------------------ whole token mixer
+def preprocess(xq, xk, xv, wq, wk, wv, cu_seqlens, H, l2_eps=L2_EPS):
+    """eqs. 6-8 on pre-conv streams x* [ntok,H,d] (float64 values); w* [H*d, K]."""
+    ntok = xq.shape[0]
+
+    def stream(x, w, norm):
+        d = x.shape[2]
+        a = silu(short_conv(x.reshape(ntok, H * d), w, cu_seqlens)).reshape(ntok, H, d)
+        return l2norm(a, l2_eps) if norm else a
+
+    return stream(xq, wq, True), stream(xk, wk, True), stream(xv, wv, False)
+
+
+def forward(q, k, v, a_raw, b_raw, A_log, dt_bias, S0=None, cu_seqlens=None, nthreads=None):
+    """eqs. 9-10 then eqs. 1-4: returns dict(g, alpha, beta, y, ST)."""
+    g, al, be = gates(a_raw, b_raw, A_log, dt_bias)
+    y, ST = recurrence(q, k, v, al, be, S0, cu_seqlens, nthreads=nthreads)
+    return dict(g=g, alpha=al, beta=be, y=y, ST=ST)
