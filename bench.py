@@ -1,0 +1,253 @@
+"""Benchmark of the Gated DeltaNet token mixer on one MI355X.
+
+A step is one pass of the prefill token mixer over the bf16 workload B=4, H=16, T=4096,
+d_k=d_v=128 (preprocess -> chunked prefill -> output gate), inputs resident in HBM.
+`value` is that pipeline's throughput in Mtok/s (a token spans all 16 heads). The decode
+half of the metric (256 sequences x 32 heads, d=128, 100 steps with fresh tokens, fp32 state
+updated in place) is timed in the same run and reported under "decode".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak, TFLOP/s
+CHUNK = 64
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_algorithmic(H, dk, dv, ntok, nseq, s0, st, in_bytes=2, y_bytes=2):
+    """Algorithmic bytes and flops of one chunked-prefill launch.
+    bytes per token-head: q, k, v read + g, beta (fp32) + y written; per (seq, head): states.
+    flops per token-head: 6 dk dv (Q S, K S (W S), K^T U) + C(2dk + dv) (causal halves of
+    Q K^T, K K^T, P U) + C(dk + dv) (T applied to both sides) + C^2/3 (triangular solve)."""
+    th = ntok * H
+    per_th_bytes = (2 * dk + dv) * in_bytes + 8 + dv * y_bytes
+    state_bytes = nseq * H * dk * dv * 4 * (int(s0) + int(st))
+    per_th_flops = 6 * dk * dv + CHUNK * (2 * dk + dv) + CHUNK * (dk + dv) + CHUNK * CHUNK / 3
+    return th * per_th_bytes + state_bytes, th * per_th_flops
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    from gated_deltanet_recurrence_chunked_amd import inputs as gi
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    def d(a, bf16=False):
+        if bf16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # ------------------------------------------------------------------ prefill workload
+    log("[bench] generating bf16 prefill inputs B=4 H=16 T=4096 d=128")
+    inp = gi.make_inputs(1, seed=0)
+    sh = inp["shape"]
+    H, dk, dv, ntok, nseq = sh.H, sh.dk, sh.dv, sh.ntok, sh.num_seqs
+    X = dict(xq=d(inp["xq"], True), xk=d(inp["xk"], True), xv=d(inp["xv"], True),
+             wq=d(inp["wq"]), wk=d(inp["wk"]), wv=d(inp["wv"]), a_raw=d(inp["a_raw"]),
+             b_raw=d(inp["b_raw"]), A_log=d(inp["A_log"]), dt_bias=d(inp["dt_bias"]),
+             z=d(inp["z"], True), nw=d(inp["norm_weight"]))
+    bf = torch.bfloat16
+    outs = dict(q=torch.empty((ntok, H, dk), dtype=bf, device=dev),
+                k=torch.empty((ntok, H, dk), dtype=bf, device=dev),
+                v=torch.empty((ntok, H, dv), dtype=bf, device=dev),
+                g=torch.empty((ntok, H), dtype=torch.float32, device=dev),
+                beta=torch.empty((ntok, H), dtype=torch.float32, device=dev))
+    y = torch.empty((ntok, H, dv), dtype=bf, device=dev)
+    o = torch.empty((ntok, H, dv), dtype=bf, device=dev)
+    ws_n = gdn.gdn_chunk_prefill_workspace_size(ntok, nseq, H, dk, dv, bf)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = {}
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.setdefault(name, []).append(e)
+
+    def step(timed):
+        if timed:
+            mark("pre0")
+        gdn.gdn_preprocess(X["xq"], X["xk"], X["xv"], X["wq"], X["wk"], X["wv"], X["a_raw"],
+                           X["b_raw"], X["A_log"], X["dt_bias"], H=H, num_seqs=nseq,
+                           out_dtype=bf, outs=outs)
+        if timed:
+            mark("pre1")
+        gdn.gdn_chunk_prefill(outs["q"], outs["k"], outs["v"], outs["g"], outs["beta"],
+                              num_seqs=nseq, y=y, workspace=ws, output_final_state=False)
+        if timed:
+            mark("pf1")
+        gdn.gdn_output_gate(y, X["z"], X["nw"], eps=1e-6, o=o)
+        if timed:
+            mark("og1")
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+
+    def avg(a, b):
+        return float(np.mean([x.elapsed_time(y_) for x, y_ in zip(ev[a], ev[b])]))
+
+    t_pre = avg("pre0", "pre1")
+    t_pf = avg("pre1", "pf1")
+    t_og = avg("pf1", "og1")
+    mtoks = ntok / (ms_step * 1e-3) / 1e6
+    log(f"[bench] pipeline {ms_step * 1e3:.1f} us/step = {mtoks:.1f} Mtok/s "
+        f"(preprocess {t_pre * 1e3:.1f} us, prefill {t_pf * 1e3:.1f} us, gate {t_og * 1e3:.1f} us)")
+
+    pf_bytes, pf_flops = prefill_algorithmic(H, dk, dv, ntok, nseq, False, False)
+    pre_bytes = ntok * H * (2 * dk + dv) * (2 + 2) + ntok * H * 16 + 3 * H * 128 * 4 * 4
+    og_bytes = ntok * H * dv * (2 + 2 + 2)
+    kernels = {
+        "gdn_preprocess": dict(us=t_pre * 1e3, GBs=pre_bytes / (t_pre * 1e-3) / 1e9),
+        "gdn_chunk_prefill": dict(us=t_pf * 1e3, GBs=pf_bytes / (t_pf * 1e-3) / 1e9,
+                                  TFLOPs=pf_flops / (t_pf * 1e-3) / 1e12,
+                                  mfma_frac=pf_flops / (t_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                  Mtok_s=ntok / (t_pf * 1e-3) / 1e6),
+        "gdn_output_gate": dict(us=t_og * 1e3, GBs=og_bytes / (t_og * 1e-3) / 1e9),
+    }
+    pf_gbs = pf_bytes / (t_pf * 1e-3) / 1e9
+    roofline = {"kernel": "gdn_chunk_prefill", "bound": "hbm", "achieved": round(pf_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pf_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "algorithmic_bytes_per_launch": pf_bytes,
+                "mfma": {"achieved_TFLOPs": round(pf_flops / (t_pf * 1e-3) / 1e12, 1),
+                         "peak_TFLOPs": BF16_PEAK_TFLOPS,
+                         "frac": round(pf_flops / (t_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": pf_flops}}
+    del X, outs, y, o, ws
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ decode workload
+    decode = None
+    if not args.no_decode:
+        S_ = args.decode_steps
+        log(f"[bench] generating decode inputs N=256 H=32 d=128, {S_} steps")
+        di = gi.make_inputs(3, seed=0, steps=S_)
+        dsh = di["shape"]
+        N, DH = dsh.num_seqs, dsh.H
+        state = d(di["state"])
+        qd, kd, vd = d(di["q"], True), d(di["k"], True), d(di["v"], True)
+        _, _, _, gd, bd = gdn.gdn_preprocess(None, None, None, None, None, None,
+                                             d(di["a_raw"].reshape(S_ * N, DH)),
+                                             d(di["b_raw"].reshape(S_ * N, DH)),
+                                             d(di["A_log"]), d(di["dt_bias"]), H=DH)
+        gd = gd.view(S_, N, DH)
+        bd = bd.view(S_, N, DH)
+        yd = torch.empty((S_, N, DH, dsh.dv), dtype=bf, device=dev)
+        for s in range(min(3, S_)):      # warm-up (advances the state; timing is unaffected)
+            gdn.gdn_decode_step(qd[s], kd[s], vd[s], gd[s], bd[s], state, y=yd[s])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(S_):
+            gdn.gdn_decode_step(qd[s], kd[s], vd[s], gd[s], bd[s], state, y=yd[s])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / S_
+        heads = N * DH
+        state_bytes = heads * dsh.dk * dsh.dv * 4 * 2
+        tok_bytes = heads * ((2 * dsh.dk + dsh.dv) * 2 + 8 + dsh.dv * 2)
+        gbs = (state_bytes + tok_bytes) / (dms * 1e-3) / 1e9
+        decode = {"workload": "decode N=256 H=32 d_k=d_v=128, fp32 state in place, bf16 tokens",
+                  "steps": S_, "us_per_step": round(dms * 1e3, 2), "GB_s": round(gbs, 1),
+                  "state_only_GB_s": round(state_bytes / (dms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                  "bytes_per_step": state_bytes + tok_bytes}
+        log(f"[bench] decode {dms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
+        del state, qd, kd, vd, gd, bd, yd
+        torch.cuda.empty_cache()
+
+    if args.calibrate_copy:
+        n = 1 << 28
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import gdn_cases as C
+        nseq_s = nseq
+        sub = C.subset(inp, seqs=list(range(nseq_s)))
+        threads = oracle.default_threads()
+        log(f"[bench] timing the fp64 oracle on {nseq_s} sequence x {H} heads x {sh.lengths[0]} "
+            f"tokens with {threads} threads")
+        t0 = time.perf_counter()
+        C.oracle_run(sub, nthreads=threads)
+        dt = time.perf_counter() - t0
+        ntok_s = int(sub["cu"][-1])
+        cpu = {"value": round(ntok_s / dt / 1e6, 6), "unit": "Mtok/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{nseq_s} of {nseq} sequences ({ntok_s} tokens x {H} heads, d=128): "
+                         f"preprocess + gates + recurrence + output gate in fp64, {dt:.1f} s",
+               "cpu": platform.processor() or platform.machine()}
+        log(f"[bench] oracle {dt:.1f} s -> {cpu['value']} Mtok/s")
+
+    out = {
+        "metric": "GDN prefill Mtok/s (H16,d128,T4096) + decode state-update HBM GB/s",
+        "value": round(mtoks, 2), "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "bf16 GDN prefill token mixer: preprocess + chunked prefill "
+                               "(C=64) + output gate", "B": 4, "H": H, "T": sh.lengths[0],
+                   "d_k": dk, "d_v": dv, "tokens_per_step": ntok},
+        "kernels": kernels, "roofline": roofline, "decode": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+"""Gated DeltaNet token mixer for MI355X (gfx950): Python binding of libgdn.so.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI of
+include/gdn.h. torch supplies device memory and the current stream. There is no
+CPU or PyTorch fallback: if libgdn.so is missing these functions raise.
+
+The functions keep the C names:
+  gdn_preprocess     eqs. (6)-(10)  ShortConv -> SiLU -> L2Norm (q, k), SiLU (v), gates
+  gdn_chunk_prefill  eqs. (1)-(4)   chunkwise (C = 64) gated delta rule over packed sequences
+  gdn_decode_step    eqs. (1)-(4)   one token per sequence, state updated in place
+  gdn_output_gate    eq. (11)       sigmoid(z) * zero-centred RMSNorm(y) (without W_o)
+(equation numbers of section 2.1.1 of the reading notes of "On the Design of
+Qwen3.8-Next Architecture").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+GDN_F32 = 0
+GDN_BF16 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GdnError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python -m gated_deltanet_recurrence_chunked_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdn_abi_version.restype = _i
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_status_string.argtypes = [_i]
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_preprocess.restype = _i
+        L.gdn_preprocess.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp,
+                                     _i, _i, _i, _i, _i, ctypes.c_float, _vp, _vp, _vp, _i, _vp,
+                                     _vp, _vp]
+        L.gdn_chunk_prefill_workspace_size.restype = ctypes.c_size_t
+        L.gdn_chunk_prefill_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
+        L.gdn_chunk_prefill.restype = _i
+        L.gdn_chunk_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                        _i, _i, _i, _vp, _i, _vp, ctypes.c_size_t, _vp]
+        L.gdn_decode_step.restype = _i
+        L.gdn_decode_step.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i,
+                                      _vp]
+        L.gdn_output_gate.restype = _i
+        L.gdn_output_gate.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, ctypes.c_float, _vp, _i,
+                                      _vp]
+        _lib = L
+    return _lib
+
+
+# ----------------------------------------------------------------------------- marshalling
+def _dtype_tag(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise GdnError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _tag_dtype(tag: int) -> torch.dtype:
+    return torch.bfloat16 if tag == GDN_BF16 else torch.float32
+
+
+def _ptr(t, name, dtype=None, device=True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise GdnError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise GdnError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise GdnError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise GdnError(f"{name} must be a device tensor")
+    return t.data_ptr() or None
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        L = lib()
+        raise GdnError(f"{fn}: {L.gdn_status_string(status).decode()}: "
+                       f"{L.gdn_last_error().decode()}")
+
+
+def _tag(dtype) -> int:
+    if dtype in (torch.bfloat16, "bf16", GDN_BF16):
+        return GDN_BF16
+    if dtype in (torch.float32, "f32", GDN_F32):
+        return GDN_F32
+    raise GdnError(f"unsupported dtype {dtype}")
+
+
+# ----------------------------------------------------------------------------- entry points
+def gdn_preprocess(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, *, H, cu_seqlens=None,
+                   num_seqs=1, l2_eps=1e-6, out_dtype=torch.bfloat16, ntok=None, outs=None,
+                   stream=None):
+    """eqs. 6-10. x*: [ntok,H,d] (bf16/fp32) or all None (gates only); w*: [H*d,4] fp32;
+    a_raw, b_raw: [ntok,H] fp32 or None (no gates); A_log, dt_bias: [H] fp32.
+    Returns (q, k, v, g, beta) with None for the parts not computed."""
+    conv = xq is not None
+    gates = a_raw is not None
+    ref = xq if conv else a_raw
+    if ntok is None:
+        ntok = ref.shape[0]
+    dk = xq.shape[-1] if conv else 128
+    dv = xv.shape[-1] if conv else 128
+    dev = ref.device
+    x_tag = _dtype_tag(xq) if conv else GDN_F32
+    o_tag = _tag(out_dtype)
+    if outs is None:
+        outs = {}
+    q = k = v = g = beta = None
+    if conv:
+        q = outs.get("q", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
+        k = outs.get("k", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
+        v = outs.get("v", torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=dev))
+    if gates:
+        g = outs.get("g", torch.empty((ntok, H), dtype=torch.float32, device=dev))
+        beta = outs.get("beta", torch.empty((ntok, H), dtype=torch.float32, device=dev))
+    f32 = torch.float32
+    st = lib().gdn_preprocess(
+        _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), x_tag,
+        _ptr(wq, "wq", f32), _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4,
+        _ptr(a_raw, "a_raw", f32), _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32),
+        _ptr(dt_bias, "dt_bias", f32), _ptr(cu_seqlens, "cu_seqlens", torch.int32), num_seqs, ntok,
+        H, dk, dv, l2_eps, _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), o_tag, _ptr(g, "g", f32),
+        _ptr(beta, "beta", f32), _stream(stream))
+    _check(st, "gdn_preprocess")
+    return q, k, v, g, beta
+
+
+def gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, in_dtype=torch.bfloat16) -> int:
+    return int(lib().gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, _tag(in_dtype)))
+
+
+def gdn_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None, cu_seqlens=None,
+                      cu_seqlens_host=None, num_seqs=1, y=None, y_dtype=None, workspace=None,
+                      output_final_state=True, stream=None):
+    """eqs. 1-4 chunkwise. q,k: [ntok,H,dk], v: [ntok,H,dv] (bf16/fp32); g, beta: [ntok,H] fp32;
+    states [num_seqs,H,dk,dv] fp32. Returns (y, final_state)."""
+    ntok, H, dk = q.shape
+    dv = v.shape[-1]
+    in_tag = _dtype_tag(q)
+    y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
+    dev = q.device
+    if y is None:
+        y = torch.empty((ntok, H, dv), dtype=_tag_dtype(y_tag), device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    need = gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, in_tag)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+    f32 = torch.float32
+    st = lib().gdn_chunk_prefill(
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), in_tag, _ptr(g, "g", f32), _ptr(beta, "beta", f32),
+        _ptr(initial_state, "initial_state", f32), _ptr(final_state, "final_state", f32),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32),
+        ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
+        _ptr(y, "y"), y_tag, _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gdn_chunk_prefill")
+    return y, final_state
+
+
+def gdn_decode_step(q, k, v, g, beta, state, *, y=None, y_dtype=None, stream=None):
+    """One token per sequence. q,k: [N,H,dk], v: [N,H,dv]; g,beta: [N,H] fp32;
+    state: [N,H,dk,dv] fp32 updated in place. Returns y [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    in_tag = _dtype_tag(q)
+    y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=_tag_dtype(y_tag), device=q.device)
+    f32 = torch.float32
+    st = lib().gdn_decode_step(_ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), in_tag, _ptr(g, "g", f32),
+                               _ptr(beta, "beta", f32), _ptr(state, "state", f32), N, H, dk, dv,
+                               _ptr(y, "y"), y_tag, _stream(stream))
+    _check(st, "gdn_decode_step")
+    return y
+
+
+def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream=None):
+    """eq. 11 without W_o. y, z: [ntok,H,dv]; norm_weight: [dv] fp32. Returns o."""
+    ntok, H, dv = y.shape
+    o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else _dtype_tag(y))
+    if o is None:
+        o = torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=y.device)
+    st = lib().gdn_output_gate(_ptr(y, "y"), _dtype_tag(y), _ptr(z, "z"), _dtype_tag(z),
+                               _ptr(norm_weight, "norm_weight", torch.float32), ntok, H, dv, eps,
+                               _ptr(o, "o"), o_tag, _stream(stream))
+    _check(st, "gdn_output_gate")
+    return o
+
+
+__all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_chunk_prefill",
+           "gdn_chunk_prefill_workspace_size", "gdn_decode_step", "gdn_output_gate"]

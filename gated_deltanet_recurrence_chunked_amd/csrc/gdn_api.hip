@@ -1,0 +1,209 @@
+// C ABI of libgdn (declared in include/gdn.h): host-side argument validation and dispatch.
+// Validation runs entirely on the host before any HIP call, so a rejected call enqueues
+// nothing and touches no device state.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return GDN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool valid_dim(int d) { return d == 64 || d == 128; }
+bool valid_dtype(int t) { return t == GDN_F32 || t == GDN_BF16; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define GDN_REQUIRE(cond, status, ...) \
+    do {                               \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+#define GDN_PTR(p)                                                               \
+    do {                                                                         \
+        GDN_REQUIRE((p) != nullptr, GDN_ERR_NULL, "%s must not be NULL", #p);   \
+        GDN_REQUIRE(aligned16(p), GDN_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+// scalar-per-element arrays (gates, per-head vectors, offsets) only need 4-byte alignment
+#define GDN_SPTR(p)                                                              \
+    do {                                                                         \
+        GDN_REQUIRE((p) != nullptr, GDN_ERR_NULL, "%s must not be NULL", #p);   \
+        GDN_REQUIRE(aligned4(p), GDN_ERR_ALIGN, "%s is not 4-byte aligned", #p); \
+    } while (0)
+
+#define GDN_OPT_PTR(p) \
+    GDN_REQUIRE((p) == nullptr || aligned16(p), GDN_ERR_ALIGN, "%s is not 16-byte aligned", #p)
+
+// Checks the packing description shared by preprocess and prefill.
+int check_packing(const int32_t* cu_host, bool have_cu, int num_seqs, int ntok) {
+    GDN_REQUIRE(num_seqs >= 1, GDN_ERR_SHAPE, "num_seqs must be >= 1 (got %d)", num_seqs);
+    GDN_REQUIRE(ntok >= 0, GDN_ERR_SHAPE, "ntok must be >= 0 (got %d)", ntok);
+    if (!have_cu)
+        GDN_REQUIRE(ntok % num_seqs == 0, GDN_ERR_SHAPE,
+                    "without cu_seqlens ntok (%d) must be a multiple of num_seqs (%d)", ntok,
+                    num_seqs);
+    if (cu_host) {
+        GDN_REQUIRE(cu_host[0] == 0, GDN_ERR_SEQLENS, "cu_seqlens[0] must be 0");
+        for (int i = 0; i < num_seqs; ++i)
+            GDN_REQUIRE(cu_host[i + 1] >= cu_host[i], GDN_ERR_SEQLENS,
+                        "cu_seqlens must be non-decreasing (index %d)", i + 1);
+        GDN_REQUIRE(cu_host[num_seqs] == ntok, GDN_ERR_SEQLENS,
+                    "cu_seqlens[num_seqs] (%d) must equal ntok (%d)", cu_host[num_seqs], ntok);
+    }
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(int s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL: return "GDN_ERR_NULL";
+        case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE";
+        case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE";
+        case GDN_ERR_SEQLENS: return "GDN_ERR_SEQLENS";
+        case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP";
+        default: return "GDN_ERR_UNKNOWN";
+    }
+}
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,
+                   const float* wk, const float* wv, int conv_k, const float* a_raw,
+                   const float* b_raw, const float* A_log, const float* dt_bias,
+                   const int32_t* cu_seqlens, int num_seqs, int ntok, int H, int dk, int dv,
+                   float l2_eps, void* q, void* k, void* v, int out_dtype, float* g, float* beta,
+                   void* stream) {
+    GDN_REQUIRE(valid_dtype(x_dtype) && valid_dtype(out_dtype), GDN_ERR_DTYPE,
+                "x_dtype/out_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need H >= 1 and dk, dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
+    const bool conv = xq || xk || xv || wq || wk || wv || q || k || v;
+    const bool gates = a_raw || b_raw || A_log || dt_bias || g || beta;
+    GDN_REQUIRE(conv || gates, GDN_ERR_NULL, "nothing to compute: all inputs are NULL");
+    if (conv) {
+        GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv);
+        GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
+        GDN_PTR(q); GDN_PTR(k); GDN_PTR(v);
+        GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
+        GDN_REQUIRE(l2_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps must be >= 0");
+    }
+    if (gates) {
+        GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias); GDN_SPTR(g);
+        GDN_SPTR(beta);
+    }
+    GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+    int st = check_packing(nullptr, cu_seqlens != nullptr, num_seqs, ntok);
+    if (st) return st;
+
+    gdn::PreprocessArgs a;
+    a.x[0] = conv ? xq : nullptr; a.x[1] = conv ? xk : nullptr; a.x[2] = conv ? xv : nullptr;
+    a.w[0] = wq; a.w[1] = wk; a.w[2] = wv;
+    a.out[0] = q; a.out[1] = k; a.out[2] = v;
+    a.d[0] = dk; a.d[1] = dk; a.d[2] = dv;
+    a.in_bf16 = x_dtype == GDN_BF16;
+    a.out_bf16 = out_dtype == GDN_BF16;
+    a.a_raw = gates ? a_raw : nullptr;
+    a.b_raw = b_raw; a.A_log = A_log; a.dt_bias = dt_bias; a.g = g; a.beta = beta;
+    a.cu = cu_seqlens;
+    a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.l2_eps = l2_eps;
+    return hip_status(gdn::launch_preprocess(a, static_cast<hipStream_t>(stream)), "gdn_preprocess");
+}
+
+size_t gdn_chunk_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, int dv, int in_dtype) {
+    (void)ntok; (void)num_seqs; (void)H; (void)dk; (void)dv; (void)in_dtype;
+    return 0;
+}
+
+int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                      const float* beta, const float* initial_state, float* final_state,
+                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
+                      int ntok, int H, int dk, int dv, void* y, int y_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    GDN_REQUIRE(valid_dtype(in_dtype) && valid_dtype(y_dtype), GDN_ERR_DTYPE,
+                "in_dtype/y_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need H >= 1 and dk, dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
+    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(y);
+    GDN_OPT_PTR(initial_state); GDN_OPT_PTR(final_state);
+    GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+    GDN_REQUIRE(cu_seqlens_host == nullptr || cu_seqlens != nullptr, GDN_ERR_NULL,
+                "cu_seqlens_host given without the device cu_seqlens");
+    int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
+    if (st) return st;
+    const size_t need = gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, in_dtype);
+    GDN_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr), GDN_ERR_WORKSPACE,
+                "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    GDN_OPT_PTR(workspace);
+
+    gdn::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.in_bf16 = in_dtype == GDN_BF16;
+    a.y_bf16 = y_dtype == GDN_BF16;
+    a.g = g; a.beta = beta; a.S0 = initial_state; a.ST = final_state;
+    a.cu = cu_seqlens;
+    a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.dk = dk; a.dv = dv;
+    a.y = y; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(gdn::launch_chunk_fp32(a, s), "gdn_chunk_prefill");
+}
+
+int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                    const float* beta, float* state, int N, int H, int dk, int dv, void* y,
+                    int y_dtype, void* stream) {
+    GDN_REQUIRE(valid_dtype(in_dtype) && valid_dtype(y_dtype), GDN_ERR_DTYPE,
+                "in_dtype/y_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(N >= 0 && H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need N >= 0, H >= 1 and dk, dv in {64, 128} (got N=%d H=%d dk=%d dv=%d)", N, H,
+                dk, dv);
+    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(state); GDN_PTR(y);
+    return hip_status(gdn::launch_decode(q, k, v, in_dtype == GDN_BF16, g, beta, state, N, H, dk,
+                                         dv, y, y_dtype == GDN_BF16,
+                                         static_cast<hipStream_t>(stream)),
+                      "gdn_decode_step");
+}
+
+int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype, const float* norm_weight,
+                    int ntok, int H, int dv, float eps, void* o, int o_dtype, void* stream) {
+    GDN_REQUIRE(valid_dtype(y_dtype) && valid_dtype(z_dtype) && valid_dtype(o_dtype), GDN_ERR_DTYPE,
+                "y_dtype/z_dtype/o_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(ntok >= 0 && H >= 1 && valid_dim(dv), GDN_ERR_SHAPE,
+                "need ntok >= 0, H >= 1 and dv in {64, 128} (got ntok=%d H=%d dv=%d)", ntok, H, dv);
+    GDN_REQUIRE(eps >= 0.f, GDN_ERR_SHAPE, "eps must be >= 0");
+    GDN_PTR(y); GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o);
+    return hip_status(gdn::launch_output_gate(y, y_dtype == GDN_BF16, z, z_dtype == GDN_BF16,
+                                              norm_weight, ntok, H, dv, eps, o,
+                                              o_dtype == GDN_BF16, static_cast<hipStream_t>(stream)),
+                      "gdn_output_gate");
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Device helpers shared by the gfx950 kernels of libgdn: bf16 <-> fp32, typed vector
+// loads and stores, wave64 reductions, and the math functions of the gates.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kWave = 64;
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// --------------------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+// --------------------------------------------------------------------------- typed 8-wide IO
+// Element type tags: float (fp32) or uint16_t (bf16 bits).
+template <typename T> struct Vec8;
+
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float* p, float (&x)[8]) {
+        const float4 a = reinterpret_cast<const float4*>(p)[0];
+        const float4 b = reinterpret_cast<const float4*>(p)[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&x)[8]) {
+        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+};
+
+template <> struct Vec8<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[8]) {
+        uint4 a;
+        a.x = pack_bf2(x[0], x[1]);
+        a.y = pack_bf2(x[2], x[3]);
+        a.z = pack_bf2(x[4], x[5]);
+        a.w = pack_bf2(x[6], x[7]);
+        *reinterpret_cast<uint4*>(p) = a;
+    }
+};
+
+// 4-wide
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ void load(const float* p, float (&x)[4]) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&x)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+};
+template <> struct Vec4<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[4]) {
+        const uint2 a = *reinterpret_cast<const uint2*>(p);
+        x[0] = __uint_as_float(a.x << 16);
+        x[1] = __uint_as_float(a.x & 0xffff0000u);
+        x[2] = __uint_as_float(a.y << 16);
+        x[3] = __uint_as_float(a.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[4]) {
+        uint2 a;
+        a.x = pack_bf2(x[0], x[1]);
+        a.y = pack_bf2(x[2], x[3]);
+        *reinterpret_cast<uint2*>(p) = a;
+    }
+};
+
+template <typename T> __device__ __forceinline__ float load1(const T* p);
+template <> __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+
+template <typename T> __device__ __forceinline__ void store1(T* p, float x);
+template <> __device__ __forceinline__ void store1<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void store1<uint16_t>(uint16_t* p, float x) { *p = f2bf(x); }
+
+// --------------------------------------------------------------------------- reductions
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int o = width / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
+// --------------------------------------------------------------------------- gate math
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}): no overflow, no cancellation
+__device__ __forceinline__ float softplusf_(float x) {
+    return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+}
+
+}  // namespace gdn

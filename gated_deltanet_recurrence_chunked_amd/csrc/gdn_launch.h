@@ -1,0 +1,46 @@
+// Host-side launchers of the libgdn kernels (internal; the public ABI is include/gdn.h).
+// Each launcher assumes its arguments were validated by the caller and returns the
+// HIP error of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct PreprocessArgs {
+    const void* x[3];     // xq, xk, xv (NULL: stream skipped)
+    const float* w[3];    // conv taps [H*d, 4]
+    void* out[3];         // q, k, v
+    int d[3];             // dk, dk, dv
+    int in_bf16, out_bf16;
+    const float *a_raw, *b_raw, *A_log, *dt_bias;  // NULL a_raw: gates skipped
+    float *g, *beta;
+    const int32_t* cu;    // NULL: equal lengths
+    int num_seqs, ntok, H;
+    float l2_eps;
+};
+hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s);
+
+hipError_t launch_output_gate(const void* y, int y_bf16, const void* z, int z_bf16,
+                              const float* w, int ntok, int H, int dv, float eps, void* o,
+                              int o_bf16, hipStream_t s);
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, int in_bf16,
+                         const float* g, const float* beta, float* state, int N, int H,
+                         int dk, int dv, void* y, int y_bf16, hipStream_t s);
+
+struct ChunkArgs {
+    const void *q, *k, *v;
+    int in_bf16, y_bf16;
+    const float *g, *beta, *S0;
+    float* ST;
+    const int32_t* cu;    // NULL: equal lengths
+    int num_seqs, ntok, H, dk, dv;
+    void* y;
+    void* workspace;
+    size_t workspace_bytes;
+};
+// all-fp32 chunked path (vector ALU)
+hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,240 @@
+// Pre- and post-processing of the Gated DeltaNet layer on gfx950: memory-bound streaming
+// kernels (reading notes of "On the Design of Qwen3.8-Next Architecture", section 2.1.1).
+//
+//   preprocess  : eqs. (6)-(8) ShortConv (width 4, depthwise, causal) -> SiLU -> L2Norm on
+//                 q and k, ShortConv -> SiLU on v; eqs. (9)-(10) the per-head gates.
+//   output gate : eq. (11) without W_o, sigmoid(z) * zero-centred RMSNorm(y).
+//
+// Layout: token-major [ntok, H, d], so one token's H*d channels are contiguous. A thread
+// owns 8 consecutive channels (one 16-byte bf16 or 32-byte fp32 access), a workgroup of
+// 256 threads owns a 2048-channel tile, and the d/8 lanes of one head are adjacent lanes
+// of one wave, so the L2Norm / RMSNorm reductions are in-register shuffles.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int kPreThreads = 256;
+constexpr int kPreTile = kPreThreads * 8;   // channels per workgroup
+constexpr int kPreTokens = 32;              // tokens per workgroup (3-token conv halo)
+constexpr int kConvK = 4;
+
+struct PreKernelArgs {
+    PreprocessArgs a;
+    int tiles[3];        // channel tiles per stream
+    int gate_blocks;     // 1 if gates are computed
+};
+
+// Index of the sequence holding token t: largest s with cu[s] <= t (skips empty sequences).
+__device__ __forceinline__ int seq_of(const int32_t* cu, int num_seqs, int t) {
+    int lo = 0, hi = num_seqs;   // invariant: cu[lo] <= t < cu[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+template <typename Tin, typename Tout>
+__device__ void conv_stream(const PreprocessArgs& a, int role, int tile, int t0) {
+    const int d = a.d[role];
+    const int C = a.H * d;
+    const int c = tile * kPreTile + threadIdx.x * 8;
+    if (c >= C) return;   // whole heads drop out together (C and the tile are multiples of d)
+    const Tin* x = static_cast<const Tin*>(a.x[role]);
+    Tout* out = static_cast<Tout*>(a.out[role]);
+    const bool norm = role < 2;
+
+    float w[8][kConvK];
+    {
+        const float4* wp = reinterpret_cast<const float4*>(a.w[role] + (size_t)c * kConvK);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float4 t = wp[i];
+            w[i][0] = t.x; w[i][1] = t.y; w[i][2] = t.z; w[i][3] = t.w;
+        }
+    }
+    const int t1 = min(a.ntok, t0 + kPreTokens);
+
+    // sequence bookkeeping (uniform over the workgroup)
+    int s, seq_lo, seq_hi;
+    if (a.cu) {
+        s = seq_of(a.cu, a.num_seqs, t0);
+        seq_lo = a.cu[s];
+        seq_hi = a.cu[s + 1];
+    } else {
+        const int L = a.ntok / a.num_seqs;
+        s = t0 / L;
+        seq_lo = s * L;
+        seq_hi = seq_lo + L;
+    }
+
+    // history window: win[0] = x[t-3] ... win[2] = x[t-1], zero before the sequence start
+    float win[3][8];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int src = t0 - 3 + j;
+        if (src >= seq_lo) {
+            Vec8<Tin>::load(x + (size_t)src * C + c, win[j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) win[j][i] = 0.f;
+        }
+    }
+
+    for (int t = t0; t < t1; ++t) {
+        if (t >= seq_hi) {   // crossed into the next non-empty sequence: history restarts
+            if (a.cu) {
+                while (a.cu[s + 1] <= t) ++s;
+                seq_hi = a.cu[s + 1];
+            } else {
+                seq_hi += a.ntok / a.num_seqs;
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) win[j][i] = 0.f;
+        }
+        float cur[8];
+        Vec8<Tin>::load(x + (size_t)t * C + c, cur);
+        float act[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float u = w[i][0] * win[0][i] + w[i][1] * win[1][i] + w[i][2] * win[2][i] +
+                      w[i][3] * cur[i];
+            float sv = u / (1.0f + expf(-u));   // SiLU
+            act[i] = sv;
+            ss += sv * sv;
+        }
+        if (norm) {
+            ss = (d == 128) ? group_sum<16>(ss) : group_sum<8>(ss);
+            const float inv = 1.0f / sqrtf(ss + a.l2_eps);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) act[i] *= inv;
+        }
+        Vec8<Tout>::store(out + (size_t)t * C + c, act);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            win[0][i] = win[1][i];
+            win[1][i] = win[2][i];
+            win[2][i] = cur[i];
+        }
+    }
+}
+
+__device__ void gates_block(const PreprocessArgs& a, int t0) {
+    const int n = min(kPreTokens, a.ntok - t0) * a.H;
+    for (int i = threadIdx.x; i < n; i += kPreThreads) {
+        const size_t e = (size_t)t0 * a.H + i;
+        const int h = i % a.H;
+        a.g[e] = -expf(a.A_log[h]) * softplusf_(a.a_raw[e] + a.dt_bias[h]);
+        a.beta[e] = sigmoidf_(a.b_raw[e]);
+    }
+}
+
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(kPreThreads) preprocess_kernel(PreKernelArgs p) {
+    const int t0 = blockIdx.x * kPreTokens;
+    int y = blockIdx.y;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        if (y < p.tiles[r]) {
+            conv_stream<Tin, Tout>(p.a, r, y, t0);
+            return;
+        }
+        y -= p.tiles[r];
+    }
+    if (y < p.gate_blocks) gates_block(p.a, t0);
+}
+
+hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s) {
+    PreKernelArgs p;
+    p.a = a;
+    int ny = 0;
+    for (int r = 0; r < 3; ++r) {
+        p.tiles[r] = a.x[r] ? (a.H * a.d[r] + kPreTile - 1) / kPreTile : 0;
+        ny += p.tiles[r];
+    }
+    p.gate_blocks = a.a_raw ? 1 : 0;
+    ny += p.gate_blocks;
+    if (a.ntok == 0 || ny == 0) return hipSuccess;
+    dim3 grid((a.ntok + kPreTokens - 1) / kPreTokens, ny);
+    if (a.in_bf16 && a.out_bf16)
+        hipLaunchKernelGGL((preprocess_kernel<uint16_t, uint16_t>), grid, dim3(kPreThreads), 0, s, p);
+    else if (a.in_bf16)
+        hipLaunchKernelGGL((preprocess_kernel<uint16_t, float>), grid, dim3(kPreThreads), 0, s, p);
+    else if (a.out_bf16)
+        hipLaunchKernelGGL((preprocess_kernel<float, uint16_t>), grid, dim3(kPreThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((preprocess_kernel<float, float>), grid, dim3(kPreThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------- output gate
+constexpr int kGateThreads = 256;
+
+template <typename Ty, typename Tz, typename To, int DV>
+__global__ void __launch_bounds__(kGateThreads)
+output_gate_kernel(const Ty* __restrict__ y, const Tz* __restrict__ z, const float* __restrict__ w,
+                   long rows, float eps, To* __restrict__ o) {
+    constexpr int LPR = DV / 8;                    // lanes per (token, head) row
+    constexpr int RPB = kGateThreads / LPR;        // rows per workgroup pass
+    const int lane_c = (threadIdx.x % LPR) * 8;
+    float gain[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gain[i] = 1.0f + w[lane_c + i];
+    for (long r = (long)blockIdx.x * RPB + threadIdx.x / LPR; r < rows; r += (long)gridDim.x * RPB) {
+        const size_t off = (size_t)r * DV + lane_c;
+        float yv[8], zv[8];
+        Vec8<Ty>::load(y + off, yv);
+        Vec8<Tz>::load(z + off, zv);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += yv[i] * yv[i];
+        ss = group_sum<LPR>(ss);
+        const float inv = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+        float ov[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ov[i] = sigmoidf_(zv[i]) * (gain[i] * (yv[i] * inv));
+        Vec8<To>::store(o + off, ov);
+    }
+}
+
+template <int DV>
+static void launch_gate_dv(const void* y, int yb, const void* z, int zb, const float* w, long rows,
+                           float eps, void* o, int ob, hipStream_t s) {
+    constexpr int RPB = kGateThreads / (DV / 8);
+    long blocks = (rows + RPB - 1) / RPB;
+    int grid = (int)(blocks < 16384 ? blocks : 16384);
+#define GDN_GATE(TY, TZ, TO)                                                                 \
+    hipLaunchKernelGGL((output_gate_kernel<TY, TZ, TO, DV>), dim3(grid), dim3(kGateThreads), 0, s, \
+                       static_cast<const TY*>(y), static_cast<const TZ*>(z), w, rows, eps,   \
+                       static_cast<TO*>(o))
+    const int key = (yb << 2) | (zb << 1) | ob;
+    switch (key) {
+        case 0: GDN_GATE(float, float, float); break;
+        case 1: GDN_GATE(float, float, uint16_t); break;
+        case 2: GDN_GATE(float, uint16_t, float); break;
+        case 3: GDN_GATE(float, uint16_t, uint16_t); break;
+        case 4: GDN_GATE(uint16_t, float, float); break;
+        case 5: GDN_GATE(uint16_t, float, uint16_t); break;
+        case 6: GDN_GATE(uint16_t, uint16_t, float); break;
+        default: GDN_GATE(uint16_t, uint16_t, uint16_t); break;
+    }
+#undef GDN_GATE
+}
+
+hipError_t launch_output_gate(const void* y, int y_bf16, const void* z, int z_bf16, const float* w,
+                              int ntok, int H, int dv, float eps, void* o, int o_bf16,
+                              hipStream_t s) {
+    const long rows = (long)ntok * H;
+    if (rows == 0) return hipSuccess;
+    if (dv == 128)
+        launch_gate_dv<128>(y, y_bf16, z, z_bf16, w, rows, eps, o, o_bf16, s);
+    else
+        launch_gate_dv<64>(y, y_bf16, z, z_bf16, w, rows, eps, o, o_bf16, s);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

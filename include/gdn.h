@@ -1,0 +1,157 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) Gated DeltaNet token-mixer library (libgdn.so).
+ *
+ * The operations are those of the Gated DeltaNet layer in the reading notes of
+ * "On the Design of Qwen3.8-Next Architecture" (arXiv 2608.30320), section 2.1.1:
+ *   eqs. (1)-(4) the gated delta rule, eq. (5) its closed form,
+ *   eqs. (6)-(8) q,k = L2Norm(SiLU(ShortConv(.))), v = SiLU(ShortConv(.)),
+ *   eqs. (9)-(10) beta = sigmoid(.), alpha = exp[-exp(A) softplus(. + b_alpha)],
+ *   eq. (11) o = W_o[sigmoid(W_z x) * RMSNorm(y)] with a zero-centred RMSNorm.
+ * Per head: q, k in R^dk, v in R^dv, state S in R^{dk x dv} (rows over dk, columns
+ * over dv: the transpose of the original GDN convention), y = S^T q. The decay and
+ * write-strength gates are one scalar per (token, head) (section 3.1 of the same notes).
+ * The projections W_q, W_k, W_v, W_alpha, W_beta, W_z, W_o are dense GEMMs of the
+ * surrounding model and are not part of this library: its inputs are the projected
+ * streams.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees or retains device memory and keeps no mutable global state.
+ *   - Layouts are dense, row-major and token-major over packed sequences:
+ *       q, k [ntok, H, dk]; v, y, z, o [ntok, H, dv]; g, beta, a_raw, b_raw [ntok, H];
+ *       states [num_seqs, H, dk, dv] (fp32); per-head vectors [H]; norm weight [dv].
+ *   - bf16 tensors hold IEEE bfloat16 bit patterns (round-to-nearest-even on output).
+ *   - Pointers to vector data (x*, q, k, v, y, z, o, conv taps, states, workspace) must be
+ *     16-byte aligned; scalar arrays (g, beta, a_raw, b_raw, A_log, dt_bias, norm weight,
+ *     cu_seqlens) 4-byte aligned. dk, dv in {64, 128}. H >= 1.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
+ *     asynchronous on it: it validates its arguments on the host, enqueues its kernels
+ *     and returns. Device faults surface when the caller synchronises.
+ *   - On invalid arguments a call returns a non-zero gdn_status, enqueues nothing and
+ *     records a message readable with gdn_last_error() on the calling thread. A failed
+ *     launch returns GDN_ERR_HIP with the HIP error text. No C++ exception crosses the ABI.
+ *   - Calls are re-entrant and thread-safe; calls on one stream execute in order.
+ *   - NaN/Inf inputs are not checked; they propagate into their own (token, head)
+ *     slice (and, for the recurrence, into that sequence-head's later outputs and state).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,      /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,     /* unsupported or inconsistent sizes */
+    GDN_ERR_DTYPE = 3,     /* unsupported dtype tag */
+    GDN_ERR_SEQLENS = 4,   /* cu_seqlens (host mirror) is not 0 = c0 <= c1 <= ... = ntok */
+    GDN_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
+    GDN_ERR_WORKSPACE = 6, /* workspace missing or smaller than required */
+    GDN_ERR_HIP = 7        /* a HIP runtime call failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+/* Static text naming a status code. */
+const char* gdn_status_string(int status);
+
+/* Message of the last failed call on the calling thread ("" if none). Valid until the
+ * next call from the same thread. */
+const char* gdn_last_error(void);
+
+/*
+ * gdn_preprocess - eqs. (6)-(10): ShortConv -> SiLU -> L2Norm for q and k,
+ * ShortConv -> SiLU for v, and the per-head scalar gates.
+ *
+ *   xq, xk: [ntok, H, dk], xv: [ntok, H, dv] in x_dtype - the projected streams W x.
+ *   wq, wk: [H*dk, conv_k], wv: [H*dv, conv_k] fp32 - depthwise causal conv taps; tap
+ *       conv_k-1 multiplies the current token, tap 0 the oldest. No bias. Inputs before
+ *       each sequence start count as zero (the conv restarts at every sequence).
+ *   conv_k must be 4.
+ *   a_raw, b_raw: [ntok, H] fp32 - W_alpha x and W_beta x.
+ *   A_log, dt_bias: [H] fp32 - A and b_alpha of eq. (10).
+ *   cu_seqlens: [num_seqs+1] int32 device offsets, or NULL for num_seqs equal-length
+ *       sequences (ntok must then be a multiple of num_seqs).
+ *   l2_eps: L2Norm(x) = x / sqrt(sum(x^2) + l2_eps) over the dk channels of one head-token.
+ *   q, k, v: outputs in out_dtype, same layouts as xq, xk, xv.
+ *   g: [ntok, H] fp32 output, g = log(alpha) = -exp(A_log) * softplus(a_raw + dt_bias).
+ *   beta: [ntok, H] fp32 output, beta = sigmoid(b_raw).
+ * Gates-only mode: pass xq, xk, xv, wq, wk, wv, q, k, v all NULL; then only g and beta
+ * are computed. Passing g, beta, a_raw, b_raw, A_log, dt_bias all NULL skips the gates.
+ */
+int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype,
+                   const float* wq, const float* wk, const float* wv, int conv_k,
+                   const float* a_raw, const float* b_raw, const float* A_log,
+                   const float* dt_bias, const int32_t* cu_seqlens, int num_seqs, int ntok,
+                   int H, int dk, int dv, float l2_eps, void* q, void* k, void* v,
+                   int out_dtype, float* g, float* beta, void* stream);
+
+/* Bytes of device workspace gdn_chunk_prefill needs for these sizes (may be 0). */
+size_t gdn_chunk_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, int dv,
+                                        int in_dtype);
+
+/*
+ * gdn_chunk_prefill - eqs. (1)-(4) over packed sequences, evaluated chunkwise with
+ * C = 64 tokens per chunk (an exact re-association of eq. (5)'s product; chunks restart
+ * at every sequence start).
+ *
+ *   q, k: [ntok, H, dk], v: [ntok, H, dv] in in_dtype (q, k are expected L2-normalised).
+ *   g: [ntok, H] fp32 log-decay (alpha = exp(g), g <= 0); beta: [ntok, H] fp32.
+ *   initial_state: [num_seqs, H, dk, dv] fp32, or NULL for zero states.
+ *   final_state: [num_seqs, H, dk, dv] fp32 output, or NULL (not written). It may be the
+ *       same pointer as initial_state (updated in place); otherwise it must not overlap
+ *       any input.
+ *   cu_seqlens: [num_seqs+1] int32 device offsets, or NULL for equal lengths.
+ *   cu_seqlens_host: optional host copy of cu_seqlens; when given it is validated.
+ *   y: [ntok, H, dv] output in y_dtype, y_t = S_t^T q_t.
+ *   workspace: device scratch of at least gdn_chunk_prefill_workspace_size(...) bytes
+ *       (may be NULL when that size is 0); it must not be shared by concurrent calls.
+ * in_dtype GDN_F32 runs an all-fp32 chunked path; GDN_BF16 runs bf16 matrix-core
+ * products with fp32 accumulation and an fp32 state.
+ */
+int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
+                      const float* g, const float* beta, const float* initial_state,
+                      float* final_state, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
+                      int dv, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * gdn_decode_step - one token per sequence through eqs. (1)-(4), state updated in place:
+ * S <- alpha S; e = v - S^T k; S <- S + beta k e^T; y = S^T q.
+ *
+ *   q, k: [N, H, dk], v: [N, H, dv] in in_dtype; g, beta: [N, H] fp32 (alpha = exp(g)).
+ *   state: [N, H, dk, dv] fp32, read and overwritten.
+ *   y: [N, H, dv] output in y_dtype.
+ */
+int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                    const float* beta, float* state, int N, int H, int dk, int dv, void* y,
+                    int y_dtype, void* stream);
+
+/*
+ * gdn_output_gate - eq. (11) without W_o:
+ *   o = sigmoid(z) * (1 + w) * y / sqrt(mean_j(y_j^2) + eps)
+ * per (token, head) over the dv channels; w is the zero-centred RMSNorm weight, shared
+ * by all heads.
+ *
+ *   y: [ntok, H, dv] in y_dtype; z: [ntok, H, dv] in z_dtype (W_z x, before the sigmoid);
+ *   norm_weight: [dv] fp32; o: [ntok, H, dv] output in o_dtype.
+ */
+int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype,
+                    const float* norm_weight, int ntok, int H, int dv, float eps, void* o,
+                    int o_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

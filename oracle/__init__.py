@@ -159,6 +159,17 @@ def output_gate(y, z, w, eps=RMS_EPS):
     return o
 
 
+# ------------------------------------------------------------------ storage format
+def round_bf16(x):
+    """Values as stored in bfloat16: fp64 -> fp32 (round to nearest even) -> bf16 (round to
+    nearest even), widened back to fp64. Models a path that keeps an intermediate in bf16."""
+    f = np.ascontiguousarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    b = ((u + r) >> np.uint32(16)) << np.uint32(16)
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 # ------------------------------------------------------------------ whole token mixer
 def preprocess(xq, xk, xv, wq, wk, wv, cu_seqlens, H, l2_eps=L2_EPS):
     """eqs. 6-8 on pre-conv streams x* [ntok,H,d] (float64 values); w* [H*d, K]."""

@@ -1,0 +1,191 @@
+"""Shared drivers of the parity tests: run one workload through the HIP path (libgdn via the
+Python binding) and through the fp64 oracle, on the same seeded raw draws.
+
+The oracle side never sees a value produced by the HIP path: both start from the input
+generator's arrays. Sampled comparisons restrict the oracle to a subset of (sequence, head)
+slices; the recurrence of one slice depends on nothing outside it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from gated_deltanet_recurrence_chunked_amd import inputs as gi
+
+L2_EPS = 1e-6
+RMS_EPS = 1e-6
+
+# Tolerances of the parity bar: max over (sequence, head) slices of ||a-b|| / ||b||, and
+# an elementwise bound on the bf16-input path.
+TOL_REL = {False: 1e-4, True: 5e-3}        # keyed by "bf16 path"
+TOL_ABS = 2e-2
+BF16_HALF_ULP_REL = 2.0 ** -8              # RNE rounding bound of a bf16-stored output
+
+
+# ----------------------------------------------------------------------------- host <-> device
+def dev(a: np.ndarray, bf16: bool = False):
+    import torch
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def f64(inp, key):
+    sh = inp["shape"]
+    bf = inp[key].dtype == np.uint16
+    return gi.as_f64(inp[key], bf)
+
+
+# ----------------------------------------------------------------------------- metrics
+def slice_rel_errors(a: np.ndarray, b: np.ndarray, cu, H: int) -> np.ndarray:
+    """Relative L2 error per (sequence, head) slice of token-major [ntok, H, ...] arrays."""
+    errs = []
+    for lo, hi in zip(cu[:-1], cu[1:]):
+        if hi == lo:
+            continue
+        for h in range(H):
+            x = a[lo:hi, h].ravel()
+            y = b[lo:hi, h].ravel()
+            errs.append(np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-30))
+    return np.array(errs)
+
+
+def state_rel_errors(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Per (sequence, head) relative L2 error of [nseq, H, dk, dv] states."""
+    n = a.shape[0] * a.shape[1]
+    x = a.reshape(n, -1)
+    y = b.reshape(n, -1)
+    return np.linalg.norm(x - y, axis=1) / np.maximum(np.linalg.norm(y, axis=1), 1e-30)
+
+
+def assert_close(name, got, ref, bf16_path, stored_bf16=False, cu=None, H=None, state=False,
+                 ref_elem=None):
+    """The parity bar: max slice relative L2 <= TOL_REL; on the bf16 path also
+    |got - ref| <= 2e-2 (+ the output's own bf16 rounding if it is stored in bf16).
+    ref_elem, when given, is the reference of the elementwise check (the oracle with the
+    pipeline's bf16 storage of intermediates modelled)."""
+    if state:
+        errs = state_rel_errors(got, ref)
+    else:
+        errs = slice_rel_errors(got, ref, cu, H)
+    worst = float(errs.max()) if errs.size else 0.0
+    tol = TOL_REL[bf16_path]
+    assert worst <= tol, f"{name}: max slice rel L2 {worst:.3e} > {tol:.0e}"
+    if bf16_path:
+        r = ref if ref_elem is None else ref_elem
+        bound = TOL_ABS + (BF16_HALF_ULP_REL * np.abs(r) if stored_bf16 else 0.0)
+        excess = np.abs(got - r) - bound
+        assert np.all(excess <= 0), (f"{name}: max |diff| {np.abs(got - r).max():.3e} "
+                                     f"exceeds elementwise bound")
+    return worst
+
+
+# ----------------------------------------------------------------------------- oracle side
+def subset(inp: dict, seqs=None, heads=None) -> dict:
+    """Restrict a workload to some sequences and heads (the oracle evaluates only those).
+    Returns a dict of float64 arrays plus cu_seqlens, H and the token index map."""
+    sh = inp["shape"]
+    cu = inp["cu_seqlens"]
+    seqs = list(range(sh.num_seqs)) if seqs is None else list(seqs)
+    heads = list(range(sh.H)) if heads is None else list(heads)
+    tok = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs]).astype(np.int64) \
+        if seqs else np.zeros(0, np.int64)
+    new_cu = np.concatenate([[0], np.cumsum([cu[s + 1] - cu[s] for s in seqs])]).astype(np.int32)
+    out = dict(cu=new_cu, H=len(heads), tok=tok, seqs=seqs, heads=heads)
+    for key in ("q", "k", "v", "xq", "xk", "xv", "z"):
+        if key in inp:
+            out[key] = f64(inp, key)[tok][:, heads]
+    for key in ("a_raw", "b_raw"):
+        if key in inp:
+            out[key] = inp[key].astype(np.float64)[tok][:, heads]
+    for key in ("A_log", "dt_bias"):
+        out[key] = inp[key].astype(np.float64)[heads]
+    for key, d in (("wq", sh.dk), ("wk", sh.dk), ("wv", sh.dv)):
+        if key in inp:
+            w = inp[key].astype(np.float64).reshape(sh.H, d, -1)
+            out[key] = w[heads].reshape(len(heads) * d, -1)
+    if "norm_weight" in inp:
+        out["norm_weight"] = inp["norm_weight"].astype(np.float64)
+    if inp.get("S0") is not None:
+        out["S0"] = inp["S0"].astype(np.float64)[seqs][:, heads]
+    return out
+
+
+def oracle_run(sub: dict, nthreads=None, storage_bf16=False, y_bf16=True) -> dict:
+    """The oracle's token mixer on a subset: eqs. 6-10 (if pre-conv streams), 1-4, 11.
+    storage_bf16 rounds the intermediates the bf16 pipeline stores (q, k, v after the
+    preprocess, y before the output gate) to bf16, in the oracle's own arithmetic."""
+    H = sub["H"]
+    res = {}
+    if "xq" in sub:
+        q, k, v = oracle.preprocess(sub["xq"], sub["xk"], sub["xv"], sub["wq"], sub["wk"],
+                                    sub["wv"], sub["cu"], H, L2_EPS)
+        if storage_bf16:
+            q, k, v = oracle.round_bf16(q), oracle.round_bf16(k), oracle.round_bf16(v)
+        res.update(q=q, k=k, v=v)
+    else:
+        q, k, v = sub["q"], sub["k"], sub["v"]
+    g, al, be = oracle.gates(sub["a_raw"], sub["b_raw"], sub["A_log"], sub["dt_bias"])
+    res.update(g=g, beta=be)
+    y, ST = oracle.recurrence(q, k, v, al, be, sub.get("S0"), sub["cu"], nthreads=nthreads)
+    res.update(y=y, ST=ST)
+    if "z" in sub:
+        yo = oracle.round_bf16(y) if (storage_bf16 and y_bf16) else y
+        res["o"] = oracle.output_gate(yo, sub["z"], sub["norm_weight"], RMS_EPS)
+    return res
+
+
+# ----------------------------------------------------------------------------- HIP side
+def gpu_run(inp: dict, y_dtype="bf16", state_out=True) -> dict:
+    """The HIP path on the whole workload. Returns device tensors."""
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    sh = inp["shape"]
+    bf = sh.bf16
+    cu = inp["cu_seqlens"]
+    cu_d = None if sh.equal_lengths else dev(cu)
+    cu_h = None if sh.equal_lengths else cu
+    f32 = lambda a: dev(np.asarray(a, dtype=np.float32))  # noqa: E731
+    res = {}
+    if sh.conv:
+        q, k, v, g, beta = gdn.gdn_preprocess(
+            dev(inp["xq"], True), dev(inp["xk"], True), dev(inp["xv"], True),
+            f32(inp["wq"]), f32(inp["wk"]), f32(inp["wv"]), f32(inp["a_raw"]), f32(inp["b_raw"]),
+            f32(inp["A_log"]), f32(inp["dt_bias"]), H=sh.H, cu_seqlens=cu_d,
+            num_seqs=sh.num_seqs, l2_eps=L2_EPS, out_dtype=torch.bfloat16)
+    else:
+        q, k, v = dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf)
+        _, _, _, g, beta = gdn.gdn_preprocess(None, None, None, None, None, None,
+                                              f32(inp["a_raw"]), f32(inp["b_raw"]),
+                                              f32(inp["A_log"]), f32(inp["dt_bias"]), H=sh.H,
+                                              num_seqs=1)
+    res.update(q=q, k=k, v=v, g=g, beta=beta)
+    S0 = f32(inp["S0"]) if inp.get("S0") is not None else None
+    y, ST = gdn.gdn_chunk_prefill(q, k, v, g, beta, initial_state=S0, cu_seqlens=cu_d,
+                                  cu_seqlens_host=cu_h, num_seqs=sh.num_seqs, y_dtype=y_dtype,
+                                  output_final_state=state_out)
+    res.update(y=y, ST=ST)
+    if "z" in inp:
+        res["o"] = gdn.gdn_output_gate(y, dev(inp["z"], True), f32(inp["norm_weight"]),
+                                       eps=RMS_EPS, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    return res
+
+
+def gpu_slice(t, tok, heads):
+    """Token/head subset of a device [ntok, H, ...] tensor, as float64 numpy."""
+    import torch
+    idx_t = torch.as_tensor(tok, device=t.device)
+    idx_h = torch.as_tensor(heads, device=t.device)
+    return host(t.index_select(0, idx_t).index_select(1, idx_h))
+
+
+def gpu_state_slice(t, seqs, heads):
+    import torch
+    return host(t.index_select(0, torch.as_tensor(seqs, device=t.device))
+                .index_select(1, torch.as_tensor(heads, device=t.device)))

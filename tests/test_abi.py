@@ -1,0 +1,88 @@
+"""The C ABI without a GPU: libgdn.so loads, exports every function include/gdn.h declares,
+and rejects invalid arguments on the host before any HIP call (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_recurrence_chunked_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.skip("libgdn.so not built")
+    return gdn.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"gdn_preprocess", "gdn_chunk_prefill", "gdn_decode_step", "gdn_output_gate"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.gdn_abi_version() == 1
+
+
+def test_status_strings(L):
+    assert L.gdn_status_string(0) == b"GDN_OK"
+    assert L.gdn_status_string(7) == b"GDN_ERR_HIP"
+
+
+FAKE = 0x10000      # 16-byte aligned non-null address; never dereferenced (validation fails first)
+MIS = 0x10004       # misaligned
+
+
+def _prefill(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=1, g=FAKE, beta=FAKE, s0=None, st=None, cu=None,
+             cu_host=None, num_seqs=1, ntok=128, H=2, dk=128, dv=128, y=FAKE, y_dtype=1, ws=None,
+             wsb=0)
+    a.update(kw)
+    return L.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["in_dtype"], a["g"], a["beta"], a["s0"],
+                               a["st"], a["cu"], a["cu_host"], a["num_seqs"], a["ntok"], a["H"],
+                               a["dk"], a["dv"], a["y"], a["y_dtype"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_validation(L):
+    assert _prefill(L, q=None) == 1
+    assert L.gdn_last_error().startswith(b"q must not be NULL")
+    assert _prefill(L, dk=96) == 2
+    assert _prefill(L, in_dtype=5) == 3
+    assert _prefill(L, k=MIS) == 5
+    assert _prefill(L, num_seqs=3, ntok=128) == 2          # 128 not a multiple of 3
+    bad = (ctypes.c_int32 * 3)(0, 100, 120)                # last offset != ntok
+    assert _prefill(L, num_seqs=2, cu=FAKE, cu_host=ctypes.cast(bad, ctypes.c_void_p)) == 4
+    dec = (ctypes.c_int32 * 3)(0, 100, 90)
+    dec2 = (ctypes.c_int32 * 3)(0, 100, 128)
+    assert _prefill(L, num_seqs=2, cu=FAKE, cu_host=ctypes.cast(dec, ctypes.c_void_p)) == 4
+    assert _prefill(L, num_seqs=2, cu=None, cu_host=ctypes.cast(dec2, ctypes.c_void_p)) == 1
+
+
+def test_decode_and_gate_validation(L):
+    assert L.gdn_decode_step(FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 4, 2, 128, 128, FAKE, 1, None) == 1
+    assert L.gdn_decode_step(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 0, 128, 128, FAKE, 1, None) == 2
+    assert L.gdn_output_gate(FAKE, 1, FAKE, 1, FAKE, 10, 2, 32, 1e-6, FAKE, 1, None) == 2
+    assert L.gdn_output_gate(FAKE, 1, FAKE, 1, FAKE, 10, 2, 128, -1.0, FAKE, 1, None) == 2
+    assert L.gdn_output_gate(FAKE, 2, FAKE, 1, FAKE, 10, 2, 128, 1e-6, FAKE, 1, None) == 3
+
+
+def test_preprocess_validation(L):
+    n = None
+    # nothing to do
+    assert L.gdn_preprocess(n, n, n, 1, n, n, n, 4, n, n, n, n, n, 1, 8, 2, 128, 128, 1e-6,
+                            n, n, n, 1, n, n, None) == 1
+    # conv width other than 4
+    assert L.gdn_preprocess(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 3, n, n, n, n, n, 1, 8, 2, 128,
+                            128, 1e-6, FAKE, FAKE, FAKE, 1, n, n, None) == 2
+    # half of the gate pointers
+    assert L.gdn_preprocess(n, n, n, 1, n, n, n, 4, FAKE, FAKE, n, n, n, 1, 8, 2, 128, 128, 1e-6,
+                            n, n, n, 1, n, n, None) == 1

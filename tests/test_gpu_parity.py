@@ -1,0 +1,117 @@
+"""GPU parity of the HIP path against the fp64 oracle (reduced sizes: several chunks,
+ragged tails, empty and short sequences). Every case prints its name before touching the GPU."""
+import sys
+
+import numpy as np
+import pytest
+
+from gated_deltanet_recurrence_chunked_amd import inputs as gi
+import gdn_cases as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _compare_prefill(inp, res, ref, sub, y_bf16, ref_st=None):
+    sh = inp["shape"]
+    bf = sh.bf16
+    tok, heads, seqs = sub["tok"], sub["heads"], sub["seqs"]
+    cu, H = sub["cu"], sub["H"]
+    report = {}
+    if sh.conv:
+        for key in ("q", "k", "v"):
+            report[key] = C.assert_close(key, C.gpu_slice(res[key], tok, heads), ref[key], True,
+                                         stored_bf16=True, cu=cu, H=H)
+    for key in ("g", "beta"):
+        got = C.gpu_slice(res[key], tok, heads)
+        err = np.abs(got - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30)
+        assert err < 1e-5, f"{key}: {err}"
+    report["y"] = C.assert_close("y", C.gpu_slice(res["y"], tok, heads), ref["y"], bf,
+                                 stored_bf16=y_bf16, cu=cu, H=H)
+    if res.get("ST") is not None:
+        report["ST"] = C.assert_close("ST", C.gpu_state_slice(res["ST"], seqs, heads), ref["ST"], bf,
+                                      state=True)
+    if "o" in res:
+        # RMSNorm rescales each (token, head) row of y to unit RMS, so in rows where y is
+        # small (first tokens of a sequence) the bf16 storage rounding of q, k, v is amplified;
+        # the elementwise check therefore models that storage in the oracle.
+        report["o"] = C.assert_close("o", C.gpu_slice(res["o"], tok, heads), ref["o"], True,
+                                     stored_bf16=True, cu=cu, H=H,
+                                     ref_elem=None if ref_st is None else ref_st["o"])
+    print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in report.items()}, flush=True)
+
+
+CASES = [
+    # (cfg, overrides, y dtype)
+    (0, {}, "f32"),
+    (0, dict(T=200, d=128), "f32"),
+    (0, dict(B=3, T=130, d=64), "f32"),
+    (1, dict(B=2, H=3, T=200), "f32"),
+    (1, dict(B=2, H=3, T=200), "bf16"),
+    (1, dict(B=1, H=2, T=70, d=64), "f32"),
+    (2, dict(H=2, T=1000), "f32"),
+    (4, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130]), "f32"),
+    (4, dict(H=2, nseq=5, lmax=600), "bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg,ov,ydt", CASES, ids=[f"cfg{c}-{o}-{y}" for c, o, y in CASES])
+def test_prefill_pipeline_parity(gpu, cfg, ov, ydt):
+    _announce(f"prefill cfg={cfg} {ov} y={ydt}")
+    inp = gi.make_inputs(cfg, seed=0, **ov)
+    res = C.gpu_run(inp, y_dtype=ydt)
+    sub = C.subset(inp)
+    ref = C.oracle_run(sub)
+    ref_st = C.oracle_run(sub, storage_bf16=True, y_bf16=(ydt == "bf16")) if "z" in sub else None
+    _compare_prefill(inp, res, ref, sub, ydt == "bf16", ref_st)
+
+
+@pytest.mark.parametrize("ov,ydt", [(dict(N=8, H=2, steps=6), "f32"),
+                                    (dict(N=5, H=3, steps=4, d=64), "bf16")])
+def test_decode_steps_parity(gpu, ov, ydt):
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    _announce(f"decode {ov} y={ydt}")
+    inp = gi.make_inputs(3, seed=0, **ov)
+    sh = inp["shape"]
+    S_, N, H = sh.steps, sh.num_seqs, sh.H
+    state = C.dev(inp["state"])
+    f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))  # noqa: E731
+    _, _, _, g, beta = gdn.gdn_preprocess(None, None, None, None, None, None,
+                                          f32(inp["a_raw"].reshape(S_ * N, H)),
+                                          f32(inp["b_raw"].reshape(S_ * N, H)),
+                                          f32(inp["A_log"]), f32(inp["dt_bias"]), H=H)
+    g = g.view(S_, N, H)
+    beta = beta.view(S_, N, H)
+    ys = []
+    for s in range(S_):
+        ys.append(gdn.gdn_decode_step(C.dev(inp["q"][s], True), C.dev(inp["k"][s], True),
+                                      C.dev(inp["v"][s], True), g[s].contiguous(),
+                                      beta[s].contiguous(), state, y_dtype=ydt))
+    torch.cuda.synchronize()
+    # oracle: each sequence is the S-token sequence of its decode steps
+    perm = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1).reshape(N * S_, *a.shape[2:]))  # noqa
+    q = perm(gi.as_f64(inp["q"], True))
+    k = perm(gi.as_f64(inp["k"], True))
+    v = perm(gi.as_f64(inp["v"], True))
+    og, al, be = C.oracle.gates(perm(inp["a_raw"].astype(np.float64)),
+                                perm(inp["b_raw"].astype(np.float64)),
+                                inp["A_log"].astype(np.float64), inp["dt_bias"].astype(np.float64))
+    cu = np.arange(0, N * S_ + 1, S_)
+    y_ref, S_ref = C.oracle.recurrence(q, k, v, al, be, inp["state"].astype(np.float64), cu)
+    y_gpu = np.stack([C.host(y) for y in ys], axis=1).reshape(N * S_, H, sh.dv)
+    C.assert_close("y", y_gpu, y_ref, True, stored_bf16=(ydt == "bf16"), cu=cu, H=H)
+    C.assert_close("S", C.host(state), S_ref, True, state=True)
+
+
+def test_prefill_is_deterministic(gpu):
+    _announce("determinism cfg1 small")
+    inp = gi.make_inputs(1, seed=3, B=2, H=2, T=150)
+    a = C.gpu_run(inp, y_dtype="f32")
+    b = C.gpu_run(inp, y_dtype="f32")
+    for key in ("q", "k", "v", "y", "ST", "o"):
+        assert np.array_equal(C.host(a[key]), C.host(b[key])), key

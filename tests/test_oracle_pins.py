@@ -313,3 +313,10 @@ def test_output_gate_constant_rows_and_scale_invariance():
     # w = 0 and a saturated gate: RMS of the output is one
     o3 = oracle.output_gate(y, np.full_like(y, 800.0), np.zeros(dv), eps=0.0)
     assert np.allclose(np.sqrt(np.mean(o3 * o3, axis=-1)), 1.0, rtol=1e-14)
+
+
+def test_bf16_storage_rounding_matches_torch():
+    import torch
+    x = np.random.default_rng(25).standard_normal(50000) * 7
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(oracle.round_bf16(x), ref)
