@@ -1,0 +1,552 @@
+// Chunkwise gated delta rule on gfx950 matrix cores (bf16 operands, fp32 accumulation,
+// fp32 state). Reading notes of "On the Design of Qwen3.8-Next Architecture", section
+// 2.1.1, eqs. (1)-(5); chunk length C = 64.
+//
+// Inside one chunk of one (sequence, head), with G_r the running sum of g = log(alpha),
+// gamma_r = e^{G_r}, unrolling eq. (5) gives (rows = tokens):
+//   A[r,i] = beta_r e^{G_r-G_i} (k_r . k_i) for i < r,   T = (I + A)^{-1}   (unit lower)
+//   P[r,i] = e^{G_r-G_i} (q_r . k_i) for i <= r
+//   R      = diag(beta) (V - diag(gamma) K S)             U = T R
+//   Y      = diag(gamma) Q S + P U
+//   S_next = gamma_C S + K^T diag(gamma_C / gamma) U
+// T and P depend on the chunk's q, k, g, beta only, so they are produced for every chunk at
+// once by chunk_prep_kernel (massively parallel: KK^T and QK^T on MFMA, the 64x64 unit
+// lower-triangular inverse by fp32 forward substitution). chunk_scan_kernel then walks the
+// chunks of each (sequence, head) in order. The columns of S, V, U and Y are independent, so
+// a scan workgroup owns a 32-column slice of dv: 4 workgroups per head at dv = 128, mapped to
+// the same XCD so the shared q, k, T, P tiles are fetched from HBM once and hit that XCD's L2.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 operand layout (lane l of 64): A element j is A[l%32][(l/32)*8+j],
+// B element j is B[(l/32)*8+j][l%32], accumulator element i is C[8(i/4)+4(l/32)+i%4][l%32].
+// Every LDS tile is stored with the contraction index contiguous (A as [row][k], B as
+// [col][k]) so each operand fragment is one 16-byte LDS read; rows are padded by 16 bytes
+// so the 32 rows read by one fragment load fall in distinct banks.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kC = 64;                // chunk length
+constexpr int kThreads = 256;         // 4 waves
+constexpr int kDK = 128;              // key dim of the matrix-core path
+constexpr int kSl = 32;               // dv columns per scan workgroup
+constexpr int kStrD = kDK + 8;        // LDS row stride (elements) of [*, 128] bf16 tiles
+constexpr int kStrC = kC + 8;         // LDS row stride (elements) of [*, 64] bf16 tiles
+constexpr int kStrA = kC + 4;         // LDS row stride of the fp32 A matrix
+constexpr int kMaxSorted = 1024;      // longest-first ordering up to this many sequences
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// accumulator element i of lane l -> tile row
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// Stores the 32x32 accumulator tile, converted to bf16, transposed: dst[col][row0 + row].
+__device__ __forceinline__ void store_acc_t(uint16_t* dst, int stride, int row0, const f32x16& c,
+                                            int lane) {
+    uint16_t* base = dst + (lane & 31) * stride + row0 + 4 * (lane >> 5);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        u32x2 v;
+        v.x = pack_bf2(c[4 * q + 0], c[4 * q + 1]);
+        v.y = pack_bf2(c[4 * q + 2], c[4 * q + 3]);
+        *reinterpret_cast<u32x2*>(base + 8 * q) = v;
+    }
+}
+
+// Same, as a two-term bf16 split: hi = bf16(x), lo = bf16(x - hi), so hi + lo carries about
+// 16 significant bits; products against it take two MFMAs.
+__device__ __forceinline__ void store_acc_t2(uint16_t* hi, uint16_t* lo, int stride, int row0,
+                                             const f32x16& c, int lane) {
+    const int off = (lane & 31) * stride + row0 + 4 * (lane >> 5);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = bf2f(f2bf(c[4 * q + e]));
+            l[e] = c[4 * q + e] - h[e];
+        }
+        u32x2 vh, vl;
+        vh.x = pack_bf2(h[0], h[1]);
+        vh.y = pack_bf2(h[2], h[3]);
+        vl.x = pack_bf2(l[0], l[1]);
+        vl.y = pack_bf2(l[2], l[3]);
+        *reinterpret_cast<u32x2*>(hi + off + 8 * q) = vh;
+        *reinterpret_cast<u32x2*>(lo + off + 8 * q) = vl;
+    }
+}
+
+struct Layout {
+    size_t cs, ord, T, P, Plo, total;
+    int max_chunks;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline Layout ws_layout(int ntok, int num_seqs, int H) {
+    Layout L;
+    L.max_chunks = (ntok + kC - 1) / kC + num_seqs;
+    size_t o = 0;
+    L.cs = o;  o = align256(o + sizeof(int32_t) * (num_seqs + 1));
+    L.ord = o; o = align256(o + sizeof(int32_t) * num_seqs);
+    const size_t tile = (size_t)kC * kC * sizeof(uint16_t);
+    L.T = o;   o = align256(o + tile * L.max_chunks * H);
+    L.P = o;   o = align256(o + tile * L.max_chunks * H);
+    L.Plo = o; o = align256(o + tile * L.max_chunks * H);
+    L.total = o;
+    return L;
+}
+
+struct DevArgs {
+    const uint16_t *q, *k, *v;
+    const float *g, *beta, *S0;
+    float* ST;
+    void* y;
+    const int32_t* cu;          // NULL: equal lengths
+    int32_t* chunk_start;       // [num_seqs+1] (varlen)
+    int32_t* order;             // [num_seqs] longest first (varlen)
+    uint16_t *Tw, *Pw, *Plw;    // [max_chunks][H][64][64]; P = Pw + Plw (hi + lo bf16)
+    int num_seqs, ntok, H, dv, L;  // L: equal length (when cu == NULL)
+    int y_bf16;
+};
+
+// ------------------------------------------------------------------ chunk table (varlen)
+__global__ void __launch_bounds__(kThreads) chunk_table_kernel(DevArgs a) {
+    __shared__ int scan[kThreads];
+    const int tid = threadIdx.x;
+    int running = 0;
+    if (tid == 0) a.chunk_start[0] = 0;
+    for (int base = 0; base < a.num_seqs; base += kThreads) {
+        const int s = base + tid;
+        const int c = s < a.num_seqs ? (a.cu[s + 1] - a.cu[s] + kC - 1) / kC : 0;
+        scan[tid] = c;
+        __syncthreads();
+        for (int off = 1; off < kThreads; off <<= 1) {
+            const int v = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        if (s < a.num_seqs) a.chunk_start[s + 1] = running + scan[tid];
+        running += scan[kThreads - 1];
+        __syncthreads();
+    }
+    // longest sequences first, so their scans start first (stable for equal lengths)
+    for (int i = tid; i < a.num_seqs; i += kThreads) {
+        if (a.num_seqs > kMaxSorted) {
+            a.order[i] = i;
+            continue;
+        }
+        const int Li = a.cu[i + 1] - a.cu[i];
+        int rank = 0;
+        for (int j = 0; j < a.num_seqs; ++j) {
+            const int Lj = a.cu[j + 1] - a.cu[j];
+            rank += (Lj > Li) || (Lj == Li && j < i);
+        }
+        a.order[rank] = i;
+    }
+}
+
+// Rows [0, 64) of one chunk of a [ntok, H, 128] bf16 tensor: 256 threads x 4 x 16 bytes,
+// fetched into registers (all loads in flight together; rows >= n read row n-1 and are
+// zeroed when written to LDS, so no load sits behind a branch).
+__device__ __forceinline__ void fetch_rows128(u32x4 (&R)[4], const uint16_t* src, int t0, int n,
+                                              int H, int h) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = threadIdx.x + kThreads * it;
+        const int r = min(idx >> 4, n - 1), d0 = (idx & 15) * 8;
+        R[it] = *reinterpret_cast<const u32x4*>(src + ((size_t)(t0 + r) * H + h) * kDK + d0);
+    }
+}
+__device__ __forceinline__ void put_rows128(uint16_t* dst, const u32x4 (&R)[4], int n) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = threadIdx.x + kThreads * it;
+        const int r = idx >> 4, d0 = (idx & 15) * 8;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(dst + r * kStrD + d0) = r < n ? R[it] : z;
+    }
+}
+
+// Wave 0: the chunk's gates (lane = token; rows >= n read row n-1, zeroed below).
+__device__ __forceinline__ void fetch_gates(const DevArgs& a, int t0, int n, int h, float& gv,
+                                            float& bv) {
+    const int r = min((int)(threadIdx.x & (kWave - 1)), n - 1);
+    gv = a.g[(size_t)(t0 + r) * a.H + h];
+    bv = a.beta[(size_t)(t0 + r) * a.H + h];
+}
+
+// Wave 0: running sum of g over the chunk (rows >= n contribute 0), written with beta.
+__device__ __forceinline__ void chunk_gates(float gv, float bv, int n, float* sG, float* sB,
+                                            float* sGam, float* sGd) {
+    const int lane = threadIdx.x;
+    if (lane >= n) {
+        gv = 0.f;
+        bv = 0.f;
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(gv, off, kWave);
+        if (lane >= off) gv += o;
+    }
+    const float gC = __shfl(gv, kC - 1, kWave);
+    sG[lane] = gv;
+    sB[lane] = bv;
+    if (sGam) sGam[lane] = expf(gv);
+    if (sGd) sGd[lane] = expf(gC - gv);
+}
+
+// chunk index -> (sequence, first token, length)
+__device__ __forceinline__ bool chunk_of(const DevArgs& a, int chunk, int& seq, int& t0, int& n) {
+    if (!a.cu) {
+        const int cps = (a.L + kC - 1) / kC;
+        if (cps == 0) return false;
+        seq = chunk / cps;
+        if (seq >= a.num_seqs) return false;
+        const int c = chunk - seq * cps;
+        t0 = seq * a.L + c * kC;
+        n = min(kC, a.L - c * kC);
+        return true;
+    }
+    if (chunk >= a.chunk_start[a.num_seqs]) return false;
+    int lo = 0, hi = a.num_seqs;   // chunk_start[lo] <= chunk < chunk_start[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.chunk_start[mid] <= chunk) lo = mid; else hi = mid;
+    }
+    seq = lo;
+    const int c = chunk - a.chunk_start[seq];
+    t0 = a.cu[seq] + c * kC;
+    n = min(kC, a.cu[seq + 1] - t0);
+    return true;
+}
+
+// ------------------------------------------------------------------ per-chunk T and P
+__global__ void __launch_bounds__(kThreads) chunk_prep_kernel(DevArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kStrD];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kStrD];
+    __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
+    __shared__ float sG[kC], sB[kC];
+
+    const int chunk = blockIdx.x, h = blockIdx.y;
+    int seq, t0, n;
+    if (!chunk_of(a, chunk, seq, t0, n)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    u32x4 rk[4], rq[4];
+    fetch_rows128(rk, a.k, t0, n, a.H, h);
+    fetch_rows128(rq, a.q, t0, n, a.H, h);
+    float gv, bv;
+    fetch_gates(a, t0, n, h, gv, bv);
+    put_rows128(sK, rk, n);
+    put_rows128(sQ, rq, n);
+    if (wave == 0) chunk_gates(gv, bv, n, sG, sB, nullptr, nullptr);
+    __syncthreads();
+
+    const size_t tile = ((size_t)chunk * a.H + h) * kC * kC;
+    if (wave < 3) {
+        // wave 0: rows 0-31 x cols 0-31; wave 1: rows 32-63 x cols 0-31; wave 2: rows 32-63 x cols 32-63
+        const int R0 = wave == 0 ? 0 : 32, C0 = wave == 2 ? 32 : 0;
+        f32x16 ckk = {}, cqk = {};
+#pragma unroll
+        for (int kk = 0; kk < kDK / 16; ++kk) {
+            const int ko = kk * 16 + (lane >> 5) * 8;
+            const bf16x8 b = frag(sK + (C0 + (lane & 31)) * kStrD + ko);
+            const bf16x8 ak = frag(sK + (R0 + (lane & 31)) * kStrD + ko);
+            const bf16x8 aq = frag(sQ + (R0 + (lane & 31)) * kStrD + ko);
+            ckk = mfma(ak, b, ckk);
+            cqk = mfma(aq, b, cqk);
+        }
+        const int c = C0 + (lane & 31);
+        const float Gc = sG[c];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = R0 + acc_row(i, lane);
+            const float dec = c <= r ? expf(sG[r] - Gc) : 0.f;
+            sA[r * kStrA + c] = c < r ? sB[r] * dec * ckk[i] : 0.f;
+            const float p = dec * cqk[i];
+            const uint16_t ph = f2bf(p);
+            a.Pw[tile + r * kC + c] = ph;
+            a.Plw[tile + r * kC + c] = f2bf(p - bf2f(ph));
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // T = (I + A)^{-1}: lane = column, forward substitution over the rows
+        const int c = lane;
+        float t[kC];
+#pragma unroll
+        for (int r = 0; r < kC; ++r) {
+            float acc = r == c ? 1.f : 0.f;
+            const float* Ar = sA + r * kStrA;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= Ar[i] * t[i];
+            t[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < kC; ++r) a.Tw[tile + r * kC + c] = f2bf(t[r]);
+    }
+}
+
+// ------------------------------------------------------------------ sequential chunk scan
+constexpr int kStrV = kSl + 8;
+
+// Next chunk's inputs, held in registers while the current chunk computes (all loads are
+// unconditional so the compiler keeps them in VGPRs and waits for them only where used).
+#define GDN_FETCH_STAGE(T0, N, TILE)                                                           \
+    do {                                                                                       \
+        fetch_rows128(stq, a.q, (T0), (N), a.H, h);                                            \
+        fetch_rows128(stk, a.k, (T0), (N), a.H, h);                                            \
+        _Pragma("unroll") for (int it = 0; it < 2; ++it) {                                     \
+            const int idx = tid + kThreads * it;                                               \
+            const size_t off = (TILE) + (idx >> 3) * kC + (idx & 7) * 8;                       \
+            stt[it] = *reinterpret_cast<const u32x4*>(a.Tw + off);                             \
+            stp[it] = *reinterpret_cast<const u32x4*>(a.Pw + off);                             \
+            stpl[it] = *reinterpret_cast<const u32x4*>(a.Plw + off);                           \
+        }                                                                                      \
+        const int vr = min(tid >> 2, (N) - 1);                                                 \
+        stv = *reinterpret_cast<const u32x4*>(a.v + ((size_t)((T0) + vr) * a.H + h) * a.dv +  \
+                                              j0 + (tid & 3) * 8);                             \
+        fetch_gates(a, (T0), (N), h, stg, stb);                                                \
+    } while (0)
+
+template <typename Ty>
+__global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kStrD];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kStrD];
+    __shared__ __attribute__((aligned(16))) uint16_t sT[kC * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sP[kC * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sPl[kC * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kStrV];
+    __shared__ __attribute__((aligned(16))) uint16_t sSt[kSl * kStrD];    // S^T hi
+    __shared__ __attribute__((aligned(16))) uint16_t sStl[kSl * kStrD];   // S^T lo
+    __shared__ __attribute__((aligned(16))) uint16_t sRt[kSl * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sRtl[kSl * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sUt[kSl * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sUtl[kSl * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sUht[kSl * kStrC];   // (diag(gamma_C/gamma) U)^T
+    __shared__ __attribute__((aligned(16))) uint16_t sUhtl[kSl * kStrC];
+    __shared__ float sG[kC], sB[kC], sGam[kC], sGd[kC];
+
+    // block -> (pair, slice): the slices of one pair are 8 blocks apart, so the same XCD
+    const int nsl = a.dv / kSl;
+    const int b = blockIdx.x;
+    const int group = b / (8 * nsl), within = b % (8 * nsl);
+    const int slice = within >> 3;
+    const int pair = group * 8 + (within & 7);
+    if (pair >= a.num_seqs * a.H) return;
+    const int rank = pair / a.H, h = pair % a.H;
+    const int seq = a.order ? a.order[rank] : rank;
+    int lo, hi, cbase;
+    if (a.cu) {
+        lo = a.cu[seq];
+        hi = a.cu[seq + 1];
+        cbase = a.chunk_start[seq];
+    } else {
+        lo = seq * a.L;
+        hi = lo + a.L;
+        cbase = seq * ((a.L + kC - 1) / kC);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j0 = slice * kSl;
+    const int col = lane & 31;
+    const int kofs = (lane >> 5) * 8;
+    const size_t sbase = ((size_t)seq * a.H + h) * kDK * a.dv;
+
+    // state rows [32 wave, 32 wave + 32) of this slice, accumulator layout
+    f32x16 S;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = 32 * wave + acc_row(i, lane);
+        S[i] = a.S0 ? a.S0[sbase + (size_t)row * a.dv + j0 + col] : 0.f;
+    }
+    store_acc_t2(sSt, sStl, kStrD, 32 * wave, S, lane);
+
+    const int nchunks = (hi - lo + kC - 1) / kC;
+    u32x4 stq[4], stk[4], stt[2], stp[2], stpl[2], stv;
+    float stg, stb;
+    if (nchunks > 0) GDN_FETCH_STAGE(lo, min(kC, hi - lo), ((size_t)cbase * a.H + h) * kC * kC);
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = lo + c * kC;
+        const int n = min(kC, hi - t0);
+        // ---- commit the staged chunk to LDS
+        put_rows128(sQ, stq, n);
+        put_rows128(sK, stk, n);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int idx = tid + kThreads * it;
+            const int o = (idx >> 3) * kStrC + (idx & 7) * 8;
+            *reinterpret_cast<u32x4*>(sT + o) = stt[it];
+            *reinterpret_cast<u32x4*>(sP + o) = stp[it];
+            *reinterpret_cast<u32x4*>(sPl + o) = stpl[it];
+        }
+        {
+            const int r = tid >> 2;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(sV + r * kStrV + (tid & 3) * 8) = r < n ? stv : z;
+        }
+        if (wave == 0) chunk_gates(stg, stb, n, sG, sB, sGam, sGd);
+        __syncthreads();
+        // ---- prefetch the next chunk while this one computes (the last chunk re-reads itself)
+        {
+            const int cn = min(c + 1, nchunks - 1);
+            const int t1 = lo + cn * kC;
+            GDN_FETCH_STAGE(t1, min(kC, hi - t1), ((size_t)(cbase + cn) * a.H + h) * kC * kC);
+        }
+
+        // ---- step 1: [Q; K] S (waves 0, 1: Q rows; waves 2, 3: K rows), S = S_hi + S_lo
+        f32x16 acc = {};
+        {
+            const uint16_t* Arow = (wave < 2 ? sQ : sK) + (32 * (wave & 1) + col) * kStrD + kofs;
+            const uint16_t* Bh = sSt + col * kStrD + kofs;
+            const uint16_t* Bl = sStl + col * kStrD + kofs;
+#pragma unroll
+            for (int kk = 0; kk < kDK / 16; ++kk) {
+                const bf16x8 af = frag(Arow + kk * 16);
+                acc = mfma(af, frag(Bh + kk * 16), acc);
+                acc = mfma(af, frag(Bl + kk * 16), acc);
+            }
+        }
+        if (wave >= 2) {
+            // R = beta (V - gamma K S)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 32 * (wave - 2) + acc_row(i, lane);
+                acc[i] = sB[r] * (bf2f(sV[r * kStrV + col]) - sGam[r] * acc[i]);
+            }
+            store_acc_t2(sRt, sRtl, kStrC, 32 * (wave - 2), acc, lane);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] *= sGam[32 * wave + acc_row(i, lane)];
+        }
+        __syncthreads();
+
+        // ---- step 2: U = T R (T is unit lower triangular: rows 0-31 need k < 32 only)
+        if (wave >= 2) {
+            const int r0 = 32 * (wave - 2);
+            f32x16 u = {};
+            const uint16_t* Arow = sT + (r0 + col) * kStrC + kofs;
+            const uint16_t* Bh = sRt + col * kStrC + kofs;
+            const uint16_t* Bl = sRtl + col * kStrC + kofs;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 2 * (wave - 1)) {
+                    const bf16x8 af = frag(Arow + kk * 16);
+                    u = mfma(af, frag(Bh + kk * 16), u);
+                    u = mfma(af, frag(Bl + kk * 16), u);
+                }
+            }
+            store_acc_t2(sUt, sUtl, kStrC, r0, u, lane);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) u[i] *= sGd[r0 + acc_row(i, lane)];
+            store_acc_t2(sUht, sUhtl, kStrC, r0, u, lane);
+        }
+        __syncthreads();
+
+        // ---- step 3a: Y = gamma Q S + P U  (waves 0, 1), P = P_hi + P_lo, U = U_hi + U_lo
+        if (wave < 2) {
+            const uint16_t* Ah = sP + (32 * wave + col) * kStrC + kofs;
+            const uint16_t* Al = sPl + (32 * wave + col) * kStrC + kofs;
+            const uint16_t* Bh = sUt + col * kStrC + kofs;
+            const uint16_t* Bl = sUtl + col * kStrC + kofs;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 2 * (wave + 1)) {
+                    const bf16x8 ah = frag(Ah + kk * 16), bh = frag(Bh + kk * 16);
+                    acc = mfma(ah, bh, acc);
+                    acc = mfma(ah, frag(Bl + kk * 16), acc);
+                    acc = mfma(frag(Al + kk * 16), bh, acc);
+                }
+            }
+            Ty* y = static_cast<Ty*>(a.y);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 32 * wave + acc_row(i, lane);
+                if (r < n) store1(y + ((size_t)(t0 + r) * a.H + h) * a.dv + j0 + col, acc[i]);
+            }
+        }
+        // ---- step 3b: S = gamma_C S + K^T Uh  (rows 32 wave.. of S; K^T fragments read
+        //      column-wise from the row-major K tile)
+        {
+            const float gC = sGam[kC - 1];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S[i] *= gC;
+            const int d = 32 * wave + col;
+            const uint16_t* Bh = sUht + col * kStrC + kofs;
+            const uint16_t* Bl = sUhtl + col * kStrC + kofs;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int ko = kk * 16 + kofs;
+                bf16x8 af;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    af[j] = __builtin_bit_cast(__bf16, sK[(ko + j) * kStrD + d]);
+                S = mfma(af, frag(Bh + kk * 16), S);
+                S = mfma(af, frag(Bl + kk * 16), S);
+            }
+            store_acc_t2(sSt, sStl, kStrD, 32 * wave, S, lane);
+        }
+        __syncthreads();
+    }
+    if (a.ST) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 32 * wave + acc_row(i, lane);
+            a.ST[sbase + (size_t)row * a.dv + j0 + col] = S[i];
+        }
+    }
+}
+#undef GDN_FETCH_STAGE
+
+}  // namespace
+
+size_t chunk_bf16_workspace(int ntok, int num_seqs, int H) {
+    return ws_layout(ntok, num_seqs, H).total;
+}
+
+hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
+    const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
+    char* ws = static_cast<char*>(c.workspace);
+    DevArgs a;
+    a.q = static_cast<const uint16_t*>(c.q);
+    a.k = static_cast<const uint16_t*>(c.k);
+    a.v = static_cast<const uint16_t*>(c.v);
+    a.g = c.g; a.beta = c.beta; a.S0 = c.S0; a.ST = c.ST; a.y = c.y;
+    a.cu = c.cu;
+    a.chunk_start = c.cu ? reinterpret_cast<int32_t*>(ws + L.cs) : nullptr;
+    a.order = c.cu ? reinterpret_cast<int32_t*>(ws + L.ord) : nullptr;
+    a.Tw = reinterpret_cast<uint16_t*>(ws + L.T);
+    a.Pw = reinterpret_cast<uint16_t*>(ws + L.P);
+    a.Plw = reinterpret_cast<uint16_t*>(ws + L.Plo);
+    a.num_seqs = c.num_seqs; a.ntok = c.ntok; a.H = c.H; a.dv = c.dv;
+    a.L = c.cu ? 0 : c.ntok / c.num_seqs;
+    a.y_bf16 = c.y_bf16;
+    if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
+    if (nchunks > 0)
+        hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kThreads), 0, s, a);
+    const int nsl = c.dv / kSl;
+    const int pairs = c.num_seqs * c.H;
+    const int blocks = (pairs + 7) / 8 * 8 * nsl;
+    if (c.y_bf16)
+        hipLaunchKernelGGL(chunk_scan_kernel<uint16_t>, dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(chunk_scan_kernel<float>, dim3(blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

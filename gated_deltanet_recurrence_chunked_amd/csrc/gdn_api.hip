@@ -139,9 +139,14 @@ int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype, 
     return hip_status(gdn::launch_preprocess(a, static_cast<hipStream_t>(stream)), "gdn_preprocess");
 }
 
+// The bf16 path with dk = 128 runs on the matrix cores and keeps per-chunk T and P tiles
+// in the workspace; every other combination runs the all-fp32 kernel, which needs none.
+static bool use_matrix_path(int in_dtype, int dk) { return in_dtype == GDN_BF16 && dk == 128; }
+
 size_t gdn_chunk_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, int dv, int in_dtype) {
-    (void)ntok; (void)num_seqs; (void)H; (void)dk; (void)dv; (void)in_dtype;
-    return 0;
+    (void)dv;
+    if (ntok < 0 || num_seqs < 1 || H < 1) return 0;
+    return use_matrix_path(in_dtype, dk) ? gdn::chunk_bf16_workspace(ntok, num_seqs, H) : 0;
 }
 
 int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype, const float* g,
@@ -174,6 +179,8 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
     a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.dk = dk; a.dv = dv;
     a.y = y; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (use_matrix_path(in_dtype, dk))
+        return hip_status(gdn::launch_chunk_bf16(a, s), "gdn_chunk_prefill");
     return hip_status(gdn::launch_chunk_fp32(a, s), "gdn_chunk_prefill");
 }
 

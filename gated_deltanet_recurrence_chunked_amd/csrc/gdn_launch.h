@@ -43,4 +43,8 @@ struct ChunkArgs {
 // all-fp32 chunked path (vector ALU)
 hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t s);
 
+// bf16 matrix-core chunked path (dk = 128): per-chunk T/P kernel + sequential scan kernel
+size_t chunk_bf16_workspace(int ntok, int num_seqs, int H);
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s);
+
 }  // namespace gdn
