@@ -9,6 +9,8 @@
 //   R      = diag(beta) (V - diag(gamma) K S)             U = T R
 //   Y      = diag(gamma) Q S + P U
 //   S_next = gamma_C S + K^T diag(gamma_C / gamma) U
+// Operands that are not exact bf16 inputs (S, R, T, U, P) enter the MFMAs as hi + lo bf16
+// pairs (about 16 significant bits), so each such product costs two or three MFMAs.
 // T and P depend on the chunk's q, k, g, beta only, so they are produced for every chunk at
 // once by chunk_prep_kernel (massively parallel: KK^T and QK^T on MFMA, the 64x64 unit
 // lower-triangular inverse by fp32 forward substitution). chunk_scan_kernel then walks the
@@ -90,7 +92,7 @@ __device__ __forceinline__ void store_acc_t2(uint16_t* hi, uint16_t* lo, int str
 }
 
 struct Layout {
-    size_t cs, ord, T, P, Plo, total;
+    size_t cs, ord, T, Tlo, P, Plo, total;
     int max_chunks;
 };
 
@@ -104,6 +106,7 @@ __host__ __device__ inline Layout ws_layout(int ntok, int num_seqs, int H) {
     L.ord = o; o = align256(o + sizeof(int32_t) * num_seqs);
     const size_t tile = (size_t)kC * kC * sizeof(uint16_t);
     L.T = o;   o = align256(o + tile * L.max_chunks * H);
+    L.Tlo = o; o = align256(o + tile * L.max_chunks * H);
     L.P = o;   o = align256(o + tile * L.max_chunks * H);
     L.Plo = o; o = align256(o + tile * L.max_chunks * H);
     L.total = o;
@@ -118,7 +121,7 @@ struct DevArgs {
     const int32_t* cu;          // NULL: equal lengths
     int32_t* chunk_start;       // [num_seqs+1] (varlen)
     int32_t* order;             // [num_seqs] longest first (varlen)
-    uint16_t *Tw, *Pw, *Plw;    // [max_chunks][H][64][64]; P = Pw + Plw (hi + lo bf16)
+    uint16_t *Tw, *Tlw, *Pw, *Plw;  // [max_chunks][H][64][64]; T = Tw + Tlw, P = Pw + Plw (hi + lo)
     int num_seqs, ntok, H, dv, L;  // L: equal length (when cu == NULL)
     int y_bf16;
 };
@@ -298,7 +301,11 @@ __global__ void __launch_bounds__(kThreads) chunk_prep_kernel(DevArgs a) {
             t[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < kC; ++r) a.Tw[tile + r * kC + c] = f2bf(t[r]);
+        for (int r = 0; r < kC; ++r) {
+            const uint16_t th = f2bf(t[r]);
+            a.Tw[tile + r * kC + c] = th;
+            a.Tlw[tile + r * kC + c] = f2bf(t[r] - bf2f(th));
+        }
     }
 }
 
@@ -315,6 +322,7 @@ constexpr int kStrV = kSl + 8;
             const int idx = tid + kThreads * it;                                               \
             const size_t off = (TILE) + (idx >> 3) * kC + (idx & 7) * 8;                       \
             stt[it] = *reinterpret_cast<const u32x4*>(a.Tw + off);                             \
+            sttl[it] = *reinterpret_cast<const u32x4*>(a.Tlw + off);                           \
             stp[it] = *reinterpret_cast<const u32x4*>(a.Pw + off);                             \
             stpl[it] = *reinterpret_cast<const u32x4*>(a.Plw + off);                           \
         }                                                                                      \
@@ -329,6 +337,7 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kStrD];
     __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kStrD];
     __shared__ __attribute__((aligned(16))) uint16_t sT[kC * kStrC];
+    __shared__ __attribute__((aligned(16))) uint16_t sTl[kC * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sP[kC * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sPl[kC * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kStrV];
@@ -377,7 +386,7 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
     store_acc_t2(sSt, sStl, kStrD, 32 * wave, S, lane);
 
     const int nchunks = (hi - lo + kC - 1) / kC;
-    u32x4 stq[4], stk[4], stt[2], stp[2], stpl[2], stv;
+    u32x4 stq[4], stk[4], stt[2], sttl[2], stp[2], stpl[2], stv;
     float stg, stb;
     if (nchunks > 0) GDN_FETCH_STAGE(lo, min(kC, hi - lo), ((size_t)cbase * a.H + h) * kC * kC);
     for (int c = 0; c < nchunks; ++c) {
@@ -391,6 +400,7 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
             const int idx = tid + kThreads * it;
             const int o = (idx >> 3) * kStrC + (idx & 7) * 8;
             *reinterpret_cast<u32x4*>(sT + o) = stt[it];
+            *reinterpret_cast<u32x4*>(sTl + o) = sttl[it];
             *reinterpret_cast<u32x4*>(sP + o) = stp[it];
             *reinterpret_cast<u32x4*>(sPl + o) = stpl[it];
         }
@@ -435,19 +445,22 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
         }
         __syncthreads();
 
-        // ---- step 2: U = T R (T is unit lower triangular: rows 0-31 need k < 32 only)
+        // ---- step 2: U = T R (T is unit lower triangular: rows 0-31 need k < 32 only),
+        //      T = T_hi + T_lo, R = R_hi + R_lo (the lo x lo term is below fp32 rounding)
         if (wave >= 2) {
             const int r0 = 32 * (wave - 2);
             f32x16 u = {};
-            const uint16_t* Arow = sT + (r0 + col) * kStrC + kofs;
+            const uint16_t* Ah = sT + (r0 + col) * kStrC + kofs;
+            const uint16_t* Al = sTl + (r0 + col) * kStrC + kofs;
             const uint16_t* Bh = sRt + col * kStrC + kofs;
             const uint16_t* Bl = sRtl + col * kStrC + kofs;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 if (kk < 2 * (wave - 1)) {
-                    const bf16x8 af = frag(Arow + kk * 16);
-                    u = mfma(af, frag(Bh + kk * 16), u);
-                    u = mfma(af, frag(Bl + kk * 16), u);
+                    const bf16x8 ah = frag(Ah + kk * 16), bh = frag(Bh + kk * 16);
+                    u = mfma(ah, bh, u);
+                    u = mfma(ah, frag(Bl + kk * 16), u);
+                    u = mfma(frag(Al + kk * 16), bh, u);
                 }
             }
             store_acc_t2(sUt, sUtl, kStrC, r0, u, lane);
@@ -530,6 +543,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
     a.chunk_start = c.cu ? reinterpret_cast<int32_t*>(ws + L.cs) : nullptr;
     a.order = c.cu ? reinterpret_cast<int32_t*>(ws + L.ord) : nullptr;
     a.Tw = reinterpret_cast<uint16_t*>(ws + L.T);
+    a.Tlw = reinterpret_cast<uint16_t*>(ws + L.Tlo);
     a.Pw = reinterpret_cast<uint16_t*>(ws + L.P);
     a.Plw = reinterpret_cast<uint16_t*>(ws + L.Plo);
     a.num_seqs = c.num_seqs; a.ntok = c.ntok; a.H = c.H; a.dv = c.dv;

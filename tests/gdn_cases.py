@@ -20,6 +20,7 @@ RMS_EPS = 1e-6
 TOL_REL = {False: 1e-4, True: 5e-3}        # keyed by "bf16 path"
 TOL_ABS = 2e-2
 BF16_HALF_ULP_REL = 2.0 ** -8              # RNE rounding bound of a bf16-stored output
+BF16_ULP_REL = 2.0 ** -7                   # one bf16 ulp, relative (bottom of a binade)
 
 
 # ----------------------------------------------------------------------------- host <-> device
@@ -33,12 +34,6 @@ def dev(a: np.ndarray, bf16: bool = False):
 def host(t) -> np.ndarray:
     import torch
     return t.detach().to(torch.float64).cpu().numpy()
-
-
-def f64(inp, key):
-    sh = inp["shape"]
-    bf = inp[key].dtype == np.uint16
-    return gi.as_f64(inp[key], bf)
 
 
 # ----------------------------------------------------------------------------- metrics
@@ -64,11 +59,14 @@ def state_rel_errors(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def assert_close(name, got, ref, bf16_path, stored_bf16=False, cu=None, H=None, state=False,
-                 ref_elem=None):
+                 ref_elem=None, inherits_bf16_input=False):
     """The parity bar: max slice relative L2 <= TOL_REL; on the bf16 path also
     |got - ref| <= 2e-2 (+ the output's own bf16 rounding if it is stored in bf16).
     ref_elem, when given, is the reference of the elementwise check (the oracle with the
-    pipeline's bf16 storage of intermediates modelled)."""
+    pipeline's bf16 storage of intermediates modelled). inherits_bf16_input marks an output
+    whose elements scale a bf16-stored input elementwise (the output gate's o = c_j y_j):
+    both sides round their own y to bf16, and two roundings of slightly different values
+    can land one ulp apart, which o inherits as up to 2^-7 of |o|."""
     if state:
         errs = state_rel_errors(got, ref)
     else:
@@ -79,9 +77,17 @@ def assert_close(name, got, ref, bf16_path, stored_bf16=False, cu=None, H=None, 
     if bf16_path:
         r = ref if ref_elem is None else ref_elem
         bound = TOL_ABS + (BF16_HALF_ULP_REL * np.abs(r) if stored_bf16 else 0.0)
+        if inherits_bf16_input:
+            bound = bound + BF16_ULP_REL * np.abs(r)
         excess = np.abs(got - r) - bound
-        assert np.all(excess <= 0), (f"{name}: max |diff| {np.abs(got - r).max():.3e} "
-                                     f"exceeds elementwise bound")
+        if not np.all(excess <= 0):
+            i = np.unravel_index(np.argmax(excess), excess.shape)
+            row = r[i[:-1]] if r.ndim > 1 else r
+            raise AssertionError(
+                f"{name}: max |diff| {np.abs(got - r).max():.3e} exceeds the elementwise bound; "
+                f"worst at {tuple(int(x) for x in i)}: got {got[i]:.6g} ref {r[i]:.6g} "
+                f"bound {bound[i] if np.ndim(bound) else bound:.4g}; row rms {np.sqrt(np.mean(row * row)):.4g}, "
+                f"{int(np.sum(excess > 0))} elements over")
     return worst
 
 
@@ -99,10 +105,11 @@ def subset(inp: dict, seqs=None, heads=None) -> dict:
     out = dict(cu=new_cu, H=len(heads), tok=tok, seqs=seqs, heads=heads)
     for key in ("q", "k", "v", "xq", "xk", "xv", "z"):
         if key in inp:
-            out[key] = f64(inp, key)[tok][:, heads]
+            a = inp[key][tok][:, heads]          # slice first, widen the slice only
+            out[key] = gi.as_f64(a, a.dtype == np.uint16)
     for key in ("a_raw", "b_raw"):
         if key in inp:
-            out[key] = inp[key].astype(np.float64)[tok][:, heads]
+            out[key] = inp[key][tok][:, heads].astype(np.float64)
     for key in ("A_log", "dt_bias"):
         out[key] = inp[key].astype(np.float64)[heads]
     for key, d in (("wq", sh.dk), ("wk", sh.dk), ("wv", sh.dv)):

@@ -1,0 +1,100 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark
+uses (one call over the whole packed batch). The HIP path computes every output; the fp64
+oracle evaluates sampled (sequence, head) slices, which depend on nothing outside them."""
+import sys
+
+import numpy as np
+import pytest
+
+from gated_deltanet_recurrence_chunked_amd import inputs as gi
+import gdn_cases as C
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _announce(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _check_prefill(inp, res, seqs, heads, y_bf16):
+    sh = inp["shape"]
+    sub = C.subset(inp, seqs=seqs, heads=heads)
+    ref = C.oracle_run(sub)
+    tok, cu, H = sub["tok"], sub["cu"], sub["H"]
+    rep = {}
+    if sh.conv:
+        for key in ("q", "k", "v"):
+            rep[key] = C.assert_close(key, C.gpu_slice(res[key], tok, heads), ref[key], True,
+                                      stored_bf16=True, cu=cu, H=H)
+    for key in ("g", "beta"):
+        got = C.gpu_slice(res[key], tok, heads)
+        assert np.abs(got - ref[key]).max() / np.abs(ref[key]).max() < 1e-5, key
+    rep["y"] = C.assert_close("y", C.gpu_slice(res["y"], tok, heads), ref["y"], sh.bf16,
+                              stored_bf16=y_bf16, cu=cu, H=H)
+    rep["ST"] = C.assert_close("ST", C.gpu_state_slice(res["ST"], seqs, heads), ref["ST"], sh.bf16,
+                               state=True)
+    if "o" in res:
+        st = C.oracle_run(sub, storage_bf16=True, y_bf16=y_bf16)
+        rep["o"] = C.assert_close("o", C.gpu_slice(res["o"], tok, heads), ref["o"], True,
+                                  stored_bf16=True, cu=cu, H=H, ref_elem=st["o"], inherits_bf16_input=y_bf16)
+    print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in rep.items()}, flush=True)
+
+
+def test_config1_prefill_pipeline_full(gpu):
+    _announce("config 1 full: B=4 H=16 T=4096 d=128 bf16, preprocess + prefill + output gate")
+    inp = gi.make_inputs(1, seed=0)
+    res = C.gpu_run(inp, y_dtype="bf16")
+    _check_prefill(inp, res, seqs=[0, 3], heads=[0, 9, 15], y_bf16=True)
+
+
+def test_config2_long_context_full(gpu):
+    _announce("config 2 full: B=1 H=32 T=65536 d=128 bf16, S0 ~ N(0, 0.01)")
+    inp = gi.make_inputs(2, seed=0)
+    res = C.gpu_run(inp, y_dtype="bf16")
+    _check_prefill(inp, res, seqs=[0], heads=[0, 17, 31], y_bf16=True)
+
+
+def test_config4_varlen_full(gpu):
+    _announce("config 4 full: 64 packed sequences, log-uniform lengths [128, 32768], H=16")
+    inp = gi.make_inputs(4, seed=0)
+    L = np.diff(inp["cu_seqlens"])
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 5, 40})
+    res = C.gpu_run(inp, y_dtype="bf16")
+    _check_prefill(inp, res, seqs=seqs, heads=[0, 11], y_bf16=True)
+
+
+def test_config3_decode_100_steps_full(gpu):
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    _announce("config 3 full: decode N=256 H=32 d=128, 100 steps, fp32 state in place")
+    inp = gi.make_inputs(3, seed=0)
+    sh = inp["shape"]
+    S_, N, H = sh.steps, sh.num_seqs, sh.H
+    state = C.dev(inp["state"])
+    f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))  # noqa: E731
+    _, _, _, g, beta = gdn.gdn_preprocess(None, None, None, None, None, None,
+                                          f32(inp["a_raw"].reshape(S_ * N, H)),
+                                          f32(inp["b_raw"].reshape(S_ * N, H)),
+                                          f32(inp["A_log"]), f32(inp["dt_bias"]), H=H)
+    g = g.view(S_, N, H)
+    beta = beta.view(S_, N, H)
+    q, k, v = C.dev(inp["q"], True), C.dev(inp["k"], True), C.dev(inp["v"], True)
+    y = torch.empty((S_, N, H, sh.dv), dtype=torch.bfloat16, device="cuda")
+    for s in range(S_):
+        gdn.gdn_decode_step(q[s], k[s], v[s], g[s], beta[s], state, y=y[s])
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (17, 5), (100, 31), (255, 12), (128, 16)]
+    for n, h in pairs:
+        qq = gi.as_f64(inp["q"][:, n, h], True)[:, None, :]
+        kk = gi.as_f64(inp["k"][:, n, h], True)[:, None, :]
+        vv = gi.as_f64(inp["v"][:, n, h], True)[:, None, :]
+        _, al, be = C.oracle.gates(inp["a_raw"][:, n, h:h + 1].astype(np.float64),
+                                   inp["b_raw"][:, n, h:h + 1].astype(np.float64),
+                                   inp["A_log"][h:h + 1].astype(np.float64),
+                                   inp["dt_bias"][h:h + 1].astype(np.float64))
+        y_ref, S_ref = C.oracle.recurrence(qq, kk, vv, al, be,
+                                           inp["state"][n:n + 1, h:h + 1].astype(np.float64))
+        y_got = C.host(y[:, n, h])[:, None, :]
+        C.assert_close(f"y[{n},{h}]", y_got, y_ref, True, stored_bf16=True, cu=[0, S_], H=1)
+        C.assert_close(f"S[{n},{h}]", C.host(state[n:n + 1, h:h + 1]), S_ref, True, state=True)

@@ -41,7 +41,8 @@ def _compare_prefill(inp, res, ref, sub, y_bf16, ref_st=None):
         # the elementwise check therefore models that storage in the oracle.
         report["o"] = C.assert_close("o", C.gpu_slice(res["o"], tok, heads), ref["o"], True,
                                      stored_bf16=True, cu=cu, H=H,
-                                     ref_elem=None if ref_st is None else ref_st["o"])
+                                     ref_elem=None if ref_st is None else ref_st["o"],
+                                     inherits_bf16_input=y_bf16)
     print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in report.items()}, flush=True)
 
 
