@@ -75,17 +75,14 @@ __device__ __forceinline__ void store_acc_t2(uint16_t* hi, uint16_t* lo, int str
     const int off = (lane & 31) * stride + row0 + 4 * (lane >> 5);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        float h[4], l[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            h[e] = bf2f(f2bf(c[4 * q + e]));
-            l[e] = c[4 * q + e] - h[e];
-        }
         u32x2 vh, vl;
-        vh.x = pack_bf2(h[0], h[1]);
-        vh.y = pack_bf2(h[2], h[3]);
-        vl.x = pack_bf2(l[0], l[1]);
-        vl.y = pack_bf2(l[2], l[3]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float x0 = c[4 * q + 2 * e], x1 = c[4 * q + 2 * e + 1];
+            const uint32_t hp = pack_bf2(x0, x1);   // one v_cvt_pk_bf16_f32
+            vh[e] = hp;
+            vl[e] = pack_bf2(x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xffff0000u));
+        }
         *reinterpret_cast<u32x2*>(hi + off + 8 * q) = vh;
         *reinterpret_cast<u32x2*>(lo + off + 8 * q) = vl;
     }
@@ -166,16 +163,26 @@ __global__ void __launch_bounds__(kThreads) chunk_table_kernel(DevArgs a) {
 // Rows [0, 64) of one chunk of a [ntok, H, 128] bf16 tensor: 256 threads x 4 x 16 bytes,
 // fetched into registers (all loads in flight together; rows >= n read row n-1 and are
 // zeroed when written to LDS, so no load sits behind a branch).
+// The chunk's base address is wave-uniform (scalar registers); a lane adds a 32-bit offset.
 __device__ __forceinline__ void fetch_rows128(u32x4 (&R)[4], const uint16_t* src, int t0, int n,
                                               int H, int h) {
+    const uint16_t* base = src + ((size_t)t0 * H + h) * kDK;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int idx = threadIdx.x + kThreads * it;
         const int r = min(idx >> 4, n - 1), d0 = (idx & 15) * 8;
-        R[it] = *reinterpret_cast<const u32x4*>(src + ((size_t)(t0 + r) * H + h) * kDK + d0);
+        R[it] = *reinterpret_cast<const u32x4*>(base + (r * H * kDK + d0));
     }
 }
 __device__ __forceinline__ void put_rows128(uint16_t* dst, const u32x4 (&R)[4], int n) {
+    if (n == kC) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = threadIdx.x + kThreads * it;
+            *reinterpret_cast<u32x4*>(dst + (idx >> 4) * kStrD + (idx & 15) * 8) = R[it];
+        }
+        return;
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int idx = threadIdx.x + kThreads * it;
@@ -189,8 +196,9 @@ __device__ __forceinline__ void put_rows128(uint16_t* dst, const u32x4 (&R)[4], 
 __device__ __forceinline__ void fetch_gates(const DevArgs& a, int t0, int n, int h, float& gv,
                                             float& bv) {
     const int r = min((int)(threadIdx.x & (kWave - 1)), n - 1);
-    gv = a.g[(size_t)(t0 + r) * a.H + h];
-    bv = a.beta[(size_t)(t0 + r) * a.H + h];
+    const size_t base = (size_t)t0 * a.H + h;
+    gv = a.g[base + r * a.H];
+    bv = a.beta[base + r * a.H];
 }
 
 // Wave 0: running sum of g over the chunk (rows >= n contribute 0), written with beta.
@@ -209,8 +217,8 @@ __device__ __forceinline__ void chunk_gates(float gv, float bv, int n, float* sG
     const float gC = __shfl(gv, kC - 1, kWave);
     sG[lane] = gv;
     sB[lane] = bv;
-    if (sGam) sGam[lane] = expf(gv);
-    if (sGd) sGd[lane] = expf(gC - gv);
+    if (sGam) sGam[lane] = fexp(gv);
+    if (sGd) sGd[lane] = fexp(gC - gv);
 }
 
 // chunk index -> (sequence, first token, length)
@@ -239,73 +247,135 @@ __device__ __forceinline__ bool chunk_of(const DevArgs& a, int chunk, int& seq, 
 }
 
 // ------------------------------------------------------------------ per-chunk T and P
-__global__ void __launch_bounds__(kThreads) chunk_prep_kernel(DevArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kStrD];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kStrD];
+// One wave per (chunk, head). The MFMA operands of K K^T and Q K^T are read from global
+// memory straight into registers in fragment layout (a lane's 8 consecutive d_k of one row
+// are one 16-byte load), so only the fp32 A matrix lives in LDS and eight chunk-heads share
+// a CU: while one wave waits on its loads or on the forward substitution (a lane per column
+// of T), the other wave on its SIMD issues.
+constexpr int kPrepThreads = kWave;
+
+__global__ void __launch_bounds__(kPrepThreads) chunk_prep_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
     __shared__ float sG[kC], sB[kC];
 
     const int chunk = blockIdx.x, h = blockIdx.y;
     int seq, t0, n;
     if (!chunk_of(a, chunk, seq, t0, n)) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x;
 
-    u32x4 rk[4], rq[4];
-    fetch_rows128(rk, a.k, t0, n, a.H, h);
-    fetch_rows128(rq, a.q, t0, n, a.H, h);
+    // fragment rows (lane % 32) and (32 + lane % 32); rows >= n are zero
+    const int r0 = lane & 31, r1 = 32 + (lane & 31);
+    const uint16_t* k0p = a.k + ((size_t)(t0 + min(r0, n - 1)) * a.H + h) * kDK + (lane >> 5) * 8;
+    const uint16_t* k1p = a.k + ((size_t)(t0 + min(r1, n - 1)) * a.H + h) * kDK + (lane >> 5) * 8;
+    const uint16_t* q0p = a.q + ((size_t)(t0 + min(r0, n - 1)) * a.H + h) * kDK + (lane >> 5) * 8;
+    const uint16_t* q1p = a.q + ((size_t)(t0 + min(r1, n - 1)) * a.H + h) * kDK + (lane >> 5) * 8;
+    u32x4 fk0[8], fk1[8], fq0[8], fq1[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        fk0[kk] = *reinterpret_cast<const u32x4*>(k0p + kk * 16);
+        fk1[kk] = *reinterpret_cast<const u32x4*>(k1p + kk * 16);
+        fq0[kk] = *reinterpret_cast<const u32x4*>(q0p + kk * 16);
+        fq1[kk] = *reinterpret_cast<const u32x4*>(q1p + kk * 16);
+    }
     float gv, bv;
     fetch_gates(a, t0, n, h, gv, bv);
-    put_rows128(sK, rk, n);
-    put_rows128(sQ, rq, n);
-    if (wave == 0) chunk_gates(gv, bv, n, sG, sB, nullptr, nullptr);
-    __syncthreads();
+    chunk_gates(gv, bv, n, sG, sB, nullptr, nullptr);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool v0 = r0 < n, v1 = r1 < n;
+
+    // lower tiles of K K^T and Q K^T: (rows 0-31, cols 0-31), (32-63, 0-31), (32-63, 32-63)
+    f32x16 ckk[3], cqk[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        ckk[t] = f32x16{};
+        cqk[t] = f32x16{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < kDK / 16; ++kk) {
+        const bf16x8 k0 = __builtin_bit_cast(bf16x8, v0 ? fk0[kk] : z);
+        const bf16x8 k1 = __builtin_bit_cast(bf16x8, v1 ? fk1[kk] : z);
+        const bf16x8 q0 = __builtin_bit_cast(bf16x8, v0 ? fq0[kk] : z);
+        const bf16x8 q1 = __builtin_bit_cast(bf16x8, v1 ? fq1[kk] : z);
+        ckk[0] = mfma(k0, k0, ckk[0]);
+        ckk[1] = mfma(k1, k0, ckk[1]);
+        ckk[2] = mfma(k1, k1, ckk[2]);
+        cqk[0] = mfma(q0, k0, cqk[0]);
+        cqk[1] = mfma(q1, k0, cqk[1]);
+        cqk[2] = mfma(q1, k1, cqk[2]);
+    }
+    __syncthreads();   // gates visible
 
     const size_t tile = ((size_t)chunk * a.H + h) * kC * kC;
-    if (wave < 3) {
-        // wave 0: rows 0-31 x cols 0-31; wave 1: rows 32-63 x cols 0-31; wave 2: rows 32-63 x cols 32-63
-        const int R0 = wave == 0 ? 0 : 32, C0 = wave == 2 ? 32 : 0;
-        f32x16 ckk = {}, cqk = {};
 #pragma unroll
-        for (int kk = 0; kk < kDK / 16; ++kk) {
-            const int ko = kk * 16 + (lane >> 5) * 8;
-            const bf16x8 b = frag(sK + (C0 + (lane & 31)) * kStrD + ko);
-            const bf16x8 ak = frag(sK + (R0 + (lane & 31)) * kStrD + ko);
-            const bf16x8 aq = frag(sQ + (R0 + (lane & 31)) * kStrD + ko);
-            ckk = mfma(ak, b, ckk);
-            cqk = mfma(aq, b, cqk);
-        }
+    for (int t = 0; t < 3; ++t) {
+        const int R0 = t == 0 ? 0 : 32, C0 = t == 2 ? 32 : 0;
         const int c = C0 + (lane & 31);
         const float Gc = sG[c];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = R0 + acc_row(i, lane);
-            const float dec = c <= r ? expf(sG[r] - Gc) : 0.f;
-            sA[r * kStrA + c] = c < r ? sB[r] * dec * ckk[i] : 0.f;
-            const float p = dec * cqk[i];
+            const float dec = c <= r ? fexp(sG[r] - Gc) : 0.f;
+            sA[r * kStrA + c] = c < r ? sB[r] * dec * ckk[t][i] : 0.f;
+            const float p = dec * cqk[t][i];
             const uint16_t ph = f2bf(p);
             a.Pw[tile + r * kC + c] = ph;
             a.Plw[tile + r * kC + c] = f2bf(p - bf2f(ph));
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        // T = (I + A)^{-1}: lane = column, forward substitution over the rows
-        const int c = lane;
-        float t[kC];
+    // T = (I + A)^{-1} in 32x32 blocks: T = [[T0, 0], [T10, T1]] with T0 = (I + A00)^{-1},
+    // T1 = (I + A11)^{-1}, T10 = -T1 A10 T0.
+    // (1) the two diagonal inverses by forward substitution, one half-wave each, a lane per
+    //     column (4 partial sums per row);
+    const int half = lane >> 5, c = lane & 31, off = 32 * half;
+    float t[32];
 #pragma unroll
-        for (int r = 0; r < kC; ++r) {
-            float acc = r == c ? 1.f : 0.f;
-            const float* Ar = sA + r * kStrA;
+    for (int r = 0; r < 32; ++r) {
+        const float* Ar = sA + (off + r) * kStrA + off;
+        float acc[4] = {r == c ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < r; ++i) acc -= Ar[i] * t[i];
-            t[r] = acc;
-        }
+        for (int i = 0; i < r; ++i) acc[i & 3] -= Ar[i] * t[i];
+        t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+    __syncthreads();   // all reads of A00 and A11 done: T0 and T1 take their place
 #pragma unroll
-        for (int r = 0; r < kC; ++r) {
-            const uint16_t th = f2bf(t[r]);
-            a.Tw[tile + r * kC + c] = th;
-            a.Tlw[tile + r * kC + c] = f2bf(t[r] - bf2f(th));
-        }
+    for (int r = 0; r < 32; ++r) sA[(off + r) * kStrA + off + c] = t[r];
+    __syncthreads();
+    // (2) X = A10 T0 and T10 = -T1 X on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: lane l
+    //     supplies A[l%32][l/32] and B[l/32][l%32] of each k-pair); X goes through the unused
+    //     upper-right block of the tile.
+    f32x16 X = {};
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+        const int k = 2 * s2 + half;
+        X = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(32 + c) * kStrA + k], sA[k * kStrA + c], X, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sA[acc_row(i, lane) * kStrA + 32 + c] = X[i];
+    __syncthreads();
+    f32x16 T10 = {};
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+        const int k = 2 * s2 + half;
+        T10 = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(32 + c) * kStrA + 32 + k], sA[k * kStrA + 32 + c],
+                                                  T10, 0, 0, 0);
+    }
+    // (3) T as hi + lo bf16: diagonal blocks from the lanes' columns, T10 from the
+    //     accumulators (the upper-right block is never read and is left unwritten)
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        const size_t o = tile + (off + r) * kC + off + c;
+        const uint16_t th = f2bf(t[r]);
+        a.Tw[o] = th;
+        a.Tlw[o] = f2bf(t[r] - bf2f(th));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const size_t o = tile + (32 + acc_row(i, lane)) * kC + c;
+        const float v = -T10[i];
+        const uint16_t th = f2bf(v);
+        a.Tw[o] = th;
+        a.Tlw[o] = f2bf(v - bf2f(th));
     }
 }
 
@@ -319,16 +389,15 @@ constexpr int kStrV = kSl + 8;
         fetch_rows128(stq, a.q, (T0), (N), a.H, h);                                            \
         fetch_rows128(stk, a.k, (T0), (N), a.H, h);                                            \
         _Pragma("unroll") for (int it = 0; it < 2; ++it) {                                     \
-            const int idx = tid + kThreads * it;                                               \
-            const size_t off = (TILE) + (idx >> 3) * kC + (idx & 7) * 8;                       \
-            stt[it] = *reinterpret_cast<const u32x4*>(a.Tw + off);                             \
-            sttl[it] = *reinterpret_cast<const u32x4*>(a.Tlw + off);                           \
-            stp[it] = *reinterpret_cast<const u32x4*>(a.Pw + off);                             \
-            stpl[it] = *reinterpret_cast<const u32x4*>(a.Plw + off);                           \
+            const int off = tid * 8 + kThreads * 8 * it;   /* = row * 64 + col */              \
+            stt[it] = *reinterpret_cast<const u32x4*>(a.Tw + (TILE) + off);                    \
+            sttl[it] = *reinterpret_cast<const u32x4*>(a.Tlw + (TILE) + off);                  \
+            stp[it] = *reinterpret_cast<const u32x4*>(a.Pw + (TILE) + off);                    \
+            stpl[it] = *reinterpret_cast<const u32x4*>(a.Plw + (TILE) + off);                  \
         }                                                                                      \
         const int vr = min(tid >> 2, (N) - 1);                                                 \
-        stv = *reinterpret_cast<const u32x4*>(a.v + ((size_t)((T0) + vr) * a.H + h) * a.dv +  \
-                                              j0 + (tid & 3) * 8);                             \
+        stv = *reinterpret_cast<const u32x4*>(a.v + ((size_t)(T0) * a.H + h) * a.dv + j0 +    \
+                                              (vr * a.H * a.dv + (tid & 3) * 8));              \
         fetch_gates(a, (T0), (N), h, stg, stb);                                                \
     } while (0)
 
@@ -349,6 +418,8 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sUtl[kSl * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sUht[kSl * kStrC];   // (diag(gamma_C/gamma) U)^T
     __shared__ __attribute__((aligned(16))) uint16_t sUhtl[kSl * kStrC];
+    constexpr int kStrY = sizeof(Ty) == 2 ? kSl + 8 : kSl + 4;          // 16-byte aligned rows
+    __shared__ __attribute__((aligned(16))) Ty sY[kC * kStrY];            // the chunk's y slice
     __shared__ float sG[kC], sB[kC], sGam[kC], sGd[kC];
 
     // block -> (pair, slice): the slices of one pair are 8 blocks apart, so the same XCD
@@ -407,7 +478,7 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
         {
             const int r = tid >> 2;
             const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(sV + r * kStrV + (tid & 3) * 8) = r < n ? stv : z;
+            *reinterpret_cast<u32x4*>(sV + r * kStrV + (tid & 3) * 8) = (n == kC || r < n) ? stv : z;
         }
         if (wave == 0) chunk_gates(stg, stb, n, sG, sB, sGam, sGd);
         __syncthreads();
@@ -485,12 +556,8 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
                     acc = mfma(frag(Al + kk * 16), bh, acc);
                 }
             }
-            Ty* y = static_cast<Ty*>(a.y);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 32 * wave + acc_row(i, lane);
-                if (r < n) store1(y + ((size_t)(t0 + r) * a.H + h) * a.dv + j0 + col, acc[i]);
-            }
+            for (int i = 0; i < 16; ++i) store1(sY + (32 * wave + acc_row(i, lane)) * kStrY + col, acc[i]);
         }
         // ---- step 3b: S = gamma_C S + K^T Uh  (rows 32 wave.. of S; K^T fragments read
         //      column-wise from the row-major K tile)
@@ -514,6 +581,19 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
             store_acc_t2(sSt, sStl, kStrD, 32 * wave, S, lane);
         }
         __syncthreads();
+        // ---- the chunk's y slice: 16-byte stores of whole rows
+        {
+            constexpr int kPer = 8 / sizeof(Ty) * 2;          // elements per 16 bytes
+            constexpr int kRowPieces = kSl / kPer;
+#pragma unroll
+            for (int it = 0; it < kC * kRowPieces / kThreads; ++it) {
+                const int idx = tid + kThreads * it;
+                const int r = idx / kRowPieces, c0 = (idx % kRowPieces) * kPer;
+                if (r < n)
+                    *reinterpret_cast<u32x4*>(static_cast<Ty*>(a.y) + ((size_t)(t0 + r) * a.H + h) * a.dv +
+                                              j0 + c0) = *reinterpret_cast<const u32x4*>(sY + r * kStrY + c0);
+            }
+        }
     }
     if (a.ST) {
 #pragma unroll
@@ -552,7 +632,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
     if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
     if (nchunks > 0)
-        hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
     const int nsl = c.dv / kSl;
     const int pairs = c.num_seqs * c.H;
     const int blocks = (pairs + 7) / 8 * 8 * nsl;

@@ -104,8 +104,17 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// --------------------------------------------------------------------------- fast math
+// Single hardware instructions (v_exp_f32, v_rcp_f32, v_rsq_f32), each within about one ulp
+// in the range these kernels use; the accurate library forms cost ~10-25 instructions each
+// and made the streaming kernels VALU-bound.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float frsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
 // --------------------------------------------------------------------------- gate math
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float sigmoidf_(float x) { return frcp(1.0f + fexp(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x * frcp(1.0f + fexp(-x)); }
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}): no overflow, no cancellation
 __device__ __forceinline__ float softplusf_(float x) {

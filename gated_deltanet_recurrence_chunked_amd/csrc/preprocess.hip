@@ -18,6 +18,7 @@ constexpr int kPreThreads = 256;
 constexpr int kPreTile = kPreThreads * 8;   // channels per workgroup
 constexpr int kPreTokens = 32;              // tokens per workgroup (3-token conv halo)
 constexpr int kConvK = 4;
+constexpr int kPreGroup = 4;                // tokens loaded together
 
 struct PreKernelArgs {
     PreprocessArgs a;
@@ -82,43 +83,51 @@ __device__ void conv_stream(const PreprocessArgs& a, int role, int tile, int t0)
         }
     }
 
-    for (int t = t0; t < t1; ++t) {
-        if (t >= seq_hi) {   // crossed into the next non-empty sequence: history restarts
-            if (a.cu) {
-                while (a.cu[s + 1] <= t) ++s;
-                seq_hi = a.cu[s + 1];
-            } else {
-                seq_hi += a.ntok / a.num_seqs;
+    // four tokens per step: their loads are issued together, so each thread keeps four
+    // 16-byte requests in flight (the window recurrence runs on registers afterwards)
+    for (int tb = t0; tb < t1; tb += kPreGroup) {
+        float grp[kPreGroup][8];
+#pragma unroll
+        for (int j = 0; j < kPreGroup; ++j) Vec8<Tin>::load(x + (size_t)min(tb + j, t1 - 1) * C + c, grp[j]);
+#pragma unroll
+        for (int j = 0; j < kPreGroup; ++j) {
+            const int t = tb + j;
+            if (t >= t1) break;
+            if (t >= seq_hi) {   // crossed into the next non-empty sequence: history restarts
+                if (a.cu) {
+                    while (a.cu[s + 1] <= t) ++s;
+                    seq_hi = a.cu[s + 1];
+                } else {
+                    seq_hi += a.ntok / a.num_seqs;
+                }
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) win[q][i] = 0.f;
             }
+            float act[8];
+            float ss = 0.f;
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+            for (int i = 0; i < 8; ++i) {
+                float u = w[i][0] * win[0][i] + w[i][1] * win[1][i] + w[i][2] * win[2][i] +
+                          w[i][3] * grp[j][i];
+                float sv = siluf_(u);
+                act[i] = sv;
+                ss += sv * sv;
+            }
+            if (norm) {
+                ss = (d == 128) ? group_sum<16>(ss) : group_sum<8>(ss);
+                const float inv = frsq(ss + a.l2_eps);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) win[j][i] = 0.f;
-        }
-        float cur[8];
-        Vec8<Tin>::load(x + (size_t)t * C + c, cur);
-        float act[8];
-        float ss = 0.f;
+                for (int i = 0; i < 8; ++i) act[i] *= inv;
+            }
+            Vec8<Tout>::store(out + (size_t)t * C + c, act);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float u = w[i][0] * win[0][i] + w[i][1] * win[1][i] + w[i][2] * win[2][i] +
-                      w[i][3] * cur[i];
-            float sv = u / (1.0f + expf(-u));   // SiLU
-            act[i] = sv;
-            ss += sv * sv;
-        }
-        if (norm) {
-            ss = (d == 128) ? group_sum<16>(ss) : group_sum<8>(ss);
-            const float inv = 1.0f / sqrtf(ss + a.l2_eps);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) act[i] *= inv;
-        }
-        Vec8<Tout>::store(out + (size_t)t * C + c, act);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            win[0][i] = win[1][i];
-            win[1][i] = win[2][i];
-            win[2][i] = cur[i];
+            for (int i = 0; i < 8; ++i) {
+                win[0][i] = win[1][i];
+                win[1][i] = win[2][i];
+                win[2][i] = grp[j][i];
+            }
         }
     }
 }
@@ -184,20 +193,29 @@ output_gate_kernel(const Ty* __restrict__ y, const Tz* __restrict__ z, const flo
     float gain[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) gain[i] = 1.0f + w[lane_c + i];
-    for (long r = (long)blockIdx.x * RPB + threadIdx.x / LPR; r < rows; r += (long)gridDim.x * RPB) {
-        const size_t off = (size_t)r * DV + lane_c;
-        float yv[8], zv[8];
-        Vec8<Ty>::load(y + off, yv);
-        Vec8<Tz>::load(z + off, zv);
-        float ss = 0.f;
+    // two row groups per step, so four 16-byte loads per thread are in flight together
+    const long stride = (long)gridDim.x * RPB;
+    for (long r0 = (long)blockIdx.x * RPB + threadIdx.x / LPR; r0 < rows; r0 += 2 * stride) {
+        const long r1 = r0 + stride;
+        const size_t off0 = (size_t)r0 * DV + lane_c;
+        const size_t off1 = (size_t)(r1 < rows ? r1 : r0) * DV + lane_c;
+        float yv[2][8], zv[2][8];
+        Vec8<Ty>::load(y + off0, yv[0]);
+        Vec8<Tz>::load(z + off0, zv[0]);
+        Vec8<Ty>::load(y + off1, yv[1]);
+        Vec8<Tz>::load(z + off1, zv[1]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss += yv[i] * yv[i];
-        ss = group_sum<LPR>(ss);
-        const float inv = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
-        float ov[8];
+        for (int u = 0; u < 2; ++u) {
+            float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ov[i] = sigmoidf_(zv[i]) * (gain[i] * (yv[i] * inv));
-        Vec8<To>::store(o + off, ov);
+            for (int i = 0; i < 8; ++i) ss += yv[u][i] * yv[u][i];
+            ss = group_sum<LPR>(ss);
+            const float inv = frsq(ss * (1.0f / DV) + eps);
+            float ov[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ov[i] = sigmoidf_(zv[u][i]) * (gain[i] * (yv[u][i] * inv));
+            if (u == 0 || r1 < rows) Vec8<To>::store(o + (u ? off1 : off0), ov);
+        }
     }
 }
 
