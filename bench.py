@@ -154,9 +154,18 @@ def main():
         "gdn_output_gate": dict(us=t_og * 1e3, GBs=og_bytes / (t_og * 1e-3) / 1e9),
     }
     pf_gbs = pf_bytes / (t_pf * 1e-3) / 1e9
-    roofline = {"kernel": "gdn_chunk_prefill", "bound": "hbm", "achieved": round(pf_gbs, 1),
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic_gdn_chunk_prefill_B4_H16_T4096_d128.json")
+    if os.path.exists(tpath):
+        from gated_deltanet_recurrence_chunked_amd import rocprof_summary
+        with open(tpath) as f:
+            rec = json.load(f)
+        if rec.get("kernel_source_sha256") == rocprof_summary.prefill_source_sha():
+            traffic = int(rec["gdn_chunk_prefill_bytes_per_call"])
+    roofline = {"kernel": "gdn_chunk_prefill (chunk_prep_kernel + chunk_scan_kernel)",
+                "bound": "hbm", "achieved": round(pf_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pf_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": traffic,
                 "algorithmic_bytes_per_launch": pf_bytes,
                 "mfma": {"achieved_TFLOPs": round(pf_flops / (t_pf * 1e-3) / 1e12, 1),
                          "peak_TFLOPs": BF16_PEAK_TFLOPS,

@@ -254,7 +254,7 @@ __device__ __forceinline__ bool chunk_of(const DevArgs& a, int chunk, int& seq, 
 // of T), the other wave on its SIMD issues.
 constexpr int kPrepThreads = kWave;
 
-__global__ void __launch_bounds__(kPrepThreads) chunk_prep_kernel(DevArgs a) {
+__global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
     __shared__ float sG[kC], sB[kC];
 
@@ -316,10 +316,7 @@ __global__ void __launch_bounds__(kPrepThreads) chunk_prep_kernel(DevArgs a) {
             const int r = R0 + acc_row(i, lane);
             const float dec = c <= r ? fexp(sG[r] - Gc) : 0.f;
             sA[r * kStrA + c] = c < r ? sB[r] * dec * ckk[t][i] : 0.f;
-            const float p = dec * cqk[t][i];
-            const uint16_t ph = f2bf(p);
-            a.Pw[tile + r * kC + c] = ph;
-            a.Plw[tile + r * kC + c] = f2bf(p - bf2f(ph));
+            cqk[t][i] *= dec;   // P, written out after T
         }
     }
     __syncthreads();
@@ -360,23 +357,43 @@ __global__ void __launch_bounds__(kPrepThreads) chunk_prep_kernel(DevArgs a) {
         T10 = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(32 + c) * kStrA + 32 + k], sA[k * kStrA + 32 + c],
                                                   T10, 0, 0, 0);
     }
-    // (3) T as hi + lo bf16: diagonal blocks from the lanes' columns, T10 from the
-    //     accumulators (the upper-right block is never read and is left unwritten)
+    // (3) T and P as hi + lo bf16 tiles, assembled in LDS (the A matrix is dead now) and
+    //     written as whole 128-byte rows. T's upper-right block is never read; it is zero.
+    __syncthreads();
+    uint16_t* sH = reinterpret_cast<uint16_t*>(sA);   // [64][64] hi
+    uint16_t* sL = sH + kC * kC;                      // [64][64] lo
+    auto put = [&](int r, int cc, float v) {
+        const uint16_t hb = f2bf(v);
+        sH[r * kC + cc] = hb;
+        sL[r * kC + cc] = f2bf(v - bf2f(hb));
+    };
+    auto flush = [&](uint16_t* dh, uint16_t* dl) {
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kC * kC / 8 / kWave; ++it) {
+            const int e = (lane + kWave * it) * 8;
+            *reinterpret_cast<u32x4*>(dh + tile + e) = *reinterpret_cast<const u32x4*>(sH + e);
+            *reinterpret_cast<u32x4*>(dl + tile + e) = *reinterpret_cast<const u32x4*>(sL + e);
+        }
+        __syncthreads();
+    };
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-        const size_t o = tile + (off + r) * kC + off + c;
-        const uint16_t th = f2bf(t[r]);
-        a.Tw[o] = th;
-        a.Tlw[o] = f2bf(t[r] - bf2f(th));
+        put(off + r, off + c, t[r]);
+        put(r, 32 + c, 0.f);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const size_t o = tile + (32 + acc_row(i, lane)) * kC + c;
-        const float v = -T10[i];
-        const uint16_t th = f2bf(v);
-        a.Tw[o] = th;
-        a.Tlw[o] = f2bf(v - bf2f(th));
+    for (int i = 0; i < 16; ++i) put(32 + acc_row(i, lane), c, -T10[i]);
+    flush(a.Tw, a.Tlw);
+#pragma unroll
+    for (int tt = 0; tt < 3; ++tt) {
+        const int R0 = tt == 0 ? 0 : 32, C0 = tt == 2 ? 32 : 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) put(R0 + acc_row(i, lane), C0 + c, cqk[tt][i]);
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) put(acc_row(i, lane), 32 + c, 0.f);
+    flush(a.Pw, a.Plw);
 }
 
 // ------------------------------------------------------------------ sequential chunk scan
