@@ -9,8 +9,8 @@
 //   R      = diag(beta) (V - diag(gamma) K S)             U = T R
 //   Y      = diag(gamma) Q S + P U
 //   S_next = gamma_C S + K^T diag(gamma_C / gamma) U
-// Operands that are not exact bf16 inputs (S, R, T, U, P) enter the MFMAs as hi + lo bf16
-// pairs (about 16 significant bits), so each such product costs two or three MFMAs.
+// The state-side operands S, R and U enter the MFMAs as hi + lo bf16 pairs (about 16
+// significant bits: two MFMAs per product); the chunk-local T and P are single bf16.
 // T and P depend on the chunk's q, k, g, beta only, so they are produced for every chunk at
 // once by chunk_prep_kernel (massively parallel: KK^T and QK^T on MFMA, the 64x64 unit
 // lower-triangular inverse by fp32 forward substitution). chunk_scan_kernel then walks the
@@ -89,7 +89,7 @@ __device__ __forceinline__ void store_acc_t2(uint16_t* hi, uint16_t* lo, int str
 }
 
 struct Layout {
-    size_t cs, ord, T, Tlo, P, Plo, total;
+    size_t cs, ord, T, P, total;
     int max_chunks;
 };
 
@@ -103,9 +103,7 @@ __host__ __device__ inline Layout ws_layout(int ntok, int num_seqs, int H) {
     L.ord = o; o = align256(o + sizeof(int32_t) * num_seqs);
     const size_t tile = (size_t)kC * kC * sizeof(uint16_t);
     L.T = o;   o = align256(o + tile * L.max_chunks * H);
-    L.Tlo = o; o = align256(o + tile * L.max_chunks * H);
     L.P = o;   o = align256(o + tile * L.max_chunks * H);
-    L.Plo = o; o = align256(o + tile * L.max_chunks * H);
     L.total = o;
     return L;
 }
@@ -118,7 +116,7 @@ struct DevArgs {
     const int32_t* cu;          // NULL: equal lengths
     int32_t* chunk_start;       // [num_seqs+1] (varlen)
     int32_t* order;             // [num_seqs] longest first (varlen)
-    uint16_t *Tw, *Tlw, *Pw, *Plw;  // [max_chunks][H][64][64]; T = Tw + Tlw, P = Pw + Plw (hi + lo)
+    uint16_t *Tw, *Pw;          // [max_chunks][H][64][64] bf16
     int num_seqs, ntok, H, dv, L;  // L: equal length (when cu == NULL)
     int y_bf16;
 };
@@ -357,23 +355,17 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
         T10 = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(32 + c) * kStrA + 32 + k], sA[k * kStrA + 32 + c],
                                                   T10, 0, 0, 0);
     }
-    // (3) T and P as hi + lo bf16 tiles, assembled in LDS (the A matrix is dead now) and
-    //     written as whole 128-byte rows. T's upper-right block is never read; it is zero.
+    // (3) T and P as bf16 tiles, assembled in LDS (the A matrix is dead now) and written as
+    //     whole 128-byte rows. T's upper-right block is never read; it is zero.
     __syncthreads();
-    uint16_t* sH = reinterpret_cast<uint16_t*>(sA);   // [64][64] hi
-    uint16_t* sL = sH + kC * kC;                      // [64][64] lo
-    auto put = [&](int r, int cc, float v) {
-        const uint16_t hb = f2bf(v);
-        sH[r * kC + cc] = hb;
-        sL[r * kC + cc] = f2bf(v - bf2f(hb));
-    };
-    auto flush = [&](uint16_t* dh, uint16_t* dl) {
+    uint16_t* sH = reinterpret_cast<uint16_t*>(sA);   // [64][64]
+    auto put = [&](int r, int cc, float v) { sH[r * kC + cc] = f2bf(v); };
+    auto flush = [&](uint16_t* dh) {
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < kC * kC / 8 / kWave; ++it) {
             const int e = (lane + kWave * it) * 8;
             *reinterpret_cast<u32x4*>(dh + tile + e) = *reinterpret_cast<const u32x4*>(sH + e);
-            *reinterpret_cast<u32x4*>(dl + tile + e) = *reinterpret_cast<const u32x4*>(sL + e);
         }
         __syncthreads();
     };
@@ -384,7 +376,7 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) put(32 + acc_row(i, lane), c, -T10[i]);
-    flush(a.Tw, a.Tlw);
+    flush(a.Tw);
 #pragma unroll
     for (int tt = 0; tt < 3; ++tt) {
         const int R0 = tt == 0 ? 0 : 32, C0 = tt == 2 ? 32 : 0;
@@ -393,39 +385,51 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) put(acc_row(i, lane), 32 + c, 0.f);
-    flush(a.Pw, a.Plw);
+    flush(a.Pw);
 }
 
 // ------------------------------------------------------------------ sequential chunk scan
+// One 8-wave workgroup per (sequence, head, 32-column dv slice); two waves per SIMD, so the
+// latency of one wave's LDS reads and MFMAs hides behind the other's work. Products are
+// tiled in 16x16 blocks (v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][(l/16)*8+j] and
+// B[(l/16)*8+j][l%16]; accumulator element i is C[(l/16)*4+i][l%16]) and every wave owns
+// 16 rows of each product:
+//   step 1  waves 0-3: rows 16w.. of Q S (kept for Y);  waves 4-7: rows of K S -> R
+//   step 2  waves 4-7: rows of U = T R (and diag(gamma_C/gamma) U)
+//   step 3  waves 0-3: rows of Y = gamma Q S + P U;  all waves: d_k rows 16w.. of the state
+// The fp32 state lives in registers (2 tiles per wave); bf16 hi + lo copies of S, R, U go
+// through LDS as the next product's B operand.
+constexpr int kScanThreads = 512;
 constexpr int kStrV = kSl + 8;
 
-// Next chunk's inputs, held in registers while the current chunk computes (all loads are
-// unconditional so the compiler keeps them in VGPRs and waits for them only where used).
-#define GDN_FETCH_STAGE(T0, N, TILE)                                                           \
-    do {                                                                                       \
-        fetch_rows128(stq, a.q, (T0), (N), a.H, h);                                            \
-        fetch_rows128(stk, a.k, (T0), (N), a.H, h);                                            \
-        _Pragma("unroll") for (int it = 0; it < 2; ++it) {                                     \
-            const int off = tid * 8 + kThreads * 8 * it;   /* = row * 64 + col */              \
-            stt[it] = *reinterpret_cast<const u32x4*>(a.Tw + (TILE) + off);                    \
-            sttl[it] = *reinterpret_cast<const u32x4*>(a.Tlw + (TILE) + off);                  \
-            stp[it] = *reinterpret_cast<const u32x4*>(a.Pw + (TILE) + off);                    \
-            stpl[it] = *reinterpret_cast<const u32x4*>(a.Plw + (TILE) + off);                  \
-        }                                                                                      \
-        const int vr = min(tid >> 2, (N) - 1);                                                 \
-        stv = *reinterpret_cast<const u32x4*>(a.v + ((size_t)(T0) * a.H + h) * a.dv + j0 +    \
-                                              (vr * a.H * a.dv + (tid & 3) * 8));              \
-        fetch_gates(a, (T0), (N), h, stg, stb);                                                \
-    } while (0)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16 accumulator tile -> transposed bf16 hi + lo: dst[col0 + col][row0 + row]
+__device__ __forceinline__ void store16_t2(uint16_t* hi, uint16_t* lo, int stride, int row0, int col0,
+                                           const f32x4& c, int lane) {
+    const int off = (col0 + (lane & 15)) * stride + row0 + 4 * (lane >> 4);
+    u32x2 vh, vl;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float x0 = c[2 * e], x1 = c[2 * e + 1];
+        const uint32_t hp = pack_bf2(x0, x1);
+        vh[e] = hp;
+        vl[e] = pack_bf2(x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xffff0000u));
+    }
+    *reinterpret_cast<u32x2*>(hi + off) = vh;
+    *reinterpret_cast<u32x2*>(lo + off) = vl;
+}
 
 template <typename Ty>
-__global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
+__global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kStrD];
     __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kStrD];
     __shared__ __attribute__((aligned(16))) uint16_t sT[kC * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sTl[kC * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sP[kC * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sPl[kC * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kStrV];
     __shared__ __attribute__((aligned(16))) uint16_t sSt[kSl * kStrD];    // S^T hi
     __shared__ __attribute__((aligned(16))) uint16_t sStl[kSl * kStrD];   // S^T lo
@@ -460,151 +464,190 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j0 = slice * kSl;
-    const int col = lane & 31;
-    const int kofs = (lane >> 5) * 8;
+    const int c16 = lane & 15;              // tile column
+    const int r4 = 4 * (lane >> 4);         // first of the lane's 4 accumulator rows
+    const int kq = (lane >> 4) * 8;         // the lane's k offset inside a 32-wide k step
+    const int rb = wave & 3;                // 16-row block of steps 1-3a
     const size_t sbase = ((size_t)seq * a.H + h) * kDK * a.dv;
 
-    // state rows [32 wave, 32 wave + 32) of this slice, accumulator layout
-    f32x16 S;
+    // state rows [16 wave, 16 wave + 16) x 32 columns: two 16x16 accumulator tiles
+    f32x4 S[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = 32 * wave + acc_row(i, lane);
-        S[i] = a.S0 ? a.S0[sbase + (size_t)row * a.dv + j0 + col] : 0.f;
-    }
-    store_acc_t2(sSt, sStl, kStrD, 32 * wave, S, lane);
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * wave + r4 + i;
+            S[ct][i] = a.S0 ? a.S0[sbase + (size_t)row * a.dv + j0 + 16 * ct + c16] : 0.f;
+        }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) store16_t2(sSt, sStl, kStrD, 16 * wave, 16 * ct, S[ct], lane);
 
+    // next chunk's inputs, staged in registers while the current chunk computes
     const int nchunks = (hi - lo + kC - 1) / kC;
-    u32x4 stq[4], stk[4], stt[2], sttl[2], stp[2], stpl[2], stv;
+    u32x4 stq[2], stk[2], stt, stp, stv;
     float stg, stb;
-    if (nchunks > 0) GDN_FETCH_STAGE(lo, min(kC, hi - lo), ((size_t)cbase * a.H + h) * kC * kC);
+    auto fetch = [&](int t0, int n, size_t tile) {
+        const uint16_t* qb = a.q + ((size_t)t0 * a.H + h) * kDK;
+        const uint16_t* kb = a.k + ((size_t)t0 * a.H + h) * kDK;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int idx = tid + kScanThreads * it;
+            const int r = min(idx >> 4, n - 1), d0 = (idx & 15) * 8;
+            stq[it] = *reinterpret_cast<const u32x4*>(qb + (r * a.H * kDK + d0));
+            stk[it] = *reinterpret_cast<const u32x4*>(kb + (r * a.H * kDK + d0));
+        }
+        const int off = tid * 8;   // row * 64 + col of the 64x64 tiles
+        stt = *reinterpret_cast<const u32x4*>(a.Tw + tile + off);
+        stp = *reinterpret_cast<const u32x4*>(a.Pw + tile + off);
+        const int vr = min((tid & 255) >> 2, n - 1);
+        stv = *reinterpret_cast<const u32x4*>(a.v + ((size_t)t0 * a.H + h) * a.dv + j0 +
+                                              (vr * a.H * a.dv + (tid & 3) * 8));
+        fetch_gates(a, t0, n, h, stg, stb);
+    };
+    if (nchunks > 0) fetch(lo, min(kC, hi - lo), ((size_t)cbase * a.H + h) * kC * kC);
+
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = lo + c * kC;
         const int n = min(kC, hi - t0);
         // ---- commit the staged chunk to LDS
-        put_rows128(sQ, stq, n);
-        put_rows128(sK, stk, n);
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int idx = tid + kThreads * it;
-            const int o = (idx >> 3) * kStrC + (idx & 7) * 8;
-            *reinterpret_cast<u32x4*>(sT + o) = stt[it];
-            *reinterpret_cast<u32x4*>(sTl + o) = sttl[it];
-            *reinterpret_cast<u32x4*>(sP + o) = stp[it];
-            *reinterpret_cast<u32x4*>(sPl + o) = stpl[it];
-        }
         {
-            const int r = tid >> 2;
             const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(sV + r * kStrV + (tid & 3) * 8) = (n == kC || r < n) ? stv : z;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int idx = tid + kScanThreads * it;
+                const int r = idx >> 4, o = r * kStrD + (idx & 15) * 8;
+                const bool ok = n == kC || r < n;
+                *reinterpret_cast<u32x4*>(sQ + o) = ok ? stq[it] : z;
+                *reinterpret_cast<u32x4*>(sK + o) = ok ? stk[it] : z;
+            }
+            const int o = (tid >> 3) * kStrC + (tid & 7) * 8;
+            *reinterpret_cast<u32x4*>(sT + o) = stt;
+            *reinterpret_cast<u32x4*>(sP + o) = stp;
+            if (tid < 256) {
+                const int r = tid >> 2;
+                *reinterpret_cast<u32x4*>(sV + r * kStrV + (tid & 3) * 8) = (n == kC || r < n) ? stv : z;
+            }
         }
         if (wave == 0) chunk_gates(stg, stb, n, sG, sB, sGam, sGd);
         __syncthreads();
-        // ---- prefetch the next chunk while this one computes (the last chunk re-reads itself)
+        // ---- prefetch the next chunk (the last chunk re-reads itself)
         {
             const int cn = min(c + 1, nchunks - 1);
             const int t1 = lo + cn * kC;
-            GDN_FETCH_STAGE(t1, min(kC, hi - t1), ((size_t)(cbase + cn) * a.H + h) * kC * kC);
+            fetch(t1, min(kC, hi - t1), ((size_t)(cbase + cn) * a.H + h) * kC * kC);
         }
 
-        // ---- step 1: [Q; K] S (waves 0, 1: Q rows; waves 2, 3: K rows), S = S_hi + S_lo
-        f32x16 acc = {};
+        // ---- step 1: rows 16 rb.. of Q S (waves 0-3) or K S (waves 4-7), S = S_hi + S_lo
+        f32x4 acc[2] = {f32x4{}, f32x4{}};
         {
-            const uint16_t* Arow = (wave < 2 ? sQ : sK) + (32 * (wave & 1) + col) * kStrD + kofs;
-            const uint16_t* Bh = sSt + col * kStrD + kofs;
-            const uint16_t* Bl = sStl + col * kStrD + kofs;
+            const uint16_t* Arow = (wave < 4 ? sQ : sK) + (16 * rb + c16) * kStrD + kq;
 #pragma unroll
-            for (int kk = 0; kk < kDK / 16; ++kk) {
-                const bf16x8 af = frag(Arow + kk * 16);
-                acc = mfma(af, frag(Bh + kk * 16), acc);
-                acc = mfma(af, frag(Bl + kk * 16), acc);
+            for (int kk = 0; kk < kDK / 32; ++kk) {
+                const bf16x8 af = frag(Arow + kk * 32);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const uint16_t* Bp = (16 * ct + c16) * kStrD + kq + kk * 32 + sSt;
+                    acc[ct] = mfma16(af, frag(Bp), acc[ct]);
+                    acc[ct] = mfma16(af, frag(Bp - sSt + sStl), acc[ct]);
+                }
             }
         }
-        if (wave >= 2) {
+        if (wave >= 4) {
             // R = beta (V - gamma K S)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 32 * (wave - 2) + acc_row(i, lane);
-                acc[i] = sB[r] * (bf2f(sV[r * kStrV + col]) - sGam[r] * acc[i]);
+            for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + r4 + i;
+                    acc[ct][i] = sB[r] * (bf2f(sV[r * kStrV + 16 * ct + c16]) - sGam[r] * acc[ct][i]);
+                }
+                store16_t2(sRt, sRtl, kStrC, 16 * rb, 16 * ct, acc[ct], lane);
             }
-            store_acc_t2(sRt, sRtl, kStrC, 32 * (wave - 2), acc, lane);
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] *= sGam[32 * wave + acc_row(i, lane)];
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[ct][i] *= sGam[16 * rb + r4 + i];
         }
         __syncthreads();
 
-        // ---- step 2: U = T R (T is unit lower triangular: rows 0-31 need k < 32 only),
-        //      T = T_hi + T_lo, R = R_hi + R_lo (the lo x lo term is below fp32 rounding)
-        if (wave >= 2) {
-            const int r0 = 32 * (wave - 2);
-            f32x16 u = {};
-            const uint16_t* Ah = sT + (r0 + col) * kStrC + kofs;
-            const uint16_t* Al = sTl + (r0 + col) * kStrC + kofs;
-            const uint16_t* Bh = sRt + col * kStrC + kofs;
-            const uint16_t* Bl = sRtl + col * kStrC + kofs;
+        // ---- step 2 (waves 4-7): U rows 16 rb.. = T R, R = R_hi + R_lo;
+        //      T is unit lower triangular, so rows < 32 need only k < 32
+        if (wave >= 4) {
+            const int nk = rb < 2 ? 1 : 2;
+            f32x4 u[2] = {f32x4{}, f32x4{}};
+            const uint16_t* Ah = sT + (16 * rb + c16) * kStrC + kq;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 * (wave - 1)) {
-                    const bf16x8 ah = frag(Ah + kk * 16), bh = frag(Bh + kk * 16);
-                    u = mfma(ah, bh, u);
-                    u = mfma(ah, frag(Bl + kk * 16), u);
-                    u = mfma(frag(Al + kk * 16), bh, u);
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk < nk) {
+                    const bf16x8 ah = frag(Ah + kk * 32);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const int bo = (16 * ct + c16) * kStrC + kq + kk * 32;
+                        u[ct] = mfma16(ah, frag(sRt + bo), u[ct]);
+                        u[ct] = mfma16(ah, frag(sRtl + bo), u[ct]);
+                    }
                 }
             }
-            store_acc_t2(sUt, sUtl, kStrC, r0, u, lane);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) u[i] *= sGd[r0 + acc_row(i, lane)];
-            store_acc_t2(sUht, sUhtl, kStrC, r0, u, lane);
+            for (int ct = 0; ct < 2; ++ct) {
+                store16_t2(sUt, sUtl, kStrC, 16 * rb, 16 * ct, u[ct], lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[ct][i] *= sGd[16 * rb + r4 + i];
+                store16_t2(sUht, sUhtl, kStrC, 16 * rb, 16 * ct, u[ct], lane);
+            }
         }
         __syncthreads();
 
-        // ---- step 3a: Y = gamma Q S + P U  (waves 0, 1), P = P_hi + P_lo, U = U_hi + U_lo
-        if (wave < 2) {
-            const uint16_t* Ah = sP + (32 * wave + col) * kStrC + kofs;
-            const uint16_t* Al = sPl + (32 * wave + col) * kStrC + kofs;
-            const uint16_t* Bh = sUt + col * kStrC + kofs;
-            const uint16_t* Bl = sUtl + col * kStrC + kofs;
+        // ---- step 3a (waves 0-3): Y rows 16 rb.. = gamma Q S + P U, U = U_hi + U_lo
+        if (wave < 4) {
+            const int nk = rb < 2 ? 1 : 2;
+            const uint16_t* Ah = sP + (16 * rb + c16) * kStrC + kq;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 * (wave + 1)) {
-                    const bf16x8 ah = frag(Ah + kk * 16), bh = frag(Bh + kk * 16);
-                    acc = mfma(ah, bh, acc);
-                    acc = mfma(ah, frag(Bl + kk * 16), acc);
-                    acc = mfma(frag(Al + kk * 16), bh, acc);
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk < nk) {
+                    const bf16x8 ah = frag(Ah + kk * 32);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const int bo = (16 * ct + c16) * kStrC + kq + kk * 32;
+                        acc[ct] = mfma16(ah, frag(sUt + bo), acc[ct]);
+                        acc[ct] = mfma16(ah, frag(sUtl + bo), acc[ct]);
+                    }
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) store1(sY + (32 * wave + acc_row(i, lane)) * kStrY + col, acc[i]);
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) store1(sY + (16 * rb + r4 + i) * kStrY + 16 * ct + c16, acc[ct][i]);
         }
-        // ---- step 3b: S = gamma_C S + K^T Uh  (rows 32 wave.. of S; K^T fragments read
+        // ---- step 3b (all waves): state rows 16 w.. = gamma_C S + K^T Uh (K^T fragments read
         //      column-wise from the row-major K tile)
         {
             const float gC = sGam[kC - 1];
+            const int d = 16 * wave + c16;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) S[i] *= gC;
-            const int d = 32 * wave + col;
-            const uint16_t* Bh = sUht + col * kStrC + kofs;
-            const uint16_t* Bl = sUhtl + col * kStrC + kofs;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int ko = kk * 16 + kofs;
+            for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 af;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    af[j] = __builtin_bit_cast(__bf16, sK[(ko + j) * kStrD + d]);
-                S = mfma(af, frag(Bh + kk * 16), S);
-                S = mfma(af, frag(Bl + kk * 16), S);
+                for (int j = 0; j < 8; ++j) af[j] = __builtin_bit_cast(__bf16, sK[(kk * 32 + kq + j) * kStrD + d]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    if (kk == 0) S[ct] *= gC;
+                    const int bo = (16 * ct + c16) * kStrC + kq + kk * 32;
+                    S[ct] = mfma16(af, frag(sUht + bo), S[ct]);
+                    S[ct] = mfma16(af, frag(sUhtl + bo), S[ct]);
+                }
             }
-            store_acc_t2(sSt, sStl, kStrD, 32 * wave, S, lane);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) store16_t2(sSt, sStl, kStrD, 16 * wave, 16 * ct, S[ct], lane);
         }
         __syncthreads();
         // ---- the chunk's y slice: 16-byte stores of whole rows
         {
-            constexpr int kPer = 8 / sizeof(Ty) * 2;          // elements per 16 bytes
+            constexpr int kPer = 16 / sizeof(Ty);             // elements per 16 bytes
             constexpr int kRowPieces = kSl / kPer;
-#pragma unroll
-            for (int it = 0; it < kC * kRowPieces / kThreads; ++it) {
-                const int idx = tid + kThreads * it;
+            const int idx = tid;
+            if (idx < kC * kRowPieces) {
                 const int r = idx / kRowPieces, c0 = (idx % kRowPieces) * kPer;
                 if (r < n)
                     *reinterpret_cast<u32x4*>(static_cast<Ty*>(a.y) + ((size_t)(t0 + r) * a.H + h) * a.dv +
@@ -614,13 +657,14 @@ __global__ void __launch_bounds__(kThreads) chunk_scan_kernel(DevArgs a) {
     }
     if (a.ST) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 32 * wave + acc_row(i, lane);
-            a.ST[sbase + (size_t)row * a.dv + j0 + col] = S[i];
-        }
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * wave + r4 + i;
+                a.ST[sbase + (size_t)row * a.dv + j0 + 16 * ct + c16] = S[ct][i];
+            }
     }
 }
-#undef GDN_FETCH_STAGE
 
 }  // namespace
 
@@ -640,9 +684,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
     a.chunk_start = c.cu ? reinterpret_cast<int32_t*>(ws + L.cs) : nullptr;
     a.order = c.cu ? reinterpret_cast<int32_t*>(ws + L.ord) : nullptr;
     a.Tw = reinterpret_cast<uint16_t*>(ws + L.T);
-    a.Tlw = reinterpret_cast<uint16_t*>(ws + L.Tlo);
     a.Pw = reinterpret_cast<uint16_t*>(ws + L.P);
-    a.Plw = reinterpret_cast<uint16_t*>(ws + L.Plo);
     a.num_seqs = c.num_seqs; a.ntok = c.ntok; a.H = c.H; a.dv = c.dv;
     a.L = c.cu ? 0 : c.ntok / c.num_seqs;
     a.y_bf16 = c.y_bf16;
@@ -654,9 +696,9 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
     const int pairs = c.num_seqs * c.H;
     const int blocks = (pairs + 7) / 8 * 8 * nsl;
     if (c.y_bf16)
-        hipLaunchKernelGGL(chunk_scan_kernel<uint16_t>, dim3(blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chunk_scan_kernel<uint16_t>, dim3(blocks), dim3(kScanThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(chunk_scan_kernel<float>, dim3(blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chunk_scan_kernel<float>, dim3(blocks), dim3(kScanThreads), 0, s, a);
     return hipGetLastError();
 }
 
