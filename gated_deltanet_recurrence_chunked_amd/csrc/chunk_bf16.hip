@@ -89,7 +89,7 @@ __device__ __forceinline__ void store_acc_t2(uint16_t* hi, uint16_t* lo, int str
 }
 
 struct Layout {
-    size_t cs, ord, T, P, total;
+    size_t cs, ord, T, P, Gt, total;
     int max_chunks;
 };
 
@@ -104,6 +104,7 @@ __host__ __device__ inline Layout ws_layout(int ntok, int num_seqs, int H) {
     const size_t tile = (size_t)kC * kC * sizeof(uint16_t);
     L.T = o;   o = align256(o + tile * L.max_chunks * H);
     L.P = o;   o = align256(o + tile * L.max_chunks * H);
+    L.Gt = o;  o = align256(o + sizeof(float) * 3 * kC * (size_t)L.max_chunks * H);
     L.total = o;
     return L;
 }
@@ -117,6 +118,7 @@ struct DevArgs {
     int32_t* chunk_start;       // [num_seqs+1] (varlen)
     int32_t* order;             // [num_seqs] longest first (varlen)
     uint16_t *Tw, *Pw;          // [max_chunks][H][64][64] bf16
+    float* Gw;                  // [max_chunks][H][3][64]: beta, gamma = e^G, gamma_C / gamma
     int num_seqs, ntok, H, dv, L;  // L: equal length (when cu == NULL)
     int y_bf16;
 };
@@ -277,6 +279,20 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     }
     float gv, bv;
     fetch_gates(a, t0, n, h, gv, bv);
+    {
+        // the chunk's beta, gamma_r = e^{G_r} and gamma_C / gamma_r for the scan
+        float* gw = a.Gw + ((size_t)chunk * a.H + h) * 3 * kC;
+        float Gr = lane < n ? gv : 0.f;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float o = __shfl_up(Gr, off, kWave);
+            if (lane >= off) Gr += o;
+        }
+        const float GC = __shfl(Gr, kC - 1, kWave);
+        gw[lane] = lane < n ? bv : 0.f;
+        gw[kC + lane] = fexp(Gr);
+        gw[2 * kC + lane] = fexp(GC - Gr);
+    }
     chunk_gates(gv, bv, n, sG, sB, nullptr, nullptr);
     const u32x4 z = {0u, 0u, 0u, 0u};
     const bool v0 = r0 < n, v1 = r1 < n;
@@ -428,6 +444,7 @@ template <typename Ty>
 __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kStrD];
     __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kStrD];
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[kDK * kStrC];    // K^T: [d_k][token]
     __shared__ __attribute__((aligned(16))) uint16_t sT[kC * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sP[kC * kStrC];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kStrV];
@@ -441,7 +458,10 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sUhtl[kSl * kStrC];
     constexpr int kStrY = sizeof(Ty) == 2 ? kSl + 8 : kSl + 4;          // 16-byte aligned rows
     __shared__ __attribute__((aligned(16))) Ty sY[kC * kStrY];            // the chunk's y slice
-    __shared__ float sG[kC], sB[kC], sGam[kC], sGd[kC];
+    __shared__ __attribute__((aligned(16))) float sGates[3 * kC];       // beta, gamma, gamma_C/gamma
+    const float* sB = sGates;
+    const float* sGam = sGates + kC;
+    const float* sGd = sGates + 2 * kC;
 
     // block -> (pair, slice): the slices of one pair are 8 blocks apart, so the same XCD
     const int nsl = a.dv / kSl;
@@ -484,8 +504,9 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
 
     // next chunk's inputs, staged in registers while the current chunk computes
     const int nchunks = (hi - lo + kC - 1) / kC;
-    u32x4 stq[2], stk[2], stt, stp, stv;
-    float stg, stb;
+    // K pieces are taken token-fastest across lanes (token idx % 64, d_k group idx / 64), so
+    // the transposed copy K^T is written as contiguous 128-byte runs of one d_k row.
+    u32x4 stq[2], stk[2], stt, stp, stv, stgt;
     auto fetch = [&](int t0, int n, size_t tile) {
         const uint16_t* qb = a.q + ((size_t)t0 * a.H + h) * kDK;
         const uint16_t* kb = a.k + ((size_t)t0 * a.H + h) * kDK;
@@ -494,7 +515,8 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
             const int idx = tid + kScanThreads * it;
             const int r = min(idx >> 4, n - 1), d0 = (idx & 15) * 8;
             stq[it] = *reinterpret_cast<const u32x4*>(qb + (r * a.H * kDK + d0));
-            stk[it] = *reinterpret_cast<const u32x4*>(kb + (r * a.H * kDK + d0));
+            const int rk = min(idx & 63, n - 1), dk0 = (idx >> 6) * 8;
+            stk[it] = *reinterpret_cast<const u32x4*>(kb + (rk * a.H * kDK + dk0));
         }
         const int off = tid * 8;   // row * 64 + col of the 64x64 tiles
         stt = *reinterpret_cast<const u32x4*>(a.Tw + tile + off);
@@ -502,7 +524,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         const int vr = min((tid & 255) >> 2, n - 1);
         stv = *reinterpret_cast<const u32x4*>(a.v + ((size_t)t0 * a.H + h) * a.dv + j0 +
                                               (vr * a.H * a.dv + (tid & 3) * 8));
-        fetch_gates(a, t0, n, h, stg, stb);
+        stgt = *reinterpret_cast<const u32x4*>(a.Gw + tile / (kC * kC) * 3 * kC + 4 * (tid % 48));
     };
     if (nchunks > 0) fetch(lo, min(kC, hi - lo), ((size_t)cbase * a.H + h) * kC * kC);
 
@@ -516,10 +538,17 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
             for (int it = 0; it < 2; ++it) {
                 const int idx = tid + kScanThreads * it;
                 const int r = idx >> 4, o = r * kStrD + (idx & 15) * 8;
-                const bool ok = n == kC || r < n;
-                *reinterpret_cast<u32x4*>(sQ + o) = ok ? stq[it] : z;
-                *reinterpret_cast<u32x4*>(sK + o) = ok ? stk[it] : z;
+                *reinterpret_cast<u32x4*>(sQ + o) = (n == kC || r < n) ? stq[it] : z;
+                const int rk = idx & 63, dk0 = (idx >> 6) * 8;
+                const u32x4 kv = (n == kC || rk < n) ? stk[it] : z;
+                *reinterpret_cast<u32x4*>(sK + rk * kStrD + dk0) = kv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sKt[(dk0 + 2 * e) * kStrC + rk] = uint16_t(kv[e] & 0xffffu);
+                    sKt[(dk0 + 2 * e + 1) * kStrC + rk] = uint16_t(kv[e] >> 16);
+                }
             }
+            if (tid < 48) *reinterpret_cast<u32x4*>(sGates + 4 * tid) = stgt;
             const int o = (tid >> 3) * kStrC + (tid & 7) * 8;
             *reinterpret_cast<u32x4*>(sT + o) = stt;
             *reinterpret_cast<u32x4*>(sP + o) = stp;
@@ -528,7 +557,6 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
                 *reinterpret_cast<u32x4*>(sV + r * kStrV + (tid & 3) * 8) = (n == kC || r < n) ? stv : z;
             }
         }
-        if (wave == 0) chunk_gates(stg, stb, n, sG, sB, sGam, sGd);
         __syncthreads();
         // ---- prefetch the next chunk (the last chunk re-reads itself)
         {
@@ -620,16 +648,13 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) store1(sY + (16 * rb + r4 + i) * kStrY + 16 * ct + c16, acc[ct][i]);
         }
-        // ---- step 3b (all waves): state rows 16 w.. = gamma_C S + K^T Uh (K^T fragments read
-        //      column-wise from the row-major K tile)
+        // ---- step 3b (all waves): state rows 16 w.. = gamma_C S + K^T Uh
         {
             const float gC = sGam[kC - 1];
-            const int d = 16 * wave + c16;
+            const uint16_t* Arow = sKt + (16 * wave + c16) * kStrC + kq;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 af;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) af[j] = __builtin_bit_cast(__bf16, sK[(kk * 32 + kq + j) * kStrD + d]);
+                const bf16x8 af = frag(Arow + kk * 32);
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     if (kk == 0) S[ct] *= gC;
@@ -685,6 +710,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
     a.order = c.cu ? reinterpret_cast<int32_t*>(ws + L.ord) : nullptr;
     a.Tw = reinterpret_cast<uint16_t*>(ws + L.T);
     a.Pw = reinterpret_cast<uint16_t*>(ws + L.P);
+    a.Gw = reinterpret_cast<float*>(ws + L.Gt);
     a.num_seqs = c.num_seqs; a.ntok = c.ntok; a.H = c.H; a.dv = c.dv;
     a.L = c.cu ? 0 : c.ntok / c.num_seqs;
     a.y_bf16 = c.y_bf16;
