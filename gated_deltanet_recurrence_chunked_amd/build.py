@@ -25,10 +25,17 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source extras. The chunk scan keeps its MFMA accumulators in architectural VGPRs: it runs
+# one wave per SIMD with room for them, and accumulators left in AGPRs cost a v_accvgpr_read
+# for every element that the fp32 -> bf16 hi/lo splits and the gate scalings touch.
+EXTRA = {
+    "chunk_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -13,16 +13,14 @@
 // significant bits: two MFMAs per product); the chunk-local T and P are single bf16.
 // T and P depend on the chunk's q, k, g, beta only, so they are produced for every chunk at
 // once by chunk_prep_kernel (massively parallel: KK^T and QK^T on MFMA, the 64x64 unit
-// lower-triangular inverse by fp32 forward substitution). chunk_scan_kernel then walks the
-// chunks of each (sequence, head) in order. The columns of S, V, U and Y are independent, so
-// a scan workgroup owns a 32-column slice of dv: 4 workgroups per head at dv = 128, mapped to
-// the same XCD so the shared q, k, T, P tiles are fetched from HBM once and hit that XCD's L2.
+// lower-triangular inverse by fp32 forward substitution and 32x32 fp32 MFMA blocks).
+// chunk_scan_kernel then walks the chunks of each (sequence, head) in order. The columns of
+// S, V, U and Y are independent, so a scan workgroup owns a 32-column slice of d_v: 4
+// workgroups per head at d_v = 128, mapped to the same XCD so the shared q, k, T, P tiles are
+// fetched from HBM once and hit that XCD's L2.
 //
 // MFMA v_mfma_f32_32x32x16_bf16 operand layout (lane l of 64): A element j is A[l%32][(l/32)*8+j],
 // B element j is B[(l/32)*8+j][l%32], accumulator element i is C[8(i/4)+4(l/32)+i%4][l%32].
-// Every LDS tile is stored with the contraction index contiguous (A as [row][k], B as
-// [col][k]) so each operand fragment is one 16-byte LDS read; rows are padded by 16 bytes
-// so the 32 rows read by one fragment load fall in distinct banks.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -54,39 +52,6 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
 
 // accumulator element i of lane l -> tile row
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
-
-// Stores the 32x32 accumulator tile, converted to bf16, transposed: dst[col][row0 + row].
-__device__ __forceinline__ void store_acc_t(uint16_t* dst, int stride, int row0, const f32x16& c,
-                                            int lane) {
-    uint16_t* base = dst + (lane & 31) * stride + row0 + 4 * (lane >> 5);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        u32x2 v;
-        v.x = pack_bf2(c[4 * q + 0], c[4 * q + 1]);
-        v.y = pack_bf2(c[4 * q + 2], c[4 * q + 3]);
-        *reinterpret_cast<u32x2*>(base + 8 * q) = v;
-    }
-}
-
-// Same, as a two-term bf16 split: hi = bf16(x), lo = bf16(x - hi), so hi + lo carries about
-// 16 significant bits; products against it take two MFMAs.
-__device__ __forceinline__ void store_acc_t2(uint16_t* hi, uint16_t* lo, int stride, int row0,
-                                             const f32x16& c, int lane) {
-    const int off = (lane & 31) * stride + row0 + 4 * (lane >> 5);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        u32x2 vh, vl;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const float x0 = c[4 * q + 2 * e], x1 = c[4 * q + 2 * e + 1];
-            const uint32_t hp = pack_bf2(x0, x1);   // one v_cvt_pk_bf16_f32
-            vh[e] = hp;
-            vl[e] = pack_bf2(x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xffff0000u));
-        }
-        *reinterpret_cast<u32x2*>(hi + off + 8 * q) = vh;
-        *reinterpret_cast<u32x2*>(lo + off + 8 * q) = vl;
-    }
-}
 
 struct Layout {
     size_t cs, ord, T, P, Gt, total;
@@ -157,38 +122,6 @@ __global__ void __launch_bounds__(kThreads) chunk_table_kernel(DevArgs a) {
             rank += (Lj > Li) || (Lj == Li && j < i);
         }
         a.order[rank] = i;
-    }
-}
-
-// Rows [0, 64) of one chunk of a [ntok, H, 128] bf16 tensor: 256 threads x 4 x 16 bytes,
-// fetched into registers (all loads in flight together; rows >= n read row n-1 and are
-// zeroed when written to LDS, so no load sits behind a branch).
-// The chunk's base address is wave-uniform (scalar registers); a lane adds a 32-bit offset.
-__device__ __forceinline__ void fetch_rows128(u32x4 (&R)[4], const uint16_t* src, int t0, int n,
-                                              int H, int h) {
-    const uint16_t* base = src + ((size_t)t0 * H + h) * kDK;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int idx = threadIdx.x + kThreads * it;
-        const int r = min(idx >> 4, n - 1), d0 = (idx & 15) * 8;
-        R[it] = *reinterpret_cast<const u32x4*>(base + (r * H * kDK + d0));
-    }
-}
-__device__ __forceinline__ void put_rows128(uint16_t* dst, const u32x4 (&R)[4], int n) {
-    if (n == kC) {
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = threadIdx.x + kThreads * it;
-            *reinterpret_cast<u32x4*>(dst + (idx >> 4) * kStrD + (idx & 15) * 8) = R[it];
-        }
-        return;
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int idx = threadIdx.x + kThreads * it;
-        const int r = idx >> 4, d0 = (idx & 15) * 8;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(dst + r * kStrD + d0) = r < n ? R[it] : z;
     }
 }
 
@@ -405,63 +338,109 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
 }
 
 // ------------------------------------------------------------------ sequential chunk scan
-// One 8-wave workgroup per (sequence, head, 32-column dv slice); two waves per SIMD, so the
-// latency of one wave's LDS reads and MFMAs hides behind the other's work. Products are
-// tiled in 16x16 blocks (v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][(l/16)*8+j] and
-// B[(l/16)*8+j][l%16]; accumulator element i is C[(l/16)*4+i][l%16]) and every wave owns
-// 16 rows of each product:
-//   step 1  waves 0-3: rows 16w.. of Q S (kept for Y);  waves 4-7: rows of K S -> R
-//   step 2  waves 4-7: rows of U = T R (and diag(gamma_C/gamma) U)
-//   step 3  waves 0-3: rows of Y = gamma Q S + P U;  all waves: d_k rows 16w.. of the state
-// The fp32 state lives in registers (2 tiles per wave); bf16 hi + lo copies of S, R, U go
-// through LDS as the next product's B operand.
-constexpr int kScanThreads = 512;
-constexpr int kStrV = kSl + 8;
+// One 4-wave workgroup per (sequence, head, 32-column slice of d_v). Waves 0-1 compute, one
+// 16-column slice each; waves 2-3 stream every chunk's tiles (Q, K, T, P, the V slice and the
+// gate rows) into a three-deep LDS ring with direct global->LDS loads, two chunks ahead.
+//
+// A compute wave keeps everything that depends on the state in registers, so a chunk needs
+// no exchange between waves: products are v_mfma_f32_16x16x32_bf16 tiles (lane l = (c, g),
+// c = l%16, g = l/16, supplies A[c][8g+j] and B[8g+j][c]; accumulator element i is
+// C[4g+i][c]). An accumulator therefore holds, per lane, 4 rows of one column, while an
+// operand needs 8 consecutive contraction indices of one row or column. Instead of moving
+// data between lanes, the rows of a tile are relabelled: tile 2s+a of a 64-row (tokens) or
+// 128-row (d_k) dimension has row r standing for index 32s + 8(r/4) + 4a + r%4. With that
+// labelling, accumulator tiles 2s and 2s+1 of one lane hold exactly indices 32s+8g .. 32s+8g+7
+// of their column, i.e. the operand fragment of contraction step s: the state S, the residual
+// R and the update U go from accumulator to bf16 operand in registers. The relabelling only
+// changes which LDS row an operand lane reads (the tiles stay row-major); the K^T operand of
+// the state update comes from the row-major K tile through the transposing LDS read
+// ds_read_b64_tr_b16.
+//
+// Per chunk and wave (S, R, U enter as bf16 hi + lo pairs, two MFMAs per product):
+//   KS = K S,  R = diag(beta) (V - diag(gamma) KS),  U = T R,
+//   S  = gamma_C S + K^T diag(gamma_C / gamma) U,
+//   Y^T = gamma-scaled S^T Q^T + U^T P^T  (Y^T rows are d_v, so a lane stores 4 adjacent y).
+// LDS tiles are row-major with 16-byte units XOR-swizzled by a function of the row, so the
+// 16 rows read by one fragment load and the 4x4 rows/units read by one transposing load
+// spread over the banks.
+constexpr int kScanThreads = 256;
+constexpr int kRing = 3;
+constexpr int kOffQ = 0;                      // ring slot layout, in bf16 elements
+constexpr int kOffK = kOffQ + kC * kDK;
+constexpr int kOffT = kOffK + kC * kDK;
+constexpr int kOffP = kOffT + kC * kC;
+constexpr int kOffV = kOffP + kC * kC;
+constexpr int kOffG = kOffV + kC * kSl;       // 3 x 64 floats (+ 256 bytes of padding)
+constexpr int kSlot = kOffG + 512;
+constexpr int kLoadsW2 = 16 + 8 + 1;          // direct loads per chunk: Q, T, gates
+constexpr int kLoadsW3 = 16 + 8 + 4;          //                         K, P, V
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16x16 accumulator tile -> transposed bf16 hi + lo: dst[col0 + col][row0 + row]
-__device__ __forceinline__ void store16_t2(uint16_t* hi, uint16_t* lo, int stride, int row0, int col0,
-                                           const f32x4& c, int lane) {
-    const int off = (col0 + (lane & 15)) * stride + row0 + 4 * (lane >> 4);
-    u32x2 vh, vl;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const float x0 = c[2 * e], x1 = c[2 * e + 1];
-        const uint32_t hp = pack_bf2(x0, x1);
-        vh[e] = hp;
-        vl[e] = pack_bf2(x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xffff0000u));
-    }
-    *reinterpret_cast<u32x2*>(hi + off) = vh;
-    *reinterpret_cast<u32x2*>(lo + off) = vl;
+// 16-byte unit swizzle of LDS row `row`: distinct for the 8 rows {0..7} and for {0-3, 8-11}
+// (+ any multiple of 4), and spreads the 4 consecutive rows of a transposing read.
+__device__ __forceinline__ int swz(int row) {
+    return (((row & 1) << 2) | ((row >> 1) & 3)) ^ (((row >> 3) & 1) << 1);
 }
+
+// tile row r of tile t (2s + a) of a relabelled dimension -> index 32s + 8(r/4) + 4a + r%4
+__device__ __forceinline__ int relabel(int t, int r) {
+    return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
+}
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
+}
+
+// two fp32 accumulator quads -> bf16 hi and lo operand fragments (8 values each)
+__device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float a0 = e < 2 ? x0[2 * e] : x1[2 * e - 4];
+        const float a1 = e < 2 ? x0[2 * e + 1] : x1[2 * e - 3];
+        const uint32_t hp = pack_bf2(a0, a1);
+        h[e] = hp;
+        l[e] = pack_bf2(a0 - __uint_as_float(hp << 16), a1 - __uint_as_float(hp & 0xffff0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ void dma16(const void* src, uint16_t* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads (the ring refills) and y stores
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The loader waves' side of that barrier. Their only LDS writes are the direct loads, which the
+// vector-memory counter tracks: each loader waits for the chunk it owes with an explicit
+// s_waitcnt first, and the chunk it just issued stays in flight across the barrier (a fence
+// would wait for it too).
+__device__ __forceinline__ void loader_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// keeps the instruction scheduler from moving anything across this point (reads issued before
+// it stay ahead of the MFMAs after it)
+#define GDN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
+#define GDN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
 
 template <typename Ty>
 __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kStrD];
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kStrD];
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[kDK * kStrC];    // K^T: [d_k][token]
-    __shared__ __attribute__((aligned(16))) uint16_t sT[kC * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sP[kC * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kStrV];
-    __shared__ __attribute__((aligned(16))) uint16_t sSt[kSl * kStrD];    // S^T hi
-    __shared__ __attribute__((aligned(16))) uint16_t sStl[kSl * kStrD];   // S^T lo
-    __shared__ __attribute__((aligned(16))) uint16_t sRt[kSl * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sRtl[kSl * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sUt[kSl * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sUtl[kSl * kStrC];
-    __shared__ __attribute__((aligned(16))) uint16_t sUht[kSl * kStrC];   // (diag(gamma_C/gamma) U)^T
-    __shared__ __attribute__((aligned(16))) uint16_t sUhtl[kSl * kStrC];
-    constexpr int kStrY = sizeof(Ty) == 2 ? kSl + 8 : kSl + 4;          // 16-byte aligned rows
-    __shared__ __attribute__((aligned(16))) Ty sY[kC * kStrY];            // the chunk's y slice
-    __shared__ __attribute__((aligned(16))) float sGates[3 * kC];       // beta, gamma, gamma_C/gamma
-    const float* sB = sGates;
-    const float* sGam = sGates + kC;
-    const float* sGd = sGates + 2 * kC;
+    __shared__ __attribute__((aligned(16))) uint16_t ring[kRing * kSlot];
 
     // block -> (pair, slice): the slices of one pair are 8 blocks apart, so the same XCD
     const int nsl = a.dv / kSl;
@@ -482,212 +461,309 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         hi = lo + a.L;
         cbase = seq * ((a.L + kC - 1) / kC);
     }
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int j0 = slice * kSl;
-    const int c16 = lane & 15;              // tile column
-    const int r4 = 4 * (lane >> 4);         // first of the lane's 4 accumulator rows
-    const int kq = (lane >> 4) * 8;         // the lane's k offset inside a 32-wide k step
-    const int rb = wave & 3;                // 16-row block of steps 1-3a
-    const size_t sbase = ((size_t)seq * a.H + h) * kDK * a.dv;
-
-    // state rows [16 wave, 16 wave + 16) x 32 columns: two 16x16 accumulator tiles
-    f32x4 S[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * wave + r4 + i;
-            S[ct][i] = a.S0 ? a.S0[sbase + (size_t)row * a.dv + j0 + 16 * ct + c16] : 0.f;
-        }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) store16_t2(sSt, sStl, kStrD, 16 * wave, 16 * ct, S[ct], lane);
-
-    // next chunk's inputs, staged in registers while the current chunk computes
     const int nchunks = (hi - lo + kC - 1) / kC;
-    // K pieces are taken token-fastest across lanes (token idx % 64, d_k group idx / 64), so
-    // the transposed copy K^T is written as contiguous 128-byte runs of one d_k row.
-    u32x4 stq[2], stk[2], stt, stp, stv, stgt;
-    auto fetch = [&](int t0, int n, size_t tile) {
-        const uint16_t* qb = a.q + ((size_t)t0 * a.H + h) * kDK;
-        const uint16_t* kb = a.k + ((size_t)t0 * a.H + h) * kDK;
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int idx = tid + kScanThreads * it;
-            const int r = min(idx >> 4, n - 1), d0 = (idx & 15) * 8;
-            stq[it] = *reinterpret_cast<const u32x4*>(qb + (r * a.H * kDK + d0));
-            const int rk = min(idx & 63, n - 1), dk0 = (idx >> 6) * 8;
-            stk[it] = *reinterpret_cast<const u32x4*>(kb + (rk * a.H * kDK + dk0));
-        }
-        const int off = tid * 8;   // row * 64 + col of the 64x64 tiles
-        stt = *reinterpret_cast<const u32x4*>(a.Tw + tile + off);
-        stp = *reinterpret_cast<const u32x4*>(a.Pw + tile + off);
-        const int vr = min((tid & 255) >> 2, n - 1);
-        stv = *reinterpret_cast<const u32x4*>(a.v + ((size_t)t0 * a.H + h) * a.dv + j0 +
-                                              (vr * a.H * a.dv + (tid & 3) * 8));
-        stgt = *reinterpret_cast<const u32x4*>(a.Gw + tile / (kC * kC) * 3 * kC + 4 * (tid % 48));
-    };
-    if (nchunks > 0) fetch(lo, min(kC, hi - lo), ((size_t)cbase * a.H + h) * kC * kC);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform branches
+    const int j0 = slice * kSl;
 
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = lo + c * kC;
-        const int n = min(kC, hi - t0);
-        // ---- commit the staged chunk to LDS
-        {
-            const u32x4 z = {0u, 0u, 0u, 0u};
+    if (wave >= 2) {
+        // ---------------- loader waves
+        auto issue = [&](int ck) {
+            const int t0 = lo + ck * kC, n = min(kC, hi - t0);
+            const size_t ch = (size_t)(cbase + ck) * a.H + h;   // chunk-head index
+            uint16_t* slot = ring + (ck % kRing) * kSlot;
+            if (wave == 2) {
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int idx = tid + kScanThreads * it;
-                const int r = idx >> 4, o = r * kStrD + (idx & 15) * 8;
-                *reinterpret_cast<u32x4*>(sQ + o) = (n == kC || r < n) ? stq[it] : z;
-                const int rk = idx & 63, dk0 = (idx >> 6) * 8;
-                const u32x4 kv = (n == kC || rk < n) ? stk[it] : z;
-                *reinterpret_cast<u32x4*>(sK + rk * kStrD + dk0) = kv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sKt[(dk0 + 2 * e) * kStrC + rk] = uint16_t(kv[e] & 0xffffu);
-                    sKt[(dk0 + 2 * e + 1) * kStrC + rk] = uint16_t(kv[e] >> 16);
+                for (int i = 0; i < 16; ++i) {
+                    const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
+                    dma16(a.q + ((size_t)(t0 + min(row, n - 1)) * a.H + h) * kDK + u * 8, slot + kOffQ + i * 512);
                 }
-            }
-            if (tid < 48) *reinterpret_cast<u32x4*>(sGates + 4 * tid) = stgt;
-            const int o = (tid >> 3) * kStrC + (tid & 7) * 8;
-            *reinterpret_cast<u32x4*>(sT + o) = stt;
-            *reinterpret_cast<u32x4*>(sP + o) = stp;
-            if (tid < 256) {
-                const int r = tid >> 2;
-                *reinterpret_cast<u32x4*>(sV + r * kStrV + (tid & 3) * 8) = (n == kC || r < n) ? stv : z;
-            }
-        }
-        __syncthreads();
-        // ---- prefetch the next chunk (the last chunk re-reads itself)
-        {
-            const int cn = min(c + 1, nchunks - 1);
-            const int t1 = lo + cn * kC;
-            fetch(t1, min(kC, hi - t1), ((size_t)(cbase + cn) * a.H + h) * kC * kC);
-        }
-
-        // ---- step 1: rows 16 rb.. of Q S (waves 0-3) or K S (waves 4-7), S = S_hi + S_lo
-        f32x4 acc[2] = {f32x4{}, f32x4{}};
-        {
-            const uint16_t* Arow = (wave < 4 ? sQ : sK) + (16 * rb + c16) * kStrD + kq;
 #pragma unroll
-            for (int kk = 0; kk < kDK / 32; ++kk) {
-                const bf16x8 af = frag(Arow + kk * 32);
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const uint16_t* Bp = (16 * ct + c16) * kStrD + kq + kk * 32 + sSt;
-                    acc[ct] = mfma16(af, frag(Bp), acc[ct]);
-                    acc[ct] = mfma16(af, frag(Bp - sSt + sStl), acc[ct]);
+                for (int i = 0; i < 8; ++i) {
+                    const int row = 8 * i + (lane >> 3), u = (lane & 7) ^ swz(row);
+                    dma16(a.Tw + ch * kC * kC + row * kC + u * 8, slot + kOffT + i * 512);
                 }
-            }
-        }
-        if (wave >= 4) {
-            // R = beta (V - gamma K S)
+                dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kOffG);
+            } else {
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+                for (int i = 0; i < 16; ++i) {
+                    const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
+                    dma16(a.k + ((size_t)(t0 + min(row, n - 1)) * a.H + h) * kDK + u * 8, slot + kOffK + i * 512);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int row = 8 * i + (lane >> 3), u = (lane & 7) ^ swz(row);
+                    dma16(a.Pw + ch * kC * kC + row * kC + u * 8, slot + kOffP + i * 512);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + r4 + i;
-                    acc[ct][i] = sB[r] * (bf2f(sV[r * kStrV + 16 * ct + c16]) - sGam[r] * acc[ct][i]);
+                    const int row = 16 * i + (lane >> 2);
+                    dma16(a.v + ((size_t)(t0 + min(row, n - 1)) * a.H + h) * a.dv + j0 + (lane & 3) * 8,
+                          slot + kOffV + i * 512);
                 }
-                store16_t2(sRt, sRtl, kStrC, 16 * rb, 16 * ct, acc[ct], lane);
             }
+        };
+        auto wait_all_but_one_chunk = [&]() {
+            if (wave == 2) GDN_WAIT_VMCNT(kLoadsW2); else GDN_WAIT_VMCNT(kLoadsW3);
+        };
+        if (nchunks > 0) issue(0);
+        if (nchunks > 1) {
+            issue(1);
+            wait_all_but_one_chunk();
         } else {
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[ct][i] *= sGam[16 * rb + r4 + i];
+            GDN_WAIT_VMCNT(0);
         }
-        __syncthreads();
+        loader_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 2 < nchunks) {
+                issue(c + 2);   // ring slot of chunk c - 1, released by the barrier before c
+                wait_all_but_one_chunk();
+            } else {
+                GDN_WAIT_VMCNT(0);
+            }
+            loader_barrier();
+        }
+        return;
+    }
 
-        // ---- step 2 (waves 4-7): U rows 16 rb.. = T R, R = R_hi + R_lo;
-        //      T is unit lower triangular, so rows < 32 need only k < 32
-        if (wave >= 4) {
-            const int nk = rb < 2 ? 1 : 2;
-            f32x4 u[2] = {f32x4{}, f32x4{}};
-            const uint16_t* Ah = sT + (16 * rb + c16) * kStrC + kq;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk < nk) {
-                    const bf16x8 ah = frag(Ah + kk * 32);
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const int bo = (16 * ct + c16) * kStrC + kq + kk * 32;
-                        u[ct] = mfma16(ah, frag(sRt + bo), u[ct]);
-                        u[ct] = mfma16(ah, frag(sRtl + bo), u[ct]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                store16_t2(sUt, sUtl, kStrC, 16 * rb, 16 * ct, u[ct], lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) u[ct][i] *= sGd[16 * rb + r4 + i];
-                store16_t2(sUht, sUhtl, kStrC, 16 * rb, 16 * ct, u[ct], lane);
-            }
-        }
-        __syncthreads();
+    // ---------------- compute waves: d_v columns j0w .. j0w + 15
+    const int j0w = j0 + 16 * wave;
+    const int c16 = lane & 15, g = lane >> 4;
+    const size_t sbase = ((size_t)seq * a.H + h) * kDK * a.dv;
 
-        // ---- step 3a (waves 0-3): Y rows 16 rb.. = gamma Q S + P U, U = U_hi + U_lo
-        if (wave < 4) {
-            const int nk = rb < 2 ? 1 : 2;
-            const uint16_t* Ah = sP + (16 * rb + c16) * kStrC + kq;
+    // state: tile t holds d_k rows relabel(t, 4g + i) of column j0w + c16
+    f32x4 S[8];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk < nk) {
-                    const bf16x8 ah = frag(Ah + kk * 32);
+    for (int t = 0; t < 8; ++t) S[t] = f32x4{};
+    if (a.S0) {
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const int bo = (16 * ct + c16) * kStrC + kq + kk * 32;
-                        acc[ct] = mfma16(ah, frag(sUt + bo), acc[ct]);
-                        acc[ct] = mfma16(ah, frag(sUtl + bo), acc[ct]);
-                    }
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sbase + (size_t)relabel(t, 4 * g + i) * a.dv + j0w + c16];
+    }
+    bf16x8 Sh[4], Sl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) split8(S[2 * s], S[2 * s + 1], Sh[s], Sl[s]);
+
+    // Per-lane LDS offsets (elements, from the ring slot) of the fragment reads. The swizzle
+    // sees only the low 4 bits of a row, so rows 16 or 32 apart and units 8 apart are constant
+    // offsets from one of these bases and become immediates of the LDS reads.
+    int okf[2][2], otf[2][2], oqf[2], opf[2], okt[2][2];
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2) {
+        const int r = relabel(a2, c16);
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            okf[a2][sp] = kOffK + r * kDK + (((4 * sp + g) ^ swz(r)) << 3);
+            otf[a2][sp] = kOffT + r * kC + (((4 * sp + g) ^ swz(r)) << 3);
+        }
+    }
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+        oqf[sp] = kOffQ + c16 * kDK + (((4 * sp + g) ^ swz(c16)) << 3);
+        opf[sp] = kOffP + c16 * kC + (((4 * sp + g) ^ swz(c16)) << 3);
+    }
+    const int jj = (lane & 15) >> 2, r4 = lane & 3;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int tok = 8 * g + jj + 4 * hf;
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) okt[hf][tp] = kOffK + tok * kDK + (((4 * tp + r4) ^ swz(tok)) << 3);
+    }
+    const int ov = kOffV + (8 * g + jj) * kSl + 16 * wave + 4 * r4;
+
+    lds_barrier();   // chunk 0 in the ring
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = lo + c * kC, n = min(kC, hi - t0);
+        const uint16_t* slot = ring + (c % kRing) * kSlot;
+        const float* sG = reinterpret_cast<const float*>(slot + kOffG);   // beta | gamma | gamma_C/gamma
+        // fragment reads (tile rows relabelled as described above)
+        auto kfrag = [&](int rt, int s) {   // A of K S: K[relabel(rt, c16)][32s + 8g ..]
+            return frag(slot + okf[rt & 1][s & 1] + (rt >> 1) * 32 * kDK + (s >> 1) * 64);
+        };
+        auto qfrag = [&](int rt, int s) {   // B of S^T Q^T: Q[16 rt + c16][32s + 8g ..]
+            return frag(slot + oqf[s & 1] + rt * 16 * kDK + (s >> 1) * 64);
+        };
+        auto tfrag = [&](int rt, int s) {   // A of T R: T[relabel(rt, c16)][32s + 8g ..]
+            return frag(slot + otf[rt & 1][s] + (rt >> 1) * 32 * kC);
+        };
+        auto pfrag = [&](int rt, int s) {   // B of U^T P^T: P[16 rt + c16][32s + 8g ..]
+            return frag(slot + opf[s] + rt * 16 * kC);
+        };
+        auto ktr = [&](int t, int s, int hf) {   // K^T[relabel(t, c16)][32s + 8g + 4hf ..]
+            return lds_tr16(slot + okt[hf][(t >> 1) & 1] + s * 32 * kDK + (t >> 2) * 64 + 4 * (t & 1));
+        };
+        auto grow = [&](int which, int rt) {   // gate row `which` at the lane's 4 relabelled tokens
+            return *reinterpret_cast<const f32x4*>(sG + which * kC + 8 * g + 32 * (rt >> 1) + 4 * (rt & 1));
+        };
+
+        // ---- K S and S^T Q^T, each contraction step's fragments read one step ahead
+        bf16x8 kf[4][4], qf[4][4];
+        f32x4 KS[4], YT[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            KS[rt] = f32x4{};
+            YT[rt] = f32x4{};
+        }
+        auto load_kq = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                kf[s][rt] = kfrag(rt, s);
+                qf[s][rt] = qfrag(rt, s);
+            }
+        };
+        auto mma_kq = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                KS[rt] = mfma16(kf[s][rt], Sh[s], KS[rt]);
+                YT[rt] = mfma16(Sh[s], qf[s][rt], YT[rt]);
+                KS[rt] = mfma16(kf[s][rt], Sl[s], KS[rt]);
+                YT[rt] = mfma16(Sl[s], qf[s][rt], YT[rt]);
+            }
+        };
+        load_kq(0);
+        load_kq(1);
+        GDN_SCHED_FENCE();
+        mma_kq(0);
+        GDN_SCHED_FENCE();
+        load_kq(2);
+        GDN_SCHED_FENCE();
+        mma_kq(1);
+        GDN_SCHED_FENCE();
+        load_kq(3);
+        GDN_SCHED_FENCE();
+        mma_kq(2);
+        GDN_SCHED_FENCE();
+        f32x4 bet[4], gam[4];
+        s16x4 vv[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            bet[rt] = grow(0, rt);
+            gam[rt] = grow(1, rt);
+            vv[rt] = lds_tr16(slot + ov + (32 * (rt >> 1) + 4 * (rt & 1)) * kSl);
+        }
+        GDN_SCHED_FENCE();
+        mma_kq(3);
+        GDN_SCHED_FENCE();
+        bf16x8 tf[4][2];
+        f32x4 gd[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (s <= (rt >> 1)) tf[rt][s] = tfrag(rt, s);
+            gd[rt] = grow(2, rt);
+        }
+        GDN_SCHED_FENCE();
+        // ---- R = beta (V - gamma KS): the lane's rows are 4 consecutive tokens of its column
+        f32x4 R[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                R[rt][i] = bet[rt][i] * (bf2f(uint16_t(vv[rt][i])) - gam[rt][i] * KS[rt][i]);
+        bf16x8 Rh[2], Rl[2];
+        split8(R[0], R[1], Rh[0], Rl[0]);
+        split8(R[2], R[3], Rh[1], Rl[1]);
+        GDN_SCHED_FENCE();
+        bf16x8 pf[4][2];
+        float gq[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (s <= (rt >> 1)) pf[rt][s] = pfrag(rt, s);
+            gq[rt] = sG[kC + 16 * rt + c16];
+        }
+        const float gC = sG[kC + kC - 1];
+        GDN_SCHED_FENCE();
+        // ---- U = T R (T unit lower triangular: token rows < 32 need contraction step 0 only)
+        f32x4 U[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            U[rt] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (s <= (rt >> 1)) {
+                    U[rt] = mfma16(tf[rt][s], Rh[s], U[rt]);
+                    U[rt] = mfma16(tf[rt][s], Rl[s], U[rt]);
                 }
             }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) store1(sY + (16 * rb + r4 + i) * kStrY + 16 * ct + c16, acc[ct][i]);
         }
-        // ---- step 3b (all waves): state rows 16 w.. = gamma_C S + K^T Uh
-        {
-            const float gC = sGam[kC - 1];
-            const uint16_t* Arow = sKt + (16 * wave + c16) * kStrC + kq;
+        GDN_SCHED_FENCE();
+        s16x4 kt[8][2][2];   // K^T fragments [d_k tile][step][half]
+        auto load_kt = [&](int t) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 af = frag(Arow + kk * 32);
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    if (kk == 0) S[ct] *= gC;
-                    const int bo = (16 * ct + c16) * kStrC + kq + kk * 32;
-                    S[ct] = mfma16(af, frag(sUht + bo), S[ct]);
-                    S[ct] = mfma16(af, frag(sUhtl + bo), S[ct]);
+                for (int hf = 0; hf < 2; ++hf) kt[t][s][hf] = ktr(t, s, hf);
+        };
+        load_kt(0);
+        load_kt(1);
+        load_kt(2);
+        GDN_SCHED_FENCE();
+        bf16x8 Uh[2], Ul[2], Wh[2], Wl[2];   // U and diag(gamma_C / gamma) U
+        split8(U[0], U[1], Uh[0], Ul[0]);
+        split8(U[2], U[3], Uh[1], Ul[1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            U[rt] *= gd[rt];
+            YT[rt] *= gq[rt];
+        }
+        split8(U[0], U[1], Wh[0], Wl[0]);
+        split8(U[2], U[3], Wh[1], Wl[1]);
+        GDN_SCHED_FENCE();
+        // ---- S = gamma_C S + K^T W, tile by tile with three tiles of K^T reads in flight;
+        //      Y^T += U^T P^T (P lower triangular) rides along, two MFMAs per tile
+        auto pu = [&](int idx) {   // (rt, s) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+            const int rt = idx < 2 ? idx : (idx < 4 ? 2 : 3);
+            const int s = idx < 2 ? 0 : ((idx - 2) & 1);
+            YT[rt] = mfma16(Uh[s], pf[rt][s], YT[rt]);
+            YT[rt] = mfma16(Ul[s], pf[rt][s], YT[rt]);
+        };
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t + 3 < 8) load_kt(t + 3);
+            GDN_SCHED_FENCE();
+            S[t] *= gC;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const u32x2 p0 = __builtin_bit_cast(u32x2, kt[t][s][0]);
+                const u32x2 p1 = __builtin_bit_cast(u32x2, kt[t][s][1]);
+                const u32x4 pk = {p0.x, p0.y, p1.x, p1.y};
+                const bf16x8 ktf = __builtin_bit_cast(bf16x8, pk);
+                S[t] = mfma16(ktf, Wh[s], S[t]);
+                S[t] = mfma16(ktf, Wl[s], S[t]);
+            }
+            if (t < 6) pu(t);
+            GDN_SCHED_FENCE();
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) split8(S[2 * s], S[2 * s + 1], Sh[s], Sl[s]);
+        // ---- the chunk's y slice: a lane holds 4 adjacent d_v of token 16 rt + c16
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int rp = 16 * rt + c16;
+            if (rp < n) {
+                Ty* yp = static_cast<Ty*>(a.y) + ((size_t)(t0 + rp) * a.H + h) * a.dv + j0w + 4 * g;
+                if constexpr (sizeof(Ty) == 2) {
+                    u32x2 o;
+                    o.x = pack_bf2(YT[rt][0], YT[rt][1]);
+                    o.y = pack_bf2(YT[rt][2], YT[rt][3]);
+                    *reinterpret_cast<u32x2*>(yp) = o;
+                } else {
+                    *reinterpret_cast<f32x4*>(yp) = YT[rt];
                 }
             }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) store16_t2(sSt, sStl, kStrD, 16 * wave, 16 * ct, S[ct], lane);
         }
-        __syncthreads();
-        // ---- the chunk's y slice: 16-byte stores of whole rows
-        {
-            constexpr int kPer = 16 / sizeof(Ty);             // elements per 16 bytes
-            constexpr int kRowPieces = kSl / kPer;
-            const int idx = tid;
-            if (idx < kC * kRowPieces) {
-                const int r = idx / kRowPieces, c0 = (idx % kRowPieces) * kPer;
-                if (r < n)
-                    *reinterpret_cast<u32x4*>(static_cast<Ty*>(a.y) + ((size_t)(t0 + r) * a.H + h) * a.dv +
-                                              j0 + c0) = *reinterpret_cast<const u32x4*>(sY + r * kStrY + c0);
-            }
-        }
+        lds_barrier();   // past this barrier the loaders refill this slot
     }
     if (a.ST) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * wave + r4 + i;
-                a.ST[sbase + (size_t)row * a.dv + j0 + 16 * ct + c16] = S[ct][i];
-            }
+            for (int i = 0; i < 4; ++i)
+                a.ST[sbase + (size_t)relabel(t, 4 * g + i) * a.dv + j0w + c16] = S[t][i];
     }
 }
 

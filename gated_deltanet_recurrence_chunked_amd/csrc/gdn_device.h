@@ -19,8 +19,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// two floats -> packed bf16 pair (lo in bits 0-15), one v_cvt_pk_bf16_f32
+typedef __bf16 gdn_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float gdn_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+    const gdn_f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, gdn_bf16x2));
 }
 
 // --------------------------------------------------------------------------- typed 8-wide IO
