@@ -9,8 +9,9 @@
 //   R      = diag(beta) (V - diag(gamma) K S)             U = T R
 //   Y      = diag(gamma) Q S + P U
 //   S_next = gamma_C S + K^T diag(gamma_C / gamma) U
-// The state-side operands S, R and U enter the MFMAs as hi + lo bf16 pairs (about 16
-// significant bits: two MFMAs per product); the chunk-local T and P are single bf16.
+// The residual R and the update U (and diag(gamma_C/gamma) U) enter the MFMAs as hi + lo bf16
+// pairs (about 16 significant bits: two MFMAs per product); the fp32 state S is rounded to a
+// single bf16 operand, like q, k and the chunk-local T and P.
 // T and P depend on the chunk's q, k, g, beta only, so they are produced for every chunk at
 // once by chunk_prep_kernel (massively parallel: KK^T and QK^T on MFMA, the 64x64 unit
 // lower-triangular inverse by fp32 forward substitution and 32x32 fp32 MFMA blocks).
@@ -356,7 +357,7 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
 // the state update comes from the row-major K tile through the transposing LDS read
 // ds_read_b64_tr_b16.
 //
-// Per chunk and wave (S, R, U enter as bf16 hi + lo pairs, two MFMAs per product):
+// Per chunk and wave (R, U and W enter as bf16 hi + lo pairs, two MFMAs per product):
 //   KS = K S,  R = diag(beta) (V - diag(gamma) KS),  U = T R,
 //   S  = gamma_C S + K^T diag(gamma_C / gamma) U,
 //   Y^T = gamma-scaled S^T Q^T + U^T P^T  (Y^T rows are d_v, so a lane stores 4 adjacent y).
@@ -413,6 +414,13 @@ __device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, bf16x8&
     lo = __builtin_bit_cast(bf16x8, l);
 }
 
+// two fp32 accumulator quads -> one bf16 operand fragment (8 values)
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& x0, const f32x4& x1) {
+    const u32x4 h = {pack_bf2(x0[0], x0[1]), pack_bf2(x0[2], x0[3]), pack_bf2(x1[0], x1[1]),
+                     pack_bf2(x1[2], x1[3])};
+    return __builtin_bit_cast(bf16x8, h);
+}
+
 __device__ __forceinline__ void dma16(const void* src, uint16_t* lds_dst) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
 }
@@ -434,6 +442,15 @@ __device__ __forceinline__ void loader_barrier() { asm volatile("s_barrier" ::: 
 // keeps the instruction scheduler from moving anything across this point (reads issued before
 // it stay ahead of the MFMAs after it)
 #define GDN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Interleaving request for the scheduling region it closes: nm times {one MFMA, up to nv VALU
+// instructions, up to nd LDS reads}.
+#define GDN_IGLP(nm, nv, nd)                                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < (nm); ++i_) {     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    \
+        __builtin_amdgcn_sched_group_barrier(0x002, (nv), 0); \
+        __builtin_amdgcn_sched_group_barrier(0x100, (nd), 0); \
+    }
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
 #define GDN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
@@ -541,9 +558,9 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sbase + (size_t)relabel(t, 4 * g + i) * a.dv + j0w + c16];
     }
-    bf16x8 Sh[4], Sl[4];
+    bf16x8 Sb[4];   // S as bf16 operand fragments, one per contraction step
 #pragma unroll
-    for (int s = 0; s < 4; ++s) split8(S[2 * s], S[2 * s + 1], Sh[s], Sl[s]);
+    for (int s = 0; s < 4; ++s) Sb[s] = to_bf16x8(S[2 * s], S[2 * s + 1]);
 
     // Per-lane LDS offsets (elements, from the ring slot) of the fragment reads. The swizzle
     // sees only the low 4 bits of a row, so rows 16 or 32 apart and units 8 apart are constant
@@ -572,6 +589,32 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     }
     const int ov = kOffV + (8 * g + jj) * kSl + 16 * wave + 4 * r4;
 
+    // Y^T of the current chunk; a lane holds 4 adjacent d_v of token 16 rt + c16. The lane's
+    // y address is formed once; a chunk adds a wave-uniform offset (64-bit multiplies per
+    // store are quarter-rate VALU work).
+    f32x4 YT[4];
+    const size_t ytok = (size_t)a.H * a.dv;   // elements between consecutive tokens of y
+    Ty* const ylane = static_cast<Ty*>(a.y) + (size_t)h * a.dv + j0w + 4 * g + (size_t)c16 * ytok;
+    auto store_y = [&](int cy) {
+        const int ty = lo + cy * kC, ny = min(kC, hi - ty);
+        Ty* const yc = ylane + (size_t)ty * ytok;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int rp = 16 * rt + c16;
+            if (rp < ny) {
+                Ty* yp = yc + (size_t)(16 * rt) * ytok;
+                if constexpr (sizeof(Ty) == 2) {
+                    u32x2 o;
+                    o.x = pack_bf2(YT[rt][0], YT[rt][1]);
+                    o.y = pack_bf2(YT[rt][2], YT[rt][3]);
+                    *reinterpret_cast<u32x2*>(yp) = o;
+                } else {
+                    *reinterpret_cast<f32x4*>(yp) = YT[rt];
+                }
+            }
+        }
+    };
+
     lds_barrier();   // chunk 0 in the ring
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = lo + c * kC, n = min(kC, hi - t0);
@@ -597,65 +640,75 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
             return *reinterpret_cast<const f32x4*>(sG + which * kC + 8 * g + 32 * (rt >> 1) + 4 * (rt & 1));
         };
 
-        // ---- K S and S^T Q^T, each contraction step's fragments read one step ahead
+        // The MFMA chain of a chunk is K S -> R -> U = T R -> W -> S update; the fp32 -> bf16
+        // splits and gate scalings between its links are VALU work, and every operand comes
+        // from LDS. Each block below is one scheduling region whose MFMAs are interleaved with
+        // VALU work that does not feed them and with the LDS reads of later regions; Y^T's
+        // products and the gamma_C scaling of S, which are off the chain, fill the gaps.
         bf16x8 kf[4][4], qf[4][4];
-        f32x4 KS[4], YT[4];
+        f32x4 KS[4];
+        auto mma_k = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) KS[rt] = mfma16(kf[s][rt], Sb[s], KS[rt]);
+        };
+        auto mma_q = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Sb[s], qf[s][rt], YT[rt]);
+        };
+        auto load_k = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) kf[s][rt] = kfrag(rt, s);
+        };
+        auto load_q = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) qf[s][rt] = qfrag(rt, s);
+        };
+        load_k(0);
+        load_k(1);
+        const float gC = sG[kC + kC - 1];
+        GDN_SCHED_FENCE();
+        // ---- K S step 0 | gamma_C S (tiles 0-3) | K fragments of steps 2-3
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             KS[rt] = f32x4{};
             YT[rt] = f32x4{};
         }
-        auto load_kq = [&](int s) {
+        mma_k(0);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                kf[s][rt] = kfrag(rt, s);
-                qf[s][rt] = qfrag(rt, s);
-            }
-        };
-        auto mma_kq = [&](int s) {
+        for (int t = 0; t < 4; ++t) S[t] *= gC;
+        load_k(2);
+        load_k(3);
+        GDN_IGLP(4, 4, 2);
+        GDN_SCHED_FENCE();
+        // ---- K S step 1 | gamma_C S (tiles 4-7) | Q fragments of steps 0-1
+        mma_k(1);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                KS[rt] = mfma16(kf[s][rt], Sh[s], KS[rt]);
-                YT[rt] = mfma16(Sh[s], qf[s][rt], YT[rt]);
-                KS[rt] = mfma16(kf[s][rt], Sl[s], KS[rt]);
-                YT[rt] = mfma16(Sl[s], qf[s][rt], YT[rt]);
-            }
-        };
-        load_kq(0);
-        load_kq(1);
+        for (int t = 4; t < 8; ++t) S[t] *= gC;
+        load_q(0);
+        load_q(1);
+        GDN_IGLP(4, 4, 2);
         GDN_SCHED_FENCE();
-        mma_kq(0);
-        GDN_SCHED_FENCE();
-        load_kq(2);
-        GDN_SCHED_FENCE();
-        mma_kq(1);
-        GDN_SCHED_FENCE();
-        load_kq(3);
-        GDN_SCHED_FENCE();
-        mma_kq(2);
-        GDN_SCHED_FENCE();
+        // ---- K S step 2 | gate rows and V at the lane's tokens
         f32x4 bet[4], gam[4];
         s16x4 vv[4];
+        mma_k(2);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             bet[rt] = grow(0, rt);
             gam[rt] = grow(1, rt);
             vv[rt] = lds_tr16(slot + ov + (32 * (rt >> 1) + 4 * (rt & 1)) * kSl);
         }
+        GDN_IGLP(4, 1, 3);
         GDN_SCHED_FENCE();
-        mma_kq(3);
+        // ---- K S step 3 | Q fragments of steps 2-3
+        mma_k(3);
+        load_q(2);
+        load_q(3);
+        GDN_IGLP(4, 1, 2);
         GDN_SCHED_FENCE();
+        // ---- R = beta (V - gamma KS) and its split | S^T Q^T (all steps) | T fragments, gd
         bf16x8 tf[4][2];
         f32x4 gd[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s <= (rt >> 1)) tf[rt][s] = tfrag(rt, s);
-            gd[rt] = grow(2, rt);
-        }
-        GDN_SCHED_FENCE();
-        // ---- R = beta (V - gamma KS): the lane's rows are 4 consecutive tokens of its column
         f32x4 R[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -665,32 +718,21 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         bf16x8 Rh[2], Rl[2];
         split8(R[0], R[1], Rh[0], Rl[0]);
         split8(R[2], R[3], Rh[1], Rl[1]);
-        GDN_SCHED_FENCE();
-        bf16x8 pf[4][2];
-        float gq[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mma_q(s);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                if (s <= (rt >> 1)) pf[rt][s] = pfrag(rt, s);
-            gq[rt] = sG[kC + 16 * rt + c16];
+                if (s <= (rt >> 1)) tf[rt][s] = tfrag(rt, s);
+            gd[rt] = grow(2, rt);
         }
-        const float gC = sG[kC + kC - 1];
+        GDN_IGLP(16, 6, 1);
         GDN_SCHED_FENCE();
-        // ---- U = T R (T unit lower triangular: token rows < 32 need contraction step 0 only)
-        f32x4 U[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            U[rt] = f32x4{};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s <= (rt >> 1)) {
-                    U[rt] = mfma16(tf[rt][s], Rh[s], U[rt]);
-                    U[rt] = mfma16(tf[rt][s], Rl[s], U[rt]);
-                }
-            }
-        }
-        GDN_SCHED_FENCE();
+        // ---- U = T R (T unit lower triangular: token rows < 32 need step 0 only) |
+        //      gamma (S^T Q^T) | P fragments, gamma at Y's tokens, K^T fragments of tiles 0-1
+        bf16x8 pf[4][2];
+        float gq[4];
         s16x4 kt[8][2][2];   // K^T fragments [d_k tile][step][half]
         auto load_kt = [&](int t) {
 #pragma unroll
@@ -698,34 +740,43 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) kt[t][s][hf] = ktr(t, s, hf);
         };
-        load_kt(0);
-        load_kt(1);
-        load_kt(2);
-        GDN_SCHED_FENCE();
-        bf16x8 Uh[2], Ul[2], Wh[2], Wl[2];   // U and diag(gamma_C / gamma) U
-        split8(U[0], U[1], Uh[0], Ul[0]);
-        split8(U[2], U[3], Uh[1], Ul[1]);
+        f32x4 U[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = f32x4{};
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rh[0], U[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rl[0], U[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rh[1], U[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rl[1], U[rt]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            U[rt] *= gd[rt];
-            YT[rt] *= gq[rt];
-        }
-        split8(U[0], U[1], Wh[0], Wl[0]);
-        split8(U[2], U[3], Wh[1], Wl[1]);
-        GDN_SCHED_FENCE();
-        // ---- S = gamma_C S + K^T W, tile by tile with three tiles of K^T reads in flight;
-        //      Y^T += U^T P^T (P lower triangular) rides along, two MFMAs per tile
-        auto pu = [&](int idx) {   // (rt, s) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-            const int rt = idx < 2 ? idx : (idx < 4 ? 2 : 3);
-            const int s = idx < 2 ? 0 : ((idx - 2) & 1);
-            YT[rt] = mfma16(Uh[s], pf[rt][s], YT[rt]);
-            YT[rt] = mfma16(Ul[s], pf[rt][s], YT[rt]);
-        };
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t + 3 < 8) load_kt(t + 3);
-            GDN_SCHED_FENCE();
-            S[t] *= gC;
+            for (int s = 0; s < 2; ++s)
+                if (s <= (rt >> 1)) pf[rt][s] = pfrag(rt, s);
+            gq[rt] = sG[kC + 16 * rt + c16];
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) YT[rt] *= gq[rt];
+        load_kt(0);
+        load_kt(1);
+        GDN_IGLP(12, 2, 2);
+        GDN_SCHED_FENCE();
+        // ---- W = diag(gamma_C / gamma) U and its split | K^T fragments of tiles 2-3
+        bf16x8 Wh[2], Wl[2];
+        f32x4 Wf[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Wf[rt] = U[rt] * gd[rt];
+        split8(Wf[0], Wf[1], Wh[0], Wl[0]);
+        split8(Wf[2], Wf[3], Wh[1], Wl[1]);
+        load_kt(2);
+        load_kt(3);
+        GDN_SCHED_FENCE();
+        // ---- S = gamma_C S + K^T W (tiles 0-3) | U's split, finished S pairs split |
+        //      K^T fragments of tiles 4-7
+        auto upd = [&](int t) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const u32x2 p0 = __builtin_bit_cast(u32x2, kt[t][s][0]);
@@ -735,27 +786,33 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
                 S[t] = mfma16(ktf, Wh[s], S[t]);
                 S[t] = mfma16(ktf, Wl[s], S[t]);
             }
-            if (t < 6) pu(t);
-            GDN_SCHED_FENCE();
-        }
+            if (t & 1) Sb[t >> 1] = to_bf16x8(S[t - 1], S[t]);
+        };
+        bf16x8 Uh[2], Ul[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) split8(S[2 * s], S[2 * s + 1], Sh[s], Sl[s]);
-        // ---- the chunk's y slice: a lane holds 4 adjacent d_v of token 16 rt + c16
+        for (int t = 0; t < 4; ++t) upd(t);
+        split8(U[0], U[1], Uh[0], Ul[0]);
+        split8(U[2], U[3], Uh[1], Ul[1]);
+        load_kt(4);
+        load_kt(5);
+        load_kt(6);
+        load_kt(7);
+        GDN_IGLP(16, 4, 1);
+        GDN_SCHED_FENCE();
+        // ---- S update (tiles 4-7) | Y^T += U^T P^T (P lower triangular)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int rp = 16 * rt + c16;
-            if (rp < n) {
-                Ty* yp = static_cast<Ty*>(a.y) + ((size_t)(t0 + rp) * a.H + h) * a.dv + j0w + 4 * g;
-                if constexpr (sizeof(Ty) == 2) {
-                    u32x2 o;
-                    o.x = pack_bf2(YT[rt][0], YT[rt][1]);
-                    o.y = pack_bf2(YT[rt][2], YT[rt][3]);
-                    *reinterpret_cast<u32x2*>(yp) = o;
-                } else {
-                    *reinterpret_cast<f32x4*>(yp) = YT[rt];
-                }
-            }
-        }
+        for (int t = 4; t < 8; ++t) upd(t);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Uh[0], pf[rt][0], YT[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Ul[0], pf[rt][0], YT[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) YT[rt] = mfma16(Uh[1], pf[rt][1], YT[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) YT[rt] = mfma16(Ul[1], pf[rt][1], YT[rt]);
+        GDN_IGLP(28, 1, 0);
+        GDN_SCHED_FENCE();
+        store_y(c);
         lds_barrier();   // past this barrier the loaders refill this slot
     }
     if (a.ST) {
