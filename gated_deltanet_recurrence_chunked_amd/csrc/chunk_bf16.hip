@@ -339,42 +339,48 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
 }
 
 // ------------------------------------------------------------------ sequential chunk scan
-// One 4-wave workgroup per (sequence, head, 32-column slice of d_v). Waves 0-1 compute, one
-// 16-column slice each; waves 2-3 stream every chunk's tiles (Q, K, T, P, the V slice and the
-// gate rows) into a three-deep LDS ring with direct global->LDS loads, two chunks ahead.
+// One 4-wave workgroup per (sequence, head, 32-column slice of d_v), one wave per SIMD:
+//   waves 0-1 ("chain" waves) carry the recurrence of one 16-column slice each,
+//     K S -> R -> U = T R -> W = diag(gamma_C/gamma) U -> S = gamma_C S + K^T W;
+//   wave 2 (the "output" wave), one chunk behind the chain, forms Y^T = gamma-scaled
+//     S^T Q^T + U^T P^T for both slices (they share the Q and P fragments) and stores y;
+//   wave 3 (the loader) streams, with direct global->LDS loads, the chain's tiles (K, T, the
+//     V slice and the gate rows) one chunk ahead into a two-slot ring and the output wave's
+//     tiles (Q, P, the gate rows) into two slots of their own.
+// The chain waves hand each chunk's bf16 state operand and fp32 U to the output wave through
+// a double-buffered LDS exchange, so the MFMAs and VALU work off the chain run on other SIMDs
+// and only the loader issues global loads.
 //
-// A compute wave keeps everything that depends on the state in registers, so a chunk needs
-// no exchange between waves: products are v_mfma_f32_16x16x32_bf16 tiles (lane l = (c, g),
-// c = l%16, g = l/16, supplies A[c][8g+j] and B[8g+j][c]; accumulator element i is
-// C[4g+i][c]). An accumulator therefore holds, per lane, 4 rows of one column, while an
-// operand needs 8 consecutive contraction indices of one row or column. Instead of moving
-// data between lanes, the rows of a tile are relabelled: tile 2s+a of a 64-row (tokens) or
-// 128-row (d_k) dimension has row r standing for index 32s + 8(r/4) + 4a + r%4. With that
-// labelling, accumulator tiles 2s and 2s+1 of one lane hold exactly indices 32s+8g .. 32s+8g+7
-// of their column, i.e. the operand fragment of contraction step s: the state S, the residual
-// R and the update U go from accumulator to bf16 operand in registers. The relabelling only
-// changes which LDS row an operand lane reads (the tiles stay row-major); the K^T operand of
-// the state update comes from the row-major K tile through the transposing LDS read
-// ds_read_b64_tr_b16.
+// A chain wave keeps everything that depends on the state in registers: products are
+// v_mfma_f32_16x16x32_bf16 tiles (lane l = (c, g), c = l%16, g = l/16, supplies A[c][8g+j]
+// and B[8g+j][c]; accumulator element i is C[4g+i][c]). An accumulator therefore holds, per
+// lane, 4 rows of one column, while an operand needs 8 consecutive contraction indices of one
+// row or column. Instead of moving data between lanes, the rows of a tile are relabelled:
+// tile 2s+a of a 64-row (tokens) or 128-row (d_k) dimension has row r standing for index
+// 32s + 8(r/4) + 4a + r%4. With that labelling, accumulator tiles 2s and 2s+1 of one lane
+// hold exactly indices 32s+8g .. 32s+8g+7 of their column, i.e. the operand fragment of
+// contraction step s: the state S, the residual R and the update U go from accumulator to
+// bf16 operand in registers (and are the same fragments whether they enter a product as A or
+// as B). The relabelling only changes which LDS row an operand lane reads (the tiles stay
+// row-major); the K^T operand of the state update comes from the row-major K tile through
+// the transposing LDS read ds_read_b64_tr_b16. Y^T has d_v rows, so an output lane stores 4
+// adjacent y values of one token.
 //
-// Per chunk and wave (R, U and W enter as bf16 hi + lo pairs, two MFMAs per product):
-//   KS = K S,  R = diag(beta) (V - diag(gamma) KS),  U = T R,
-//   S  = gamma_C S + K^T diag(gamma_C / gamma) U,
-//   Y^T = gamma-scaled S^T Q^T + U^T P^T  (Y^T rows are d_v, so a lane stores 4 adjacent y).
-// LDS tiles are row-major with 16-byte units XOR-swizzled by a function of the row, so the
-// 16 rows read by one fragment load and the 4x4 rows/units read by one transposing load
-// spread over the banks.
+// R, U and W enter their products as bf16 hi + lo pairs (two MFMAs per product). LDS tiles are
+// row-major with 16-byte units XOR-swizzled by a function of the row, so the 16 rows read by
+// one fragment load and the 4x4 rows/units read by one transposing load spread over the banks.
 constexpr int kScanThreads = 256;
-constexpr int kRing = 3;
-constexpr int kOffQ = 0;                      // ring slot layout, in bf16 elements
-constexpr int kOffK = kOffQ + kC * kDK;
+constexpr int kRing = 2;
+constexpr int kOffK = 0;                      // ring slot layout, in bf16 elements
 constexpr int kOffT = kOffK + kC * kDK;
-constexpr int kOffP = kOffT + kC * kC;
-constexpr int kOffV = kOffP + kC * kC;
+constexpr int kOffV = kOffT + kC * kC;
 constexpr int kOffG = kOffV + kC * kSl;       // 3 x 64 floats (+ 256 bytes of padding)
 constexpr int kSlot = kOffG + 512;
-constexpr int kLoadsW2 = 16 + 8 + 1;          // direct loads per chunk: Q, T, gates
-constexpr int kLoadsW3 = 16 + 8 + 4;          //                         K, P, V
+
+constexpr int kQOffQ = 0;                     // output slot layout, in bf16 elements
+constexpr int kQOffP = kQOffQ + kC * kDK;
+constexpr int kQOffG = kQOffP + kC * kC;      // 3 x 64 floats (+ 256 bytes of padding)
+constexpr int kQPSlot = kQOffG + 512;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -425,19 +431,19 @@ __device__ __forceinline__ void dma16(const void* src, uint16_t* lds_dst) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
 }
 
-// Workgroup barrier that orders LDS accesses only: global loads (the ring refills) and y stores
-// stay in flight across it.
+// Workgroup barrier that orders LDS accesses only (global loads and stores stay in flight).
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// The loader waves' side of that barrier. Their only LDS writes are the direct loads, which the
-// vector-memory counter tracks: each loader waits for the chunk it owes with an explicit
-// s_waitcnt first, and the chunk it just issued stays in flight across the barrier (a fence
-// would wait for it too).
-__device__ __forceinline__ void loader_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The output waves' side of that barrier. Their direct loads into the ring are tracked by the
+// vector-memory counter, which they wait on explicitly (for the chunk they owe) before it, so
+// the chunk just issued stays in flight across it (a fence would wait for it too); their own
+// LDS reads are complete at the barrier (lgkmcnt), and the memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // keeps the instruction scheduler from moving anything across this point (reads issued before
 // it stay ahead of the MFMAs after it)
@@ -457,7 +463,11 @@ __device__ __forceinline__ void loader_barrier() { asm volatile("s_barrier" ::: 
 
 template <typename Ty>
 __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t ring[kRing * kSlot];
+    __shared__ __attribute__((aligned(16))) uint16_t ring[kRing * kSlot];      // the chain's tiles
+    __shared__ __attribute__((aligned(16))) uint16_t qpbuf[2 * kQPSlot];     // the output wave's tiles
+    // chain -> output exchange: [chunk parity][slice][8 x 64 lanes x 16 bytes]; rows 0-3 hold
+    // the bf16 state fragments of contraction steps 0-3, rows 4-7 the fp32 U tiles
+    __shared__ __attribute__((aligned(16))) u32x4 xbuf[2][2][8 * 64];
 
     // block -> (pair, slice): the slices of one pair are 8 blocks apart, so the same XCD
     const int nsl = a.dv / kSl;
@@ -482,70 +492,169 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform branches
     const int j0 = slice * kSl;
+    const int c16 = lane & 15, g = lane >> 4;
 
-    if (wave >= 2) {
-        // ---------------- loader waves
-        auto issue = [&](int ck) {
+    if (wave == 3) {
+        // ================= loader wave
+        // Step c refills ring slot (c + 1) % 2 with chunk c + 1's K, T, V slice and gate rows
+        // for the chain (the slot held chunk c - 1, which the chain finished before this step's
+        // barrier) and output slot c % 2 with chunk c's Q, P and gate rows for the output wave
+        // (which used that slot for chunk c - 2 during the previous step), then waits for both
+        // before the barrier. For a full chunk the per-lane global offsets do not depend on the
+        // chunk, so they are formed once; a chunk adds wave-uniform bases.
+        int offk[16], offv[4];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
+            offk[i] = (row * a.H + h) * kDK + u * 8;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) offv[i] = ((16 * i + (lane >> 2)) * a.H + h) * a.dv + j0 + (lane & 3) * 8;
+        // [64][128] tile rows of a chunk of x (q or k), 16-byte units swizzled per row
+        auto rows128 = [&](const uint16_t* x, int t0, int n, uint16_t* dst) __attribute__((always_inline)) {
+            const uint16_t* xb = x + (size_t)t0 * a.H * kDK;
+            if (n == kC) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dma16(xb + offk[i], dst + i * 512);
+            } else {   // the ragged last chunk: rows >= n repeat row n - 1
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
+                    dma16(xb + (min(row, n - 1) * a.H + h) * kDK + u * 8, dst + i * 512);
+                }
+            }
+        };
+        auto tile64 = [&](const uint16_t* src, uint16_t* dst) __attribute__((always_inline)) {   // [64][64]
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 8 * i + (lane >> 3), u = (lane & 7) ^ swz(row);
+                dma16(src + row * kC + u * 8, dst + i * 512);
+            }
+        };
+        auto chain_tiles = [&](int ck) __attribute__((always_inline)) {
             const int t0 = lo + ck * kC, n = min(kC, hi - t0);
             const size_t ch = (size_t)(cbase + ck) * a.H + h;   // chunk-head index
-            uint16_t* slot = ring + (ck % kRing) * kSlot;
-            if (wave == 2) {
+            uint16_t* slot = ring + (ck & 1) * kSlot;
+            rows128(a.k, t0, n, slot + kOffK);
+            const uint16_t* vb = a.v + (size_t)t0 * a.H * a.dv;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
-                    dma16(a.q + ((size_t)(t0 + min(row, n - 1)) * a.H + h) * kDK + u * 8, slot + kOffQ + i * 512);
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int row = 8 * i + (lane >> 3), u = (lane & 7) ^ swz(row);
-                    dma16(a.Tw + ch * kC * kC + row * kC + u * 8, slot + kOffT + i * 512);
-                }
-                dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kOffG);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
-                    dma16(a.k + ((size_t)(t0 + min(row, n - 1)) * a.H + h) * kDK + u * 8, slot + kOffK + i * 512);
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int row = 8 * i + (lane >> 3), u = (lane & 7) ^ swz(row);
-                    dma16(a.Pw + ch * kC * kC + row * kC + u * 8, slot + kOffP + i * 512);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * i + (lane >> 2);
-                    dma16(a.v + ((size_t)(t0 + min(row, n - 1)) * a.H + h) * a.dv + j0 + (lane & 3) * 8,
-                          slot + kOffV + i * 512);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * i + (lane >> 2);
+                const int o = n == kC ? offv[i] : (min(row, n - 1) * a.H + h) * a.dv + j0 + (lane & 3) * 8;
+                dma16(vb + o, slot + kOffV + i * 512);
             }
+            tile64(a.Tw + ch * kC * kC, slot + kOffT);
+            dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kOffG);
         };
-        auto wait_all_but_one_chunk = [&]() {
-            if (wave == 2) GDN_WAIT_VMCNT(kLoadsW2); else GDN_WAIT_VMCNT(kLoadsW3);
+        auto output_tiles = [&](int ck) __attribute__((always_inline)) {
+            const int t0 = lo + ck * kC, n = min(kC, hi - t0);
+            const size_t ch = (size_t)(cbase + ck) * a.H + h;
+            uint16_t* slot = qpbuf + (ck & 1) * kQPSlot;
+            rows128(a.q, t0, n, slot + kQOffQ);
+            tile64(a.Pw + ch * kC * kC, slot + kQOffP);
+            dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kQOffG);
         };
-        if (nchunks > 0) issue(0);
-        if (nchunks > 1) {
-            issue(1);
-            wait_all_but_one_chunk();
-        } else {
+        if (nchunks > 0) chain_tiles(0);
+        GDN_WAIT_VMCNT(0);
+        dma_barrier();
+        for (int c = 0; c <= nchunks; ++c) {
+            if (c + 1 < nchunks) chain_tiles(c + 1);
+            if (c < nchunks) output_tiles(c);
             GDN_WAIT_VMCNT(0);
+            dma_barrier();
         }
-        loader_barrier();
-        for (int c = 0; c < nchunks; ++c) {
-            if (c + 2 < nchunks) {
-                issue(c + 2);   // ring slot of chunk c - 1, released by the barrier before c
-                wait_all_but_one_chunk();
-            } else {
-                GDN_WAIT_VMCNT(0);
+        return;
+    }
+    if (wave == 2) {
+        // ================= output wave: Y^T of both 16-column slices, one chunk behind the chain
+        // Y^T = gamma (S^T Q^T) + U^T P^T: S^T and U^T are the chain's operand fragments (lane
+        // (c, g): d_v row c, contraction indices 32s + 8g ..), Q and P the B operands with
+        // natural token columns; a lane holds 4 adjacent d_v of token 16 rt + c16 of y.
+        int oqf[2], opf[2];
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            oqf[sp] = kQOffQ + c16 * kDK + (((4 * sp + g) ^ swz(c16)) << 3);
+            opf[sp] = kQOffP + c16 * kC + (((4 * sp + g) ^ swz(c16)) << 3);
+        }
+        const size_t ytok = (size_t)a.H * a.dv;   // elements between consecutive tokens of y
+        Ty* const ylane = static_cast<Ty*>(a.y) + (size_t)h * a.dv + j0 + 4 * g + (size_t)c16 * ytok;
+        auto output = [&](int cy) __attribute__((always_inline)) {
+            const uint16_t* slot = qpbuf + (cy & 1) * kQPSlot;
+            const float* sGq = reinterpret_cast<const float*>(slot + kQOffG);
+            bf16x8 qf[4][4], pf[4][2];
+            float gq[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                // rows 16 apart share the swizzle, units 8 apart are 64 elements apart
+#pragma unroll
+                for (int s = 0; s < 4; ++s) qf[rt][s] = frag(slot + oqf[s & 1] + rt * 16 * kDK + (s >> 1) * 64);
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s <= (rt >> 1)) pf[rt][s] = frag(slot + opf[s] + rt * 16 * kC);
+                gq[rt] = sGq[kC + 16 * rt + c16];
             }
-            loader_barrier();
+            f32x4 YT[2][4];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                const u32x4* xb = xbuf[cy & 1][sl];
+                bf16x8 Sb[4];
+                f32x4 U[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Sb[s] = __builtin_bit_cast(bf16x8, xb[s * 64 + lane]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) U[rt] = __builtin_bit_cast(f32x4, xb[(4 + rt) * 64 + lane]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = f32x4{};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = mfma16(Sb[s], qf[rt][s], YT[sl][rt]);
+                bf16x8 Uh[2], Ul[2];
+                split8(U[0], U[1], Uh[0], Ul[0]);
+                split8(U[2], U[3], Uh[1], Ul[1]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] *= gq[rt];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = mfma16(Uh[0], pf[rt][0], YT[sl][rt]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = mfma16(Ul[0], pf[rt][0], YT[sl][rt]);
+#pragma unroll
+                for (int rt = 2; rt < 4; ++rt) YT[sl][rt] = mfma16(Uh[1], pf[rt][1], YT[sl][rt]);
+#pragma unroll
+                for (int rt = 2; rt < 4; ++rt) YT[sl][rt] = mfma16(Ul[1], pf[rt][1], YT[sl][rt]);
+            }
+            const int ty = lo + cy * kC, ny = min(kC, hi - ty);
+            Ty* const yc = ylane + (size_t)ty * ytok;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (16 * rt + c16 < ny) {
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) {
+                        Ty* yp = yc + (size_t)(16 * rt) * ytok + 16 * sl;
+                        if constexpr (sizeof(Ty) == 2) {
+                            u32x2 o;
+                            o.x = pack_bf2(YT[sl][rt][0], YT[sl][rt][1]);
+                            o.y = pack_bf2(YT[sl][rt][2], YT[sl][rt][3]);
+                            *reinterpret_cast<u32x2*>(yp) = o;
+                        } else {
+                            *reinterpret_cast<f32x4*>(yp) = YT[sl][rt];
+                        }
+                    }
+                }
+            }
+        };
+        // step c (after its barrier) forms chunk c - 1's y from the exchange buffer the chain
+        // filled and the output slot the loader filled during step c - 1
+        lds_barrier();   // chunk 0 in the ring
+        for (int c = 0; c <= nchunks; ++c) {
+            if (c >= 1) output(c - 1);
+            lds_barrier();
         }
         return;
     }
 
-    // ---------------- compute waves: d_v columns j0w .. j0w + 15
+    // ================= chain waves: d_v columns j0w .. j0w + 15
     const int j0w = j0 + 16 * wave;
-    const int c16 = lane & 15, g = lane >> 4;
     const size_t sbase = ((size_t)seq * a.H + h) * kDK * a.dv;
 
     // state: tile t holds d_k rows relabel(t, 4g + i) of column j0w + c16
@@ -565,7 +674,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     // Per-lane LDS offsets (elements, from the ring slot) of the fragment reads. The swizzle
     // sees only the low 4 bits of a row, so rows 16 or 32 apart and units 8 apart are constant
     // offsets from one of these bases and become immediates of the LDS reads.
-    int okf[2][2], otf[2][2], oqf[2], opf[2], okt[2][2];
+    int okf[2][2], otf[2][2], okt[2][2];
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2) {
         const int r = relabel(a2, c16);
@@ -574,11 +683,6 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
             okf[a2][sp] = kOffK + r * kDK + (((4 * sp + g) ^ swz(r)) << 3);
             otf[a2][sp] = kOffT + r * kC + (((4 * sp + g) ^ swz(r)) << 3);
         }
-    }
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-        oqf[sp] = kOffQ + c16 * kDK + (((4 * sp + g) ^ swz(c16)) << 3);
-        opf[sp] = kOffP + c16 * kC + (((4 * sp + g) ^ swz(c16)) << 3);
     }
     const int jj = (lane & 15) >> 2, r4 = lane & 3;
 #pragma unroll
@@ -589,49 +693,20 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     }
     const int ov = kOffV + (8 * g + jj) * kSl + 16 * wave + 4 * r4;
 
-    // Y^T of the current chunk; a lane holds 4 adjacent d_v of token 16 rt + c16. The lane's
-    // y address is formed once; a chunk adds a wave-uniform offset (64-bit multiplies per
-    // store are quarter-rate VALU work).
-    f32x4 YT[4];
-    const size_t ytok = (size_t)a.H * a.dv;   // elements between consecutive tokens of y
-    Ty* const ylane = static_cast<Ty*>(a.y) + (size_t)h * a.dv + j0w + 4 * g + (size_t)c16 * ytok;
-    auto store_y = [&](int cy) {
-        const int ty = lo + cy * kC, ny = min(kC, hi - ty);
-        Ty* const yc = ylane + (size_t)ty * ytok;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int rp = 16 * rt + c16;
-            if (rp < ny) {
-                Ty* yp = yc + (size_t)(16 * rt) * ytok;
-                if constexpr (sizeof(Ty) == 2) {
-                    u32x2 o;
-                    o.x = pack_bf2(YT[rt][0], YT[rt][1]);
-                    o.y = pack_bf2(YT[rt][2], YT[rt][3]);
-                    *reinterpret_cast<u32x2*>(yp) = o;
-                } else {
-                    *reinterpret_cast<f32x4*>(yp) = YT[rt];
-                }
-            }
-        }
-    };
-
     lds_barrier();   // chunk 0 in the ring
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = lo + c * kC, n = min(kC, hi - t0);
+    for (int c = 0; c <= nchunks; ++c) {
+        if (c == nchunks) {   // the output waves finish the last chunk
+            lds_barrier();
+            break;
+        }
         const uint16_t* slot = ring + (c % kRing) * kSlot;
         const float* sG = reinterpret_cast<const float*>(slot + kOffG);   // beta | gamma | gamma_C/gamma
-        // fragment reads (tile rows relabelled as described above)
+        u32x4* xb = xbuf[c & 1][wave];
         auto kfrag = [&](int rt, int s) {   // A of K S: K[relabel(rt, c16)][32s + 8g ..]
             return frag(slot + okf[rt & 1][s & 1] + (rt >> 1) * 32 * kDK + (s >> 1) * 64);
         };
-        auto qfrag = [&](int rt, int s) {   // B of S^T Q^T: Q[16 rt + c16][32s + 8g ..]
-            return frag(slot + oqf[s & 1] + rt * 16 * kDK + (s >> 1) * 64);
-        };
         auto tfrag = [&](int rt, int s) {   // A of T R: T[relabel(rt, c16)][32s + 8g ..]
             return frag(slot + otf[rt & 1][s] + (rt >> 1) * 32 * kC);
-        };
-        auto pfrag = [&](int rt, int s) {   // B of U^T P^T: P[16 rt + c16][32s + 8g ..]
-            return frag(slot + opf[s] + rt * 16 * kC);
         };
         auto ktr = [&](int t, int s, int hf) {   // K^T[relabel(t, c16)][32s + 8g + 4hf ..]
             return lds_tr16(slot + okt[hf][(t >> 1) & 1] + s * 32 * kDK + (t >> 2) * 64 + 4 * (t & 1));
@@ -640,75 +715,73 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
             return *reinterpret_cast<const f32x4*>(sG + which * kC + 8 * g + 32 * (rt >> 1) + 4 * (rt & 1));
         };
 
-        // The MFMA chain of a chunk is K S -> R -> U = T R -> W -> S update; the fp32 -> bf16
-        // splits and gate scalings between its links are VALU work, and every operand comes
-        // from LDS. Each block below is one scheduling region whose MFMAs are interleaved with
-        // VALU work that does not feed them and with the LDS reads of later regions; Y^T's
-        // products and the gamma_C scaling of S, which are off the chain, fill the gaps.
-        bf16x8 kf[4][4], qf[4][4];
+        // The chain K S -> R -> U = T R -> W -> S update; the fp32 -> bf16 splits and gate
+        // scalings between its links are VALU work. Each block is one scheduling region whose
+        // MFMAs are interleaved with VALU work that does not feed them and with the LDS reads
+        // of later regions.
+        bf16x8 kf[4][4];
         f32x4 KS[4];
         auto mma_k = [&](int s) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) KS[rt] = mfma16(kf[s][rt], Sb[s], KS[rt]);
         };
-        auto mma_q = [&](int s) {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Sb[s], qf[s][rt], YT[rt]);
-        };
         auto load_k = [&](int s) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) kf[s][rt] = kfrag(rt, s);
-        };
-        auto load_q = [&](int s) {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) qf[s][rt] = qfrag(rt, s);
         };
         load_k(0);
         load_k(1);
         const float gC = sG[kC + kC - 1];
         GDN_SCHED_FENCE();
-        // ---- K S step 0 | gamma_C S (tiles 0-3) | K fragments of steps 2-3
+        // ---- K S step 0 | the state operand to the output waves | gamma_C S (tiles 0-3) |
+        //      K fragments of steps 2-3
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            KS[rt] = f32x4{};
-            YT[rt] = f32x4{};
-        }
+        for (int rt = 0; rt < 4; ++rt) KS[rt] = f32x4{};
         mma_k(0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xb[s * 64 + lane] = __builtin_bit_cast(u32x4, Sb[s]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) S[t] *= gC;
         load_k(2);
         load_k(3);
         GDN_IGLP(4, 4, 2);
         GDN_SCHED_FENCE();
-        // ---- K S step 1 | gamma_C S (tiles 4-7) | Q fragments of steps 0-1
+        // ---- K S step 1 | gamma_C S (tiles 4-7) | gate rows and V at the lane's tokens
+        f32x4 bet[4], gam[4];
+        s16x4 vv[4];
         mma_k(1);
 #pragma unroll
         for (int t = 4; t < 8; ++t) S[t] *= gC;
-        load_q(0);
-        load_q(1);
-        GDN_IGLP(4, 4, 2);
-        GDN_SCHED_FENCE();
-        // ---- K S step 2 | gate rows and V at the lane's tokens
-        f32x4 bet[4], gam[4];
-        s16x4 vv[4];
-        mma_k(2);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             bet[rt] = grow(0, rt);
             gam[rt] = grow(1, rt);
             vv[rt] = lds_tr16(slot + ov + (32 * (rt >> 1) + 4 * (rt & 1)) * kSl);
         }
-        GDN_IGLP(4, 1, 3);
+        GDN_IGLP(4, 4, 3);
         GDN_SCHED_FENCE();
-        // ---- K S step 3 | Q fragments of steps 2-3
-        mma_k(3);
-        load_q(2);
-        load_q(3);
-        GDN_IGLP(4, 1, 2);
-        GDN_SCHED_FENCE();
-        // ---- R = beta (V - gamma KS) and its split | S^T Q^T (all steps) | T fragments, gd
+        // ---- K S steps 2-3 | T fragments, gamma_C / gamma
         bf16x8 tf[4][2];
         f32x4 gd[4];
+        mma_k(2);
+        mma_k(3);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (s <= (rt >> 1)) tf[rt][s] = tfrag(rt, s);
+            gd[rt] = grow(2, rt);
+        }
+        GDN_IGLP(8, 1, 2);
+        GDN_SCHED_FENCE();
+        // ---- R = beta (V - gamma KS) and its split | K^T fragments of tiles 0-1
+        s16x4 kt[8][2][2];   // K^T fragments [d_k tile][step][half]
+        auto load_kt = [&](int t) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) kt[t][s][hf] = ktr(t, s, hf);
+        };
         f32x4 R[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -718,28 +791,11 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         bf16x8 Rh[2], Rl[2];
         split8(R[0], R[1], Rh[0], Rl[0]);
         split8(R[2], R[3], Rh[1], Rl[1]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) mma_q(s);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s <= (rt >> 1)) tf[rt][s] = tfrag(rt, s);
-            gd[rt] = grow(2, rt);
-        }
-        GDN_IGLP(16, 6, 1);
+        load_kt(0);
+        load_kt(1);
         GDN_SCHED_FENCE();
         // ---- U = T R (T unit lower triangular: token rows < 32 need step 0 only) |
-        //      gamma (S^T Q^T) | P fragments, gamma at Y's tokens, K^T fragments of tiles 0-1
-        bf16x8 pf[4][2];
-        float gq[4];
-        s16x4 kt[8][2][2];   // K^T fragments [d_k tile][step][half]
-        auto load_kt = [&](int t) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) kt[t][s][hf] = ktr(t, s, hf);
-        };
+        //      K^T fragments of tiles 2-3
         f32x4 U[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) U[rt] = f32x4{};
@@ -751,31 +807,24 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rh[1], U[rt]);
 #pragma unroll
         for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rl[1], U[rt]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s <= (rt >> 1)) pf[rt][s] = pfrag(rt, s);
-            gq[rt] = sG[kC + 16 * rt + c16];
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) YT[rt] *= gq[rt];
-        load_kt(0);
-        load_kt(1);
-        GDN_IGLP(12, 2, 2);
-        GDN_SCHED_FENCE();
-        // ---- W = diag(gamma_C / gamma) U and its split | K^T fragments of tiles 2-3
-        bf16x8 Wh[2], Wl[2];
-        f32x4 Wf[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) Wf[rt] = U[rt] * gd[rt];
-        split8(Wf[0], Wf[1], Wh[0], Wl[0]);
-        split8(Wf[2], Wf[3], Wh[1], Wl[1]);
         load_kt(2);
         load_kt(3);
+        GDN_IGLP(12, 1, 1);
         GDN_SCHED_FENCE();
-        // ---- S = gamma_C S + K^T W (tiles 0-3) | U's split, finished S pairs split |
-        //      K^T fragments of tiles 4-7
+        // ---- U to the output waves | W = diag(gamma_C / gamma) U and its split |
+        //      K^T fragments of tiles 4-5
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) xb[(4 + rt) * 64 + lane] = __builtin_bit_cast(u32x4, U[rt]);
+        bf16x8 Wh[2], Wl[2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] *= gd[rt];
+        split8(U[0], U[1], Wh[0], Wl[0]);
+        split8(U[2], U[3], Wh[1], Wl[1]);
+        load_kt(4);
+        load_kt(5);
+        GDN_SCHED_FENCE();
+        // ---- S = gamma_C S + K^T W, each finished pair of tiles split for the next chunk |
+        //      K^T fragments of tiles 6-7
         auto upd = [&](int t) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -788,32 +837,17 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
             }
             if (t & 1) Sb[t >> 1] = to_bf16x8(S[t - 1], S[t]);
         };
-        bf16x8 Uh[2], Ul[2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) upd(t);
-        split8(U[0], U[1], Uh[0], Ul[0]);
-        split8(U[2], U[3], Uh[1], Ul[1]);
-        load_kt(4);
-        load_kt(5);
         load_kt(6);
         load_kt(7);
-        GDN_IGLP(16, 4, 1);
+        GDN_IGLP(16, 2, 1);
         GDN_SCHED_FENCE();
-        // ---- S update (tiles 4-7) | Y^T += U^T P^T (P lower triangular)
 #pragma unroll
         for (int t = 4; t < 8; ++t) upd(t);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Uh[0], pf[rt][0], YT[rt]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Ul[0], pf[rt][0], YT[rt]);
-#pragma unroll
-        for (int rt = 2; rt < 4; ++rt) YT[rt] = mfma16(Uh[1], pf[rt][1], YT[rt]);
-#pragma unroll
-        for (int rt = 2; rt < 4; ++rt) YT[rt] = mfma16(Ul[1], pf[rt][1], YT[rt]);
-        GDN_IGLP(28, 1, 0);
+        GDN_IGLP(16, 1, 0);
         GDN_SCHED_FENCE();
-        store_y(c);
-        lds_barrier();   // past this barrier the loaders refill this slot
+        lds_barrier();   // past this barrier the ring slot is refilled and xb is read
     }
     if (a.ST) {
 #pragma unroll
