@@ -135,26 +135,6 @@ __device__ __forceinline__ void fetch_gates(const DevArgs& a, int t0, int n, int
     bv = a.beta[base + r * a.H];
 }
 
-// Wave 0: running sum of g over the chunk (rows >= n contribute 0), written with beta.
-__device__ __forceinline__ void chunk_gates(float gv, float bv, int n, float* sG, float* sB,
-                                            float* sGam, float* sGd) {
-    const int lane = threadIdx.x;
-    if (lane >= n) {
-        gv = 0.f;
-        bv = 0.f;
-    }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const float o = __shfl_up(gv, off, kWave);
-        if (lane >= off) gv += o;
-    }
-    const float gC = __shfl(gv, kC - 1, kWave);
-    sG[lane] = gv;
-    sB[lane] = bv;
-    if (sGam) sGam[lane] = fexp(gv);
-    if (sGd) sGd[lane] = fexp(gC - gv);
-}
-
 // chunk index -> (sequence, first token, length)
 __device__ __forceinline__ bool chunk_of(const DevArgs& a, int chunk, int& seq, int& t0, int& n) {
     if (!a.cu) {
@@ -184,13 +164,54 @@ __device__ __forceinline__ bool chunk_of(const DevArgs& a, int chunk, int& seq, 
 // One wave per (chunk, head). The MFMA operands of K K^T and Q K^T are read from global
 // memory straight into registers in fragment layout (a lane's 8 consecutive d_k of one row
 // are one 16-byte load), so only the fp32 A matrix lives in LDS and eight chunk-heads share
-// a CU: while one wave waits on its loads or on the forward substitution (a lane per column
-// of T), the other wave on its SIMD issues.
+// a CU. T = (I + A)^{-1} (A strictly lower triangular) is built in three levels:
+//   (1) the four 16x16 diagonal blocks by forward substitution in registers: lane (b, c)
+//       owns column c of block b, and the entry A[r][i] it needs is broadcast from lane
+//       (b, i) of its 16-lane row by DPP (row_newbcast), so no LDS traffic;
+//   (2) 16 -> 32: T_10 = -T_11 (A_10 T_00) for the blocks (1,0) and (3,2), on the fp32
+//       matrix cores (v_mfma_f32_16x16x4_f32);
+//   (3) 32 -> 64: the same with 32x32 blocks (v_mfma_f32_32x32x2_f32).
+// T and P leave through LDS as fp32 rows converted to bf16 with 16-byte global stores.
 constexpr int kPrepThreads = kWave;
+
+typedef float f32x4p __attribute__((ext_vector_type(4)));
+
+template <int I> __device__ __forceinline__ float row_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + I, 0xF, 0xF, false));
+}
+// lane i of the caller's 16-lane row (i a compile-time constant after unrolling)
+__device__ __forceinline__ float row_bcast(int i, float v) {
+    switch (i) {
+        case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
+        case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
+        case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
+        case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
+        case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
+        case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
+        case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
+        case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
+    }
+}
+
+// [64][64] fp32 tile in LDS (row stride kStrA) -> bf16 rows in global memory
+__device__ __forceinline__ void store_tile_bf16(const float* src, uint16_t* dst, int lane) {
+#pragma unroll
+    for (int it = 0; it < kC * kC / 8 / kWave; ++it) {
+        const int e = (lane + kWave * it) * 8, r = e / kC, c0 = e % kC;
+        const f32x4p x0 = *reinterpret_cast<const f32x4p*>(src + r * kStrA + c0);
+        const f32x4p x1 = *reinterpret_cast<const f32x4p*>(src + r * kStrA + c0 + 4);
+        u32x4 o;
+        o.x = pack_bf2(x0[0], x0[1]);
+        o.y = pack_bf2(x0[2], x0[3]);
+        o.z = pack_bf2(x1[0], x1[1]);
+        o.w = pack_bf2(x1[2], x1[3]);
+        *reinterpret_cast<u32x4*>(dst + e) = o;
+    }
+}
 
 __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
-    __shared__ float sG[kC], sB[kC];
+    __shared__ __attribute__((aligned(16))) float sG[kC], sB[kC];
 
     const int chunk = blockIdx.x, h = blockIdx.y;
     int seq, t0, n;
@@ -214,8 +235,8 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     float gv, bv;
     fetch_gates(a, t0, n, h, gv, bv);
     {
-        // the chunk's beta, gamma_r = e^{G_r} and gamma_C / gamma_r for the scan
-        float* gw = a.Gw + ((size_t)chunk * a.H + h) * 3 * kC;
+        // running sum G of g over the chunk (rows >= n add nothing), and the chunk's beta,
+        // gamma_r = e^{G_r} and gamma_C / gamma_r for the scan
         float Gr = lane < n ? gv : 0.f;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
@@ -223,11 +244,14 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
             if (lane >= off) Gr += o;
         }
         const float GC = __shfl(Gr, kC - 1, kWave);
-        gw[lane] = lane < n ? bv : 0.f;
+        const float br = lane < n ? bv : 0.f;
+        float* gw = a.Gw + ((size_t)chunk * a.H + h) * 3 * kC;
+        gw[lane] = br;
         gw[kC + lane] = fexp(Gr);
         gw[2 * kC + lane] = fexp(GC - Gr);
+        sG[lane] = Gr;
+        sB[lane] = br;
     }
-    chunk_gates(gv, bv, n, sG, sB, nullptr, nullptr);
     const u32x4 z = {0u, 0u, 0u, 0u};
     const bool v0 = r0 < n, v1 = r1 < n;
 
@@ -253,42 +277,90 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     }
     __syncthreads();   // gates visible
 
-    const size_t tile = ((size_t)chunk * a.H + h) * kC * kC;
+    // A[r][c] = beta_r e^{G_r - G_c} (k_r . k_c) for c < r, else 0 (fp32, to LDS);
+    // P[r][c] = e^{G_r - G_c} (q_r . k_c) for c <= r (kept in registers).
+    // Accumulator element i of lane l is row R0 + 8(i/4) + 4(l/32) + i%4 of column C0 + l%32,
+    // so a lane's rows come in 4 runs of 4: the gates of each run are one 16-byte read.
+    {
+        f32x4p Grow[2][4], Brow[2][4];
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-        const int R0 = t == 0 ? 0 : 32, C0 = t == 2 ? 32 : 0;
-        const int c = C0 + (lane & 31);
-        const float Gc = sG[c];
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = R0 + acc_row(i, lane);
-            const float dec = c <= r ? fexp(sG[r] - Gc) : 0.f;
-            sA[r * kStrA + c] = c < r ? sB[r] * dec * ckk[t][i] : 0.f;
-            cqk[t][i] *= dec;   // P, written out after T
+            for (int q = 0; q < 4; ++q) {
+                const int r = 32 * rb + 8 * q + 4 * (lane >> 5);
+                Grow[rb][q] = *reinterpret_cast<const f32x4p*>(sG + r);
+                Brow[rb][q] = *reinterpret_cast<const f32x4p*>(sB + r);
+            }
+        const float Gcol[2] = {sG[lane & 31], sG[32 + (lane & 31)]};
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int rb = t == 0 ? 0 : 1, cb = t == 2 ? 1 : 0;
+            const int c = 32 * cb + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int q = i >> 2, e = i & 3;
+                const int r = 32 * rb + 8 * q + 4 * (lane >> 5) + e;
+                const float dec = c <= r ? fexp(Grow[rb][q][e] - Gcol[cb]) : 0.f;
+                sA[r * kStrA + c] = c < r ? Brow[rb][q][e] * dec * ckk[t][i] : 0.f;
+                cqk[t][i] *= dec;
+            }
+        }
+        // the upper-right block of A is zero
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sA[acc_row(i, lane) * kStrA + 32 + (lane & 31)] = 0.f;
+    }
+    __syncthreads();
+
+    // (1) the 16x16 diagonal blocks: lane (b, c) owns column c of block b
+    {
+        const int b = lane >> 4, c = lane & 15, d0 = 16 * b;
+        float Acol[16], t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Acol[r] = sA[(d0 + r) * kStrA + d0 + c];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc[4] = {r == c ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc[i & 3] -= row_bcast(i, Acol[r]) * t[i];
+            t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        }
+        __syncthreads();   // every lane has read its column of A
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sA[(d0 + r) * kStrA + d0 + c] = t[r];
+    }
+    __syncthreads();
+    // (2) 16 -> 32: for the blocks (1,0) and (3,2), Y = A_10 T_00 then T_10 = -T_11 Y, on
+    //     v_mfma_f32_16x16x4_f32 (lane (c, g) supplies A[c][4k + g] and B[4k + g][c]; the
+    //     accumulator holds C[4g + i][c]). Y goes through the block itself (A_10 is dead).
+    {
+        const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int o0 = 32 * p, o1 = 32 * p + 16;   // block rows / columns of T_00 and T_11
+            f32x4p Y = {};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                Y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(o1 + c) * kStrA + o0 + 4 * kk + g],
+                                                         sA[(o0 + 4 * kk + g) * kStrA + o0 + c], Y, 0, 0, 0);
+            __syncthreads();   // all reads of A_10 done
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sA[(o1 + 4 * g + i) * kStrA + o0 + c] = Y[i];
+            __syncthreads();
+            f32x4p T10 = {};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                T10 = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(o1 + c) * kStrA + o1 + 4 * kk + g],
+                                                           sA[(o1 + 4 * kk + g) * kStrA + o0 + c], T10, 0, 0, 0);
+            __syncthreads();   // all reads of Y done
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sA[(o1 + 4 * g + i) * kStrA + o0 + c] = -T10[i];
         }
     }
     __syncthreads();
-    // T = (I + A)^{-1} in 32x32 blocks: T = [[T0, 0], [T10, T1]] with T0 = (I + A00)^{-1},
-    // T1 = (I + A11)^{-1}, T10 = -T1 A10 T0.
-    // (1) the two diagonal inverses by forward substitution, one half-wave each, a lane per
-    //     column (4 partial sums per row);
-    const int half = lane >> 5, c = lane & 31, off = 32 * half;
-    float t[32];
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        const float* Ar = sA + (off + r) * kStrA + off;
-        float acc[4] = {r == c ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < r; ++i) acc[i & 3] -= Ar[i] * t[i];
-        t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    }
-    __syncthreads();   // all reads of A00 and A11 done: T0 and T1 take their place
-#pragma unroll
-    for (int r = 0; r < 32; ++r) sA[(off + r) * kStrA + off + c] = t[r];
-    __syncthreads();
-    // (2) X = A10 T0 and T10 = -T1 X on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: lane l
-    //     supplies A[l%32][l/32] and B[l/32][l%32] of each k-pair); X goes through the unused
+    // (3) 32 -> 64: X = A10 T0 and T10 = -T1 X on v_mfma_f32_32x32x2_f32 (lane l supplies
+    //     A[l%32][l/32] and B[l/32][l%32] of each k-pair); X goes through the unused
     //     upper-right block of the tile.
+    const int half = lane >> 5, c = lane & 31;
     f32x16 X = {};
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) {
@@ -305,37 +377,26 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
         T10 = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(32 + c) * kStrA + 32 + k], sA[k * kStrA + 32 + c],
                                                   T10, 0, 0, 0);
     }
-    // (3) T and P as bf16 tiles, assembled in LDS (the A matrix is dead now) and written as
-    //     whole 128-byte rows. T's upper-right block is never read; it is zero.
+    __syncthreads();   // all reads of A10 and X done
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        sA[(32 + acc_row(i, lane)) * kStrA + c] = -T10[i];
+        sA[acc_row(i, lane) * kStrA + 32 + c] = 0.f;   // T's upper-right block
+    }
     __syncthreads();
-    uint16_t* sH = reinterpret_cast<uint16_t*>(sA);   // [64][64]
-    auto put = [&](int r, int cc, float v) { sH[r * kC + cc] = f2bf(v); };
-    auto flush = [&](uint16_t* dh) {
-        __syncthreads();
+    const size_t tile = ((size_t)chunk * a.H + h) * kC * kC;
+    store_tile_bf16(sA, a.Tw + tile, lane);
+    __syncthreads();   // T read out: P takes its place
 #pragma unroll
-        for (int it = 0; it < kC * kC / 8 / kWave; ++it) {
-            const int e = (lane + kWave * it) * 8;
-            *reinterpret_cast<u32x4*>(dh + tile + e) = *reinterpret_cast<const u32x4*>(sH + e);
-        }
-        __syncthreads();
-    };
+    for (int t = 0; t < 3; ++t) {
+        const int R0 = t == 0 ? 0 : 32, C0 = t == 2 ? 32 : 0;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        put(off + r, off + c, t[r]);
-        put(r, 32 + c, 0.f);
+        for (int i = 0; i < 16; ++i) sA[(R0 + acc_row(i, lane)) * kStrA + C0 + c] = cqk[t][i];
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) put(32 + acc_row(i, lane), c, -T10[i]);
-    flush(a.Tw);
-#pragma unroll
-    for (int tt = 0; tt < 3; ++tt) {
-        const int R0 = tt == 0 ? 0 : 32, C0 = tt == 2 ? 32 : 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) put(R0 + acc_row(i, lane), C0 + c, cqk[tt][i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) put(acc_row(i, lane), 32 + c, 0.f);
-    flush(a.Pw);
+    for (int i = 0; i < 16; ++i) sA[acc_row(i, lane) * kStrA + 32 + c] = 0.f;
+    __syncthreads();
+    store_tile_bf16(sA, a.Pw + tile, lane);
 }
 
 // ------------------------------------------------------------------ sequential chunk scan

@@ -16,7 +16,7 @@ namespace gdn {
 
 constexpr int kPreThreads = 256;
 constexpr int kPreTile = kPreThreads * 8;   // channels per workgroup
-constexpr int kPreTokens = 32;              // tokens per workgroup (3-token conv halo)
+constexpr int kPreTokens = 64;              // tokens per workgroup (3-token conv halo)
 constexpr int kConvK = 4;
 constexpr int kPreGroup = 4;                // tokens loaded together
 
