@@ -55,6 +55,9 @@ CASES = [
     (1, dict(B=2, H=3, T=200), "bf16"),
     (1, dict(B=1, H=2, T=70, d=64), "f32"),
     (2, dict(H=2, T=1000), "f32"),
+    # d_k = 128, d_v = 64 on the matrix-core path: two 32-column slices per head
+    (1, dict(B=2, H=2, T=150, dv=64), "bf16"),
+    (2, dict(H=3, T=330, dv=64), "f32"),
     (4, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130]), "f32"),
     (4, dict(H=2, nseq=5, lmax=600), "bf16"),
 ]
