@@ -684,6 +684,9 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
 #pragma unroll
                 for (int rt = 2; rt < 4; ++rt) YT[sl][rt] = mfma16(Ul[1], pf[rt][1], YT[sl][rt]);
             }
+            // y is written once and never read here: streaming (nontemporal) stores keep its
+            // lines from displacing the q, k, T and P lines the head's other slices still read
+            // from the shared L2
             const int ty = lo + cy * kC, ny = min(kC, hi - ty);
             Ty* const yc = ylane + (size_t)ty * ytok;
 #pragma unroll
@@ -696,9 +699,9 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
                             u32x2 o;
                             o.x = pack_bf2(YT[sl][rt][0], YT[sl][rt][1]);
                             o.y = pack_bf2(YT[sl][rt][2], YT[sl][rt][3]);
-                            *reinterpret_cast<u32x2*>(yp) = o;
+                            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(yp));
                         } else {
-                            *reinterpret_cast<f32x4*>(yp) = YT[sl][rt];
+                            __builtin_nontemporal_store(YT[sl][rt], reinterpret_cast<f32x4*>(yp));
                         }
                     }
                 }

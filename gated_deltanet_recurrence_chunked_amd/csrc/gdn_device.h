@@ -28,39 +28,61 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 }
 
 // --------------------------------------------------------------------------- typed 8-wide IO
-// Element type tags: float (fp32) or uint16_t (bf16 bits).
+// Element type tags: float (fp32) or uint16_t (bf16 bits). The *_stream forms use
+// nontemporal accesses, for data a kernel touches exactly once: such lines then do not
+// displace the lines that the next kernel of the pipeline reads back (the outputs just
+// written stay cached for their consumer).
+typedef uint32_t gdn_u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kStream> __device__ __forceinline__ gdn_u32x4 ld16(const void* p) {
+    const gdn_u32x4* q = reinterpret_cast<const gdn_u32x4*>(p);
+    if constexpr (kStream) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+template <bool kStream> __device__ __forceinline__ void st16(void* p, const gdn_u32x4& v) {
+    gdn_u32x4* q = reinterpret_cast<gdn_u32x4*>(p);
+    if constexpr (kStream) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
 template <typename T> struct Vec8;
 
 template <> struct Vec8<float> {
+    template <bool kStream = false>
     static __device__ __forceinline__ void load(const float* p, float (&x)[8]) {
-        const float4 a = reinterpret_cast<const float4*>(p)[0];
-        const float4 b = reinterpret_cast<const float4*>(p)[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        const gdn_u32x4 a = ld16<kStream>(p), b = ld16<kStream>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = __uint_as_float(a[i]);
+            x[4 + i] = __uint_as_float(b[i]);
+        }
     }
+    template <bool kStream = false>
     static __device__ __forceinline__ void store(float* p, const float (&x)[8]) {
-        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+        const gdn_u32x4 a = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                             __float_as_uint(x[3])};
+        const gdn_u32x4 b = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]),
+                             __float_as_uint(x[7])};
+        st16<kStream>(p, a);
+        st16<kStream>(p + 4, b);
     }
 };
 
 template <> struct Vec8<uint16_t> {
+    template <bool kStream = false>
     static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        const gdn_u32x4 a = ld16<kStream>(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            x[2 * i] = __uint_as_float(a[i] << 16);
+            x[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
         }
     }
+    template <bool kStream = false>
     static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[8]) {
-        uint4 a;
-        a.x = pack_bf2(x[0], x[1]);
-        a.y = pack_bf2(x[2], x[3]);
-        a.z = pack_bf2(x[4], x[5]);
-        a.w = pack_bf2(x[6], x[7]);
-        *reinterpret_cast<uint4*>(p) = a;
+        const gdn_u32x4 a = {pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]),
+                             pack_bf2(x[6], x[7])};
+        st16<kStream>(p, a);
     }
 };
 

@@ -84,11 +84,14 @@ __device__ void conv_stream(const PreprocessArgs& a, int role, int tile, int t0)
     }
 
     // four tokens per step: their loads are issued together, so each thread keeps four
-    // 16-byte requests in flight (the window recurrence runs on registers afterwards)
+    // 16-byte requests in flight (the window recurrence runs on registers afterwards). These
+    // rows are read once (the next workgroup's 3-token history aside), so they stream past
+    // the caches and leave them to q, k, v, which the prefill reads next.
     for (int tb = t0; tb < t1; tb += kPreGroup) {
         float grp[kPreGroup][8];
 #pragma unroll
-        for (int j = 0; j < kPreGroup; ++j) Vec8<Tin>::load(x + (size_t)min(tb + j, t1 - 1) * C + c, grp[j]);
+        for (int j = 0; j < kPreGroup; ++j)
+            Vec8<Tin>::template load<true>(x + (size_t)min(tb + j, t1 - 1) * C + c, grp[j]);
 #pragma unroll
         for (int j = 0; j < kPreGroup; ++j) {
             const int t = tb + j;
@@ -193,7 +196,8 @@ output_gate_kernel(const Ty* __restrict__ y, const Tz* __restrict__ z, const flo
     float gain[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) gain[i] = 1.0f + w[lane_c + i];
-    // two row groups per step, so four 16-byte loads per thread are in flight together
+    // two row groups per step, so four 16-byte loads per thread are in flight together; z and
+    // o are touched once and stream past the caches, y (just written by the prefill) does not
     const long stride = (long)gridDim.x * RPB;
     for (long r0 = (long)blockIdx.x * RPB + threadIdx.x / LPR; r0 < rows; r0 += 2 * stride) {
         const long r1 = r0 + stride;
@@ -201,9 +205,9 @@ output_gate_kernel(const Ty* __restrict__ y, const Tz* __restrict__ z, const flo
         const size_t off1 = (size_t)(r1 < rows ? r1 : r0) * DV + lane_c;
         float yv[2][8], zv[2][8];
         Vec8<Ty>::load(y + off0, yv[0]);
-        Vec8<Tz>::load(z + off0, zv[0]);
+        Vec8<Tz>::template load<true>(z + off0, zv[0]);
         Vec8<Ty>::load(y + off1, yv[1]);
-        Vec8<Tz>::load(z + off1, zv[1]);
+        Vec8<Tz>::template load<true>(z + off1, zv[1]);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             float ss = 0.f;
@@ -214,7 +218,7 @@ output_gate_kernel(const Ty* __restrict__ y, const Tz* __restrict__ z, const flo
             float ov[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) ov[i] = sigmoidf_(zv[u][i]) * (gain[i] * (yv[u][i] * inv));
-            if (u == 0 || r1 < rows) Vec8<To>::store(o + (u ? off1 : off0), ov);
+            if (u == 0 || r1 < rows) Vec8<To>::template store<true>(o + (u ? off1 : off0), ov);
         }
     }
 }
