@@ -48,6 +48,20 @@ template <bool kStream> __device__ __forceinline__ void st16(void* p, const gdn_
 template <typename T> struct Vec8;
 
 template <> struct Vec8<float> {
+    struct Raw {
+        gdn_u32x4 a, b;
+    };
+    template <bool kStream = false>
+    static __device__ __forceinline__ Raw load_raw(const float* p) {
+        return Raw{ld16<kStream>(p), ld16<kStream>(p + 4)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&x)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = __uint_as_float(r.a[i]);
+            x[4 + i] = __uint_as_float(r.b[i]);
+        }
+    }
     template <bool kStream = false>
     static __device__ __forceinline__ void load(const float* p, float (&x)[8]) {
         const gdn_u32x4 a = ld16<kStream>(p), b = ld16<kStream>(p + 4);
@@ -69,6 +83,20 @@ template <> struct Vec8<float> {
 };
 
 template <> struct Vec8<uint16_t> {
+    struct Raw {
+        gdn_u32x4 a;
+    };
+    template <bool kStream = false>
+    static __device__ __forceinline__ Raw load_raw(const uint16_t* p) {
+        return Raw{ld16<kStream>(p)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&x)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(r.a[i] << 16);
+            x[2 * i + 1] = __uint_as_float(r.a[i] & 0xffff0000u);
+        }
+    }
     template <bool kStream = false>
     static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
         const gdn_u32x4 a = ld16<kStream>(p);

@@ -18,7 +18,7 @@ constexpr int kPreThreads = 256;
 constexpr int kPreTile = kPreThreads * 8;   // channels per workgroup
 constexpr int kPreTokens = 64;              // tokens per workgroup (3-token conv halo)
 constexpr int kConvK = 4;
-constexpr int kPreGroup = 4;                // tokens loaded together
+constexpr int kPreGroup = 2;                // tokens per step (loaded one step ahead)
 
 struct PreKernelArgs {
     PreprocessArgs a;
@@ -83,15 +83,22 @@ __device__ void conv_stream(const PreprocessArgs& a, int role, int tile, int t0)
         }
     }
 
-    // four tokens per step: their loads are issued together, so each thread keeps four
-    // 16-byte requests in flight (the window recurrence runs on registers afterwards). These
+    // kPreGroup tokens per step, software-pipelined: the next step's rows are loaded while
+    // this step's conv / SiLU / L2Norm runs (the window recurrence runs on registers). These
     // rows are read once (the next workgroup's 3-token history aside), so they stream past
     // the caches and leave them to q, k, v, which the prefill reads next.
+    typename Vec8<Tin>::Raw nxt[kPreGroup];
+    auto issue = [&](int tb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kPreGroup; ++j)
+            nxt[j] = Vec8<Tin>::template load_raw<true>(x + (size_t)min(tb + j, t1 - 1) * C + c);
+    };
+    issue(t0);
     for (int tb = t0; tb < t1; tb += kPreGroup) {
         float grp[kPreGroup][8];
 #pragma unroll
-        for (int j = 0; j < kPreGroup; ++j)
-            Vec8<Tin>::template load<true>(x + (size_t)min(tb + j, t1 - 1) * C + c, grp[j]);
+        for (int j = 0; j < kPreGroup; ++j) Vec8<Tin>::unpack(nxt[j], grp[j]);
+        if (tb + kPreGroup < t1) issue(tb + kPreGroup);   // the next group loads under this one's math
 #pragma unroll
         for (int j = 0; j < kPreGroup; ++j) {
             const int t = tb + j;
@@ -198,9 +205,10 @@ output_gate_kernel(const Ty* __restrict__ y, const Tz* __restrict__ z, const flo
     for (int i = 0; i < 8; ++i) gain[i] = 1.0f + w[lane_c + i];
     // two row groups per step, so four 16-byte loads per thread are in flight together; z and
     // o are touched once and stream past the caches, y (just written by the prefill) does not
-    const long stride = (long)gridDim.x * RPB;
-    for (long r0 = (long)blockIdx.x * RPB + threadIdx.x / LPR; r0 < rows; r0 += 2 * stride) {
-        const long r1 = r0 + stride;
+    const long tiles = (rows + 2 * RPB - 1) / (2 * RPB);   // 2 RPB rows per workgroup tile
+    for (long bt = blockIdx.x; bt < tiles; bt += gridDim.x) {
+        const long r0 = bt * 2 * RPB + threadIdx.x / LPR, r1 = r0 + RPB;
+        if (r0 >= rows) break;
         const size_t off0 = (size_t)r0 * DV + lane_c;
         const size_t off1 = (size_t)(r1 < rows ? r1 : r0) * DV + lane_c;
         float yv[2][8], zv[2][8];
@@ -227,7 +235,7 @@ template <int DV>
 static void launch_gate_dv(const void* y, int yb, const void* z, int zb, const float* w, long rows,
                            float eps, void* o, int ob, hipStream_t s) {
     constexpr int RPB = kGateThreads / (DV / 8);
-    long blocks = (rows + RPB - 1) / RPB;
+    long blocks = (rows + 2 * RPB - 1) / (2 * RPB);
     int grid = (int)(blocks < 16384 ? blocks : 16384);
 #define GDN_GATE(TY, TZ, TO)                                                                 \
     hipLaunchKernelGGL((output_gate_kernel<TY, TZ, TO, DV>), dim3(grid), dim3(kGateThreads), 0, s, \
