@@ -9,7 +9,8 @@ Architecture", section 2.1.1: eqs. (1)-(5) for the recurrence, eqs. (6)-(10) for
 the pre-processing and gates, eq. (11) (without W_o) for the output gate; the
 C source states the passage per function.
 
-Parity status: the recurrence, conv, SiLU, L2Norm, gates and output gate are all
+Parity status: the recurrence, conv (with and without a carried history), SiLU, L2Norm,
+gates and output gate are all
 pinned by the CPU tests (closed forms, invariants, exact-rational brute force,
 library routines). The conventions the pages leave open (conv tap order, the
 epsilons, RMSNorm scope) are pinned only by the stated readings.
@@ -53,6 +54,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.gdn_oracle_short_conv.argtypes = [_dp, _dp, ctypes.c_int, _ip, ctypes.c_int,
                                               ctypes.c_int, _dp]
+        lib.gdn_oracle_short_conv_hist.argtypes = [_dp, _dp, ctypes.c_int, _ip, ctypes.c_int,
+                                                   ctypes.c_int, _dp, _dp, _dp]
         lib.gdn_oracle_silu.argtypes = [_dp, ctypes.c_long, _dp]
         lib.gdn_oracle_l2norm.argtypes = [_dp, ctypes.c_long, ctypes.c_int, ctypes.c_double, _dp]
         lib.gdn_oracle_gates.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_int,
@@ -93,6 +96,25 @@ def short_conv(x, w, cu_seqlens):
     _load().gdn_oracle_short_conv(_p(x), _p(w), w.shape[1], cu.ctypes.data_as(_ip),
                                   len(cu) - 1, C, _p(u))
     return u
+
+
+def short_conv_hist(x, w, cu_seqlens, hist_in=None):
+    """ShortConv continuing earlier input: x: [ntok, C]; w: [C, K]; hist_in: [nseq, K-1, C]
+    (row K-2 = the input just before each sequence start) or None (zero history).
+    Returns (u [ntok, C], hist_out [nseq, K-1, C]): hist_out holds the last K-1 inputs of
+    history + sequence, ready to be the next call's hist_in."""
+    x = _d(x)
+    w = _d(w)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ntok, C = x.shape
+    K = w.shape[1]
+    nseq = len(cu) - 1
+    hin = None if hist_in is None else _d(hist_in)
+    u = np.empty_like(x)
+    hout = np.empty((nseq, K - 1, C))
+    _load().gdn_oracle_short_conv_hist(_p(x), _p(w), K, cu.ctypes.data_as(_ip), nseq, C,
+                                       _p(hin), _p(u), _p(hout))
+    return u, hout
 
 
 def silu(u):
@@ -181,6 +203,25 @@ def preprocess(xq, xk, xv, wq, wk, wv, cu_seqlens, H, l2_eps=L2_EPS):
         return l2norm(a, l2_eps) if norm else a
 
     return stream(xq, wq, True), stream(xk, wk, True), stream(xv, wv, False)
+
+
+def preprocess_stateful(xq, xk, xv, wq, wk, wv, cu_seqlens, H, conv_state_in=None,
+                        l2_eps=L2_EPS):
+    """eqs. 6-8 for sequences that continue earlier input. conv_state_in: [nseq, K-1, C_all]
+    or None, with C_all = H*(2 dk + dv) channels ordered q | k | v. Returns
+    (q, k, v, conv_state_out) with conv_state_out in the same layout."""
+    ntok = xq.shape[0]
+    dk, dv = xq.shape[2], xv.shape[2]
+    cuts = np.cumsum([0, H * dk, H * dk, H * dv])
+    outs, hist = [], []
+    for i, (x, w, norm) in enumerate(((xq, wq, True), (xk, wk, True), (xv, wv, False))):
+        d = x.shape[2]
+        hin = None if conv_state_in is None else conv_state_in[:, :, cuts[i]:cuts[i + 1]]
+        u, hout = short_conv_hist(x.reshape(ntok, H * d), w, cu_seqlens, hin)
+        a = silu(u).reshape(ntok, H, d)
+        outs.append(l2norm(a, l2_eps) if norm else a)
+        hist.append(hout)
+    return outs[0], outs[1], outs[2], np.concatenate(hist, axis=2)
 
 
 def forward(q, k, v, a_raw, b_raw, A_log, dt_bias, S0=None, cu_seqlens=None, nthreads=None):

@@ -57,6 +57,40 @@ void gdn_oracle_short_conv(const double* x, const double* w, int K, const int* c
     }
 }
 
+/* ShortConv with a carried history: the streaming form of the conv above, for a sequence
+ * that continues one processed earlier (chunked prefill, decode). The K-1 inputs before the
+ * start of sequence s are hist_in[s] ([nseq, K-1, C], row j = the input K-1-j positions
+ * before the start, so row K-2 is the newest); hist_in NULL means zero history, which is the
+ * conv above. hist_out[s] (nullable) receives the last K-1 inputs of the history followed by
+ * the sequence, in the same row order: for a sequence shorter than K-1 its older rows come
+ * from hist_in. */
+static double conv_input(const double* x, const double* hist_in, const int* cu, int s, int K,
+                         int C, long p, int c) {
+    if (p >= cu[s]) return x[p * C + c];
+    if (!hist_in) return 0.0;
+    long j = (K - 1) - (cu[s] - p); /* cu[s] - p in 1..K-1 */
+    return hist_in[((long)s * (K - 1) + j) * C + c];
+}
+
+void gdn_oracle_short_conv_hist(const double* x, const double* w, int K, const int* cu, int nseq,
+                                int C, const double* hist_in, double* u, double* hist_out) {
+    for (int s = 0; s < nseq; ++s) {
+        for (int t = cu[s]; t < cu[s + 1]; ++t) {
+            for (int c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < K; ++j)
+                    acc += w[(long)c * K + j] * conv_input(x, hist_in, cu, s, K, C, t - (K - 1) + j, c);
+                u[(long)t * C + c] = acc;
+            }
+        }
+        if (hist_out)
+            for (int j = 0; j < K - 1; ++j)
+                for (int c = 0; c < C; ++c)
+                    hist_out[((long)s * (K - 1) + j) * C + c] =
+                        conv_input(x, hist_in, cu, s, K, C, (long)cu[s + 1] - (K - 1) + j, c);
+    }
+}
+
 /* SiLU(u) = u * sigmoid(u) = u / (1 + exp(-u)) */
 void gdn_oracle_silu(const double* u, long n, double* a) {
     for (long i = 0; i < n; ++i) a[i] = u[i] / (1.0 + exp(-u[i]));

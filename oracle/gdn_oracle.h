@@ -9,6 +9,8 @@ extern "C" {
 
 void gdn_oracle_short_conv(const double* x, const double* w, int K, const int* cu, int nseq,
                            int C, double* u);
+void gdn_oracle_short_conv_hist(const double* x, const double* w, int K, const int* cu, int nseq,
+                                int C, const double* hist_in, double* u, double* hist_out);
 void gdn_oracle_silu(const double* u, long n, double* a);
 void gdn_oracle_l2norm(const double* a, long rows, int d, double eps, double* out);
 void gdn_oracle_gates(const double* a_raw, const double* b_raw, const double* A_log,

@@ -247,6 +247,59 @@ def test_conv_matches_numpy_convolve_with_resets():
             assert np.allclose(u[lo:hi, c], ref, rtol=1e-14, atol=1e-14)
 
 
+# ---------------------------------------------------------------- conv with a carried history
+def _joined(hist_rows, piece):
+    return np.concatenate([hist_rows, piece], axis=0)
+
+
+def test_conv_history_matches_numpy_convolve_over_the_joined_stream():
+    rng = np.random.default_rng(22)
+    C, K = 5, 4
+    x = rng.standard_normal((23, C))
+    w = rng.standard_normal((C, K))
+    cu = [0, 0, 1, 3, 10, 23]      # empty, 1- and 2-token sequences keep part of the history
+    hist = rng.standard_normal((len(cu) - 1, K - 1, C))
+    u, hout = oracle.short_conv_hist(x, w, cu, hist)
+    for s, (lo, hi) in enumerate(zip(cu[:-1], cu[1:])):
+        ext = _joined(hist[s], x[lo:hi])
+        for c in range(C):
+            ref = np.convolve(ext[:, c], w[c, ::-1], mode="full")[K - 1: K - 1 + hi - lo]
+            assert np.allclose(u[lo:hi, c], ref, rtol=1e-14, atol=1e-14)
+        # the carried history is the last K-1 rows of the joined stream, oldest first
+        assert np.array_equal(hout[s], ext[-(K - 1):])
+
+
+def test_conv_history_oldest_tap_reads_history_rows_in_order():
+    rng = np.random.default_rng(23)
+    C = 3
+    x = rng.standard_normal((6, C))
+    hist = rng.standard_normal((1, 3, C))
+    shift = np.tile([1.0, 0.0, 0.0, 0.0], (C, 1))        # u[t] = input three positions back
+    u, _ = oracle.short_conv_hist(x, shift, [0, 6], hist)
+    assert np.array_equal(u[:3], hist[0])                 # row 0 is the oldest input
+    assert np.array_equal(u[3:], x[:3])
+
+
+def test_conv_history_split_stream_equals_whole_sequence():
+    rng = np.random.default_rng(24)
+    C, K, n = 4, 4, 57
+    x = rng.standard_normal((n, C))
+    w = rng.standard_normal((C, K))
+    whole = oracle.short_conv(x, w, [0, n])
+    cuts = [0, 0, 1, 3, 4, 20, 21, 21, 40, n]            # pieces of 0, 1, 2, 1, 16, ... tokens
+    hist = np.zeros((1, K - 1, C))
+    parts = []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        u, hist = oracle.short_conv_hist(x[lo:hi], w, [0, hi - lo], hist)
+        parts.append(u)
+    assert np.allclose(np.concatenate(parts), whole, rtol=0, atol=1e-15)
+    assert np.array_equal(hist[0], x[-(K - 1):])
+    # no history given == zero history == the resetting conv
+    u0, h0 = oracle.short_conv_hist(x, w, [0, 30, n])
+    assert np.array_equal(u0, oracle.short_conv(x, w, [0, 30, n]))
+    assert np.array_equal(h0[0], x[27:30]) and np.array_equal(h0[1], x[n - 3:])
+
+
 def test_activations_against_mpmath():
     mpmath.mp.dps = 40
     xs = np.array([-30.0, -7.5, -1.0, -1e-3, 0.0, 0.3, 2.0, 9.0, 25.0])
