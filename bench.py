@@ -4,7 +4,8 @@ A step is one pass of the prefill token mixer over the bf16 workload B=4, H=16, 
 d_k=d_v=128 (preprocess -> chunked prefill -> output gate), inputs resident in HBM.
 `value` is that pipeline's throughput in Mtok/s (a token spans all 16 heads). The decode
 half of the metric (256 sequences x 32 heads, d=128, 100 steps with fresh tokens, fp32 state
-updated in place) is timed in the same run and reported under "decode".
+updated in place) is timed in the same run and reported under "decode", with the
+multi-token decode (4 tokens per sequence per step, as in MTP verification) beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 Prints one JSON line.
@@ -213,6 +214,43 @@ def main():
                   "bytes_per_step": state_bytes + tok_bytes}
         log(f"[bench] decode {dms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
         del state, qd, kd, vd, gd, bd, yd
+        torch.cuda.empty_cache()
+
+        # multi-token decode (MTP verify): the same sequences and heads, T = 4 tokens per step,
+        # a quarter as many steps (the same number of tokens)
+        T4, S4 = 4, max(1, S_ // 4)
+        log(f"[bench] generating multi-token decode inputs N=256 H=32 d=128 T={T4}, {S4} steps")
+        mi = gi.make_inputs(3, seed=1, steps=S4, tokens=T4)
+        state = d(mi["state"])
+        qm, km, vm = d(mi["q"], True), d(mi["k"], True), d(mi["v"], True)
+        _, _, _, gm, bm = gdn.gdn_preprocess(None, None, None, None, None, None,
+                                             d(mi["a_raw"].reshape(S4 * N * T4, DH)),
+                                             d(mi["b_raw"].reshape(S4 * N * T4, DH)),
+                                             d(mi["A_log"]), d(mi["dt_bias"]), H=DH)
+        gm = gm.view(S4, N, T4, DH)
+        bm = bm.view(S4, N, T4, DH)
+        ym = torch.empty((S4, N, T4, DH, dsh.dv), dtype=bf, device=dev)
+        for s in range(min(3, S4)):
+            gdn.gdn_decode_multi(qm[s], km[s], vm[s], gm[s], bm[s], state, y=ym[s])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(S4):
+            gdn.gdn_decode_multi(qm[s], km[s], vm[s], gm[s], bm[s], state, y=ym[s])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mms = e0.elapsed_time(e1) / S4
+        mtok_bytes = T4 * tok_bytes
+        mgbs = (state_bytes + mtok_bytes) / (mms * 1e-3) / 1e9
+        decode["multi_token"] = {
+            "workload": f"decode N=256 H=32 d_k=d_v=128, {T4} tokens per sequence per step "
+                        "(gdn_decode_multi), fp32 state in place, bf16 tokens",
+            "tokens_per_step": T4, "steps": S4, "us_per_step": round(mms * 1e3, 2),
+            "Mtok_s": round(N * T4 / (mms * 1e-3) / 1e6, 3), "GB_s": round(mgbs, 1),
+            "hbm_frac": round(mgbs / HBM_PEAK_GBS, 4), "bytes_per_step": state_bytes + mtok_bytes,
+            "vs_single_token_steps": round(T4 * dms / mms, 2)}
+        log(f"[bench] multi-token decode T={T4}: {mms * 1e3:.1f} us/step, {mgbs:.0f} GB/s "
+            f"({mgbs / HBM_PEAK_GBS:.1%} of HBM), {T4 * dms / mms:.2f}x the tokens/s of T=1 steps")
+        del state, qm, km, vm, gm, bm, ym
         torch.cuda.empty_cache()
 
     if args.calibrate_copy:

@@ -7,7 +7,11 @@ CPU or PyTorch fallback: if libgdn.so is missing these functions raise.
 The functions keep the C names:
   gdn_preprocess     eqs. (6)-(10)  ShortConv -> SiLU -> L2Norm (q, k), SiLU (v), gates
   gdn_chunk_prefill  eqs. (1)-(4)   chunkwise (C = 64) gated delta rule over packed sequences
+  gdn_preprocess_stateful           the same for sequences that continue earlier input
+                                    (carried conv history in and out)
   gdn_decode_step    eqs. (1)-(4)   one token per sequence, state updated in place
+  gdn_decode_multi   eqs. (1)-(4)   T <= 8 tokens per sequence (multi-token prediction
+                                    verify) in one pass over each state
   gdn_output_gate    eq. (11)       sigmoid(z) * zero-centred RMSNorm(y) (without W_o)
 (equation numbers of section 2.1.1 of the reading notes of "On the Design of
 Qwen3.8-Next Architecture").
@@ -50,6 +54,8 @@ def lib():
         L.gdn_preprocess.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp,
                                      _i, _i, _i, _i, _i, ctypes.c_float, _vp, _vp, _vp, _i, _vp,
                                      _vp, _vp]
+        L.gdn_preprocess_stateful.restype = _i
+        L.gdn_preprocess_stateful.argtypes = L.gdn_preprocess.argtypes[:-1] + [_vp, _vp, _vp]
         L.gdn_chunk_prefill_workspace_size.restype = ctypes.c_size_t
         L.gdn_chunk_prefill_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
         L.gdn_chunk_prefill.restype = _i
@@ -58,6 +64,9 @@ def lib():
         L.gdn_decode_step.restype = _i
         L.gdn_decode_step.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i,
                                       _vp]
+        L.gdn_decode_multi.restype = _i
+        L.gdn_decode_multi.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
+                                       _i, _vp, _vp]
         L.gdn_output_gate.restype = _i
         L.gdn_output_gate.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, ctypes.c_float, _vp, _i,
                                       _vp]
@@ -152,6 +161,41 @@ def gdn_preprocess(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, *, H, c
     return q, k, v, g, beta
 
 
+def gdn_preprocess_stateful(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, *, H,
+                            conv_state_in=None, conv_state_out=None, cu_seqlens=None,
+                            num_seqs=1, l2_eps=1e-6, out_dtype=torch.bfloat16, outs=None,
+                            stream=None):
+    """gdn_preprocess for sequences that continue earlier input. conv_state_in/out:
+    [num_seqs, 3, H*(2*dk+dv)] in the dtype of x* (channels q | k | v), conv_state_in None =
+    zero history; pass conv_state_out=True to have it allocated. The two must not overlap.
+    Returns (q, k, v, g, beta, conv_state_out)."""
+    ntok, _, dk = xq.shape
+    dv = xv.shape[-1]
+    dev = xq.device
+    o_tag = _tag(out_dtype)
+    if conv_state_out is True:
+        conv_state_out = torch.empty((num_seqs, 3, H * (2 * dk + dv)), dtype=xq.dtype, device=dev)
+    outs = {} if outs is None else outs
+    q = outs.get("q", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
+    k = outs.get("k", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
+    v = outs.get("v", torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=dev))
+    g = beta = None
+    if a_raw is not None:
+        g = outs.get("g", torch.empty((ntok, H), dtype=torch.float32, device=dev))
+        beta = outs.get("beta", torch.empty((ntok, H), dtype=torch.float32, device=dev))
+    f32 = torch.float32
+    st = lib().gdn_preprocess_stateful(
+        _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), _dtype_tag(xq),
+        _ptr(wq, "wq", f32), _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4,
+        _ptr(a_raw, "a_raw", f32), _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32),
+        _ptr(dt_bias, "dt_bias", f32), _ptr(cu_seqlens, "cu_seqlens", torch.int32), num_seqs, ntok,
+        H, dk, dv, l2_eps, _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), o_tag, _ptr(g, "g", f32),
+        _ptr(beta, "beta", f32), _ptr(conv_state_in, "conv_state_in", xq.dtype),
+        _ptr(conv_state_out, "conv_state_out", xq.dtype), _stream(stream))
+    _check(st, "gdn_preprocess_stateful")
+    return q, k, v, g, beta, conv_state_out
+
+
 def gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, in_dtype=torch.bfloat16) -> int:
     return int(lib().gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, _tag(in_dtype)))
 
@@ -205,6 +249,29 @@ def gdn_decode_step(q, k, v, g, beta, state, *, y=None, y_dtype=None, stream=Non
     return y
 
 
+def gdn_decode_multi(q, k, v, g, beta, state, *, y=None, y_dtype=None, step_states=None,
+                     stream=None):
+    """T tokens per sequence in one pass over each state. q,k: [N,T,H,dk], v: [N,T,H,dv];
+    g,beta: [N,T,H] fp32; state: [N,H,dk,dv] fp32 updated in place; step_states: None, True
+    (allocate) or [N,T,H,dk,dv] fp32 receiving the state after each token.
+    Returns (y [N,T,H,dv], step_states)."""
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    in_tag = _dtype_tag(q)
+    y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
+    if y is None:
+        y = torch.empty((N, T, H, dv), dtype=_tag_dtype(y_tag), device=q.device)
+    if step_states is True:
+        step_states = torch.empty((N, T, H, dk, dv), dtype=torch.float32, device=q.device)
+    f32 = torch.float32
+    st = lib().gdn_decode_multi(_ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), in_tag,
+                                _ptr(g, "g", f32), _ptr(beta, "beta", f32),
+                                _ptr(state, "state", f32), N, T, H, dk, dv, _ptr(y, "y"), y_tag,
+                                _ptr(step_states, "step_states", f32), _stream(stream))
+    _check(st, "gdn_decode_multi")
+    return y, step_states
+
+
 def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream=None):
     """eq. 11 without W_o. y, z: [ntok,H,dv]; norm_weight: [dv] fp32. Returns o."""
     ntok, H, dv = y.shape
@@ -218,5 +285,6 @@ def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream
     return o
 
 
-__all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_chunk_prefill",
-           "gdn_chunk_prefill_workspace_size", "gdn_decode_step", "gdn_output_gate"]
+__all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_preprocess_stateful",
+           "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_decode_step",
+           "gdn_decode_multi", "gdn_output_gate"]

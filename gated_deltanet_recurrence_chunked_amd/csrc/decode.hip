@@ -110,6 +110,240 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     if (rg == 0) Vec4<Tout>::store(y + (size_t)head * DV + c, yo);
 }
 
+// ----------------------------------------------------------------------------------------
+// T consecutive tokens per sequence in one pass over the state: the chunkwise form of eq. (5)
+// with the chunk being the T new tokens. With G_t = g_1 + ... + g_t (g = log alpha) and
+// sk_t = S^T k_t, sq_t = S^T q_t of the state S the call starts from:
+//   U_t = beta_t (v_t - e^{G_t} sk_t) - sum_{i<t} beta_t e^{G_t - G_i} (k_t.k_i) U_i
+//   y_t = e^{G_t} sq_t + sum_{i<=t} e^{G_t - G_i} (q_t.k_i) U_i
+//   S_t = e^{G_t} S + sum_{i<=t} e^{G_t - G_i} k_i U_i^T
+// (U_t = beta_t e_t of eqs. (2)-(3); expanding eqs. (1)-(4) token by token gives these
+// sums). All 2T column reductions run against the one state in registers, so the state is
+// read once and written once however many tokens the step carries. Decays are exp of
+// differences of the running sum (never above 1).
+// 512 threads (two waves per SIMD): a thread holds dk/16 contiguous rows of 4 columns, half
+// of what the single-token kernel's threads hold, which leaves registers for the per-token
+// arrays. Column sums: in registers over a thread's rows, by shuffles over the wave's row
+// groups, then once per (value, column) across the waves in LDS.
+constexpr int kDecMultiThreads = 512;
+
+// kMaxDecT (2, 4 or 8) bounds T at compile time: the per-token register arrays are sized by
+// it, so a short step does not pay the registers (and occupancy) of the longest one.
+template <int DK, int DV, int kMaxDecT, typename Tin, typename Tout>
+__global__ void __launch_bounds__(kDecMultiThreads, kMaxDecT <= 4 ? 4 : 2)
+decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+                    const float* __restrict__ g, const float* __restrict__ beta, float* state,
+                    Tout* __restrict__ y, float* __restrict__ steps, int T, int H) {
+    constexpr int TPR = DV / 4;                  // threads per state row
+    constexpr int RG = kDecMultiThreads / TPR;   // row groups
+    constexpr int RPT = DK / RG;                 // contiguous rows per thread
+    constexpr int NW = kDecMultiThreads / kWave;
+    constexpr int NV = 2 * kMaxDecT;             // column sums per token pair: S^T k_t, S^T q_t
+    static_assert(RPT >= 1 && DK % RG == 0 && TPR <= kWave, "shape");
+
+    __shared__ __attribute__((aligned(16))) float ks[kMaxDecT][DK];
+    __shared__ __attribute__((aligned(16))) float qs[kMaxDecT][DK];
+    __shared__ __attribute__((aligned(16))) float red[NW][NV][DV];   // per-wave column partials
+    __shared__ __attribute__((aligned(16))) float fin[NV][DV];       // column sums
+    // token-pair scalars: A[t][i] = beta_t e^{G_t-G_i} k_t.k_i (i < t),
+    // P[t][i] = e^{G_t-G_i} q_t.k_i (i <= t), D[t][i] = e^{G_t-G_i} (i <= t)
+    __shared__ float Am[kMaxDecT][kMaxDecT], Pm[kMaxDecT][kMaxDecT], Dm[kMaxDecT][kMaxDecT];
+    __shared__ float Gs[kMaxDecT], Bs[kMaxDecT];   // G_t and beta_t
+
+    const int head = blockIdx.x;             // flattened (sequence, head)
+    const int n = head / H, h = head % H;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int c = (tid % TPR) * 4;
+    const int r0 = (tid / TPR) * RPT;        // first of this thread's rows
+    auto tok = [&](int t) { return (size_t)(n * T + t) * H + h; };   // (token, head) row
+
+    float* S = state + (size_t)head * DK * DV;
+    float s[RPT][4];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const floatx4 x = __builtin_nontemporal_load(
+            reinterpret_cast<const floatx4*>(S + (size_t)(r0 + i) * DV + c));
+        s[i][0] = x.x; s[i][1] = x.y; s[i][2] = x.z; s[i][3] = x.w;
+    }
+    for (int i = tid; i < T * DK; i += kDecMultiThreads) {
+        const int t = i / DK, r = i % DK;
+        ks[t][r] = load1(k + tok(t) * DK + r);
+        qs[t][r] = load1(q + tok(t) * DK + r);
+    }
+    float vv[kMaxDecT][4];
+    float run = 0.f;
+#pragma unroll
+    for (int t = 0; t < kMaxDecT; ++t) {
+        if (t < T) {
+            Vec4<Tin>::load(v + tok(t) * DV + c, vv[t]);
+            run += g[tok(t)];
+            if (tid == t) {
+                Gs[t] = run;
+                Bs[t] = beta[tok(t)];
+            }
+        }
+    }
+    __syncthreads();
+
+    // this thread's RPT rows of a token vector (LDS, 16-byte reads where they fit)
+    auto rows_of = [&](const float* vec, float (&out)[RPT]) __attribute__((always_inline)) {
+        if constexpr (RPT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < RPT; i += 4) {
+                const floatx4 x = *reinterpret_cast<const floatx4*>(vec + r0 + i);
+                out[i] = x.x; out[i + 1] = x.y; out[i + 2] = x.z; out[i + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) out[i] = vec[r0 + i];
+        }
+    };
+
+    // token-pair scalars, one pair per wave in turn
+    for (int p = wave; p < T * T; p += NW) {
+        const int t = p / T, i = p % T;
+        if (i > t) continue;   // wave-uniform
+        float kk = 0.f, qk = 0.f;
+        for (int r = lane; r < DK; r += kWave) {
+            kk += ks[t][r] * ks[i][r];
+            qk += qs[t][r] * ks[i][r];
+        }
+        kk = group_sum<kWave>(kk);
+        qk = group_sum<kWave>(qk);
+        if (lane == 0) {
+            const float d = expf(Gs[t] - Gs[i]);
+            Dm[t][i] = d;
+            Pm[t][i] = d * qk;
+            Am[t][i] = i < t ? Bs[t] * d * kk : 0.f;
+        }
+    }
+
+    // column partials of S^T k_t and S^T q_t over this thread's rows, then over the wave's
+    // row groups (lanes TPR apart); lanes of the first row group write the wave's partial
+#pragma unroll
+    for (int t = 0; t < kMaxDecT; ++t) {
+        if (t < T) {
+            float kr[RPT], qr[RPT];
+            rows_of(ks[t], kr);
+            rows_of(qs[t], qr);
+            float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < RPT; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pk[j] += s[i][j] * kr[i];
+                    pq[j] += s[i][j] * qr[i];
+                }
+#pragma unroll
+            for (int o = TPR; o < kWave; o <<= 1)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pk[j] += __shfl_xor(pk[j], o, kWave);
+                    pq[j] += __shfl_xor(pq[j], o, kWave);
+                }
+            if (lane < TPR) {
+                *reinterpret_cast<floatx4*>(&red[wave][2 * t][c]) = floatx4{pk[0], pk[1], pk[2], pk[3]};
+                *reinterpret_cast<floatx4*>(&red[wave][2 * t + 1][c]) = floatx4{pq[0], pq[1], pq[2], pq[3]};
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < 2 * T * DV; e += kDecMultiThreads) {   // across the waves, once
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += (&red[w][0][0])[e];
+        (&fin[0][0])[e] = acc;
+    }
+    __syncthreads();
+
+    // U_t and y_t for this thread's 4 columns (every row group forms them; the first stores y)
+    float U[kMaxDecT][4];
+#pragma unroll
+    for (int t = 0; t < kMaxDecT; ++t) {
+        if (t < T) {
+            const float gt = expf(Gs[t]), bt = Bs[t];
+            const floatx4 sk = *reinterpret_cast<const floatx4*>(&fin[2 * t][c]);
+            const floatx4 sq = *reinterpret_cast<const floatx4*>(&fin[2 * t + 1][c]);
+            float yo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float u = bt * (vv[t][j] - gt * sk[j]);
+#pragma unroll
+                for (int i = 0; i < kMaxDecT; ++i)
+                    if (i < t) u -= Am[t][i] * U[i][j];
+                U[t][j] = u;
+                float yv = gt * sq[j];
+#pragma unroll
+                for (int i = 0; i < kMaxDecT; ++i)
+                    if (i <= t) yv += Pm[t][i] * U[i][j];
+                yo[j] = yv;
+            }
+            if (r0 == 0) Vec4<Tout>::store(y + tok(t) * DV + c, yo);
+        }
+    }
+
+    // S_t = e^{G_t} S + sum_{i<=t} e^{G_t-G_i} k_i U_i^T: every step's state when asked for,
+    // the last one in place
+    auto state_at = [&](int t, float* dst) __attribute__((always_inline)) {
+        const float gt = expf(Gs[t]);
+        float o[RPT][4];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[r][j] = gt * s[r][j];
+#pragma unroll
+        for (int i = 0; i < kMaxDecT; ++i) {
+            if (i <= t) {
+                float kr[RPT];
+                rows_of(ks[i], kr);
+                const float d = Dm[t][i];
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const float dk = d * kr[r];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[r][j] += dk * U[i][j];
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            __builtin_nontemporal_store(floatx4{o[r][0], o[r][1], o[r][2], o[r][3]},
+                                        reinterpret_cast<floatx4*>(dst + (size_t)(r0 + r) * DV + c));
+    };
+    if (steps)
+        for (int t = 0; t < T; ++t) state_at(t, steps + ((size_t)(n * T + t) * H + h) * DK * DV);
+    state_at(T - 1, S);
+}
+
+template <int DK, int DV, int MT>
+static void launch_dec_multi_t(const void* q, const void* k, const void* v, int in_bf16,
+                               const float* g, const float* beta, float* state, int heads, int T,
+                               int H, void* y, int y_bf16, float* steps, hipStream_t s) {
+#define GDN_DECM(TI, TO)                                                                        \
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, MT, TI, TO>), dim3(heads), dim3(kDecMultiThreads), \
+                       0, s, static_cast<const TI*>(q), static_cast<const TI*>(k),               \
+                       static_cast<const TI*>(v), g, beta, state, static_cast<TO*>(y), steps, T, H)
+    if (in_bf16 && y_bf16) GDN_DECM(uint16_t, uint16_t);
+    else if (in_bf16) GDN_DECM(uint16_t, float);
+    else if (y_bf16) GDN_DECM(float, uint16_t);
+    else GDN_DECM(float, float);
+#undef GDN_DECM
+}
+
+template <int DK, int DV>
+static void launch_dec_multi(const void* q, const void* k, const void* v, int in_bf16,
+                             const float* g, const float* beta, float* state, int heads, int T,
+                             int H, void* y, int y_bf16, float* steps, hipStream_t s) {
+    static_assert(kMaxDecodeTokens == 8, "token buckets");
+    if (T <= 2)
+        launch_dec_multi_t<DK, DV, 2>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s);
+    else if (T <= 4)
+        launch_dec_multi_t<DK, DV, 4>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s);
+    else
+        launch_dec_multi_t<DK, DV, 8>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s);
+}
+
 template <int DK, int DV>
 static void launch_dec(const void* q, const void* k, const void* v, int in_bf16, const float* g,
                        const float* beta, float* state, int heads, void* y, int y_bf16,
@@ -134,6 +368,22 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int in_bf1
     else if (dk == 128 && dv == 64) launch_dec<128, 64>(q, k, v, in_bf16, g, beta, state, heads, y, y_bf16, s);
     else if (dk == 64 && dv == 128) launch_dec<64, 128>(q, k, v, in_bf16, g, beta, state, heads, y, y_bf16, s);
     else launch_dec<64, 64>(q, k, v, in_bf16, g, beta, state, heads, y, y_bf16, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_multi(const void* q, const void* k, const void* v, int in_bf16,
+                               const float* g, const float* beta, float* state, int N, int T,
+                               int H, int dk, int dv, void* y, int y_bf16, float* steps,
+                               hipStream_t s) {
+    const int heads = N * H;
+    if (heads == 0) return hipSuccess;
+#define GDN_DM(DK_, DV_) \
+    launch_dec_multi<DK_, DV_>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s)
+    if (dk == 128 && dv == 128) GDN_DM(128, 128);
+    else if (dk == 128 && dv == 64) GDN_DM(128, 64);
+    else if (dk == 64 && dv == 128) GDN_DM(64, 128);
+    else GDN_DM(64, 64);
+#undef GDN_DM
     return hipGetLastError();
 }
 

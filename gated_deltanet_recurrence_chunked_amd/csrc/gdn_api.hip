@@ -8,6 +8,8 @@
 #include "../../include/gdn.h"
 #include "gdn_launch.h"
 
+static_assert(gdn::kMaxDecodeTokens == GDN_DECODE_MAX_TOKENS, "decode token limit");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -97,12 +99,17 @@ const char* gdn_status_string(int s) {
 
 const char* gdn_last_error(void) { return g_last_error; }
 
-int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,
-                   const float* wk, const float* wv, int conv_k, const float* a_raw,
-                   const float* b_raw, const float* A_log, const float* dt_bias,
-                   const int32_t* cu_seqlens, int num_seqs, int ntok, int H, int dk, int dv,
-                   float l2_eps, void* q, void* k, void* v, int out_dtype, float* g, float* beta,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+int preprocess_impl(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,
+                    const float* wk, const float* wv, int conv_k, const float* a_raw,
+                    const float* b_raw, const float* A_log, const float* dt_bias,
+                    const int32_t* cu_seqlens, int num_seqs, int ntok, int H, int dk, int dv,
+                    float l2_eps, void* q, void* k, void* v, int out_dtype, float* g, float* beta,
+                    const void* conv_state_in, void* conv_state_out, void* stream,
+                    const char* name) {
     GDN_REQUIRE(valid_dtype(x_dtype) && valid_dtype(out_dtype), GDN_ERR_DTYPE,
                 "x_dtype/out_dtype must be GDN_F32 or GDN_BF16");
     GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
@@ -124,6 +131,17 @@ int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype, 
     GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
     int st = check_packing(nullptr, cu_seqlens != nullptr, num_seqs, ntok);
     if (st) return st;
+    const int hC = H * (2 * dk + dv);
+    if (conv_state_in || conv_state_out) {
+        GDN_REQUIRE(conv, GDN_ERR_NULL, "a conv state needs the conv inputs and outputs");
+        GDN_OPT_PTR(conv_state_in);
+        GDN_OPT_PTR(conv_state_out);
+        const size_t bytes = (size_t)num_seqs * (conv_k - 1) * hC * (x_dtype == GDN_BF16 ? 2 : 4);
+        const char* i0 = static_cast<const char*>(conv_state_in);
+        const char* o0 = static_cast<const char*>(conv_state_out);
+        GDN_REQUIRE(!i0 || !o0 || i0 + bytes <= o0 || o0 + bytes <= i0, GDN_ERR_SHAPE,
+                    "conv_state_in and conv_state_out must not overlap");
+    }
 
     gdn::PreprocessArgs a;
     a.x[0] = conv ? xq : nullptr; a.x[1] = conv ? xk : nullptr; a.x[2] = conv ? xv : nullptr;
@@ -136,7 +154,35 @@ int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype, 
     a.b_raw = b_raw; a.A_log = A_log; a.dt_bias = dt_bias; a.g = g; a.beta = beta;
     a.cu = cu_seqlens;
     a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.l2_eps = l2_eps;
-    return hip_status(gdn::launch_preprocess(a, static_cast<hipStream_t>(stream)), "gdn_preprocess");
+    a.hin = conv_state_in; a.hout = conv_state_out; a.hC = hC;
+    return hip_status(gdn::launch_preprocess(a, static_cast<hipStream_t>(stream)), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,
+                   const float* wk, const float* wv, int conv_k, const float* a_raw,
+                   const float* b_raw, const float* A_log, const float* dt_bias,
+                   const int32_t* cu_seqlens, int num_seqs, int ntok, int H, int dk, int dv,
+                   float l2_eps, void* q, void* k, void* v, int out_dtype, float* g, float* beta,
+                   void* stream) {
+    return preprocess_impl(xq, xk, xv, x_dtype, wq, wk, wv, conv_k, a_raw, b_raw, A_log, dt_bias,
+                           cu_seqlens, num_seqs, ntok, H, dk, dv, l2_eps, q, k, v, out_dtype, g,
+                           beta, nullptr, nullptr, stream, "gdn_preprocess");
+}
+
+int gdn_preprocess_stateful(const void* xq, const void* xk, const void* xv, int x_dtype,
+                            const float* wq, const float* wk, const float* wv, int conv_k,
+                            const float* a_raw, const float* b_raw, const float* A_log,
+                            const float* dt_bias, const int32_t* cu_seqlens, int num_seqs,
+                            int ntok, int H, int dk, int dv, float l2_eps, void* q, void* k,
+                            void* v, int out_dtype, float* g, float* beta,
+                            const void* conv_state_in, void* conv_state_out, void* stream) {
+    return preprocess_impl(xq, xk, xv, x_dtype, wq, wk, wv, conv_k, a_raw, b_raw, A_log, dt_bias,
+                           cu_seqlens, num_seqs, ntok, H, dk, dv, l2_eps, q, k, v, out_dtype, g,
+                           beta, conv_state_in, conv_state_out, stream, "gdn_preprocess_stateful");
 }
 
 // The bf16 path with dk = 128 runs on the matrix cores and keeps per-chunk T and P tiles
@@ -197,6 +243,31 @@ int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, c
                                          dv, y, y_dtype == GDN_BF16,
                                          static_cast<hipStream_t>(stream)),
                       "gdn_decode_step");
+}
+
+int gdn_decode_multi(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                     const float* beta, float* state, int N, int T, int H, int dk, int dv,
+                     void* y, int y_dtype, float* step_states, void* stream) {
+    GDN_REQUIRE(valid_dtype(in_dtype) && valid_dtype(y_dtype), GDN_ERR_DTYPE,
+                "in_dtype/y_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(N >= 0 && H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need N >= 0, H >= 1 and dk, dv in {64, 128} (got N=%d H=%d dk=%d dv=%d)", N, H,
+                dk, dv);
+    GDN_REQUIRE(T >= 1 && T <= GDN_DECODE_MAX_TOKENS, GDN_ERR_SHAPE,
+                "T must be in 1..%d (got %d)", GDN_DECODE_MAX_TOKENS, T);
+    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(state); GDN_PTR(y);
+    GDN_OPT_PTR(step_states);
+    if (step_states) {
+        const char* a0 = reinterpret_cast<const char*>(state);
+        const char* b0 = reinterpret_cast<const char*>(step_states);
+        const size_t sb = (size_t)N * H * dk * dv * sizeof(float);
+        GDN_REQUIRE(a0 + sb <= b0 || b0 + sb * T <= a0, GDN_ERR_SHAPE,
+                    "step_states must not overlap state");
+    }
+    return hip_status(gdn::launch_decode_multi(q, k, v, in_dtype == GDN_BF16, g, beta, state, N, T,
+                                               H, dk, dv, y, y_dtype == GDN_BF16, step_states,
+                                               static_cast<hipStream_t>(stream)),
+                      "gdn_decode_multi");
 }
 
 int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype, const float* norm_weight,

@@ -18,6 +18,11 @@ struct PreprocessArgs {
     const int32_t* cu;    // NULL: equal lengths
     int num_seqs, ntok, H;
     float l2_eps;
+    // carried conv history [num_seqs, 3, hC] in the input dtype, channels q | k | v
+    // (hC = H * (2 dk + dv)); NULL hin: zero history, NULL hout: not written
+    const void* hin;
+    void* hout;
+    int hC;
 };
 hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s);
 
@@ -28,6 +33,13 @@ hipError_t launch_output_gate(const void* y, int y_bf16, const void* z, int z_bf
 hipError_t launch_decode(const void* q, const void* k, const void* v, int in_bf16,
                          const float* g, const float* beta, float* state, int N, int H,
                          int dk, int dv, void* y, int y_bf16, hipStream_t s);
+
+// T <= kMaxDecodeTokens tokens per sequence; steps (nullable): the state after each token
+constexpr int kMaxDecodeTokens = 8;
+hipError_t launch_decode_multi(const void* q, const void* k, const void* v, int in_bf16,
+                               const float* g, const float* beta, float* state, int N, int T,
+                               int H, int dk, int dv, void* y, int y_bf16, float* steps,
+                               hipStream_t s);
 
 struct ChunkArgs {
     const void *q, *k, *v;

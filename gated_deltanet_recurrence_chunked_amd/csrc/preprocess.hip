@@ -70,13 +70,37 @@ __device__ void conv_stream(const PreprocessArgs& a, int role, int tile, int t0)
         seq_hi = seq_lo + L;
     }
 
-    // history window: win[0] = x[t-3] ... win[2] = x[t-1], zero before the sequence start
+    // Carried conv history (optional): [num_seqs, 3, hC] rows of this stream's channels,
+    // row 2 the input just before the sequence start. Absent, the history is zero.
+    const Tin* hin = static_cast<const Tin*>(a.hin);
+    Tin* hout = static_cast<Tin*>(a.hout);
+    const int hoff = role == 0 ? 0 : (role == 1 ? a.H * a.d[0] : 2 * a.H * a.d[0]);
+    auto hist_row = [&](int seq, int r) __attribute__((always_inline)) {
+        return (size_t)(seq * 3 + r) * a.hC + hoff + c;
+    };
+    // history of sequence `seq` into the window (the conv restarts at its first token)
+    auto restart = [&](int seq, float (&wn)[3][8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            if (hin) {
+                Vec8<Tin>::load(hin + hist_row(seq, r), wn[r]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wn[r][i] = 0.f;
+            }
+        }
+    };
+
+    // history window: win[0] = x[t-3] ... win[2] = x[t-1]; before the sequence start it
+    // comes from the carried history
     float win[3][8];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int src = t0 - 3 + j;
         if (src >= seq_lo) {
             Vec8<Tin>::load(x + (size_t)src * C + c, win[j]);
+        } else if (hin) {
+            Vec8<Tin>::load(hin + hist_row(s, 3 - (seq_lo - src)), win[j]);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) win[j][i] = 0.f;
@@ -108,13 +132,13 @@ __device__ void conv_stream(const PreprocessArgs& a, int role, int tile, int t0)
                     while (a.cu[s + 1] <= t) ++s;
                     seq_hi = a.cu[s + 1];
                 } else {
+                    ++s;
                     seq_hi += a.ntok / a.num_seqs;
                 }
-#pragma unroll
-                for (int q = 0; q < 3; ++q)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) win[q][i] = 0.f;
+                restart(s, win);
             }
+            // the last three inputs of a sequence become its carried history
+            if (hout && t >= seq_hi - 3) Vec8<Tin>::store(hout + hist_row(s, 3 - (seq_hi - t)), grp[j]);
             float act[8];
             float ss = 0.f;
 #pragma unroll
@@ -152,6 +176,22 @@ __device__ void gates_block(const PreprocessArgs& a, int t0) {
     }
 }
 
+// Carried history of sequences shorter than 3 tokens (empty ones included): their older rows
+// are the input history shifted by the sequence length (zero without one). The rows of the
+// sequence's own tokens are written by the conv. Copies 16-byte units of raw input.
+__global__ void __launch_bounds__(kPreThreads) conv_carry_kernel(PreprocessArgs a, int elem_bytes) {
+    const int s = blockIdx.x;
+    const int L = a.cu ? a.cu[s + 1] - a.cu[s] : a.ntok / a.num_seqs;
+    if (L >= 3) return;
+    const int units = a.hC * elem_bytes / 16;   // 16-byte units per history row
+    const uint4* hin = static_cast<const uint4*>(a.hin);
+    uint4* hout = static_cast<uint4*>(a.hout);
+    for (int r = 0; r < 3 - L; ++r)
+        for (int u = threadIdx.x; u < units; u += kPreThreads)
+            hout[(size_t)(s * 3 + r) * units + u] =
+                hin ? hin[(size_t)(s * 3 + r + L) * units + u] : make_uint4(0u, 0u, 0u, 0u);
+}
+
 template <typename Tin, typename Tout>
 __global__ void __launch_bounds__(kPreThreads) preprocess_kernel(PreKernelArgs p) {
     const int t0 = blockIdx.x * kPreTokens;
@@ -177,7 +217,11 @@ hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s) {
     }
     p.gate_blocks = a.a_raw ? 1 : 0;
     ny += p.gate_blocks;
-    if (a.ntok == 0 || ny == 0) return hipSuccess;
+    if (ny == 0 || (a.ntok == 0 && !a.hout)) return hipSuccess;
+    if (a.hout && a.x[0])
+        hipLaunchKernelGGL(conv_carry_kernel, dim3(a.num_seqs), dim3(kPreThreads), 0, s, a,
+                           a.in_bf16 ? 2 : 4);
+    if (a.ntok == 0) return hipGetLastError();
     dim3 grid((a.ntok + kPreTokens - 1) / kPreTokens, ny);
     if (a.in_bf16 && a.out_bf16)
         hipLaunchKernelGGL((preprocess_kernel<uint16_t, uint16_t>), grid, dim3(kPreThreads), 0, s, p);

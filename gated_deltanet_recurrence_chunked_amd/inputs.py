@@ -59,6 +59,7 @@ class Shape:
     has_s0: bool
     steps: int = 0        # decode steps (config 3 only)
     equal_lengths: bool = True
+    tokens: int = 1       # tokens per sequence per decode step (config 3; > 1: multi-token)
 
     @property
     def num_seqs(self) -> int:
@@ -107,8 +108,9 @@ def make_shape(cfg: int, seed: int = 0, **ov) -> Shape:
         return Shape(cfg, p["H"], dk, dv, list(lengths), bf16=(cfg != 0), conv=(cfg == 1),
                      has_s0=(cfg == 2), equal_lengths=len(set(lengths)) <= 1)
     if cfg == 3:
-        return Shape(cfg, p["H"], dk, dv, [1] * p["N"], bf16=True, conv=False, has_s0=True,
-                     steps=p["steps"])
+        T = int(p.get("tokens", 1))
+        return Shape(cfg, p["H"], dk, dv, [T] * p["N"], bf16=True, conv=False, has_s0=True,
+                     steps=p["steps"], tokens=T)
     if cfg == 4:
         if "lengths" in p and p["lengths"]:
             lengths = list(p["lengths"])
@@ -224,11 +226,55 @@ def make_inputs(cfg: int, seed: int = 0, **ov) -> dict:
             out["S0"] = _normal(st.rng("S0"), (sh.num_seqs, H, dk, dv), std=0.1)
     elif cfg == 3:
         N, S = sh.num_seqs, sh.steps
+        lead = (S, N) if sh.tokens == 1 else (S, N, sh.tokens)   # multi-token: [S, N, T, ...]
         out["state"] = _normal(st.rng("S0"), (N, H, dk, dv), std=0.1)
-        out["q"] = _unit_rows(st.rng("q"), (S, N, H, dk), True)
-        out["k"] = _unit_rows(st.rng("k"), (S, N, H, dk), True)
-        out["v"] = _normal_bf16(st.rng("v"), (S, N, H, dv))
-        out.update(_gate_draws(st, (S, N), H))
+        out["q"] = _unit_rows(st.rng("q"), lead + (H, dk), True)
+        out["k"] = _unit_rows(st.rng("k"), lead + (H, dk), True)
+        out["v"] = _normal_bf16(st.rng("v"), lead + (H, dv))
+        out.update(_gate_draws(st, lead, H))
+    return out
+
+
+def conv_state_draw(seed: int, num_seqs: int, H: int, dk: int, dv: int,
+                    conv_k: int = 4) -> np.ndarray:
+    """A carried conv history [num_seqs, conv_k-1, H*(2dk+dv)] of bf16 N(0,1) bits, as if the
+    sequences had seen earlier input (channels q | k | v)."""
+    rng = np.random.default_rng(np.random.SeedSequence([SEED_TAG, 77, seed]))
+    return _normal_bf16(rng, (num_seqs, conv_k - 1, H * (2 * dk + dv)))
+
+
+def make_stream_inputs(seed: int, N: int, H: int, prompt_lengths, steps: int, tokens: int,
+                       dk: int = 128, dv: int = 128) -> dict:
+    """A prompt per sequence followed by `steps` decode steps of `tokens` tokens each, as the
+    pre-conv projected streams of the config-1 distributions (bf16 bits).
+      prompt: xq, xk [P, H, dk], xv [P, H, dv], a_raw, b_raw [P, H], packed by
+              cu_seqlens (lengths prompt_lengths);
+      decode: dxq, dxk [steps, N, tokens, H, dk], dxv [..., dv], da_raw, db_raw
+              [steps, N, tokens, H];
+      shared: wq, wk, wv [H*d, 4] conv taps, A_log, dt_bias [H]."""
+    assert len(prompt_lengths) == N
+    kids = dict(zip(["p", "d", "w", "g"],
+                    np.random.SeedSequence([SEED_TAG, 88, seed]).spawn(4)))
+    rp, rd, rw = (np.random.default_rng(kids[x]) for x in "pdw")
+    P = int(sum(prompt_lengths))
+    lead = (steps, N, tokens)
+    out = dict(cu_seqlens=np.concatenate([[0], np.cumsum(prompt_lengths)]).astype(np.int32),
+               H=H, dk=dk, dv=dv, N=N, steps=steps, tokens=tokens)
+    out["xq"] = _normal_bf16(rp, (P, H, dk))
+    out["xk"] = _normal_bf16(rp, (P, H, dk))
+    out["xv"] = _normal_bf16(rp, (P, H, dv))
+    out["a_raw"] = _normal(rp, (P, H))
+    out["b_raw"] = _normal(rp, (P, H))
+    out["dxq"] = _normal_bf16(rd, lead + (H, dk))
+    out["dxk"] = _normal_bf16(rd, lead + (H, dk))
+    out["dxv"] = _normal_bf16(rd, lead + (H, dv))
+    out["da_raw"] = _normal(rd, lead + (H,))
+    out["db_raw"] = _normal(rd, lead + (H,))
+    out["wq"] = _normal(rw, (H * dk, 4), std=0.5)
+    out["wk"] = _normal(rw, (H * dk, 4), std=0.5)
+    out["wv"] = _normal(rw, (H * dv, 4), std=0.5)
+    out["A_log"] = np.log(np.random.default_rng(kids["g"]).uniform(1.0, 16.0, size=H)).astype(np.float32)
+    out["dt_bias"] = np.full(H, -4.6, dtype=np.float32)
     return out
 
 

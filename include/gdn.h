@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -96,6 +96,32 @@ int gdn_preprocess(const void* xq, const void* xk, const void* xv, int x_dtype,
                    int H, int dk, int dv, float l2_eps, void* q, void* k, void* v,
                    int out_dtype, float* g, float* beta, void* stream);
 
+/*
+ * gdn_preprocess_stateful - gdn_preprocess for sequences that continue earlier input
+ * (a prompt prefilled in pieces, or decode steps of one or more tokens per sequence).
+ * eqs. (6)-(8) apply a causal conv along the whole stream (section 2.1.1 of the notes above;
+ * the design-paper summary "设计 LLM 架构", section "Token 混合：GDN 加 QSA", calls the short
+ * conv causal and depthwise), so each sequence carries the last conv_k-1 inputs it has seen.
+ *
+ *   Arguments as gdn_preprocess (the conv inputs and outputs are required), plus:
+ *   conv_state_in: [num_seqs, conv_k-1, H*(2*dk+dv)] in x_dtype, or NULL for zero history.
+ *       Row j of sequence s holds the input conv_k-1-j positions before its first token
+ *       (the last row is the newest); channels are ordered q | k | v, each [H, d] as in
+ *       xq, xk, xv.
+ *   conv_state_out: same layout, or NULL. Receives, per sequence, the last conv_k-1 inputs
+ *       of its history followed by its tokens: the next call's conv_state_in. A sequence
+ *       shorter than conv_k-1 (even an empty one) shifts its history by its length.
+ *   The two states must not overlap (double-buffer them; GDN_ERR_SHAPE otherwise).
+ *   With both NULL the call is gdn_preprocess. Values are copied bit for bit.
+ */
+int gdn_preprocess_stateful(const void* xq, const void* xk, const void* xv, int x_dtype,
+                            const float* wq, const float* wk, const float* wv, int conv_k,
+                            const float* a_raw, const float* b_raw, const float* A_log,
+                            const float* dt_bias, const int32_t* cu_seqlens, int num_seqs,
+                            int ntok, int H, int dk, int dv, float l2_eps, void* q, void* k,
+                            void* v, int out_dtype, float* g, float* beta,
+                            const void* conv_state_in, void* conv_state_out, void* stream);
+
 /* Bytes of device workspace gdn_chunk_prefill needs for these sizes (may be 0). */
 size_t gdn_chunk_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, int dv,
                                         int in_dtype);
@@ -137,6 +163,31 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
 int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, const float* g,
                     const float* beta, float* state, int N, int H, int dk, int dv, void* y,
                     int y_dtype, void* stream);
+
+/*
+ * gdn_decode_multi - T consecutive tokens per sequence through eqs. (1)-(4), state updated in
+ * place: the decode step of multi-token prediction, where one real token and T-1 drafts are
+ * verified together. The design-paper summary "设计 LLM 架构" (section "高层设计", output
+ * head and MTP) has the MTP module draft tokens for speculative decoding; the reading notes'
+ * efficiency analysis (Figure 6) times decode with three extra MTP steps (next_n = 4). The
+ * T tokens form one micro-chunk of the chunkwise form of eq. (5), so each state is read
+ * once and written once.
+ *
+ *   q, k: [N, T, H, dk], v: [N, T, H, dv] in in_dtype (token-major: the T tokens of
+ *       sequence n are rows n*T .. n*T+T-1 of a packed [N*T, H, d] tensor).
+ *   g, beta: [N, T, H] fp32 (alpha = exp(g)).
+ *   state: [N, H, dk, dv] fp32, read and overwritten with the state after token T-1.
+ *   y: [N, T, H, dv] output in y_dtype; y[n][t] is the output of token t.
+ *   step_states: NULL, or [N, T, H, dk, dv] fp32 receiving the state after each token
+ *       (step_states[n][T-1] equals the new state), so a caller that accepts only the
+ *       first a tokens of a draft restores sequence n from step_states[n][a-1]. Must not
+ *       overlap state.
+ *   1 <= T <= GDN_DECODE_MAX_TOKENS. T = 1 computes what gdn_decode_step computes.
+ */
+#define GDN_DECODE_MAX_TOKENS 8
+int gdn_decode_multi(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                     const float* beta, float* state, int N, int T, int H, int dk, int dv,
+                     void* y, int y_dtype, float* step_states, void* stream);
 
 /*
  * gdn_output_gate - eq. (11) without W_o:

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
     assert {"gdn_preprocess", "gdn_chunk_prefill", "gdn_decode_step", "gdn_output_gate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 1
+    assert L.gdn_abi_version() == 2
 
 
 def test_status_strings(L):
@@ -86,3 +86,22 @@ def test_preprocess_validation(L):
     # half of the gate pointers
     assert L.gdn_preprocess(n, n, n, 1, n, n, n, 4, FAKE, FAKE, n, n, n, 1, 8, 2, 128, 128, 1e-6,
                             n, n, n, 1, n, n, None) == 1
+
+
+def test_stateful_preprocess_and_multi_decode_validation(L):
+    n = None
+    F = FAKE
+    # conv state without the conv inputs
+    assert L.gdn_preprocess_stateful(n, n, n, 1, n, n, n, 4, F, F, F, F, n, 1, 8, 2, 128, 128,
+                                     1e-6, n, n, n, 1, F, F, F, n, None) == 1
+    # overlapping states (double-buffer them)
+    st = L.gdn_preprocess_stateful(F, F, F, 1, F, F, F, 4, n, n, n, n, n, 1, 8, 2, 128, 128, 1e-6,
+                                   F, F, F, 1, n, n, F, F + 16, None)
+    assert st == 2 and b"overlap" in L.gdn_last_error()
+    assert L.gdn_preprocess_stateful(F, F, F, 1, F, F, F, 4, n, n, n, n, n, 1, 8, 2, 128, 128,
+                                     1e-6, F, F, F, 1, n, n, MIS, n, None) == 5
+    for T in (0, 9):   # 1 <= T <= GDN_DECODE_MAX_TOKENS
+        st = L.gdn_decode_multi(F, F, F, 1, F, F, F, 1, T, 1, 128, 128, F, 1, n, None)
+        assert st == 2 and b"T must be" in L.gdn_last_error()
+    st = L.gdn_decode_multi(F, F, F, 1, F, F, F, 2, 4, 1, 128, 128, F, 1, F + 64, None)
+    assert st == 2 and b"overlap" in L.gdn_last_error()
