@@ -121,11 +121,15 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
 // sums). All 2T column reductions run against the one state in registers, so the state is
 // read once and written once however many tokens the step carries. Decays are exp of
 // differences of the running sum (never above 1).
-// 512 threads (two waves per SIMD): a thread holds dk/16 contiguous rows of 4 columns, half
-// of what the single-token kernel's threads hold, which leaves registers for the per-token
-// arrays. Column sums: in registers over a thread's rows, by shuffles over the wave's row
-// groups, then once per (value, column) across the waves in LDS.
+// One 512-thread workgroup per state (two waves per SIMD): a thread holds dk/16 contiguous
+// rows of 4 columns, half of what the single-token kernel's threads hold, which leaves
+// registers for the per-token arrays. Column sums: in registers over a thread's rows, by
+// shuffles over the wave's row groups, then once per (value, column) across the waves in LDS.
+// kDecColSplit > 1 would give each workgroup 1/kDecColSplit of the columns (a column's sums
+// and update need only that column); measured slower at split 2 (the per-workgroup token
+// work is repeated and each workgroup moves half the bytes).
 constexpr int kDecMultiThreads = 512;
+constexpr int kDecColSplit = 1;
 
 // kMaxDecT (2, 4 or 8) bounds T at compile time: the per-token register arrays are sized by
 // it, so a short step does not pay the registers (and occupancy) of the longest one.
@@ -134,7 +138,8 @@ __global__ void __launch_bounds__(kDecMultiThreads, kMaxDecT <= 4 ? 4 : 2)
 decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
                     const float* __restrict__ g, const float* __restrict__ beta, float* state,
                     Tout* __restrict__ y, float* __restrict__ steps, int T, int H) {
-    constexpr int TPR = DV / 4;                  // threads per state row
+    constexpr int DVS = DV / kDecColSplit;       // columns of this workgroup
+    constexpr int TPR = DVS / 4;                 // threads per state row
     constexpr int RG = kDecMultiThreads / TPR;   // row groups
     constexpr int RPT = DK / RG;                 // contiguous rows per thread
     constexpr int NW = kDecMultiThreads / kWave;
@@ -143,19 +148,20 @@ decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const 
 
     __shared__ __attribute__((aligned(16))) float ks[kMaxDecT][DK];
     __shared__ __attribute__((aligned(16))) float qs[kMaxDecT][DK];
-    __shared__ __attribute__((aligned(16))) float red[NW][NV][DV];   // per-wave column partials
-    __shared__ __attribute__((aligned(16))) float fin[NV][DV];       // column sums
+    __shared__ __attribute__((aligned(16))) float red[NW][NV][DVS];  // per-wave column partials
+    __shared__ __attribute__((aligned(16))) float fin[NV][DVS];      // column sums
     // token-pair scalars: A[t][i] = beta_t e^{G_t-G_i} k_t.k_i (i < t),
     // P[t][i] = e^{G_t-G_i} q_t.k_i (i <= t), D[t][i] = e^{G_t-G_i} (i <= t)
     __shared__ float Am[kMaxDecT][kMaxDecT], Pm[kMaxDecT][kMaxDecT], Dm[kMaxDecT][kMaxDecT];
     __shared__ float Gs[kMaxDecT], Bs[kMaxDecT];   // G_t and beta_t
 
-    const int head = blockIdx.x;             // flattened (sequence, head)
+    const int head = blockIdx.x / kDecColSplit;   // flattened (sequence, head)
     const int n = head / H, h = head % H;
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
-    const int c = (tid % TPR) * 4;
-    const int r0 = (tid / TPR) * RPT;        // first of this thread's rows
+    const int cl = (tid % TPR) * 4;               // column within this workgroup's half
+    const int c = (blockIdx.x % kDecColSplit) * DVS + cl;
+    const int r0 = (tid / TPR) * RPT;             // first of this thread's rows
     auto tok = [&](int t) { return (size_t)(n * T + t) * H + h; };   // (token, head) row
 
     float* S = state + (size_t)head * DK * DV;
@@ -243,13 +249,13 @@ decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const 
                     pq[j] += __shfl_xor(pq[j], o, kWave);
                 }
             if (lane < TPR) {
-                *reinterpret_cast<floatx4*>(&red[wave][2 * t][c]) = floatx4{pk[0], pk[1], pk[2], pk[3]};
-                *reinterpret_cast<floatx4*>(&red[wave][2 * t + 1][c]) = floatx4{pq[0], pq[1], pq[2], pq[3]};
+                *reinterpret_cast<floatx4*>(&red[wave][2 * t][cl]) = floatx4{pk[0], pk[1], pk[2], pk[3]};
+                *reinterpret_cast<floatx4*>(&red[wave][2 * t + 1][cl]) = floatx4{pq[0], pq[1], pq[2], pq[3]};
             }
         }
     }
     __syncthreads();
-    for (int e = tid; e < 2 * T * DV; e += kDecMultiThreads) {   // across the waves, once
+    for (int e = tid; e < 2 * T * DVS; e += kDecMultiThreads) {   // across the waves, once
         float acc = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) acc += (&red[w][0][0])[e];
@@ -263,8 +269,8 @@ decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const 
     for (int t = 0; t < kMaxDecT; ++t) {
         if (t < T) {
             const float gt = expf(Gs[t]), bt = Bs[t];
-            const floatx4 sk = *reinterpret_cast<const floatx4*>(&fin[2 * t][c]);
-            const floatx4 sq = *reinterpret_cast<const floatx4*>(&fin[2 * t + 1][c]);
+            const floatx4 sk = *reinterpret_cast<const floatx4*>(&fin[2 * t][cl]);
+            const floatx4 sq = *reinterpret_cast<const floatx4*>(&fin[2 * t + 1][cl]);
             float yo[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -321,8 +327,9 @@ static void launch_dec_multi_t(const void* q, const void* k, const void* v, int 
                                const float* g, const float* beta, float* state, int heads, int T,
                                int H, void* y, int y_bf16, float* steps, hipStream_t s) {
 #define GDN_DECM(TI, TO)                                                                        \
-    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, MT, TI, TO>), dim3(heads), dim3(kDecMultiThreads), \
-                       0, s, static_cast<const TI*>(q), static_cast<const TI*>(k),               \
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, MT, TI, TO>), dim3(heads * kDecColSplit),       \
+                       dim3(kDecMultiThreads), 0, s, static_cast<const TI*>(q),                   \
+                       static_cast<const TI*>(k),                                                \
                        static_cast<const TI*>(v), g, beta, state, static_cast<TO*>(y), steps, T, H)
     if (in_bf16 && y_bf16) GDN_DECM(uint16_t, uint16_t);
     else if (in_bf16) GDN_DECM(uint16_t, float);
