@@ -64,6 +64,11 @@ def _load():
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, _dp, _dp, ctypes.c_int]
         lib.gdn_oracle_recurrence.restype = ctypes.c_int
+        lib.gdn_oracle_recurrence_backward.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip,
+                                                       ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.c_int, _dp, _dp, _dp, _dp, _dp,
+                                                       _dp, _dp, _dp, ctypes.c_int]
+        lib.gdn_oracle_recurrence_backward.restype = ctypes.c_int
         lib.gdn_oracle_output_gate.argtypes = [_dp, _dp, _dp, ctypes.c_long, ctypes.c_int,
                                                ctypes.c_double, _dp]
         _lib = lib
@@ -168,6 +173,31 @@ def recurrence(q, k, v, alpha, beta, S0=None, cu_seqlens=None, closed_form=False
                                   cu.ctypes.data_as(_ip), nseq, H, dk, dv, int(closed_form),
                                   _p(y), _p(ST), nthreads or default_threads())
     return y, ST
+
+
+def recurrence_backward(q, k, v, alpha, beta, dy, S0=None, dST=None, cu_seqlens=None,
+                        nthreads=None):
+    """Gradients of eqs. 1-4 (reverse mode, token by token). Shapes as recurrence(); dy like
+    y, dST like S_T (None = zero). Returns dict(dq, dk, dv, dalpha, dbeta, dg, dS0) where
+    dg = dalpha * alpha is the gradient with respect to g = log alpha."""
+    q, k, v, alpha, beta, dy = (_d(x) for x in (q, k, v, alpha, beta, dy))
+    ntok, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = [0, ntok]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    nseq = len(cu) - 1
+    s0 = None if S0 is None else _d(S0)
+    dst = None if dST is None else _d(dST)
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dalpha=np.zeros_like(alpha), dbeta=np.zeros_like(beta),
+               dS0=np.zeros((nseq, H, dk, dv)))
+    _load().gdn_oracle_recurrence_backward(
+        _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(s0), cu.ctypes.data_as(_ip), nseq, H, dk,
+        dv, _p(dy), _p(dst), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dalpha"]),
+        _p(out["dbeta"]), _p(out["dS0"]), nthreads or default_threads())
+    out["dg"] = out["dalpha"] * alpha
+    return out
 
 
 # ------------------------------------------------------------------ eq. 11 without W_o

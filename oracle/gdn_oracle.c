@@ -228,6 +228,181 @@ int gdn_oracle_recurrence(const double* q, const double* k, const double* v, con
     return 0;
 }
 
+/* ------------------------------------------------------------------ gradients of eqs. 1-4 */
+
+/* Reverse-mode derivative of the recurrence above (eqs. 1-4 as written), token by token in
+ * reverse order: given dL/dy for every token and dL/dS_T, it returns dL/d(q, k, v, alpha,
+ * beta, S0). Each token's step is undone in the opposite order of its forward operations:
+ *   y = S^T q             -> dq = S dy,  dS += q dy^T
+ *   S = S~ + beta k e^T   -> dbeta = k^T dS e,  dk += beta dS e,  de = beta dS^T k,  dS~ = dS
+ *   e = v - S~^T k        -> dv = de,  dS~ -= k de^T,  dk -= S~ de
+ *   S~ = alpha S_prev     -> dalpha = <dS~, S_prev>,  dS_prev = alpha dS~
+ * The state before each token is recomputed from checkpoints taken every CK tokens of the
+ * forward pass (the forward is the plain recurrence of eqs. 1-4). */
+#define CK 64
+
+typedef struct {
+    const double *q, *k, *v, *alpha, *beta, *S0, *dy, *dST;
+    const int* cu;
+    int nseq, H, dk, dv;
+    double *dq, *dk_, *dv_, *dalpha, *dbeta, *dS0;
+    int next;
+    pthread_mutex_t mu;
+} bwd_job;
+
+/* S <- state after token `row` from the state before it (eqs. 1-3); e receives the residual */
+static void fwd_token(const bwd_job* J, long row, double* S, double* e) {
+    const int dk = J->dk, dv = J->dv;
+    const double* k = J->k + row * dk;
+    const double* v = J->v + row * dv;
+    const double a = J->alpha[row], b = J->beta[row];
+    for (long i = 0; i < (long)dk * dv; ++i) S[i] = a * S[i];
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * k[i];
+        e[j] = v[j] - acc;
+    }
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * k[i] * e[j];
+}
+
+static void bwd_pair(bwd_job* J, int s, int h, double* ckpt, double* prev, double* S, double* dS,
+                     double* e, double* de) {
+    const int H = J->H, dk = J->dk, dv = J->dv;
+    const long sz = (long)dk * dv;
+    const int t0 = J->cu[s], t1 = J->cu[s + 1];
+    const int nck = (t1 - t0 + CK - 1) / CK;
+    /* forward: checkpoints of the state before each CK-token block */
+    if (J->S0) memcpy(S, J->S0 + ((long)s * H + h) * sz, sizeof(double) * sz);
+    else memset(S, 0, sizeof(double) * sz);
+    for (int c = 0; c < nck; ++c) {
+        memcpy(ckpt + (long)c * sz, S, sizeof(double) * sz);
+        for (int t = t0 + c * CK; t < t0 + (c + 1) * CK && t < t1; ++t)
+            fwd_token(J, (long)t * H + h, S, e);
+    }
+    /* reverse */
+    if (J->dST) memcpy(dS, J->dST + ((long)s * H + h) * sz, sizeof(double) * sz);
+    else memset(dS, 0, sizeof(double) * sz);
+    for (int c = nck - 1; c >= 0; --c) {
+        const int ta = t0 + c * CK, tb = (ta + CK < t1) ? ta + CK : t1;
+        /* states before each token of the block */
+        memcpy(S, ckpt + (long)c * sz, sizeof(double) * sz);
+        for (int t = ta; t < tb; ++t) {
+            memcpy(prev + (long)(t - ta) * sz, S, sizeof(double) * sz);
+            fwd_token(J, (long)t * H + h, S, e);
+        }
+        for (int t = tb - 1; t >= ta; --t) {
+            const long row = (long)t * H + h;
+            const double* Sp = prev + (long)(t - ta) * sz;   /* S_{t-1} */
+            const double* q = J->q + row * dk;
+            const double* k = J->k + row * dk;
+            const double* v = J->v + row * dv;
+            const double* dy = J->dy + row * dv;
+            const double a = J->alpha[row], b = J->beta[row];
+            double* dq = J->dq + row * dk;
+            double* dkk = J->dk_ + row * dk;
+            double* dvv = J->dv_ + row * dv;
+            /* recompute S~ = a S_prev (into S), e, and S_t (into S after the write) */
+            for (long i = 0; i < sz; ++i) S[i] = a * Sp[i];
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * k[i];
+                e[j] = v[j] - acc;
+            }
+            /* y = S_t^T q with S_t = S~ + b k e^T */
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j)
+                    acc += (S[(long)i * dv + j] + b * k[i] * e[j]) * dy[j];
+                dq[i] = acc;
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) dS[(long)i * dv + j] += q[i] * dy[j];
+            /* S_t = S~ + b k e^T */
+            double db = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) acc += dS[(long)i * dv + j] * e[j];
+                db += k[i] * acc;
+                dkk[i] = b * acc;
+            }
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += dS[(long)i * dv + j] * k[i];
+                de[j] = b * acc;
+            }
+            /* e = v - S~^T k */
+            for (int j = 0; j < dv; ++j) dvv[j] = de[j];
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) acc += S[(long)i * dv + j] * de[j];
+                dkk[i] -= acc;
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) dS[(long)i * dv + j] -= k[i] * de[j];
+            /* S~ = a S_prev */
+            double da = 0.0;
+            for (long i = 0; i < sz; ++i) da += dS[i] * Sp[i];
+            for (long i = 0; i < sz; ++i) dS[i] *= a;
+            J->dalpha[row] = da;
+            J->dbeta[row] = db;
+        }
+    }
+    if (J->dS0) memcpy(J->dS0 + ((long)s * H + h) * sz, dS, sizeof(double) * sz);
+}
+
+static void* bwd_worker(void* arg) {
+    bwd_job* J = (bwd_job*)arg;
+    const long sz = (long)J->dk * J->dv;
+    double* ckpt = NULL;
+    int maxck = 1;
+    for (int s = 0; s < J->nseq; ++s) {
+        int n = (J->cu[s + 1] - J->cu[s] + CK - 1) / CK;
+        if (n > maxck) maxck = n;
+    }
+    ckpt = (double*)malloc(sizeof(double) * (size_t)(sz * maxck));
+    double* prev = (double*)malloc(sizeof(double) * (size_t)(sz * CK));
+    double* S = (double*)malloc(sizeof(double) * (size_t)sz);
+    double* dS = (double*)malloc(sizeof(double) * (size_t)sz);
+    double* e = (double*)malloc(sizeof(double) * (size_t)J->dv);
+    double* de = (double*)malloc(sizeof(double) * (size_t)J->dv);
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int p = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (p >= J->nseq * J->H) break;
+        bwd_pair(J, p / J->H, p % J->H, ckpt, prev, S, dS, e, de);
+    }
+    free(ckpt); free(prev); free(S); free(dS); free(e); free(de);
+    return NULL;
+}
+
+/* Gradients of eqs. 1-4 over packed sequences. Inputs as gdn_oracle_recurrence plus
+ * dy [ntok,H,dv] and dST [nseq,H,dk,dv] (nullable => zero). Outputs dq, dk [ntok,H,dk],
+ * dv [ntok,H,dv], dalpha, dbeta [ntok,H], dS0 [nseq,H,dk,dv] (nullable). Returns 0. */
+int gdn_oracle_recurrence_backward(const double* q, const double* k, const double* v,
+                                   const double* alpha, const double* beta, const double* S0,
+                                   const int* cu, int nseq, int H, int dk, int dv,
+                                   const double* dy, const double* dST, double* dq, double* dk_,
+                                   double* dv_, double* dalpha, double* dbeta, double* dS0,
+                                   int nthreads) {
+    bwd_job J;
+    J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.S0 = S0; J.dy = dy; J.dST = dST;
+    J.cu = cu; J.nseq = nseq; J.H = H; J.dk = dk; J.dv = dv;
+    J.dq = dq; J.dk_ = dk_; J.dv_ = dv_; J.dalpha = dalpha; J.dbeta = dbeta; J.dS0 = dS0;
+    J.next = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    int pairs = nseq * H;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pairs) nthreads = pairs > 0 ? pairs : 1;
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, bwd_worker, &J);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ eq. 11 (without W_o) */
 
 /* o = sigmoid(z) * RMSNorm(y) with zero-centred gain: RMSNorm(y) = (1 + w) * y / sqrt(mean y^2 + eps).

@@ -373,3 +373,66 @@ def test_bf16_storage_rounding_matches_torch():
     x = np.random.default_rng(25).standard_normal(50000) * 7
     ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
     assert np.array_equal(oracle.round_bf16(x), ref)
+
+
+# ---------------------------------------------------------------- gradients of eqs. 1-4
+def _fd_check(T, H, dk, dv, cu, seed, n_probe=None):
+    """Central finite differences of L = <y, Wy> + <S_T, WS> against the oracle's reverse-mode
+    gradients, for every input element (or n_probe random ones per input)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    al = rng.uniform(0.5, 0.99, (T, H))
+    be = rng.uniform(0.1, 0.9, (T, H))
+    nseq = len(cu) - 1
+    S0 = rng.standard_normal((nseq, H, dk, dv))
+    Wy = rng.standard_normal((T, H, dv))
+    WS = rng.standard_normal((nseq, H, dk, dv))
+
+    def loss():
+        y, ST = oracle.recurrence(q, k, v, al, be, S0, cu, nthreads=1)
+        return float((y * Wy).sum() + (ST * WS).sum())
+
+    grads = oracle.recurrence_backward(q, k, v, al, be, Wy, S0, WS, cu, nthreads=1)
+    h = 1e-6
+    for arr, key in ((q, "dq"), (k, "dk"), (v, "dv"), (al, "dalpha"), (be, "dbeta"), (S0, "dS0")):
+        idxs = list(np.ndindex(arr.shape))
+        if n_probe is not None:
+            idxs = [idxs[i] for i in rng.choice(len(idxs), min(n_probe, len(idxs)), replace=False)]
+        for idx in idxs:
+            a0 = arr[idx]
+            arr[idx] = a0 + h
+            lp = loss()
+            arr[idx] = a0 - h
+            lm = loss()
+            arr[idx] = a0
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grads[key][idx]) <= 1e-6 * max(1.0, abs(fd)), (key, idx, fd, grads[key][idx])
+    return grads
+
+
+def test_backward_matches_finite_differences():
+    _fd_check(T=9, H=2, dk=3, dv=4, cu=[0, 4, 4, 9], seed=30)     # includes an empty sequence
+
+
+def test_backward_across_checkpoint_blocks_matches_finite_differences():
+    # 150 tokens: the oracle recomputes states from checkpoints every 64 tokens
+    _fd_check(T=150, H=1, dk=2, dv=3, cu=[0, 150], seed=31, n_probe=12)
+
+
+def test_backward_zero_write_is_pure_decay():
+    # beta = 0: S_T = (prod alpha) S0 and y_t = (prod_{i<=t} alpha_i) S0^T q_t, so with dy = 0
+    # the state gradient is transported back with the same product
+    rng = np.random.default_rng(32)
+    T, dk, dv = 20, 4, 5
+    q, k = rng.standard_normal((T, 1, dk)), rng.standard_normal((T, 1, dk))
+    v = rng.standard_normal((T, 1, dv))
+    al = rng.uniform(0.6, 0.99, (T, 1))
+    be = np.zeros((T, 1))
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    dST = rng.standard_normal((1, 1, dk, dv))
+    g = oracle.recurrence_backward(q, k, v, al, be, np.zeros((T, 1, dv)), S0, dST)
+    assert np.allclose(g["dS0"], np.prod(al) * dST, rtol=1e-13, atol=0)
+    assert np.all(g["dv"] == 0.0)
+    assert np.allclose(g["dg"], np.full((T, 1), np.sum(dST * np.prod(al) * S0)), rtol=1e-12)
