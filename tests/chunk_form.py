@@ -41,3 +41,115 @@ def chunked_forward(q, k, v, g, beta, S0=None, cu_seqlens=None, C=64):
                 S = gam[-1] * S + (np.exp(G[-1] - G)[:, None] * K).T @ U
             ST[s, h] = S
     return y, ST
+
+
+def chunked_backward(q, k, v, g, beta, dy, S0=None, dST=None, cu_seqlens=None, C=64):
+    """Reverse-mode derivative of chunked_forward, chunk by chunk in reverse order, from the
+    state at each chunk start (recomputed by a forward sweep). Per chunk, with
+    KS = K S, R = beta o (V - gamma o KS), U = T R, W = w o U (w_r = e^{G_C - G_r}),
+    Y = gamma o (Q S) + P U and S' = gamma_C S + K^T W, the adjoints are taken in the
+    reverse order of those products. Returns dict(dq, dk, dv, dg, dbeta, dS0)."""
+    ntok, H, dk = q.shape
+    dv = v.shape[2]
+    cu = [0, ntok] if cu_seqlens is None else list(cu_seqlens)
+    nseq = len(cu) - 1
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dg=np.zeros_like(g), dbeta=np.zeros_like(beta), dS0=np.zeros((nseq, H, dk, dv)))
+    for s in range(nseq):
+        for h in range(H):
+            starts = list(range(cu[s], cu[s + 1], C))
+            S = np.zeros((dk, dv)) if S0 is None else S0[s, h].copy()
+            Sc = []
+            for c0 in starts:                      # forward: the state at each chunk start
+                Sc.append(S.copy())
+                sl = slice(c0, min(c0 + C, cu[s + 1]))
+                _, S = _chunk_fwd(q[sl, h], k[sl, h], v[sl, h], g[sl, h], beta[sl, h], S)
+            dS = np.zeros((dk, dv)) if dST is None else dST[s, h].copy()
+            for c0, S in zip(reversed(starts), reversed(Sc)):
+                sl = slice(c0, min(c0 + C, cu[s + 1]))
+                grads, dS = _chunk_bwd(q[sl, h], k[sl, h], v[sl, h], g[sl, h], beta[sl, h], S,
+                                       dy[sl, h], dS)
+                for key in ("dq", "dk", "dv"):
+                    out[key][sl, h] = grads[key]
+                out["dg"][sl, h] = grads["dg"]
+                out["dbeta"][sl, h] = grads["dbeta"]
+            out["dS0"][s, h] = dS
+    return out
+
+
+def _chunk_parts(Q, K, V, g, b, S):
+    n = len(g)
+    G = np.cumsum(g)
+    D = G[:, None] - G[None, :]
+    low = np.tril(np.ones((n, n)), -1).astype(bool)
+    incl = np.tril(np.ones((n, n))).astype(bool)
+    EA = np.where(low, np.exp(np.where(low, D, 0.0)), 0.0)
+    EP = np.where(incl, np.exp(np.where(incl, D, 0.0)), 0.0)
+    KK, QK = K @ K.T, Q @ K.T
+    A = b[:, None] * EA * KK
+    T = np.linalg.inv(np.eye(n) + A)
+    gam = np.exp(G)
+    KS = K @ S
+    R = b[:, None] * (V - gam[:, None] * KS)
+    U = T @ R
+    P = EP * QK
+    w = np.exp(G[-1] - G)
+    return dict(G=G, EA=EA, EP=EP, KK=KK, QK=QK, A=A, T=T, gam=gam, KS=KS, R=R, U=U, P=P, w=w,
+                low=low, incl=incl)
+
+
+def _chunk_fwd(Q, K, V, g, b, S):
+    p = _chunk_parts(Q, K, V, g, b, S)
+    Y = p["gam"][:, None] * (Q @ S) + p["P"] @ p["U"]
+    S1 = p["gam"][-1] * S + K.T @ (p["w"][:, None] * p["U"])
+    return Y, S1
+
+
+def _chunk_bwd(Q, K, V, g, b, S, dY, dS1):
+    p = _chunk_parts(Q, K, V, g, b, S)
+    gam, w, U, R, KS, T = p["gam"], p["w"], p["U"], p["R"], p["KS"], p["T"]
+    n = len(g)
+    W = w[:, None] * U
+    # S' = gamma_C S + K^T W
+    dS = gam[-1] * dS1
+    dgamC = np.sum(S * dS1)
+    dK = W @ dS1.T
+    dW = K @ dS1
+    # W = w o U
+    dU = w[:, None] * dW
+    dw = np.sum(dW * U, axis=1)
+    # Y = gamma o (Q S) + P U
+    QS = Q @ S
+    dQ = gam[:, None] * (dY @ S.T)
+    dS = dS + Q.T @ (gam[:, None] * dY)
+    dgam = np.sum(dY * QS, axis=1)
+    dP = np.where(p["incl"], dY @ U.T, 0.0)
+    dU = dU + p["P"].T @ dY
+    # U = T R
+    dR = T.T @ dU
+    dA = np.where(p["low"], -dR @ U.T, 0.0)
+    # R = b o (V - gamma o KS)
+    dV = b[:, None] * dR
+    db = np.sum(dR * (V - gam[:, None] * KS), axis=1)
+    dKS = -(b * gam)[:, None] * dR
+    dgam = dgam - b * np.sum(dR * KS, axis=1)
+    # KS = K S
+    dK = dK + dKS @ S.T
+    dS = dS + K.T @ dKS
+    # A = b o EA o K K^T (strictly lower)
+    dKK = dA * b[:, None] * p["EA"]
+    dK = dK + dKK @ K + dKK.T @ K
+    db = db + np.sum(dA * p["EA"] * p["KK"], axis=1)
+    dD = dA * p["A"]
+    # P = EP o Q K^T (lower, with the diagonal)
+    dQK = dP * p["EP"]
+    dQ = dQ + dQK @ K
+    dK = dK + dQK.T @ Q
+    dD = dD + dP * p["P"]
+    # D = G_r - G_i; gamma = e^G; gamma_C = gamma_{n-1}; w = e^{G_C - G}
+    dG = dD.sum(axis=1) - dD.sum(axis=0) + dgam * gam
+    dG[n - 1] += dgamC * gam[-1] + np.sum(dw * w)
+    dG = dG - dw * w
+    # G = cumsum(g)
+    dg = np.cumsum(dG[::-1])[::-1]
+    return dict(dq=dQ, dk=dK, dv=dV, dg=dg, dbeta=db), dS

@@ -22,3 +22,25 @@ def test_chunked_form_is_exact(C):
     y, s = chunked_forward(q, k, v, g, beta, S0, cu, C=C)
     assert np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref) < 1e-12
     assert np.linalg.norm(s - s_ref) / np.linalg.norm(s_ref) < 1e-12
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_chunked_backward_is_exact(C):
+    from chunk_form import chunked_backward
+    rng = np.random.default_rng(4)
+    ntok, H, dk, dv = 200, 2, 16, 12
+    q = rng.standard_normal((ntok, H, dk))
+    k = rng.standard_normal((ntok, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((ntok, H, dv))
+    g = -np.exp(rng.uniform(0, np.log(16), H)) * np.log1p(np.exp(rng.standard_normal((ntok, H)) - 4.6))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((ntok, H))))
+    S0 = rng.standard_normal((3, H, dk, dv)) * 0.1
+    dy = rng.standard_normal((ntok, H, dv))
+    dST = rng.standard_normal((3, H, dk, dv))
+    cu = [0, 90, 91, 200]
+    ref = oracle.recurrence_backward(q, k, v, np.exp(g), beta, dy, S0, dST, cu)
+    got = chunked_backward(q, k, v, g, beta, dy, S0, dST, cu, C=C)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        err = np.linalg.norm(got[key] - ref[key]) / np.linalg.norm(ref[key])
+        assert err < 1e-11, (key, err)
