@@ -9,6 +9,7 @@ The functions keep the C names:
   gdn_chunk_prefill  eqs. (1)-(4)   chunkwise (C = 64) gated delta rule over packed sequences
   gdn_preprocess_stateful           the same for sequences that continue earlier input
                                     (carried conv history in and out)
+  gdn_chunk_backward eqs. (1)-(4)   gradients of the chunked prefill (dq, dk, dv, dg, dbeta, dS0)
   gdn_decode_step    eqs. (1)-(4)   one token per sequence, state updated in place
   gdn_decode_multi   eqs. (1)-(4)   T <= 8 tokens per sequence (multi-token prediction
                                     verify) in one pass over each state
@@ -61,6 +62,12 @@ def lib():
         L.gdn_chunk_prefill.restype = _i
         L.gdn_chunk_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                         _i, _i, _i, _vp, _i, _vp, ctypes.c_size_t, _vp]
+        L.gdn_chunk_backward_workspace_size.restype = ctypes.c_size_t
+        L.gdn_chunk_backward_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+        L.gdn_chunk_backward.restype = _i
+        L.gdn_chunk_backward.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp,
+                                         _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         ctypes.c_size_t, _vp]
         L.gdn_decode_step.restype = _i
         L.gdn_decode_step.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i,
                                       _vp]
@@ -232,6 +239,47 @@ def gdn_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
     return y, final_state
 
 
+def gdn_chunk_backward_workspace_size(ntok, num_seqs, H, dk, dv) -> int:
+    return int(lib().gdn_chunk_backward_workspace_size(ntok, num_seqs, H, dk, dv))
+
+
+def gdn_chunk_backward(q, k, v, g, beta, dy, *, initial_state=None, dfinal_state=None,
+                       cu_seqlens=None, cu_seqlens_host=None, num_seqs=1, workspace=None,
+                       want_dinitial_state=True, stream=None):
+    """Gradients of gdn_chunk_prefill. Inputs as its forward (q,k,v bf16/fp32; g, beta fp32),
+    dy [ntok,H,dv] (bf16/fp32), dfinal_state [num_seqs,H,dk,dv] fp32 or None.
+    Returns dict(dq, dk, dv, dg, dbeta, dinitial_state) of fp32 tensors."""
+    ntok, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    f32 = torch.float32
+    out = dict(dq=torch.empty((ntok, H, dk), dtype=f32, device=dev),
+               dk=torch.empty((ntok, H, dk), dtype=f32, device=dev),
+               dv=torch.empty((ntok, H, dv), dtype=f32, device=dev),
+               dg=torch.empty((ntok, H), dtype=f32, device=dev),
+               dbeta=torch.empty((ntok, H), dtype=f32, device=dev),
+               dinitial_state=(torch.empty((num_seqs, H, dk, dv), dtype=f32, device=dev)
+                               if want_dinitial_state else None))
+    need = gdn_chunk_backward_workspace_size(ntok, num_seqs, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+    st = lib().gdn_chunk_backward(
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _dtype_tag(q), _ptr(g, "g", f32),
+        _ptr(beta, "beta", f32), _ptr(initial_state, "initial_state", f32), _ptr(dy, "dy"),
+        _dtype_tag(dy), _ptr(dfinal_state, "dfinal_state", f32),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32),
+        ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
+        _ptr(out["dq"], "dq"), _ptr(out["dk"], "dk"), _ptr(out["dv"], "dv"), _ptr(out["dg"], "dg"),
+        _ptr(out["dbeta"], "dbeta"), _ptr(out["dinitial_state"], "dinitial_state"),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "gdn_chunk_backward")
+    return out
+
+
 def gdn_decode_step(q, k, v, g, beta, state, *, y=None, y_dtype=None, stream=None):
     """One token per sequence. q,k: [N,H,dk], v: [N,H,dv]; g,beta: [N,H] fp32;
     state: [N,H,dk,dv] fp32 updated in place. Returns y [N,H,dv]."""
@@ -286,5 +334,6 @@ def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream
 
 
 __all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_preprocess_stateful",
-           "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_decode_step",
+           "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_chunk_backward",
+           "gdn_chunk_backward_workspace_size", "gdn_decode_step",
            "gdn_decode_multi", "gdn_output_gate"]

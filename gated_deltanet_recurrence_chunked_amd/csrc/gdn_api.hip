@@ -230,6 +230,45 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
     return hip_status(gdn::launch_chunk_fp32(a, s), "gdn_chunk_prefill");
 }
 
+size_t gdn_chunk_backward_workspace_size(int ntok, int num_seqs, int H, int dk, int dv) {
+    if (ntok < 0 || num_seqs < 1 || H < 1 || !valid_dim(dk) || !valid_dim(dv)) return 0;
+    return gdn::chunk_bwd_workspace(ntok, num_seqs, H, dk, dv);
+}
+
+int gdn_chunk_backward(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                       const float* beta, const float* initial_state, const void* dy,
+                       int dy_dtype, const float* dfinal_state, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
+                       int dv, float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                       float* dinitial_state, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    GDN_REQUIRE(valid_dtype(in_dtype) && valid_dtype(dy_dtype), GDN_ERR_DTYPE,
+                "in_dtype/dy_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need H >= 1 and dk, dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
+    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(dy);
+    GDN_PTR(dq); GDN_PTR(dk_out); GDN_PTR(dv_out); GDN_SPTR(dg); GDN_SPTR(dbeta);
+    GDN_OPT_PTR(initial_state); GDN_OPT_PTR(dfinal_state); GDN_OPT_PTR(dinitial_state);
+    GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+    GDN_REQUIRE(cu_seqlens_host == nullptr || cu_seqlens != nullptr, GDN_ERR_NULL,
+                "cu_seqlens_host given without the device cu_seqlens");
+    int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
+    if (st) return st;
+    const size_t need = gdn::chunk_bwd_workspace(ntok, num_seqs, H, dk, dv);
+    GDN_REQUIRE(workspace_bytes >= need && workspace != nullptr, GDN_ERR_WORKSPACE,
+                "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    GDN_OPT_PTR(workspace);
+    gdn::ChunkBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.dy = dy;
+    a.in_bf16 = in_dtype == GDN_BF16; a.dy_bf16 = dy_dtype == GDN_BF16;
+    a.g = g; a.beta = beta; a.S0 = initial_state; a.dST = dfinal_state; a.cu = cu_seqlens;
+    a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.dk = dk; a.dv = dv;
+    a.dq = dq; a.dk_ = dk_out; a.dv_ = dv_out; a.dg = dg; a.dbeta = dbeta;
+    a.dS0 = dinitial_state; a.workspace = workspace;
+    return hip_status(gdn::launch_chunk_bwd(a, static_cast<hipStream_t>(stream)),
+                      "gdn_chunk_backward");
+}
+
 int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, const float* g,
                     const float* beta, float* state, int N, int H, int dk, int dv, void* y,
                     int y_dtype, void* stream) {

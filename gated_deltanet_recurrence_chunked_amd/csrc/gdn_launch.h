@@ -59,4 +59,17 @@ hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t s);
 size_t chunk_bf16_workspace(int ntok, int num_seqs, int H);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s);
 
+// backward of the chunked gated delta rule (fp32 vector ALU)
+struct ChunkBwdArgs {
+    const void *q, *k, *v, *dy;
+    int in_bf16, dy_bf16;
+    const float *g, *beta, *S0, *dST;
+    const int32_t* cu;    // NULL: equal lengths
+    int num_seqs, ntok, H, dk, dv;
+    float *dq, *dk_, *dv_, *dg, *dbeta, *dS0;
+    void* workspace;
+};
+size_t chunk_bwd_workspace(int ntok, int num_seqs, int H, int dk, int dv);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t s);
+
 }  // namespace gdn

@@ -235,6 +235,16 @@ def make_inputs(cfg: int, seed: int = 0, **ov) -> dict:
     return out
 
 
+def grad_draws(seed: int, ntok: int, num_seqs: int, H: int, dk: int, dv: int,
+               bf16: bool = False) -> dict:
+    """Upstream gradients for a backward pass: dy [ntok, H, dv] ~ N(0,1) (bf16 bits if bf16)
+    and dST [num_seqs, H, dk, dv] ~ N(0,1) fp32."""
+    kids = np.random.SeedSequence([SEED_TAG, 66, seed]).spawn(2)
+    r1, r2 = (np.random.default_rng(k) for k in kids)
+    dy = _normal_bf16(r1, (ntok, H, dv)) if bf16 else _normal(r1, (ntok, H, dv))
+    return dict(dy=dy, dST=_normal(r2, (num_seqs, H, dk, dv)))
+
+
 def conv_state_draw(seed: int, num_seqs: int, H: int, dk: int, dv: int,
                     conv_k: int = 4) -> np.ndarray:
     """A carried conv history [num_seqs, conv_k-1, H*(2dk+dv)] of bf16 N(0,1) bits, as if the

@@ -152,6 +152,34 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
                       int dv, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Bytes of device workspace gdn_chunk_backward needs for these sizes. */
+size_t gdn_chunk_backward_workspace_size(int ntok, int num_seqs, int H, int dk, int dv);
+
+/*
+ * gdn_chunk_backward - gradients of gdn_chunk_prefill for training: given dL/dy and
+ * dL/dS_T, the gradients with respect to q, k, v, g (= log alpha), beta and S0 of
+ * eqs. (1)-(4) (section 2.1.1; the reading notes' "Kernel 效率" cites backward speedups
+ * for chunked GDN kernels, and their section 3.1 trains the decay and beta projections
+ * with AdamW). Computed chunkwise (C = 64) in fp32: a forward sweep stores the state at
+ * every chunk start in the workspace, a reverse sweep carries dS back through the chunks.
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, num_seqs, ntok, H, dk, dv:
+ *       as gdn_chunk_prefill (the forward's inputs; q, k, v in in_dtype).
+ *   dy: [ntok, H, dv] in dy_dtype - dL/dy.
+ *   dfinal_state: [num_seqs, H, dk, dv] fp32 dL/dS_T, or NULL (zero).
+ *   dq, dk_out: [ntok, H, dk]; dv_out: [ntok, H, dv]; dg, dbeta: [ntok, H]: fp32 outputs.
+ *   dinitial_state: [num_seqs, H, dk, dv] fp32 dL/dS0, or NULL (not written).
+ *   workspace: at least gdn_chunk_backward_workspace_size(...) bytes of device scratch.
+ *   Results are deterministic (no atomics). All outputs are overwritten.
+ */
+int gdn_chunk_backward(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                       const float* beta, const float* initial_state, const void* dy,
+                       int dy_dtype, const float* dfinal_state, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
+                       int dv, float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                       float* dinitial_state, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /*
  * gdn_decode_step - one token per sequence through eqs. (1)-(4), state updated in place:
  * S <- alpha S; e = v - S^T k; S <- S + beta k e^T; y = S^T q.

@@ -1,0 +1,86 @@
+"""GPU parity of gdn_chunk_backward (gradients of the chunked prefill) against the fp64
+oracle's reverse-mode gradients of eqs. (1)-(4), token by token. The backward computes in
+fp32 throughout, so the bar is the fp32 path's (1e-4 relative L2 per (sequence, head))."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_recurrence_chunked_amd import inputs as gi
+import gdn_cases as C
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def _announce(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _f32(a):
+    return C.dev(np.ascontiguousarray(a, dtype=np.float32))
+
+
+def _run(inp, grads, bf16_in, bf16_dy, seqs=None, heads=None, with_s0=True, with_dst=True):
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    sh = inp["shape"]
+    H, cu = sh.H, inp["cu_seqlens"]
+    q, k, v = (C.dev(inp[x], bf16_in) for x in ("q", "k", "v"))
+    _, _, _, g, beta = gdn.gdn_preprocess(None, None, None, None, None, None, _f32(inp["a_raw"]),
+                                          _f32(inp["b_raw"]), _f32(inp["A_log"]),
+                                          _f32(inp["dt_bias"]), H=H)
+    S0 = inp.get("S0") if with_s0 else None
+    dST = grads["dST"] if with_dst else None
+    cu_d = None if sh.equal_lengths else C.dev(cu)
+    out = gdn.gdn_chunk_backward(q, k, v, g, beta, C.dev(grads["dy"], bf16_dy),
+                                 initial_state=None if S0 is None else _f32(S0),
+                                 dfinal_state=None if dST is None else _f32(dST),
+                                 cu_seqlens=cu_d, cu_seqlens_host=None if cu_d is None else cu,
+                                 num_seqs=sh.num_seqs)
+    torch.cuda.synchronize()
+    seqs = list(range(sh.num_seqs)) if seqs is None else seqs
+    heads = list(range(H)) if heads is None else heads
+    sub = C.subset(inp, seqs=seqs, heads=heads)
+    tok, scu = sub["tok"], sub["cu"]
+    _, al, be = oracle.gates(sub["a_raw"], sub["b_raw"], sub["A_log"], sub["dt_bias"])
+    dy = gi.as_f64(grads["dy"], bf16_dy)[tok][:, heads]
+    s0 = None if S0 is None else S0.astype(np.float64)[seqs][:, heads]
+    dst = None if dST is None else dST.astype(np.float64)[seqs][:, heads]
+    ref = oracle.recurrence_backward(sub["q"], sub["k"], sub["v"], al, be, dy, s0, dst, scu)
+    rep = {}
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        got = C.gpu_slice(out[key], tok, heads)
+        rep[key] = C.assert_close(key, got, ref[key], False, cu=scu, H=len(heads))
+    got = C.gpu_state_slice(out["dinitial_state"], seqs, heads)
+    rep["dS0"] = C.assert_close("dS0", got, ref["dS0"], False, state=True)
+    print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in rep.items()}, flush=True)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_backward_fp32_inputs_ragged(gpu, dims):
+    dk, dv = dims
+    _announce(f"backward fp32 inputs, lengths [70, 1, 129, 0, 64] H=2 dk={dk} dv={dv}")
+    inp = gi.make_inputs(0, seed=5, H=2, lengths=[70, 1, 129, 0, 64], dk=dk, dv=dv)
+    inp["S0"] = gi.make_inputs(2, seed=5, H=2, T=1, dk=dk, dv=dv)["S0"].repeat(5, axis=0)
+    sh = inp["shape"]
+    grads = gi.grad_draws(5, sh.ntok, sh.num_seqs, sh.H, dk, dv)
+    _run(inp, grads, bf16_in=False, bf16_dy=False)
+
+
+@pytest.mark.parametrize("with_s0,with_dst", [(True, True), (False, False)])
+def test_backward_bf16_inputs(gpu, with_s0, with_dst):
+    _announce(f"backward bf16 inputs B=1 H=2 T=300 d=128 S0={with_s0} dST={with_dst}")
+    inp = gi.make_inputs(2, seed=6, H=2, T=300)
+    grads = gi.grad_draws(6, 300, 1, 2, 128, 128, bf16=True)
+    _run(inp, grads, bf16_in=True, bf16_dy=True, with_s0=with_s0, with_dst=with_dst)
+
+
+def test_backward_config1_shape_sampled(gpu):
+    _announce("backward at the config-1 shape (B=4 H=16 T=4096 d=128), sampled slices")
+    inp = gi.make_inputs(2, seed=7, B=4, H=16, T=4096)
+    sh = inp["shape"]
+    grads = gi.grad_draws(7, sh.ntok, sh.num_seqs, sh.H, 128, 128, bf16=True)
+    _run(inp, grads, bf16_in=True, bf16_dy=True, seqs=[0, 3], heads=[2, 13])
