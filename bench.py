@@ -52,6 +52,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
@@ -172,6 +173,40 @@ def main():
                          "peak_TFLOPs": BF16_PEAK_TFLOPS,
                          "frac": round(pf_flops / (t_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "algorithmic_flops_per_launch": pf_flops}}
+    # ------------------------------------------------------------------ backward (training)
+    backward = None
+    if not args.no_backward:
+        gen = torch.Generator(device=dev).manual_seed(0)
+        dy = torch.randn((ntok, H, dv), generator=gen, device=dev).to(bf)
+        ws_b = torch.empty(gdn.gdn_chunk_backward_workspace_size(ntok, nseq, H, dk, dv),
+                           dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return gdn.gdn_chunk_backward(outs["q"], outs["k"], outs["v"], outs["g"],
+                                          outs["beta"], dy, num_seqs=nseq, workspace=ws_b,
+                                          want_dinitial_state=False)
+        for _ in range(3):
+            bstep()
+        torch.cuda.synchronize()
+        nb = 10
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(nb):
+            bstep()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / nb
+        backward = {"workload": "gdn_chunk_backward at B=4 H=16 T=4096 d=128 (bf16 q, k, v, dy; "
+                                "fp32 gradients of q, k, v, g, beta)",
+                    "calls": nb, "us_per_call": round(bms * 1e3, 1),
+                    "Mtok_s": round(ntok / (bms * 1e-3) / 1e6, 2),
+                    "workspace_bytes": ws_b.numel(),
+                    "vs_forward_prefill": round(bms / t_pf, 2)}
+        log(f"[bench] backward {bms * 1e3:.1f} us/call ({backward['Mtok_s']} Mtok/s, "
+            f"{bms / t_pf:.1f}x the forward prefill)")
+        del dy, ws_b
+
     del X, outs, y, o, ws
     torch.cuda.empty_cache()
 
@@ -291,7 +326,8 @@ def main():
         "config": {"workload": "bf16 GDN prefill token mixer: preprocess + chunked prefill "
                                "(C=64) + output gate", "B": 4, "H": H, "T": sh.lengths[0],
                    "d_k": dk, "d_v": dv, "tokens_per_step": ntok},
-        "kernels": kernels, "roofline": roofline, "decode": decode, "cpu_baseline": cpu,
+        "kernels": kernels, "roofline": roofline, "decode": decode, "backward": backward,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

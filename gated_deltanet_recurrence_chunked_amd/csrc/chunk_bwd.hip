@@ -15,7 +15,9 @@
 // plus the q, k, beta and gate terms collected below.
 //
 // Four kernels:
-//   ap     per (chunk, head): G, A and P of the chunk (fp32 workspace);
+//   ap     per (chunk, head): G, Ak = e^{D} o KK^T (strictly lower, so A = beta o Ak),
+//          P, and T = (I + A)^{-1} (fp32 workspace; the inverse turns both triangular solves
+//          of every slice into plain products);
 //   states per (sequence, head, 16-column slice of dv): the forward sweep, storing the state at
 //          every chunk start;
 //   scan   per (sequence, head, slice): the reverse sweep; writes dv and dS0 for its columns
@@ -31,11 +33,14 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 64;
-constexpr int kBT = 256;          // threads per workgroup
+constexpr int kBT = 1024;         // threads per workgroup: 16 waves hide the LDS latency of the
+                                  // small products every chunk step is made of
 constexpr int kSL = 16;           // dv columns per scan workgroup
+constexpr int kFinT = 256;        // threads of the per-chunk-head kernels (plenty of workgroups)
+constexpr int kP = kSL + 1;       // padded row of a [64][16] tile
 
 struct BwdLayout {
-    size_t G, A, P, Sc, part, total;
+    size_t G, Ak, P, T, Sc, part, total;
     int max_chunks;
 };
 
@@ -55,8 +60,9 @@ BwdLayout bwd_layout(int ntok, int num_seqs, int H, int dk, int dv) {
         return o;
     };
     L.G = take(ch * kC * sizeof(float));
-    L.A = take(ch * kC * kC * sizeof(float));
+    L.Ak = take(ch * kC * kC * sizeof(float));
     L.P = take(ch * kC * kC * sizeof(float));
+    L.T = take(ch * kC * kC * sizeof(float));
     L.Sc = take(ch * (size_t)dk * dv * sizeof(float));
     L.part = take(ch * slices * part_floats(dk) * sizeof(float));
     L.total = off;
@@ -70,7 +76,7 @@ struct BwdArgs {
     const int32_t* cu;
     int num_seqs, ntok, H, dk, dv;
     float *dq, *dk_, *dv_, *dg, *dbeta, *dS0;
-    float *G, *A, *P, *Sc, *part;
+    float *G, *Ak, *P, *T, *Sc, *part;
 };
 
 // bounds of sequence s and its first chunk's index in the packed chunk numbering
@@ -88,8 +94,7 @@ __device__ void seq_info(const BwdArgs& a, int s, int& lo, int& hi, int& cbase) 
     }
 }
 
-// (chunk index, head) of a chunk-head workgroup -> sequence and token range; false if the
-// packed chunk index is past the last chunk
+// packed chunk index c -> its token range; false if c is past the last chunk
 __device__ bool chunk_info(const BwdArgs& a, int c, int& t0, int& n) {
     int base = 0;
     for (int s = 0; s < a.num_seqs; ++s) {
@@ -118,22 +123,27 @@ __device__ __forceinline__ float ld(const void* p, size_t i) {
     return load1(static_cast<const T*>(p) + i);
 }
 
-// ------------------------------------------------------------------ ap: G, A, P per chunk-head
+// [64][DK] rows of a token-major [ntok, H, DK] tensor (zero past n) into LDS rows of stride DK+1
+template <int DK, typename Tin, int NT = kBT>
+__device__ __forceinline__ void load_rows(const void* x, int t0, int n, int H, int h, float (*dst)[DK + 1]) {
+    for (int e = threadIdx.x; e < kC * DK; e += NT) {
+        const int r = e / DK, d = e % DK;
+        dst[r][d] = r < n ? ld<Tin>(x, ((size_t)(t0 + r) * H + h) * DK + d) : 0.f;
+    }
+}
+
+// ------------------------------------------------------------------ ap: G, Ak, P, T per chunk-head
 template <int DK, typename Tin>
-__global__ void __launch_bounds__(kBT) bwd_ap_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kFinT) bwd_ap_kernel(BwdArgs a) {
     __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1];
+    __shared__ float A[kC][kC + 1];
     __shared__ float G[kC], Bt[kC];
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int t0, n;
     if (!chunk_info(a, c, t0, n)) return;
     const int H = a.H;
-    for (int e = tid; e < kC * DK; e += kBT) {
-        const int r = e / DK, d = e % DK;
-        const bool ok = r < n;
-        const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
-        Ks[r][d] = ok ? ld<Tin>(a.k, off) : 0.f;
-        Qs[r][d] = ok ? ld<Tin>(a.q, off) : 0.f;
-    }
+    load_rows<DK, Tin, kFinT>(a.k, t0, n, H, h, Ks);
+    load_rows<DK, Tin, kFinT>(a.q, t0, n, H, h, Qs);
     if (tid < kC) {
         G[tid] = tid < n ? a.g[(size_t)(t0 + tid) * H + h] : 0.f;
         Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
@@ -149,9 +159,9 @@ __global__ void __launch_bounds__(kBT) bwd_ap_kernel(BwdArgs a) {
     __syncthreads();
     const size_t ch = (size_t)c * H + h;
     if (tid < kC) a.G[ch * kC + tid] = G[tid];
-    for (int e = tid; e < kC * kC; e += kBT) {
+    for (int e = tid; e < kC * kC; e += kFinT) {
         const int r = e / kC, i = e % kC;
-        float av = 0.f, pv = 0.f;
+        float ak = 0.f, pv = 0.f;
         if (i <= r && r < n) {
             float kk = 0.f, qk = 0.f;
             for (int d = 0; d < DK; ++d) {
@@ -160,10 +170,26 @@ __global__ void __launch_bounds__(kBT) bwd_ap_kernel(BwdArgs a) {
             }
             const float dec = expf(G[r] - G[i]);
             pv = dec * qk;
-            if (i < r) av = Bt[r] * dec * kk;
+            if (i < r) ak = dec * kk;
         }
-        a.A[ch * kC * kC + e] = av;
+        A[r][i] = Bt[r] * ak;
+        a.Ak[ch * kC * kC + e] = ak;
         a.P[ch * kC * kC + e] = pv;
+    }
+    __syncthreads();
+    // T = (I + A)^{-1}: thread c forward-substitutes column c, held in registers (fully
+    // unrolled, so every index is static); rows above c come out zero.
+    if (tid < kC) {
+        float x[kC];
+#pragma unroll
+        for (int r = 0; r < kC; ++r) {
+            float acc = r == tid ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= A[r][i] * x[i];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < kC; ++r) a.T[ch * kC * kC + r * kC + tid] = x[r];
     }
 }
 
@@ -172,9 +198,9 @@ template <int DK, typename Tin>
 __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
     __shared__ float Ks[kC][DK + 1];
     __shared__ float S[DK][kSL];
-    __shared__ float A[kC][kC + 1];
-    __shared__ float U[kC][kSL + 1];
-    __shared__ float G[kC], Bt[kC];
+    __shared__ float T[kC][kC + 1];
+    __shared__ float R[kC][kP], W[kC][kP];
+    __shared__ float gam[kC], w[kC], Bt[kC];
     const int slices = a.dv / kSL;
     const int slice = blockIdx.x % slices;
     const int h = (blockIdx.x / slices) % a.H;
@@ -195,38 +221,37 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
             const int d = e / kSL, j = e % kSL;
             a.Sc[ch * DK * dv + (size_t)d * dv + j0 + j] = S[d][j];
         }
-        for (int e = tid; e < kC * DK; e += kBT) {
-            const int r = e / DK, d = e % DK;
-            Ks[r][d] = r < n ? ld<Tin>(a.k, ((size_t)(t0 + r) * H + h) * DK + d) : 0.f;
-        }
-        for (int e = tid; e < kC * kC; e += kBT) A[e / kC][e % kC] = a.A[ch * kC * kC + e];
+        load_rows<DK, Tin>(a.k, t0, n, H, h, Ks);
+        for (int e = tid; e < kC * kC; e += kBT) T[e / kC][e % kC] = a.T[ch * kC * kC + e];
         if (tid < kC) {
-            G[tid] = a.G[ch * kC + tid];
+            const float* Gc = a.G + ch * kC;
+            gam[tid] = expf(Gc[tid]);
+            w[tid] = tid < n ? expf(Gc[n - 1] - Gc[tid]) : 0.f;
             Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
         }
         __syncthreads();
-        for (int e = tid; e < kC * kSL; e += kBT) {   // R = beta (V - gamma K S)
+        for (int e = tid; e < kC * kSL; e += kBT) {   // R = beta o (V - gamma o K S)
             const int r = e / kSL, j = e % kSL;
             float ks = 0.f;
+#pragma unroll 4
             for (int d = 0; d < DK; ++d) ks += Ks[r][d] * S[d][j];
             const float vr = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
-            U[r][j] = Bt[r] * (vr - expf(G[r]) * ks);
+            R[r][j] = Bt[r] * (vr - gam[r] * ks);
         }
         __syncthreads();
-        if (tid < kSL) {   // (I + A) U = R
-            for (int r = 1; r < n; ++r) {
-                float acc = U[r][tid];
-                for (int i = 0; i < r; ++i) acc -= A[r][i] * U[i][tid];
-                U[r][tid] = acc;
-            }
+        for (int e = tid; e < kC * kSL; e += kBT) {   // W = w o (T R)
+            const int r = e / kSL, j = e % kSL;
+            float u = 0.f;
+            for (int i = 0; i <= r; ++i) u += T[r][i] * R[i][j];
+            W[r][j] = w[r] * u;
         }
         __syncthreads();
-        const float gC = G[n - 1];
-        for (int e = tid; e < DK * kSL; e += kBT) {   // S' = gamma_C S + K^T (w o U)
+        const float gC = gam[n - 1];
+        for (int e = tid; e < DK * kSL; e += kBT) {   // S' = gamma_C S + K^T W
             const int d = e / kSL, j = e % kSL;
             float acc = 0.f;
-            for (int i = 0; i < n; ++i) acc += expf(gC - G[i]) * Ks[i][d] * U[i][j];
-            S[d][j] = expf(gC) * S[d][j] + acc;
+            for (int i = 0; i < n; ++i) acc += Ks[i][d] * W[i][j];
+            S[d][j] = gC * S[d][j] + acc;
         }
     }
 }
@@ -235,12 +260,13 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
 template <int DK, typename Tin, typename Tdy>
 __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
     __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1];
-    __shared__ float S[DK][kSL], dS[DK][kSL];        // state entering the chunk; its gradient after
-    __shared__ float Vs[kC][kSL + 1], dY[kC][kSL + 1];
-    __shared__ float A[kC][kC + 1], P[kC][kC + 1];
-    __shared__ float U[kC][kSL + 1], KS[kC][kSL + 1], dR[kC][kSL + 1];
-    __shared__ float G[kC], Bt[kC], gam[kC], w[kC];
-    __shared__ float red[kBT];
+    __shared__ float S[DK][kSL], dS[DK][kSL];        // state entering the chunk; gradient after
+    __shared__ float T[kC][kC + 1], P[kC][kC + 1];
+    // [64][16] tiles: Vr = V - gamma o KS (then reused), dY, KS, QS, U, KdS (= K dS'), dU, dR
+    __shared__ float Vr[kC][kP], dY[kC][kP], KS[kC][kP], QS[kC][kP];
+    __shared__ float U[kC][kP], KdS[kC][kP], dU[kC][kP], dR[kC][kP];
+    __shared__ float gam[kC], w[kC], Bt[kC];
+    __shared__ float red[kBT / kWave];
 
     const int slices = a.dv / kSL;
     const int slice = blockIdx.x % slices;
@@ -265,18 +291,13 @@ __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
         float* pdP = pdA + kC * kC;                // [64][64]
         float* pvec = pdP + kC * kC;               // [4][64]
         __syncthreads();
-        for (int e = tid; e < kC * DK; e += kBT) {
-            const int r = e / DK, d = e % DK;
-            const bool ok = r < n;
-            const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
-            Ks[r][d] = ok ? ld<Tin>(a.k, off) : 0.f;
-            Qs[r][d] = ok ? ld<Tin>(a.q, off) : 0.f;
-        }
+        load_rows<DK, Tin>(a.k, t0, n, H, h, Ks);
+        load_rows<DK, Tin>(a.q, t0, n, H, h, Qs);
         for (int e = tid; e < kC * kSL; e += kBT) {
             const int r = e / kSL, j = e % kSL;
             const bool ok = r < n;
             const size_t off = ((size_t)(t0 + r) * H + h) * dv + j0 + j;
-            Vs[r][j] = ok ? ld<Tin>(a.v, off) : 0.f;
+            Vr[r][j] = ok ? ld<Tin>(a.v, off) : 0.f;
             dY[r][j] = ok ? ld<Tdy>(a.dy, off) : 0.f;
         }
         for (int e = tid; e < DK * kSL; e += kBT) {
@@ -284,118 +305,99 @@ __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
             S[d][j] = a.Sc[ch * DK * dv + (size_t)d * dv + j0 + j];
         }
         for (int e = tid; e < kC * kC; e += kBT) {
-            A[e / kC][e % kC] = a.A[ch * kC * kC + e];
+            T[e / kC][e % kC] = a.T[ch * kC * kC + e];
             P[e / kC][e % kC] = a.P[ch * kC * kC + e];
         }
-        if (tid < kC) G[tid] = a.G[ch * kC + tid];
-        __syncthreads();
         if (tid < kC) {
+            const float* Gc = a.G + ch * kC;
+            gam[tid] = expf(Gc[tid]);
+            w[tid] = tid < n ? expf(Gc[n - 1] - Gc[tid]) : 0.f;
             Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
-            gam[tid] = expf(G[tid]);
-            w[tid] = tid < n ? expf(G[n - 1] - G[tid]) : 0.f;
         }
-        // dgamma_C share: <S, dS'>
+        __syncthreads();
+        // dgamma_C share <S, dS'>; KS = K S, QS = Q S, K dS'
         float sdot = 0.f;
         for (int e = tid; e < DK * kSL; e += kBT) sdot += S[e / kSL][e % kSL] * dS[e / kSL][e % kSL];
-        red[tid] = sdot;
-        __syncthreads();
-        // KS = K S and R = beta (V - gamma KS)
+        sdot = group_sum<kWave>(sdot);
+        if (tid % kWave == 0) red[tid / kWave] = sdot;
         for (int e = tid; e < kC * kSL; e += kBT) {
             const int r = e / kSL, j = e % kSL;
-            float ks = 0.f;
-            for (int d = 0; d < DK; ++d) ks += Ks[r][d] * S[d][j];
+            float ks = 0.f, qs = 0.f, kd = 0.f;
+#pragma unroll 4
+            for (int d = 0; d < DK; ++d) {
+                ks += Ks[r][d] * S[d][j];
+                qs += Qs[r][d] * S[d][j];
+                kd += Ks[r][d] * dS[d][j];
+            }
             KS[r][j] = ks;
-            U[r][j] = Bt[r] * (Vs[r][j] - gam[r] * ks);
+            QS[r][j] = qs;
+            KdS[r][j] = kd;
+            Vr[r][j] -= gam[r] * ks;                 // V - gamma o KS
         }
+        __syncthreads();
         if (tid == 0) {
             float acc = 0.f;
-            for (int i = 0; i < kBT; ++i) acc += red[i];
+            for (int i = 0; i < kBT / kWave; ++i) acc += red[i];
             pvec[3 * kC] = acc;
         }
-        __syncthreads();
-        if (tid < kSL) {   // (I + A) U = R
-            for (int r = 1; r < n; ++r) {
-                float acc = U[r][tid];
-                for (int i = 0; i < r; ++i) acc -= A[r][i] * U[i][tid];
-                U[r][tid] = acc;
-            }
-        }
-        __syncthreads();
-        // dU = w o (K dS') + P^T dY  (into dR, solved in place below)
+        // U = T R with R = beta o Vr;  dU = w o K dS' + P^T dY
         for (int e = tid; e < kC * kSL; e += kBT) {
             const int r = e / kSL, j = e % kSL;
-            float dw = 0.f;
-            for (int d = 0; d < DK; ++d) dw += Ks[r][d] * dS[d][j];
+            float u = 0.f;
+            for (int i = 0; i <= r; ++i) u += T[r][i] * (Bt[i] * Vr[i][j]);
+            U[r][j] = u;
             float pt = 0.f;
             for (int i = r; i < n; ++i) pt += P[i][r] * dY[i][j];
-            dR[r][j] = w[r] * dw + pt;
+            dU[r][j] = w[r] * KdS[r][j] + pt;
         }
         __syncthreads();
-        // per-token sums that need K dS' and QS: dw_r, dgamma (Q S part)
+        // dR = T^T dU
+        for (int e = tid; e < kC * kSL; e += kBT) {
+            const int r = e / kSL, j = e % kSL;
+            float acc = 0.f;
+            for (int i = r; i < n; ++i) acc += T[i][r] * dU[i][j];
+            dR[r][j] = acc;
+        }
+        __syncthreads();
+        // per-token sums over this slice's columns
         if (tid < kC) {
             const int r = tid;
-            float dwr = 0.f, dg1 = 0.f;
-            if (r < n) {
-                for (int j = 0; j < kSL; ++j) {
-                    float kd = 0.f, qs = 0.f;
-                    for (int d = 0; d < DK; ++d) {
-                        kd += Ks[r][d] * dS[d][j];
-                        qs += Qs[r][d] * S[d][j];
-                    }
-                    dwr += kd * U[r][j];
-                    dg1 += dY[r][j] * qs;
-                }
+            float dwr = 0.f, dg1 = 0.f, db = 0.f, dg2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < kSL; ++j) {
+                dwr += KdS[r][j] * U[r][j];
+                dg1 += dY[r][j] * QS[r][j];
+                db += dR[r][j] * Vr[r][j];
+                dg2 += dR[r][j] * KS[r][j];
             }
+            pvec[r] = db;
+            pvec[kC + r] = dg1 - Bt[r] * dg2;
             pvec[2 * kC + r] = dwr;
-            pvec[1 * kC + r] = dg1;
         }
-        // dk share, first part: W dS'^T (W = w o U), before dS is overwritten
-        for (int e = tid; e < kC * DK; e += kBT) {
-            const int r = e / DK, d = e % DK;
-            float acc = 0.f;
-            for (int j = 0; j < kSL; ++j) acc += U[r][j] * dS[d][j];
-            pdk[e] = w[r] * acc;
-        }
-        __syncthreads();
-        if (tid < kSL) {   // (I + A)^T dR = dU, from the last token back
-            for (int r = n - 2; r >= 0; --r) {
-                float acc = dR[r][tid];
-                for (int i = r + 1; i < n; ++i) acc -= A[i][r] * dR[i][tid];
-                dR[r][tid] = acc;
-            }
-        }
-        __syncthreads();
-        // dv (this slice's columns), and the per-token sums of dR
+        // dv for this slice's columns
         for (int e = tid; e < kC * kSL; e += kBT) {
             const int r = e / kSL, j = e % kSL;
             if (r < n) a.dv_[((size_t)(t0 + r) * H + h) * dv + j0 + j] = Bt[r] * dR[r][j];
         }
-        if (tid < kC) {
-            const int r = tid;
-            float db = 0.f, dg2 = 0.f;
-            for (int j = 0; j < kSL; ++j) {
-                db += dR[r][j] * (Vs[r][j] - gam[r] * KS[r][j]);
-                dg2 += dR[r][j] * KS[r][j];
-            }
-            pvec[r] = db;
-            pvec[kC + r] -= Bt[r] * dg2;
-        }
-        // dk share, second part: dKS S^T with dKS = -(beta gamma) o dR; dq share: gamma o (dY S^T)
+        // dk share: (w o U) dS'^T - ((beta gamma) o dR) S^T;  dq share: (gamma o dY) S^T
         for (int e = tid; e < kC * DK; e += kBT) {
             const int r = e / DK, d = e % DK;
-            float a1 = 0.f, a2 = 0.f;
+            float a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 4
             for (int j = 0; j < kSL; ++j) {
-                a1 += dR[r][j] * S[d][j];
-                a2 += dY[r][j] * S[d][j];
+                a1 += U[r][j] * dS[d][j];
+                a2 += dR[r][j] * S[d][j];
+                a3 += dY[r][j] * S[d][j];
             }
-            pdk[e] += -Bt[r] * gam[r] * a1;
-            pdq[e] = gam[r] * a2;
+            pdk[e] = w[r] * a1 - Bt[r] * gam[r] * a2;
+            pdq[e] = gam[r] * a3;
         }
         // dA = -(dR U^T) strictly lower, dP = (dY U^T) lower
         for (int e = tid; e < kC * kC; e += kBT) {
             const int r = e / kC, i = e % kC;
             float da = 0.f, dp = 0.f;
             if (i <= r && r < n) {
+#pragma unroll 4
                 for (int j = 0; j < kSL; ++j) {
                     da += dR[r][j] * U[i][j];
                     dp += dY[r][j] * U[i][j];
@@ -405,13 +407,19 @@ __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
             pdP[e] = dp;
         }
         __syncthreads();
+        // scale in place for the state gradient: dY <- gamma o dY, dR <- (beta gamma) o dR
+        for (int e = tid; e < kC * kSL; e += kBT) {
+            const int r = e / kSL, j = e % kSL;
+            dY[r][j] *= gam[r];
+            dR[r][j] *= Bt[r] * gam[r];
+        }
+        __syncthreads();
         // dS = gamma_C dS' + Q^T (gamma o dY) - K^T ((beta gamma) o dR)
         const float gC = gam[n - 1];
         for (int e = tid; e < DK * kSL; e += kBT) {
             const int d = e / kSL, j = e % kSL;
             float acc = gC * dS[d][j];
-            for (int r = 0; r < n; ++r)
-                acc += Qs[r][d] * gam[r] * dY[r][j] - Ks[r][d] * Bt[r] * gam[r] * dR[r][j];
+            for (int r = 0; r < n; ++r) acc += Qs[r][d] * dY[r][j] - Ks[r][d] * dR[r][j];
             dS[d][j] = acc;   // each element read and written by the same thread
         }
     }
@@ -426,9 +434,11 @@ __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ finish per chunk-head
 template <int DK, typename Tin>
-__global__ void __launch_bounds__(kBT) bwd_finish_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
     __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1];
-    __shared__ float dAe[kC][kC + 1], dQK[kC][kC + 1];   // dA o e^{D}, dP o e^{D}
+    __shared__ float dKK[kC][kC + 1], dQK[kC][kC + 1];   // coefficients of k_r.k_i, q_r.k_i
+    __shared__ float dDr[kC][kC + 1];                    // dD = dA o A + dP o P
+    __shared__ float dAk[kC][kC + 1];                    // dA o Ak (its row sums feed dbeta)
     __shared__ float G[kC], Bt[kC], dG[kC], dgam[kC], dw[kC], dbs[kC];
     __shared__ float dgC;
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -436,13 +446,8 @@ __global__ void __launch_bounds__(kBT) bwd_finish_kernel(BwdArgs a) {
     if (!chunk_info(a, c, t0, n)) return;
     const int H = a.H, slices = a.dv / kSL;
     const size_t ch = (size_t)c * H + h;
-    for (int e = tid; e < kC * DK; e += kBT) {
-        const int r = e / DK, d = e % DK;
-        const bool ok = r < n;
-        const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
-        Ks[r][d] = ok ? ld<Tin>(a.k, off) : 0.f;
-        Qs[r][d] = ok ? ld<Tin>(a.q, off) : 0.f;
-    }
+    load_rows<DK, Tin, kFinT>(a.k, t0, n, H, h, Ks);
+    load_rows<DK, Tin, kFinT>(a.q, t0, n, H, h, Qs);
     if (tid < kC) {
         G[tid] = a.G[ch * kC + tid];
         Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
@@ -456,7 +461,6 @@ __global__ void __launch_bounds__(kBT) bwd_finish_kernel(BwdArgs a) {
         dbs[tid] = db;
         dgam[tid] = dgm;
         dw[tid] = dww;
-        dG[tid] = 0.f;
     }
     if (tid == 0) {
         float s0 = 0.f;
@@ -465,44 +469,36 @@ __global__ void __launch_bounds__(kBT) bwd_finish_kernel(BwdArgs a) {
         dgC = s0;
     }
     __syncthreads();
-    // dA, dP summed over slices, times the decay: dAe = dA o e^{D} (strict lower; the k_r.k_i
-    // coefficient of A is beta_r dAe), dQK = dP o e^{D} (the q_r.k_i coefficient of P). Their
-    // products with A and P feed dG through D = G_r - G_i.
-    for (int e = tid; e < kC * kC; e += kBT) {
+    // dA, dP summed over slices. With A = beta o Ak (Ak = e^{D} o KK^T) and P = e^{D} o QK^T:
+    // dKK = beta o dA o e^{D}, dQK = dP o e^{D}, dbeta += rowsum(dA o Ak),
+    // dD = beta o dA o Ak + dP o P
+    for (int e = tid; e < kC * kC; e += kFinT) {
         const int r = e / kC, i = e % kC;
         float da = 0.f, dp = 0.f;
+#pragma unroll 2
         for (int s = 0; s < slices; ++s) {
             const float* pp = a.part + (ch * slices + s) * part_floats(DK) + 2 * kC * DK;
             da += pp[e];
             dp += pp[kC * kC + e];
         }
+        const float ak = a.Ak[ch * kC * kC + e], pv = a.P[ch * kC * kC + e];
         const float dec = (i <= r && r < n) ? expf(G[r] - G[i]) : 0.f;
-        dAe[r][i] = i < r ? da * dec : 0.f;
+        dKK[r][i] = i < r ? Bt[r] * da * dec : 0.f;
         dQK[r][i] = dp * dec;
+        dDr[r][i] = Bt[r] * da * ak + dp * pv;
+        dAk[r][i] = da * ak;
     }
     __syncthreads();
-    // dbeta: sum_i dA[r,i] e^{D} k_r.k_i, and dD -> dG rows and columns
     if (tid < kC) {
         const int r = tid;
-        float db = 0.f, dgr = 0.f, dgc = 0.f;
-        if (r < n) {
-            for (int i = 0; i < n; ++i) {
-                float kk_ri = 0.f, kk_ir = 0.f, qk_ri = 0.f, qk_ir = 0.f;
-                for (int d = 0; d < DK; ++d) {
-                    kk_ri += Ks[r][d] * Ks[i][d];
-                    qk_ri += Qs[r][d] * Ks[i][d];
-                    qk_ir += Qs[i][d] * Ks[r][d];
-                }
-                kk_ir = kk_ri;
-                // row r of dD: dA[r,i] A[r,i] + dP[r,i] P[r,i]
-                dgr += Bt[r] * dAe[r][i] * kk_ri + dQK[r][i] * qk_ri;
-                // column r of dD (entry [i,r])
-                dgc += Bt[i] * dAe[i][r] * kk_ir + dQK[i][r] * qk_ir;
-                db += dAe[r][i] * kk_ri;
-            }
+        float rs = 0.f, cs = 0.f, db = 0.f;
+        for (int i = 0; i < kC; ++i) {
+            rs += dDr[r][i];
+            cs += dDr[i][r];
+            db += dAk[r][i];
         }
         dbs[r] += db;
-        dG[r] = dgr - dgc + dgam[r] * expf(G[r]) - dw[r] * (r < n ? expf(G[n - 1] - G[r]) : 0.f);
+        dG[r] = rs - cs + dgam[r] * expf(G[r]) - dw[r] * (r < n ? expf(G[n - 1] - G[r]) : 0.f);
     }
     __syncthreads();
     if (tid == 0) {
@@ -521,9 +517,8 @@ __global__ void __launch_bounds__(kBT) bwd_finish_kernel(BwdArgs a) {
         a.dg[row] = dG[tid];
         a.dbeta[row] = dbs[tid];
     }
-    // dq = sum of shares + dQK K;  dk = sum of shares + (dKK + dKK^T) K + dQK^T Q with
-    // dKK[r,i] = beta_r dAe[r,i]
-    for (int e = tid; e < kC * DK; e += kBT) {
+    // dq = sum of shares + dQK K;  dk = sum of shares + (dKK + dKK^T) K + dQK^T Q
+    for (int e = tid; e < kC * DK; e += kFinT) {
         const int r = e / DK, d = e % DK;
         if (r >= n) continue;
         float dq = 0.f, dk = 0.f;
@@ -532,9 +527,10 @@ __global__ void __launch_bounds__(kBT) bwd_finish_kernel(BwdArgs a) {
             dq += pp[e];
             dk += pp[kC * DK + e];
         }
+#pragma unroll 4
         for (int i = 0; i < n; ++i) {
             dq += dQK[r][i] * Ks[i][d];
-            dk += (Bt[r] * dAe[r][i] + Bt[i] * dAe[i][r]) * Ks[i][d] + dQK[i][r] * Qs[i][d];
+            dk += (dKK[r][i] + dKK[i][r]) * Ks[i][d] + dQK[i][r] * Qs[i][d];
         }
         const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
         a.dq[off] = dq;
@@ -558,8 +554,9 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
     a.num_seqs = c.num_seqs; a.ntok = c.ntok; a.H = c.H; a.dk = c.dk; a.dv = c.dv;
     a.dq = c.dq; a.dk_ = c.dk_; a.dv_ = c.dv_; a.dg = c.dg; a.dbeta = c.dbeta; a.dS0 = c.dS0;
     a.G = reinterpret_cast<float*>(ws + L.G);
-    a.A = reinterpret_cast<float*>(ws + L.A);
+    a.Ak = reinterpret_cast<float*>(ws + L.Ak);
     a.P = reinterpret_cast<float*>(ws + L.P);
+    a.T = reinterpret_cast<float*>(ws + L.T);
     a.Sc = reinterpret_cast<float*>(ws + L.Sc);
     a.part = reinterpret_cast<float*>(ws + L.part);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((c.ntok / c.num_seqs + kC - 1) / kC);
@@ -575,10 +572,10 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
     }
 #define GDN_BWD(DK, TI, TD)                                                                     \
     do {                                                                                        \
-        hipLaunchKernelGGL((bwd_ap_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kBT), 0, s, a);    \
+        hipLaunchKernelGGL((bwd_ap_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kFinT), 0, s, a);    \
         hipLaunchKernelGGL((bwd_states_kernel<DK, TI>), dim3(seq_blocks), dim3(kBT), 0, s, a);  \
         hipLaunchKernelGGL((bwd_scan_kernel<DK, TI, TD>), dim3(seq_blocks), dim3(kBT), 0, s, a); \
-        hipLaunchKernelGGL((bwd_finish_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kBT), 0, s, a); \
+        hipLaunchKernelGGL((bwd_finish_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kFinT), 0, s, a); \
     } while (0)
     if (c.dk == 128) {
         if (c.in_bf16 && c.dy_bf16) GDN_BWD(128, uint16_t, uint16_t);

@@ -105,3 +105,27 @@ def test_stateful_preprocess_and_multi_decode_validation(L):
         assert st == 2 and b"T must be" in L.gdn_last_error()
     st = L.gdn_decode_multi(F, F, F, 1, F, F, F, 2, 4, 1, 128, 128, F, 1, F + 64, None)
     assert st == 2 and b"overlap" in L.gdn_last_error()
+
+
+def test_backward_validation(L):
+    n = None
+    F = FAKE
+    need = L.gdn_chunk_backward_workspace_size(128, 1, 2, 128, 128)
+    assert need > 0
+    assert L.gdn_chunk_backward_workspace_size(128, 1, 2, 96, 128) == 0
+
+    def call(**kw):
+        a = dict(q=F, k=F, v=F, it=1, g=F, b=F, s0=n, dy=F, dyt=1, dst=n, cu=n, cuh=n, ns=1,
+                 nt=128, H=2, dk=128, dv=128, dq=F, dkk=F, dvv=F, dg=F, db=F, ds0=n, ws=F,
+                 wsb=need)
+        a.update(kw)
+        return L.gdn_chunk_backward(a["q"], a["k"], a["v"], a["it"], a["g"], a["b"], a["s0"],
+                                    a["dy"], a["dyt"], a["dst"], a["cu"], a["cuh"], a["ns"],
+                                    a["nt"], a["H"], a["dk"], a["dv"], a["dq"], a["dkk"], a["dvv"],
+                                    a["dg"], a["db"], a["ds0"], a["ws"], a["wsb"], None)
+    assert call(dy=None) == 1
+    assert call(dyt=3) == 3
+    assert call(dv=32) == 2
+    assert call(wsb=need - 1) == 6
+    assert call(dq=MIS) == 5
+    assert call(ns=3) == 2
