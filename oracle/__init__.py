@@ -64,6 +64,10 @@ def _load():
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, _dp, _dp, ctypes.c_int]
         lib.gdn_oracle_recurrence.restype = ctypes.c_int
+        lib.gdn_oracle_kda_recurrence.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp,
+                                                  _dp, ctypes.c_int]
+        lib.gdn_oracle_kda_recurrence.restype = ctypes.c_int
         lib.gdn_oracle_recurrence_backward.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip,
                                                        ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                        ctypes.c_int, _dp, _dp, _dp, _dp, _dp,
@@ -172,6 +176,26 @@ def recurrence(q, k, v, alpha, beta, S0=None, cu_seqlens=None, closed_form=False
     _load().gdn_oracle_recurrence(_p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(s0),
                                   cu.ctypes.data_as(_ip), nseq, H, dk, dv, int(closed_form),
                                   _p(y), _p(ST), nthreads or default_threads())
+    return y, ST
+
+
+def kda_recurrence(q, k, v, alpha, beta, S0=None, cu_seqlens=None, nthreads=None):
+    """The delta rule with a per-channel decay alpha [ntok, H, dk] (Kimi Delta Attention's
+    diagonal gate in place of GDN's scalar): row i of the state decays by alpha_t[i].
+    Returns (y [ntok,H,dv], S_T [nseq,H,dk,dv])."""
+    q, k, v, alpha, beta = (_d(x) for x in (q, k, v, alpha, beta))
+    ntok, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = [0, ntok]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    nseq = len(cu) - 1
+    s0 = None if S0 is None else _d(S0)
+    y = np.zeros((ntok, H, dv))
+    ST = np.zeros((nseq, H, dk, dv))
+    _load().gdn_oracle_kda_recurrence(_p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(s0),
+                                      cu.ctypes.data_as(_ip), nseq, H, dk, dv, _p(y), _p(ST),
+                                      nthreads or default_threads())
     return y, ST
 
 

@@ -228,6 +228,89 @@ int gdn_oracle_recurrence(const double* q, const double* k, const double* v, con
     return 0;
 }
 
+/* ------------------------------------------------------------------ per-channel decay */
+
+/* The delta rule with a per-channel (diagonal) decay, as in Kimi Delta Attention, to which the
+ * reading notes compare GDN (related work on Kimi K3: a KDA layer whose log-decay has a lower
+ * bound). Reading: the scalar alpha of eq. 1 becomes a diagonal over the key channels,
+ *   S~ = Diag(alpha_t) S_{t-1};  e = v_t - S~^T k_t;  S_t = S~ + beta_t k_t e^T;  y_t = S_t^T q_t
+ * i.e. eqs. 1-4 with row i of the state decayed by alpha_t[i]. alpha: [ntok, H, dk].
+ * Other arguments as gdn_oracle_recurrence. */
+typedef struct {
+    const double *q, *k, *v, *alpha, *beta, *S0;
+    const int* cu;
+    int nseq, H, dk, dv;
+    double *y, *ST;
+    int next;
+    pthread_mutex_t mu;
+} kda_job;
+
+static void kda_pair(kda_job* J, int s, int h, double* S, double* e) {
+    const int H = J->H, dk = J->dk, dv = J->dv;
+    const long sz = (long)dk * dv;
+    if (J->S0) memcpy(S, J->S0 + ((long)s * H + h) * sz, sizeof(double) * sz);
+    else memset(S, 0, sizeof(double) * sz);
+    for (int t = J->cu[s]; t < J->cu[s + 1]; ++t) {
+        const long row = (long)t * H + h;
+        const double* q = J->q + row * dk;
+        const double* k = J->k + row * dk;
+        const double* v = J->v + row * dv;
+        const double* al = J->alpha + row * dk;
+        const double b = J->beta[row];
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(long)i * dv + j] *= al[i];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * k[i];
+            e[j] = v[j] - acc;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * k[i] * e[j];
+        double* y = J->y + row * dv;
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * q[i];
+            y[j] = acc;
+        }
+    }
+    if (J->ST) memcpy(J->ST + ((long)s * H + h) * sz, S, sizeof(double) * sz);
+}
+
+static void* kda_worker(void* arg) {
+    kda_job* J = (kda_job*)arg;
+    double* S = (double*)malloc(sizeof(double) * (size_t)J->dk * J->dv);
+    double* e = (double*)malloc(sizeof(double) * (size_t)J->dv);
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int p = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (p >= J->nseq * J->H) break;
+        kda_pair(J, p / J->H, p % J->H, S, e);
+    }
+    free(S);
+    free(e);
+    return NULL;
+}
+
+int gdn_oracle_kda_recurrence(const double* q, const double* k, const double* v,
+                              const double* alpha, const double* beta, const double* S0,
+                              const int* cu, int nseq, int H, int dk, int dv, double* y,
+                              double* ST, int nthreads) {
+    kda_job J;
+    J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.S0 = S0; J.cu = cu;
+    J.nseq = nseq; J.H = H; J.dk = dk; J.dv = dv; J.y = y; J.ST = ST; J.next = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    int pairs = nseq * H;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pairs) nthreads = pairs > 0 ? pairs : 1;
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, kda_worker, &J);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ gradients of eqs. 1-4 */
 
 /* Reverse-mode derivative of the recurrence above (eqs. 1-4 as written), token by token in

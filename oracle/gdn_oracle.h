@@ -19,6 +19,10 @@ void gdn_oracle_gates(const double* a_raw, const double* b_raw, const double* A_
 int gdn_oracle_recurrence(const double* q, const double* k, const double* v, const double* alpha,
                           const double* beta, const double* S0, const int* cu, int nseq, int H,
                           int dk, int dv, int closed_form, double* y, double* ST, int nthreads);
+int gdn_oracle_kda_recurrence(const double* q, const double* k, const double* v,
+                              const double* alpha, const double* beta, const double* S0,
+                              const int* cu, int nseq, int H, int dk, int dv, double* y,
+                              double* ST, int nthreads);
 int gdn_oracle_recurrence_backward(const double* q, const double* k, const double* v,
                                    const double* alpha, const double* beta, const double* S0,
                                    const int* cu, int nseq, int H, int dk, int dv,

@@ -436,3 +436,54 @@ def test_backward_zero_write_is_pure_decay():
     assert np.allclose(g["dS0"], np.prod(al) * dST, rtol=1e-13, atol=0)
     assert np.all(g["dv"] == 0.0)
     assert np.allclose(g["dg"], np.full((T, 1), np.sum(dST * np.prod(al) * S0)), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- per-channel decay (KDA)
+def _kda_case(T, H, dk, dv, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv))
+    al = rng.uniform(0.3, 0.999, (T, H, dk))
+    be = rng.uniform(0.05, 0.95, (T, H))
+    return q, k, v, al, be
+
+
+def test_kda_with_equal_channel_decays_is_gdn():
+    q, k, v, _, be = _kda_case(50, 2, 8, 6, seed=40)
+    al = np.random.default_rng(41).uniform(0.3, 0.999, (50, 2))
+    S0 = np.random.default_rng(42).standard_normal((2, 2, 8, 6))
+    cu = [0, 23, 50]
+    y1, s1 = oracle.kda_recurrence(q, k, v, np.repeat(al[:, :, None], 8, axis=2), be, S0, cu)
+    y2, s2 = oracle.recurrence(q, k, v, al, be, S0, cu)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+
+
+def test_kda_zero_write_decays_each_row_by_its_own_product():
+    q, k, v, al, be = _kda_case(30, 1, 5, 4, seed=43)
+    be[:] = 0.0
+    S0 = np.random.default_rng(44).standard_normal((1, 1, 5, 4))
+    y, ST = oracle.kda_recurrence(q, k, v, al, be, S0)
+    cum = np.cumprod(al[:, 0, :], axis=0)                     # [T, dk]
+    assert np.allclose(ST[0, 0], cum[-1][:, None] * S0[0, 0], rtol=1e-13, atol=0)
+    ref = np.einsum("ti,ti,ij->tj", q[:, 0], cum, S0[0, 0])
+    assert np.allclose(y[:, 0], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_kda_channel_permutation_equivariance():
+    q, k, v, al, be = _kda_case(40, 1, 7, 3, seed=45)
+    S0 = np.random.default_rng(46).standard_normal((1, 1, 7, 3))
+    perm = np.random.default_rng(47).permutation(7)
+    y1, s1 = oracle.kda_recurrence(q, k, v, al, be, S0)
+    y2, s2 = oracle.kda_recurrence(q[:, :, perm], k[:, :, perm], v, al[:, :, perm], be,
+                                   S0[:, :, perm])
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-13)
+    assert np.allclose(s1[:, :, perm], s2, rtol=1e-12, atol=1e-13)
+
+
+def test_kda_full_write_strength_stores_value():
+    q, k, v, al, be = _kda_case(25, 1, 6, 4, seed=48)
+    be[:] = 1.0
+    y, _ = oracle.kda_recurrence(k, k, v, al, be)            # read back with q = k
+    assert np.allclose(y, v, rtol=1e-12, atol=1e-12)
