@@ -153,3 +153,38 @@ def _chunk_bwd(Q, K, V, g, b, S, dY, dS1):
     # G = cumsum(g)
     dg = np.cumsum(dG[::-1])[::-1]
     return dict(dq=dQ, dk=dK, dv=dV, dg=dg, dbeta=db), dS
+
+
+def chunked_forward_kda(q, k, v, g, beta, S0=None, cu_seqlens=None, C=64):
+    """Chunkwise form with a per-channel log-decay g [ntok, H, dk]. With Gc[r, c] the running
+    sum of g over the chunk (per channel), unrolling the recurrence inside a chunk gives
+        A[r,i] = beta_r sum_c k_r[c] k_i[c] e^{Gc[r,c] - Gc[i,c]}   (i < r)
+        U = (I + A)^{-1} (diag(beta) V - diag(beta) (K o e^{Gc}) S0)
+        Y = (Q o e^{Gc}) S0 + P U,   P[r,i] = sum_c q_r[c] k_i[c] e^{Gc[r,c] - Gc[i,c]} (i <= r)
+        S_C = Diag(e^{Gc[C]}) S0 + (K o e^{Gc[C] - Gc})^T U"""
+    ntok, H, dk = q.shape
+    dv = v.shape[2]
+    cu = [0, ntok] if cu_seqlens is None else list(cu_seqlens)
+    nseq = len(cu) - 1
+    y = np.zeros((ntok, H, dv))
+    ST = np.zeros((nseq, H, dk, dv))
+    for s in range(nseq):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else S0[s, h].copy()
+            for c0 in range(cu[s], cu[s + 1], C):
+                sl = slice(c0, min(c0 + C, cu[s + 1]))
+                Q, K, V = q[sl, h], k[sl, h], v[sl, h]
+                Gc = np.cumsum(g[sl, h], axis=0)              # [n, dk]
+                b = beta[sl, h]
+                n = len(b)
+                E = np.exp(np.minimum(Gc[:, None, :] - Gc[None, :, :], 0.0))   # [r, i, c]
+                low = np.tril(np.ones((n, n)), -1).astype(bool)
+                incl = np.tril(np.ones((n, n))).astype(bool)
+                A = np.where(low, b[:, None] * np.einsum("rc,ic,ric->ri", K, K, E), 0.0)
+                P = np.where(incl, np.einsum("rc,ic,ric->ri", Q, K, E), 0.0)
+                T = np.linalg.inv(np.eye(n) + A)
+                U = T @ (b[:, None] * (V - (K * np.exp(Gc)) @ S))
+                y[sl, h] = (Q * np.exp(Gc)) @ S + P @ U
+                S = np.exp(Gc[-1])[:, None] * S + (K * np.exp(Gc[-1] - Gc)).T @ U
+            ST[s, h] = S
+    return y, ST
