@@ -207,6 +207,39 @@ def main():
             f"{bms / t_pf:.1f}x the forward prefill)")
         del dy, ws_b
 
+    # ------------------------------------------------------------------ per-channel decay variant
+    kda = None
+    if not args.no_backward:
+        gen = torch.Generator(device=dev).manual_seed(1)
+        gk = -torch.clamp(torch.exp(torch.randn((ntok, H, dk), generator=gen, device=dev) - 2.0),
+                          max=5.0)
+        ws_k = torch.empty(int(gdn.lib().gdn_kda_chunk_prefill_workspace_size(ntok, nseq, H, dk)),
+                           dtype=torch.uint8, device=dev)
+
+        def kstep():
+            return gdn.gdn_kda_chunk_prefill(outs["q"], outs["k"], outs["v"], gk, outs["beta"],
+                                             num_seqs=nseq, y=y, workspace=ws_k,
+                                             output_final_state=False)
+        for _ in range(3):
+            kstep()
+        torch.cuda.synchronize()
+        nk = 10
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(nk):
+            kstep()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        kms = b0.elapsed_time(b1) / nk
+        kda = {"workload": "gdn_kda_chunk_prefill at B=4 H=16 T=4096 d=128 (bf16 q, k, v, y; "
+                           "per-channel fp32 log-decays)",
+               "calls": nk, "us_per_call": round(kms * 1e3, 1),
+               "Mtok_s": round(ntok / (kms * 1e-3) / 1e6, 2),
+               "vs_scalar_decay_prefill": round(kms / t_pf, 2)}
+        log(f"[bench] per-channel-decay prefill {kms * 1e3:.1f} us/call ({kda['Mtok_s']} Mtok/s)")
+        del gk, ws_k
+
     del X, outs, y, o, ws
     torch.cuda.empty_cache()
 
@@ -327,6 +360,7 @@ def main():
                                "(C=64) + output gate", "B": 4, "H": H, "T": sh.lengths[0],
                    "d_k": dk, "d_v": dv, "tokens_per_step": ntok},
         "kernels": kernels, "roofline": roofline, "decode": decode, "backward": backward,
+        "per_channel_decay": kda,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

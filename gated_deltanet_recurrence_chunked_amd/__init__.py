@@ -10,6 +10,7 @@ The functions keep the C names:
   gdn_preprocess_stateful           the same for sequences that continue earlier input
                                     (carried conv history in and out)
   gdn_chunk_backward eqs. (1)-(4)   gradients of the chunked prefill (dq, dk, dv, dg, dbeta, dS0)
+  gdn_kda_chunk_prefill             the same recurrence with a per-channel decay (KDA-style)
   gdn_decode_step    eqs. (1)-(4)   one token per sequence, state updated in place
   gdn_decode_multi   eqs. (1)-(4)   T <= 8 tokens per sequence (multi-token prediction
                                     verify) in one pass over each state
@@ -68,6 +69,11 @@ def lib():
         L.gdn_chunk_backward.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp,
                                          _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]
+        L.gdn_kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
+        L.gdn_kda_chunk_prefill_workspace_size.argtypes = [_i, _i, _i, _i]
+        L.gdn_kda_chunk_prefill.restype = _i
+        L.gdn_kda_chunk_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                            _i, _i, _i, _i, _vp, _i, _vp, ctypes.c_size_t, _vp]
         L.gdn_decode_step.restype = _i
         L.gdn_decode_step.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i,
                                       _vp]
@@ -280,6 +286,38 @@ def gdn_chunk_backward(q, k, v, g, beta, dy, *, initial_state=None, dfinal_state
     return out
 
 
+def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, cu_seqlens=None,
+                          cu_seqlens_host=None, num_seqs=1, y=None, y_dtype=None, workspace=None,
+                          output_final_state=True, stream=None):
+    """Per-channel-decay delta rule. q,k: [ntok,H,dk], v: [ntok,H,dv] (bf16/fp32);
+    g: [ntok,H,dk] fp32 log-decays; beta: [ntok,H] fp32. Returns (y, final_state)."""
+    ntok, H, dk = q.shape
+    dv = v.shape[-1]
+    in_tag = _dtype_tag(q)
+    y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
+    dev = q.device
+    if y is None:
+        y = torch.empty((ntok, H, dv), dtype=_tag_dtype(y_tag), device=dev)
+    final_state = (torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+                   if output_final_state else None)
+    need = int(lib().gdn_kda_chunk_prefill_workspace_size(ntok, num_seqs, H, dk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+    f32 = torch.float32
+    st = lib().gdn_kda_chunk_prefill(
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), in_tag, _ptr(g, "g", f32), _ptr(beta, "beta", f32),
+        _ptr(initial_state, "initial_state", f32), _ptr(final_state, "final_state", f32),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32),
+        ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
+        _ptr(y, "y"), y_tag, _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gdn_kda_chunk_prefill")
+    return y, final_state
+
+
 def gdn_decode_step(q, k, v, g, beta, state, *, y=None, y_dtype=None, stream=None):
     """One token per sequence. q,k: [N,H,dk], v: [N,H,dv]; g,beta: [N,H] fp32;
     state: [N,H,dk,dv] fp32 updated in place. Returns y [N,H,dv]."""
@@ -335,5 +373,5 @@ def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream
 
 __all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_preprocess_stateful",
            "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_chunk_backward",
-           "gdn_chunk_backward_workspace_size", "gdn_decode_step",
+           "gdn_chunk_backward_workspace_size", "gdn_kda_chunk_prefill", "gdn_decode_step",
            "gdn_decode_multi", "gdn_output_gate"]

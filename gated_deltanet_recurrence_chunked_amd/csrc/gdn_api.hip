@@ -269,6 +269,41 @@ int gdn_chunk_backward(const void* q, const void* k, const void* v, int in_dtype
                       "gdn_chunk_backward");
 }
 
+size_t gdn_kda_chunk_prefill_workspace_size(int ntok, int num_seqs, int H, int dk) {
+    if (ntok < 0 || num_seqs < 1 || H < 1 || !valid_dim(dk)) return 0;
+    return gdn::chunk_kda_workspace(ntok, num_seqs, H, dk);
+}
+
+int gdn_kda_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
+                          const float* g, const float* beta, const float* initial_state,
+                          float* final_state, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
+                          int dv, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    GDN_REQUIRE(valid_dtype(in_dtype) && valid_dtype(y_dtype), GDN_ERR_DTYPE,
+                "in_dtype/y_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need H >= 1 and dk, dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
+    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(y);
+    GDN_OPT_PTR(initial_state); GDN_OPT_PTR(final_state);
+    GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+    GDN_REQUIRE(cu_seqlens_host == nullptr || cu_seqlens != nullptr, GDN_ERR_NULL,
+                "cu_seqlens_host given without the device cu_seqlens");
+    int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
+    if (st) return st;
+    const size_t need = gdn::chunk_kda_workspace(ntok, num_seqs, H, dk);
+    GDN_REQUIRE(workspace_bytes >= need && workspace != nullptr, GDN_ERR_WORKSPACE,
+                "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    GDN_OPT_PTR(workspace);
+    gdn::ChunkKdaArgs a;
+    a.q = q; a.k = k; a.v = v; a.in_bf16 = in_dtype == GDN_BF16; a.y_bf16 = y_dtype == GDN_BF16;
+    a.g = g; a.beta = beta; a.S0 = initial_state; a.ST = final_state; a.cu = cu_seqlens;
+    a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.dk = dk; a.dv = dv; a.y = y;
+    a.workspace = workspace;
+    return hip_status(gdn::launch_chunk_kda(a, static_cast<hipStream_t>(stream)),
+                      "gdn_kda_chunk_prefill");
+}
+
 int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, const float* g,
                     const float* beta, float* state, int N, int H, int dk, int dv, void* y,
                     int y_dtype, void* stream) {

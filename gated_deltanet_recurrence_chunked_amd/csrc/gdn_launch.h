@@ -72,4 +72,18 @@ struct ChunkBwdArgs {
 size_t chunk_bwd_workspace(int ntok, int num_seqs, int H, int dk, int dv);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t s);
 
+// per-channel-decay (KDA-style) chunked forward (fp32 vector ALU)
+struct ChunkKdaArgs {
+    const void *q, *k, *v;
+    int in_bf16, y_bf16;
+    const float *g, *beta, *S0;   // g: [ntok, H, dk]
+    float* ST;
+    const int32_t* cu;
+    int num_seqs, ntok, H, dk, dv;
+    void* y;
+    void* workspace;
+};
+size_t chunk_kda_workspace(int ntok, int num_seqs, int H, int dk);
+hipError_t launch_chunk_kda(const ChunkKdaArgs& a, hipStream_t s);
+
 }  // namespace gdn

@@ -129,3 +129,22 @@ def test_backward_validation(L):
     assert call(wsb=need - 1) == 6
     assert call(dq=MIS) == 5
     assert call(ns=3) == 2
+
+
+def test_kda_validation(L):
+    n = None
+    F = FAKE
+    need = L.gdn_kda_chunk_prefill_workspace_size(128, 1, 2, 128)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(q=F, k=F, v=F, it=1, g=F, b=F, s0=n, st=n, cu=n, cuh=n, ns=1, nt=128, H=2,
+                 dk=128, dv=128, y=F, yt=1, ws=F, wsb=need)
+        a.update(kw)
+        return L.gdn_kda_chunk_prefill(a["q"], a["k"], a["v"], a["it"], a["g"], a["b"], a["s0"],
+                                       a["st"], a["cu"], a["cuh"], a["ns"], a["nt"], a["H"],
+                                       a["dk"], a["dv"], a["y"], a["yt"], a["ws"], a["wsb"], None)
+    assert call(g=None) == 1
+    assert call(dk=32) == 2
+    assert call(wsb=need - 1) == 6
+    assert call(yt=9) == 3
