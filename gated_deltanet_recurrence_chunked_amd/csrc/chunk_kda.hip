@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kC = 64;
 constexpr int kPT = 256;          // prep threads
-constexpr int kST = 256;          // scan threads
+constexpr int kST = 1024;         // scan threads: 16 waves hide the LDS latency of the small products
 constexpr int kSL = 16;           // dv columns per scan workgroup
 
 struct KdaLayout {
