@@ -36,7 +36,7 @@ constexpr int kC = 64;
 constexpr int kBT = 1024;         // threads per workgroup: 16 waves hide the LDS latency of the
                                   // small products every chunk step is made of
 constexpr int kSL = 16;           // dv columns per scan workgroup
-constexpr int kFinT = 256;        // threads of the per-chunk-head kernels (plenty of workgroups)
+constexpr int kFinT = 512;        // threads of the per-chunk-head kernels (one workgroup per CU fits their LDS)
 constexpr int kP = kSL + 1;       // padded row of a [64][16] tile
 
 struct BwdLayout {

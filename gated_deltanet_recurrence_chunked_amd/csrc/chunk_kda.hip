@@ -21,7 +21,7 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 64;
-constexpr int kPT = 256;          // prep threads
+constexpr int kPT = 512;          // prep threads (one workgroup per CU fits its LDS)
 constexpr int kST = 1024;         // scan threads: 16 waves hide the LDS latency of the small products
 constexpr int kSL = 16;           // dv columns per scan workgroup
 
