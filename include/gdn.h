@@ -180,6 +180,27 @@ int gdn_chunk_backward(const void* q, const void* k, const void* v, int in_dtype
                        float* dinitial_state, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* Bytes of device workspace gdn_kda_chunk_prefill needs for these sizes. */
+size_t gdn_kda_chunk_prefill_workspace_size(int ntok, int num_seqs, int H, int dk);
+
+/*
+ * gdn_kda_chunk_prefill - the delta rule with a per-channel (diagonal) decay, the variant the
+ * reading notes compare GDN with (related work on Kimi K3: Kimi Delta Attention, whose
+ * log-decay is lower-bounded). eq. (1)'s scalar alpha_t becomes Diag(alpha_t) over the key
+ * channels: row c of the state decays by alpha_t[c] = exp(g[t][h][c]); eqs. (2)-(4) are
+ * unchanged. Chunkwise (C = 64) in fp32.
+ *
+ *   Arguments as gdn_chunk_prefill except g: [ntok, H, dk] fp32 per-channel log-decays
+ *   (any g <= 0; the kernels form only exponentials of non-positive differences).
+ *   workspace: at least gdn_kda_chunk_prefill_workspace_size(...) bytes.
+ */
+int gdn_kda_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
+                          const float* g, const float* beta, const float* initial_state,
+                          float* final_state, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
+                          int dv, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /*
  * gdn_decode_step - one token per sequence through eqs. (1)-(4), state updated in place:
  * S <- alpha S; e = v - S^T k; S <- S + beta k e^T; y = S^T q.
