@@ -257,27 +257,34 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ scan: reverse sweep
+// Every product of a chunk step runs on the fp32 matrix core, one 16x16 output tile per wave at a
+// time (16 waves), with its operands read from LDS as strided views.
+constexpr int kScanT = 1024;
 template <int DK, typename Tin, typename Tdy>
-__global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
     __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1];
     __shared__ float S[DK][kSL], dS[DK][kSL];        // state entering the chunk; gradient after
     __shared__ float T[kC][kC + 1], P[kC][kC + 1];
-    // [64][16] tiles: Vr = V - gamma o KS (then reused), dY, KS, QS, U, KdS (= K dS'), dU, dR
+    // [64][16] tiles: Vr = V - gamma o KS, dY, KS, QS, U, KdS = K dS', dU, dR; late in the step
+    // QS and KS are reused for gamma o dY and (beta gamma) o dR, and dR holds R = beta o Vr
+    // until dR itself is formed
     __shared__ float Vr[kC][kP], dY[kC][kP], KS[kC][kP], QS[kC][kP];
     __shared__ float U[kC][kP], KdS[kC][kP], dU[kC][kP], dR[kC][kP];
     __shared__ float gam[kC], w[kC], Bt[kC];
-    __shared__ float red[kBT / kWave];
+    __shared__ float red[kScanT / kWave];
 
     const int slices = a.dv / kSL;
     const int slice = blockIdx.x % slices;
     const int h = (blockIdx.x / slices) % a.H;
     const int sq = blockIdx.x / (slices * a.H);
     const int j0 = slice * kSL, tid = threadIdx.x, H = a.H, dv = a.dv;
+    const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
+    constexpr int NW = kScanT / kWave;
     int lo, hi, cbase;
     seq_info(a, sq, lo, hi, cbase);
     const int nch = (hi - lo + kC - 1) / kC;
     const size_t st_off = ((size_t)sq * H + h) * DK * dv;
-    for (int e = tid; e < DK * kSL; e += kBT) {
+    for (int e = tid; e < DK * kSL; e += kScanT) {
         const int d = e / kSL, j = e % kSL;
         dS[d][j] = a.dST ? a.dST[st_off + (size_t)d * dv + j0 + j] : 0.f;
     }
@@ -291,20 +298,20 @@ __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
         float* pdP = pdA + kC * kC;                // [64][64]
         float* pvec = pdP + kC * kC;               // [4][64]
         __syncthreads();
-        load_rows<DK, Tin>(a.k, t0, n, H, h, Ks);
-        load_rows<DK, Tin>(a.q, t0, n, H, h, Qs);
-        for (int e = tid; e < kC * kSL; e += kBT) {
+        load_rows<DK, Tin, kScanT>(a.k, t0, n, H, h, Ks);
+        load_rows<DK, Tin, kScanT>(a.q, t0, n, H, h, Qs);
+        for (int e = tid; e < kC * kSL; e += kScanT) {
             const int r = e / kSL, j = e % kSL;
             const bool ok = r < n;
             const size_t off = ((size_t)(t0 + r) * H + h) * dv + j0 + j;
             Vr[r][j] = ok ? ld<Tin>(a.v, off) : 0.f;
             dY[r][j] = ok ? ld<Tdy>(a.dy, off) : 0.f;
         }
-        for (int e = tid; e < DK * kSL; e += kBT) {
+        for (int e = tid; e < DK * kSL; e += kScanT) {
             const int d = e / kSL, j = e % kSL;
             S[d][j] = a.Sc[ch * DK * dv + (size_t)d * dv + j0 + j];
         }
-        for (int e = tid; e < kC * kC; e += kBT) {
+        for (int e = tid; e < kC * kC; e += kScanT) {
             T[e / kC][e % kC] = a.T[ch * kC * kC + e];
             P[e / kC][e % kC] = a.P[ch * kC * kC + e];
         }
@@ -315,51 +322,87 @@ __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
             Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
         }
         __syncthreads();
-        // dgamma_C share <S, dS'>; KS = K S, QS = Q S, K dS'
-        float sdot = 0.f;
-        for (int e = tid; e < DK * kSL; e += kBT) sdot += S[e / kSL][e % kSL] * dS[e / kSL][e % kSL];
-        sdot = group_sum<kWave>(sdot);
-        if (tid % kWave == 0) red[tid / kWave] = sdot;
-        for (int e = tid; e < kC * kSL; e += kBT) {
-            const int r = e / kSL, j = e % kSL;
-            float ks = 0.f, qs = 0.f, kd = 0.f;
-#pragma unroll 4
-            for (int d = 0; d < DK; ++d) {
-                ks += Ks[r][d] * S[d][j];
-                qs += Qs[r][d] * S[d][j];
-                kd += Ks[r][d] * dS[d][j];
-            }
-            KS[r][j] = ks;
-            QS[r][j] = qs;
-            KdS[r][j] = kd;
-            Vr[r][j] -= gam[r] * ks;                 // V - gamma o KS
+        // ---- step 1: KS = K S, QS = Q S, KdS = K dS' (12 tiles); <S, dS'>
+        for (int tile = wave; tile < 12; tile += NW) {
+            const int kind = tile >> 2, rt = tile & 3;
+            const float* A = kind == 1 ? &Qs[rt * 16][0] : &Ks[rt * 16][0];
+            const float* B = kind == 2 ? &dS[0][0] : &S[0][0];
+            const floatx4 acc = mma_f32_tile(A, DK + 1, 1, B, kSL, 1, DK, floatx4{0.f, 0.f, 0.f, 0.f});
+            float(*dst)[kP] = kind == 0 ? KS : (kind == 1 ? QS : KdS);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[rt * 16 + 4 * lg + i][lc] = acc[i];
+        }
+        {
+            float sdot = 0.f;
+            for (int e = tid; e < DK * kSL; e += kScanT) sdot += S[e / kSL][e % kSL] * dS[e / kSL][e % kSL];
+            sdot = group_sum<kWave>(sdot);
+            if (lane == 0) red[wave] = sdot;
         }
         __syncthreads();
         if (tid == 0) {
             float acc = 0.f;
-            for (int i = 0; i < kBT / kWave; ++i) acc += red[i];
+            for (int i = 0; i < NW; ++i) acc += red[i];
             pvec[3 * kC] = acc;
         }
-        // U = T R with R = beta o Vr;  dU = w o K dS' + P^T dY
-        for (int e = tid; e < kC * kSL; e += kBT) {
+        for (int e = tid; e < kC * kSL; e += kScanT) {   // Vr = V - gamma KS;  R = beta Vr (in dR)
             const int r = e / kSL, j = e % kSL;
-            float u = 0.f;
-            for (int i = 0; i <= r; ++i) u += T[r][i] * (Bt[i] * Vr[i][j]);
-            U[r][j] = u;
-            float pt = 0.f;
-            for (int i = r; i < n; ++i) pt += P[i][r] * dY[i][j];
-            dU[r][j] = w[r] * KdS[r][j] + pt;
+            const float vr = Vr[r][j] - gam[r] * KS[r][j];
+            Vr[r][j] = vr;
+            dR[r][j] = Bt[r] * vr;
         }
         __syncthreads();
-        // dR = T^T dU
-        for (int e = tid; e < kC * kSL; e += kBT) {
-            const int r = e / kSL, j = e % kSL;
-            float acc = 0.f;
-            for (int i = r; i < n; ++i) acc += T[i][r] * dU[i][j];
-            dR[r][j] = acc;
+        // ---- step 2: U = T R;  dU = w o KdS + P^T dY (8 tiles)
+        for (int tile = wave; tile < 8; tile += NW) {
+            const int rt = tile & 3;
+            if (tile < 4) {
+                const floatx4 acc = mma_f32_tile(&T[rt * 16][0], kC + 1, 1, &dR[0][0], kP, 1, kC,
+                                                 floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i) U[rt * 16 + 4 * lg + i][lc] = acc[i];
+            } else {
+                const floatx4 acc = mma_f32_tile(&P[0][rt * 16], 1, kC + 1, &dY[0][0], kP, 1, kC,
+                                                 floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rt * 16 + 4 * lg + i;
+                    dU[r][lc] = w[r] * KdS[r][lc] + acc[i];
+                }
+            }
         }
         __syncthreads();
-        // per-token sums over this slice's columns
+        // ---- step 3: dR = T^T dU (4 tiles); dq share (gamma o dY) S^T and dP = dY U^T (48 tiles)
+        if (wave < 4) {
+            const int rt = wave;
+            const floatx4 acc = mma_f32_tile(&T[0][rt * 16], 1, kC + 1, &dU[0][0], kP, 1, kC,
+                                             floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dR[rt * 16 + 4 * lg + i][lc] = acc[i];
+        }
+        {
+            for (int tile = (wave + NW - 4) % NW; tile < 4 * (DK / 16) + 16; tile += NW) {
+                if (tile < 4 * (DK / 16)) {   // dq share tile (rt, dt)
+                    const int rt = tile / (DK / 16), dt = tile % (DK / 16);
+                    const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], kP, 1, &S[dt * 16][0], 1, kSL,
+                                                     kSL, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = rt * 16 + 4 * lg + i;
+                        pdq[r * DK + dt * 16 + lc] = gam[r] * acc[i];
+                    }
+                } else {                      // dP tile (rt, it), lower with the diagonal
+                    const int t2 = tile - 4 * (DK / 16), rt = t2 >> 2, it = t2 & 3;
+                    const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], kP, 1, &U[it * 16][0], 1, kP,
+                                                     kSL, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = rt * 16 + 4 * lg + i, c = it * 16 + lc;
+                        pdP[r * kC + c] = (c <= r && r < n) ? acc[i] : 0.f;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // ---- step 4: per-token sums, dv, dk share and dA (48 tiles)
         if (tid < kC) {
             const int r = tid;
             float dwr = 0.f, dg1 = 0.f, db = 0.f, dg2 = 0.f;
@@ -374,58 +417,70 @@ __global__ void __launch_bounds__(kBT) bwd_scan_kernel(BwdArgs a) {
             pvec[kC + r] = dg1 - Bt[r] * dg2;
             pvec[2 * kC + r] = dwr;
         }
-        // dv for this slice's columns
-        for (int e = tid; e < kC * kSL; e += kBT) {
+        for (int e = tid; e < kC * kSL; e += kScanT) {
             const int r = e / kSL, j = e % kSL;
             if (r < n) a.dv_[((size_t)(t0 + r) * H + h) * dv + j0 + j] = Bt[r] * dR[r][j];
         }
-        // dk share: (w o U) dS'^T - ((beta gamma) o dR) S^T;  dq share: (gamma o dY) S^T
-        for (int e = tid; e < kC * DK; e += kBT) {
-            const int r = e / DK, d = e % DK;
-            float a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll 4
-            for (int j = 0; j < kSL; ++j) {
-                a1 += U[r][j] * dS[d][j];
-                a2 += dR[r][j] * S[d][j];
-                a3 += dY[r][j] * S[d][j];
-            }
-            pdk[e] = w[r] * a1 - Bt[r] * gam[r] * a2;
-            pdq[e] = gam[r] * a3;
-        }
-        // dA = -(dR U^T) strictly lower, dP = (dY U^T) lower
-        for (int e = tid; e < kC * kC; e += kBT) {
-            const int r = e / kC, i = e % kC;
-            float da = 0.f, dp = 0.f;
-            if (i <= r && r < n) {
-#pragma unroll 4
-                for (int j = 0; j < kSL; ++j) {
-                    da += dR[r][j] * U[i][j];
-                    dp += dY[r][j] * U[i][j];
+        for (int tile = wave; tile < 4 * (DK / 16) + 16; tile += NW) {
+            if (tile < 4 * (DK / 16)) {   // dk share: w o (U dS'^T) - (beta gamma) o (dR S^T)
+                const int rt = tile / (DK / 16), dt = tile % (DK / 16);
+                const floatx4 a1 = mma_f32_tile(&U[rt * 16][0], kP, 1, &dS[dt * 16][0], 1, kSL, kSL,
+                                                floatx4{0.f, 0.f, 0.f, 0.f});
+                const floatx4 a2 = mma_f32_tile(&dR[rt * 16][0], kP, 1, &S[dt * 16][0], 1, kSL, kSL,
+                                                floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rt * 16 + 4 * lg + i;
+                    pdk[r * DK + dt * 16 + lc] = w[r] * a1[i] - Bt[r] * gam[r] * a2[i];
+                }
+            } else {                      // dA = -(dR U^T), strictly lower
+                const int t2 = tile - 4 * (DK / 16), rt = t2 >> 2, it = t2 & 3;
+                const floatx4 acc = mma_f32_tile(&dR[rt * 16][0], kP, 1, &U[it * 16][0], 1, kP, kSL,
+                                                 floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rt * 16 + 4 * lg + i, c = it * 16 + lc;
+                    pdA[r * kC + c] = (c < r && r < n) ? -acc[i] : 0.f;
                 }
             }
-            pdA[e] = i < r ? -da : 0.f;
-            pdP[e] = dp;
         }
         __syncthreads();
-        // scale in place for the state gradient: dY <- gamma o dY, dR <- (beta gamma) o dR
-        for (int e = tid; e < kC * kSL; e += kBT) {
+        // ---- step 5: dS = gamma_C dS' + Q^T (gamma o dY) - K^T ((beta gamma) o dR)
+        for (int e = tid; e < kC * kSL; e += kScanT) {   // scaled copies into QS and KS
             const int r = e / kSL, j = e % kSL;
-            dY[r][j] *= gam[r];
-            dR[r][j] *= Bt[r] * gam[r];
+            QS[r][j] = gam[r] * dY[r][j];
+            KS[r][j] = Bt[r] * gam[r] * dR[r][j];
         }
         __syncthreads();
-        // dS = gamma_C dS' + Q^T (gamma o dY) - K^T ((beta gamma) o dR)
+        static_assert(DK / 16 <= 2 * NW, "dS tiles per wave");
+        floatx4 dsn[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         const float gC = gam[n - 1];
-        for (int e = tid; e < DK * kSL; e += kBT) {
-            const int d = e / kSL, j = e % kSL;
-            float acc = gC * dS[d][j];
-            for (int r = 0; r < n; ++r) acc += Qs[r][d] * dY[r][j] - Ks[r][d] * dR[r][j];
-            dS[d][j] = acc;   // each element read and written by the same thread
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int dt = wave + u * NW;
+            if (dt < DK / 16) {
+                const floatx4 a1 = mma_f32_tile(&Qs[0][dt * 16], 1, DK + 1, &QS[0][0], kP, 1, kC,
+                                                floatx4{0.f, 0.f, 0.f, 0.f});
+                const floatx4 a2 = mma_f32_tile(&Ks[0][dt * 16], 1, DK + 1, &KS[0][0], kP, 1, kC,
+                                                floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dsn[u][i] = gC * dS[dt * 16 + 4 * lg + i][lc] + a1[i] - a2[i];
+            }
+        }
+        __syncthreads();   // every read of dS' is done
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int dt = wave + u * NW;
+            if (dt < DK / 16) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dS[dt * 16 + 4 * lg + i][lc] = dsn[u][i];
+            }
         }
     }
     __syncthreads();
     if (a.dS0) {
-        for (int e = tid; e < DK * kSL; e += kBT) {
+        for (int e = tid; e < DK * kSL; e += kScanT) {
             const int d = e / kSL, j = e % kSL;
             a.dS0[st_off + (size_t)d * dv + j0 + j] = dS[d][j];
         }
@@ -574,7 +629,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
     do {                                                                                        \
         hipLaunchKernelGGL((bwd_ap_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kFinT), 0, s, a);    \
         hipLaunchKernelGGL((bwd_states_kernel<DK, TI>), dim3(seq_blocks), dim3(kBT), 0, s, a);  \
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, TI, TD>), dim3(seq_blocks), dim3(kBT), 0, s, a); \
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, TI, TD>), dim3(seq_blocks), dim3(kScanT), 0, s, a); \
         hipLaunchKernelGGL((bwd_finish_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kFinT), 0, s, a); \
     } while (0)
     if (c.dk == 128) {
