@@ -1,4 +1,4 @@
-// Backward pass of the chunkwise gated delta rule on gfx950 (fp32 vector ALU).
+// Backward pass of the chunkwise gated delta rule on gfx950 (fp32, products on the matrix core).
 //
 // Reading notes of "On the Design of Qwen3.8-Next Architecture", section 2.1.1, eqs. (1)-(5):
 // the gradients of y and S_T with respect to q, k, v, g = log(alpha), beta and S0. Per chunk of
@@ -159,22 +159,40 @@ __global__ void __launch_bounds__(kFinT) bwd_ap_kernel(BwdArgs a) {
     __syncthreads();
     const size_t ch = (size_t)c * H + h;
     if (tid < kC) a.G[ch * kC + tid] = G[tid];
-    for (int e = tid; e < kC * kC; e += kFinT) {
-        const int r = e / kC, i = e % kC;
-        float ak = 0.f, pv = 0.f;
-        if (i <= r && r < n) {
-            float kk = 0.f, qk = 0.f;
-            for (int d = 0; d < DK; ++d) {
-                kk += Ks[r][d] * Ks[i][d];
-                qk += Qs[r][d] * Ks[i][d];
+    // K K^T and Q K^T on the matrix core, one 16x16 tile per wave (the 10 tiles on or below the
+    // diagonal of each), then the decay and the masks per element; tiles above are zero
+    const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
+    for (int tile = wave; tile < 32; tile += kFinT / kWave) {
+        const int kind = tile / 16, rt = (tile % 16) / 4, it = tile % 4;
+        const size_t base = ch * kC * kC;
+        if (it > rt) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = rt * 16 + 4 * lg + u, i = it * 16 + lc;
+                if (kind == 0) {
+                    A[r][i] = 0.f;
+                    a.Ak[base + r * kC + i] = 0.f;
+                } else {
+                    a.P[base + r * kC + i] = 0.f;
+                }
             }
-            const float dec = expf(G[r] - G[i]);
-            pv = dec * qk;
-            if (i < r) ak = dec * kk;
+            continue;
         }
-        A[r][i] = Bt[r] * ak;
-        a.Ak[ch * kC * kC + e] = ak;
-        a.P[ch * kC * kC + e] = pv;
+        const float* X = kind ? &Qs[rt * 16][0] : &Ks[rt * 16][0];
+        const floatx4 acc = mma_f32_tile(X, DK + 1, 1, &Ks[it * 16][0], 1, DK + 1, DK,
+                                         floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = rt * 16 + 4 * lg + u, i = it * 16 + lc;
+            const float dec = (i <= r && r < n) ? expf(G[r] - G[i]) : 0.f;
+            if (kind == 0) {
+                const float ak = i < r ? dec * acc[u] : 0.f;
+                A[r][i] = Bt[r] * ak;
+                a.Ak[base + r * kC + i] = ak;
+            } else {
+                a.P[base + r * kC + i] = dec * acc[u];
+            }
+        }
     }
     __syncthreads();
     // T = (I + A)^{-1}: thread c forward-substitutes column c, held in registers (fully
@@ -194,6 +212,7 @@ __global__ void __launch_bounds__(kFinT) bwd_ap_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ states: forward sweep
+// The three products of a chunk step run on the fp32 matrix core, one 16x16 output tile per wave.
 template <int DK, typename Tin>
 __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
     __shared__ float Ks[kC][DK + 1];
@@ -201,11 +220,14 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
     __shared__ float T[kC][kC + 1];
     __shared__ float R[kC][kP], W[kC][kP];
     __shared__ float gam[kC], w[kC], Bt[kC];
+    static_assert(DK / 16 <= kBT / kWave, "one state tile per wave");
     const int slices = a.dv / kSL;
     const int slice = blockIdx.x % slices;
     const int h = (blockIdx.x / slices) % a.H;
     const int sq = blockIdx.x / (slices * a.H);
     const int j0 = slice * kSL, tid = threadIdx.x, H = a.H, dv = a.dv;
+    const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
     int lo, hi, cbase;
     seq_info(a, sq, lo, hi, cbase);
     const size_t st_off = ((size_t)sq * H + h) * DK * dv;
@@ -223,6 +245,10 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
         }
         load_rows<DK, Tin>(a.k, t0, n, H, h, Ks);
         for (int e = tid; e < kC * kC; e += kBT) T[e / kC][e % kC] = a.T[ch * kC * kC + e];
+        for (int e = tid; e < kC * kSL; e += kBT) {   // V, zero past n
+            const int r = e / kSL, j = e % kSL;
+            R[r][j] = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
+        }
         if (tid < kC) {
             const float* Gc = a.G + ch * kC;
             gam[tid] = expf(Gc[tid]);
@@ -230,28 +256,35 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
             Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
         }
         __syncthreads();
-        for (int e = tid; e < kC * kSL; e += kBT) {   // R = beta o (V - gamma o K S)
-            const int r = e / kSL, j = e % kSL;
-            float ks = 0.f;
-#pragma unroll 4
-            for (int d = 0; d < DK; ++d) ks += Ks[r][d] * S[d][j];
-            const float vr = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
-            R[r][j] = Bt[r] * (vr - gam[r] * ks);
+        if (wave < kC / 16) {   // R = beta o (V - gamma o K S)
+            const floatx4 ks = mma_f32_tile(&Ks[wave * 16][0], DK + 1, 1, &S[0][0], kSL, 1, DK, zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wave * 16 + 4 * lg + i;
+                R[r][lc] = Bt[r] * (R[r][lc] - gam[r] * ks[i]);
+            }
         }
         __syncthreads();
-        for (int e = tid; e < kC * kSL; e += kBT) {   // W = w o (T R)
-            const int r = e / kSL, j = e % kSL;
-            float u = 0.f;
-            for (int i = 0; i <= r; ++i) u += T[r][i] * R[i][j];
-            W[r][j] = w[r] * u;
+        if (wave < kC / 16) {   // W = w o (T R); T is lower triangular
+            const floatx4 u = mma_f32_tile(&T[wave * 16][0], kC + 1, 1, &R[0][0], kP, 1, kC, zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wave * 16 + 4 * lg + i;
+                W[r][lc] = w[r] * u[i];
+            }
         }
         __syncthreads();
-        const float gC = gam[n - 1];
-        for (int e = tid; e < DK * kSL; e += kBT) {   // S' = gamma_C S + K^T W
-            const int d = e / kSL, j = e % kSL;
-            float acc = 0.f;
-            for (int i = 0; i < n; ++i) acc += Ks[i][d] * W[i][j];
-            S[d][j] = gC * S[d][j] + acc;
+        floatx4 sn = zero;   // S' = gamma_C S + K^T W (rows of K past n are zero)
+        if (wave < DK / 16) {
+            const float gC = gam[n - 1];
+            sn = mma_f32_tile(&Ks[0][wave * 16], 1, DK + 1, &W[0][0], kP, 1, kC, zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sn[i] += gC * S[wave * 16 + 4 * lg + i][lc];
+        }
+        __syncthreads();
+        if (wave < DK / 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[wave * 16 + 4 * lg + i][lc] = sn[i];
         }
     }
 }
@@ -572,24 +605,30 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
         a.dg[row] = dG[tid];
         a.dbeta[row] = dbs[tid];
     }
-    // dq = sum of shares + dQK K;  dk = sum of shares + (dKK + dKK^T) K + dQK^T Q
-    for (int e = tid; e < kC * DK; e += kFinT) {
-        const int r = e / DK, d = e % DK;
-        if (r >= n) continue;
-        float dq = 0.f, dk = 0.f;
-        for (int s = 0; s < slices; ++s) {
-            const float* pp = a.part + (ch * slices + s) * part_floats(DK);
-            dq += pp[e];
-            dk += pp[kC * DK + e];
+    // dq = sum of shares + dQK K;  dk = sum of shares + (dKK + dKK^T) K + dQK^T Q, one 16x16
+    // output tile per wave on the matrix core (entries past n are zero on both sides)
+    const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int tile = wave; tile < (kC / 16) * (DK / 16); tile += kFinT / kWave) {
+        const int rt = tile / (DK / 16), dt = tile % (DK / 16);
+        const floatx4 q1 = mma_f32_tile(&dQK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, zero);
+        floatx4 k1 = mma_f32_tile(&dKK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, zero);
+        k1 = mma_f32_tile(&dKK[0][rt * 16], 1, kC + 1, &Ks[0][dt * 16], DK + 1, 1, kC, k1);
+        k1 = mma_f32_tile(&dQK[0][rt * 16], 1, kC + 1, &Qs[0][dt * 16], DK + 1, 1, kC, k1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rt * 16 + 4 * lg + i, d = dt * 16 + lc;
+            if (r >= n) continue;
+            float dq = q1[i], dk = k1[i];
+            for (int s = 0; s < slices; ++s) {
+                const float* pp = a.part + (ch * slices + s) * part_floats(DK) + r * DK + d;
+                dq += pp[0];
+                dk += pp[kC * DK];
+            }
+            const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
+            a.dq[off] = dq;
+            a.dk_[off] = dk;
         }
-#pragma unroll 4
-        for (int i = 0; i < n; ++i) {
-            dq += dQK[r][i] * Ks[i][d];
-            dk += (dKK[r][i] + dKK[i][r]) * Ks[i][d] + dQK[i][r] * Qs[i][d];
-        }
-        const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
-        a.dq[off] = dq;
-        a.dk_[off] = dk;
     }
 }
 
