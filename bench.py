@@ -144,6 +144,33 @@ def main():
     log(f"[bench] pipeline {ms_step * 1e3:.1f} us/step = {mtoks:.1f} Mtok/s "
         f"(preprocess {t_pre * 1e3:.1f} us, prefill {t_pf * 1e3:.1f} us, gate {t_og * 1e3:.1f} us)")
 
+    # the same token mixer through the fused entry point (conv, SiLU, L2Norm and gates inside
+    # the per-chunk kernel; bit-identical outputs)
+    ws_f = torch.empty(gdn.gdn_fused_prefill_workspace_size(ntok, nseq, H, dk, dv),
+                       dtype=torch.uint8, device=dev)
+    o_f = torch.empty_like(o)
+
+    def fstep():
+        gdn.gdn_fused_prefill(X["xq"], X["xk"], X["xv"], X["wq"], X["wk"], X["wv"], X["a_raw"],
+                              X["b_raw"], X["A_log"], X["dt_bias"], X["z"], X["nw"], H=H,
+                              num_seqs=nseq, output_final_state=False, o=o_f, workspace=ws_f)
+    for _ in range(10):
+        fstep()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        fstep()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_fused = t_start.elapsed_time(t_end) / args.steps
+    fused_prefill = {"workload": "gdn_fused_prefill at B=4 H=16 T=4096 d=128 (bf16 x, z, o)",
+                     "calls": args.steps, "us_per_call": round(ms_fused * 1e3, 1),
+                     "Mtok_s": round(ntok / (ms_fused * 1e-3) / 1e6, 2),
+                     "vs_separate_kernels": round(ms_step / ms_fused, 3)}
+    log(f"[bench] fused prefill {ms_fused * 1e3:.1f} us/call = {fused_prefill['Mtok_s']} Mtok/s "
+        f"({ms_step / ms_fused:.2f}x the separate kernels)")
+    del ws_f, o_f
+
     pf_bytes, pf_flops = prefill_algorithmic(H, dk, dv, ntok, nseq, False, False)
     pre_bytes = ntok * H * (2 * dk + dv) * (2 + 2) + ntok * H * 16 + 3 * H * 128 * 4 * 4
     og_bytes = ntok * H * dv * (2 + 2 + 2)
@@ -321,6 +348,73 @@ def main():
         del state, qm, km, vm, gm, bm, ym
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------------ fused decode step
+    if decode is not None:
+        S_ = args.decode_steps
+        log(f"[bench] generating fused decode inputs N=256 H=32 d=128, {S_} steps")
+        fi = gi.decode_layer_draws(0, S_, 256, 32)
+        N, DH, fdk, fdv = fi["N"], fi["H"], fi["dk"], fi["dv"]
+        F = {x: d(fi[x], True) for x in ("xq", "xk", "xv", "z", "conv_state")}
+        F.update({x: d(fi[x]) for x in ("wq", "wk", "wv", "a_raw", "b_raw", "A_log", "dt_bias",
+                                        "norm_weight", "state")})
+        of = torch.empty((N, DH, fdv), dtype=bf, device=dev)
+
+        def fdec(s):
+            gdn.gdn_fused_decode(F["xq"][s], F["xk"][s], F["xv"][s], F["wq"], F["wk"], F["wv"],
+                                 F["conv_state"], F["a_raw"][s], F["b_raw"][s], F["A_log"],
+                                 F["dt_bias"], F["state"], F["z"][s], F["norm_weight"], o=of)
+        for s in range(min(3, S_)):
+            fdec(s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(S_):
+            fdec(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fms = e0.elapsed_time(e1) / S_
+        # the same step through the separate kernels: preprocess with the conv history carried
+        # (double-buffered), the single-token update, the output gate
+        hist = [F["conv_state"], torch.empty_like(F["conv_state"])]
+        qkv = dict(q=torch.empty((N, DH, fdk), dtype=bf, device=dev),
+                   k=torch.empty((N, DH, fdk), dtype=bf, device=dev),
+                   v=torch.empty((N, DH, fdv), dtype=bf, device=dev),
+                   g=torch.empty((N, DH), dtype=torch.float32, device=dev),
+                   beta=torch.empty((N, DH), dtype=torch.float32, device=dev))
+        ysep = torch.empty((N, DH, fdv), dtype=bf, device=dev)
+
+        def sdec(s):
+            gdn.gdn_preprocess_stateful(F["xq"][s], F["xk"][s], F["xv"][s], F["wq"], F["wk"],
+                                        F["wv"], F["a_raw"][s], F["b_raw"][s], F["A_log"],
+                                        F["dt_bias"], H=DH, num_seqs=N, out_dtype=bf, outs=qkv,
+                                        conv_state_in=hist[s % 2], conv_state_out=hist[1 - s % 2])
+            gdn.gdn_decode_step(qkv["q"], qkv["k"], qkv["v"], qkv["g"], qkv["beta"], F["state"],
+                                y=ysep)
+            gdn.gdn_output_gate(ysep, F["z"][s], F["norm_weight"], eps=1e-6, o=of)
+        for s in range(min(2, S_)):
+            sdec(s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(S_ - S_ % 2):
+            sdec(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / max(1, S_ - S_ % 2)
+        heads = N * DH
+        f_state = heads * fdk * fdv * 4 * 2
+        f_tok = heads * ((2 * fdk + fdv) * 2 * (1 + 3 + 3) + 8 + fdv * (2 + 2))
+        fgbs = (f_state + f_tok) / (fms * 1e-3) / 1e9
+        decode["fused"] = {
+            "workload": "gdn_fused_decode N=256 H=32 d_k=d_v=128: conv with carried history, "
+                        "gates, state update and output gate in one kernel (bf16 x, z, o)",
+            "steps": S_, "us_per_step": round(fms * 1e3, 2), "GB_s": round(fgbs, 1),
+            "hbm_frac": round(fgbs / HBM_PEAK_GBS, 4), "bytes_per_step": f_state + f_tok,
+            "separate_kernels_us_per_step": round(sms * 1e3, 2),
+            "vs_separate_kernels": round(sms / fms, 3)}
+        log(f"[bench] fused decode {fms * 1e3:.1f} us/step ({fgbs:.0f} GB/s, {fgbs / HBM_PEAK_GBS:.1%} "
+            f"of HBM); separate kernels {sms * 1e3:.1f} us/step")
+        del F, of, hist, qkv, ysep
+        torch.cuda.empty_cache()
+
     if args.calibrate_copy:
         n = 1 << 28
         src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -360,7 +454,7 @@ def main():
                                "(C=64) + output gate", "B": 4, "H": H, "T": sh.lengths[0],
                    "d_k": dk, "d_v": dv, "tokens_per_step": ntok},
         "kernels": kernels, "roofline": roofline, "decode": decode, "backward": backward,
-        "per_channel_decay": kda,
+        "per_channel_decay": kda, "fused_prefill": fused_prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -83,6 +83,17 @@ def lib():
         L.gdn_output_gate.restype = _i
         L.gdn_output_gate.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, ctypes.c_float, _vp, _i,
                                       _vp]
+        L.gdn_fused_prefill_workspace_size.restype = ctypes.c_size_t
+        L.gdn_fused_prefill_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+        L.gdn_fused_prefill.restype = _i
+        L.gdn_fused_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
+                                        ctypes.c_float, _vp, _i, _vp, ctypes.c_float, _vp, _vp,
+                                        _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.gdn_fused_decode.restype = _i
+        L.gdn_fused_decode.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
+                                       _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_float, _i, _i,
+                                       _i, _i, _vp, _i, _vp, _vp]
         _lib = L
     return _lib
 
@@ -371,7 +382,85 @@ def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream
     return o
 
 
+def gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv) -> int:
+    return int(lib().gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv))
+
+
+def gdn_fused_prefill(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, z, norm_weight, *,
+                      H, initial_state=None, output_final_state=True, cu_seqlens=None,
+                      cu_seqlens_host=None, num_seqs=1, l2_eps=1e-6, rms_eps=1e-6, o=None,
+                      o_dtype=torch.bfloat16, export=False, workspace=None, stream=None):
+    """eqs. 6-11 in one call. xq, xk: [ntok,H,128], xv, z: [ntok,H,dv] (bf16/fp32); conv taps
+    [H*d,4] fp32; a_raw, b_raw: [ntok,H] fp32; A_log, dt_bias: [H]; norm_weight: [dv].
+    Returns (o, final_state) or, with export=True, (o, final_state, dict(q, k, v, g, beta, y))."""
+    ntok = xq.shape[0]
+    dk, dv = xq.shape[-1], xv.shape[-1]
+    dev = xq.device
+    if o is None:
+        o = torch.empty((ntok, H, dv), dtype=_tag_dtype(_tag(o_dtype)), device=dev)
+    final_state = (torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+                   if output_final_state else None)
+    ex = {}
+    if export:
+        bf = torch.bfloat16
+        ex = dict(q=torch.empty((ntok, H, dk), dtype=bf, device=dev),
+                  k=torch.empty((ntok, H, dk), dtype=bf, device=dev),
+                  v=torch.empty((ntok, H, dv), dtype=bf, device=dev),
+                  g=torch.empty((ntok, H), dtype=torch.float32, device=dev),
+                  beta=torch.empty((ntok, H), dtype=torch.float32, device=dev),
+                  y=torch.empty((ntok, H, dv), dtype=bf, device=dev))
+    need = gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+    f32 = torch.float32
+    st = lib().gdn_fused_prefill(
+        _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), _dtype_tag(xq), _ptr(wq, "wq", f32),
+        _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4, _ptr(a_raw, "a_raw", f32),
+        _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32), _ptr(dt_bias, "dt_bias", f32),
+        l2_eps, _ptr(z, "z"), _dtype_tag(z), _ptr(norm_weight, "norm_weight", f32), rms_eps,
+        _ptr(initial_state, "initial_state", f32), _ptr(final_state, "final_state", f32),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32),
+        ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
+        _ptr(o, "o"), _dtype_tag(o), _ptr(ex.get("q"), "q"), _ptr(ex.get("k"), "k"),
+        _ptr(ex.get("v"), "v"), _ptr(ex.get("g"), "g"), _ptr(ex.get("beta"), "beta"),
+        _ptr(ex.get("y"), "y"), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gdn_fused_prefill")
+    return (o, final_state, ex) if export else (o, final_state)
+
+
+def gdn_fused_decode(xq, xk, xv, wq, wk, wv, conv_state, a_raw, b_raw, A_log, dt_bias, state, z,
+                     norm_weight, *, l2_eps=1e-6, rms_eps=1e-6, o=None, o_dtype=None,
+                     want_y=False, stream=None):
+    """One decode step from the projected streams. xq, xk: [N,H,dk], xv, z: [N,H,dv] (bf16/fp32,
+    z in the dtype of x); conv_state: [N,3,H*(2dk+dv)] (x dtype) and state: [N,H,dk,dv] fp32,
+    both updated in place. Returns o, or (o, y) with want_y=True."""
+    N, H, dk = xq.shape
+    dv = xv.shape[-1]
+    x_tag = _dtype_tag(xq)
+    if z.dtype != xq.dtype:
+        raise GdnError("z must have the dtype of xq")
+    o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else x_tag)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=_tag_dtype(o_tag), device=xq.device)
+    y = torch.empty_like(o) if want_y else None
+    f32 = torch.float32
+    st = lib().gdn_fused_decode(
+        _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), x_tag, _ptr(wq, "wq", f32),
+        _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4, _ptr(conv_state, "conv_state", xq.dtype),
+        _ptr(a_raw, "a_raw", f32), _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32),
+        _ptr(dt_bias, "dt_bias", f32), l2_eps, _ptr(state, "state", f32), _ptr(z, "z"),
+        _ptr(norm_weight, "norm_weight", f32), rms_eps, N, H, dk, dv, _ptr(o, "o"), o_tag,
+        _ptr(y, "y"), _stream(stream))
+    _check(st, "gdn_fused_decode")
+    return (o, y) if want_y else o
+
+
 __all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_preprocess_stateful",
            "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_chunk_backward",
            "gdn_chunk_backward_workspace_size", "gdn_kda_chunk_prefill", "gdn_decode_step",
-           "gdn_decode_multi", "gdn_output_gate"]
+           "gdn_decode_multi", "gdn_output_gate", "gdn_fused_prefill",
+           "gdn_fused_prefill_workspace_size", "gdn_fused_decode"]

@@ -209,14 +209,13 @@ __device__ __forceinline__ void store_tile_bf16(const float* src, uint16_t* dst,
     }
 }
 
-__global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) {
-    __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
-    __shared__ __attribute__((aligned(16))) float sG[kC], sB[kC];
-
-    const int chunk = blockIdx.x, h = blockIdx.y;
-    int seq, t0, n;
-    if (!chunk_of(a, chunk, seq, t0, n)) return;
-    const int lane = threadIdx.x;
+// T, P and the gate rows of one (chunk, head), by one wave. (gv, bv) are g and beta of row
+// min(lane, n-1). sA, sG, sB are the wave's own LDS; the barriers inside are workgroup-wide,
+// so in a workgroup of several waves every wave calls this together (one head each).
+__device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int h, int t0, int n,
+                                                float gv, float bv, float* sA, float* sG,
+                                                float* sB) {
+    const int lane = threadIdx.x & (kWave - 1);
 
     // fragment rows (lane % 32) and (32 + lane % 32); rows >= n are zero
     const int r0 = lane & 31, r1 = 32 + (lane & 31);
@@ -232,8 +231,6 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
         fq0[kk] = *reinterpret_cast<const u32x4*>(q0p + kk * 16);
         fq1[kk] = *reinterpret_cast<const u32x4*>(q1p + kk * 16);
     }
-    float gv, bv;
-    fetch_gates(a, t0, n, h, gv, bv);
     {
         // running sum G of g over the chunk (rows >= n add nothing), and the chunk's beta,
         // gamma_r = e^{G_r} and gamma_C / gamma_r for the scan
@@ -397,6 +394,148 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     for (int i = 0; i < 16; ++i) sA[acc_row(i, lane) * kStrA + 32 + c] = 0.f;
     __syncthreads();
     store_tile_bf16(sA, a.Pw + tile, lane);
+}
+
+__global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) {
+    __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
+    __shared__ __attribute__((aligned(16))) float sG[kC], sB[kC];
+    const int chunk = blockIdx.x, h = blockIdx.y;
+    int seq, t0, n;
+    if (!chunk_of(a, chunk, seq, t0, n)) return;
+    float gv, bv;
+    fetch_gates(a, t0, n, h, gv, bv);
+    prep_chunk_head(a, chunk, h, t0, n, gv, bv, sA, sG, sB);
+}
+
+// ------------------------------------------------------------------ fused front end
+// eqs. (6)-(10) of the notes for one chunk of HPW heads, then each head's T and P (one wave
+// per head), in one workgroup: conv (width 4, zero input before the sequence start) -> SiLU
+// -> L2Norm for q and k, conv -> SiLU for v, the gates beta = sigmoid(b), g = -e^A
+// softplus(a + dt_bias). q, k, v leave in bf16 (the scan reads them) with plain stores, so the
+// T/P stage that follows the barrier reads q and k back from L2, not HBM.
+// Stream layout: a thread owns 8 adjacent channels (one 16-byte bf16 store) of a strip of
+// D/8 consecutive rows; the D/8 threads of one (row, head) are adjacent lanes, so the L2Norm
+// is an in-register shuffle reduction. The 3 rows before a strip are its conv window.
+// A thread's rows of one stream come in P pieces of RP consecutive rows, each with the 3 rows
+// before it as its conv window: issue() puts a piece's loads in flight, run() computes and
+// stores it. Two pieces are in flight at a time (the next one loads while this one runs).
+template <int HPW, int D, typename Tin>
+struct FrontPiece {
+    static constexpr int G = HPW * D / 8;              // channel groups of the head group
+    static constexpr int RS = kC * G / (HPW * kWave);  // rows per thread per stream (D / 8)
+    static constexpr int P = sizeof(Tin) == 2 ? 2 : 4; // pieces per stream
+    static constexpr int RP = RS / P;                  // rows per piece
+    typename Vec8<Tin>::Raw raw[RP + 3];               // rows r0-3 .. r0+RP-1
+
+    __device__ __forceinline__ static int first_row(int part) {
+        return (threadIdx.x / G) * RS + part * RP;
+    }
+
+    __device__ __forceinline__ void issue(const FrontArgs& f, int role, int part, int t0, int n,
+                                          int seq_lo, int h0, int H) {
+        const int r0 = first_row(part), c = h0 * D + (threadIdx.x % G) * 8;
+        const Tin* x = static_cast<const Tin*>(f.x[role]);
+        // addresses clamped into the chunk's sequence: rows before its start are zeroed in
+        // run(), rows past n are not stored
+#pragma unroll
+        for (int j = 0; j < RP + 3; ++j) {
+            const int t = min(max(t0 + r0 - 3 + j, seq_lo), t0 + n - 1);
+            raw[j] = Vec8<Tin>::template load_raw<true>(x + (size_t)t * H * D + c);
+        }
+    }
+
+    __device__ __forceinline__ void run(const FrontArgs& f, int role, int part, int t0, int n,
+                                        int seq_lo, int h0, int H) const {
+        const int r0 = first_row(part), c = h0 * D + (threadIdx.x % G) * 8;
+        uint16_t* out = f.out[role];
+        float w[8][4];
+        {
+            const float4* wp = reinterpret_cast<const float4*>(f.w[role] + (size_t)c * 4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 t = wp[i];
+                w[i][0] = t.x; w[i][1] = t.y; w[i][2] = t.z; w[i][3] = t.w;
+            }
+        }
+        float win[3][8];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            Vec8<Tin>::unpack(raw[j], win[j]);
+            if (t0 + r0 - 3 + j < seq_lo)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) win[j][i] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < RP; ++j) {
+            float xi[8], act[8], ss = 0.f;
+            Vec8<Tin>::unpack(raw[j + 3], xi);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                act[i] = siluf_(conv4(w[i][0], w[i][1], w[i][2], w[i][3], win[0][i], win[1][i],
+                                      win[2][i], xi[i]));
+                ss = __builtin_fmaf(act[i], act[i], ss);
+            }
+            if (role < 2) {
+                ss = group_sum<D / 8>(ss);
+                const float inv = frsq(ss + f.l2_eps);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) act[i] *= inv;
+            }
+            if (r0 + j < n) Vec8<uint16_t>::store(out + (size_t)(t0 + r0 + j) * H * D + c, act);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                win[0][i] = win[1][i];
+                win[1][i] = win[2][i];
+                win[2][i] = xi[i];
+            }
+        }
+    }
+};
+
+template <int HPW, int DV, typename Tin>
+__global__ void __launch_bounds__(HPW * kWave, 2) chunk_front_kernel(DevArgs a, FrontArgs f) {
+    __shared__ __attribute__((aligned(16))) float sA[HPW][kC * kStrA];
+    __shared__ __attribute__((aligned(16))) float sG[HPW][kC], sB[HPW][kC];
+    const int chunk = blockIdx.x, h0 = blockIdx.y * HPW;
+    int seq, t0, n;
+    if (!chunk_of(a, chunk, seq, t0, n)) return;
+    const int seq_lo = a.cu ? a.cu[seq] : seq * a.L, H = a.H;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, h = h0 + wave;
+    const size_t e = (size_t)(t0 + min(lane, n - 1)) * H + h;
+    const float ar = f.a_raw[e], br = f.b_raw[e];
+    {
+        // pieces in order q0..q(P-1), k0..k(P-1), v0..; buffers x0/x1 alternate (P is even)
+        using PK = FrontPiece<HPW, kDK, Tin>;
+        using PV = FrontPiece<HPW, DV, Tin>;
+        constexpr int NQK = 2 * PK::P;
+        PK x0, x1;
+        PV y0, y1;
+        x0.issue(f, 0, 0, t0, n, seq_lo, h0, H);
+#pragma unroll
+        for (int i = 0; i < NQK; i += 2) {
+            x1.issue(f, (i + 1) / PK::P, (i + 1) % PK::P, t0, n, seq_lo, h0, H);
+            x0.run(f, i / PK::P, i % PK::P, t0, n, seq_lo, h0, H);
+            if (i + 2 < NQK) x0.issue(f, (i + 2) / PK::P, (i + 2) % PK::P, t0, n, seq_lo, h0, H);
+            else y0.issue(f, 2, 0, t0, n, seq_lo, h0, H);
+            x1.run(f, (i + 1) / PK::P, (i + 1) % PK::P, t0, n, seq_lo, h0, H);
+        }
+#pragma unroll
+        for (int i = 0; i < PV::P; i += 2) {
+            y1.issue(f, 2, i + 1, t0, n, seq_lo, h0, H);
+            y0.run(f, 2, i, t0, n, seq_lo, h0, H);
+            if (i + 2 < PV::P) y0.issue(f, 2, i + 2, t0, n, seq_lo, h0, H);
+            y1.run(f, 2, i + 1, t0, n, seq_lo, h0, H);
+        }
+    }
+    // gates: wave = head of the group, lane = row (rows >= n repeat row n-1, as the prep expects)
+    const float gv = gate_g(f.A_log[h], ar, f.dt_bias[h]);
+    const float bv = gate_beta(br);
+    if (f.g_out && lane < n) {
+        f.g_out[e] = gv;
+        f.beta_out[e] = bv;
+    }
+    __syncthreads();   // the chunk's q, k rows of every head are written (and in L2)
+    prep_chunk_head(a, chunk, h, t0, n, gv, bv, sA[wave], sG[wave], sB[wave]);
 }
 
 // ------------------------------------------------------------------ sequential chunk scan
@@ -928,7 +1067,23 @@ size_t chunk_bf16_workspace(int ntok, int num_seqs, int H) {
     return ws_layout(ntok, num_seqs, H).total;
 }
 
-hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
+template <int HPW, typename Tin>
+static void launch_front(const DevArgs& a, const FrontArgs& f, int nchunks, int dv, hipStream_t s) {
+    const dim3 grid(nchunks, a.H / HPW);
+    if (dv == 128)
+        hipLaunchKernelGGL((chunk_front_kernel<HPW, 128, Tin>), grid, dim3(HPW * kWave), 0, s, a, f);
+    else
+        hipLaunchKernelGGL((chunk_front_kernel<HPW, 64, Tin>), grid, dim3(HPW * kWave), 0, s, a, f);
+}
+
+template <typename Tin>
+static void launch_front_h(const DevArgs& a, const FrontArgs& f, int nchunks, int dv, hipStream_t s) {
+    if (a.H % 4 == 0) launch_front<4, Tin>(a, f, nchunks, dv, s);
+    else if (a.H % 2 == 0) launch_front<2, Tin>(a, f, nchunks, dv, s);
+    else launch_front<1, Tin>(a, f, nchunks, dv, s);
+}
+
+hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const FrontArgs* front) {
     const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
     char* ws = static_cast<char*>(c.workspace);
     DevArgs a;
@@ -947,7 +1102,11 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s) {
     a.y_bf16 = c.y_bf16;
     if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
-    if (nchunks > 0)
+    if (nchunks > 0 && front && front->in_bf16)
+        launch_front_h<uint16_t>(a, *front, nchunks, c.dv, s);
+    else if (nchunks > 0 && front)
+        launch_front_h<float>(a, *front, nchunks, c.dv, s);
+    else if (nchunks > 0)
         hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
     const int nsl = c.dv / kSl;
     const int pairs = c.num_seqs * c.H;

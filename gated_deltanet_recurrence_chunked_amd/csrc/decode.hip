@@ -111,6 +111,143 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
 }
 
 // ----------------------------------------------------------------------------------------
+// The whole decode step of the token mixer in one kernel: eqs. (6)-(10) on this step's
+// projected inputs with the carried conv history (depthwise width-4 conv -> SiLU -> L2Norm
+// for q and k, conv -> SiLU for v, the per-head gates), then the single-token update above,
+// then eq. (11) without W_o (o = sigmoid(z) (1 + w) y / rms(y) over the dv channels).
+// The state pass is the same as decode_kernel's; the extra bytes (history, x, z, o) are about
+// 3% of the state's, and the front end runs while the state loads are in flight. q and k stay
+// fp32 (never rounded to bf16 between steps); their L2 norms are folded into the products.
+template <int DK, int DV, typename Tin, typename Tout>
+__global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(DecodeFusedArgs f) {
+    constexpr int TPR = DV / 4;
+    constexpr int RG = kDecThreads / TPR;
+    constexpr int RPT = DK / RG;
+    constexpr int NW = kDecThreads / kWave;
+    static_assert(RPT >= 1 && DK % RG == 0, "shape");
+
+    __shared__ float ks[DK], qs[DK], vs[DV];
+    __shared__ float red[NW][2][DV];
+
+    const int head = blockIdx.x, H = f.H;
+    const int n = head / H, h = head % H;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int c = (tid % TPR) * 4;
+    const int rg = tid / TPR;
+
+    float* S = f.state + (size_t)head * DK * DV;
+    float s[RPT][4];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const floatx4 t = __builtin_nontemporal_load(
+            reinterpret_cast<const floatx4*>(S + (size_t)(rg + RG * i) * DV + c));
+        s[i][0] = t.x; s[i][1] = t.y; s[i][2] = t.z; s[i][3] = t.w;
+    }
+    float zv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (rg == 0) Vec4<Tin>::load(static_cast<const Tin*>(f.z) + (size_t)head * DV + c, zv);
+
+    // conv over [history rows 0..2, x]; the history shifts by one token in place (each
+    // channel's four values are touched by this thread only)
+    Tin* hist = static_cast<Tin*>(f.conv_state) + (size_t)n * 3 * f.hC;
+    for (int ch = tid; ch < 2 * DK + DV; ch += kDecThreads) {
+        const int role = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
+        const int cl = ch - (role == 0 ? 0 : (role == 1 ? DK : 2 * DK));
+        const int d = role < 2 ? DK : DV;
+        const int cs = h * d + cl;                                   // channel in its stream
+        const int hc = (role == 0 ? 0 : (role == 1 ? H * DK : 2 * H * DK)) + cs;
+        const Tin x = static_cast<const Tin*>(f.x[role])[(size_t)n * H * d + cs];
+        const Tin h0 = hist[hc], h1 = hist[f.hC + hc], h2 = hist[2 * f.hC + hc];
+        const float4 w = reinterpret_cast<const float4*>(f.w[role])[cs];
+        const float u = conv4(w.x, w.y, w.z, w.w, load1(&h0), load1(&h1), load1(&h2), load1(&x));
+        hist[hc] = h1;
+        hist[f.hC + hc] = h2;
+        hist[2 * f.hC + hc] = x;
+        const float act = siluf_(u);
+        if (role == 0) qs[cl] = act;
+        else if (role == 1) ks[cl] = act;
+        else vs[cl] = act;
+    }
+    const float a = expf(gate_g(f.A_log[h], f.a_raw[head], f.dt_bias[h]));
+    const float b = gate_beta(f.b_raw[head]);
+    __syncthreads();
+
+    // L2 norms of q and k and the raw k.q (every wave, no extra barrier)
+    float nq = 0.f, nk = 0.f, kq = 0.f;
+#pragma unroll
+    for (int i = lane; i < DK; i += kWave) {
+        nq += qs[i] * qs[i];
+        nk += ks[i] * ks[i];
+        kq += ks[i] * qs[i];
+    }
+    nq = group_sum<kWave>(nq);
+    nk = group_sum<kWave>(nk);
+    kq = group_sum<kWave>(kq);
+    const float iq = frsq(nq + f.l2_eps), ik = frsq(nk + f.l2_eps);
+    kq *= iq * ik;
+
+    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float kr = ks[rg + RG * i], qr = qs[rg + RG * i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pk[j] += s[i][j] * kr;
+            pq[j] += s[i][j] * qr;
+        }
+    }
+#pragma unroll
+    for (int o = TPR; o < kWave; o <<= 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pk[j] += __shfl_xor(pk[j], o, kWave);
+            pq[j] += __shfl_xor(pq[j], o, kWave);
+        }
+    if (lane < TPR) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            red[wave][0][c + j] = pk[j];
+            red[wave][1][c + j] = pq[j];
+        }
+    }
+    __syncthreads();
+    float e[4], yo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            sk += red[w][0][c + j];
+            sq += red[w][1][c + j];
+        }
+        e[j] = vs[c + j] - a * (sk * ik);
+        yo[j] = a * (sq * iq) + b * kq * e[j];
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float bk = b * ik * ks[rg + RG * i];
+        floatx4 t;
+        t.x = a * s[i][0] + bk * e[0];
+        t.y = a * s[i][1] + bk * e[1];
+        t.z = a * s[i][2] + bk * e[2];
+        t.w = a * s[i][3] + bk * e[3];
+        __builtin_nontemporal_store(t, reinterpret_cast<floatx4*>(S + (size_t)(rg + RG * i) * DV + c));
+    }
+    if (rg == 0) {   // the TPR lanes of row group 0 (an aligned group of wave 0) hold all of y
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss += yo[j] * yo[j];
+        ss = group_sum<TPR>(ss);
+        const float inv = frsq(ss * (1.0f / DV) + f.rms_eps);
+        float ov[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[j] = sigmoidf_(zv[j]) * ((1.0f + f.norm_w[c + j]) * (yo[j] * inv));
+        Vec4<Tout>::store(static_cast<Tout*>(f.o) + (size_t)head * DV + c, ov);
+        if (f.y) Vec4<Tout>::store(static_cast<Tout*>(f.y) + (size_t)head * DV + c, yo);
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 // T consecutive tokens per sequence in one pass over the state: the chunkwise form of eq. (5)
 // with the chunk being the T new tokens. With G_t = g_1 + ... + g_t (g = log alpha) and
 // sk_t = S^T k_t, sq_t = S^T q_t of the state S the call starts from:
@@ -375,6 +512,28 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int in_bf1
     else if (dk == 128 && dv == 64) launch_dec<128, 64>(q, k, v, in_bf16, g, beta, state, heads, y, y_bf16, s);
     else if (dk == 64 && dv == 128) launch_dec<64, 128>(q, k, v, in_bf16, g, beta, state, heads, y, y_bf16, s);
     else launch_dec<64, 64>(q, k, v, in_bf16, g, beta, state, heads, y, y_bf16, s);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static void launch_dec_fused(const DecodeFusedArgs& f, hipStream_t s) {
+    const dim3 grid(f.N * f.H), block(kDecThreads);
+    if (f.in_bf16 && f.out_bf16)
+        hipLaunchKernelGGL((decode_fused_kernel<DK, DV, uint16_t, uint16_t>), grid, block, 0, s, f);
+    else if (f.in_bf16)
+        hipLaunchKernelGGL((decode_fused_kernel<DK, DV, uint16_t, float>), grid, block, 0, s, f);
+    else if (f.out_bf16)
+        hipLaunchKernelGGL((decode_fused_kernel<DK, DV, float, uint16_t>), grid, block, 0, s, f);
+    else
+        hipLaunchKernelGGL((decode_fused_kernel<DK, DV, float, float>), grid, block, 0, s, f);
+}
+
+hipError_t launch_decode_fused(const DecodeFusedArgs& f, int dk, int dv, hipStream_t s) {
+    if (f.N * f.H == 0) return hipSuccess;
+    if (dk == 128 && dv == 128) launch_dec_fused<128, 128>(f, s);
+    else if (dk == 128 && dv == 64) launch_dec_fused<128, 64>(f, s);
+    else if (dk == 64 && dv == 128) launch_dec_fused<64, 128>(f, s);
+    else launch_dec_fused<64, 64>(f, s);
     return hipGetLastError();
 }
 

@@ -344,6 +344,123 @@ int gdn_decode_multi(const void* q, const void* k, const void* v, int in_dtype, 
                       "gdn_decode_multi");
 }
 
+size_t gdn_fused_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, int dv) {
+    if (ntok < 0 || num_seqs < 1 || H < 1 || dk != 128 || !valid_dim(dv)) return 0;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t rows = (size_t)ntok * H;
+    return up(gdn::chunk_bf16_workspace(ntok, num_seqs, H)) + 2 * up(rows * dk * 2) +
+           2 * up(rows * dv * 2);
+}
+
+int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,
+                      const float* wk, const float* wv, int conv_k, const float* a_raw,
+                      const float* b_raw, const float* A_log, const float* dt_bias, float l2_eps,
+                      const void* z, int z_dtype, const float* norm_weight, float rms_eps,
+                      const float* initial_state, float* final_state, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
+                      int dv, void* o, int o_dtype, void* q, void* k, void* v, float* g,
+                      float* beta, void* y, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    GDN_REQUIRE(valid_dtype(x_dtype) && valid_dtype(z_dtype) && valid_dtype(o_dtype), GDN_ERR_DTYPE,
+                "x_dtype/z_dtype/o_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(H >= 1 && dk == 128 && valid_dim(dv), GDN_ERR_SHAPE,
+                "need H >= 1, dk = 128 and dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
+    GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
+    GDN_REQUIRE(l2_eps >= 0.f && rms_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps and rms_eps must be >= 0");
+    GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
+    GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
+    GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o);
+    GDN_OPT_PTR(initial_state); GDN_OPT_PTR(final_state);
+    GDN_OPT_PTR(q); GDN_OPT_PTR(k); GDN_OPT_PTR(v); GDN_OPT_PTR(y);
+    GDN_REQUIRE(aligned4(g) && aligned4(beta), GDN_ERR_ALIGN, "g/beta are not 4-byte aligned");
+    GDN_REQUIRE((g == nullptr) == (beta == nullptr), GDN_ERR_NULL,
+                "g and beta are exported together (both or neither)");
+    GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+    GDN_REQUIRE(cu_seqlens_host == nullptr || cu_seqlens != nullptr, GDN_ERR_NULL,
+                "cu_seqlens_host given without the device cu_seqlens");
+    int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
+    if (st) return st;
+    const size_t need = gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv);
+    GDN_REQUIRE(workspace != nullptr && workspace_bytes >= need, GDN_ERR_WORKSPACE,
+                "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    GDN_OPT_PTR(workspace);
+
+    // workspace: [prefill tiles | q | k | v | y]; exported intermediates replace their slot
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t rows = (size_t)ntok * H;
+    char* ws = static_cast<char*>(workspace);
+    size_t off = up(gdn::chunk_bf16_workspace(ntok, num_seqs, H));
+    void* slot[4];
+    const size_t bytes[4] = {rows * dk * 2, rows * dk * 2, rows * dv * 2, rows * dv * 2};
+    for (int i = 0; i < 4; ++i) {
+        slot[i] = ws + off;
+        off += up(bytes[i]);
+    }
+    void* qb = q ? q : slot[0];
+    void* kb = k ? k : slot[1];
+    void* vb = v ? v : slot[2];
+    void* yb = y ? y : slot[3];
+
+    gdn::FrontArgs f;
+    f.x[0] = xq; f.x[1] = xk; f.x[2] = xv;
+    f.in_bf16 = x_dtype == GDN_BF16;
+    f.w[0] = wq; f.w[1] = wk; f.w[2] = wv;
+    f.out[0] = static_cast<uint16_t*>(qb);
+    f.out[1] = static_cast<uint16_t*>(kb);
+    f.out[2] = static_cast<uint16_t*>(vb);
+    f.a_raw = a_raw; f.b_raw = b_raw; f.A_log = A_log; f.dt_bias = dt_bias;
+    f.g_out = g; f.beta_out = beta;
+    f.l2_eps = l2_eps;
+
+    gdn::ChunkArgs a;
+    a.q = qb; a.k = kb; a.v = vb;
+    a.in_bf16 = 1;
+    a.y_bf16 = 1;
+    a.g = nullptr; a.beta = nullptr; a.S0 = initial_state; a.ST = final_state;
+    a.cu = cu_seqlens;
+    a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.dk = dk; a.dv = dv;
+    a.y = yb; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_chunk_bf16(a, s, &f);
+    if (e != hipSuccess) return hip_status(e, "gdn_fused_prefill");
+    return hip_status(gdn::launch_output_gate(yb, 1, z, z_dtype == GDN_BF16, norm_weight, ntok, H,
+                                              dv, rms_eps, o, o_dtype == GDN_BF16, s),
+                      "gdn_fused_prefill");
+}
+
+int gdn_fused_decode(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,
+                     const float* wk, const float* wv, int conv_k, void* conv_state,
+                     const float* a_raw, const float* b_raw, const float* A_log,
+                     const float* dt_bias, float l2_eps, float* state, const void* z,
+                     const float* norm_weight, float rms_eps, int N, int H, int dk, int dv,
+                     void* o, int o_dtype, void* y, void* stream) {
+    GDN_REQUIRE(valid_dtype(x_dtype) && valid_dtype(o_dtype), GDN_ERR_DTYPE,
+                "x_dtype/o_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(N >= 0 && H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need N >= 0, H >= 1 and dk, dv in {64, 128} (got N=%d H=%d dk=%d dv=%d)", N, H,
+                dk, dv);
+    GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
+    GDN_REQUIRE(l2_eps >= 0.f && rms_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps and rms_eps must be >= 0");
+    GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
+    GDN_PTR(conv_state);
+    GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
+    GDN_PTR(state); GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o); GDN_OPT_PTR(y);
+    gdn::DecodeFusedArgs f;
+    f.x[0] = xq; f.x[1] = xk; f.x[2] = xv;
+    f.w[0] = wq; f.w[1] = wk; f.w[2] = wv;
+    f.conv_state = conv_state;
+    f.hC = H * (2 * dk + dv);
+    f.a_raw = a_raw; f.b_raw = b_raw; f.A_log = A_log; f.dt_bias = dt_bias;
+    f.l2_eps = l2_eps;
+    f.state = state; f.z = z; f.norm_w = norm_weight; f.rms_eps = rms_eps;
+    f.o = o; f.y = y;
+    f.N = N; f.H = H;
+    f.in_bf16 = x_dtype == GDN_BF16;
+    f.out_bf16 = o_dtype == GDN_BF16;
+    return hip_status(gdn::launch_decode_fused(f, dk, dv, static_cast<hipStream_t>(stream)),
+                      "gdn_fused_decode");
+}
+
 int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype, const float* norm_weight,
                     int ntok, int H, int dv, float eps, void* o, int o_dtype, void* stream) {
     GDN_REQUIRE(valid_dtype(y_dtype) && valid_dtype(z_dtype) && valid_dtype(o_dtype), GDN_ERR_DTYPE,

@@ -187,9 +187,24 @@ __device__ __forceinline__ float frsq(float x) { return __builtin_amdgcn_rsqf(x)
 __device__ __forceinline__ float sigmoidf_(float x) { return frcp(1.0f + fexp(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x * frcp(1.0f + fexp(-x)); }
 
+// The width-4 causal conv of one channel, oldest tap first (w[3] multiplies the current input),
+// with its fused multiply-adds spelled out, so every kernel that evaluates it (the preprocess,
+// the fused prefill front end, the fused decode) rounds identically.
+__device__ __forceinline__ float conv4(float w0, float w1, float w2, float w3, float x0, float x1,
+                                       float x2, float x3) {
+    return __builtin_fmaf(w3, x3, __builtin_fmaf(w2, x2, __builtin_fmaf(w1, x1, w0 * x0)));
+}
+
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}): no overflow, no cancellation
 __device__ __forceinline__ float softplusf_(float x) {
     return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
 }
+
+// The per-head gates of eqs. (9)-(10): g = log(alpha) = -e^{A} softplus(a + dt_bias),
+// beta = sigmoid(b).
+__device__ __forceinline__ float gate_g(float A_log, float a_raw, float dt_bias) {
+    return -expf(A_log) * softplusf_(a_raw + dt_bias);
+}
+__device__ __forceinline__ float gate_beta(float b_raw) { return sigmoidf_(b_raw); }
 
 }  // namespace gdn

@@ -34,6 +34,24 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int in_bf1
                          const float* g, const float* beta, float* state, int N, int H,
                          int dk, int dv, void* y, int y_bf16, hipStream_t s);
 
+// one decode step from the projected streams: conv with the carried history (updated in
+// place), gates, the state update and the output gate in one kernel
+struct DecodeFusedArgs {
+    const void* x[3];          // xq, xk [N, H, dk], xv [N, H, dv]
+    const float* w[3];         // conv taps [H*d, 4]
+    void* conv_state;          // [N, 3, hC], x dtype, in/out
+    int hC;                    // H * (2 dk + dv)
+    const float *a_raw, *b_raw, *A_log, *dt_bias;
+    float l2_eps;
+    float* state;              // [N, H, dk, dv] fp32, in/out
+    const void* z;             // [N, H, dv], x dtype
+    const float* norm_w;       // [dv]
+    float rms_eps;
+    void* o;                   // [N, H, dv]
+    void* y;                   // nullable, o dtype
+    int N, H, in_bf16, out_bf16;
+};
+hipError_t launch_decode_fused(const DecodeFusedArgs& f, int dk, int dv, hipStream_t s);
 // T <= kMaxDecodeTokens tokens per sequence; steps (nullable): the state after each token
 constexpr int kMaxDecodeTokens = 8;
 hipError_t launch_decode_multi(const void* q, const void* k, const void* v, int in_bf16,
@@ -57,7 +75,18 @@ hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t s);
 
 // bf16 matrix-core chunked path (dk = 128): per-chunk T/P kernel + sequential scan kernel
 size_t chunk_bf16_workspace(int ntok, int num_seqs, int H);
-hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s);
+// The fused front end: q, k, v (bf16, written to out[]) and the gates computed from the
+// projected streams inside the per-chunk T/P kernel (zero conv history at sequence starts).
+struct FrontArgs {
+    const void* x[3];          // xq, xk, xv [ntok, H, d]
+    int in_bf16;               // x dtype
+    const float* w[3];         // conv taps [H*d, 4]
+    uint16_t* out[3];          // q, k, v [ntok, H, d] bf16 (the ChunkArgs q, k, v)
+    const float *a_raw, *b_raw, *A_log, *dt_bias;
+    float *g_out, *beta_out;   // nullable (both or neither)
+    float l2_eps;
+};
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s, const FrontArgs* front = nullptr);
 
 // backward of the chunked gated delta rule (fp32 vector ALU)
 struct ChunkBwdArgs {

@@ -143,11 +143,10 @@ __device__ void conv_stream(const PreprocessArgs& a, int role, int tile, int t0)
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                float u = w[i][0] * win[0][i] + w[i][1] * win[1][i] + w[i][2] * win[2][i] +
-                          w[i][3] * grp[j][i];
-                float sv = siluf_(u);
+                const float sv = siluf_(conv4(w[i][0], w[i][1], w[i][2], w[i][3], win[0][i],
+                                              win[1][i], win[2][i], grp[j][i]));
                 act[i] = sv;
-                ss += sv * sv;
+                ss = __builtin_fmaf(sv, sv, ss);
             }
             if (norm) {
                 ss = (d == 128) ? group_sum<16>(ss) : group_sum<8>(ss);
@@ -171,8 +170,8 @@ __device__ void gates_block(const PreprocessArgs& a, int t0) {
     for (int i = threadIdx.x; i < n; i += kPreThreads) {
         const size_t e = (size_t)t0 * a.H + i;
         const int h = i % a.H;
-        a.g[e] = -expf(a.A_log[h]) * softplusf_(a.a_raw[e] + a.dt_bias[h]);
-        a.beta[e] = sigmoidf_(a.b_raw[e]);
+        a.g[e] = gate_g(a.A_log[h], a.a_raw[e], a.dt_bias[h]);
+        a.beta[e] = gate_beta(a.b_raw[e]);
     }
 }
 

@@ -297,6 +297,37 @@ def make_stream_inputs(seed: int, N: int, H: int, prompt_lengths, steps: int, to
     return out
 
 
+def decode_layer_draws(seed: int, steps: int, N: int, H: int, dk: int = 128, dv: int = 128,
+                       bf16: bool = True) -> dict:
+    """Raw inputs of `steps` decode steps of the whole token mixer (the fused decode step),
+    with the config-1 distributions: per step xq, xk [steps, N, H, dk], xv, z [steps, N, H, dv]
+    (bf16 bits, or float32 with bf16=False), a_raw, b_raw [steps, N, H]; conv taps
+    wq, wk, wv [H*d, 4] ~ N(0, 1/4); A_log, dt_bias [H]; norm_weight [dv] ~ N(0, 0.02);
+    a carried conv history conv_state [N, 3, H*(2dk+dv)] ~ N(0,1) in the x dtype and a
+    state [N, H, dk, dv] ~ N(0, 0.01) fp32."""
+    kids = dict(zip(["x", "g", "w", "z", "h", "s"],
+                    np.random.SeedSequence([SEED_TAG, 99, seed]).spawn(6)))
+    rx, rg, rw, rz, rh, rs = (np.random.default_rng(kids[c]) for c in "xgwzhs")
+    draw = _normal_bf16 if bf16 else _normal
+    lead = (steps, N, H)
+    out = dict(steps=steps, N=N, H=H, dk=dk, dv=dv, bf16=bf16)
+    out["xq"] = draw(rx, lead + (dk,))
+    out["xk"] = draw(rx, lead + (dk,))
+    out["xv"] = draw(rx, lead + (dv,))
+    out["a_raw"] = _normal(rg, lead)
+    out["b_raw"] = _normal(rg, lead)
+    out["A_log"] = np.log(rg.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    out["dt_bias"] = np.full(H, -4.6, dtype=np.float32)
+    out["wq"] = _normal(rw, (H * dk, 4), std=0.5)
+    out["wk"] = _normal(rw, (H * dk, 4), std=0.5)
+    out["wv"] = _normal(rw, (H * dv, 4), std=0.5)
+    out["z"] = draw(rz, lead + (dv,))
+    out["norm_weight"] = _normal(rz, (dv,), std=math.sqrt(0.02))
+    out["conv_state"] = draw(rh, (N, 3, H * (2 * dk + dv)))
+    out["state"] = _normal(rs, (N, H, dk, dv), std=0.1)
+    return out
+
+
 def checksums(inp: dict) -> dict:
     """SHA-256 (first 16 hex digits) of every array, for the results record."""
     res = {}

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -250,6 +250,65 @@ int gdn_decode_multi(const void* q, const void* k, const void* v, int in_dtype, 
 int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype,
                     const float* norm_weight, int ntok, int H, int dv, float eps, void* o,
                     int o_dtype, void* stream);
+
+/* Bytes of device workspace gdn_fused_prefill needs for these sizes (0 for unsupported sizes). */
+size_t gdn_fused_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, int dv);
+
+/*
+ * gdn_fused_prefill - the token mixer between the projections in one call: eqs. (6)-(10)
+ * (conv -> SiLU -> L2Norm, the gates), eqs. (1)-(4) chunkwise, and eq. (11) without W_o,
+ * for packed sequences that start from zero conv history (section 2.1.1 of the notes).
+ * The conv, SiLU, L2Norm and gates run inside the per-chunk kernel that forms each chunk's
+ * (I + A)^{-1} and P, so q and k are written once and read back from cache there, and g and
+ * beta never reach memory unless exported; then the scan and the output gate.
+ *
+ *   xq, xk: [ntok, H, 128], xv: [ntok, H, dv] in x_dtype (the projected streams);
+ *   wq, wk, wv, conv_k (= 4), a_raw, b_raw, A_log, dt_bias, l2_eps: as gdn_preprocess;
+ *   z: [ntok, H, dv] in z_dtype; norm_weight: [dv] fp32; rms_eps: as gdn_output_gate's eps;
+ *   initial_state, final_state, cu_seqlens, cu_seqlens_host, num_seqs: as gdn_chunk_prefill;
+ *   o: [ntok, H, dv] output in o_dtype.
+ *   q, k, v ([ntok, H, d] bf16), y ([ntok, H, dv] bf16): optional exports of the
+ *       intermediates (a backward pass needs q, k, v, g, beta); NULL keeps each in the
+ *       workspace. g, beta ([ntok, H] fp32): exported together, or both NULL (not written).
+ *   workspace: at least gdn_fused_prefill_workspace_size(...) bytes, not shared by
+ *       concurrent calls.
+ * dk must be 128 (the bf16 matrix-core path: q, k, v are bf16 between the kernels).
+ * Results equal gdn_preprocess -> gdn_chunk_prefill -> gdn_output_gate with bf16 q, k, v, y.
+ */
+int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtype,
+                      const float* wq, const float* wk, const float* wv, int conv_k,
+                      const float* a_raw, const float* b_raw, const float* A_log,
+                      const float* dt_bias, float l2_eps, const void* z, int z_dtype,
+                      const float* norm_weight, float rms_eps, const float* initial_state,
+                      float* final_state, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
+                      int dv, void* o, int o_dtype, void* q, void* k, void* v, float* g,
+                      float* beta, void* y, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * gdn_fused_decode - one decode step of the token mixer in one kernel: eqs. (6)-(10) on this
+ * step's projected inputs with each sequence's carried conv history, eqs. (1)-(4) for one
+ * token (state in place), and eq. (11) without W_o (section 2.1.1 of the notes; the conv is
+ * causal and depthwise, design summary "设计 LLM 架构", section "Token 混合：GDN 加 QSA").
+ *
+ *   xq, xk: [N, H, dk], xv: [N, H, dv] in x_dtype;
+ *   wq, wk, wv: [H*d, 4] fp32 conv taps; conv_k must be 4;
+ *   conv_state: [N, 3, H*(2*dk+dv)] in x_dtype, in/out: the layout of
+ *       gdn_preprocess_stateful's conv states (row 2 the newest input), shifted by this
+ *       step's input in place;
+ *   a_raw, b_raw: [N, H] fp32; A_log, dt_bias: [H] fp32; l2_eps as gdn_preprocess;
+ *   state: [N, H, dk, dv] fp32, in/out;
+ *   z: [N, H, dv] in x_dtype; norm_weight: [dv] fp32; rms_eps as gdn_output_gate's eps;
+ *   o: [N, H, dv] output in o_dtype; y: optional [N, H, dv] in o_dtype (before the gate).
+ * q and k stay fp32 inside the kernel (no bf16 rounding between the steps).
+ */
+int gdn_fused_decode(const void* xq, const void* xk, const void* xv, int x_dtype,
+                     const float* wq, const float* wk, const float* wv, int conv_k,
+                     void* conv_state, const float* a_raw, const float* b_raw,
+                     const float* A_log, const float* dt_bias, float l2_eps, float* state,
+                     const void* z, const float* norm_weight, float rms_eps, int N, int H,
+                     int dk, int dv, void* o, int o_dtype, void* y, void* stream);
 
 #ifdef __cplusplus
 }

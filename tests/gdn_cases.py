@@ -184,6 +184,27 @@ def gpu_run(inp: dict, y_dtype="bf16", state_out=True) -> dict:
     return res
 
 
+def gpu_run_fused(inp: dict) -> dict:
+    """The fused token mixer (gdn_fused_prefill) on the whole workload, with its intermediates
+    exported. Returns device tensors under the keys gpu_run uses (y is bf16)."""
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    sh = inp["shape"]
+    cu = inp["cu_seqlens"]
+    cu_d = None if sh.equal_lengths else dev(cu)
+    cu_h = None if sh.equal_lengths else cu
+    f32 = lambda a: dev(np.asarray(a, dtype=np.float32))  # noqa: E731
+    S0 = f32(inp["S0"]) if inp.get("S0") is not None else None
+    o, ST, ex = gdn.gdn_fused_prefill(
+        dev(inp["xq"], True), dev(inp["xk"], True), dev(inp["xv"], True), f32(inp["wq"]),
+        f32(inp["wk"]), f32(inp["wv"]), f32(inp["a_raw"]), f32(inp["b_raw"]), f32(inp["A_log"]),
+        f32(inp["dt_bias"]), dev(inp["z"], True), f32(inp["norm_weight"]), H=sh.H,
+        initial_state=S0, cu_seqlens=cu_d, cu_seqlens_host=cu_h, num_seqs=sh.num_seqs,
+        l2_eps=L2_EPS, rms_eps=RMS_EPS, o_dtype=torch.bfloat16, export=True)
+    torch.cuda.synchronize()
+    return dict(o=o, ST=ST, **ex)
+
+
 def gpu_slice(t, tok, heads):
     """Token/head subset of a device [ntok, H, ...] tensor, as float64 numpy."""
     import torch

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
     assert {"gdn_preprocess", "gdn_chunk_prefill", "gdn_decode_step", "gdn_output_gate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 2
+    assert L.gdn_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -148,3 +148,39 @@ def test_kda_validation(L):
     assert call(dk=32) == 2
     assert call(wsb=need - 1) == 6
     assert call(yt=9) == 3
+
+
+def test_fused_validation(L):
+    n = None
+    F = FAKE
+    need = L.gdn_fused_prefill_workspace_size(128, 1, 2, 128, 128)
+    assert need > 0
+    assert L.gdn_fused_prefill_workspace_size(128, 1, 2, 64, 128) == 0   # dk must be 128
+
+    def prefill(**kw):
+        a = dict(xq=F, xk=F, xv=F, xt=1, wq=F, wk=F, wv=F, ck=4, ar=F, br=F, al=F, dt=F, l2=1e-6,
+                 z=F, zt=1, nw=F, re=1e-6, s0=n, st=n, cu=n, cuh=n, ns=1, nt=128, H=2, dk=128,
+                 dv=128, o=F, ot=1, q=n, k=n, v=n, g=n, b=n, y=n, ws=F, wsb=need)
+        a.update(kw)
+        return L.gdn_fused_prefill(*a.values(), None)
+    assert prefill(xq=None) == 1
+    assert prefill(dk=64) == 2
+    assert prefill(ck=3) == 2
+    assert prefill(zt=4) == 3
+    assert prefill(wsb=need - 1) == 6
+    assert prefill(ws=None) == 6
+    assert prefill(g=F) == 1                  # g without beta
+    assert prefill(q=MIS) == 5
+    assert prefill(ns=3) == 2                 # 128 tokens do not split into 3 equal sequences
+
+    def decode(**kw):
+        a = dict(xq=F, xk=F, xv=F, xt=1, wq=F, wk=F, wv=F, ck=4, cs=F, ar=F, br=F, al=F, dt=F,
+                 l2=1e-6, state=F, z=F, nw=F, re=1e-6, N=4, H=2, dk=128, dv=128, o=F, ot=1, y=n)
+        a.update(kw)
+        return L.gdn_fused_decode(*a.values(), None)
+    assert decode(cs=None) == 1
+    assert decode(dv=96) == 2
+    assert decode(ck=2) == 2
+    assert decode(ot=2) == 3
+    assert decode(y=MIS) == 5
+    assert decode(re=-1.0) == 2

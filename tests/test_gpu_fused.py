@@ -1,0 +1,142 @@
+"""GPU parity of the fused entry points against the fp64 oracle:
+  * gdn_fused_prefill (conv, SiLU, L2Norm and gates inside the per-chunk kernel, then the scan
+    and the output gate): against the oracle's eqs. (6)-(11), and element for element against
+    the separate-kernel pipeline gdn_preprocess -> gdn_chunk_prefill -> gdn_output_gate;
+  * gdn_fused_decode (one kernel per decode step from the projected streams, conv history and
+    state carried in place): against the oracle over each sequence's whole token stream.
+Sources: reading notes "Qwen3.8-Next 架构设计：评测、效率与训练稳定性", section 2.1.1,
+eqs. (1)-(11); the design summary "设计 LLM 架构" (causal depthwise short conv)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_recurrence_chunked_amd import inputs as gi
+import gdn_cases as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _compare_to_oracle(inp, res, sub):
+    tok, heads, seqs, cu, H = sub["tok"], sub["heads"], sub["seqs"], sub["cu"], sub["H"]
+    ref = C.oracle_run(sub)
+    ref_st = C.oracle_run(sub, storage_bf16=True, y_bf16=True)
+    rep = {}
+    for key in ("q", "k", "v"):
+        rep[key] = C.assert_close(key, C.gpu_slice(res[key], tok, heads), ref[key], True,
+                                  stored_bf16=True, cu=cu, H=H)
+    for key in ("g", "beta"):
+        got = C.gpu_slice(res[key], tok, heads)
+        err = np.abs(got - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30)
+        assert err < 1e-5, f"{key}: {err}"
+    rep["y"] = C.assert_close("y", C.gpu_slice(res["y"], tok, heads), ref["y"], True,
+                              stored_bf16=True, cu=cu, H=H)
+    rep["ST"] = C.assert_close("ST", C.gpu_state_slice(res["ST"], seqs, heads), ref["ST"], True,
+                               state=True)
+    rep["o"] = C.assert_close("o", C.gpu_slice(res["o"], tok, heads), ref["o"], True,
+                              stored_bf16=True, cu=cu, H=H, ref_elem=ref_st["o"],
+                              inherits_bf16_input=True)
+    print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in rep.items()}, flush=True)
+
+
+def _equal_to_pipeline(fused, sep):
+    """The fused path computes q, k, v and the gates with the preprocess kernel's arithmetic, so
+    every output equals the separate kernels' bit for bit."""
+    import torch
+    for key in ("q", "k", "v", "g", "beta", "y", "o", "ST"):
+        a, b = fused[key], sep[key]
+        assert a.dtype == b.dtype and a.shape == b.shape, key
+        if not torch.equal(a, b):
+            d = (a.float() - b.float()).abs().max().item()
+            raise AssertionError(f"{key}: fused differs from the separate kernels (max |diff| {d:.3e})")
+
+
+PREFILL_CASES = [
+    (1, dict(B=2, H=3, T=200)),                                      # one head per workgroup
+    (1, dict(B=2, H=4, T=300)),                                      # four heads per workgroup
+    (1, dict(B=2, H=2, T=150, dv=64)),                               # two heads, dv = 64
+    (4, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130])),      # empty/short seqs, S0
+    (4, dict(H=4, nseq=5, lmax=600)),
+]
+
+
+@pytest.mark.parametrize("cfg,ov", PREFILL_CASES, ids=[f"cfg{c}-{o}" for c, o in PREFILL_CASES])
+def test_fused_prefill(gpu, cfg, ov):
+    _announce(f"fused prefill cfg={cfg} {ov}")
+    inp = gi.make_inputs(cfg, seed=1, **ov)
+    fused = C.gpu_run_fused(inp)
+    _compare_to_oracle(inp, fused, C.subset(inp))
+    _equal_to_pipeline(fused, C.gpu_run(inp, y_dtype="bf16"))
+
+
+@pytest.mark.slow
+def test_fused_prefill_config1_full(gpu):
+    _announce("fused prefill at B=4 H=16 T=4096 d=128 (bf16), sampled slices")
+    inp = gi.make_inputs(1, seed=0)
+    fused = C.gpu_run_fused(inp)
+    _compare_to_oracle(inp, fused, C.subset(inp, seqs=[0, 3], heads=[0, 9, 15]))
+    _equal_to_pipeline(fused, C.gpu_run(inp, y_dtype="bf16"))
+
+
+# ----------------------------------------------------------------------------- decode
+DECODE_CASES = [
+    # (N, H, dk, dv, x bf16, o bf16, steps)
+    (8, 2, 128, 128, True, True, 5),
+    (5, 3, 64, 128, False, False, 4),
+    (4, 2, 128, 64, True, False, 3),
+    (3, 1, 64, 64, False, True, 6),
+]
+
+
+@pytest.mark.parametrize("N,H,dk,dv,xbf,obf,steps", DECODE_CASES,
+                         ids=[f"N{c[0]}-H{c[1]}-dk{c[2]}-dv{c[3]}-x{'bf' if c[4] else 'f32'}-o{'bf' if c[5] else 'f32'}"
+                              for c in DECODE_CASES])
+def test_fused_decode_steps(gpu, N, H, dk, dv, xbf, obf, steps):
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    _announce(f"fused decode N={N} H={H} dk={dk} dv={dv} x_bf16={xbf} o_bf16={obf} steps={steps}")
+    d = gi.decode_layer_draws(11, steps, N, H, dk, dv, bf16=xbf)
+    xd = lambda a: C.dev(a, xbf)                                               # noqa: E731
+    f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))            # noqa: E731
+    w = [f32(d[x]) for x in ("wq", "wk", "wv")]
+    conv_state = xd(d["conv_state"])
+    state = f32(d["state"])
+    os_, ys = [], []
+    for s in range(steps):
+        o, y = gdn.gdn_fused_decode(xd(d["xq"][s]), xd(d["xk"][s]), xd(d["xv"][s]), *w, conv_state,
+                                    f32(d["a_raw"][s]), f32(d["b_raw"][s]), f32(d["A_log"]),
+                                    f32(d["dt_bias"]), state, xd(d["z"][s]),
+                                    f32(d["norm_weight"]), l2_eps=C.L2_EPS, rms_eps=C.RMS_EPS,
+                                    o_dtype=torch.bfloat16 if obf else torch.float32, want_y=True)
+        os_.append(C.host(o))
+        ys.append(C.host(y))
+    torch.cuda.synchronize()
+
+    # oracle: sequence n is its `steps` tokens in order, starting from the carried history
+    perm = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1).reshape(N * steps, *a.shape[2:]))  # noqa
+    f64 = lambda a: gi.as_f64(a, xbf)                                          # noqa: E731
+    cu = np.arange(0, N * steps + 1, steps).astype(np.int32)
+    q, k, v, hist = oracle.preprocess_stateful(perm(f64(d["xq"])), perm(f64(d["xk"])),
+                                               perm(f64(d["xv"])), d["wq"], d["wk"], d["wv"], cu,
+                                               H, conv_state_in=f64(d["conv_state"]),
+                                               l2_eps=C.L2_EPS)
+    _, al, be = oracle.gates(perm(d["a_raw"].astype(np.float64)), perm(d["b_raw"].astype(np.float64)),
+                             d["A_log"].astype(np.float64), d["dt_bias"].astype(np.float64))
+    y_ref, S_ref = oracle.recurrence(q, k, v, al, be, d["state"].astype(np.float64), cu)
+    o_ref = oracle.output_gate(y_ref, perm(f64(d["z"])), d["norm_weight"].astype(np.float64),
+                               C.RMS_EPS)
+    gather = lambda L: np.stack(L, axis=1).reshape(N * steps, H, dv)           # noqa: E731
+    bf_path = xbf or obf
+    rep = dict(
+        y=C.assert_close("y", gather(ys), y_ref, bf_path, stored_bf16=obf, cu=cu, H=H),
+        o=C.assert_close("o", gather(os_), o_ref, bf_path, stored_bf16=obf, cu=cu, H=H),
+        S=C.assert_close("S", C.host(state), S_ref, bf_path, state=True))
+    print("  max slice rel L2:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
+    # the carried history is raw input moved, bit for bit
+    assert np.array_equal(C.host(conv_state), hist)
