@@ -35,9 +35,14 @@ namespace {
 constexpr int kC = 64;
 constexpr int kBT = 1024;         // threads per workgroup: 16 waves hide the LDS latency of the
                                   // small products every chunk step is made of
-constexpr int kSL = 16;           // dv columns per scan workgroup
 constexpr int kFinT = 512;        // threads of the per-chunk-head kernels (one workgroup per CU fits their LDS)
-constexpr int kP = kSL + 1;       // padded row of a [64][16] tile
+constexpr int kStSL = 32;         // dv columns per forward-sweep workgroup
+
+// dv columns per reverse-sweep workgroup: 32 with bf16 inputs (K and Q then sit in LDS as bf16,
+// exactly), 16 with fp32 inputs (their fp32 rows leave no LDS room for wider slices). Fewer,
+// wider slices mean fewer shares of the column-summed terms to write and add up.
+template <typename Tin> constexpr int scan_cols() { return sizeof(Tin) == 2 ? 32 : 16; }
+constexpr int kMinSL = 16;
 
 struct BwdLayout {
     size_t G, Ak, P, T, Sc, part, total;
@@ -45,14 +50,18 @@ struct BwdLayout {
 };
 
 // per-(chunk, head, slice) share: dq part, dk part [64][dk], dA, dP [64][64], and 4 token
-// vectors: sum_j dR (V - gamma KS), dgamma, dw, and dgamma_C (one value, in slot 0)
+// vectors: sum_j dR (V - gamma KS), dgamma, dw, and dgamma_C (one value, in slot 0). The four
+// matrices are stored in the 16x16 tile layout of the products that write and read them:
+// tile t (row tile rt, column tile ct, t = rt * (columns / 16) + ct), then lane l, then the
+// lane's 4 accumulator elements (rows 16 rt + 4 (l / 16) + i, column 16 ct + l % 16), so a lane
+// moves one 16-byte piece per tile.
 __host__ __device__ inline size_t part_floats(int dk) { return (size_t)2 * kC * dk + 2 * kC * kC + 4 * kC; }
 
 BwdLayout bwd_layout(int ntok, int num_seqs, int H, int dk, int dv) {
     BwdLayout L;
     L.max_chunks = (ntok + kC - 1) / kC + num_seqs;
     const size_t ch = (size_t)L.max_chunks * H;
-    const int slices = dv / kSL;
+    const int slices = dv / kMinSL;   // room for the narrowest slicing
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -75,6 +84,7 @@ struct BwdArgs {
     const float *g, *beta, *S0, *dST;
     const int32_t* cu;
     int num_seqs, ntok, H, dk, dv;
+    int slices;                   // reverse-sweep slices of dv (dv / scan_cols<Tin>())
     float *dq, *dk_, *dv_, *dg, *dbeta, *dS0;
     float *G, *Ak, *P, *T, *Sc, *part;
 };
@@ -129,6 +139,16 @@ __device__ __forceinline__ void load_rows(const void* x, int t0, int n, int H, i
     for (int e = threadIdx.x; e < kC * DK; e += NT) {
         const int r = e / DK, d = e % DK;
         dst[r][d] = r < n ? ld<Tin>(x, ((size_t)(t0 + r) * H + h) * DK + d) : 0.f;
+    }
+}
+
+// the same rows kept in their input type (bf16 bits are copied, not widened), row stride RS
+template <int DK, int RS, typename Tin, int NT>
+__device__ __forceinline__ void load_rows_raw(const void* x, int t0, int n, int H, int h, Tin (*dst)[RS]) {
+    const Tin* xp = static_cast<const Tin*>(x);
+    for (int e = threadIdx.x; e < kC * DK; e += NT) {
+        const int r = e / DK, d = e % DK;
+        dst[r][d] = r < n ? xp[((size_t)(t0 + r) * H + h) * DK + d] : Tin(0);
     }
 }
 
@@ -215,38 +235,39 @@ __global__ void __launch_bounds__(kFinT) bwd_ap_kernel(BwdArgs a) {
 // The three products of a chunk step run on the fp32 matrix core, one 16x16 output tile per wave.
 template <int DK, typename Tin>
 __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
+    constexpr int SL = kStSL, CT = SL / 16, PR = SL + 1;
     __shared__ float Ks[kC][DK + 1];
-    __shared__ float S[DK][kSL];
+    __shared__ float S[DK][SL];
     __shared__ float T[kC][kC + 1];
-    __shared__ float R[kC][kP], W[kC][kP];
+    __shared__ float R[kC][PR], W[kC][PR];
     __shared__ float gam[kC], w[kC], Bt[kC];
-    static_assert(DK / 16 <= kBT / kWave, "one state tile per wave");
-    const int slices = a.dv / kSL;
+    static_assert((DK / 16) * CT <= kBT / kWave, "one state tile per wave");
+    const int slices = a.dv / SL;
     const int slice = blockIdx.x % slices;
     const int h = (blockIdx.x / slices) % a.H;
     const int sq = blockIdx.x / (slices * a.H);
-    const int j0 = slice * kSL, tid = threadIdx.x, H = a.H, dv = a.dv;
+    const int j0 = slice * SL, tid = threadIdx.x, H = a.H, dv = a.dv;
     const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
     int lo, hi, cbase;
     seq_info(a, sq, lo, hi, cbase);
     const size_t st_off = ((size_t)sq * H + h) * DK * dv;
-    for (int e = tid; e < DK * kSL; e += kBT) {
-        const int d = e / kSL, j = e % kSL;
+    for (int e = tid; e < DK * SL; e += kBT) {
+        const int d = e / SL, j = e % SL;
         S[d][j] = a.S0 ? a.S0[st_off + (size_t)d * dv + j0 + j] : 0.f;
     }
     for (int t0 = lo, c = cbase; t0 < hi; t0 += kC, ++c) {
         const int n = min(kC, hi - t0);
         const size_t ch = (size_t)c * H + h;
         __syncthreads();
-        for (int e = tid; e < DK * kSL; e += kBT) {   // the state entering this chunk
-            const int d = e / kSL, j = e % kSL;
+        for (int e = tid; e < DK * SL; e += kBT) {   // the state entering this chunk
+            const int d = e / SL, j = e % SL;
             a.Sc[ch * DK * dv + (size_t)d * dv + j0 + j] = S[d][j];
         }
         load_rows<DK, Tin>(a.k, t0, n, H, h, Ks);
         for (int e = tid; e < kC * kC; e += kBT) T[e / kC][e % kC] = a.T[ch * kC * kC + e];
-        for (int e = tid; e < kC * kSL; e += kBT) {   // V, zero past n
-            const int r = e / kSL, j = e % kSL;
+        for (int e = tid; e < kC * SL; e += kBT) {   // V, zero past n
+            const int r = e / SL, j = e % SL;
             R[r][j] = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
         }
         if (tid < kC) {
@@ -256,69 +277,77 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
             Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
         }
         __syncthreads();
-        if (wave < kC / 16) {   // R = beta o (V - gamma o K S)
-            const floatx4 ks = mma_f32_tile(&Ks[wave * 16][0], DK + 1, 1, &S[0][0], kSL, 1, DK, zero);
+        if (wave < 4 * CT) {   // R = beta o (V - gamma o K S)
+            const int rt = wave % 4, ct = wave / 4;
+            const floatx4 ks = mma_f32_tile(&Ks[rt * 16][0], DK + 1, 1, &S[0][ct * 16], SL, 1, DK, zero);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = wave * 16 + 4 * lg + i;
-                R[r][lc] = Bt[r] * (R[r][lc] - gam[r] * ks[i]);
+                const int r = rt * 16 + 4 * lg + i, j = ct * 16 + lc;
+                R[r][j] = Bt[r] * (R[r][j] - gam[r] * ks[i]);
             }
         }
         __syncthreads();
-        if (wave < kC / 16) {   // W = w o (T R); T is lower triangular
-            const floatx4 u = mma_f32_tile(&T[wave * 16][0], kC + 1, 1, &R[0][0], kP, 1, kC, zero);
+        if (wave < 4 * CT) {   // W = w o (T R); T is lower triangular
+            const int rt = wave % 4, ct = wave / 4;
+            const floatx4 u = mma_f32_tile(&T[rt * 16][0], kC + 1, 1, &R[0][ct * 16], PR, 1, kC, zero);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = wave * 16 + 4 * lg + i;
-                W[r][lc] = w[r] * u[i];
+                const int r = rt * 16 + 4 * lg + i;
+                W[r][ct * 16 + lc] = w[r] * u[i];
             }
         }
         __syncthreads();
         floatx4 sn = zero;   // S' = gamma_C S + K^T W (rows of K past n are zero)
-        if (wave < DK / 16) {
+        const int dt = wave % (DK / 16), ct = wave / (DK / 16);
+        if (wave < (DK / 16) * CT) {
             const float gC = gam[n - 1];
-            sn = mma_f32_tile(&Ks[0][wave * 16], 1, DK + 1, &W[0][0], kP, 1, kC, zero);
+            sn = mma_f32_tile(&Ks[0][dt * 16], 1, DK + 1, &W[0][ct * 16], PR, 1, kC, zero);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sn[i] += gC * S[wave * 16 + 4 * lg + i][lc];
+            for (int i = 0; i < 4; ++i) sn[i] += gC * S[dt * 16 + 4 * lg + i][ct * 16 + lc];
         }
         __syncthreads();
-        if (wave < DK / 16) {
+        if (wave < (DK / 16) * CT) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[wave * 16 + 4 * lg + i][lc] = sn[i];
+            for (int i = 0; i < 4; ++i) S[dt * 16 + 4 * lg + i][ct * 16 + lc] = sn[i];
         }
     }
 }
 
 // ------------------------------------------------------------------ scan: reverse sweep
 // Every product of a chunk step runs on the fp32 matrix core, one 16x16 output tile per wave at a
-// time (16 waves), with its operands read from LDS as strided views.
+// time (16 waves), with its operands read from LDS as strided views. SL dv columns per
+// workgroup (scan_cols); K and Q rows stay in the input type in LDS.
 constexpr int kScanT = 1024;
-template <int DK, typename Tin, typename Tdy>
+template <int DK, int SL, typename Tin, typename Tdy>
 __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
-    __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1];
-    __shared__ float S[DK][kSL], dS[DK][kSL];        // state entering the chunk; gradient after
+    constexpr int CT = SL / 16;                    // column tiles of a [64][SL] slice
+    constexpr int PR = SL + 1;                     // padded row of a [64][SL] tile
+    constexpr int KR = DK + (sizeof(Tin) == 2 ? 2 : 1);
+    __shared__ Tin Ks[kC][KR], Qs[kC][KR];
+    __shared__ float S[DK][SL], dS[DK][SL];        // state entering the chunk; gradient after
     __shared__ float T[kC][kC + 1], P[kC][kC + 1];
-    // [64][16] tiles: Vr = V - gamma o KS, dY, KS, QS, U, KdS = K dS', dU, dR; late in the step
-    // QS and KS are reused for gamma o dY and (beta gamma) o dR, and dR holds R = beta o Vr
-    // until dR itself is formed
-    __shared__ float Vr[kC][kP], dY[kC][kP], KS[kC][kP], QS[kC][kP];
-    __shared__ float U[kC][kP], KdS[kC][kP], dU[kC][kP], dR[kC][kP];
-    __shared__ float gam[kC], w[kC], Bt[kC];
+    // [64][SL] tiles: dY, KS, QS, U, KdS = K dS', dU, dR; late in the step QS and KS are reused
+    // for gamma o dY and (beta gamma) o dR, and dR holds R = beta o (V - gamma o KS) until dR
+    // itself is formed
+    __shared__ float dY[kC][PR], KS[kC][PR], QS[kC][PR];
+    __shared__ float U[kC][PR], KdS[kC][PR], dU[kC][PR], dR[kC][PR];
+    __shared__ float gam[kC], w[kC], Bt[kC], dRV[kC];
     __shared__ float red[kScanT / kWave];
 
-    const int slices = a.dv / kSL;
+    const int slices = a.dv / SL;
     const int slice = blockIdx.x % slices;
     const int h = (blockIdx.x / slices) % a.H;
     const int sq = blockIdx.x / (slices * a.H);
-    const int j0 = slice * kSL, tid = threadIdx.x, H = a.H, dv = a.dv;
+    const int j0 = slice * SL, tid = threadIdx.x, H = a.H, dv = a.dv;
     const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
     constexpr int NW = kScanT / kWave;
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
     int lo, hi, cbase;
     seq_info(a, sq, lo, hi, cbase);
     const int nch = (hi - lo + kC - 1) / kC;
     const size_t st_off = ((size_t)sq * H + h) * DK * dv;
-    for (int e = tid; e < DK * kSL; e += kScanT) {
-        const int d = e / kSL, j = e % kSL;
+    for (int e = tid; e < DK * SL; e += kScanT) {
+        const int d = e / SL, j = e % SL;
         dS[d][j] = a.dST ? a.dST[st_off + (size_t)d * dv + j0 + j] : 0.f;
     }
     for (int cc = nch - 1; cc >= 0; --cc) {
@@ -331,17 +360,14 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
         float* pdP = pdA + kC * kC;                // [64][64]
         float* pvec = pdP + kC * kC;               // [4][64]
         __syncthreads();
-        load_rows<DK, Tin, kScanT>(a.k, t0, n, H, h, Ks);
-        load_rows<DK, Tin, kScanT>(a.q, t0, n, H, h, Qs);
-        for (int e = tid; e < kC * kSL; e += kScanT) {
-            const int r = e / kSL, j = e % kSL;
-            const bool ok = r < n;
-            const size_t off = ((size_t)(t0 + r) * H + h) * dv + j0 + j;
-            Vr[r][j] = ok ? ld<Tin>(a.v, off) : 0.f;
-            dY[r][j] = ok ? ld<Tdy>(a.dy, off) : 0.f;
+        load_rows_raw<DK, KR, Tin, kScanT>(a.k, t0, n, H, h, Ks);
+        load_rows_raw<DK, KR, Tin, kScanT>(a.q, t0, n, H, h, Qs);
+        for (int e = tid; e < kC * SL; e += kScanT) {
+            const int r = e / SL, j = e % SL;
+            dY[r][j] = r < n ? ld<Tdy>(a.dy, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
         }
-        for (int e = tid; e < DK * kSL; e += kScanT) {
-            const int d = e / kSL, j = e % kSL;
+        for (int e = tid; e < DK * SL; e += kScanT) {
+            const int d = e / SL, j = e % SL;
             S[d][j] = a.Sc[ch * DK * dv + (size_t)d * dv + j0 + j];
         }
         for (int e = tid; e < kC * kC; e += kScanT) {
@@ -355,19 +381,19 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
             Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
         }
         __syncthreads();
-        // ---- step 1: KS = K S, QS = Q S, KdS = K dS' (12 tiles); <S, dS'>
-        for (int tile = wave; tile < 12; tile += NW) {
-            const int kind = tile >> 2, rt = tile & 3;
-            const float* A = kind == 1 ? &Qs[rt * 16][0] : &Ks[rt * 16][0];
-            const float* B = kind == 2 ? &dS[0][0] : &S[0][0];
-            const floatx4 acc = mma_f32_tile(A, DK + 1, 1, B, kSL, 1, DK, floatx4{0.f, 0.f, 0.f, 0.f});
-            float(*dst)[kP] = kind == 0 ? KS : (kind == 1 ? QS : KdS);
+        // ---- step 1: KS = K S, QS = Q S, KdS = K dS' (3 x 4 x CT tiles); <S, dS'>
+        for (int tile = wave; tile < 12 * CT; tile += NW) {
+            const int kind = tile / (4 * CT), rt = tile % 4, ct = (tile / 4) % CT;
+            const Tin* A = kind == 1 ? &Qs[rt * 16][0] : &Ks[rt * 16][0];
+            const float* B = kind == 2 ? &dS[0][ct * 16] : &S[0][ct * 16];
+            const floatx4 acc = mma_f32_tile(A, KR, 1, B, SL, 1, DK, zero);
+            float(*dst)[PR] = kind == 0 ? KS : (kind == 1 ? QS : KdS);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[rt * 16 + 4 * lg + i][lc] = acc[i];
+            for (int i = 0; i < 4; ++i) dst[rt * 16 + 4 * lg + i][ct * 16 + lc] = acc[i];
         }
         {
             float sdot = 0.f;
-            for (int e = tid; e < DK * kSL; e += kScanT) sdot += S[e / kSL][e % kSL] * dS[e / kSL][e % kSL];
+            for (int e = tid; e < DK * SL; e += kScanT) sdot += S[e / SL][e % SL] * dS[e / SL][e % SL];
             sdot = group_sum<kWave>(sdot);
             if (lane == 0) red[wave] = sdot;
         }
@@ -377,144 +403,148 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
             for (int i = 0; i < NW; ++i) acc += red[i];
             pvec[3 * kC] = acc;
         }
-        for (int e = tid; e < kC * kSL; e += kScanT) {   // Vr = V - gamma KS;  R = beta Vr (in dR)
-            const int r = e / kSL, j = e % kSL;
-            const float vr = Vr[r][j] - gam[r] * KS[r][j];
-            Vr[r][j] = vr;
-            dR[r][j] = Bt[r] * vr;
+        for (int e = tid; e < kC * SL; e += kScanT) {   // R = beta o (V - gamma o KS), in dR
+            const int r = e / SL, j = e % SL;
+            const float vv = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
+            dR[r][j] = Bt[r] * (vv - gam[r] * KS[r][j]);
         }
         __syncthreads();
-        // ---- step 2: U = T R;  dU = w o KdS + P^T dY (8 tiles)
-        for (int tile = wave; tile < 8; tile += NW) {
-            const int rt = tile & 3;
-            if (tile < 4) {
-                const floatx4 acc = mma_f32_tile(&T[rt * 16][0], kC + 1, 1, &dR[0][0], kP, 1, kC,
-                                                 floatx4{0.f, 0.f, 0.f, 0.f});
+        // ---- step 2: U = T R;  dU = w o KdS + P^T dY (2 x 4 x CT tiles)
+        for (int tile = wave; tile < 8 * CT; tile += NW) {
+            const int rt = tile % 4, ct = (tile / 4) % CT;
+            if (tile < 4 * CT) {
+                const floatx4 acc = mma_f32_tile(&T[rt * 16][0], kC + 1, 1, &dR[0][ct * 16], PR, 1,
+                                                 kC, zero);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) U[rt * 16 + 4 * lg + i][lc] = acc[i];
+                for (int i = 0; i < 4; ++i) U[rt * 16 + 4 * lg + i][ct * 16 + lc] = acc[i];
             } else {
-                const floatx4 acc = mma_f32_tile(&P[0][rt * 16], 1, kC + 1, &dY[0][0], kP, 1, kC,
-                                                 floatx4{0.f, 0.f, 0.f, 0.f});
+                const floatx4 acc = mma_f32_tile(&P[0][rt * 16], 1, kC + 1, &dY[0][ct * 16], PR, 1,
+                                                 kC, zero);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = rt * 16 + 4 * lg + i;
-                    dU[r][lc] = w[r] * KdS[r][lc] + acc[i];
+                    const int r = rt * 16 + 4 * lg + i, j = ct * 16 + lc;
+                    dU[r][j] = w[r] * KdS[r][j] + acc[i];
                 }
             }
         }
         __syncthreads();
-        // ---- step 3: dR = T^T dU (4 tiles); dq share (gamma o dY) S^T and dP = dY U^T (48 tiles)
-        if (wave < 4) {
-            const int rt = wave;
-            const floatx4 acc = mma_f32_tile(&T[0][rt * 16], 1, kC + 1, &dU[0][0], kP, 1, kC,
-                                             floatx4{0.f, 0.f, 0.f, 0.f});
+        // ---- step 3: dR = T^T dU (4 x CT tiles); dq share (gamma o dY) S^T and dP = dY U^T
+        if (wave < 4 * CT) {
+            const int rt = wave % 4, ct = wave / 4;
+            const floatx4 acc = mma_f32_tile(&T[0][rt * 16], 1, kC + 1, &dU[0][ct * 16], PR, 1, kC,
+                                             zero);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dR[rt * 16 + 4 * lg + i][lc] = acc[i];
+            for (int i = 0; i < 4; ++i) dR[rt * 16 + 4 * lg + i][ct * 16 + lc] = acc[i];
         }
-        {
-            for (int tile = (wave + NW - 4) % NW; tile < 4 * (DK / 16) + 16; tile += NW) {
-                if (tile < 4 * (DK / 16)) {   // dq share tile (rt, dt)
-                    const int rt = tile / (DK / 16), dt = tile % (DK / 16);
-                    const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], kP, 1, &S[dt * 16][0], 1, kSL,
-                                                     kSL, floatx4{0.f, 0.f, 0.f, 0.f});
+        for (int tile = (wave + NW - 4 * CT) % NW; tile < 4 * (DK / 16) + 16; tile += NW) {
+            if (tile < 4 * (DK / 16)) {   // dq share tile (rt, dt)
+                const int rt = tile / (DK / 16), dt = tile % (DK / 16);
+                const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], PR, 1, &S[dt * 16][0], 1, SL, SL,
+                                                 zero);
+                floatx4 o;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = rt * 16 + 4 * lg + i;
-                        pdq[r * DK + dt * 16 + lc] = gam[r] * acc[i];
-                    }
-                } else {                      // dP tile (rt, it), lower with the diagonal
-                    const int t2 = tile - 4 * (DK / 16), rt = t2 >> 2, it = t2 & 3;
-                    const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], kP, 1, &U[it * 16][0], 1, kP,
-                                                     kSL, floatx4{0.f, 0.f, 0.f, 0.f});
+                for (int i = 0; i < 4; ++i) o[i] = gam[rt * 16 + 4 * lg + i] * acc[i];
+                reinterpret_cast<floatx4*>(pdq)[tile * kWave + lane] = o;
+            } else {                      // dP tile (rt, it), lower with the diagonal
+                const int t2 = tile - 4 * (DK / 16), rt = t2 >> 2, it = t2 & 3;
+                const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], PR, 1, &U[it * 16][0], 1, PR, SL,
+                                                 zero);
+                floatx4 o;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = rt * 16 + 4 * lg + i, c = it * 16 + lc;
-                        pdP[r * kC + c] = (c <= r && r < n) ? acc[i] : 0.f;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rt * 16 + 4 * lg + i, c = it * 16 + lc;
+                    o[i] = (c <= r && r < n) ? acc[i] : 0.f;
                 }
+                reinterpret_cast<floatx4*>(pdP)[t2 * kWave + lane] = o;
             }
         }
         __syncthreads();
-        // ---- step 4: per-token sums, dv, dk share and dA (48 tiles)
+        // ---- step 4: dv = beta o dR and, per token, sum_j dR V (the SL lanes of a row are an
+        // aligned lane group); then the other per-token sums, the dk share and dA
+        for (int e = tid; e < kC * SL; e += kScanT) {
+            const int r = e / SL, j = e % SL;
+            const size_t off = ((size_t)(t0 + min(r, n - 1)) * H + h) * dv + j0 + j;
+            const float vv = r < n ? ld<Tin>(a.v, off) : 0.f;
+            const float x = dR[r][j];
+            if (r < n) a.dv_[off] = Bt[r] * x;
+            const float rv = group_sum<SL>(x * vv);
+            if (j == 0) dRV[r] = rv;
+        }
+        __syncthreads();
         if (tid < kC) {
             const int r = tid;
-            float dwr = 0.f, dg1 = 0.f, db = 0.f, dg2 = 0.f;
-#pragma unroll
-            for (int j = 0; j < kSL; ++j) {
+            float dwr = 0.f, dg1 = 0.f, dg2 = 0.f;
+#pragma unroll 8
+            for (int j = 0; j < SL; ++j) {
                 dwr += KdS[r][j] * U[r][j];
                 dg1 += dY[r][j] * QS[r][j];
-                db += dR[r][j] * Vr[r][j];
                 dg2 += dR[r][j] * KS[r][j];
             }
-            pvec[r] = db;
+            pvec[r] = dRV[r] - gam[r] * dg2;   // sum_j dR (V - gamma KS)
             pvec[kC + r] = dg1 - Bt[r] * dg2;
             pvec[2 * kC + r] = dwr;
-        }
-        for (int e = tid; e < kC * kSL; e += kScanT) {
-            const int r = e / kSL, j = e % kSL;
-            if (r < n) a.dv_[((size_t)(t0 + r) * H + h) * dv + j0 + j] = Bt[r] * dR[r][j];
         }
         for (int tile = wave; tile < 4 * (DK / 16) + 16; tile += NW) {
             if (tile < 4 * (DK / 16)) {   // dk share: w o (U dS'^T) - (beta gamma) o (dR S^T)
                 const int rt = tile / (DK / 16), dt = tile % (DK / 16);
-                const floatx4 a1 = mma_f32_tile(&U[rt * 16][0], kP, 1, &dS[dt * 16][0], 1, kSL, kSL,
-                                                floatx4{0.f, 0.f, 0.f, 0.f});
-                const floatx4 a2 = mma_f32_tile(&dR[rt * 16][0], kP, 1, &S[dt * 16][0], 1, kSL, kSL,
-                                                floatx4{0.f, 0.f, 0.f, 0.f});
+                const floatx4 a1 = mma_f32_tile(&U[rt * 16][0], PR, 1, &dS[dt * 16][0], 1, SL, SL, zero);
+                const floatx4 a2 = mma_f32_tile(&dR[rt * 16][0], PR, 1, &S[dt * 16][0], 1, SL, SL, zero);
+                floatx4 o;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rt * 16 + 4 * lg + i;
-                    pdk[r * DK + dt * 16 + lc] = w[r] * a1[i] - Bt[r] * gam[r] * a2[i];
+                    o[i] = w[r] * a1[i] - Bt[r] * gam[r] * a2[i];
                 }
+                reinterpret_cast<floatx4*>(pdk)[tile * kWave + lane] = o;
             } else {                      // dA = -(dR U^T), strictly lower
                 const int t2 = tile - 4 * (DK / 16), rt = t2 >> 2, it = t2 & 3;
-                const floatx4 acc = mma_f32_tile(&dR[rt * 16][0], kP, 1, &U[it * 16][0], 1, kP, kSL,
-                                                 floatx4{0.f, 0.f, 0.f, 0.f});
+                const floatx4 acc = mma_f32_tile(&dR[rt * 16][0], PR, 1, &U[it * 16][0], 1, PR, SL, zero);
+                floatx4 o;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rt * 16 + 4 * lg + i, c = it * 16 + lc;
-                    pdA[r * kC + c] = (c < r && r < n) ? -acc[i] : 0.f;
+                    o[i] = (c < r && r < n) ? -acc[i] : 0.f;
                 }
+                reinterpret_cast<floatx4*>(pdA)[t2 * kWave + lane] = o;
             }
         }
         __syncthreads();
         // ---- step 5: dS = gamma_C dS' + Q^T (gamma o dY) - K^T ((beta gamma) o dR)
-        for (int e = tid; e < kC * kSL; e += kScanT) {   // scaled copies into QS and KS
-            const int r = e / kSL, j = e % kSL;
+        for (int e = tid; e < kC * SL; e += kScanT) {   // scaled copies into QS and KS
+            const int r = e / SL, j = e % SL;
             QS[r][j] = gam[r] * dY[r][j];
             KS[r][j] = Bt[r] * gam[r] * dR[r][j];
         }
         __syncthreads();
-        static_assert(DK / 16 <= 2 * NW, "dS tiles per wave");
-        floatx4 dsn[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        constexpr int NT5 = (DK / 16) * CT;        // state tiles
+        static_assert(NT5 <= 2 * NW, "dS tiles per wave");
+        floatx4 dsn[2] = {zero, zero};
         const float gC = gam[n - 1];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int dt = wave + u * NW;
-            if (dt < DK / 16) {
-                const floatx4 a1 = mma_f32_tile(&Qs[0][dt * 16], 1, DK + 1, &QS[0][0], kP, 1, kC,
-                                                floatx4{0.f, 0.f, 0.f, 0.f});
-                const floatx4 a2 = mma_f32_tile(&Ks[0][dt * 16], 1, DK + 1, &KS[0][0], kP, 1, kC,
-                                                floatx4{0.f, 0.f, 0.f, 0.f});
+            const int tile = wave + u * NW, dt = tile % (DK / 16), ct = tile / (DK / 16);
+            if (tile < NT5) {
+                const floatx4 a1 = mma_f32_tile(&Qs[0][dt * 16], 1, KR, &QS[0][ct * 16], PR, 1, kC, zero);
+                const floatx4 a2 = mma_f32_tile(&Ks[0][dt * 16], 1, KR, &KS[0][ct * 16], PR, 1, kC, zero);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dsn[u][i] = gC * dS[dt * 16 + 4 * lg + i][lc] + a1[i] - a2[i];
+                    dsn[u][i] = gC * dS[dt * 16 + 4 * lg + i][ct * 16 + lc] + a1[i] - a2[i];
             }
         }
         __syncthreads();   // every read of dS' is done
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int dt = wave + u * NW;
-            if (dt < DK / 16) {
+            const int tile = wave + u * NW, dt = tile % (DK / 16), ct = tile / (DK / 16);
+            if (tile < NT5) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dS[dt * 16 + 4 * lg + i][lc] = dsn[u][i];
+                for (int i = 0; i < 4; ++i) dS[dt * 16 + 4 * lg + i][ct * 16 + lc] = dsn[u][i];
             }
         }
     }
     __syncthreads();
     if (a.dS0) {
-        for (int e = tid; e < DK * kSL; e += kScanT) {
-            const int d = e / kSL, j = e % kSL;
+        for (int e = tid; e < DK * SL; e += kScanT) {
+            const int d = e / SL, j = e % SL;
             a.dS0[st_off + (size_t)d * dv + j0 + j] = dS[d][j];
         }
     }
@@ -532,7 +562,7 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int t0, n;
     if (!chunk_info(a, c, t0, n)) return;
-    const int H = a.H, slices = a.dv / kSL;
+    const int H = a.H, slices = a.slices;
     const size_t ch = (size_t)c * H + h;
     load_rows<DK, Tin, kFinT>(a.k, t0, n, H, h, Ks);
     load_rows<DK, Tin, kFinT>(a.q, t0, n, H, h, Qs);
@@ -559,22 +589,27 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
     __syncthreads();
     // dA, dP summed over slices. With A = beta o Ak (Ak = e^{D} o KK^T) and P = e^{D} o QK^T:
     // dKK = beta o dA o e^{D}, dQK = dP o e^{D}, dbeta += rowsum(dA o Ak),
-    // dD = beta o dA o Ak + dP o P
-    for (int e = tid; e < kC * kC; e += kFinT) {
-        const int r = e / kC, i = e % kC;
-        float da = 0.f, dp = 0.f;
-#pragma unroll 2
+    // dD = beta o dA o Ak + dP o P. The shares are in tile layout: one 16-byte piece per lane.
+    for (int idx = tid; idx < 16 * kWave; idx += kFinT) {
+        const int t2 = idx / kWave, l = idx % kWave, rt = t2 >> 2, it = t2 & 3;
+        floatx4 da = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < slices; ++s) {
-            const float* pp = a.part + (ch * slices + s) * part_floats(DK) + 2 * kC * DK;
-            da += pp[e];
-            dp += pp[kC * kC + e];
+            const floatx4* pp = reinterpret_cast<const floatx4*>(
+                a.part + (ch * slices + s) * part_floats(DK) + 2 * kC * DK);
+            da += pp[idx];
+            dp += pp[kC * kC / 4 + idx];
         }
-        const float ak = a.Ak[ch * kC * kC + e], pv = a.P[ch * kC * kC + e];
-        const float dec = (i <= r && r < n) ? expf(G[r] - G[i]) : 0.f;
-        dKK[r][i] = i < r ? Bt[r] * da * dec : 0.f;
-        dQK[r][i] = dp * dec;
-        dDr[r][i] = Bt[r] * da * ak + dp * pv;
-        dAk[r][i] = da * ak;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = rt * 16 + 4 * (l >> 4) + u, i = it * 16 + (l & 15);
+            const size_t e = (size_t)r * kC + i;
+            const float ak = a.Ak[ch * kC * kC + e], pv = a.P[ch * kC * kC + e];
+            const float dec = (i <= r && r < n) ? expf(G[r] - G[i]) : 0.f;
+            dKK[r][i] = i < r ? Bt[r] * da[u] * dec : 0.f;
+            dQK[r][i] = dp[u] * dec;
+            dDr[r][i] = Bt[r] * da[u] * ak + dp[u] * pv;
+            dAk[r][i] = da[u] * ak;
+        }
     }
     __syncthreads();
     if (tid < kC) {
@@ -611,23 +646,23 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int tile = wave; tile < (kC / 16) * (DK / 16); tile += kFinT / kWave) {
         const int rt = tile / (DK / 16), dt = tile % (DK / 16);
-        const floatx4 q1 = mma_f32_tile(&dQK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, zero);
-        floatx4 k1 = mma_f32_tile(&dKK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, zero);
+        floatx4 q0 = zero, k0 = zero;   // the slices' shares of this tile (tile layout)
+        for (int s = 0; s < slices; ++s) {
+            const floatx4* pp = reinterpret_cast<const floatx4*>(a.part + (ch * slices + s) * part_floats(DK));
+            q0 += pp[tile * kWave + lane];
+            k0 += pp[kC * DK / 4 + tile * kWave + lane];
+        }
+        const floatx4 q1 = mma_f32_tile(&dQK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, q0);
+        floatx4 k1 = mma_f32_tile(&dKK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, k0);
         k1 = mma_f32_tile(&dKK[0][rt * 16], 1, kC + 1, &Ks[0][dt * 16], DK + 1, 1, kC, k1);
         k1 = mma_f32_tile(&dQK[0][rt * 16], 1, kC + 1, &Qs[0][dt * 16], DK + 1, 1, kC, k1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rt * 16 + 4 * lg + i, d = dt * 16 + lc;
             if (r >= n) continue;
-            float dq = q1[i], dk = k1[i];
-            for (int s = 0; s < slices; ++s) {
-                const float* pp = a.part + (ch * slices + s) * part_floats(DK) + r * DK + d;
-                dq += pp[0];
-                dk += pp[kC * DK];
-            }
             const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
-            a.dq[off] = dq;
-            a.dk_[off] = dk;
+            a.dq[off] = q1[i];
+            a.dk_[off] = k1[i];
         }
     }
 }
@@ -654,7 +689,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
     a.Sc = reinterpret_cast<float*>(ws + L.Sc);
     a.part = reinterpret_cast<float*>(ws + L.part);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((c.ntok / c.num_seqs + kC - 1) / kC);
-    const int seq_blocks = c.num_seqs * c.H * (c.dv / kSL);
+    const int seq_blocks = c.num_seqs * c.H;
     if (nchunks == 0 || seq_blocks == 0) {
         // no tokens: dS0 = dS_T
         if (c.dS0) {
@@ -666,9 +701,13 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
     }
 #define GDN_BWD(DK, TI, TD)                                                                     \
     do {                                                                                        \
+        constexpr int SL = scan_cols<TI>();                                                     \
+        a.slices = c.dv / SL;                                                                   \
         hipLaunchKernelGGL((bwd_ap_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kFinT), 0, s, a);    \
-        hipLaunchKernelGGL((bwd_states_kernel<DK, TI>), dim3(seq_blocks), dim3(kBT), 0, s, a);  \
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, TI, TD>), dim3(seq_blocks), dim3(kScanT), 0, s, a); \
+        hipLaunchKernelGGL((bwd_states_kernel<DK, TI>), dim3(c.num_seqs * c.H * (c.dv / kStSL)), \
+                           dim3(kBT), 0, s, a);                                                 \
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, SL, TI, TD>), dim3(c.num_seqs * c.H * a.slices), \
+                           dim3(kScanT), 0, s, a);                                              \
         hipLaunchKernelGGL((bwd_finish_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kFinT), 0, s, a); \
     } while (0)
     if (c.dk == 128) {

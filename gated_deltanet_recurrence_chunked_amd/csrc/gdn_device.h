@@ -152,17 +152,20 @@ template <> __device__ __forceinline__ void store1<uint16_t>(uint16_t* p, float 
 // --------------------------------------------------------------------------- fp32 matrix core
 // acc (a 16x16 tile) += A (16 x K) B (K x 16) on v_mfma_f32_16x16x4f32, whose products and sums
 // are full fp32. Element (r, k) of A is A[r * ar + k * ak] and element (k, c) of B is
-// B[k * bk + c * bc], so transposed views are strides. K is a multiple of 4. One wave computes
+// B[k * bk + c * bc], so transposed views are strides; operands are fp32, or bf16 (uint16_t) that
+// widen exactly. K is a multiple of 4. One wave computes
 // the tile: lane l supplies A(l%16, k0 + l/16) and B(k0 + l/16, l%16) per step and holds
 // C(4 (l/16) + i, l%16) in acc[i].
-__device__ __forceinline__ floatx4 mma_f32_tile(const float* A, int ar, int ak, const float* B,
-                                                int bk, int bc, int K, floatx4 acc) {
+template <typename TA, typename TB>
+__device__ __forceinline__ floatx4 mma_f32_tile(const TA* A, int ar, int ak, const TB* B, int bk,
+                                                int bc, int K, floatx4 acc) {
     const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-    const float* pa = A + c * ar + g * ak;
-    const float* pb = B + g * bk + c * bc;
+    const TA* pa = A + c * ar + g * ak;
+    const TB* pb = B + g * bk + c * bc;
 #pragma unroll 4
     for (int k0 = 0; k0 < K; k0 += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0 * ak], pb[k0 * bk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(load1(pa + k0 * ak), load1(pb + k0 * bk), acc, 0,
+                                                   0, 0);
     return acc;
 }
 
