@@ -142,13 +142,29 @@ __device__ __forceinline__ void load_rows(const void* x, int t0, int n, int H, i
     }
 }
 
-// the same rows kept in their input type (bf16 bits are copied, not widened), row stride RS
+// the same rows kept in their input type (bf16 bits are copied, not widened), row stride RS:
+// one 16-byte global load per unit, written to LDS as 4-byte words (RS keeps them 4-aligned)
 template <int DK, int RS, typename Tin, int NT>
 __device__ __forceinline__ void load_rows_raw(const void* x, int t0, int n, int H, int h, Tin (*dst)[RS]) {
+    constexpr int PER = 16 / sizeof(Tin), UPR = DK / PER;
+    static_assert((RS * sizeof(Tin)) % 4 == 0, "row stride");
     const Tin* xp = static_cast<const Tin*>(x);
-    for (int e = threadIdx.x; e < kC * DK; e += NT) {
-        const int r = e / DK, d = e % DK;
-        dst[r][d] = r < n ? xp[((size_t)(t0 + r) * H + h) * DK + d] : Tin(0);
+    for (int u = threadIdx.x; u < kC * UPR; u += NT) {
+        const int r = u / UPR, c = (u % UPR) * PER;
+        gdn_u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < n) v = *reinterpret_cast<const gdn_u32x4*>(xp + ((size_t)(t0 + r) * H + h) * DK + c);
+        uint32_t* d = reinterpret_cast<uint32_t*>(&dst[r][c]);
+        d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+    }
+}
+
+// a [64][64] fp32 tile of the workspace into LDS rows of stride 65, 16 bytes per global load
+template <int NT>
+__device__ __forceinline__ void load_tile64(const float* src, float (*dst)[kC + 1]) {
+    for (int u = threadIdx.x; u < kC * kC / 4; u += NT) {
+        const int r = u / (kC / 4), c = (u % (kC / 4)) * 4;
+        const float4 v = reinterpret_cast<const float4*>(src)[u];
+        dst[r][c] = v.x; dst[r][c + 1] = v.y; dst[r][c + 2] = v.z; dst[r][c + 3] = v.w;
     }
 }
 
@@ -237,7 +253,7 @@ template <int DK, typename Tin>
 __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
     constexpr int SL = kStSL, CT = SL / 16, PR = SL + 1;
     __shared__ float Ks[kC][DK + 1];
-    __shared__ float S[DK][SL];
+    __shared__ float S[DK][PR];
     __shared__ float T[kC][kC + 1];
     __shared__ float R[kC][PR], W[kC][PR];
     __shared__ float gam[kC], w[kC], Bt[kC];
@@ -279,7 +295,7 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
         __syncthreads();
         if (wave < 4 * CT) {   // R = beta o (V - gamma o K S)
             const int rt = wave % 4, ct = wave / 4;
-            const floatx4 ks = mma_f32_tile(&Ks[rt * 16][0], DK + 1, 1, &S[0][ct * 16], SL, 1, DK, zero);
+            const floatx4 ks = mma_f32_tile(&Ks[rt * 16][0], DK + 1, 1, &S[0][ct * 16], PR, 1, DK, zero);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rt * 16 + 4 * lg + i, j = ct * 16 + lc;
@@ -324,7 +340,9 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
     constexpr int PR = SL + 1;                     // padded row of a [64][SL] tile
     constexpr int KR = DK + (sizeof(Tin) == 2 ? 2 : 1);
     __shared__ Tin Ks[kC][KR], Qs[kC][KR];
-    __shared__ float S[DK][SL], dS[DK][SL];        // state entering the chunk; gradient after
+    // state entering the chunk and the gradient after it; rows padded by one so the transposed
+    // operand reads (16 rows, 4 columns per step) spread over the banks
+    __shared__ float S[DK][PR], dS[DK][PR];
     __shared__ float T[kC][kC + 1], P[kC][kC + 1];
     // [64][SL] tiles: dY, KS, QS, U, KdS = K dS', dU, dR; late in the step QS and KS are reused
     // for gamma o dY and (beta gamma) o dR, and dR holds R = beta o (V - gamma o KS) until dR
@@ -366,14 +384,13 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
             const int r = e / SL, j = e % SL;
             dY[r][j] = r < n ? ld<Tdy>(a.dy, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
         }
-        for (int e = tid; e < DK * SL; e += kScanT) {
-            const int d = e / SL, j = e % SL;
-            S[d][j] = a.Sc[ch * DK * dv + (size_t)d * dv + j0 + j];
+        for (int u = tid; u < DK * SL / 4; u += kScanT) {   // 16 bytes per load
+            const int d = u / (SL / 4), j = (u % (SL / 4)) * 4;
+            const float4 v = *reinterpret_cast<const float4*>(a.Sc + ch * DK * dv + (size_t)d * dv + j0 + j);
+            S[d][j] = v.x; S[d][j + 1] = v.y; S[d][j + 2] = v.z; S[d][j + 3] = v.w;
         }
-        for (int e = tid; e < kC * kC; e += kScanT) {
-            T[e / kC][e % kC] = a.T[ch * kC * kC + e];
-            P[e / kC][e % kC] = a.P[ch * kC * kC + e];
-        }
+        load_tile64<kScanT>(a.T + ch * kC * kC, T);
+        load_tile64<kScanT>(a.P + ch * kC * kC, P);
         if (tid < kC) {
             const float* Gc = a.G + ch * kC;
             gam[tid] = expf(Gc[tid]);
@@ -386,7 +403,7 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
             const int kind = tile / (4 * CT), rt = tile % 4, ct = (tile / 4) % CT;
             const Tin* A = kind == 1 ? &Qs[rt * 16][0] : &Ks[rt * 16][0];
             const float* B = kind == 2 ? &dS[0][ct * 16] : &S[0][ct * 16];
-            const floatx4 acc = mma_f32_tile(A, KR, 1, B, SL, 1, DK, zero);
+            const floatx4 acc = mma_f32_tile(A, KR, 1, B, PR, 1, DK, zero);
             float(*dst)[PR] = kind == 0 ? KS : (kind == 1 ? QS : KdS);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[rt * 16 + 4 * lg + i][ct * 16 + lc] = acc[i];
@@ -439,7 +456,7 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
         for (int tile = (wave + NW - 4 * CT) % NW; tile < 4 * (DK / 16) + 16; tile += NW) {
             if (tile < 4 * (DK / 16)) {   // dq share tile (rt, dt)
                 const int rt = tile / (DK / 16), dt = tile % (DK / 16);
-                const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], PR, 1, &S[dt * 16][0], 1, SL, SL,
+                const floatx4 acc = mma_f32_tile(&dY[rt * 16][0], PR, 1, &S[dt * 16][0], 1, PR, SL,
                                                  zero);
                 floatx4 o;
 #pragma unroll
@@ -487,8 +504,8 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
         for (int tile = wave; tile < 4 * (DK / 16) + 16; tile += NW) {
             if (tile < 4 * (DK / 16)) {   // dk share: w o (U dS'^T) - (beta gamma) o (dR S^T)
                 const int rt = tile / (DK / 16), dt = tile % (DK / 16);
-                const floatx4 a1 = mma_f32_tile(&U[rt * 16][0], PR, 1, &dS[dt * 16][0], 1, SL, SL, zero);
-                const floatx4 a2 = mma_f32_tile(&dR[rt * 16][0], PR, 1, &S[dt * 16][0], 1, SL, SL, zero);
+                const floatx4 a1 = mma_f32_tile(&U[rt * 16][0], PR, 1, &dS[dt * 16][0], 1, PR, SL, zero);
+                const floatx4 a2 = mma_f32_tile(&dR[rt * 16][0], PR, 1, &S[dt * 16][0], 1, PR, SL, zero);
                 floatx4 o;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
