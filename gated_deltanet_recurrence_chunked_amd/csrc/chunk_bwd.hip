@@ -133,12 +133,26 @@ __device__ __forceinline__ float ld(const void* p, size_t i) {
     return load1(static_cast<const T*>(p) + i);
 }
 
-// [64][DK] rows of a token-major [ntok, H, DK] tensor (zero past n) into LDS rows of stride DK+1
+// [64][DK] rows of a token-major [ntok, H, DK] tensor (zero past n) into fp32 LDS rows of stride
+// DK+1, one 16-byte global load per unit of 8 (bf16) or 4 (fp32) elements
 template <int DK, typename Tin, int NT = kBT>
 __device__ __forceinline__ void load_rows(const void* x, int t0, int n, int H, int h, float (*dst)[DK + 1]) {
-    for (int e = threadIdx.x; e < kC * DK; e += NT) {
-        const int r = e / DK, d = e % DK;
-        dst[r][d] = r < n ? ld<Tin>(x, ((size_t)(t0 + r) * H + h) * DK + d) : 0.f;
+    constexpr int PER = 16 / sizeof(Tin), UPR = DK / PER;
+    const Tin* xp = static_cast<const Tin*>(x);
+    for (int u = threadIdx.x; u < kC * UPR; u += NT) {
+        const int r = u / UPR, c = (u % UPR) * PER;
+        gdn_u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < n) v = *reinterpret_cast<const gdn_u32x4*>(xp + ((size_t)(t0 + r) * H + h) * DK + c);
+        if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dst[r][c + 2 * i] = __uint_as_float(v[i] << 16);
+                dst[r][c + 2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[r][c + i] = __uint_as_float(v[i]);
+        }
     }
 }
 
@@ -276,12 +290,13 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
         const int n = min(kC, hi - t0);
         const size_t ch = (size_t)c * H + h;
         __syncthreads();
-        for (int e = tid; e < DK * SL; e += kBT) {   // the state entering this chunk
-            const int d = e / SL, j = e % SL;
-            a.Sc[ch * DK * dv + (size_t)d * dv + j0 + j] = S[d][j];
+        for (int u = tid; u < DK * SL / 4; u += kBT) {   // the state entering this chunk
+            const int d = u / (SL / 4), j = (u % (SL / 4)) * 4;
+            *reinterpret_cast<float4*>(a.Sc + ch * DK * dv + (size_t)d * dv + j0 + j) =
+                make_float4(S[d][j], S[d][j + 1], S[d][j + 2], S[d][j + 3]);
         }
         load_rows<DK, Tin>(a.k, t0, n, H, h, Ks);
-        for (int e = tid; e < kC * kC; e += kBT) T[e / kC][e % kC] = a.T[ch * kC * kC + e];
+        load_tile64<kBT>(a.T + ch * kC * kC, T);
         for (int e = tid; e < kC * SL; e += kBT) {   // V, zero past n
             const int r = e / SL, j = e % SL;
             R[r][j] = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
