@@ -1,5 +1,5 @@
 // Chunkwise delta rule with a per-channel (diagonal) decay on gfx950: the KDA-style variant
-// of the Gated DeltaNet recurrence (fp32 vector ALU).
+// of the Gated DeltaNet recurrence (fp32; the scan's products on the matrix core).
 //
 // The reading notes of "On the Design of Qwen3.8-Next Architecture" compare GDN with Kimi K3's
 // Kimi Delta Attention (related work), whose decay is per channel with a lower-bounded log-decay.
@@ -105,13 +105,21 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, H = a.H;
     int t0, n;
     if (!kda_chunk(a, c, t0, n)) return;
-    for (int e = tid; e < kC * DK; e += kPT) {
-        const int r = e / DK, d = e % DK;
+    for (int u = tid; u < kC * DK / 4; u += kPT) {   // 4 channels per thread and step
+        const int r = u / (DK / 4), d = (u % (DK / 4)) * 4;
         const bool ok = r < n;
-        const size_t off = ((size_t)(t0 + r) * H + h) * DK + d;
-        Ks[r][d] = ok ? ldx<Tin>(a.k, off) : 0.f;
-        Qs[r][d] = ok ? ldx<Tin>(a.q, off) : 0.f;
-        Gc[r][d] = ok ? a.g[off] : 0.f;
+        const size_t off = ((size_t)(t0 + min(r, n - 1)) * H + h) * DK + d;
+        float kv[4], qv[4];
+        Vec4<Tin>::load(static_cast<const Tin*>(a.k) + off, kv);
+        Vec4<Tin>::load(static_cast<const Tin*>(a.q) + off, qv);
+        const float4 gv = *reinterpret_cast<const float4*>(a.g + off);
+        const float gs[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Ks[r][d + i] = ok ? kv[i] : 0.f;
+            Qs[r][d + i] = ok ? qv[i] : 0.f;
+            Gc[r][d + i] = ok ? gs[i] : 0.f;
+        }
     }
     if (tid < kC) Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
     __syncthreads();
@@ -124,19 +132,33 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
     }
     __syncthreads();
     const size_t ch = (size_t)c * H + h;
-    // A (strictly lower) and P (lower with the diagonal): decays per channel and pair
+    // A (strictly lower) and P (lower with the diagonal): decays per channel and pair. Only the
+    // 64*65/2 pairs i <= r are enumerated (pair p -> row r with r(r+1)/2 <= p, column
+    // i = p - r(r+1)/2), so no lane idles on the upper triangle; that one is zeroed apart.
     for (int e = tid; e < kC * kC; e += kPT) {
         const int r = e / kC, i = e % kC;
+        if (i > r) {
+            A[r][i] = 0.f;
+            a.P[ch * kC * kC + e] = 0.f;
+        }
+    }
+    for (int p = tid; p < kC * (kC + 1) / 2; p += kPT) {
+        int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+        while (r * (r + 1) / 2 > p) --r;                 // guard the float root
+        while ((r + 1) * (r + 2) / 2 <= p) ++r;
+        const int i = p - r * (r + 1) / 2;
         float kk = 0.f, qk = 0.f;
-        if (i <= r && r < n) {
+        if (r < n) {
+#pragma unroll 4
             for (int d = 0; d < DK; ++d) {
                 const float dec = fexp(Gc[r][d] - Gc[i][d]);
-                kk += Ks[r][d] * Ks[i][d] * dec;
-                qk += Qs[r][d] * Ks[i][d] * dec;
+                const float kd = Ks[i][d] * dec;
+                kk += Ks[r][d] * kd;
+                qk += Qs[r][d] * kd;
             }
         }
         A[r][i] = i < r ? Bt[r] * kk : 0.f;
-        a.P[ch * kC * kC + e] = qk;
+        a.P[ch * kC * kC + r * kC + i] = qk;
     }
     // decayed operands of the scan
     const int last = n - 1;
@@ -166,18 +188,35 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
 }
 
 // ------------------------------------------------------------------ scan per (seq, head, slice)
+// Each chunk step's products run on the fp32 matrix core (v_mfma_f32_16x16x4f32), one 16x16
+// output tile per wave, operands read from LDS as strided views.
+template <int NT>
+__device__ __forceinline__ void kda_load_tile(const float* src, int rows, int cols, float* dst, int stride) {
+    const int upr = cols / 4;
+    for (int u = threadIdx.x; u < rows * upr; u += NT) {
+        const int r = u / upr, c = (u % upr) * 4;
+        const float4 v = reinterpret_cast<const float4*>(src)[u];
+        float* d = dst + r * stride + c;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+}
+
 template <int DK, typename Tin, typename Tout>
 __global__ void __launch_bounds__(kST) kda_scan_kernel(KdaArgs a) {
+    constexpr int PR = kSL + 1;
     __shared__ float Kg[kC][DK + 1], Qg[kC][DK + 1], Kc[kC][DK + 1];
     __shared__ float T[kC][kC + 1], P[kC][kC + 1];
-    __shared__ float S[DK][kSL];
-    __shared__ float R[kC][kSL + 1], U[kC][kSL + 1];
+    __shared__ float S[DK][PR];
+    __shared__ float R[kC][PR], U[kC][PR];
     __shared__ float eC[DK], Bt[kC];
     const int slices = a.dv / kSL;
     const int slice = blockIdx.x % slices;
     const int h = (blockIdx.x / slices) % a.H;
     const int sq = blockIdx.x / (slices * a.H);
     const int j0 = slice * kSL, tid = threadIdx.x, H = a.H, dv = a.dv;
+    const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    static_assert(4 + DK / 16 <= kST / kWave, "one tile per wave in the last step");
     Tout* y = static_cast<Tout*>(a.y);
     int lo, hi, cbase;
     kda_seq(a, sq, lo, hi, cbase);
@@ -190,51 +229,57 @@ __global__ void __launch_bounds__(kST) kda_scan_kernel(KdaArgs a) {
         const int n = min(kC, hi - t0);
         const size_t ch = (size_t)c * H + h;
         __syncthreads();
-        for (int e = tid; e < kC * DK; e += kST) {
-            const size_t o = ch * kC * DK + e;
-            Kg[e / DK][e % DK] = a.Kg[o];
-            Qg[e / DK][e % DK] = a.Qg[o];
-            Kc[e / DK][e % DK] = a.Kc[o];
-        }
-        for (int e = tid; e < kC * kC; e += kST) {
-            T[e / kC][e % kC] = a.T[ch * kC * kC + e];
-            P[e / kC][e % kC] = a.P[ch * kC * kC + e];
+        kda_load_tile<kST>(a.Kg + ch * kC * DK, kC, DK, &Kg[0][0], DK + 1);
+        kda_load_tile<kST>(a.Qg + ch * kC * DK, kC, DK, &Qg[0][0], DK + 1);
+        kda_load_tile<kST>(a.Kc + ch * kC * DK, kC, DK, &Kc[0][0], DK + 1);
+        kda_load_tile<kST>(a.T + ch * kC * kC, kC, kC, &T[0][0], kC + 1);
+        kda_load_tile<kST>(a.P + ch * kC * kC, kC, kC, &P[0][0], kC + 1);
+        for (int e = tid; e < kC * kSL; e += kST) {   // V into R, zero past n
+            const int r = e / kSL, j = e % kSL;
+            R[r][j] = r < n ? ldx<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
         }
         if (tid < DK) eC[tid] = a.eC[ch * DK + tid];
         if (tid < kC) Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
         __syncthreads();
-        for (int e = tid; e < kC * kSL; e += kST) {   // R = beta o (V - Kg S)
-            const int r = e / kSL, j = e % kSL;
-            float ks = 0.f;
-#pragma unroll 4
-            for (int d = 0; d < DK; ++d) ks += Kg[r][d] * S[d][j];
-            const float vr = r < n ? ldx<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
-            R[r][j] = Bt[r] * (vr - ks);
-        }
-        __syncthreads();
-        for (int e = tid; e < kC * kSL; e += kST) {   // U = T R
-            const int r = e / kSL, j = e % kSL;
-            float u = 0.f;
-            for (int i = 0; i <= r; ++i) u += T[r][i] * R[i][j];
-            U[r][j] = u;
-        }
-        __syncthreads();
-        for (int e = tid; e < kC * kSL; e += kST) {   // Y = Qg S + P U
-            const int r = e / kSL, j = e % kSL;
-            if (r < n) {
-                float acc = 0.f;
-#pragma unroll 4
-                for (int d = 0; d < DK; ++d) acc += Qg[r][d] * S[d][j];
-                for (int i = 0; i <= r; ++i) acc += P[r][i] * U[i][j];
-                store1(y + ((size_t)(t0 + r) * H + h) * dv + j0 + j, acc);
+        if (wave < 4) {   // R = beta o (V - Kg S)
+            const floatx4 ks = mma_f32_tile(&Kg[wave * 16][0], DK + 1, 1, &S[0][0], PR, 1, DK, zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wave * 16 + 4 * lg + i;
+                R[r][lc] = Bt[r] * (R[r][lc] - ks[i]);
             }
         }
-        __syncthreads();   // Y read S before it moves on
-        for (int e = tid; e < DK * kSL; e += kST) {   // S' = e^{Gc[C]} o S + Kc^T U
-            const int d = e / kSL, j = e % kSL;
-            float acc = 0.f;
-            for (int i = 0; i < n; ++i) acc += Kc[i][d] * U[i][j];
-            S[d][j] = eC[d] * S[d][j] + acc;
+        __syncthreads();
+        if (wave < 4) {   // U = T R (T lower triangular)
+            const floatx4 u = mma_f32_tile(&T[wave * 16][0], kC + 1, 1, &R[0][0], PR, 1, kC, zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) U[wave * 16 + 4 * lg + i][lc] = u[i];
+        }
+        __syncthreads();
+        // waves 0-3: Y = Qg S + P U (rows past n are not stored);
+        // waves 4..: S' = e^{Gc[C]} o S + Kc^T U, held in registers until every read of S is done
+        floatx4 sn = zero;
+        if (wave < 4) {
+            floatx4 acc = mma_f32_tile(&Qg[wave * 16][0], DK + 1, 1, &S[0][0], PR, 1, DK, zero);
+            acc = mma_f32_tile(&P[wave * 16][0], kC + 1, 1, &U[0][0], PR, 1, kC, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wave * 16 + 4 * lg + i;
+                if (r < n) store1(y + ((size_t)(t0 + r) * H + h) * dv + j0 + lc, acc[i]);
+            }
+        } else if (wave < 4 + DK / 16) {
+            const int dt = wave - 4;
+            sn = mma_f32_tile(&Kc[0][dt * 16], 1, DK + 1, &U[0][0], PR, 1, kC, zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = dt * 16 + 4 * lg + i;
+                sn[i] += eC[d] * S[d][lc];
+            }
+        }
+        __syncthreads();
+        if (wave >= 4 && wave < 4 + DK / 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[(wave - 4) * 16 + 4 * lg + i][lc] = sn[i];
         }
     }
     __syncthreads();
