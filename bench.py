@@ -415,6 +415,71 @@ def main():
         del F, of, hist, qkv, ysep
         torch.cuda.empty_cache()
 
+        # the same with 4 tokens per sequence per step (MTP verify from the projected streams)
+        T4, S4 = 4, max(1, S_ // 4)
+        fm = gi.decode_layer_draws(1, S4, 256, 32, tokens=T4)
+        F = {x: d(fm[x], True) for x in ("xq", "xk", "xv", "z", "conv_state")}
+        F.update({x: d(fm[x]) for x in ("wq", "wk", "wv", "a_raw", "b_raw", "A_log", "dt_bias",
+                                        "norm_weight", "state")})
+        of = torch.empty((N, T4, DH, fdv), dtype=bf, device=dev)
+
+        def fmdec(s):
+            gdn.gdn_fused_decode_multi(F["xq"][s], F["xk"][s], F["xv"][s], F["wq"], F["wk"],
+                                       F["wv"], F["conv_state"], F["a_raw"][s], F["b_raw"][s],
+                                       F["A_log"], F["dt_bias"], F["state"], F["z"][s],
+                                       F["norm_weight"], o=of)
+        for s in range(min(3, S4)):
+            fmdec(s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(S4):
+            fmdec(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fmms = e0.elapsed_time(e1) / S4
+        hist = [F["conv_state"], torch.empty_like(F["conv_state"])]
+        qkv = dict(q=torch.empty((N * T4, DH, fdk), dtype=bf, device=dev),
+                   k=torch.empty((N * T4, DH, fdk), dtype=bf, device=dev),
+                   v=torch.empty((N * T4, DH, fdv), dtype=bf, device=dev),
+                   g=torch.empty((N * T4, DH), dtype=torch.float32, device=dev),
+                   beta=torch.empty((N * T4, DH), dtype=torch.float32, device=dev))
+        ysep = torch.empty((N, T4, DH, fdv), dtype=bf, device=dev)
+
+        def smdec(s):
+            gdn.gdn_preprocess_stateful(
+                F["xq"][s].view(N * T4, DH, fdk), F["xk"][s].view(N * T4, DH, fdk),
+                F["xv"][s].view(N * T4, DH, fdv), F["wq"], F["wk"], F["wv"],
+                F["a_raw"][s].view(N * T4, DH), F["b_raw"][s].view(N * T4, DH), F["A_log"],
+                F["dt_bias"], H=DH, num_seqs=N, out_dtype=bf, outs=qkv,
+                conv_state_in=hist[s % 2], conv_state_out=hist[1 - s % 2])
+            gdn.gdn_decode_multi(qkv["q"].view(N, T4, DH, fdk), qkv["k"].view(N, T4, DH, fdk),
+                                 qkv["v"].view(N, T4, DH, fdv), qkv["g"].view(N, T4, DH),
+                                 qkv["beta"].view(N, T4, DH), F["state"], y=ysep)
+            gdn.gdn_output_gate(ysep.view(N * T4, DH, fdv), F["z"][s].view(N * T4, DH, fdv),
+                                F["norm_weight"], eps=1e-6, o=of.view(N * T4, DH, fdv))
+        for s in range(min(2, S4)):
+            smdec(s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(S4 - S4 % 2):
+            smdec(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        smms = e0.elapsed_time(e1) / max(1, S4 - S4 % 2)
+        fm_tok = T4 * heads * ((2 * fdk + fdv) * 2 + 8 + fdv * (2 + 2)) + 2 * heads * 3 * (2 * fdk + fdv) * 2
+        fmgbs = (f_state + fm_tok) / (fmms * 1e-3) / 1e9
+        decode["fused_multi_token"] = {
+            "workload": f"gdn_fused_decode_multi N=256 H=32 d_k=d_v=128, {T4} tokens per sequence "
+                        "per step from the projected streams (bf16 x, z, o)",
+            "tokens_per_step": T4, "steps": S4, "us_per_step": round(fmms * 1e3, 2),
+            "GB_s": round(fmgbs, 1), "hbm_frac": round(fmgbs / HBM_PEAK_GBS, 4),
+            "separate_kernels_us_per_step": round(smms * 1e3, 2),
+            "vs_separate_kernels": round(smms / fmms, 3)}
+        log(f"[bench] fused multi-token decode T={T4}: {fmms * 1e3:.1f} us/step ({fmgbs:.0f} GB/s); "
+            f"separate kernels {smms * 1e3:.1f} us/step")
+        del F, of, hist, qkv, ysep
+        torch.cuda.empty_cache()
+
     if args.calibrate_copy:
         n = 1 << 28
         src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)

@@ -94,6 +94,11 @@ def lib():
         L.gdn_fused_decode.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                                        _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_float, _i, _i,
                                        _i, _i, _vp, _i, _vp, _vp]
+        L.gdn_fused_decode_multi.restype = _i
+        L.gdn_fused_decode_multi.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp,
+                                             _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                             ctypes.c_float, _i, _i, _i, _i, _i, _vp, _i, _vp,
+                                             _vp, _vp]
         _lib = L
     return _lib
 
@@ -459,8 +464,43 @@ def gdn_fused_decode(xq, xk, xv, wq, wk, wv, conv_state, a_raw, b_raw, A_log, dt
     return (o, y) if want_y else o
 
 
+def gdn_fused_decode_multi(xq, xk, xv, wq, wk, wv, conv_state_in, a_raw, b_raw, A_log, dt_bias,
+                           state, z, norm_weight, *, conv_state_out=None, l2_eps=1e-6,
+                           rms_eps=1e-6, o=None, o_dtype=None, want_y=False, step_states=None,
+                           stream=None):
+    """T tokens per sequence through the fused step. xq, xk: [N,T,H,dk], xv, z: [N,T,H,dv]
+    (x dtype); a_raw, b_raw: [N,T,H] fp32; conv_state_in: [N,3,H*(2dk+dv)]; conv_state_out:
+    None (update conv_state_in in place) or a separate buffer of that shape; state updated in
+    place; step_states: None, True (allocate) or [N,T,H,dk,dv] fp32.
+    Returns (o, y or None, step_states)."""
+    N, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    x_tag = _dtype_tag(xq)
+    if z.dtype != xq.dtype:
+        raise GdnError("z must have the dtype of xq")
+    o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else x_tag)
+    if o is None:
+        o = torch.empty((N, T, H, dv), dtype=_tag_dtype(o_tag), device=xq.device)
+    y = torch.empty_like(o) if want_y else None
+    if conv_state_out is None:
+        conv_state_out = conv_state_in
+    if step_states is True:
+        step_states = torch.empty((N, T, H, dk, dv), dtype=torch.float32, device=xq.device)
+    f32 = torch.float32
+    st = lib().gdn_fused_decode_multi(
+        _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), x_tag, _ptr(wq, "wq", f32),
+        _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4, _ptr(conv_state_in, "conv_state_in", xq.dtype),
+        _ptr(conv_state_out, "conv_state_out", xq.dtype), _ptr(a_raw, "a_raw", f32),
+        _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32), _ptr(dt_bias, "dt_bias", f32),
+        l2_eps, _ptr(state, "state", f32), _ptr(z, "z"), _ptr(norm_weight, "norm_weight", f32),
+        rms_eps, N, T, H, dk, dv, _ptr(o, "o"), o_tag, _ptr(y, "y"),
+        _ptr(step_states, "step_states", f32), _stream(stream))
+    _check(st, "gdn_fused_decode_multi")
+    return o, y, step_states
+
+
 __all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_preprocess_stateful",
            "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_chunk_backward",
            "gdn_chunk_backward_workspace_size", "gdn_kda_chunk_prefill", "gdn_decode_step",
            "gdn_decode_multi", "gdn_output_gate", "gdn_fused_prefill",
-           "gdn_fused_prefill_workspace_size", "gdn_fused_decode"]
+           "gdn_fused_prefill_workspace_size", "gdn_fused_decode", "gdn_fused_decode_multi"]

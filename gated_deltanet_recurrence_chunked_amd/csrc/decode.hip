@@ -268,13 +268,43 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(DecodeFusedAr
 constexpr int kDecMultiThreads = 512;
 constexpr int kDecColSplit = 1;
 
+// With kFused the step starts from the projected streams instead of q, k, v, g, beta: one
+// thread per channel runs the width-4 conv over the carried history and the T new inputs
+// (SiLU; the history moves on by T inputs), the gates come from a_raw, b_raw, the L2 norms of
+// q_t, k_t are applied in LDS, and the output gate runs after the state pass (the TPR lanes of
+// the first row group hold all of y_t, parked in LDS meanwhile) instead of storing y.
+struct MultiArgs {
+    const void *q, *k, *v;                 // [N, T, H, d] (unfused)
+    const float *g, *beta;                 // [N, T, H] (unfused)
+    const void* x[3];                      // xq, xk, xv [N, T, H, d] (fused)
+    const float* w[3];                     // conv taps [H*d, 4]
+    const void* hin;                       // conv history in [N, 3, hC], x dtype
+    void* hout;                            // conv history out (may equal hin)
+    int hC;
+    const float *a_raw, *b_raw, *A_log, *dt_bias;
+    float l2_eps;
+    const void* z;                         // [N, T, H, dv], x dtype
+    const float* norm_w;
+    float rms_eps;
+    void* o;                               // [N, T, H, dv] (fused)
+    float* state;
+    void* y;                               // [N, T, H, dv]; nullable when fused
+    float* steps;                          // nullable
+    int T, H;
+};
+
 // kMaxDecT (2, 4 or 8) bounds T at compile time: the per-token register arrays are sized by
 // it, so a short step does not pay the registers (and occupancy) of the longest one.
-template <int DK, int DV, int kMaxDecT, typename Tin, typename Tout>
+template <int DK, int DV, int kMaxDecT, typename Tin, typename Tout, bool kFused>
 __global__ void __launch_bounds__(kDecMultiThreads, kMaxDecT <= 4 ? 4 : 2)
-decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-                    const float* __restrict__ g, const float* __restrict__ beta, float* state,
-                    Tout* __restrict__ y, float* __restrict__ steps, int T, int H) {
+decode_multi_kernel(MultiArgs m) {
+    const Tin* __restrict__ q = static_cast<const Tin*>(m.q);
+    const Tin* __restrict__ k = static_cast<const Tin*>(m.k);
+    const Tin* __restrict__ v = static_cast<const Tin*>(m.v);
+    Tout* __restrict__ y = static_cast<Tout*>(m.y);
+    float* state = m.state;
+    float* __restrict__ steps = m.steps;
+    const int T = m.T, H = m.H;
     constexpr int DVS = DV / kDecColSplit;       // columns of this workgroup
     constexpr int TPR = DVS / 4;                 // threads per state row
     constexpr int RG = kDecMultiThreads / TPR;   // row groups
@@ -291,6 +321,9 @@ decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const 
     // P[t][i] = e^{G_t-G_i} q_t.k_i (i <= t), D[t][i] = e^{G_t-G_i} (i <= t)
     __shared__ float Am[kMaxDecT][kMaxDecT], Pm[kMaxDecT][kMaxDecT], Dm[kMaxDecT][kMaxDecT];
     __shared__ float Gs[kMaxDecT], Bs[kMaxDecT];   // G_t and beta_t
+    __shared__ __attribute__((aligned(16))) float vs[kFused ? kMaxDecT : 1][kFused ? DV : 4];
+    __shared__ __attribute__((aligned(16))) float zs[kFused ? kMaxDecT : 1][kFused ? DV : 4];
+    __shared__ float gl[kMaxDecT];
 
     const int head = blockIdx.x / kDecColSplit;   // flattened (sequence, head)
     const int n = head / H, h = head % H;
@@ -303,31 +336,114 @@ decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const 
 
     float* S = state + (size_t)head * DK * DV;
     float s[RPT][4];
+    // the state's loads go first (the unfused prologue's loads overlap them); the fused
+    // prologue's registers would not fit beside them, so there they follow it
+    auto load_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const floatx4 x = __builtin_nontemporal_load(
-            reinterpret_cast<const floatx4*>(S + (size_t)(r0 + i) * DV + c));
-        s[i][0] = x.x; s[i][1] = x.y; s[i][2] = x.z; s[i][3] = x.w;
-    }
-    for (int i = tid; i < T * DK; i += kDecMultiThreads) {
-        const int t = i / DK, r = i % DK;
-        ks[t][r] = load1(k + tok(t) * DK + r);
-        qs[t][r] = load1(q + tok(t) * DK + r);
-    }
+        for (int i = 0; i < RPT; ++i) {
+            const floatx4 x = __builtin_nontemporal_load(
+                reinterpret_cast<const floatx4*>(S + (size_t)(r0 + i) * DV + c));
+            s[i][0] = x.x; s[i][1] = x.y; s[i][2] = x.z; s[i][3] = x.w;
+        }
+    };
+    if constexpr (!kFused) load_state();
     float vv[kMaxDecT][4];
-    float run = 0.f;
+    if constexpr (!kFused) {
+        for (int i = tid; i < T * DK; i += kDecMultiThreads) {
+            const int t = i / DK, r = i % DK;
+            ks[t][r] = load1(k + tok(t) * DK + r);
+            qs[t][r] = load1(q + tok(t) * DK + r);
+        }
+        float run = 0.f;
 #pragma unroll
-    for (int t = 0; t < kMaxDecT; ++t) {
-        if (t < T) {
-            Vec4<Tin>::load(v + tok(t) * DV + c, vv[t]);
-            run += g[tok(t)];
-            if (tid == t) {
-                Gs[t] = run;
-                Bs[t] = beta[tok(t)];
+        for (int t = 0; t < kMaxDecT; ++t) {
+            if (t < T) {
+                Vec4<Tin>::load(v + tok(t) * DV + c, vv[t]);
+                run += m.g[tok(t)];
+                if (tid == t) {
+                    Gs[t] = run;
+                    Bs[t] = m.beta[tok(t)];
+                }
             }
         }
+        __syncthreads();
+    } else {
+        // conv over [history rows 0..2, x_0 .. x_{T-1}], one channel (of q | k | v) per thread
+        const Tin* hin = static_cast<const Tin*>(m.hin) + (size_t)n * 3 * m.hC;
+        Tin* hout = static_cast<Tin*>(m.hout) + (size_t)n * 3 * m.hC;
+        for (int ch = tid; ch < 2 * DK + DV; ch += kDecMultiThreads) {
+            const int role = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
+            const int cl2 = ch - (role == 0 ? 0 : (role == 1 ? DK : 2 * DK));
+            const int d = role < 2 ? DK : DV;
+            const int cs = h * d + cl2;
+            const int hc = (role == 0 ? 0 : (role == 1 ? H * DK : 2 * H * DK)) + cs;
+            const Tin* xs = static_cast<const Tin*>(m.x[role]);
+            const float4 w = reinterpret_cast<const float4*>(m.w[role])[cs];
+            Tin buf[3 + kMaxDecT];   // history then the new inputs, raw
+            buf[0] = hin[hc];
+            buf[1] = hin[m.hC + hc];
+            buf[2] = hin[2 * m.hC + hc];
+#pragma unroll
+            for (int t = 0; t < kMaxDecT; ++t)
+                if (t < T) buf[3 + t] = xs[tok(t) * d + cl2];
+            float* dst = role == 0 ? &qs[0][0] : (role == 1 ? &ks[0][0] : &vs[0][0]);
+            const int stride = role < 2 ? DK : DV;
+#pragma unroll
+            for (int t = 0; t < kMaxDecT; ++t)
+                if (t < T)
+                    dst[t * stride + cl2] = siluf_(conv4(w.x, w.y, w.z, w.w, load1(&buf[t]),
+                                                         load1(&buf[t + 1]), load1(&buf[t + 2]),
+                                                         load1(&buf[t + 3])));
+            // the next history: the last 3 of the T + 3 inputs (read above, so in place is safe)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                Tin nv = buf[j];
+#pragma unroll
+                for (int t = 1; t <= kMaxDecT; ++t)
+                    if (t == T) nv = buf[j + t];
+                hout[j * m.hC + hc] = nv;
+            }
+        }
+        // gates: thread t forms token t's; z comes in now for the epilogue's output gate
+        if (tid < T) {
+            gl[tid] = gate_g(m.A_log[h], m.a_raw[tok(tid)], m.dt_bias[h]);
+            Bs[tid] = gate_beta(m.b_raw[tok(tid)]);
+        }
+        for (int e = tid; e < T * DV; e += kDecMultiThreads) {
+            const int t = e / DV, j = e % DV;
+            zs[t][j] = load1(static_cast<const Tin*>(m.z) + tok(t) * DV + j);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float run = 0.f;
+            for (int t = 0; t < T; ++t) {
+                run += gl[t];
+                Gs[t] = run;
+            }
+        }
+        // L2Norm of q_t and k_t in place, one token per wave
+        for (int t = wave; t < T; t += NW) {
+            float nq = 0.f, nk = 0.f;
+            for (int r = lane; r < DK; r += kWave) {
+                nq += qs[t][r] * qs[t][r];
+                nk += ks[t][r] * ks[t][r];
+            }
+            nq = group_sum<kWave>(nq);
+            nk = group_sum<kWave>(nk);
+            const float iq = frsq(nq + m.l2_eps), ik = frsq(nk + m.l2_eps);
+            for (int r = lane; r < DK; r += kWave) {
+                qs[t][r] *= iq;
+                ks[t][r] *= ik;
+            }
+        }
+        load_state();
+#pragma unroll
+        for (int t = 0; t < kMaxDecT; ++t)
+            if (t < T)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vv[t][j] = vs[t][c + j];
+        __syncthreads();
     }
-    __syncthreads();
 
     // this thread's RPT rows of a token vector (LDS, 16-byte reads where they fit)
     auto rows_of = [&](const float* vec, float (&out)[RPT]) __attribute__((always_inline)) {
@@ -422,7 +538,11 @@ decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const 
                     if (i <= t) yv += Pm[t][i] * U[i][j];
                 yo[j] = yv;
             }
-            if (r0 == 0) Vec4<Tout>::store(y + tok(t) * DV + c, yo);
+            if constexpr (!kFused) {
+                if (r0 == 0) Vec4<Tout>::store(y + tok(t) * DV + c, yo);
+            } else if (r0 == 0) {   // parked in this thread's own slots of vs (v_t is in vv now)
+                *reinterpret_cast<floatx4*>(&vs[t][c]) = floatx4{yo[0], yo[1], yo[2], yo[3]};
+            }
         }
     }
 
@@ -457,35 +577,58 @@ decode_multi_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const 
     if (steps)
         for (int t = 0; t < T; ++t) state_at(t, steps + ((size_t)(n * T + t) * H + h) * DK * DV);
     state_at(T - 1, S);
+    if constexpr (kFused) {
+        // the output gate, after the state pass (its registers are free by now): the TPR lanes of
+        // the first row group (an aligned group of wave 0) hold all DV columns of every y_t
+        if (r0 == 0) {
+            for (int t = 0; t < T; ++t) {
+                const floatx4 yv = *reinterpret_cast<const floatx4*>(&vs[t][c]);
+                const float yo[4] = {yv[0], yv[1], yv[2], yv[3]};
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ss += yo[j] * yo[j];
+                ss = group_sum<TPR>(ss);
+                const float inv = frsq(ss * (1.0f / DV) + m.rms_eps);
+                float ov[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    ov[j] = sigmoidf_(zs[t][c + j]) * ((1.0f + m.norm_w[c + j]) * (yo[j] * inv));
+                Vec4<Tout>::store(static_cast<Tout*>(m.o) + tok(t) * DV + c, ov);
+                if (y) Vec4<Tout>::store(y + tok(t) * DV + c, yo);
+            }
+        }
+    }
 }
 
-template <int DK, int DV, int MT>
-static void launch_dec_multi_t(const void* q, const void* k, const void* v, int in_bf16,
-                               const float* g, const float* beta, float* state, int heads, int T,
-                               int H, void* y, int y_bf16, float* steps, hipStream_t s) {
+template <int DK, int DV, int MT, bool kFused>
+static void launch_dec_multi_t(const MultiArgs& m, int in_bf16, int out_bf16, int heads,
+                               hipStream_t s) {
 #define GDN_DECM(TI, TO)                                                                        \
-    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, MT, TI, TO>), dim3(heads * kDecColSplit),       \
-                       dim3(kDecMultiThreads), 0, s, static_cast<const TI*>(q),                   \
-                       static_cast<const TI*>(k),                                                \
-                       static_cast<const TI*>(v), g, beta, state, static_cast<TO*>(y), steps, T, H)
-    if (in_bf16 && y_bf16) GDN_DECM(uint16_t, uint16_t);
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, MT, TI, TO, kFused>),                         \
+                       dim3(heads * kDecColSplit), dim3(kDecMultiThreads), 0, s, m)
+    if (in_bf16 && out_bf16) GDN_DECM(uint16_t, uint16_t);
     else if (in_bf16) GDN_DECM(uint16_t, float);
-    else if (y_bf16) GDN_DECM(float, uint16_t);
+    else if (out_bf16) GDN_DECM(float, uint16_t);
     else GDN_DECM(float, float);
 #undef GDN_DECM
 }
 
-template <int DK, int DV>
-static void launch_dec_multi(const void* q, const void* k, const void* v, int in_bf16,
-                             const float* g, const float* beta, float* state, int heads, int T,
-                             int H, void* y, int y_bf16, float* steps, hipStream_t s) {
+template <int DK, int DV, bool kFused>
+static void launch_dec_multi(const MultiArgs& m, int in_bf16, int out_bf16, int heads,
+                             hipStream_t s) {
     static_assert(kMaxDecodeTokens == 8, "token buckets");
-    if (T <= 2)
-        launch_dec_multi_t<DK, DV, 2>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s);
-    else if (T <= 4)
-        launch_dec_multi_t<DK, DV, 4>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s);
-    else
-        launch_dec_multi_t<DK, DV, 8>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s);
+    if (m.T <= 2) launch_dec_multi_t<DK, DV, 2, kFused>(m, in_bf16, out_bf16, heads, s);
+    else if (m.T <= 4) launch_dec_multi_t<DK, DV, 4, kFused>(m, in_bf16, out_bf16, heads, s);
+    else launch_dec_multi_t<DK, DV, 8, kFused>(m, in_bf16, out_bf16, heads, s);
+}
+
+template <bool kFused>
+static void launch_dec_multi_shape(const MultiArgs& m, int in_bf16, int out_bf16, int heads,
+                                   int dk, int dv, hipStream_t s) {
+    if (dk == 128 && dv == 128) launch_dec_multi<128, 128, kFused>(m, in_bf16, out_bf16, heads, s);
+    else if (dk == 128 && dv == 64) launch_dec_multi<128, 64, kFused>(m, in_bf16, out_bf16, heads, s);
+    else if (dk == 64 && dv == 128) launch_dec_multi<64, 128, kFused>(m, in_bf16, out_bf16, heads, s);
+    else launch_dec_multi<64, 64, kFused>(m, in_bf16, out_bf16, heads, s);
 }
 
 template <int DK, int DV>
@@ -543,13 +686,28 @@ hipError_t launch_decode_multi(const void* q, const void* k, const void* v, int 
                                hipStream_t s) {
     const int heads = N * H;
     if (heads == 0) return hipSuccess;
-#define GDN_DM(DK_, DV_) \
-    launch_dec_multi<DK_, DV_>(q, k, v, in_bf16, g, beta, state, heads, T, H, y, y_bf16, steps, s)
-    if (dk == 128 && dv == 128) GDN_DM(128, 128);
-    else if (dk == 128 && dv == 64) GDN_DM(128, 64);
-    else if (dk == 64 && dv == 128) GDN_DM(64, 128);
-    else GDN_DM(64, 64);
-#undef GDN_DM
+    MultiArgs m = {};
+    m.q = q; m.k = k; m.v = v; m.g = g; m.beta = beta;
+    m.state = state; m.y = y; m.steps = steps; m.T = T; m.H = H;
+    launch_dec_multi_shape<false>(m, in_bf16, y_bf16, heads, dk, dv, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_fused_multi(const DecodeFusedArgs& f, const void* hin, int T,
+                                     float* steps, int dk, int dv, hipStream_t s) {
+    const int heads = f.N * f.H;
+    if (heads == 0) return hipSuccess;
+    MultiArgs m = {};
+    for (int r = 0; r < 3; ++r) {
+        m.x[r] = f.x[r];
+        m.w[r] = f.w[r];
+    }
+    m.hin = hin; m.hout = f.conv_state; m.hC = f.hC;
+    m.a_raw = f.a_raw; m.b_raw = f.b_raw; m.A_log = f.A_log; m.dt_bias = f.dt_bias;
+    m.l2_eps = f.l2_eps;
+    m.z = f.z; m.norm_w = f.norm_w; m.rms_eps = f.rms_eps; m.o = f.o;
+    m.state = f.state; m.y = f.y; m.steps = steps; m.T = T; m.H = f.H;
+    launch_dec_multi_shape<true>(m, f.in_bf16, f.out_bf16, heads, dk, dv, s);
     return hipGetLastError();
 }
 

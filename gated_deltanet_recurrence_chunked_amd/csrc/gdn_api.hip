@@ -461,6 +461,59 @@ int gdn_fused_decode(const void* xq, const void* xk, const void* xv, int x_dtype
                       "gdn_fused_decode");
 }
 
+int gdn_fused_decode_multi(const void* xq, const void* xk, const void* xv, int x_dtype,
+                           const float* wq, const float* wk, const float* wv, int conv_k,
+                           const void* conv_state_in, void* conv_state_out, const float* a_raw,
+                           const float* b_raw, const float* A_log, const float* dt_bias,
+                           float l2_eps, float* state, const void* z, const float* norm_weight,
+                           float rms_eps, int N, int T, int H, int dk, int dv, void* o,
+                           int o_dtype, void* y, float* step_states, void* stream) {
+    GDN_REQUIRE(valid_dtype(x_dtype) && valid_dtype(o_dtype), GDN_ERR_DTYPE,
+                "x_dtype/o_dtype must be GDN_F32 or GDN_BF16");
+    GDN_REQUIRE(N >= 0 && H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
+                "need N >= 0, H >= 1 and dk, dv in {64, 128} (got N=%d H=%d dk=%d dv=%d)", N, H,
+                dk, dv);
+    GDN_REQUIRE(T >= 1 && T <= GDN_DECODE_MAX_TOKENS, GDN_ERR_SHAPE,
+                "T must be in 1..%d (got %d)", GDN_DECODE_MAX_TOKENS, T);
+    GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
+    GDN_REQUIRE(l2_eps >= 0.f && rms_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps and rms_eps must be >= 0");
+    GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
+    GDN_PTR(conv_state_in); GDN_PTR(conv_state_out);
+    GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
+    GDN_PTR(state); GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o); GDN_OPT_PTR(y);
+    GDN_OPT_PTR(step_states);
+    const int hC = H * (2 * dk + dv);
+    {
+        const size_t hb = (size_t)N * 3 * hC * (x_dtype == GDN_BF16 ? 2 : 4);
+        const char* i0 = static_cast<const char*>(conv_state_in);
+        const char* o0 = static_cast<const char*>(conv_state_out);
+        GDN_REQUIRE(i0 == o0 || i0 + hb <= o0 || o0 + hb <= i0, GDN_ERR_SHAPE,
+                    "conv_state_in and conv_state_out must be the same buffer or not overlap");
+    }
+    if (step_states) {
+        const char* a0 = reinterpret_cast<const char*>(state);
+        const char* b0 = reinterpret_cast<const char*>(step_states);
+        const size_t sb = (size_t)N * H * dk * dv * sizeof(float);
+        GDN_REQUIRE(a0 + sb <= b0 || b0 + sb * T <= a0, GDN_ERR_SHAPE,
+                    "step_states must not overlap state");
+    }
+    gdn::DecodeFusedArgs f;
+    f.x[0] = xq; f.x[1] = xk; f.x[2] = xv;
+    f.w[0] = wq; f.w[1] = wk; f.w[2] = wv;
+    f.conv_state = conv_state_out;
+    f.hC = hC;
+    f.a_raw = a_raw; f.b_raw = b_raw; f.A_log = A_log; f.dt_bias = dt_bias;
+    f.l2_eps = l2_eps;
+    f.state = state; f.z = z; f.norm_w = norm_weight; f.rms_eps = rms_eps;
+    f.o = o; f.y = y;
+    f.N = N; f.H = H;
+    f.in_bf16 = x_dtype == GDN_BF16;
+    f.out_bf16 = o_dtype == GDN_BF16;
+    return hip_status(gdn::launch_decode_fused_multi(f, conv_state_in, T, step_states, dk, dv,
+                                                     static_cast<hipStream_t>(stream)),
+                      "gdn_fused_decode_multi");
+}
+
 int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype, const float* norm_weight,
                     int ntok, int H, int dv, float eps, void* o, int o_dtype, void* stream) {
     GDN_REQUIRE(valid_dtype(y_dtype) && valid_dtype(z_dtype) && valid_dtype(o_dtype), GDN_ERR_DTYPE,

@@ -52,6 +52,10 @@ struct DecodeFusedArgs {
     int N, H, in_bf16, out_bf16;
 };
 hipError_t launch_decode_fused(const DecodeFusedArgs& f, int dk, int dv, hipStream_t s);
+// T <= kMaxDecodeTokens tokens per sequence through the fused step: the conv history is read
+// from hin and written to f.conv_state (which may equal hin); steps (nullable) as decode_multi
+hipError_t launch_decode_fused_multi(const DecodeFusedArgs& f, const void* hin, int T,
+                                     float* steps, int dk, int dv, hipStream_t s);
 // T <= kMaxDecodeTokens tokens per sequence; steps (nullable): the state after each token
 constexpr int kMaxDecodeTokens = 8;
 hipError_t launch_decode_multi(const void* q, const void* k, const void* v, int in_bf16,

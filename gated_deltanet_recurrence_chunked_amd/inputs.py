@@ -298,10 +298,11 @@ def make_stream_inputs(seed: int, N: int, H: int, prompt_lengths, steps: int, to
 
 
 def decode_layer_draws(seed: int, steps: int, N: int, H: int, dk: int = 128, dv: int = 128,
-                       bf16: bool = True) -> dict:
+                       bf16: bool = True, tokens: int = 1) -> dict:
     """Raw inputs of `steps` decode steps of the whole token mixer (the fused decode step),
     with the config-1 distributions: per step xq, xk [steps, N, H, dk], xv, z [steps, N, H, dv]
-    (bf16 bits, or float32 with bf16=False), a_raw, b_raw [steps, N, H]; conv taps
+    (bf16 bits, or float32 with bf16=False), a_raw, b_raw [steps, N, H] (with tokens > 1, a
+    [tokens] axis after N: T tokens per sequence per step); conv taps
     wq, wk, wv [H*d, 4] ~ N(0, 1/4); A_log, dt_bias [H]; norm_weight [dv] ~ N(0, 0.02);
     a carried conv history conv_state [N, 3, H*(2dk+dv)] ~ N(0,1) in the x dtype and a
     state [N, H, dk, dv] ~ N(0, 0.01) fp32."""
@@ -309,8 +310,8 @@ def decode_layer_draws(seed: int, steps: int, N: int, H: int, dk: int = 128, dv:
                     np.random.SeedSequence([SEED_TAG, 99, seed]).spawn(6)))
     rx, rg, rw, rz, rh, rs = (np.random.default_rng(kids[c]) for c in "xgwzhs")
     draw = _normal_bf16 if bf16 else _normal
-    lead = (steps, N, H)
-    out = dict(steps=steps, N=N, H=H, dk=dk, dv=dv, bf16=bf16)
+    lead = (steps, N, H) if tokens == 1 else (steps, N, tokens, H)
+    out = dict(steps=steps, N=N, H=H, dk=dk, dv=dv, bf16=bf16, tokens=tokens)
     out["xq"] = draw(rx, lead + (dk,))
     out["xk"] = draw(rx, lead + (dk,))
     out["xv"] = draw(rx, lead + (dv,))

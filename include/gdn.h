@@ -310,6 +310,33 @@ int gdn_fused_decode(const void* xq, const void* xk, const void* xv, int x_dtype
                      const void* z, const float* norm_weight, float rms_eps, int N, int H,
                      int dk, int dv, void* o, int o_dtype, void* y, void* stream);
 
+/*
+ * gdn_fused_decode_multi - T consecutive tokens per sequence through the fused decode step in
+ * one pass over each state (multi-token prediction verify from the projected streams): the
+ * conv over the carried history and the T new inputs, the gates, eqs. (1)-(4) as in
+ * gdn_decode_multi, and eq. (11) without W_o per token (sources as gdn_fused_decode and
+ * gdn_decode_multi).
+ *
+ *   xq, xk: [N, T, H, dk], xv, z: [N, T, H, dv] in x_dtype; a_raw, b_raw: [N, T, H] fp32;
+ *   wq, wk, wv, conv_k, A_log, dt_bias, l2_eps, norm_weight, rms_eps: as gdn_fused_decode;
+ *   conv_state_in: [N, 3, H*(2*dk+dv)] in x_dtype (layout of gdn_preprocess_stateful);
+ *   conv_state_out: same layout, the history after the T inputs; it may be conv_state_in
+ *       (updated in place) or a buffer that does not overlap it (keeping the old history
+ *       lets a caller rebuild the history after the first a accepted tokens);
+ *   state: [N, H, dk, dv] fp32, updated in place to the state after all T tokens;
+ *   step_states: NULL or [N, T, H, dk, dv] fp32, the state after each token (for rolling
+ *       back rejected drafts); must not overlap state;
+ *   o: [N, T, H, dv] in o_dtype; y: NULL or [N, T, H, dv] in o_dtype (before the gate).
+ *   1 <= T <= GDN_DECODE_MAX_TOKENS.
+ */
+int gdn_fused_decode_multi(const void* xq, const void* xk, const void* xv, int x_dtype,
+                           const float* wq, const float* wk, const float* wv, int conv_k,
+                           const void* conv_state_in, void* conv_state_out, const float* a_raw,
+                           const float* b_raw, const float* A_log, const float* dt_bias,
+                           float l2_eps, float* state, const void* z, const float* norm_weight,
+                           float rms_eps, int N, int T, int H, int dk, int dv, void* o,
+                           int o_dtype, void* y, float* step_states, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -184,3 +184,23 @@ def test_fused_validation(L):
     assert decode(ot=2) == 3
     assert decode(y=MIS) == 5
     assert decode(re=-1.0) == 2
+
+
+def test_fused_decode_multi_validation(L):
+    n = None
+    F = FAKE
+
+    def call(**kw):
+        a = dict(xq=F, xk=F, xv=F, xt=1, wq=F, wk=F, wv=F, ck=4, hin=F, hout=F, ar=F, br=F, al=F,
+                 dt=F, l2=1e-6, state=F, z=F, nw=F, re=1e-6, N=4, T=4, H=2, dk=128, dv=128, o=F,
+                 ot=1, y=n, st=n)
+        a.update(kw)
+        return L.gdn_fused_decode_multi(*a.values(), None)
+    for T in (0, 9):
+        assert call(T=T) == 2 and b"T must be" in L.gdn_last_error()
+    assert call(hin=n) == 1
+    st = call(hout=F + 64)                   # partial overlap of the conv histories
+    assert st == 2 and b"conv_state_in" in L.gdn_last_error()
+    st = call(st=F + 64)                      # step states over the state
+    assert st == 2 and b"step_states" in L.gdn_last_error()
+    assert call(xt=3) == 3

@@ -3,7 +3,9 @@
     and the output gate): against the oracle's eqs. (6)-(11), and element for element against
     the separate-kernel pipeline gdn_preprocess -> gdn_chunk_prefill -> gdn_output_gate;
   * gdn_fused_decode (one kernel per decode step from the projected streams, conv history and
-    state carried in place): against the oracle over each sequence's whole token stream.
+    state carried in place) and gdn_fused_decode_multi (T tokens per sequence per step, with
+    the state after each token on request): against the oracle over each sequence's whole
+    token stream.
 Sources: reading notes "Qwen3.8-Next 架构设计：评测、效率与训练稳定性", section 2.1.1,
 eqs. (1)-(11); the design summary "设计 LLM 架构" (causal depthwise short conv)."""
 import sys
@@ -140,3 +142,107 @@ def test_fused_decode_steps(gpu, N, H, dk, dv, xbf, obf, steps):
     print("  max slice rel L2:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
     # the carried history is raw input moved, bit for bit
     assert np.array_equal(C.host(conv_state), hist)
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+MULTI_CASES = [
+    # (N, H, dk, dv, x bf16, o bf16, T, steps, conv history out of place, step states)
+    (5, 2, 128, 128, True, True, 4, 3, False, False),
+    (3, 3, 64, 128, False, False, 2, 3, True, True),
+    (4, 1, 128, 64, True, False, 8, 2, True, False),
+    (2, 2, 64, 64, False, True, 3, 4, False, True),
+]
+
+
+@pytest.mark.parametrize("N,H,dk,dv,xbf,obf,T,steps,oop,want_steps", MULTI_CASES,
+                         ids=[f"N{c[0]}-H{c[1]}-dk{c[2]}-dv{c[3]}-T{c[6]}" for c in MULTI_CASES])
+def test_fused_decode_multi_steps(gpu, N, H, dk, dv, xbf, obf, T, steps, oop, want_steps):
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    _announce(f"fused multi-token decode N={N} H={H} dk={dk} dv={dv} T={T} steps={steps} "
+              f"x_bf16={xbf} o_bf16={obf} out_of_place={oop} step_states={want_steps}")
+    d = gi.decode_layer_draws(12, steps, N, H, dk, dv, bf16=xbf, tokens=T)
+    xd = lambda a: C.dev(a, xbf)                                               # noqa: E731
+    f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))            # noqa: E731
+    w = [f32(d[x]) for x in ("wq", "wk", "wv")]
+    hist = [xd(d["conv_state"])]
+    if oop:
+        hist.append(torch.empty_like(hist[0]))
+    state = f32(d["state"])
+    os_, ys, last_steps = [], [], None
+    for s in range(steps):
+        h_in = hist[s % len(hist)]
+        h_out = hist[(s + 1) % len(hist)]
+        o, y, st = gdn.gdn_fused_decode_multi(
+            xd(d["xq"][s]), xd(d["xk"][s]), xd(d["xv"][s]), *w, h_in, f32(d["a_raw"][s]),
+            f32(d["b_raw"][s]), f32(d["A_log"]), f32(d["dt_bias"]), state, xd(d["z"][s]),
+            f32(d["norm_weight"]), conv_state_out=h_out, l2_eps=C.L2_EPS, rms_eps=C.RMS_EPS,
+            o_dtype=torch.bfloat16 if obf else torch.float32, want_y=True,
+            step_states=True if want_steps else None)
+        os_.append(C.host(o))
+        ys.append(C.host(y))
+        if want_steps:
+            last_steps = C.host(st)
+    torch.cuda.synchronize()
+    final_hist = C.host(hist[steps % len(hist)])
+
+    # oracle: sequence n is its steps*T tokens in order, from the carried history and state
+    L = steps * T
+    perm = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1).reshape(N * L, *a.shape[3:]))  # noqa
+    f64 = lambda a: gi.as_f64(a, xbf)                                          # noqa: E731
+    cu = np.arange(0, N * L + 1, L).astype(np.int32)
+    q, k, v, hist_ref = oracle.preprocess_stateful(perm(f64(d["xq"])), perm(f64(d["xk"])),
+                                                   perm(f64(d["xv"])), d["wq"], d["wk"], d["wv"],
+                                                   cu, H, conv_state_in=f64(d["conv_state"]),
+                                                   l2_eps=C.L2_EPS)
+    _, al, be = oracle.gates(perm(d["a_raw"].astype(np.float64)), perm(d["b_raw"].astype(np.float64)),
+                             d["A_log"].astype(np.float64), d["dt_bias"].astype(np.float64))
+    S0 = d["state"].astype(np.float64)
+    y_ref, S_ref = oracle.recurrence(q, k, v, al, be, S0, cu)
+    o_ref = oracle.output_gate(y_ref, perm(f64(d["z"])), d["norm_weight"].astype(np.float64),
+                               C.RMS_EPS)
+    gather = lambda Ls: np.stack(Ls, axis=1).reshape(N * L, H, dv)             # noqa: E731
+    bf_path = xbf or obf
+    rep = dict(
+        y=C.assert_close("y", gather(ys), y_ref, bf_path, stored_bf16=obf, cu=cu, H=H),
+        o=C.assert_close("o", gather(os_), o_ref, bf_path, stored_bf16=obf, cu=cu, H=H),
+        S=C.assert_close("S", C.host(state), S_ref, bf_path, state=True))
+    assert np.array_equal(final_hist, hist_ref)
+    if want_steps:
+        # the state after token t of the last step = the oracle's state after that many tokens
+        # (the kernel evaluates the last token's state twice, for the step output and in place)
+        fin = C.host(state)
+        assert np.abs(last_steps[:, T - 1] - fin).max() <= 1e-6 * np.abs(fin).max()
+        for t in range(T - 1):
+            keep = (steps - 1) * T + t + 1
+            idx = np.concatenate([np.arange(n * L, n * L + keep) for n in range(N)])
+            cu_t = np.arange(0, N * keep + 1, keep).astype(np.int32)
+            _, S_t = oracle.recurrence(q[idx], k[idx], v[idx], al[idx], be[idx], S0, cu_t)
+            rep[f"S_step{t}"] = C.assert_close(f"state after token {t}", last_steps[:, t], S_t,
+                                               bf_path, state=True)
+    print("  max slice rel L2:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
+
+
+def test_fused_decode_multi_one_token_matches_fused_decode(gpu):
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    N, H = 6, 2
+    _announce(f"fused multi-token decode T=1 vs fused decode N={N} H={H}")
+    d = gi.decode_layer_draws(13, 1, N, H, bf16=False)
+    f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))            # noqa: E731
+    args = lambda s: [f32(d[x][0]) for x in ("xq", "xk", "xv")] + [f32(d[x]) for x in ("wq", "wk", "wv")]  # noqa
+    h1, h2 = f32(d["conv_state"]), f32(d["conv_state"])
+    s1, s2 = f32(d["state"]), f32(d["state"])
+    o1 = gdn.gdn_fused_decode(*args(0), h1, f32(d["a_raw"][0]), f32(d["b_raw"][0]),
+                              f32(d["A_log"]), f32(d["dt_bias"]), s1, f32(d["z"][0]),
+                              f32(d["norm_weight"]))
+    xs = [f32(d[x][0]).view(N, 1, H, -1) for x in ("xq", "xk", "xv")]
+    o2, _, _ = gdn.gdn_fused_decode_multi(*xs, *[f32(d[x]) for x in ("wq", "wk", "wv")], h2,
+                                          f32(d["a_raw"][0]).view(N, 1, H),
+                                          f32(d["b_raw"][0]).view(N, 1, H), f32(d["A_log"]),
+                                          f32(d["dt_bias"]), s2,
+                                          f32(d["z"][0]).view(N, 1, H, -1), f32(d["norm_weight"]))
+    torch.cuda.synchronize()
+    assert np.abs(C.host(o1) - C.host(o2)[:, 0]).max() < 1e-5
+    assert np.abs(C.host(s1) - C.host(s2)).max() < 1e-5
+    assert torch.equal(h1, h2)
