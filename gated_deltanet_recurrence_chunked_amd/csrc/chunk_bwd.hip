@@ -27,6 +27,7 @@
 // Columns of dv are independent in the state recursion (as in the forward), which is what the
 // slices use; the terms that mix columns are sums over them, so slice shares add up.
 #include "gdn_device.h"
+#include "gdn_inverse.h"
 #include "gdn_launch.h"
 
 namespace gdn {
@@ -245,20 +246,11 @@ __global__ void __launch_bounds__(kFinT) bwd_ap_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    // T = (I + A)^{-1}: thread c forward-substitutes column c, held in registers (fully
-    // unrolled, so every index is static); rows above c come out zero.
-    if (tid < kC) {
-        float x[kC];
-#pragma unroll
-        for (int r = 0; r < kC; ++r) {
-            float acc = r == tid ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) acc -= A[r][i] * x[i];
-            x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < kC; ++r) a.T[ch * kC * kC + r * kC + tid] = x[r];
-    }
+    // T = (I + A)^{-1} by one wave (16x16 diagonal blocks by DPP substitution, then fp32 MFMA
+    // levels), in place in LDS, then written out by the whole workgroup
+    if (tid < kWave) unit_lower_inverse64<kC + 1, true>(&A[0][0]);
+    __syncthreads();
+    for (int e = tid; e < kC * kC; e += kFinT) a.T[ch * kC * kC + e] = A[e / kC][e % kC];
 }
 
 // ------------------------------------------------------------------ states: forward sweep

@@ -15,6 +15,7 @@
 // factor can overflow); a scan per (sequence, head, 16-column slice of dv) then needs plain
 // products only.
 #include "gdn_device.h"
+#include "gdn_inverse.h"
 #include "gdn_launch.h"
 
 namespace gdn {
@@ -172,19 +173,11 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
     }
     if (tid < DK) a.eC[ch * DK + tid] = fexp(Gc[last][tid]);
     __syncthreads();
-    // T = (I + A)^{-1}, one column per lane, forward substitution unrolled in registers
-    if (tid < kC) {
-        float x[kC];
-#pragma unroll
-        for (int r = 0; r < kC; ++r) {
-            float acc = r == tid ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) acc -= A[r][i] * x[i];
-            x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < kC; ++r) a.T[ch * kC * kC + r * kC + tid] = x[r];
-    }
+    // T = (I + A)^{-1} by one wave (16x16 diagonal blocks by DPP substitution, then fp32 MFMA
+    // levels), in place in LDS, then written out by the whole workgroup
+    if (tid < kWave) unit_lower_inverse64<kC + 1, true>(&A[0][0]);
+    __syncthreads();
+    for (int e = tid; e < kC * kC; e += kPT) a.T[ch * kC * kC + e] = A[e / kC][e % kC];
 }
 
 // ------------------------------------------------------------------ scan per (seq, head, slice)
