@@ -218,21 +218,53 @@ __global__ void __launch_bounds__(kST) kda_scan_kernel(KdaArgs a) {
         const int d = e / kSL, j = e % kSL;
         S[d][j] = a.S0 ? a.S0[st_off + (size_t)d * dv + j0 + j] : 0.f;
     }
+    // The next chunk's tiles are fetched into registers while this chunk computes (16-byte
+    // global loads, kST threads: 2 of each [64][DK] tile, 1 of each [64][64] tile per thread).
+    constexpr int NDK = kC * DK / 4 / kST;             // float4 of a [64][DK] tile per thread
+    struct Pref {
+        float4 kg[NDK], qg[NDK], kc[NDK], t, p;
+        float v, ec, bt;
+    };
+    auto fetch = [&](int t0, int n, size_t ch, Pref& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) {
+            const int u = tid + i * kST;
+            f.kg[i] = reinterpret_cast<const float4*>(a.Kg + ch * kC * DK)[u];
+            f.qg[i] = reinterpret_cast<const float4*>(a.Qg + ch * kC * DK)[u];
+            f.kc[i] = reinterpret_cast<const float4*>(a.Kc + ch * kC * DK)[u];
+        }
+        f.t = reinterpret_cast<const float4*>(a.T + ch * kC * kC)[tid];
+        f.p = reinterpret_cast<const float4*>(a.P + ch * kC * kC)[tid];
+        const int r = tid / kSL, j = tid % kSL;   // kC * kSL == kST: one V element per thread
+        f.v = r < n ? ldx<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
+        f.ec = tid < DK ? a.eC[ch * DK + tid] : 0.f;
+        f.bt = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    };
+    auto put4 = [](float* d, float4 x) __attribute__((always_inline)) {
+        d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+    };
+    auto stash = [&](const Pref& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) {
+            const int u = tid + i * kST, r = u / (DK / 4), c4 = (u % (DK / 4)) * 4;
+            put4(&Kg[r][c4], f.kg[i]);
+            put4(&Qg[r][c4], f.qg[i]);
+            put4(&Kc[r][c4], f.kc[i]);
+        }
+        put4(&T[tid / (kC / 4)][(tid % (kC / 4)) * 4], f.t);
+        put4(&P[tid / (kC / 4)][(tid % (kC / 4)) * 4], f.p);
+        R[tid / kSL][tid % kSL] = f.v;
+        if (tid < DK) eC[tid] = f.ec;
+        if (tid < kC) Bt[tid] = f.bt;
+    };
+    static_assert(kC * kSL == kST && kC * kC / 4 == kST, "one T, P float4 and one V element per thread");
+    Pref f;
+    if (lo < hi) fetch(lo, min(kC, hi - lo), (size_t)cbase * H + h, f);
     for (int t0 = lo, c = cbase; t0 < hi; t0 += kC, ++c) {
         const int n = min(kC, hi - t0);
-        const size_t ch = (size_t)c * H + h;
         __syncthreads();
-        kda_load_tile<kST>(a.Kg + ch * kC * DK, kC, DK, &Kg[0][0], DK + 1);
-        kda_load_tile<kST>(a.Qg + ch * kC * DK, kC, DK, &Qg[0][0], DK + 1);
-        kda_load_tile<kST>(a.Kc + ch * kC * DK, kC, DK, &Kc[0][0], DK + 1);
-        kda_load_tile<kST>(a.T + ch * kC * kC, kC, kC, &T[0][0], kC + 1);
-        kda_load_tile<kST>(a.P + ch * kC * kC, kC, kC, &P[0][0], kC + 1);
-        for (int e = tid; e < kC * kSL; e += kST) {   // V into R, zero past n
-            const int r = e / kSL, j = e % kSL;
-            R[r][j] = r < n ? ldx<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
-        }
-        if (tid < DK) eC[tid] = a.eC[ch * DK + tid];
-        if (tid < kC) Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        stash(f);
+        if (t0 + kC < hi) fetch(t0 + kC, min(kC, hi - t0 - kC), (size_t)(c + 1) * H + h, f);
         __syncthreads();
         if (wave < 4) {   // R = beta o (V - Kg S)
             const floatx4 ks = mma_f32_tile(&Kg[wave * 16][0], DK + 1, 1, &S[0][0], PR, 1, DK, zero);
