@@ -278,6 +278,67 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
         const int d = e / SL, j = e % SL;
         S[d][j] = a.S0 ? a.S0[st_off + (size_t)d * dv + j0 + j] : 0.f;
     }
+    // The next chunk's K rows, T, V slice and gate rows are fetched into registers while this
+    // chunk computes (16-byte loads; K stays in its input type until it is written to LDS).
+    constexpr int KPER = 16 / sizeof(Tin), KUNITS = kC * DK / KPER;
+    constexpr int KU = (KUNITS + kBT - 1) / kBT, VE = kC * SL / kBT;
+    static_assert(kC * kC / 4 == kBT && VE >= 1, "one T float4 per thread, whole V elements");
+    struct Pref {
+        gdn_u32x4 k[KU];
+        float4 t;
+        float v[VE], g, gl, b;
+    };
+    auto fetch = [&](int t0, int n, size_t ch, Pref& f) __attribute__((always_inline)) {
+        const Tin* kp = static_cast<const Tin*>(a.k);
+#pragma unroll
+        for (int i = 0; i < KU; ++i) {
+            const int u = tid + i * kBT, r = u / (DK / KPER), c0 = (u % (DK / KPER)) * KPER;
+            f.k[i] = gdn_u32x4{0u, 0u, 0u, 0u};
+            if (u < KUNITS && r < n)
+                f.k[i] = *reinterpret_cast<const gdn_u32x4*>(kp + ((size_t)(t0 + r) * H + h) * DK + c0);
+        }
+        f.t = reinterpret_cast<const float4*>(a.T + ch * kC * kC)[tid];
+#pragma unroll
+        for (int i = 0; i < VE; ++i) {
+            const int e = tid + i * kBT, r = e / SL, j = e % SL;
+            f.v[i] = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
+        }
+        f.g = tid < kC ? a.G[ch * kC + tid] : 0.f;
+        f.gl = a.G[ch * kC + n - 1];
+        f.b = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    };
+    auto stash = [&](const Pref& f, int n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < KU; ++i) {
+            const int u = tid + i * kBT, r = u / (DK / KPER), c0 = (u % (DK / KPER)) * KPER;
+            if (u < KUNITS) {
+                if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        Ks[r][c0 + 2 * q] = __uint_as_float(f.k[i][q] << 16);
+                        Ks[r][c0 + 2 * q + 1] = __uint_as_float(f.k[i][q] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) Ks[r][c0 + q] = __uint_as_float(f.k[i][q]);
+                }
+            }
+        }
+        const int tr = tid / (kC / 4), tc = (tid % (kC / 4)) * 4;
+        T[tr][tc] = f.t.x; T[tr][tc + 1] = f.t.y; T[tr][tc + 2] = f.t.z; T[tr][tc + 3] = f.t.w;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) {
+            const int e = tid + i * kBT;
+            R[e / SL][e % SL] = f.v[i];
+        }
+        if (tid < kC) {
+            gam[tid] = expf(f.g);
+            w[tid] = tid < n ? expf(f.gl - f.g) : 0.f;
+            Bt[tid] = f.b;
+        }
+    };
+    Pref f;
+    if (lo < hi) fetch(lo, min(kC, hi - lo), (size_t)cbase * H + h, f);
     for (int t0 = lo, c = cbase; t0 < hi; t0 += kC, ++c) {
         const int n = min(kC, hi - t0);
         const size_t ch = (size_t)c * H + h;
@@ -287,18 +348,8 @@ __global__ void __launch_bounds__(kBT) bwd_states_kernel(BwdArgs a) {
             *reinterpret_cast<float4*>(a.Sc + ch * DK * dv + (size_t)d * dv + j0 + j) =
                 make_float4(S[d][j], S[d][j + 1], S[d][j + 2], S[d][j + 3]);
         }
-        load_rows<DK, Tin>(a.k, t0, n, H, h, Ks);
-        load_tile64<kBT>(a.T + ch * kC * kC, T);
-        for (int e = tid; e < kC * SL; e += kBT) {   // V, zero past n
-            const int r = e / SL, j = e % SL;
-            R[r][j] = r < n ? ld<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
-        }
-        if (tid < kC) {
-            const float* Gc = a.G + ch * kC;
-            gam[tid] = expf(Gc[tid]);
-            w[tid] = tid < n ? expf(Gc[n - 1] - Gc[tid]) : 0.f;
-            Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
-        }
+        stash(f, n);
+        if (t0 + kC < hi) fetch(t0 + kC, min(kC, hi - t0 - kC), (size_t)(c + 1) * H + h, f);
         __syncthreads();
         if (wave < 4 * CT) {   // R = beta o (V - gamma o K S)
             const int rt = wave % 4, ct = wave / 4;
