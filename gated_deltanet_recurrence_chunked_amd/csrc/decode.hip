@@ -258,14 +258,22 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(DecodeFusedAr
 // sums). All 2T column reductions run against the one state in registers, so the state is
 // read once and written once however many tokens the step carries. Decays are exp of
 // differences of the running sum (never above 1).
-// One 512-thread workgroup per state (two waves per SIMD): a thread holds dk/16 contiguous
-// rows of 4 columns, half of what the single-token kernel's threads hold, which leaves
-// registers for the per-token arrays. Column sums: in registers over a thread's rows, by
-// shuffles over the wave's row groups, then once per (value, column) across the waves in LDS.
+// One 256-thread workgroup per state (one wave per SIMD; three per CU for T <= 4): a thread
+// holds dk/8 contiguous rows of 4 columns, as the single-token kernel's threads do. Measured
+// against 512-thread workgroups (two per CU), which leave more registers per thread for the
+// per-token arrays: 424-432 against 534 us per step at T = 8, within the run-to-run spread
+// (about 10 us) at T = 2 and 4 (N = 256, H = 32): more workgroups in flight per CU hide more of
+// the state's load latency, even with a few registers spilled at T = 4. Column sums: in registers over a thread's rows,
+// by shuffles over the wave's row groups, then once per (value, column) across the waves in LDS.
 // kDecColSplit > 1 would give each workgroup 1/kDecColSplit of the columns (a column's sums
 // and update need only that column); measured slower at split 2 (the per-workgroup token
 // work is repeated and each workgroup moves half the bytes).
-constexpr int kDecMultiThreads = 512;
+// The fused variant keeps 512-thread workgroups (two per CU at T <= 4): its front end has
+// 2 dk + dv channels to convolve, one per thread (276 us at T = 4 against 280 with 256).
+template <bool kFused> constexpr int dm_threads() { return kFused ? 512 : 256; }
+template <bool kFused, int kMaxDecT> constexpr int dm_min_waves() {
+    return kMaxDecT <= 4 ? (kFused ? 4 : 3) : 2;
+}
 constexpr int kDecColSplit = 1;
 
 // With kFused the step starts from the projected streams instead of q, k, v, g, beta: one
@@ -296,7 +304,7 @@ struct MultiArgs {
 // kMaxDecT (2, 4 or 8) bounds T at compile time: the per-token register arrays are sized by
 // it, so a short step does not pay the registers (and occupancy) of the longest one.
 template <int DK, int DV, int kMaxDecT, typename Tin, typename Tout, bool kFused>
-__global__ void __launch_bounds__(kDecMultiThreads, kMaxDecT <= 4 ? 4 : 2)
+__global__ void __launch_bounds__(dm_threads<kFused>(), (dm_min_waves<kFused, kMaxDecT>()))
 decode_multi_kernel(MultiArgs m) {
     const Tin* __restrict__ q = static_cast<const Tin*>(m.q);
     const Tin* __restrict__ k = static_cast<const Tin*>(m.k);
@@ -307,6 +315,7 @@ decode_multi_kernel(MultiArgs m) {
     const int T = m.T, H = m.H;
     constexpr int DVS = DV / kDecColSplit;       // columns of this workgroup
     constexpr int TPR = DVS / 4;                 // threads per state row
+    constexpr int kDecMultiThreads = dm_threads<kFused>();
     constexpr int RG = kDecMultiThreads / TPR;   // row groups
     constexpr int RPT = DK / RG;                 // contiguous rows per thread
     constexpr int NW = kDecMultiThreads / kWave;
@@ -445,17 +454,14 @@ decode_multi_kernel(MultiArgs m) {
         __syncthreads();
     }
 
-    // this thread's RPT rows of a token vector (LDS, 16-byte reads where they fit)
-    auto rows_of = [&](const float* vec, float (&out)[RPT]) __attribute__((always_inline)) {
+    // rows r0+i0 .. r0+i0+3 of a token vector (LDS; one 16-byte read when they fit)
+    auto row4 = [&](const float* vec, int i0, float (&out)[4]) __attribute__((always_inline)) {
         if constexpr (RPT % 4 == 0) {
-#pragma unroll
-            for (int i = 0; i < RPT; i += 4) {
-                const floatx4 x = *reinterpret_cast<const floatx4*>(vec + r0 + i);
-                out[i] = x.x; out[i + 1] = x.y; out[i + 2] = x.z; out[i + 3] = x.w;
-            }
+            const floatx4 x = *reinterpret_cast<const floatx4*>(vec + r0 + i0);
+            out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
         } else {
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) out[i] = vec[r0 + i];
+            for (int i = 0; i < 4; ++i) out[i] = i0 + i < RPT ? vec[r0 + i0 + i] : 0.f;
         }
     };
 
@@ -483,17 +489,20 @@ decode_multi_kernel(MultiArgs m) {
 #pragma unroll
     for (int t = 0; t < kMaxDecT; ++t) {
         if (t < T) {
-            float kr[RPT], qr[RPT];
-            rows_of(ks[t], kr);
-            rows_of(qs[t], qr);
             float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < RPT; ++i)
+            for (int i0 = 0; i0 < RPT; i0 += 4) {   // 4 rows of k_t and q_t at a time
+                float kr[4], qr[4];
+                row4(ks[t], i0, kr);
+                row4(qs[t], i0, qr);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pk[j] += s[i][j] * kr[i];
-                    pq[j] += s[i][j] * qr[i];
-                }
+                for (int i = 0; i < 4 && i0 + i < RPT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pk[j] += s[i0 + i][j] * kr[i];
+                        pq[j] += s[i0 + i][j] * qr[i];
+                    }
+            }
 #pragma unroll
             for (int o = TPR; o < kWave; o <<= 1)
 #pragma unroll
@@ -558,14 +567,17 @@ decode_multi_kernel(MultiArgs m) {
 #pragma unroll
         for (int i = 0; i < kMaxDecT; ++i) {
             if (i <= t) {
-                float kr[RPT];
-                rows_of(ks[i], kr);
                 const float d = Dm[t][i];
 #pragma unroll
-                for (int r = 0; r < RPT; ++r) {
-                    const float dk = d * kr[r];
+                for (int r0_ = 0; r0_ < RPT; r0_ += 4) {
+                    float kr[4];
+                    row4(ks[i], r0_, kr);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) o[r][j] += dk * U[i][j];
+                    for (int r = 0; r < 4 && r0_ + r < RPT; ++r) {
+                        const float dk = d * kr[r];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) o[r0_ + r][j] += dk * U[i][j];
+                    }
                 }
             }
         }
@@ -605,7 +617,7 @@ static void launch_dec_multi_t(const MultiArgs& m, int in_bf16, int out_bf16, in
                                hipStream_t s) {
 #define GDN_DECM(TI, TO)                                                                        \
     hipLaunchKernelGGL((decode_multi_kernel<DK, DV, MT, TI, TO, kFused>),                         \
-                       dim3(heads * kDecColSplit), dim3(kDecMultiThreads), 0, s, m)
+                       dim3(heads * kDecColSplit), dim3(dm_threads<kFused>()), 0, s, m)
     if (in_bf16 && out_bf16) GDN_DECM(uint16_t, uint16_t);
     else if (in_bf16) GDN_DECM(uint16_t, float);
     else if (out_bf16) GDN_DECM(float, uint16_t);
