@@ -246,3 +246,92 @@ def test_fused_decode_multi_one_token_matches_fused_decode(gpu):
     assert np.abs(C.host(o1) - C.host(o2)[:, 0]).max() < 1e-5
     assert np.abs(C.host(s1) - C.host(s2)).max() < 1e-5
     assert torch.equal(h1, h2)
+
+
+# ----------------------------------------------------------------------------- full-size decode
+def _subset_stream(d, seqs, heads, xbf):
+    """The draws of decode_layer_draws restricted to some sequences and heads, as float64, with
+    the token axes flattened per sequence (sequence-major): the oracle's packed streams."""
+    H, dk, dv = d["H"], d["dk"], d["dv"]
+    f64 = lambda a: gi.as_f64(np.ascontiguousarray(a), xbf)                    # noqa: E731
+    multi = d["tokens"] > 1
+
+    def pick(a, tail):   # [steps, N, (T,) H, ...] -> [ns * steps * T, nh, ...]
+        a = a[:, seqs][:, :, :, heads] if multi else a[:, seqs][:, :, heads]
+        if not multi:
+            a = a[:, :, None]
+        a = np.swapaxes(a, 0, 1)                          # [ns, steps, T, nh, ...]
+        return a.reshape((-1, len(heads)) + tail)
+
+    out = dict(xq=pick(f64(d["xq"]), (dk,)), xk=pick(f64(d["xk"]), (dk,)),
+               xv=pick(f64(d["xv"]), (dv,)), z=pick(f64(d["z"]), (dv,)),
+               a_raw=pick(d["a_raw"].astype(np.float64), ()),
+               b_raw=pick(d["b_raw"].astype(np.float64), ()))
+    for key, dd in (("wq", dk), ("wk", dk), ("wv", dv)):
+        out[key] = d[key].astype(np.float64).reshape(H, dd, 4)[heads].reshape(-1, 4)
+    cs = f64(d["conv_state"])[seqs]                                           # [ns, 3, C]
+    parts, off = [], 0
+    for dd in (dk, dk, dv):
+        blk = cs[:, :, off:off + H * dd].reshape(len(seqs), 3, H, dd)[:, :, heads]
+        parts.append(blk.reshape(len(seqs), 3, -1))
+        off += H * dd
+    out["conv_state"] = np.concatenate(parts, axis=2)
+    out["state"] = d["state"].astype(np.float64)[seqs][:, heads]
+    out["A_log"] = d["A_log"].astype(np.float64)[heads]
+    out["dt_bias"] = d["dt_bias"].astype(np.float64)[heads]
+    return out
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", [1, 4])
+def test_fused_decode_full_size(gpu, T):
+    """The fused decode step at N=256, H=32, d=128 (bf16 x, z, o), as the benchmark runs it, over
+    2 steps; sampled (sequence, head) slices against the oracle."""
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    N, H, steps = 256, 32, 2
+    _announce(f"fused decode full size N={N} H={H} d=128 T={T} steps={steps}")
+    d = gi.decode_layer_draws(21, steps, N, H, tokens=T)
+    bf = lambda a: C.dev(a, True)                                              # noqa: E731
+    f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))            # noqa: E731
+    w = [f32(d[x]) for x in ("wq", "wk", "wv")]
+    hist, state = bf(d["conv_state"]), f32(d["state"])
+    os_ = []
+    for s in range(steps):
+        args = (bf(d["xq"][s]), bf(d["xk"][s]), bf(d["xv"][s]), *w, hist, f32(d["a_raw"][s]),
+                f32(d["b_raw"][s]), f32(d["A_log"]), f32(d["dt_bias"]), state, bf(d["z"][s]),
+                f32(d["norm_weight"]))
+        if T == 1:
+            o = gdn.gdn_fused_decode(*args, l2_eps=C.L2_EPS, rms_eps=C.RMS_EPS)
+        else:
+            o, _, _ = gdn.gdn_fused_decode_multi(*args, l2_eps=C.L2_EPS, rms_eps=C.RMS_EPS)
+        os_.append(o)
+    torch.cuda.synchronize()
+    seqs, heads = [0, 101, 255], [0, 17, 31]
+    sub = _subset_stream(d, seqs, heads, True)
+    L = steps * T
+    cu = np.arange(0, len(seqs) * L + 1, L).astype(np.int32)
+    q, k, v, hist_ref = oracle.preprocess_stateful(sub["xq"], sub["xk"], sub["xv"], sub["wq"],
+                                                   sub["wk"], sub["wv"], cu, len(heads),
+                                                   conv_state_in=sub["conv_state"],
+                                                   l2_eps=C.L2_EPS)
+    _, al, be = oracle.gates(sub["a_raw"], sub["b_raw"], sub["A_log"], sub["dt_bias"])
+    y_ref, S_ref = oracle.recurrence(q, k, v, al, be, sub["state"], cu)
+    o_ref = oracle.output_gate(y_ref, sub["z"], d["norm_weight"].astype(np.float64), C.RMS_EPS)
+    # the GPU's o for the sampled slices, in the oracle's order
+    got, oh = [], [C.host(o) for o in os_]
+    for n in seqs:
+        for s in range(steps):
+            got.append(oh[s][n][heads] if T == 1 else oh[s][n][:, heads])
+    got = np.concatenate([g.reshape(-1, len(heads), 128) for g in got], axis=0)
+    rep = dict(o=C.assert_close("o", got, o_ref, True, stored_bf16=True, cu=cu, H=len(heads)),
+               S=C.assert_close("S", C.host(state)[seqs][:, heads], S_ref, True, state=True))
+    # the history of the sampled slices moved on by the steps' inputs, bit for bit
+    hg = C.host(hist)[seqs]
+    parts, off = [], 0
+    for dd in (128, 128, 128):
+        blk = hg[:, :, off:off + H * dd].reshape(len(seqs), 3, H, dd)[:, :, heads]
+        parts.append(blk.reshape(len(seqs), 3, -1))
+        off += H * dd
+    assert np.array_equal(np.concatenate(parts, axis=2), hist_ref)
+    print("  max slice rel L2:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
