@@ -133,21 +133,48 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
     }
     __syncthreads();
     const size_t ch = (size_t)c * H + h;
-    // A (strictly lower) and P (lower with the diagonal): decays per channel and pair. Only the
-    // 64*65/2 pairs i <= r are enumerated (pair p -> row r with r(r+1)/2 <= p, column
-    // i = p - r(r+1)/2), so no lane idles on the upper triangle; that one is zeroed apart.
+    // A (strictly lower) and P (lower with the diagonal). For a 16x16 tile below the diagonal
+    // (row block rt > column block it), with m = 16 rt the first row of the row block,
+    // e^{Gc_r - Gc_i} = e^{Gc_r - Gc_m} e^{Gc_m - Gc_i} with both exponents <= 0 (Gc falls along
+    // the rows), so the tile is a plain product of decayed operands: one wave per tile on the
+    // fp32 matrix core, the two exponentials formed as the operands are read (no overflow, and
+    // no bound on g needed). The four diagonal tiles' 136 pairs each are formed element by
+    // element; the tiles above are zero.
+    const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
     for (int e = tid; e < kC * kC; e += kPT) {
         const int r = e / kC, i = e % kC;
-        if (i > r) {
+        if ((i >> 4) > (r >> 4)) {
             A[r][i] = 0.f;
             a.P[ch * kC * kC + e] = 0.f;
         }
     }
-    for (int p = tid; p < kC * (kC + 1) / 2; p += kPT) {
-        int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-        while (r * (r + 1) / 2 > p) --r;                 // guard the float root
-        while ((r + 1) * (r + 2) / 2 <= p) ++r;
-        const int i = p - r * (r + 1) / 2;
+    if (wave < 6) {
+        const int rt = wave < 1 ? 1 : (wave < 3 ? 2 : 3);
+        const int it = wave - (rt * (rt - 1)) / 2;          // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+        const int m = 16 * rt, r = 16 * rt + lc, i = 16 * it + lc;
+        floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 4) {
+            const int d = k0 + lg;
+            const float gm = Gc[m][d];
+            const float ea = fexp(Gc[r][d] - gm), eb = fexp(gm - Gc[i][d]);
+            const float b = Ks[i][d] * eb;
+            ak = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[r][d] * ea, b, ak, 0, 0, 0);
+            aq = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[r][d] * ea, b, aq, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {   // accumulator element u: row 4 lg + u, column lc
+            const int rr = 16 * rt + 4 * lg + u, ii = 16 * it + lc;
+            A[rr][ii] = Bt[rr] * ak[u];        // rows past n: K, Q rows are zero there
+            a.P[ch * kC * kC + rr * kC + ii] = aq[u];
+        }
+    }
+    for (int p = tid; p < 4 * 136; p += kPT) {   // the diagonal tiles, pair by pair
+        const int b = p / 136, q = p % 136;
+        int rr = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+        while (rr * (rr + 1) / 2 > q) --rr;                 // guard the float root
+        while ((rr + 1) * (rr + 2) / 2 <= q) ++rr;
+        const int r = 16 * b + rr, i = 16 * b + q - rr * (rr + 1) / 2;
         float kk = 0.f, qk = 0.f;
         if (r < n) {
 #pragma unroll 4
@@ -160,6 +187,14 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
         }
         A[r][i] = i < r ? Bt[r] * kk : 0.f;
         a.P[ch * kC * kC + r * kC + i] = qk;
+    }
+    // the diagonal tiles' upper halves
+    for (int e = tid; e < 4 * 256; e += kPT) {
+        const int b = e / 256, r = 16 * b + (e % 256) / 16, i = 16 * b + e % 16;
+        if (i > r) {
+            A[r][i] = 0.f;
+            a.P[ch * kC * kC + r * kC + i] = 0.f;
+        }
     }
     // decayed operands of the scan
     const int last = n - 1;

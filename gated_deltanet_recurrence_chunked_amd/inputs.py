@@ -235,13 +235,15 @@ def make_inputs(cfg: int, seed: int = 0, **ov) -> dict:
     return out
 
 
-def kda_log_decay_draw(seed: int, ntok: int, H: int, dk: int) -> np.ndarray:
+def kda_log_decay_draw(seed: int, ntok: int, H: int, dk: int, mean: float = -2.0,
+                       cap: float = 5.0) -> np.ndarray:
     """Per-channel log-decays g [ntok, H, dk] fp32 for the per-channel-decay variant:
-    g = -min(exp(N(-2, 1)), 5), i.e. mostly mild decays (median alpha ~ 0.87) with a tail
-    down to the lower bound -5 that the KDA-style gate imposes."""
+    g = -min(exp(N(mean, 1)), cap). The default is mostly mild decays (median alpha ~ 0.87)
+    with a tail down to the lower bound -5 that the KDA-style gate imposes; mean=1, cap=60
+    gives steep decays (median alpha ~ 0.07, some channels forgotten within one token)."""
     rng = np.random.default_rng(np.random.SeedSequence([SEED_TAG, 55, seed]))
-    x = _normal(rng, (ntok, H, dk)).astype(np.float64) - 2.0
-    return (-np.minimum(np.exp(x), 5.0)).astype(np.float32)
+    x = _normal(rng, (ntok, H, dk)).astype(np.float64) + mean
+    return (-np.minimum(np.exp(x), cap)).astype(np.float32)
 
 
 def grad_draws(seed: int, ntok: int, num_seqs: int, H: int, dk: int, dv: int,

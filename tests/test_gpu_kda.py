@@ -62,6 +62,16 @@ def test_kda_fp32_ragged(gpu, dims):
     _case(inp, g, bf16=False, y_dtype="f32")
 
 
+def test_kda_steep_decays(gpu):
+    """Log-decays far below the KDA bound (down to -60 per token): the kernels form only
+    exponentials of non-positive differences, so nothing overflows however steep the decay."""
+    _announce("kda fp32 inputs with steep per-channel decays, lengths [130, 64, 7] H=2 d=128")
+    inp = gi.make_inputs(0, seed=10, H=2, lengths=[130, 64, 7], d=128)
+    g = gi.kda_log_decay_draw(10, inp["shape"].ntok, 2, 128, mean=1.0, cap=60.0)
+    assert g.min() < -30.0
+    _case(inp, g, False, "f32")
+
+
 def test_kda_bf16_long(gpu):
     _announce("kda bf16 inputs B=1 H=2 T=1000 d=128, S0, bf16 y")
     inp = gi.make_inputs(2, seed=9, H=2, T=1000)
