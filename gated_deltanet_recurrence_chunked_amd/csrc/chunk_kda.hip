@@ -10,10 +10,10 @@
 //   P[r,i] = sum_c q_r[c] k_i[c] e^{Gc[r][c]-Gc[i][c]}          (i <= r)
 //   U = T (beta o (V - Kg S)),  Y = Qg S + P U,  S' = e^{Gc[C]} o S + Kc^T U
 // with Kg = K o e^{Gc}, Qg = Q o e^{Gc} and Kc = K o e^{Gc[C] - Gc} (every exponent <= 0).
-// Two kernels: a per-(chunk, head) prep forms T, P, Kg, Qg, Kc and e^{Gc[C]} into the
-// workspace (the pair decays are exponentials of differences, element by element, so no
-// factor can overflow); a scan per (sequence, head, 16-column slice of dv) then needs plain
-// products only.
+// Two kernels: a per-(chunk, head) prep forms T, P and the running log-decays Gc into the
+// workspace (every exponential it takes is of a non-positive difference, so no factor can
+// overflow); a scan per (sequence, head, slice of dv) forms Kg, Qg, Kc and e^{Gc[C]} from K, Q
+// and Gc as it reads its matrix-core operands.
 #include "gdn_device.h"
 #include "gdn_inverse.h"
 #include "gdn_launch.h"
@@ -24,10 +24,12 @@ namespace {
 constexpr int kC = 64;
 constexpr int kPT = 512;          // prep threads (one workgroup per CU fits its LDS)
 constexpr int kST = 1024;         // scan threads: 16 waves hide the LDS latency of the small products
-constexpr int kSL = 16;           // dv columns per scan workgroup
+// dv columns per scan workgroup: 32 with bf16 inputs (K, Q sit in LDS as bf16, exactly), 16
+// with fp32 inputs (their rows leave no LDS room for wider slices)
+template <typename Tin> constexpr int kda_cols() { return sizeof(Tin) == 2 ? 32 : 16; }
 
 struct KdaLayout {
-    size_t T, P, Kg, Qg, Kc, eC, total;
+    size_t T, P, Gw, total;
     int max_chunks;
 };
 
@@ -43,10 +45,7 @@ KdaLayout kda_layout(int ntok, int num_seqs, int H, int dk) {
     };
     L.T = take(ch * kC * kC * sizeof(float));
     L.P = take(ch * kC * kC * sizeof(float));
-    L.Kg = take(ch * kC * (size_t)dk * sizeof(float));
-    L.Qg = take(ch * kC * (size_t)dk * sizeof(float));
-    L.Kc = take(ch * kC * (size_t)dk * sizeof(float));
-    L.eC = take(ch * (size_t)dk * sizeof(float));
+    L.Gw = take(ch * kC * (size_t)dk * sizeof(float));
     L.total = off;
     return L;
 }
@@ -59,7 +58,7 @@ struct KdaArgs {
     const int32_t* cu;
     int num_seqs, ntok, H, dk, dv;
     void* y;
-    float *T, *P, *Kg, *Qg, *Kc, *eC;
+    float *T, *P, *Gw;             // Gw: the chunk's running log-decays [64][dk] per chunk-head
 };
 
 __device__ void kda_seq(const KdaArgs& a, int s, int& lo, int& hi, int& cbase) {
@@ -196,17 +195,12 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
             a.P[ch * kC * kC + r * kC + i] = 0.f;
         }
     }
-    // decayed operands of the scan
-    const int last = n - 1;
-    for (int e = tid; e < kC * DK; e += kPT) {
-        const int r = e / DK, d = e % DK;
-        const size_t o = ch * kC * DK + e;
-        const bool ok = r < n;
-        a.Kg[o] = ok ? Ks[r][d] * fexp(Gc[r][d]) : 0.f;
-        a.Qg[o] = ok ? Qs[r][d] * fexp(Gc[r][d]) : 0.f;
-        a.Kc[o] = ok ? Ks[r][d] * fexp(Gc[last][d] - Gc[r][d]) : 0.f;
+    // the running log-decays for the scan (rows past n repeat row n-1: their g is zero)
+    for (int u = tid; u < kC * DK / 4; u += kPT) {
+        const int r = u / (DK / 4), d = (u % (DK / 4)) * 4;
+        reinterpret_cast<float4*>(a.Gw + ch * kC * DK)[u] =
+            make_float4(Gc[r][d], Gc[r][d + 1], Gc[r][d + 2], Gc[r][d + 3]);
     }
-    if (tid < DK) a.eC[ch * DK + tid] = fexp(Gc[last][tid]);
     __syncthreads();
     // T = (I + A)^{-1} by one wave (16x16 diagonal blocks by DPP substitution, then fp32 MFMA
     // levels), in place in LDS, then written out by the whole workgroup
@@ -217,135 +211,189 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
 
 // ------------------------------------------------------------------ scan per (seq, head, slice)
 // Each chunk step's products run on the fp32 matrix core (v_mfma_f32_16x16x4f32), one 16x16
-// output tile per wave, operands read from LDS as strided views.
-template <int NT>
-__device__ __forceinline__ void kda_load_tile(const float* src, int rows, int cols, float* dst, int stride) {
-    const int upr = cols / 4;
-    for (int u = threadIdx.x; u < rows * upr; u += NT) {
-        const int r = u / upr, c = (u % upr) * 4;
-        const float4 v = reinterpret_cast<const float4*>(src)[u];
-        float* d = dst + r * stride + c;
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    }
-}
-
-template <int DK, typename Tin, typename Tout>
+// output tile per wave. The decayed operands are formed as they are read: Kg = K o e^{Gc},
+// Qg = Q o e^{Gc}, Kc = K o e^{Gc[last] - Gc} (one exponential per operand element; every
+// exponent is <= 0). The next chunk's K, Q, Gc, T, P, V and beta are fetched into registers
+// while this chunk computes.
+template <int DK, int SL, typename Tin, typename Tout>
 __global__ void __launch_bounds__(kST) kda_scan_kernel(KdaArgs a) {
-    constexpr int PR = kSL + 1;
-    __shared__ float Kg[kC][DK + 1], Qg[kC][DK + 1], Kc[kC][DK + 1];
+    constexpr int CT = SL / 16, PR = SL + 1;
+    constexpr int KR = DK + (sizeof(Tin) == 2 ? 2 : 1);   // K, Q row stride (4-byte aligned)
+    __shared__ Tin Ks[kC][KR], Qs[kC][KR];
+    __shared__ float Gs[kC][DK + 1];
     __shared__ float T[kC][kC + 1], P[kC][kC + 1];
     __shared__ float S[DK][PR];
     __shared__ float R[kC][PR], U[kC][PR];
-    __shared__ float eC[DK], Bt[kC];
-    const int slices = a.dv / kSL;
+    __shared__ float Bt[kC];
+    const int slices = a.dv / SL;
     const int slice = blockIdx.x % slices;
     const int h = (blockIdx.x / slices) % a.H;
     const int sq = blockIdx.x / (slices * a.H);
-    const int j0 = slice * kSL, tid = threadIdx.x, H = a.H, dv = a.dv;
+    const int j0 = slice * SL, tid = threadIdx.x, H = a.H, dv = a.dv;
     const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
+    constexpr int NW = kST / kWave;
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    static_assert(4 + DK / 16 <= kST / kWave, "one tile per wave in the last step");
+    constexpr int NY = 4 * CT, NS = (DK / 16) * CT;         // output and state tiles
+    static_assert(NY <= NW && NY + NS <= 2 * NW, "tiles per wave");
     Tout* y = static_cast<Tout*>(a.y);
     int lo, hi, cbase;
     kda_seq(a, sq, lo, hi, cbase);
     const size_t st_off = ((size_t)sq * H + h) * DK * dv;
-    for (int e = tid; e < DK * kSL; e += kST) {
-        const int d = e / kSL, j = e % kSL;
+    for (int e = tid; e < DK * SL; e += kST) {
+        const int d = e / SL, j = e % SL;
         S[d][j] = a.S0 ? a.S0[st_off + (size_t)d * dv + j0 + j] : 0.f;
     }
-    // The next chunk's tiles are fetched into registers while this chunk computes (16-byte
-    // global loads, kST threads: 2 of each [64][DK] tile, 1 of each [64][64] tile per thread).
-    constexpr int NDK = kC * DK / 4 / kST;             // float4 of a [64][DK] tile per thread
+
+    constexpr int PER = 16 / sizeof(Tin), KUNITS = kC * DK / PER;
+    constexpr int KU = (KUNITS + kST - 1) / kST, GU = kC * DK / 4 / kST, VE = kC * SL / kST;
+    static_assert(GU >= 1 && kC * kC / 4 == kST && VE >= 1, "prefetch shape");
     struct Pref {
-        float4 kg[NDK], qg[NDK], kc[NDK], t, p;
-        float v, ec, bt;
+        gdn_u32x4 k[KU], q[KU];
+        float4 g[GU], t, p;
+        float v[VE], b;
     };
     auto fetch = [&](int t0, int n, size_t ch, Pref& f) __attribute__((always_inline)) {
+        const Tin* kp = static_cast<const Tin*>(a.k);
+        const Tin* qp = static_cast<const Tin*>(a.q);
 #pragma unroll
-        for (int i = 0; i < NDK; ++i) {
-            const int u = tid + i * kST;
-            f.kg[i] = reinterpret_cast<const float4*>(a.Kg + ch * kC * DK)[u];
-            f.qg[i] = reinterpret_cast<const float4*>(a.Qg + ch * kC * DK)[u];
-            f.kc[i] = reinterpret_cast<const float4*>(a.Kc + ch * kC * DK)[u];
+        for (int i = 0; i < KU; ++i) {
+            const int u = tid + i * kST, r = u / (DK / PER), c0 = (u % (DK / PER)) * PER;
+            f.k[i] = gdn_u32x4{0u, 0u, 0u, 0u};
+            f.q[i] = gdn_u32x4{0u, 0u, 0u, 0u};
+            if (u < KUNITS && r < n) {
+                const size_t off = ((size_t)(t0 + r) * H + h) * DK + c0;
+                f.k[i] = *reinterpret_cast<const gdn_u32x4*>(kp + off);
+                f.q[i] = *reinterpret_cast<const gdn_u32x4*>(qp + off);
+            }
         }
+#pragma unroll
+        for (int i = 0; i < GU; ++i) f.g[i] = reinterpret_cast<const float4*>(a.Gw + ch * kC * DK)[tid + i * kST];
         f.t = reinterpret_cast<const float4*>(a.T + ch * kC * kC)[tid];
         f.p = reinterpret_cast<const float4*>(a.P + ch * kC * kC)[tid];
-        const int r = tid / kSL, j = tid % kSL;   // kC * kSL == kST: one V element per thread
-        f.v = r < n ? ldx<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
-        f.ec = tid < DK ? a.eC[ch * DK + tid] : 0.f;
-        f.bt = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) {
+            const int e = tid + i * kST, r = e / SL, j = e % SL;
+            f.v[i] = r < n ? ldx<Tin>(a.v, ((size_t)(t0 + r) * H + h) * dv + j0 + j) : 0.f;
+        }
+        f.b = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
     };
     auto put4 = [](float* d, float4 x) __attribute__((always_inline)) {
         d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
     };
     auto stash = [&](const Pref& f) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NDK; ++i) {
-            const int u = tid + i * kST, r = u / (DK / 4), c4 = (u % (DK / 4)) * 4;
-            put4(&Kg[r][c4], f.kg[i]);
-            put4(&Qg[r][c4], f.qg[i]);
-            put4(&Kc[r][c4], f.kc[i]);
+        for (int i = 0; i < KU; ++i) {
+            const int u = tid + i * kST, r = u / (DK / PER), c0 = (u % (DK / PER)) * PER;
+            if (u < KUNITS) {
+                uint32_t* dk_ = reinterpret_cast<uint32_t*>(&Ks[r][c0]);
+                uint32_t* dq_ = reinterpret_cast<uint32_t*>(&Qs[r][c0]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    dk_[w] = f.k[i][w];
+                    dq_[w] = f.q[i][w];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < GU; ++i) {
+            const int u = tid + i * kST;
+            put4(&Gs[u / (DK / 4)][(u % (DK / 4)) * 4], f.g[i]);
         }
         put4(&T[tid / (kC / 4)][(tid % (kC / 4)) * 4], f.t);
         put4(&P[tid / (kC / 4)][(tid % (kC / 4)) * 4], f.p);
-        R[tid / kSL][tid % kSL] = f.v;
-        if (tid < DK) eC[tid] = f.ec;
-        if (tid < kC) Bt[tid] = f.bt;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) {
+            const int e = tid + i * kST;
+            R[e / SL][e % SL] = f.v[i];
+        }
+        if (tid < kC) Bt[tid] = f.b;
     };
-    static_assert(kC * kSL == kST && kC * kC / 4 == kST, "one T, P float4 and one V element per thread");
+
     Pref f;
     if (lo < hi) fetch(lo, min(kC, hi - lo), (size_t)cbase * H + h, f);
     for (int t0 = lo, c = cbase; t0 < hi; t0 += kC, ++c) {
-        const int n = min(kC, hi - t0);
+        const int n = min(kC, hi - t0), last = n - 1;
         __syncthreads();
         stash(f);
         if (t0 + kC < hi) fetch(t0 + kC, min(kC, hi - t0 - kC), (size_t)(c + 1) * H + h, f);
         __syncthreads();
-        if (wave < 4) {   // R = beta o (V - Kg S)
-            const floatx4 ks = mma_f32_tile(&Kg[wave * 16][0], DK + 1, 1, &S[0][0], PR, 1, DK, zero);
+        if (wave < NY) {   // R = beta o (V - Kg S)
+            const int rt = wave % 4, ct = wave / 4, r = rt * 16 + lc;
+            floatx4 ks = zero;
+#pragma unroll 4
+            for (int k0 = 0; k0 < DK; k0 += 4) {
+                const int d = k0 + lg;
+                ks = __builtin_amdgcn_mfma_f32_16x16x4f32(load1(&Ks[r][d]) * fexp(Gs[r][d]),
+                                                          S[d][ct * 16 + lc], ks, 0, 0, 0);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = wave * 16 + 4 * lg + i;
-                R[r][lc] = Bt[r] * (R[r][lc] - ks[i]);
+                const int rr = rt * 16 + 4 * lg + i, j = ct * 16 + lc;
+                R[rr][j] = Bt[rr] * (R[rr][j] - ks[i]);
             }
         }
         __syncthreads();
-        if (wave < 4) {   // U = T R (T lower triangular)
-            const floatx4 u = mma_f32_tile(&T[wave * 16][0], kC + 1, 1, &R[0][0], PR, 1, kC, zero);
+        if (wave < NY) {   // U = T R (T lower triangular)
+            const int rt = wave % 4, ct = wave / 4;
+            const floatx4 u = mma_f32_tile(&T[rt * 16][0], kC + 1, 1, &R[0][ct * 16], PR, 1, kC, zero);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) U[wave * 16 + 4 * lg + i][lc] = u[i];
+            for (int i = 0; i < 4; ++i) U[rt * 16 + 4 * lg + i][ct * 16 + lc] = u[i];
         }
         __syncthreads();
-        // waves 0-3: Y = Qg S + P U (rows past n are not stored);
-        // waves 4..: S' = e^{Gc[C]} o S + Kc^T U, held in registers until every read of S is done
-        floatx4 sn = zero;
-        if (wave < 4) {
-            floatx4 acc = mma_f32_tile(&Qg[wave * 16][0], DK + 1, 1, &S[0][0], PR, 1, DK, zero);
-            acc = mma_f32_tile(&P[wave * 16][0], kC + 1, 1, &U[0][0], PR, 1, kC, acc);
+        // Y = Qg S + P U (rows past n are not stored) and S' = e^{Gc[last]} o S + Kc^T U, the
+        // latter held in registers until every read of S is done
+        floatx4 sn[2] = {zero, zero};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wave * 16 + 4 * lg + i;
-                if (r < n) store1(y + ((size_t)(t0 + r) * H + h) * dv + j0 + lc, acc[i]);
-            }
-        } else if (wave < 4 + DK / 16) {
-            const int dt = wave - 4;
-            sn = mma_f32_tile(&Kc[0][dt * 16], 1, DK + 1, &U[0][0], PR, 1, kC, zero);
+        for (int uu = 0; uu < 2; ++uu) {
+            const int tile = wave + uu * NW;
+            if (tile < NY) {
+                const int rt = tile % 4, ct = tile / 4, r = rt * 16 + lc;
+                floatx4 acc = zero;
+#pragma unroll 4
+                for (int k0 = 0; k0 < DK; k0 += 4) {
+                    const int d = k0 + lg;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(load1(&Qs[r][d]) * fexp(Gs[r][d]),
+                                                               S[d][ct * 16 + lc], acc, 0, 0, 0);
+                }
+                acc = mma_f32_tile(&P[rt * 16][0], kC + 1, 1, &U[0][ct * 16], PR, 1, kC, acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = dt * 16 + 4 * lg + i;
-                sn[i] += eC[d] * S[d][lc];
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = rt * 16 + 4 * lg + i;
+                    if (rr < n) store1(y + ((size_t)(t0 + rr) * H + h) * dv + j0 + ct * 16 + lc, acc[i]);
+                }
+            } else if (tile < NY + NS) {
+                const int t2 = tile - NY, dt = t2 % (DK / 16), ct = t2 / (DK / 16);
+                const int d = dt * 16 + lc;                  // this lane's key channel (A row)
+                const float gl = Gs[last][d];
+                floatx4 acc = zero;
+#pragma unroll 4
+                for (int k0 = 0; k0 < kC; k0 += 4) {
+                    const int i = k0 + lg;                   // token (contraction index)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(load1(&Ks[i][d]) * fexp(gl - Gs[i][d]),
+                                                               U[i][ct * 16 + lc], acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int dd = dt * 16 + 4 * lg + i;
+                    sn[uu][i] = acc[i] + fexp(Gs[last][dd]) * S[dd][ct * 16 + lc];
+                }
             }
         }
         __syncthreads();
-        if (wave >= 4 && wave < 4 + DK / 16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[(wave - 4) * 16 + 4 * lg + i][lc] = sn[i];
+        for (int uu = 0; uu < 2; ++uu) {
+            const int tile = wave + uu * NW;
+            if (tile >= NY && tile < NY + NS) {
+                const int t2 = tile - NY, dt = t2 % (DK / 16), ct = t2 / (DK / 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[dt * 16 + 4 * lg + i][ct * 16 + lc] = sn[uu][i];
+            }
         }
     }
     __syncthreads();
     if (a.ST) {
-        for (int e = tid; e < DK * kSL; e += kST) {
-            const int d = e / kSL, j = e % kSL;
+        for (int e = tid; e < DK * SL; e += kST) {
+            const int d = e / SL, j = e % SL;
             a.ST[st_off + (size_t)d * dv + j0 + j] = S[d][j];
         }
     }
@@ -367,18 +415,16 @@ hipError_t launch_chunk_kda(const ChunkKdaArgs& c, hipStream_t s) {
     a.y = c.y;
     a.T = reinterpret_cast<float*>(ws + L.T);
     a.P = reinterpret_cast<float*>(ws + L.P);
-    a.Kg = reinterpret_cast<float*>(ws + L.Kg);
-    a.Qg = reinterpret_cast<float*>(ws + L.Qg);
-    a.Kc = reinterpret_cast<float*>(ws + L.Kc);
-    a.eC = reinterpret_cast<float*>(ws + L.eC);
+    a.Gw = reinterpret_cast<float*>(ws + L.Gw);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((c.ntok / c.num_seqs + kC - 1) / kC);
-    const int blocks = c.num_seqs * c.H * (c.dv / kSL);
-    if (blocks == 0) return hipSuccess;
+    if (c.num_seqs * c.H == 0) return hipSuccess;
 #define GDN_KDA(DK, TI, TO)                                                                      \
     do {                                                                                         \
+        constexpr int SL = kda_cols<TI>();                                                       \
         if (nchunks > 0)                                                                         \
             hipLaunchKernelGGL((kda_prep_kernel<DK, TI>), dim3(nchunks, c.H), dim3(kPT), 0, s, a); \
-        hipLaunchKernelGGL((kda_scan_kernel<DK, TI, TO>), dim3(blocks), dim3(kST), 0, s, a);     \
+        hipLaunchKernelGGL((kda_scan_kernel<DK, SL, TI, TO>), dim3(c.num_seqs * c.H * (c.dv / SL)), \
+                           dim3(kST), 0, s, a);                                                 \
     } while (0)
     if (c.dk == 128) {
         if (c.in_bf16 && c.y_bf16) GDN_KDA(128, uint16_t, uint16_t);
