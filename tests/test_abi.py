@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(L):
     assert {"gdn_preprocess", "gdn_chunk_prefill", "gdn_decode_step", "gdn_output_gate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 3
+    declared = int(re.search(r"#define GDN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.gdn_abi_version() == declared
 
 
 def test_status_strings(L):
