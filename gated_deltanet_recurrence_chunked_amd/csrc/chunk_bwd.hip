@@ -742,6 +742,12 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
     }
 }
 
+// dst = src, or zero without one (n float4 units; states are multiples of 4 floats)
+__global__ void __launch_bounds__(256) copy_or_zero_kernel(float4* dst, const float4* src, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 }  // namespace
 
 size_t chunk_bwd_workspace(int ntok, int num_seqs, int H, int dk, int dv) {
@@ -766,13 +772,16 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((c.ntok / c.num_seqs + kC - 1) / kC);
     const int seq_blocks = c.num_seqs * c.H;
     if (nchunks == 0 || seq_blocks == 0) {
-        // no tokens: dS0 = dS_T
-        if (c.dS0) {
-            const size_t bytes = (size_t)c.num_seqs * c.H * c.dk * c.dv * sizeof(float);
-            return c.dST ? hipMemcpyAsync(c.dS0, c.dST, bytes, hipMemcpyDeviceToDevice, s)
-                         : hipMemsetAsync(c.dS0, 0, bytes, s);
+        // no tokens: dS0 = dS_T (a kernel, not a memset or copy node, so the call can be
+        // captured in a graph like every other)
+        const size_t n = (size_t)c.num_seqs * c.H * c.dk * c.dv;
+        if (c.dS0 && n > 0) {
+            const int blocks = (int)((n / 4 + 255) / 256);
+            hipLaunchKernelGGL(copy_or_zero_kernel, dim3(blocks), dim3(256), 0, s,
+                               reinterpret_cast<float4*>(c.dS0),
+                               reinterpret_cast<const float4*>(c.dST), n / 4);
         }
-        return hipSuccess;
+        return hipGetLastError();
     }
 #define GDN_BWD(DK, TI, TD)                                                                     \
     do {                                                                                        \

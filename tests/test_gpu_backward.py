@@ -84,3 +84,27 @@ def test_backward_config1_shape_sampled(gpu):
     sh = inp["shape"]
     grads = gi.grad_draws(7, sh.ntok, sh.num_seqs, sh.H, 128, 128, bf16=True)
     _run(inp, grads, bf16_in=True, bf16_dy=True, seqs=[0, 3], heads=[2, 13])
+
+
+def test_backward_of_no_tokens_passes_the_state_gradient_through(gpu):
+    """ntok = 0: every sequence is empty, so dS0 = dS_T (zero without one). Called through the
+    C ABI directly, the token inputs pointing at a small dummy buffer the kernels never touch."""
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    _announce("backward with no tokens (2 sequences of length 0)")
+    L = gdn.lib()
+    N, H, d = 2, 2, 64
+    dummy = torch.zeros(64, dtype=torch.float32, device="cuda")
+    dST = torch.randn(N, H, d, d, device="cuda")
+    ws = torch.empty(max(int(L.gdn_chunk_backward_workspace_size(0, N, H, d, d)), 256),
+                     dtype=torch.uint8, device="cuda")
+    p = dummy.data_ptr()
+    for src in (dST, None):
+        dS0 = torch.full((N, H, d, d), 7.0, device="cuda")
+        st = L.gdn_chunk_backward(p, p, p, 0, p, p, None, p, 0, None if src is None else src.data_ptr(),
+                                  None, None, N, 0, H, d, d, p, p, p, p, p, dS0.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), None)
+        torch.cuda.synchronize()
+        assert st == 0, L.gdn_last_error()
+        ref = torch.zeros_like(dS0) if src is None else src
+        assert torch.equal(dS0, ref)
