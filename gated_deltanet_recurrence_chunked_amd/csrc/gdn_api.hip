@@ -55,6 +55,17 @@ int hip_status(hipError_t e, const char* what) {
         GDN_REQUIRE(aligned4(p), GDN_ERR_ALIGN, "%s is not 4-byte aligned", #p); \
     } while (0)
 
+// Token-indexed arrays may be NULL when there are no tokens (n == 0): nothing reads them, and
+// torch hands out a null pointer for a tensor with no elements.
+#define GDN_TPTR(p, n)                  \
+    do {                                \
+        if ((n) > 0 || (p)) GDN_PTR(p); \
+    } while (0)
+#define GDN_TSPTR(p, n)                  \
+    do {                                 \
+        if ((n) > 0 || (p)) GDN_SPTR(p); \
+    } while (0)
+
 #define GDN_OPT_PTR(p) \
     GDN_REQUIRE((p) == nullptr || aligned16(p), GDN_ERR_ALIGN, "%s is not 16-byte aligned", #p)
 
@@ -118,15 +129,15 @@ int preprocess_impl(const void* xq, const void* xk, const void* xv, int x_dtype,
     const bool gates = a_raw || b_raw || A_log || dt_bias || g || beta;
     GDN_REQUIRE(conv || gates, GDN_ERR_NULL, "nothing to compute: all inputs are NULL");
     if (conv) {
-        GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv);
+        GDN_TPTR(xq, ntok); GDN_TPTR(xk, ntok); GDN_TPTR(xv, ntok);
         GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
-        GDN_PTR(q); GDN_PTR(k); GDN_PTR(v);
+        GDN_TPTR(q, ntok); GDN_TPTR(k, ntok); GDN_TPTR(v, ntok);
         GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
         GDN_REQUIRE(l2_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps must be >= 0");
     }
     if (gates) {
-        GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias); GDN_SPTR(g);
-        GDN_SPTR(beta);
+        GDN_TSPTR(a_raw, ntok); GDN_TSPTR(b_raw, ntok); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
+        GDN_TSPTR(g, ntok); GDN_TSPTR(beta, ntok);
     }
     GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
     int st = check_packing(nullptr, cu_seqlens != nullptr, num_seqs, ntok);
@@ -204,7 +215,8 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
                 "in_dtype/y_dtype must be GDN_F32 or GDN_BF16");
     GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
                 "need H >= 1 and dk, dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
-    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(y);
+    GDN_TPTR(q, ntok); GDN_TPTR(k, ntok); GDN_TPTR(v, ntok); GDN_TSPTR(g, ntok);
+    GDN_TSPTR(beta, ntok); GDN_TPTR(y, ntok);
     GDN_OPT_PTR(initial_state); GDN_OPT_PTR(final_state);
     GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
     GDN_REQUIRE(cu_seqlens_host == nullptr || cu_seqlens != nullptr, GDN_ERR_NULL,
@@ -246,8 +258,10 @@ int gdn_chunk_backward(const void* q, const void* k, const void* v, int in_dtype
                 "in_dtype/dy_dtype must be GDN_F32 or GDN_BF16");
     GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
                 "need H >= 1 and dk, dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
-    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(dy);
-    GDN_PTR(dq); GDN_PTR(dk_out); GDN_PTR(dv_out); GDN_SPTR(dg); GDN_SPTR(dbeta);
+    GDN_TPTR(q, ntok); GDN_TPTR(k, ntok); GDN_TPTR(v, ntok); GDN_TSPTR(g, ntok);
+    GDN_TSPTR(beta, ntok); GDN_TPTR(dy, ntok);
+    GDN_TPTR(dq, ntok); GDN_TPTR(dk_out, ntok); GDN_TPTR(dv_out, ntok); GDN_TSPTR(dg, ntok);
+    GDN_TSPTR(dbeta, ntok);
     GDN_OPT_PTR(initial_state); GDN_OPT_PTR(dfinal_state); GDN_OPT_PTR(dinitial_state);
     GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
     GDN_REQUIRE(cu_seqlens_host == nullptr || cu_seqlens != nullptr, GDN_ERR_NULL,
@@ -284,7 +298,8 @@ int gdn_kda_chunk_prefill(const void* q, const void* k, const void* v, int in_dt
                 "in_dtype/y_dtype must be GDN_F32 or GDN_BF16");
     GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
                 "need H >= 1 and dk, dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
-    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(y);
+    GDN_TPTR(q, ntok); GDN_TPTR(k, ntok); GDN_TPTR(v, ntok); GDN_TSPTR(g, ntok);
+    GDN_TSPTR(beta, ntok); GDN_TPTR(y, ntok);
     GDN_OPT_PTR(initial_state); GDN_OPT_PTR(final_state);
     GDN_REQUIRE(aligned4(cu_seqlens), GDN_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
     GDN_REQUIRE(cu_seqlens_host == nullptr || cu_seqlens != nullptr, GDN_ERR_NULL,
@@ -312,7 +327,8 @@ int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, c
     GDN_REQUIRE(N >= 0 && H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
                 "need N >= 0, H >= 1 and dk, dv in {64, 128} (got N=%d H=%d dk=%d dv=%d)", N, H,
                 dk, dv);
-    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(state); GDN_PTR(y);
+    GDN_TPTR(q, N); GDN_TPTR(k, N); GDN_TPTR(v, N); GDN_TSPTR(g, N); GDN_TSPTR(beta, N);
+    GDN_TPTR(state, N); GDN_TPTR(y, N);
     return hip_status(gdn::launch_decode(q, k, v, in_dtype == GDN_BF16, g, beta, state, N, H, dk,
                                          dv, y, y_dtype == GDN_BF16,
                                          static_cast<hipStream_t>(stream)),
@@ -329,7 +345,8 @@ int gdn_decode_multi(const void* q, const void* k, const void* v, int in_dtype, 
                 dk, dv);
     GDN_REQUIRE(T >= 1 && T <= GDN_DECODE_MAX_TOKENS, GDN_ERR_SHAPE,
                 "T must be in 1..%d (got %d)", GDN_DECODE_MAX_TOKENS, T);
-    GDN_PTR(q); GDN_PTR(k); GDN_PTR(v); GDN_SPTR(g); GDN_SPTR(beta); GDN_PTR(state); GDN_PTR(y);
+    GDN_TPTR(q, N); GDN_TPTR(k, N); GDN_TPTR(v, N); GDN_TSPTR(g, N); GDN_TSPTR(beta, N);
+    GDN_TPTR(state, N); GDN_TPTR(y, N);
     GDN_OPT_PTR(step_states);
     if (step_states) {
         const char* a0 = reinterpret_cast<const char*>(state);
@@ -367,9 +384,10 @@ int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtyp
                 "need H >= 1, dk = 128 and dv in {64, 128} (got H=%d dk=%d dv=%d)", H, dk, dv);
     GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
     GDN_REQUIRE(l2_eps >= 0.f && rms_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps and rms_eps must be >= 0");
-    GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
-    GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
-    GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o);
+    GDN_TPTR(xq, ntok); GDN_TPTR(xk, ntok); GDN_TPTR(xv, ntok);
+    GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
+    GDN_TSPTR(a_raw, ntok); GDN_TSPTR(b_raw, ntok); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
+    GDN_TPTR(z, ntok); GDN_SPTR(norm_weight); GDN_TPTR(o, ntok);
     GDN_OPT_PTR(initial_state); GDN_OPT_PTR(final_state);
     GDN_OPT_PTR(q); GDN_OPT_PTR(k); GDN_OPT_PTR(v); GDN_OPT_PTR(y);
     GDN_REQUIRE(aligned4(g) && aligned4(beta), GDN_ERR_ALIGN, "g/beta are not 4-byte aligned");
@@ -441,10 +459,10 @@ int gdn_fused_decode(const void* xq, const void* xk, const void* xv, int x_dtype
                 dk, dv);
     GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
     GDN_REQUIRE(l2_eps >= 0.f && rms_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps and rms_eps must be >= 0");
-    GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
-    GDN_PTR(conv_state);
-    GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
-    GDN_PTR(state); GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o); GDN_OPT_PTR(y);
+    GDN_TPTR(xq, N); GDN_TPTR(xk, N); GDN_TPTR(xv, N); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
+    GDN_TPTR(conv_state, N);
+    GDN_TSPTR(a_raw, N); GDN_TSPTR(b_raw, N); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
+    GDN_TPTR(state, N); GDN_TPTR(z, N); GDN_SPTR(norm_weight); GDN_TPTR(o, N); GDN_OPT_PTR(y);
     gdn::DecodeFusedArgs f;
     f.x[0] = xq; f.x[1] = xk; f.x[2] = xv;
     f.w[0] = wq; f.w[1] = wk; f.w[2] = wv;
@@ -477,10 +495,10 @@ int gdn_fused_decode_multi(const void* xq, const void* xk, const void* xv, int x
                 "T must be in 1..%d (got %d)", GDN_DECODE_MAX_TOKENS, T);
     GDN_REQUIRE(conv_k == 4, GDN_ERR_SHAPE, "conv_k must be 4 (got %d)", conv_k);
     GDN_REQUIRE(l2_eps >= 0.f && rms_eps >= 0.f, GDN_ERR_SHAPE, "l2_eps and rms_eps must be >= 0");
-    GDN_PTR(xq); GDN_PTR(xk); GDN_PTR(xv); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
-    GDN_PTR(conv_state_in); GDN_PTR(conv_state_out);
-    GDN_SPTR(a_raw); GDN_SPTR(b_raw); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
-    GDN_PTR(state); GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o); GDN_OPT_PTR(y);
+    GDN_TPTR(xq, N); GDN_TPTR(xk, N); GDN_TPTR(xv, N); GDN_PTR(wq); GDN_PTR(wk); GDN_PTR(wv);
+    GDN_TPTR(conv_state_in, N); GDN_TPTR(conv_state_out, N);
+    GDN_TSPTR(a_raw, N); GDN_TSPTR(b_raw, N); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
+    GDN_TPTR(state, N); GDN_TPTR(z, N); GDN_SPTR(norm_weight); GDN_TPTR(o, N); GDN_OPT_PTR(y);
     GDN_OPT_PTR(step_states);
     const int hC = H * (2 * dk + dv);
     {
@@ -521,7 +539,7 @@ int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype, cons
     GDN_REQUIRE(ntok >= 0 && H >= 1 && valid_dim(dv), GDN_ERR_SHAPE,
                 "need ntok >= 0, H >= 1 and dv in {64, 128} (got ntok=%d H=%d dv=%d)", ntok, H, dv);
     GDN_REQUIRE(eps >= 0.f, GDN_ERR_SHAPE, "eps must be >= 0");
-    GDN_PTR(y); GDN_PTR(z); GDN_SPTR(norm_weight); GDN_PTR(o);
+    GDN_TPTR(y, ntok); GDN_TPTR(z, ntok); GDN_SPTR(norm_weight); GDN_TPTR(o, ntok);
     return hip_status(gdn::launch_output_gate(y, y_dtype == GDN_BF16, z, z_dtype == GDN_BF16,
                                               norm_weight, ntok, H, dv, eps, o,
                                               o_dtype == GDN_BF16, static_cast<hipStream_t>(stream)),

@@ -216,11 +216,12 @@ hipError_t launch_preprocess(const PreprocessArgs& a, hipStream_t s) {
     }
     p.gate_blocks = a.a_raw ? 1 : 0;
     ny += p.gate_blocks;
-    if (ny == 0 || (a.ntok == 0 && !a.hout)) return hipSuccess;
-    if (a.hout && a.x[0])
+    // the conv taps mark the conv part as asked for: x may be NULL when ntok == 0
+    const bool carry = a.hout && a.w[0];
+    if (carry)
         hipLaunchKernelGGL(conv_carry_kernel, dim3(a.num_seqs), dim3(kPreThreads), 0, s, a,
                            a.in_bf16 ? 2 : 4);
-    if (a.ntok == 0) return hipGetLastError();
+    if (ny == 0 || a.ntok == 0) return carry ? hipGetLastError() : hipSuccess;
     dim3 grid((a.ntok + kPreTokens - 1) / kPreTokens, ny);
     if (a.in_bf16 && a.out_bf16)
         hipLaunchKernelGGL((preprocess_kernel<uint16_t, uint16_t>), grid, dim3(kPreThreads), 0, s, p);

@@ -24,6 +24,10 @@
  *   - Pointers to vector data (x*, q, k, v, y, z, o, conv taps, states, workspace) must be
  *     16-byte aligned; scalar arrays (g, beta, a_raw, b_raw, A_log, dt_bias, norm weight,
  *     cu_seqlens) 4-byte aligned. dk, dv in {64, 128}. H >= 1.
+ *   - Arrays indexed by token (or, in decode, by sequence: the decode states and conv
+ *     histories included) may be NULL when that count (ntok, or N) is 0: nothing reads or
+ *     writes them then. Per-head and per-channel arrays (conv taps, A_log, dt_bias, norm
+ *     weight) and the workspace stay required.
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
  *     asynchronous on it: it validates its arguments on the host, enqueues its kernels
  *     and returns. Device faults surface when the caller synchronises.

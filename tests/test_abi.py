@@ -66,6 +66,11 @@ def test_prefill_validation(L):
     dec2 = (ctypes.c_int32 * 3)(0, 100, 128)
     assert _prefill(L, num_seqs=2, cu=FAKE, cu_host=ctypes.cast(dec, ctypes.c_void_p)) == 4
     assert _prefill(L, num_seqs=2, cu=None, cu_host=ctypes.cast(dec2, ctypes.c_void_p)) == 1
+    # with no tokens the token-indexed arrays may be NULL; alignment is still checked, and the
+    # matrix path still needs its workspace (both fail before anything is enqueued)
+    assert _prefill(L, ntok=0, q=None, k=None, v=None, g=None, beta=None, y=MIS) == 5
+    assert _prefill(L, ntok=0, q=None, k=None, v=None, g=None, beta=None, y=None) == 6
+    assert _prefill(L, ntok=1, num_seqs=1, q=None) == 1
 
 
 def test_decode_and_gate_validation(L):
