@@ -24,10 +24,17 @@ COPY_BYTES = 1 << 30
 PREFILL_KERNELS = ("chunk_prep_kernel", "chunk_scan_kernel", "chunk_table_kernel")
 
 
+PREFILL_SOURCES = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h", "gdn_launch.h")
+
+
 def prefill_source_sha() -> str:
-    """Hash of the chunked-prefill kernel source: counters are void once it changes."""
-    with open(os.path.join(PKG, "csrc", "chunk_bf16.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the chunked-prefill kernel source and the headers it includes: counters are
+    void once any of them changes."""
+    h = hashlib.sha256()
+    for name in PREFILL_SOURCES:
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _one(pattern: str) -> str:
