@@ -76,7 +76,7 @@ def main():
 
     # ------------------------------------------------------------------ prefill workload
     log("[bench] generating bf16 prefill inputs B=4 H=16 T=4096 d=128")
-    inp = gi.make_inputs(1, seed=0)
+    inp = gi.make_inputs(gi.PREFILL, seed=0)
     sh = inp["shape"]
     H, dk, dv, ntok, nseq = sh.H, sh.dk, sh.dv, sh.ntok, sh.num_seqs
     X = dict(xq=d(inp["xq"], True), xk=d(inp["xk"], True), xv=d(inp["xv"], True),
@@ -275,7 +275,7 @@ def main():
     if not args.no_decode:
         S_ = args.decode_steps
         log(f"[bench] generating decode inputs N=256 H=32 d=128, {S_} steps")
-        di = gi.make_inputs(3, seed=0, steps=S_)
+        di = gi.make_inputs(gi.DECODE, seed=0, steps=S_)
         dsh = di["shape"]
         N, DH = dsh.num_seqs, dsh.H
         state = d(di["state"])
@@ -315,7 +315,7 @@ def main():
         # a quarter as many steps (the same number of tokens)
         T4, S4 = 4, max(1, S_ // 4)
         log(f"[bench] generating multi-token decode inputs N=256 H=32 d=128 T={T4}, {S4} steps")
-        mi = gi.make_inputs(3, seed=1, steps=S4, tokens=T4)
+        mi = gi.make_inputs(gi.DECODE, seed=1, steps=S4, tokens=T4)
         state = d(mi["state"])
         qm, km, vm = d(mi["q"], True), d(mi["k"], True), d(mi["v"], True)
         _, _, _, gm, bm = gdn.gdn_preprocess(None, None, None, None, None, None,

@@ -45,11 +45,22 @@ def as_f64(a: np.ndarray, is_bf16: bool) -> np.ndarray:
     return (bf16_bits_to_f32(a) if is_bf16 else np.asarray(a, dtype=np.float32)).astype(np.float64)
 
 
-# --------------------------------------------------------------------------- configurations
+# --------------------------------------------------------------------------- workloads
+# Workload ids. They also enter the seeds, so their values are fixed.
+TINY_FP32 = 0       # fp32 recurrence, B=1 H=2 T=256 d=64, no conv, S0 = 0
+PREFILL = 1         # bf16 prefill with conv preprocess and output gate, B=4 H=16 T=4096 d=128
+LONG_CONTEXT = 2    # one bf16 sequence with S0, B=1 H=32 T=65536 d=128
+DECODE = 3          # batched decode, N=256 H=32 d=128, 100 steps, fp32 state in place
+VARLEN = 4          # 64 packed bf16 sequences, log-uniform lengths in [128, 32768], H=16 d=128
+
+TAGS = {TINY_FP32: "tiny", PREFILL: "prefill", LONG_CONTEXT: "long", DECODE: "decode",
+        VARLEN: "varlen"}
+
+
 @dataclass
 class Shape:
     """Sizes of one workload. `lengths` lists every packed sequence length."""
-    cfg: int
+    workload: int
     H: int
     dk: int
     dv: int
@@ -57,9 +68,9 @@ class Shape:
     bf16: bool
     conv: bool            # inputs are pre-conv projected streams (full preprocess)
     has_s0: bool
-    steps: int = 0        # decode steps (config 3 only)
+    steps: int = 0        # decode steps (the decode workload only)
     equal_lengths: bool = True
-    tokens: int = 1       # tokens per sequence per decode step (config 3; > 1: multi-token)
+    tokens: int = 1       # tokens per sequence per decode step (> 1: multi-token)
 
     @property
     def num_seqs(self) -> int:
@@ -74,19 +85,19 @@ class Shape:
 
 
 FULL_SIZES = {
-    0: dict(B=1, H=2, T=256, d=64),
-    1: dict(B=4, H=16, T=4096, d=128),
-    2: dict(B=1, H=32, T=65536, d=128),
-    3: dict(N=256, H=32, d=128, steps=100),
-    4: dict(nseq=64, H=16, d=128, lmin=128, lmax=32768),
+    TINY_FP32: dict(B=1, H=2, T=256, d=64),
+    PREFILL: dict(B=4, H=16, T=4096, d=128),
+    LONG_CONTEXT: dict(B=1, H=32, T=65536, d=128),
+    DECODE: dict(N=256, H=32, d=128, steps=100),
+    VARLEN: dict(nseq=64, H=16, d=128, lmin=128, lmax=32768),
 }
 
-CONFIG_NAMES = {
-    0: "tiny fp32 recurrence (B=1,H=2,T=256,d=64)",
-    1: "bf16 prefill + preprocess + output gate (B=4,H=16,T=4096,d=128)",
-    2: "long-context prefill with S0 (B=1,H=32,T=65536,d=128)",
-    3: "batched decode, 100 steps (N=256,H=32,d=128)",
-    4: "varlen packed prefill, 64 seqs log-uniform [128,32768] (H=16,d=128)",
+WORKLOAD_NAMES = {
+    TINY_FP32: "tiny fp32 recurrence (B=1,H=2,T=256,d=64)",
+    PREFILL: "bf16 prefill + preprocess + output gate (B=4,H=16,T=4096,d=128)",
+    LONG_CONTEXT: "long-context prefill with S0 (B=1,H=32,T=65536,d=128)",
+    DECODE: "batched decode, 100 steps (N=256,H=32,d=128)",
+    VARLEN: "varlen packed prefill, 64 seqs log-uniform [128,32768] (H=16,d=128)",
 }
 
 
@@ -95,31 +106,32 @@ def _varlen_lengths(rng: np.random.Generator, nseq: int, lmin: int, lmax: int) -
     return [int(math.floor(math.exp(x))) for x in u]
 
 
-def make_shape(cfg: int, seed: int = 0, **ov) -> Shape:
-    """Shape of config `cfg`; keyword overrides shrink it for fast tests
+def make_shape(workload: int, seed: int = 0, **ov) -> Shape:
+    """Shape of `workload`; keyword overrides shrink it for fast tests
     (B, H, T, d, N, steps, nseq, lmin, lmax, lengths)."""
-    p = dict(FULL_SIZES[cfg])
+    p = dict(FULL_SIZES[workload])
     p.update({k: v for k, v in ov.items() if v is not None})
     d = p["d"]
     dk = p.get("dk", d)
     dv = p.get("dv", d)
-    if cfg in (0, 1, 2):
+    if workload in (TINY_FP32, PREFILL, LONG_CONTEXT):
         lengths = p.get("lengths") or [p["T"]] * p["B"]
-        return Shape(cfg, p["H"], dk, dv, list(lengths), bf16=(cfg != 0), conv=(cfg == 1),
-                     has_s0=(cfg == 2), equal_lengths=len(set(lengths)) <= 1)
-    if cfg == 3:
+        return Shape(workload, p["H"], dk, dv, list(lengths), bf16=(workload != TINY_FP32),
+                     conv=(workload == PREFILL), has_s0=(workload == LONG_CONTEXT),
+                     equal_lengths=len(set(lengths)) <= 1)
+    if workload == DECODE:
         T = int(p.get("tokens", 1))
-        return Shape(cfg, p["H"], dk, dv, [T] * p["N"], bf16=True, conv=False, has_s0=True,
+        return Shape(workload, p["H"], dk, dv, [T] * p["N"], bf16=True, conv=False, has_s0=True,
                      steps=p["steps"], tokens=T)
-    if cfg == 4:
+    if workload == VARLEN:
         if "lengths" in p and p["lengths"]:
             lengths = list(p["lengths"])
         else:
-            rng = np.random.default_rng(np.random.SeedSequence([SEED_TAG, cfg, seed, 99]))
+            rng = np.random.default_rng(np.random.SeedSequence([SEED_TAG, workload, seed, 99]))
             lengths = _varlen_lengths(rng, p["nseq"], p["lmin"], p["lmax"])
-        return Shape(cfg, p["H"], dk, dv, lengths, bf16=True, conv=True, has_s0=True,
+        return Shape(workload, p["H"], dk, dv, lengths, bf16=True, conv=True, has_s0=True,
                      equal_lengths=False)
-    raise ValueError(f"unknown config {cfg}")
+    raise ValueError(f"unknown workload {workload}")
 
 
 # --------------------------------------------------------------------------- draws
@@ -128,8 +140,8 @@ class _Streams:
     NAMES = ["xq", "xk", "xv", "q", "k", "v", "wq", "wk", "wv", "a_raw", "b_raw", "A_log",
              "z", "norm_weight", "S0"]
 
-    def __init__(self, cfg: int, seed: int):
-        kids = np.random.SeedSequence([SEED_TAG, cfg, seed]).spawn(len(self.NAMES))
+    def __init__(self, workload: int, seed: int):
+        kids = np.random.SeedSequence([SEED_TAG, workload, seed]).spawn(len(self.NAMES))
         self._kids = dict(zip(self.NAMES, kids))
 
     def rng(self, name: str) -> np.random.Generator:
@@ -188,21 +200,21 @@ def _gate_draws(st: _Streams, lead_shape, H: int) -> dict:
     return dict(a_raw=a_raw, b_raw=b_raw, A_log=A_log, dt_bias=dt_bias)
 
 
-def make_inputs(cfg: int, seed: int = 0, **ov) -> dict:
-    """All inputs of config `cfg` as numpy arrays (bf16 tensors as uint16 bits).
+def make_inputs(workload: int, seed: int = 0, **ov) -> dict:
+    """All inputs of `workload` as numpy arrays (bf16 tensors as uint16 bits).
 
-    Keys: "shape" (Shape), "cu_seqlens" (int32 [num_seqs+1]), and per config:
-      0, 2: q, k (unit rows), v, a_raw, b_raw, A_log, dt_bias [, S0]
-      1, 4: xq, xk, xv, wq, wk, wv (conv taps [H*d, 4], tap 3 = current token),
+    Keys: "shape" (Shape), "cu_seqlens" (int32 [num_seqs+1]), and per workload:
+      TINY_FP32, LONG_CONTEXT: q, k (unit rows), v, a_raw, b_raw, A_log, dt_bias [, S0]
+      PREFILL, VARLEN: xq, xk, xv, wq, wk, wv (conv taps [H*d, 4], tap 3 = current token),
             a_raw, b_raw, A_log, dt_bias, z, norm_weight [, S0]
-      3:    state [N,H,dk,dv] and per-step q, k, v [steps,N,H,d], a_raw, b_raw [steps,N,H],
+      DECODE: state [N,H,dk,dv] and per-step q, k, v [steps,N,H,d], a_raw, b_raw [steps,N,H],
             A_log, dt_bias [H]
     """
-    sh = make_shape(cfg, seed, **ov)
-    st = _Streams(cfg, seed)
+    sh = make_shape(workload, seed, **ov)
+    st = _Streams(workload, seed)
     H, dk, dv, ntok = sh.H, sh.dk, sh.dv, sh.ntok
     out: dict = {"shape": sh, "cu_seqlens": sh.cu_seqlens()}
-    if cfg in (0, 2):
+    if workload in (TINY_FP32, LONG_CONTEXT):
         out["q"] = _unit_rows(st.rng("q"), (ntok, H, dk), sh.bf16)
         out["k"] = _unit_rows(st.rng("k"), (ntok, H, dk), sh.bf16)
         v = _normal(st.rng("v"), (ntok, H, dv))
@@ -210,7 +222,7 @@ def make_inputs(cfg: int, seed: int = 0, **ov) -> dict:
         out.update(_gate_draws(st, (ntok,), H))
         if sh.has_s0:
             out["S0"] = _normal(st.rng("S0"), (sh.num_seqs, H, dk, dv), std=0.1)
-    elif cfg in (1, 4):
+    elif workload in (PREFILL, VARLEN):
         out["xq"] = _normal_bf16(st.rng("xq"), (ntok, H, dk))
         out["xk"] = _normal_bf16(st.rng("xk"), (ntok, H, dk))
         out["xv"] = _normal_bf16(st.rng("xv"), (ntok, H, dv))
@@ -224,7 +236,7 @@ def make_inputs(cfg: int, seed: int = 0, **ov) -> dict:
         out["norm_weight"] = _normal(st.rng("norm_weight"), (dv,), std=math.sqrt(0.02))
         if sh.has_s0:
             out["S0"] = _normal(st.rng("S0"), (sh.num_seqs, H, dk, dv), std=0.1)
-    elif cfg == 3:
+    elif workload == DECODE:
         N, S = sh.num_seqs, sh.steps
         lead = (S, N) if sh.tokens == 1 else (S, N, sh.tokens)   # multi-token: [S, N, T, ...]
         out["state"] = _normal(st.rng("S0"), (N, H, dk, dv), std=0.1)
@@ -267,7 +279,7 @@ def conv_state_draw(seed: int, num_seqs: int, H: int, dk: int, dv: int,
 def make_stream_inputs(seed: int, N: int, H: int, prompt_lengths, steps: int, tokens: int,
                        dk: int = 128, dv: int = 128) -> dict:
     """A prompt per sequence followed by `steps` decode steps of `tokens` tokens each, as the
-    pre-conv projected streams of the config-1 distributions (bf16 bits).
+    pre-conv projected streams drawn as in the bf16 prefill workload (bf16 bits).
       prompt: xq, xk [P, H, dk], xv [P, H, dv], a_raw, b_raw [P, H], packed by
               cu_seqlens (lengths prompt_lengths);
       decode: dxq, dxk [steps, N, tokens, H, dk], dxv [..., dv], da_raw, db_raw
@@ -302,7 +314,7 @@ def make_stream_inputs(seed: int, N: int, H: int, prompt_lengths, steps: int, to
 def decode_layer_draws(seed: int, steps: int, N: int, H: int, dk: int = 128, dv: int = 128,
                        bf16: bool = True, tokens: int = 1) -> dict:
     """Raw inputs of `steps` decode steps of the whole token mixer (the fused decode step),
-    with the config-1 distributions: per step xq, xk [steps, N, H, dk], xv, z [steps, N, H, dv]
+    drawn as in the bf16 prefill workload: per step xq, xk [steps, N, H, dk], xv, z [steps, N, H, dv]
     (bf16 bits, or float32 with bf16=False), a_raw, b_raw [steps, N, H] (with tokens > 1, a
     [tokens] axis after N: T tokens per sequence per step); conv taps
     wq, wk, wv [H*d, 4] ~ N(0, 1/4); A_log, dt_bias [H]; norm_weight [dv] ~ N(0, 0.02);

@@ -63,8 +63,8 @@ def _run(inp, grads, bf16_in, bf16_dy, seqs=None, heads=None, with_s0=True, with
 def test_backward_fp32_inputs_ragged(gpu, dims):
     dk, dv = dims
     _announce(f"backward fp32 inputs, lengths [70, 1, 129, 0, 64] H=2 dk={dk} dv={dv}")
-    inp = gi.make_inputs(0, seed=5, H=2, lengths=[70, 1, 129, 0, 64], dk=dk, dv=dv)
-    inp["S0"] = gi.make_inputs(2, seed=5, H=2, T=1, dk=dk, dv=dv)["S0"].repeat(5, axis=0)
+    inp = gi.make_inputs(gi.TINY_FP32, seed=5, H=2, lengths=[70, 1, 129, 0, 64], dk=dk, dv=dv)
+    inp["S0"] = gi.make_inputs(gi.LONG_CONTEXT, seed=5, H=2, T=1, dk=dk, dv=dv)["S0"].repeat(5, axis=0)
     sh = inp["shape"]
     grads = gi.grad_draws(5, sh.ntok, sh.num_seqs, sh.H, dk, dv)
     _run(inp, grads, bf16_in=False, bf16_dy=False)
@@ -73,14 +73,14 @@ def test_backward_fp32_inputs_ragged(gpu, dims):
 @pytest.mark.parametrize("with_s0,with_dst", [(True, True), (False, False)])
 def test_backward_bf16_inputs(gpu, with_s0, with_dst):
     _announce(f"backward bf16 inputs B=1 H=2 T=300 d=128 S0={with_s0} dST={with_dst}")
-    inp = gi.make_inputs(2, seed=6, H=2, T=300)
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=6, H=2, T=300)
     grads = gi.grad_draws(6, 300, 1, 2, 128, 128, bf16=True)
     _run(inp, grads, bf16_in=True, bf16_dy=True, with_s0=with_s0, with_dst=with_dst)
 
 
-def test_backward_config1_shape_sampled(gpu):
-    _announce("backward at the config-1 shape (B=4 H=16 T=4096 d=128), sampled slices")
-    inp = gi.make_inputs(2, seed=7, B=4, H=16, T=4096)
+def test_backward_b4_h16_t4096_sampled(gpu):
+    _announce("backward at B=4 H=16 T=4096 d=128, sampled slices")
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=7, B=4, H=16, T=4096)
     sh = inp["shape"]
     grads = gi.grad_draws(7, sh.ntok, sh.num_seqs, sh.H, 128, 128, bf16=True)
     _run(inp, grads, bf16_in=True, bf16_dy=True, seqs=[0, 3], heads=[2, 13])

@@ -30,7 +30,7 @@ def test_backward_and_kda_are_deterministic(gpu):
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
     _announce("determinism: backward and per-channel decay, lengths [130, 70, 1] H=3 d=128 bf16")
-    inp = gi.make_inputs(2, seed=5, H=3, lengths=[130, 70, 1])
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=5, H=3, lengths=[130, 70, 1])
     sh = inp["shape"]
     q, k, v = (C.dev(inp[x], True) for x in ("q", "k", "v"))
     _, _, _, g, beta = gdn.gdn_preprocess(None, None, None, None, None, None, _f32(inp["a_raw"]),

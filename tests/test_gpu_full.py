@@ -41,34 +41,34 @@ def _check_prefill(inp, res, seqs, heads, y_bf16):
     print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in rep.items()}, flush=True)
 
 
-def test_config1_prefill_pipeline_full(gpu):
-    _announce("config 1 full: B=4 H=16 T=4096 d=128 bf16, preprocess + prefill + output gate")
-    inp = gi.make_inputs(1, seed=0)
+def test_prefill_pipeline_b4_h16_t4096_full(gpu):
+    _announce("bf16 prefill pipeline full: B=4 H=16 T=4096 d=128 bf16, preprocess + prefill + output gate")
+    inp = gi.make_inputs(gi.PREFILL, seed=0)
     res = C.gpu_run(inp, y_dtype="bf16")
     _check_prefill(inp, res, seqs=[0, 3], heads=[0, 9, 15], y_bf16=True)
 
 
-def test_config2_long_context_full(gpu):
-    _announce("config 2 full: B=1 H=32 T=65536 d=128 bf16, S0 ~ N(0, 0.01)")
-    inp = gi.make_inputs(2, seed=0)
+def test_long_context_t65536_full(gpu):
+    _announce("long-context prefill full: B=1 H=32 T=65536 d=128 bf16, S0 ~ N(0, 0.01)")
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=0)
     res = C.gpu_run(inp, y_dtype="bf16")
     _check_prefill(inp, res, seqs=[0], heads=[0, 17, 31], y_bf16=True)
 
 
-def test_config4_varlen_full(gpu):
-    _announce("config 4 full: 64 packed sequences, log-uniform lengths [128, 32768], H=16")
-    inp = gi.make_inputs(4, seed=0)
+def test_varlen_64_seqs_full(gpu):
+    _announce("varlen prefill full: 64 packed sequences, log-uniform lengths [128, 32768], H=16")
+    inp = gi.make_inputs(gi.VARLEN, seed=0)
     L = np.diff(inp["cu_seqlens"])
     seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 5, 40})
     res = C.gpu_run(inp, y_dtype="bf16")
     _check_prefill(inp, res, seqs=seqs, heads=[0, 11], y_bf16=True)
 
 
-def test_config3_decode_100_steps_full(gpu):
+def test_decode_n256_100_steps_full(gpu):
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
-    _announce("config 3 full: decode N=256 H=32 d=128, 100 steps, fp32 state in place")
-    inp = gi.make_inputs(3, seed=0)
+    _announce("batched decode full: N=256 H=32 d=128, 100 steps, fp32 state in place")
+    inp = gi.make_inputs(gi.DECODE, seed=0)
     sh = inp["shape"]
     S_, N, H = sh.steps, sh.num_seqs, sh.H
     state = C.dev(inp["state"])

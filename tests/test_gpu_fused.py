@@ -60,27 +60,28 @@ def _equal_to_pipeline(fused, sep):
 
 
 PREFILL_CASES = [
-    (1, dict(B=2, H=3, T=200)),                                      # one head per workgroup
-    (1, dict(B=2, H=4, T=300)),                                      # four heads per workgroup
-    (1, dict(B=2, H=2, T=150, dv=64)),                               # two heads, dv = 64
-    (4, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130])),      # empty/short seqs, S0
-    (4, dict(H=4, nseq=5, lmax=600)),
+    (gi.PREFILL, dict(B=2, H=3, T=200)),                                      # one head per workgroup
+    (gi.PREFILL, dict(B=2, H=4, T=300)),                                      # four heads per workgroup
+    (gi.PREFILL, dict(B=2, H=2, T=150, dv=64)),                               # two heads, dv = 64
+    (gi.VARLEN, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130])),      # empty/short seqs, S0
+    (gi.VARLEN, dict(H=4, nseq=5, lmax=600)),
 ]
 
 
-@pytest.mark.parametrize("cfg,ov", PREFILL_CASES, ids=[f"cfg{c}-{o}" for c, o in PREFILL_CASES])
-def test_fused_prefill(gpu, cfg, ov):
-    _announce(f"fused prefill cfg={cfg} {ov}")
-    inp = gi.make_inputs(cfg, seed=1, **ov)
+@pytest.mark.parametrize("workload,ov", PREFILL_CASES,
+                         ids=[f"{gi.TAGS[w]}-{o}" for w, o in PREFILL_CASES])
+def test_fused_prefill(gpu, workload, ov):
+    _announce(f"fused prefill {gi.TAGS[workload]} {ov}")
+    inp = gi.make_inputs(workload, seed=1, **ov)
     fused = C.gpu_run_fused(inp)
     _compare_to_oracle(inp, fused, C.subset(inp))
     _equal_to_pipeline(fused, C.gpu_run(inp, y_dtype="bf16"))
 
 
 @pytest.mark.slow
-def test_fused_prefill_config1_full(gpu):
+def test_fused_prefill_b4_h16_t4096_full(gpu):
     _announce("fused prefill at B=4 H=16 T=4096 d=128 (bf16), sampled slices")
-    inp = gi.make_inputs(1, seed=0)
+    inp = gi.make_inputs(gi.PREFILL, seed=0)
     fused = C.gpu_run_fused(inp)
     _compare_to_oracle(inp, fused, C.subset(inp, seqs=[0, 3], heads=[0, 9, 15]))
     _equal_to_pipeline(fused, C.gpu_run(inp, y_dtype="bf16"))

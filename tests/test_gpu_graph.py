@@ -74,7 +74,7 @@ def test_decode_step_and_prefill_replay(gpu):
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
     _announce("graph replay of gdn_decode_step and of gdn_chunk_prefill (bf16, B=2 H=4 T=200)")
-    di = gi.make_inputs(3, seed=32, N=8, H=4, steps=3)
+    di = gi.make_inputs(gi.DECODE, seed=32, N=8, H=4, steps=3)
     bf = lambda a: C.dev(a, True)                                              # noqa: E731
     f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))            # noqa: E731
     g_ = -torch.rand((3, 8, 4), device="cuda") * 0.3
@@ -99,7 +99,7 @@ def test_decode_step_and_prefill_replay(gpu):
         assert torch.equal(y, y_ref[s]), f"decode replay {s}"
     assert torch.equal(state, state_e)
 
-    inp = gi.make_inputs(2, seed=33, B=2, H=4, T=200)
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=33, B=2, H=4, T=200)
     sh = inp["shape"]
     qp, kp, vp = bf(inp["q"]), bf(inp["k"]), bf(inp["v"])
     _, _, _, gp, bp = gdn.gdn_preprocess(None, None, None, None, None, None, f32(inp["a_raw"]),

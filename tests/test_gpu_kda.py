@@ -56,8 +56,8 @@ def _case(inp, g, bf16, y_dtype, seqs=None, heads=None):
 def test_kda_fp32_ragged(gpu, dims):
     dk, dv = dims
     _announce(f"kda fp32 inputs, lengths [70, 1, 129, 0, 64] H=2 dk={dk} dv={dv}")
-    inp = gi.make_inputs(0, seed=8, H=2, lengths=[70, 1, 129, 0, 64], dk=dk, dv=dv)
-    inp["S0"] = gi.make_inputs(2, seed=8, H=2, T=1, dk=dk, dv=dv)["S0"].repeat(5, axis=0)
+    inp = gi.make_inputs(gi.TINY_FP32, seed=8, H=2, lengths=[70, 1, 129, 0, 64], dk=dk, dv=dv)
+    inp["S0"] = gi.make_inputs(gi.LONG_CONTEXT, seed=8, H=2, T=1, dk=dk, dv=dv)["S0"].repeat(5, axis=0)
     g = gi.kda_log_decay_draw(8, inp["shape"].ntok, 2, dk)
     _case(inp, g, bf16=False, y_dtype="f32")
 
@@ -66,7 +66,7 @@ def test_kda_steep_decays(gpu):
     """Log-decays far below the KDA bound (down to -60 per token): the kernels form only
     exponentials of non-positive differences, so nothing overflows however steep the decay."""
     _announce("kda fp32 inputs with steep per-channel decays, lengths [130, 64, 7] H=2 d=128")
-    inp = gi.make_inputs(0, seed=10, H=2, lengths=[130, 64, 7], d=128)
+    inp = gi.make_inputs(gi.TINY_FP32, seed=10, H=2, lengths=[130, 64, 7], d=128)
     g = gi.kda_log_decay_draw(10, inp["shape"].ntok, 2, 128, mean=1.0, cap=60.0)
     assert g.min() < -30.0
     _case(inp, g, False, "f32")
@@ -74,7 +74,7 @@ def test_kda_steep_decays(gpu):
 
 def test_kda_bf16_long(gpu):
     _announce("kda bf16 inputs B=1 H=2 T=1000 d=128, S0, bf16 y")
-    inp = gi.make_inputs(2, seed=9, H=2, T=1000)
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=9, H=2, T=1000)
     g = gi.kda_log_decay_draw(9, 1000, 2, 128)
     _case(inp, g, bf16=True, y_dtype="bf16")
 
@@ -83,7 +83,7 @@ def test_kda_equal_channel_decays_match_the_scalar_path(gpu):
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
     _announce("kda with one decay per head equals gdn_chunk_prefill (fp32 path)")
-    inp = gi.make_inputs(0, seed=10, H=2, lengths=[200, 77])
+    inp = gi.make_inputs(gi.TINY_FP32, seed=10, H=2, lengths=[200, 77])
     sh = inp["shape"]
     q, k, v = (C.dev(inp[x]) for x in ("q", "k", "v"))
     _, _, _, g, beta = gdn.gdn_preprocess(None, None, None, None, None, None, _f32(inp["a_raw"]),
@@ -98,8 +98,8 @@ def test_kda_equal_channel_decays_match_the_scalar_path(gpu):
     assert np.abs(C.host(s1) - C.host(s2)).max() / np.abs(C.host(s1)).max() < 1e-5
 
 
-def test_kda_config1_shape_sampled(gpu):
-    _announce("kda at the config-1 shape (B=4 H=16 T=4096 d=128, bf16), sampled slices")
-    inp = gi.make_inputs(2, seed=11, B=4, H=16, T=4096)
+def test_kda_b4_h16_t4096_sampled(gpu):
+    _announce("kda at B=4 H=16 T=4096 d=128 (bf16), sampled slices")
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=11, B=4, H=16, T=4096)
     g = gi.kda_log_decay_draw(11, 4 * 4096, 16, 128)
     _case(inp, g, bf16=True, y_dtype="bf16", seqs=[1, 2], heads=[0, 7])

@@ -47,26 +47,27 @@ def _compare_prefill(inp, res, ref, sub, y_bf16, ref_st=None):
 
 
 CASES = [
-    # (cfg, overrides, y dtype)
-    (0, {}, "f32"),
-    (0, dict(T=200, d=128), "f32"),
-    (0, dict(B=3, T=130, d=64), "f32"),
-    (1, dict(B=2, H=3, T=200), "f32"),
-    (1, dict(B=2, H=3, T=200), "bf16"),
-    (1, dict(B=1, H=2, T=70, d=64), "f32"),
-    (2, dict(H=2, T=1000), "f32"),
+    # (workload, overrides, y dtype)
+    (gi.TINY_FP32, {}, "f32"),
+    (gi.TINY_FP32, dict(T=200, d=128), "f32"),
+    (gi.TINY_FP32, dict(B=3, T=130, d=64), "f32"),
+    (gi.PREFILL, dict(B=2, H=3, T=200), "f32"),
+    (gi.PREFILL, dict(B=2, H=3, T=200), "bf16"),
+    (gi.PREFILL, dict(B=1, H=2, T=70, d=64), "f32"),
+    (gi.LONG_CONTEXT, dict(H=2, T=1000), "f32"),
     # d_k = 128, d_v = 64 on the matrix-core path: two 32-column slices per head
-    (1, dict(B=2, H=2, T=150, dv=64), "bf16"),
-    (2, dict(H=3, T=330, dv=64), "f32"),
-    (4, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130]), "f32"),
-    (4, dict(H=2, nseq=5, lmax=600), "bf16"),
+    (gi.PREFILL, dict(B=2, H=2, T=150, dv=64), "bf16"),
+    (gi.LONG_CONTEXT, dict(H=3, T=330, dv=64), "f32"),
+    (gi.VARLEN, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130]), "f32"),
+    (gi.VARLEN, dict(H=2, nseq=5, lmax=600), "bf16"),
 ]
 
 
-@pytest.mark.parametrize("cfg,ov,ydt", CASES, ids=[f"cfg{c}-{o}-{y}" for c, o, y in CASES])
-def test_prefill_pipeline_parity(gpu, cfg, ov, ydt):
-    _announce(f"prefill cfg={cfg} {ov} y={ydt}")
-    inp = gi.make_inputs(cfg, seed=0, **ov)
+@pytest.mark.parametrize("workload,ov,ydt", CASES,
+                         ids=[f"{gi.TAGS[w]}-{o}-{y}" for w, o, y in CASES])
+def test_prefill_pipeline_parity(gpu, workload, ov, ydt):
+    _announce(f"prefill {gi.TAGS[workload]} {ov} y={ydt}")
+    inp = gi.make_inputs(workload, seed=0, **ov)
     res = C.gpu_run(inp, y_dtype=ydt)
     sub = C.subset(inp)
     ref = C.oracle_run(sub)
@@ -80,7 +81,7 @@ def test_decode_steps_parity(gpu, ov, ydt):
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
     _announce(f"decode {ov} y={ydt}")
-    inp = gi.make_inputs(3, seed=0, **ov)
+    inp = gi.make_inputs(gi.DECODE, seed=0, **ov)
     sh = inp["shape"]
     S_, N, H = sh.steps, sh.num_seqs, sh.H
     state = C.dev(inp["state"])
@@ -113,8 +114,8 @@ def test_decode_steps_parity(gpu, ov, ydt):
 
 
 def test_prefill_is_deterministic(gpu):
-    _announce("determinism cfg1 small")
-    inp = gi.make_inputs(1, seed=3, B=2, H=2, T=150)
+    _announce("determinism: bf16 prefill pipeline B=2 H=2 T=150")
+    inp = gi.make_inputs(gi.PREFILL, seed=3, B=2, H=2, T=150)
     a = C.gpu_run(inp, y_dtype="f32")
     b = C.gpu_run(inp, y_dtype="f32")
     for key in ("q", "k", "v", "y", "ST", "o"):

@@ -36,7 +36,7 @@ def test_preprocess_stateful_varlen(gpu, with_hist, dims):
     dk, dv = dims
     lengths = [0, 1, 2, 3, 67, 130, 1, 64]      # empty and shorter-than-history sequences
     _announce(f"preprocess_stateful lengths={lengths} H=2 dk={dk} dv={dv} hist={with_hist}")
-    inp = gi.make_inputs(4, seed=3, H=2, dk=dk, dv=dv, lengths=lengths)
+    inp = gi.make_inputs(gi.VARLEN, seed=3, H=2, dk=dk, dv=dv, lengths=lengths)
     sh = inp["shape"]
     H, cu = sh.H, inp["cu_seqlens"]
     hist = gi.conv_state_draw(5, sh.num_seqs, H, dk, dv) if with_hist else None
@@ -62,8 +62,8 @@ def test_preprocess_stateful_varlen(gpu, with_hist, dims):
 
 # ----------------------------------------------------------------------------- decode
 def _decode_case(N, T, H, dk, dv, bf16, seed):
-    """Raw draws of one multi-token decode step (the config-3 distributions)."""
-    inp = gi.make_inputs(3, seed=seed, N=N, H=H, dk=dk, dv=dv, steps=1, tokens=T)
+    """Raw draws of one multi-token decode step (drawn as in the batched decode workload)."""
+    inp = gi.make_inputs(gi.DECODE, seed=seed, N=N, H=H, dk=dk, dv=dv, steps=1, tokens=T)
     q, k, v = (inp[x][0].reshape(N, T, H, -1) for x in "qkv")   # [N, T, H, d] bf16 bits
     if not bf16:                                              # fp32 inputs: the same values
         q, k, v = (gi.bf16_bits_to_f32(x) for x in (q, k, v))

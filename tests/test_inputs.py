@@ -17,29 +17,29 @@ def test_bf16_cast_matches_torch_round_to_nearest_even():
 
 
 def test_deterministic_and_seed_dependent():
-    a = gi.checksums(gi.make_inputs(1, 0, B=2, H=2, T=70))
-    b = gi.checksums(gi.make_inputs(1, 0, B=2, H=2, T=70))
-    c = gi.checksums(gi.make_inputs(1, 1, B=2, H=2, T=70))
+    a = gi.checksums(gi.make_inputs(gi.PREFILL, 0, B=2, H=2, T=70))
+    b = gi.checksums(gi.make_inputs(gi.PREFILL, 0, B=2, H=2, T=70))
+    c = gi.checksums(gi.make_inputs(gi.PREFILL, 1, B=2, H=2, T=70))
     assert a == b
     assert a["xq"] != c["xq"]
 
 
 def test_shapes_and_distributions():
-    i0 = gi.make_inputs(0)
+    i0 = gi.make_inputs(gi.TINY_FP32)
     assert i0["q"].shape == (256, 2, 64) and i0["q"].dtype == np.float32
     assert np.allclose(np.linalg.norm(i0["q"].astype(np.float64), axis=-1), 1.0, atol=1e-6)
     assert np.all((np.exp(i0["A_log"]) >= 1) & (np.exp(i0["A_log"]) <= 16))
-    i2 = gi.make_inputs(2, H=2, T=200)
+    i2 = gi.make_inputs(gi.LONG_CONTEXT, H=2, T=200)
     assert i2["k"].dtype == np.uint16 and i2["S0"].shape == (1, 2, 128, 128)
-    i3 = gi.make_inputs(3, N=4, H=2, steps=3)
+    i3 = gi.make_inputs(gi.DECODE, N=4, H=2, steps=3)
     assert i3["q"].shape == (3, 4, 2, 128) and i3["state"].shape == (4, 2, 128, 128)
-    i4 = gi.make_inputs(4, nseq=8, H=2, lmax=300)
+    i4 = gi.make_inputs(gi.VARLEN, nseq=8, H=2, lmax=300)
     L = np.diff(i4["cu_seqlens"])
     assert len(L) == 8 and L.min() >= 128 and L.max() <= 300
     assert i4["xq"].shape[0] == i4["cu_seqlens"][-1]
 
 
-def test_full_config4_lengths():
-    sh = gi.make_shape(4)
+def test_varlen_full_lengths():
+    sh = gi.make_shape(gi.VARLEN)
     assert sh.num_seqs == 64
     assert 128 <= min(sh.lengths) and max(sh.lengths) <= 32768
