@@ -75,11 +75,14 @@ __device__ void kda_seq(const KdaArgs& a, int s, int& lo, int& hi, int& cbase) {
     }
 }
 
+// packed chunk index c -> its token range; false if c is past the last chunk (one pass over
+// the sequences, so the cost per workgroup is linear in their number)
 __device__ bool kda_chunk(const KdaArgs& a, int c, int& t0, int& n) {
     int base = 0;
+    const int L = a.cu ? 0 : a.ntok / a.num_seqs;
     for (int s = 0; s < a.num_seqs; ++s) {
-        int lo, hi, cb;
-        kda_seq(a, s, lo, hi, cb);
+        const int lo = a.cu ? a.cu[s] : s * L;
+        const int hi = a.cu ? a.cu[s + 1] : lo + L;
         const int nc = (hi - lo + kC - 1) / kC;
         if (c < base + nc) {
             t0 = lo + (c - base) * kC;

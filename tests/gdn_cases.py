@@ -217,3 +217,49 @@ def gpu_state_slice(t, seqs, heads):
     import torch
     return host(t.index_select(0, torch.as_tensor(seqs, device=t.device))
                 .index_select(1, torch.as_tensor(heads, device=t.device)))
+
+
+# ----------------------------------------------------------------------------- many sequences
+def many_short_lengths(seed: int, nseq: int, lmax: int = 70) -> list[int]:
+    """nseq seeded lengths in [0, lmax], with an empty sequence first and lengths 64 and 65
+    (a full chunk, one token past it) next: a packing of many short sequences, as in serving."""
+    rng = np.random.default_rng(np.random.SeedSequence([0x6D616E79, seed, nseq]))
+    L = [int(x) for x in rng.integers(0, lmax + 1, size=nseq)]
+    L[0], L[1], L[2], L[-1] = 0, 64, 65, 1
+    return L
+
+
+def sampled_seqs(lengths, seed: int, extra: int = 6) -> list[int]:
+    """Sequences to check against the oracle: the ends, both sides of 256 and 1024 (the chunk
+    table's scan rounds and its longest-first limit), and a few seeded picks."""
+    n = len(lengths)
+    fixed = {0, 1, 2, 255, 256, 257, 1023, 1024, 1025, n - 1}
+    rng = np.random.default_rng(np.random.SeedSequence([0x73656C, seed, n]))
+    picks = set(int(x) for x in rng.integers(0, n, size=extra))
+    return sorted(i for i in fixed | picks if 0 <= i < n)
+
+
+def check_prefill_sampled(inp, res, seqs, heads, y_bf16):
+    """Sampled (sequence, head) slices of a pipeline run against the oracle on just those."""
+    sh = inp["shape"]
+    sub = subset(inp, seqs=seqs, heads=heads)
+    ref = oracle_run(sub)
+    tok, cu, H = sub["tok"], sub["cu"], sub["H"]
+    rep = {}
+    if sh.conv:
+        for key in ("q", "k", "v"):
+            rep[key] = assert_close(key, gpu_slice(res[key], tok, heads), ref[key], True,
+                                    stored_bf16=True, cu=cu, H=H)
+    for key in ("g", "beta"):
+        got = gpu_slice(res[key], tok, heads)
+        assert np.abs(got - ref[key]).max() / np.abs(ref[key]).max() < 1e-5, key
+    rep["y"] = assert_close("y", gpu_slice(res["y"], tok, heads), ref["y"], sh.bf16,
+                            stored_bf16=y_bf16, cu=cu, H=H)
+    rep["ST"] = assert_close("ST", gpu_state_slice(res["ST"], seqs, heads), ref["ST"], sh.bf16,
+                             state=True)
+    if "o" in res:
+        st = oracle_run(sub, storage_bf16=True, y_bf16=y_bf16)
+        rep["o"] = assert_close("o", gpu_slice(res["o"], tok, heads), ref["o"], True,
+                                stored_bf16=True, cu=cu, H=H, ref_elem=st["o"],
+                                inherits_bf16_input=y_bf16)
+    print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in rep.items()}, flush=True)

@@ -108,3 +108,14 @@ def test_backward_of_no_tokens_passes_the_state_gradient_through(gpu):
         assert st == 0, L.gdn_last_error()
         ref = torch.zeros_like(dS0) if src is None else src
         assert torch.equal(dS0, ref)
+
+
+def test_backward_many_sequences(gpu):
+    """1300 short packed sequences (empty ones included), fp32 inputs, sampled sequences."""
+    L = C.many_short_lengths(14, 1300)
+    _announce("backward 1300 packed sequences, lengths 0..70, H=2 d=64, fp32 inputs, S0, dS_T")
+    inp = gi.make_inputs(gi.TINY_FP32, seed=14, H=2, lengths=L)
+    inp["S0"] = gi.make_inputs(gi.LONG_CONTEXT, seed=14, B=len(L), H=2, T=1, d=64)["S0"]
+    sh = inp["shape"]
+    grads = gi.grad_draws(14, sh.ntok, sh.num_seqs, 2, 64, 64)
+    _run(inp, grads, bf16_in=False, bf16_dy=False, seqs=C.sampled_seqs(L, 14))

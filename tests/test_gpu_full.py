@@ -17,42 +17,18 @@ def _announce(msg):
     sys.stdout.flush()
 
 
-def _check_prefill(inp, res, seqs, heads, y_bf16):
-    sh = inp["shape"]
-    sub = C.subset(inp, seqs=seqs, heads=heads)
-    ref = C.oracle_run(sub)
-    tok, cu, H = sub["tok"], sub["cu"], sub["H"]
-    rep = {}
-    if sh.conv:
-        for key in ("q", "k", "v"):
-            rep[key] = C.assert_close(key, C.gpu_slice(res[key], tok, heads), ref[key], True,
-                                      stored_bf16=True, cu=cu, H=H)
-    for key in ("g", "beta"):
-        got = C.gpu_slice(res[key], tok, heads)
-        assert np.abs(got - ref[key]).max() / np.abs(ref[key]).max() < 1e-5, key
-    rep["y"] = C.assert_close("y", C.gpu_slice(res["y"], tok, heads), ref["y"], sh.bf16,
-                              stored_bf16=y_bf16, cu=cu, H=H)
-    rep["ST"] = C.assert_close("ST", C.gpu_state_slice(res["ST"], seqs, heads), ref["ST"], sh.bf16,
-                               state=True)
-    if "o" in res:
-        st = C.oracle_run(sub, storage_bf16=True, y_bf16=y_bf16)
-        rep["o"] = C.assert_close("o", C.gpu_slice(res["o"], tok, heads), ref["o"], True,
-                                  stored_bf16=True, cu=cu, H=H, ref_elem=st["o"], inherits_bf16_input=y_bf16)
-    print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in rep.items()}, flush=True)
-
-
 def test_prefill_pipeline_b4_h16_t4096_full(gpu):
     _announce("bf16 prefill pipeline full: B=4 H=16 T=4096 d=128 bf16, preprocess + prefill + output gate")
     inp = gi.make_inputs(gi.PREFILL, seed=0)
     res = C.gpu_run(inp, y_dtype="bf16")
-    _check_prefill(inp, res, seqs=[0, 3], heads=[0, 9, 15], y_bf16=True)
+    C.check_prefill_sampled(inp, res, seqs=[0, 3], heads=[0, 9, 15], y_bf16=True)
 
 
 def test_long_context_t65536_full(gpu):
     _announce("long-context prefill full: B=1 H=32 T=65536 d=128 bf16, S0 ~ N(0, 0.01)")
     inp = gi.make_inputs(gi.LONG_CONTEXT, seed=0)
     res = C.gpu_run(inp, y_dtype="bf16")
-    _check_prefill(inp, res, seqs=[0], heads=[0, 17, 31], y_bf16=True)
+    C.check_prefill_sampled(inp, res, seqs=[0], heads=[0, 17, 31], y_bf16=True)
 
 
 def test_varlen_64_seqs_full(gpu):
@@ -61,7 +37,7 @@ def test_varlen_64_seqs_full(gpu):
     L = np.diff(inp["cu_seqlens"])
     seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 5, 40})
     res = C.gpu_run(inp, y_dtype="bf16")
-    _check_prefill(inp, res, seqs=seqs, heads=[0, 11], y_bf16=True)
+    C.check_prefill_sampled(inp, res, seqs=seqs, heads=[0, 11], y_bf16=True)
 
 
 def test_decode_n256_100_steps_full(gpu):

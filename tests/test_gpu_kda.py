@@ -103,3 +103,13 @@ def test_kda_b4_h16_t4096_sampled(gpu):
     inp = gi.make_inputs(gi.LONG_CONTEXT, seed=11, B=4, H=16, T=4096)
     g = gi.kda_log_decay_draw(11, 4 * 4096, 16, 128)
     _case(inp, g, bf16=True, y_dtype="bf16", seqs=[1, 2], heads=[0, 7])
+
+
+def test_kda_many_sequences(gpu):
+    """1300 short packed sequences (empty ones included), fp32 inputs, sampled sequences."""
+    L = C.many_short_lengths(13, 1300)
+    _announce("kda 1300 packed sequences, lengths 0..70, H=2 d=64, fp32 inputs, S0")
+    inp = gi.make_inputs(gi.TINY_FP32, seed=13, H=2, lengths=L)
+    inp["S0"] = gi.make_inputs(gi.LONG_CONTEXT, seed=13, B=len(L), H=2, T=1, d=64)["S0"]
+    g = gi.kda_log_decay_draw(13, inp["shape"].ntok, 2, 64)
+    _case(inp, g, False, "f32", seqs=C.sampled_seqs(L, 13))

@@ -120,3 +120,17 @@ def test_prefill_is_deterministic(gpu):
     b = C.gpu_run(inp, y_dtype="f32")
     for key in ("q", "k", "v", "y", "ST", "o"):
         assert np.array_equal(C.host(a[key]), C.host(b[key])), key
+
+
+@pytest.mark.parametrize("nseq,bf16", [(300, True), (1300, True), (1300, False)])
+def test_prefill_many_sequences(gpu, nseq, bf16):
+    """Many short packed sequences (empty ones included): more than 256 runs the chunk
+    table's scan over several rounds, more than 1024 skips its longest-first ordering."""
+    L = C.many_short_lengths(11, nseq)
+    _announce(f"prefill {nseq} packed sequences, lengths 0..70, H=2, bf16={bf16}")
+    if bf16:   # the full pipeline on the matrix-core path, with S0
+        inp = gi.make_inputs(gi.VARLEN, seed=12, H=2, lengths=L)
+    else:      # fp32 q, k, v with d = 64 on the fp32 path
+        inp = gi.make_inputs(gi.TINY_FP32, seed=12, H=2, lengths=L)
+    res = C.gpu_run(inp, y_dtype="bf16" if bf16 else "f32")
+    C.check_prefill_sampled(inp, res, C.sampled_seqs(L, 12), [0, 1], y_bf16=bf16)
