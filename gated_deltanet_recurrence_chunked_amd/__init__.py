@@ -130,6 +130,25 @@ def _ptr(t, name, dtype=None, device=True):
     return t.data_ptr() or None
 
 
+def _shape(name, t, *shape):
+    """The kernels see bare pointers, so every tensor's extent is checked here, on the host:
+    raise unless t (when given) has exactly this shape."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise GdnError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _same_dtype(ref_name, ref, **others):
+    for name, t in others.items():
+        if t is not None and t.dtype != ref.dtype:
+            raise GdnError(f"{name} must have the dtype of {ref_name} ({ref.dtype}, got {t.dtype})")
+
+
+def _packing(cu_seqlens, cu_seqlens_host, num_seqs):
+    _shape("cu_seqlens", cu_seqlens, num_seqs + 1)
+    if cu_seqlens_host is not None and len(cu_seqlens_host) != num_seqs + 1:
+        raise GdnError(f"cu_seqlens_host has {len(cu_seqlens_host)} entries, expected {num_seqs + 1}")
+
+
 def _stream(stream=None) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -170,6 +189,23 @@ def gdn_preprocess(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, *, H, c
     o_tag = _tag(out_dtype)
     if outs is None:
         outs = {}
+    if conv:
+        _shape("xq", xq, ntok, H, dk)
+        _shape("xk", xk, ntok, H, dk)
+        _shape("xv", xv, ntok, H, dv)
+        _same_dtype("xq", xq, xk=xk, xv=xv)
+        _shape("wq", wq, H * dk, 4)
+        _shape("wk", wk, H * dk, 4)
+        _shape("wv", wv, H * dv, 4)
+    if gates:
+        _shape("a_raw", a_raw, ntok, H)
+        _shape("b_raw", b_raw, ntok, H)
+        _shape("A_log", A_log, H)
+        _shape("dt_bias", dt_bias, H)
+    _packing(cu_seqlens, None, num_seqs)
+    for name, shp in (("q", (ntok, H, dk)), ("k", (ntok, H, dk)), ("v", (ntok, H, dv)),
+                      ("g", (ntok, H)), ("beta", (ntok, H))):
+        _shape(name, outs.get(name), *shp)
     q = k = v = g = beta = None
     if conv:
         q = outs.get("q", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
@@ -205,6 +241,24 @@ def gdn_preprocess_stateful(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias
     if conv_state_out is True:
         conv_state_out = torch.empty((num_seqs, 3, H * (2 * dk + dv)), dtype=xq.dtype, device=dev)
     outs = {} if outs is None else outs
+    _shape("xq", xq, ntok, H, dk)
+    _shape("xk", xk, ntok, H, dk)
+    _shape("xv", xv, ntok, H, dv)
+    _same_dtype("xq", xq, xk=xk, xv=xv)
+    _shape("wq", wq, H * dk, 4)
+    _shape("wk", wk, H * dk, 4)
+    _shape("wv", wv, H * dv, 4)
+    if a_raw is not None:
+        _shape("a_raw", a_raw, ntok, H)
+        _shape("b_raw", b_raw, ntok, H)
+        _shape("A_log", A_log, H)
+        _shape("dt_bias", dt_bias, H)
+    _shape("conv_state_in", conv_state_in, num_seqs, 3, H * (2 * dk + dv))
+    _shape("conv_state_out", conv_state_out, num_seqs, 3, H * (2 * dk + dv))
+    _packing(cu_seqlens, None, num_seqs)
+    for name, shp in (("q", (ntok, H, dk)), ("k", (ntok, H, dk)), ("v", (ntok, H, dv)),
+                      ("g", (ntok, H)), ("beta", (ntok, H))):
+        _shape(name, outs.get(name), *shp)
     q = outs.get("q", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
     k = outs.get("k", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
     v = outs.get("v", torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=dev))
@@ -239,6 +293,15 @@ def gdn_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
     in_tag = _dtype_tag(q)
     y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
     dev = q.device
+    _shape("k", k, ntok, H, dk)
+    _shape("v", v, ntok, H, dv)
+    _same_dtype("q", q, k=k, v=v)
+    _shape("g", g, ntok, H)
+    _shape("beta", beta, ntok, H)
+    _shape("initial_state", initial_state, num_seqs, H, dk, dv)
+    _shape("final_state", final_state, num_seqs, H, dk, dv)
+    _shape("y", y, ntok, H, dv)
+    _packing(cu_seqlens, cu_seqlens_host, num_seqs)
     if y is None:
         y = torch.empty((ntok, H, dv), dtype=_tag_dtype(y_tag), device=dev)
     if final_state is None and output_final_state:
@@ -274,6 +337,15 @@ def gdn_chunk_backward(q, k, v, g, beta, dy, *, initial_state=None, dfinal_state
     ntok, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
+    _shape("k", k, ntok, H, dk)
+    _shape("v", v, ntok, H, dv)
+    _same_dtype("q", q, k=k, v=v)
+    _shape("g", g, ntok, H)
+    _shape("beta", beta, ntok, H)
+    _shape("dy", dy, ntok, H, dv)
+    _shape("initial_state", initial_state, num_seqs, H, dk, dv)
+    _shape("dfinal_state", dfinal_state, num_seqs, H, dk, dv)
+    _packing(cu_seqlens, cu_seqlens_host, num_seqs)
     f32 = torch.float32
     out = dict(dq=torch.empty((ntok, H, dk), dtype=f32, device=dev),
                dk=torch.empty((ntok, H, dk), dtype=f32, device=dev),
@@ -312,6 +384,14 @@ def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, cu_seqlens=No
     in_tag = _dtype_tag(q)
     y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
     dev = q.device
+    _shape("k", k, ntok, H, dk)
+    _shape("v", v, ntok, H, dv)
+    _same_dtype("q", q, k=k, v=v)
+    _shape("g", g, ntok, H, dk)
+    _shape("beta", beta, ntok, H)
+    _shape("initial_state", initial_state, num_seqs, H, dk, dv)
+    _shape("y", y, ntok, H, dv)
+    _packing(cu_seqlens, cu_seqlens_host, num_seqs)
     if y is None:
         y = torch.empty((ntok, H, dv), dtype=_tag_dtype(y_tag), device=dev)
     final_state = (torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
@@ -339,6 +419,13 @@ def gdn_decode_step(q, k, v, g, beta, state, *, y=None, y_dtype=None, stream=Non
     state: [N,H,dk,dv] fp32 updated in place. Returns y [N,H,dv]."""
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _shape("k", k, N, H, dk)
+    _shape("v", v, N, H, dv)
+    _same_dtype("q", q, k=k, v=v)
+    _shape("g", g, N, H)
+    _shape("beta", beta, N, H)
+    _shape("state", state, N, H, dk, dv)
+    _shape("y", y, N, H, dv)
     in_tag = _dtype_tag(q)
     y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
     if y is None:
@@ -359,6 +446,15 @@ def gdn_decode_multi(q, k, v, g, beta, state, *, y=None, y_dtype=None, step_stat
     Returns (y [N,T,H,dv], step_states)."""
     N, T, H, dk = q.shape
     dv = v.shape[-1]
+    _shape("k", k, N, T, H, dk)
+    _shape("v", v, N, T, H, dv)
+    _same_dtype("q", q, k=k, v=v)
+    _shape("g", g, N, T, H)
+    _shape("beta", beta, N, T, H)
+    _shape("state", state, N, H, dk, dv)
+    _shape("y", y, N, T, H, dv)
+    if step_states is not True:
+        _shape("step_states", step_states, N, T, H, dk, dv)
     in_tag = _dtype_tag(q)
     y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
     if y is None:
@@ -377,6 +473,9 @@ def gdn_decode_multi(q, k, v, g, beta, state, *, y=None, y_dtype=None, step_stat
 def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream=None):
     """eq. 11 without W_o. y, z: [ntok,H,dv]; norm_weight: [dv] fp32. Returns o."""
     ntok, H, dv = y.shape
+    _shape("z", z, ntok, H, dv)
+    _shape("norm_weight", norm_weight, dv)
+    _shape("o", o, ntok, H, dv)
     o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else _dtype_tag(y))
     if o is None:
         o = torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=y.device)
@@ -401,6 +500,22 @@ def gdn_fused_prefill(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, z, n
     ntok = xq.shape[0]
     dk, dv = xq.shape[-1], xv.shape[-1]
     dev = xq.device
+    _shape("xq", xq, ntok, H, dk)
+    _shape("xk", xk, ntok, H, dk)
+    _shape("xv", xv, ntok, H, dv)
+    _same_dtype("xq", xq, xk=xk, xv=xv)
+    _shape("wq", wq, H * dk, 4)
+    _shape("wk", wk, H * dk, 4)
+    _shape("wv", wv, H * dv, 4)
+    _shape("a_raw", a_raw, ntok, H)
+    _shape("b_raw", b_raw, ntok, H)
+    _shape("A_log", A_log, H)
+    _shape("dt_bias", dt_bias, H)
+    _shape("z", z, ntok, H, dv)
+    _shape("norm_weight", norm_weight, dv)
+    _shape("initial_state", initial_state, num_seqs, H, dk, dv)
+    _shape("o", o, ntok, H, dv)
+    _packing(cu_seqlens, cu_seqlens_host, num_seqs)
     if o is None:
         o = torch.empty((ntok, H, dv), dtype=_tag_dtype(_tag(o_dtype)), device=dev)
     final_state = (torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
@@ -446,8 +561,21 @@ def gdn_fused_decode(xq, xk, xv, wq, wk, wv, conv_state, a_raw, b_raw, A_log, dt
     N, H, dk = xq.shape
     dv = xv.shape[-1]
     x_tag = _dtype_tag(xq)
-    if z.dtype != xq.dtype:
-        raise GdnError("z must have the dtype of xq")
+    _shape("xk", xk, N, H, dk)
+    _shape("xv", xv, N, H, dv)
+    _same_dtype("xq", xq, xk=xk, xv=xv, z=z, conv_state=conv_state)
+    _shape("wq", wq, H * dk, 4)
+    _shape("wk", wk, H * dk, 4)
+    _shape("wv", wv, H * dv, 4)
+    _shape("conv_state", conv_state, N, 3, H * (2 * dk + dv))
+    _shape("a_raw", a_raw, N, H)
+    _shape("b_raw", b_raw, N, H)
+    _shape("A_log", A_log, H)
+    _shape("dt_bias", dt_bias, H)
+    _shape("state", state, N, H, dk, dv)
+    _shape("z", z, N, H, dv)
+    _shape("norm_weight", norm_weight, dv)
+    _shape("o", o, N, H, dv)
     o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else x_tag)
     if o is None:
         o = torch.empty((N, H, dv), dtype=_tag_dtype(o_tag), device=xq.device)
@@ -476,8 +604,25 @@ def gdn_fused_decode_multi(xq, xk, xv, wq, wk, wv, conv_state_in, a_raw, b_raw, 
     N, T, H, dk = xq.shape
     dv = xv.shape[-1]
     x_tag = _dtype_tag(xq)
-    if z.dtype != xq.dtype:
-        raise GdnError("z must have the dtype of xq")
+    _shape("xk", xk, N, T, H, dk)
+    _shape("xv", xv, N, T, H, dv)
+    _same_dtype("xq", xq, xk=xk, xv=xv, z=z, conv_state_in=conv_state_in,
+                conv_state_out=conv_state_out)
+    _shape("wq", wq, H * dk, 4)
+    _shape("wk", wk, H * dk, 4)
+    _shape("wv", wv, H * dv, 4)
+    _shape("conv_state_in", conv_state_in, N, 3, H * (2 * dk + dv))
+    _shape("conv_state_out", conv_state_out, N, 3, H * (2 * dk + dv))
+    _shape("a_raw", a_raw, N, T, H)
+    _shape("b_raw", b_raw, N, T, H)
+    _shape("A_log", A_log, H)
+    _shape("dt_bias", dt_bias, H)
+    _shape("state", state, N, H, dk, dv)
+    _shape("z", z, N, T, H, dv)
+    _shape("norm_weight", norm_weight, dv)
+    _shape("o", o, N, T, H, dv)
+    if step_states is not True:
+        _shape("step_states", step_states, N, T, H, dk, dv)
     o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else x_tag)
     if o is None:
         o = torch.empty((N, T, H, dv), dtype=_tag_dtype(o_tag), device=xq.device)
