@@ -134,3 +134,29 @@ def test_prefill_many_sequences(gpu, nseq, bf16):
         inp = gi.make_inputs(gi.TINY_FP32, seed=12, H=2, lengths=L)
     res = C.gpu_run(inp, y_dtype="bf16" if bf16 else "f32")
     C.check_prefill_sampled(inp, res, C.sampled_seqs(L, 12), [0, 1], y_bf16=bf16)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_prefill_final_state_in_place(gpu, bf16):
+    """final_state may be the initial_state buffer (updated in place): the same y and S_T, bit
+    for bit, as with a separate output buffer."""
+    import torch
+    import gated_deltanet_recurrence_chunked_amd as gdn
+    L = [130, 0, 64, 7]
+    _announce(f"prefill with final_state = initial_state, lengths {L} H=2 bf16={bf16}")
+    inp = gi.make_inputs(gi.LONG_CONTEXT if bf16 else gi.TINY_FP32, seed=15, H=2, lengths=L)
+    sh = inp["shape"]
+    S0 = gi.make_inputs(gi.LONG_CONTEXT, seed=15, B=len(L), H=2, T=1, d=sh.dk)["S0"]
+    q, k, v = (C.dev(inp[x], bf16) for x in ("q", "k", "v"))
+    f32 = lambda a: C.dev(np.ascontiguousarray(a, dtype=np.float32))          # noqa: E731
+    _, _, _, g, beta = gdn.gdn_preprocess(None, None, None, None, None, None, f32(inp["a_raw"]),
+                                          f32(inp["b_raw"]), f32(inp["A_log"]),
+                                          f32(inp["dt_bias"]), H=sh.H)
+    cu = C.dev(inp["cu_seqlens"])
+    kw = dict(cu_seqlens=cu, cu_seqlens_host=inp["cu_seqlens"], num_seqs=len(L))
+    y1, ST1 = gdn.gdn_chunk_prefill(q, k, v, g, beta, initial_state=f32(S0), **kw)
+    S = f32(S0)
+    y2, ST2 = gdn.gdn_chunk_prefill(q, k, v, g, beta, initial_state=S, final_state=S, **kw)
+    torch.cuda.synchronize()
+    assert ST2.data_ptr() == S.data_ptr()
+    assert torch.equal(y1, y2) and torch.equal(ST1, S)
