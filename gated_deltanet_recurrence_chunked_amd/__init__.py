@@ -374,11 +374,13 @@ def gdn_chunk_backward(q, k, v, g, beta, dy, *, initial_state=None, dfinal_state
     return out
 
 
-def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, cu_seqlens=None,
-                          cu_seqlens_host=None, num_seqs=1, y=None, y_dtype=None, workspace=None,
-                          output_final_state=True, stream=None):
+def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
+                          cu_seqlens=None, cu_seqlens_host=None, num_seqs=1, y=None, y_dtype=None,
+                          workspace=None, output_final_state=True, stream=None):
     """Per-channel-decay delta rule. q,k: [ntok,H,dk], v: [ntok,H,dv] (bf16/fp32);
-    g: [ntok,H,dk] fp32 log-decays; beta: [ntok,H] fp32. Returns (y, final_state)."""
+    g: [ntok,H,dk] fp32 log-decays; beta: [ntok,H] fp32; final_state: None (allocated when
+    output_final_state) or [num_seqs,H,dk,dv] fp32, which may be initial_state (updated in
+    place). Returns (y, final_state)."""
     ntok, H, dk = q.shape
     dv = v.shape[-1]
     in_tag = _dtype_tag(q)
@@ -390,12 +392,13 @@ def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, cu_seqlens=No
     _shape("g", g, ntok, H, dk)
     _shape("beta", beta, ntok, H)
     _shape("initial_state", initial_state, num_seqs, H, dk, dv)
+    _shape("final_state", final_state, num_seqs, H, dk, dv)
     _shape("y", y, ntok, H, dv)
     _packing(cu_seqlens, cu_seqlens_host, num_seqs)
     if y is None:
         y = torch.empty((ntok, H, dv), dtype=_tag_dtype(y_tag), device=dev)
-    final_state = (torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
-                   if output_final_state else None)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
     need = int(lib().gdn_kda_chunk_prefill_workspace_size(ntok, num_seqs, H, dk))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

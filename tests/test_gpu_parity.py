@@ -139,7 +139,8 @@ def test_prefill_many_sequences(gpu, nseq, bf16):
 @pytest.mark.parametrize("bf16", [True, False])
 def test_prefill_final_state_in_place(gpu, bf16):
     """final_state may be the initial_state buffer (updated in place): the same y and S_T, bit
-    for bit, as with a separate output buffer."""
+    for bit, as with a separate output buffer (the scalar-decay and per-channel-decay
+    prefills)."""
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
     L = [130, 0, 64, 7]
@@ -157,6 +158,14 @@ def test_prefill_final_state_in_place(gpu, bf16):
     y1, ST1 = gdn.gdn_chunk_prefill(q, k, v, g, beta, initial_state=f32(S0), **kw)
     S = f32(S0)
     y2, ST2 = gdn.gdn_chunk_prefill(q, k, v, g, beta, initial_state=S, final_state=S, **kw)
+    torch.cuda.synchronize()
+    assert ST2.data_ptr() == S.data_ptr()
+    assert torch.equal(y1, y2) and torch.equal(ST1, S)
+    # the per-channel-decay prefill likewise
+    gk = f32(gi.kda_log_decay_draw(15, sh.ntok, sh.H, sh.dk))
+    y1, ST1 = gdn.gdn_kda_chunk_prefill(q, k, v, gk, beta, initial_state=f32(S0), **kw)
+    S = f32(S0)
+    y2, ST2 = gdn.gdn_kda_chunk_prefill(q, k, v, gk, beta, initial_state=S, final_state=S, **kw)
     torch.cuda.synchronize()
     assert ST2.data_ptr() == S.data_ptr()
     assert torch.equal(y1, y2) and torch.equal(ST1, S)
