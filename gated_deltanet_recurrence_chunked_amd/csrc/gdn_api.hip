@@ -69,6 +69,22 @@ int hip_status(hipError_t e, const char* what) {
 #define GDN_OPT_PTR(p) \
     GDN_REQUIRE((p) == nullptr || aligned16(p), GDN_ERR_ALIGN, "%s is not 16-byte aligned", #p)
 
+// Every array a call touches holds at most 2^31 - 1 elements (the kernels index within one
+// array in 32-bit arithmetic): token arrays rows * H * d, state arrays states * H * dk * dv.
+constexpr long long kMaxElems = 2147483647LL;
+int check_extents(long long rows, int H, int d, long long states, long long state_elems) {
+    GDN_REQUIRE(rows * H * d <= kMaxElems, GDN_ERR_SHAPE,
+                "token arrays of %lld rows x H=%d x d=%d exceed 2^31-1 elements", rows, H, d);
+    GDN_REQUIRE(states * state_elems <= kMaxElems, GDN_ERR_SHAPE,
+                "state arrays of %lld x %lld elements exceed 2^31-1 elements", states, state_elems);
+    return GDN_OK;
+}
+#define GDN_EXTENTS(...)                        \
+    do {                                        \
+        const int st_ = check_extents(__VA_ARGS__); \
+        if (st_) return st_;                    \
+    } while (0)
+
 // Checks the packing description shared by preprocess and prefill.
 int check_packing(const int32_t* cu_host, bool have_cu, int num_seqs, int ntok) {
     GDN_REQUIRE(num_seqs >= 1, GDN_ERR_SHAPE, "num_seqs must be >= 1 (got %d)", num_seqs);
@@ -143,6 +159,7 @@ int preprocess_impl(const void* xq, const void* xk, const void* xv, int x_dtype,
     int st = check_packing(nullptr, cu_seqlens != nullptr, num_seqs, ntok);
     if (st) return st;
     const int hC = H * (2 * dk + dv);
+    GDN_EXTENTS(ntok, H, dk > dv ? dk : dv, num_seqs, 3LL * hC);
     if (conv_state_in || conv_state_out) {
         GDN_REQUIRE(conv, GDN_ERR_NULL, "a conv state needs the conv inputs and outputs");
         GDN_OPT_PTR(conv_state_in);
@@ -223,6 +240,7 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
                 "cu_seqlens_host given without the device cu_seqlens");
     int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
     if (st) return st;
+    GDN_EXTENTS(ntok, H, dk > dv ? dk : dv, num_seqs, (long long)H * dk * dv);
     const size_t need = gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, in_dtype);
     GDN_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr), GDN_ERR_WORKSPACE,
                 "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -268,6 +286,7 @@ int gdn_chunk_backward(const void* q, const void* k, const void* v, int in_dtype
                 "cu_seqlens_host given without the device cu_seqlens");
     int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
     if (st) return st;
+    GDN_EXTENTS(ntok, H, dk > dv ? dk : dv, num_seqs, (long long)H * dk * dv);
     const size_t need = gdn::chunk_bwd_workspace(ntok, num_seqs, H, dk, dv);
     GDN_REQUIRE(workspace_bytes >= need && workspace != nullptr, GDN_ERR_WORKSPACE,
                 "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -306,6 +325,7 @@ int gdn_kda_chunk_prefill(const void* q, const void* k, const void* v, int in_dt
                 "cu_seqlens_host given without the device cu_seqlens");
     int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
     if (st) return st;
+    GDN_EXTENTS(ntok, H, dk > dv ? dk : dv, num_seqs, (long long)H * dk * dv);
     const size_t need = gdn::chunk_kda_workspace(ntok, num_seqs, H, dk);
     GDN_REQUIRE(workspace_bytes >= need && workspace != nullptr, GDN_ERR_WORKSPACE,
                 "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -329,6 +349,7 @@ int gdn_decode_step(const void* q, const void* k, const void* v, int in_dtype, c
                 dk, dv);
     GDN_TPTR(q, N); GDN_TPTR(k, N); GDN_TPTR(v, N); GDN_TSPTR(g, N); GDN_TSPTR(beta, N);
     GDN_TPTR(state, N); GDN_TPTR(y, N);
+    GDN_EXTENTS(N, H, dk > dv ? dk : dv, N, (long long)H * dk * dv);
     return hip_status(gdn::launch_decode(q, k, v, in_dtype == GDN_BF16, g, beta, state, N, H, dk,
                                          dv, y, y_dtype == GDN_BF16,
                                          static_cast<hipStream_t>(stream)),
@@ -348,6 +369,8 @@ int gdn_decode_multi(const void* q, const void* k, const void* v, int in_dtype, 
     GDN_TPTR(q, N); GDN_TPTR(k, N); GDN_TPTR(v, N); GDN_TSPTR(g, N); GDN_TSPTR(beta, N);
     GDN_TPTR(state, N); GDN_TPTR(y, N);
     GDN_OPT_PTR(step_states);
+    GDN_EXTENTS((long long)N * T, H, dk > dv ? dk : dv, (long long)N * (step_states ? T : 1),
+                (long long)H * dk * dv);
     if (step_states) {
         const char* a0 = reinterpret_cast<const char*>(state);
         const char* b0 = reinterpret_cast<const char*>(step_states);
@@ -398,6 +421,7 @@ int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtyp
                 "cu_seqlens_host given without the device cu_seqlens");
     int st = check_packing(cu_seqlens_host, cu_seqlens != nullptr, num_seqs, ntok);
     if (st) return st;
+    GDN_EXTENTS(ntok, H, dk > dv ? dk : dv, num_seqs, (long long)H * dk * dv);
     const size_t need = gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv);
     GDN_REQUIRE(workspace != nullptr && workspace_bytes >= need, GDN_ERR_WORKSPACE,
                 "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -463,6 +487,8 @@ int gdn_fused_decode(const void* xq, const void* xk, const void* xv, int x_dtype
     GDN_TPTR(conv_state, N);
     GDN_TSPTR(a_raw, N); GDN_TSPTR(b_raw, N); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
     GDN_TPTR(state, N); GDN_TPTR(z, N); GDN_SPTR(norm_weight); GDN_TPTR(o, N); GDN_OPT_PTR(y);
+    GDN_EXTENTS(N, H, dk > dv ? dk : dv, N, (long long)H * dk * dv);
+    GDN_EXTENTS(N, 1, 3 * H * (2 * dk + dv), 0, 0);
     gdn::DecodeFusedArgs f;
     f.x[0] = xq; f.x[1] = xk; f.x[2] = xv;
     f.w[0] = wq; f.w[1] = wk; f.w[2] = wv;
@@ -500,6 +526,9 @@ int gdn_fused_decode_multi(const void* xq, const void* xk, const void* xv, int x
     GDN_TSPTR(a_raw, N); GDN_TSPTR(b_raw, N); GDN_SPTR(A_log); GDN_SPTR(dt_bias);
     GDN_TPTR(state, N); GDN_TPTR(z, N); GDN_SPTR(norm_weight); GDN_TPTR(o, N); GDN_OPT_PTR(y);
     GDN_OPT_PTR(step_states);
+    GDN_EXTENTS((long long)N * T, H, dk > dv ? dk : dv, (long long)N * (step_states ? T : 1),
+                (long long)H * dk * dv);
+    GDN_EXTENTS(N, 1, 3 * H * (2 * dk + dv), 0, 0);
     const int hC = H * (2 * dk + dv);
     {
         const size_t hb = (size_t)N * 3 * hC * (x_dtype == GDN_BF16 ? 2 : 4);
@@ -540,6 +569,7 @@ int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype, cons
                 "need ntok >= 0, H >= 1 and dv in {64, 128} (got ntok=%d H=%d dv=%d)", ntok, H, dv);
     GDN_REQUIRE(eps >= 0.f, GDN_ERR_SHAPE, "eps must be >= 0");
     GDN_TPTR(y, ntok); GDN_TPTR(z, ntok); GDN_SPTR(norm_weight); GDN_TPTR(o, ntok);
+    GDN_EXTENTS(ntok, H, dv, 0, 0);
     return hip_status(gdn::launch_output_gate(y, y_dtype == GDN_BF16, z, z_dtype == GDN_BF16,
                                               norm_weight, ntok, H, dv, eps, o,
                                               o_dtype == GDN_BF16, static_cast<hipStream_t>(stream)),

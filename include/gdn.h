@@ -24,6 +24,9 @@
  *   - Pointers to vector data (x*, q, k, v, y, z, o, conv taps, states, workspace) must be
  *     16-byte aligned; scalar arrays (g, beta, a_raw, b_raw, A_log, dt_bias, norm weight,
  *     cu_seqlens) 4-byte aligned. dk, dv in {64, 128}. H >= 1.
+ *   - Every array a call touches has at most 2^31 - 1 elements: ntok * H * max(dk, dv) for
+ *     token arrays (N * T * H * max(dk, dv) in decode), num_seqs * H * dk * dv for states,
+ *     num_seqs * 3 * H * (2 dk + dv) for conv histories. Larger calls return GDN_ERR_SHAPE.
  *   - Arrays indexed by token (or, in decode, by sequence: the decode states and conv
  *     histories included) may be NULL when that count (ntok, or N) is 0: nothing reads or
  *     writes them then. Per-head and per-channel arrays (conv taps, A_log, dt_bias, norm

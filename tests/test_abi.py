@@ -71,6 +71,11 @@ def test_prefill_validation(L):
     assert _prefill(L, ntok=0, q=None, k=None, v=None, g=None, beta=None, y=MIS) == 5
     assert _prefill(L, ntok=0, q=None, k=None, v=None, g=None, beta=None, y=None) == 6
     assert _prefill(L, ntok=1, num_seqs=1, q=None) == 1
+    # arrays beyond 2^31 - 1 elements are refused (2^24 tokens x 1024 heads x 128)
+    assert _prefill(L, ntok=1 << 24, H=1024) == 2
+    assert L.gdn_last_error().startswith(b"token arrays of 16777216 rows")
+    assert _prefill(L, ntok=1 << 17, num_seqs=1 << 17, H=2) == 2      # 2^17 states of 2^15
+    assert L.gdn_last_error().startswith(b"state arrays of 131072 x 32768")
 
 
 def test_decode_and_gate_validation(L):
