@@ -18,7 +18,7 @@ constexpr int kPreThreads = 256;
 constexpr int kPreTile = kPreThreads * 8;   // channels per workgroup
 constexpr int kPreTokens = 64;              // tokens per workgroup (3-token conv halo)
 constexpr int kConvK = 4;
-constexpr int kPreGroup = 2;                // tokens per step (loaded one step ahead)
+constexpr int kPreGroup = 1;                // tokens per step (loaded one step ahead)
 
 struct PreKernelArgs {
     PreprocessArgs a;
