@@ -184,17 +184,21 @@ __device__ __forceinline__ void load_tile64(const float* src, float (*dst)[kC + 
 }
 
 // ------------------------------------------------------------------ ap: G, Ak, P, T per chunk-head
+// K and Q stay in their input type in LDS (bf16 is widened exactly as the products read it):
+// with bf16 inputs that is 50 KB, so two workgroups share a CU (4 waves per SIMD, which caps
+// the registers at 128).
 template <int DK, typename Tin>
-__global__ void __launch_bounds__(kFinT) bwd_ap_kernel(BwdArgs a) {
-    __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1];
+__global__ void __launch_bounds__(kFinT, 4) bwd_ap_kernel(BwdArgs a) {
+    constexpr int KR = DK + (sizeof(Tin) == 2 ? 2 : 1);
+    __shared__ Tin Ks[kC][KR], Qs[kC][KR];
     __shared__ float A[kC][kC + 1];
     __shared__ float G[kC], Bt[kC];
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int t0, n;
     if (!chunk_info(a, c, t0, n)) return;
     const int H = a.H;
-    load_rows<DK, Tin, kFinT>(a.k, t0, n, H, h, Ks);
-    load_rows<DK, Tin, kFinT>(a.q, t0, n, H, h, Qs);
+    load_rows_raw<DK, KR, Tin, kFinT>(a.k, t0, n, H, h, Ks);
+    load_rows_raw<DK, KR, Tin, kFinT>(a.q, t0, n, H, h, Qs);
     if (tid < kC) {
         G[tid] = tid < n ? a.g[(size_t)(t0 + tid) * H + h] : 0.f;
         Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
@@ -229,8 +233,8 @@ __global__ void __launch_bounds__(kFinT) bwd_ap_kernel(BwdArgs a) {
             }
             continue;
         }
-        const float* X = kind ? &Qs[rt * 16][0] : &Ks[rt * 16][0];
-        const floatx4 acc = mma_f32_tile(X, DK + 1, 1, &Ks[it * 16][0], 1, DK + 1, DK,
+        const Tin* X = kind ? &Qs[rt * 16][0] : &Ks[rt * 16][0];
+        const floatx4 acc = mma_f32_tile(X, KR, 1, &Ks[it * 16][0], 1, KR, DK,
                                          floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -627,11 +631,15 @@ __global__ void __launch_bounds__(kScanT) bwd_scan_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ finish per chunk-head
 template <int DK, typename Tin>
-__global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
-    __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1];
+__global__ void __launch_bounds__(kFinT, 4) bwd_finish_kernel(BwdArgs a) {
+    // K and Q stay in their input type; dD = dA o A + dP o P and dA o Ak are needed only as row
+    // and column sums, which are formed per 16x16 tile by shuffles. With bf16 inputs that is
+    // 70 KB, so two workgroups share a CU (4 waves per SIMD, which caps the registers at 128).
+    constexpr int KR = DK + (sizeof(Tin) == 2 ? 2 : 1);
+    __shared__ Tin Ks[kC][KR], Qs[kC][KR];
     __shared__ float dKK[kC][kC + 1], dQK[kC][kC + 1];   // coefficients of k_r.k_i, q_r.k_i
-    __shared__ float dDr[kC][kC + 1];                    // dD = dA o A + dP o P
-    __shared__ float dAk[kC][kC + 1];                    // dA o Ak (its row sums feed dbeta)
+    __shared__ float rsD[kC][4], rsA[kC][4];             // row sums of dD, dA o Ak per column tile
+    __shared__ float csD[4][kC];                         // column sums of dD per row tile
     __shared__ float G[kC], Bt[kC], dG[kC], dgam[kC], dw[kC], dbs[kC];
     __shared__ float dgC;
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -639,8 +647,8 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
     if (!chunk_info(a, c, t0, n)) return;
     const int H = a.H, slices = a.slices;
     const size_t ch = (size_t)c * H + h;
-    load_rows<DK, Tin, kFinT>(a.k, t0, n, H, h, Ks);
-    load_rows<DK, Tin, kFinT>(a.q, t0, n, H, h, Qs);
+    load_rows_raw<DK, KR, Tin, kFinT>(a.k, t0, n, H, h, Ks);
+    load_rows_raw<DK, KR, Tin, kFinT>(a.q, t0, n, H, h, Qs);
     if (tid < kC) {
         G[tid] = a.G[ch * kC + tid];
         Bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
@@ -665,6 +673,9 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
     // dA, dP summed over slices. With A = beta o Ak (Ak = e^{D} o KK^T) and P = e^{D} o QK^T:
     // dKK = beta o dA o e^{D}, dQK = dP o e^{D}, dbeta += rowsum(dA o Ak),
     // dD = beta o dA o Ak + dP o P. The shares are in tile layout: one 16-byte piece per lane.
+    // Every lane of a wave runs the same iterations (kFinT is a multiple of the wave), so the
+    // tile's row and column sums are shuffle reductions over its lanes.
+    static_assert(kFinT % kWave == 0 && (16 * kWave) % kFinT == 0, "uniform tile loop");
     for (int idx = tid; idx < 16 * kWave; idx += kFinT) {
         const int t2 = idx / kWave, l = idx % kWave, rt = t2 >> 2, it = t2 & 3;
         floatx4 da = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
@@ -674,6 +685,7 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
             da += pp[idx];
             dp += pp[kC * kC / 4 + idx];
         }
+        float dd[4], dak[4], col = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = rt * 16 + 4 * (l >> 4) + u, i = it * 16 + (l & 15);
@@ -682,19 +694,35 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
             const float dec = (i <= r && r < n) ? expf(G[r] - G[i]) : 0.f;
             dKK[r][i] = i < r ? Bt[r] * da[u] * dec : 0.f;
             dQK[r][i] = dp[u] * dec;
-            dDr[r][i] = Bt[r] * da[u] * ak + dp[u] * pv;
-            dAk[r][i] = da[u] * ak;
+            dd[u] = Bt[r] * da[u] * ak + dp[u] * pv;
+            dak[u] = da[u] * ak;
+            col += dd[u];
         }
+        // row sums: over the 16 lanes of a row group (lane bits 0-3); column sums: over the
+        // 4 row groups (lane bits 4-5)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                dd[u] += __shfl_xor(dd[u], o, kWave);
+                dak[u] += __shfl_xor(dak[u], o, kWave);
+            }
+        col += __shfl_xor(col, 16, kWave);
+        col += __shfl_xor(col, 32, kWave);
+        if ((l & 15) == 0)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                rsD[rt * 16 + 4 * (l >> 4) + u][it] = dd[u];
+                rsA[rt * 16 + 4 * (l >> 4) + u][it] = dak[u];
+            }
+        if (l < 16) csD[rt][it * 16 + l] = col;
     }
     __syncthreads();
     if (tid < kC) {
         const int r = tid;
-        float rs = 0.f, cs = 0.f, db = 0.f;
-        for (int i = 0; i < kC; ++i) {
-            rs += dDr[r][i];
-            cs += dDr[i][r];
-            db += dAk[r][i];
-        }
+        const float rs = (rsD[r][0] + rsD[r][1]) + (rsD[r][2] + rsD[r][3]);
+        const float cs = (csD[0][r] + csD[1][r]) + (csD[2][r] + csD[3][r]);
+        const float db = (rsA[r][0] + rsA[r][1]) + (rsA[r][2] + rsA[r][3]);
         dbs[r] += db;
         dG[r] = rs - cs + dgam[r] * expf(G[r]) - dw[r] * (r < n ? expf(G[n - 1] - G[r]) : 0.f);
     }
@@ -727,10 +755,10 @@ __global__ void __launch_bounds__(kFinT) bwd_finish_kernel(BwdArgs a) {
             q0 += pp[tile * kWave + lane];
             k0 += pp[kC * DK / 4 + tile * kWave + lane];
         }
-        const floatx4 q1 = mma_f32_tile(&dQK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, q0);
-        floatx4 k1 = mma_f32_tile(&dKK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], DK + 1, 1, kC, k0);
-        k1 = mma_f32_tile(&dKK[0][rt * 16], 1, kC + 1, &Ks[0][dt * 16], DK + 1, 1, kC, k1);
-        k1 = mma_f32_tile(&dQK[0][rt * 16], 1, kC + 1, &Qs[0][dt * 16], DK + 1, 1, kC, k1);
+        const floatx4 q1 = mma_f32_tile(&dQK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], KR, 1, kC, q0);
+        floatx4 k1 = mma_f32_tile(&dKK[rt * 16][0], kC + 1, 1, &Ks[0][dt * 16], KR, 1, kC, k0);
+        k1 = mma_f32_tile(&dKK[0][rt * 16], 1, kC + 1, &Ks[0][dt * 16], KR, 1, kC, k1);
+        k1 = mma_f32_tile(&dQK[0][rt * 16], 1, kC + 1, &Qs[0][dt * 16], KR, 1, kC, k1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rt * 16 + 4 * lg + i, d = dt * 16 + lc;
