@@ -100,11 +100,28 @@ __device__ __forceinline__ float ldx(const void* p, size_t i) {
 }
 
 // ------------------------------------------------------------------ prep per chunk-head
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// exact for a value widened from bf16 (its low 16 bits are zero)
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
+    return (uint16_t)(__float_as_uint(x) >> 16);
+}
+
+// K and Q stay in their input type in LDS and share one region with A, which is written only
+// after every product has read them (the products' results wait in registers across a
+// barrier). With bf16 inputs that is 66 KB, so two workgroups share a CU (4 waves per SIMD,
+// which caps the registers at 128).
 template <int DK, typename Tin>
-__global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
-    __shared__ float Ks[kC][DK + 1], Qs[kC][DK + 1], Gc[kC][DK + 1];
-    __shared__ float A[kC][kC + 1];
+__global__ void __launch_bounds__(kPT, 4) kda_prep_kernel(KdaArgs a) {
+    constexpr int KR = DK + (sizeof(Tin) == 2 ? 2 : 1);
+    constexpr int kKQBytes = 2 * kC * KR * (int)sizeof(Tin);
+    constexpr int kABytes = kC * (kC + 1) * (int)sizeof(float);
+    __shared__ __attribute__((aligned(16))) unsigned char kqa[kKQBytes > kABytes ? kKQBytes : kABytes];
+    __shared__ float Gc[kC][DK + 1];
     __shared__ float Bt[kC];
+    Tin (*Ks)[KR] = reinterpret_cast<Tin (*)[KR]>(kqa);
+    Tin (*Qs)[KR] = reinterpret_cast<Tin (*)[KR]>(kqa + kC * KR * sizeof(Tin));
+    float (*A)[kC + 1] = reinterpret_cast<float (*)[kC + 1]>(kqa);
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, H = a.H;
     int t0, n;
     if (!kda_chunk(a, c, t0, n)) return;
@@ -119,8 +136,8 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
         const float gs[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            Ks[r][d + i] = ok ? kv[i] : 0.f;
-            Qs[r][d + i] = ok ? qv[i] : 0.f;
+            Ks[r][d + i] = from_f32<Tin>(ok ? kv[i] : 0.f);
+            Qs[r][d + i] = from_f32<Tin>(ok ? qv[i] : 0.f);
             Gc[r][d + i] = ok ? gs[i] : 0.f;
         }
     }
@@ -141,37 +158,40 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
     // the rows), so the tile is a plain product of decayed operands: one wave per tile on the
     // fp32 matrix core, the two exponentials formed as the operands are read (no overflow, and
     // no bound on g needed). The four diagonal tiles' 136 pairs each are formed element by
-    // element; the tiles above are zero.
+    // element; the tiles above are zero. P goes out at once; A waits in registers.
     const int wave = tid / kWave, lane = tid % kWave, lc = lane & 15, lg = lane >> 4;
     for (int e = tid; e < kC * kC; e += kPT) {
         const int r = e / kC, i = e % kC;
-        if ((i >> 4) > (r >> 4)) {
-            A[r][i] = 0.f;
-            a.P[ch * kC * kC + e] = 0.f;
-        }
+        if ((i >> 4) > (r >> 4)) a.P[ch * kC * kC + e] = 0.f;
     }
+    floatx4 ak = {0.f, 0.f, 0.f, 0.f};
     if (wave < 6) {
         const int rt = wave < 1 ? 1 : (wave < 3 ? 2 : 3);
         const int it = wave - (rt * (rt - 1)) / 2;          // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
         const int m = 16 * rt, r = 16 * rt + lc, i = 16 * it + lc;
-        floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+        floatx4 aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
         for (int k0 = 0; k0 < DK; k0 += 4) {
             const int d = k0 + lg;
             const float gm = Gc[m][d];
             const float ea = fexp(Gc[r][d] - gm), eb = fexp(gm - Gc[i][d]);
-            const float b = Ks[i][d] * eb;
-            ak = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[r][d] * ea, b, ak, 0, 0, 0);
-            aq = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[r][d] * ea, b, aq, 0, 0, 0);
+            const float b = load1(&Ks[i][d]) * eb;
+            ak = __builtin_amdgcn_mfma_f32_16x16x4f32(load1(&Ks[r][d]) * ea, b, ak, 0, 0, 0);
+            aq = __builtin_amdgcn_mfma_f32_16x16x4f32(load1(&Qs[r][d]) * ea, b, aq, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {   // accumulator element u: row 4 lg + u, column lc
             const int rr = 16 * rt + 4 * lg + u, ii = 16 * it + lc;
-            A[rr][ii] = Bt[rr] * ak[u];        // rows past n: K, Q rows are zero there
             a.P[ch * kC * kC + rr * kC + ii] = aq[u];
         }
     }
-    for (int p = tid; p < 4 * 136; p += kPT) {   // the diagonal tiles, pair by pair
+    constexpr int kPairIt = (4 * 136 + kPT - 1) / kPT;   // diagonal pairs per thread, at most
+    float kkv[kPairIt];
+#pragma unroll
+    for (int j = 0; j < kPairIt; ++j) {   // the diagonal tiles, pair by pair
+        const int p = tid + j * kPT;
+        kkv[j] = 0.f;
+        if (p >= 4 * 136) continue;
         const int b = p / 136, q = p % 136;
         int rr = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
         while (rr * (rr + 1) / 2 > q) --rr;                 // guard the float root
@@ -182,21 +202,43 @@ __global__ void __launch_bounds__(kPT) kda_prep_kernel(KdaArgs a) {
 #pragma unroll 4
             for (int d = 0; d < DK; ++d) {
                 const float dec = fexp(Gc[r][d] - Gc[i][d]);
-                const float kd = Ks[i][d] * dec;
-                kk += Ks[r][d] * kd;
-                qk += Qs[r][d] * kd;
+                const float kd = load1(&Ks[i][d]) * dec;
+                kk += load1(&Ks[r][d]) * kd;
+                qk += load1(&Qs[r][d]) * kd;
             }
         }
-        A[r][i] = i < r ? Bt[r] * kk : 0.f;
+        kkv[j] = kk;
         a.P[ch * kC * kC + r * kC + i] = qk;
     }
-    // the diagonal tiles' upper halves
+    // the diagonal tiles' upper halves of P
     for (int e = tid; e < 4 * 256; e += kPT) {
         const int b = e / 256, r = 16 * b + (e % 256) / 16, i = 16 * b + e % 16;
-        if (i > r) {
-            A[r][i] = 0.f;
-            a.P[ch * kC * kC + r * kC + i] = 0.f;
+        if (i > r) a.P[ch * kC * kC + r * kC + i] = 0.f;
+    }
+    __syncthreads();   // every read of K and Q is done: A takes their place
+    for (int e = tid; e < kC * kC; e += kPT) {
+        const int r = e / kC, i = e % kC;
+        if ((i >> 4) > (r >> 4) || ((i >> 4) == (r >> 4) && i > r)) A[r][i] = 0.f;
+    }
+    if (wave < 6) {
+        const int rt = wave < 1 ? 1 : (wave < 3 ? 2 : 3);
+        const int it = wave - (rt * (rt - 1)) / 2;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int rr = 16 * rt + 4 * lg + u, ii = 16 * it + lc;
+            A[rr][ii] = Bt[rr] * ak[u];        // rows past n: K, Q rows are zero there
         }
+    }
+#pragma unroll
+    for (int j = 0; j < kPairIt; ++j) {
+        const int p = tid + j * kPT;
+        if (p >= 4 * 136) continue;
+        const int b = p / 136, q = p % 136;
+        int rr = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+        while (rr * (rr + 1) / 2 > q) --rr;
+        while ((rr + 1) * (rr + 2) / 2 <= q) ++rr;
+        const int r = 16 * b + rr, i = 16 * b + q - rr * (rr + 1) / 2;
+        A[r][i] = i < r ? Bt[r] * kkv[j] : 0.f;
     }
     // the running log-decays for the scan (rows past n repeat row n-1: their g is zero)
     for (int u = tid; u < kC * DK / 4; u += kPT) {
