@@ -137,6 +137,14 @@ def _shape(name, t, *shape):
         raise GdnError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _dtype(name, t, dtype):
+    """An output tensor given by the caller must have the dtype the call writes: the kernels
+    see bare pointers, and a mismatch would write past a smaller-element buffer."""
+    if t is not None and t.dtype != dtype:
+        raise GdnError(f"{name} must be {dtype} to match the requested output dtype "
+                       f"(got {t.dtype})")
+
+
 def _same_dtype(ref_name, ref, **others):
     for name, t in others.items():
         if t is not None and t.dtype != ref.dtype:
@@ -153,6 +161,37 @@ def _stream(stream=None) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class _Alloc:
+    """Tensors a call allocates on the caller's behalf (see _keep)."""
+
+    def __init__(self, device):
+        self.device = device
+        self.made = []
+
+    def __call__(self, shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=self.device)
+        self.made.append(t)
+        return t
+
+    def get(self, outs, name, shape, dtype):
+        return outs[name] if outs.get(name) is not None else self(shape, dtype)
+
+
+def _keep(stream, *tensors):
+    """Tensors a call allocates (workspaces, default outputs) come from torch's caching
+    allocator on torch's current stream, while the kernels run on `stream`. When the two
+    differ, record the tensors on `stream`, so their memory is not handed to other work
+    before the kernels that use it have finished."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s == torch.cuda.current_stream(s.device):
+        return
+    for t in tensors:
+        if t is not None and t.numel() > 0:
+            t.record_stream(s)
 
 
 def _check(status: int, fn: str):
@@ -207,22 +246,26 @@ def gdn_preprocess(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, *, H, c
                       ("g", (ntok, H)), ("beta", (ntok, H))):
         _shape(name, outs.get(name), *shp)
     q = k = v = g = beta = None
+    od, f32 = _tag_dtype(o_tag), torch.float32
+    for name, dt in (("q", od), ("k", od), ("v", od), ("g", f32), ("beta", f32)):
+        _dtype(name, outs.get(name), dt)
+    new = _Alloc(dev)
     if conv:
-        q = outs.get("q", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
-        k = outs.get("k", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
-        v = outs.get("v", torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=dev))
+        q = new.get(outs, "q", (ntok, H, dk), od)
+        k = new.get(outs, "k", (ntok, H, dk), od)
+        v = new.get(outs, "v", (ntok, H, dv), od)
     if gates:
-        g = outs.get("g", torch.empty((ntok, H), dtype=torch.float32, device=dev))
-        beta = outs.get("beta", torch.empty((ntok, H), dtype=torch.float32, device=dev))
-    f32 = torch.float32
+        g = new.get(outs, "g", (ntok, H), f32)
+        beta = new.get(outs, "beta", (ntok, H), f32)
     st = lib().gdn_preprocess(
         _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), x_tag,
         _ptr(wq, "wq", f32), _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4,
         _ptr(a_raw, "a_raw", f32), _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32),
         _ptr(dt_bias, "dt_bias", f32), _ptr(cu_seqlens, "cu_seqlens", torch.int32), num_seqs, ntok,
-        H, dk, dv, l2_eps, _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), o_tag, _ptr(g, "g", f32),
-        _ptr(beta, "beta", f32), _stream(stream))
+        H, dk, dv, l2_eps, _ptr(q, "q", od), _ptr(k, "k", od), _ptr(v, "v", od), o_tag,
+        _ptr(g, "g", f32), _ptr(beta, "beta", f32), _stream(stream))
     _check(st, "gdn_preprocess")
+    _keep(stream, *new.made)
     return q, k, v, g, beta
 
 
@@ -238,8 +281,9 @@ def gdn_preprocess_stateful(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias
     dv = xv.shape[-1]
     dev = xq.device
     o_tag = _tag(out_dtype)
+    new = _Alloc(dev)
     if conv_state_out is True:
-        conv_state_out = torch.empty((num_seqs, 3, H * (2 * dk + dv)), dtype=xq.dtype, device=dev)
+        conv_state_out = new((num_seqs, 3, H * (2 * dk + dv)), xq.dtype)
     outs = {} if outs is None else outs
     _shape("xq", xq, ntok, H, dk)
     _shape("xk", xk, ntok, H, dk)
@@ -259,23 +303,27 @@ def gdn_preprocess_stateful(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias
     for name, shp in (("q", (ntok, H, dk)), ("k", (ntok, H, dk)), ("v", (ntok, H, dv)),
                       ("g", (ntok, H)), ("beta", (ntok, H))):
         _shape(name, outs.get(name), *shp)
-    q = outs.get("q", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
-    k = outs.get("k", torch.empty((ntok, H, dk), dtype=_tag_dtype(o_tag), device=dev))
-    v = outs.get("v", torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=dev))
+    od, f32 = _tag_dtype(o_tag), torch.float32
+    for name, dt in (("q", od), ("k", od), ("v", od), ("g", f32), ("beta", f32)):
+        _dtype(name, outs.get(name), dt)
+    q = new.get(outs, "q", (ntok, H, dk), od)
+    k = new.get(outs, "k", (ntok, H, dk), od)
+    v = new.get(outs, "v", (ntok, H, dv), od)
     g = beta = None
     if a_raw is not None:
-        g = outs.get("g", torch.empty((ntok, H), dtype=torch.float32, device=dev))
-        beta = outs.get("beta", torch.empty((ntok, H), dtype=torch.float32, device=dev))
-    f32 = torch.float32
+        g = new.get(outs, "g", (ntok, H), f32)
+        beta = new.get(outs, "beta", (ntok, H), f32)
     st = lib().gdn_preprocess_stateful(
         _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), _dtype_tag(xq),
         _ptr(wq, "wq", f32), _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4,
         _ptr(a_raw, "a_raw", f32), _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32),
         _ptr(dt_bias, "dt_bias", f32), _ptr(cu_seqlens, "cu_seqlens", torch.int32), num_seqs, ntok,
-        H, dk, dv, l2_eps, _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), o_tag, _ptr(g, "g", f32),
-        _ptr(beta, "beta", f32), _ptr(conv_state_in, "conv_state_in", xq.dtype),
+        H, dk, dv, l2_eps, _ptr(q, "q", od), _ptr(k, "k", od), _ptr(v, "v", od), o_tag,
+        _ptr(g, "g", f32), _ptr(beta, "beta", f32),
+        _ptr(conv_state_in, "conv_state_in", xq.dtype),
         _ptr(conv_state_out, "conv_state_out", xq.dtype), _stream(stream))
     _check(st, "gdn_preprocess_stateful")
+    _keep(stream, *new.made)
     return q, k, v, g, beta, conv_state_out
 
 
@@ -302,13 +350,17 @@ def gdn_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
     _shape("final_state", final_state, num_seqs, H, dk, dv)
     _shape("y", y, ntok, H, dv)
     _packing(cu_seqlens, cu_seqlens_host, num_seqs)
+    yd = _tag_dtype(y_tag)
+    _dtype("y", y, yd)
+    _dtype("final_state", final_state, torch.float32)
+    new = _Alloc(dev)
     if y is None:
-        y = torch.empty((ntok, H, dv), dtype=_tag_dtype(y_tag), device=dev)
+        y = new((ntok, H, dv), yd)
     if final_state is None and output_final_state:
-        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+        final_state = new((num_seqs, H, dk, dv), torch.float32)
     need = gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, in_tag)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = new(need, torch.uint8)
     host_cu = None
     if cu_seqlens_host is not None:
         host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
@@ -318,9 +370,10 @@ def gdn_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
         _ptr(initial_state, "initial_state", f32), _ptr(final_state, "final_state", f32),
         _ptr(cu_seqlens, "cu_seqlens", torch.int32),
         ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
-        _ptr(y, "y"), y_tag, _ptr(workspace, "workspace"),
+        _ptr(y, "y", yd), y_tag, _ptr(workspace, "workspace"),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_chunk_prefill")
+    _keep(stream, *new.made)
     return y, final_state
 
 
@@ -347,16 +400,13 @@ def gdn_chunk_backward(q, k, v, g, beta, dy, *, initial_state=None, dfinal_state
     _shape("dfinal_state", dfinal_state, num_seqs, H, dk, dv)
     _packing(cu_seqlens, cu_seqlens_host, num_seqs)
     f32 = torch.float32
-    out = dict(dq=torch.empty((ntok, H, dk), dtype=f32, device=dev),
-               dk=torch.empty((ntok, H, dk), dtype=f32, device=dev),
-               dv=torch.empty((ntok, H, dv), dtype=f32, device=dev),
-               dg=torch.empty((ntok, H), dtype=f32, device=dev),
-               dbeta=torch.empty((ntok, H), dtype=f32, device=dev),
-               dinitial_state=(torch.empty((num_seqs, H, dk, dv), dtype=f32, device=dev)
-                               if want_dinitial_state else None))
+    new = _Alloc(dev)
+    out = dict(dq=new((ntok, H, dk), f32), dk=new((ntok, H, dk), f32), dv=new((ntok, H, dv), f32),
+               dg=new((ntok, H), f32), dbeta=new((ntok, H), f32),
+               dinitial_state=new((num_seqs, H, dk, dv), f32) if want_dinitial_state else None)
     need = gdn_chunk_backward_workspace_size(ntok, num_seqs, H, dk, dv)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = new(max(need, 1), torch.uint8)
     host_cu = None
     if cu_seqlens_host is not None:
         host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
@@ -371,6 +421,7 @@ def gdn_chunk_backward(q, k, v, g, beta, dy, *, initial_state=None, dfinal_state
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "gdn_chunk_backward")
+    _keep(stream, *new.made)
     return out
 
 
@@ -395,13 +446,17 @@ def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=N
     _shape("final_state", final_state, num_seqs, H, dk, dv)
     _shape("y", y, ntok, H, dv)
     _packing(cu_seqlens, cu_seqlens_host, num_seqs)
+    yd = _tag_dtype(y_tag)
+    _dtype("y", y, yd)
+    _dtype("final_state", final_state, torch.float32)
+    new = _Alloc(dev)
     if y is None:
-        y = torch.empty((ntok, H, dv), dtype=_tag_dtype(y_tag), device=dev)
+        y = new((ntok, H, dv), yd)
     if final_state is None and output_final_state:
-        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+        final_state = new((num_seqs, H, dk, dv), torch.float32)
     need = int(lib().gdn_kda_chunk_prefill_workspace_size(ntok, num_seqs, H, dk))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = new(max(need, 1), torch.uint8)
     host_cu = None
     if cu_seqlens_host is not None:
         host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
@@ -411,9 +466,10 @@ def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=N
         _ptr(initial_state, "initial_state", f32), _ptr(final_state, "final_state", f32),
         _ptr(cu_seqlens, "cu_seqlens", torch.int32),
         ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
-        _ptr(y, "y"), y_tag, _ptr(workspace, "workspace"),
+        _ptr(y, "y", yd), y_tag, _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_kda_chunk_prefill")
+    _keep(stream, *new.made)
     return y, final_state
 
 
@@ -431,13 +487,17 @@ def gdn_decode_step(q, k, v, g, beta, state, *, y=None, y_dtype=None, stream=Non
     _shape("y", y, N, H, dv)
     in_tag = _dtype_tag(q)
     y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
+    yd = _tag_dtype(y_tag)
+    _dtype("y", y, yd)
+    new = _Alloc(q.device)
     if y is None:
-        y = torch.empty((N, H, dv), dtype=_tag_dtype(y_tag), device=q.device)
+        y = new((N, H, dv), yd)
     f32 = torch.float32
     st = lib().gdn_decode_step(_ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), in_tag, _ptr(g, "g", f32),
                                _ptr(beta, "beta", f32), _ptr(state, "state", f32), N, H, dk, dv,
-                               _ptr(y, "y"), y_tag, _stream(stream))
+                               _ptr(y, "y", yd), y_tag, _stream(stream))
     _check(st, "gdn_decode_step")
+    _keep(stream, *new.made)
     return y
 
 
@@ -460,16 +520,20 @@ def gdn_decode_multi(q, k, v, g, beta, state, *, y=None, y_dtype=None, step_stat
         _shape("step_states", step_states, N, T, H, dk, dv)
     in_tag = _dtype_tag(q)
     y_tag = _tag(y_dtype) if y_dtype is not None else (_dtype_tag(y) if y is not None else in_tag)
+    yd = _tag_dtype(y_tag)
+    _dtype("y", y, yd)
+    new = _Alloc(q.device)
     if y is None:
-        y = torch.empty((N, T, H, dv), dtype=_tag_dtype(y_tag), device=q.device)
+        y = new((N, T, H, dv), yd)
     if step_states is True:
-        step_states = torch.empty((N, T, H, dk, dv), dtype=torch.float32, device=q.device)
+        step_states = new((N, T, H, dk, dv), torch.float32)
     f32 = torch.float32
     st = lib().gdn_decode_multi(_ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), in_tag,
                                 _ptr(g, "g", f32), _ptr(beta, "beta", f32),
-                                _ptr(state, "state", f32), N, T, H, dk, dv, _ptr(y, "y"), y_tag,
+                                _ptr(state, "state", f32), N, T, H, dk, dv, _ptr(y, "y", yd), y_tag,
                                 _ptr(step_states, "step_states", f32), _stream(stream))
     _check(st, "gdn_decode_multi")
+    _keep(stream, *new.made)
     return y, step_states
 
 
@@ -480,12 +544,16 @@ def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream
     _shape("norm_weight", norm_weight, dv)
     _shape("o", o, ntok, H, dv)
     o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else _dtype_tag(y))
+    od = _tag_dtype(o_tag)
+    _dtype("o", o, od)
+    new = _Alloc(y.device)
     if o is None:
-        o = torch.empty((ntok, H, dv), dtype=_tag_dtype(o_tag), device=y.device)
+        o = new((ntok, H, dv), od)
     st = lib().gdn_output_gate(_ptr(y, "y"), _dtype_tag(y), _ptr(z, "z"), _dtype_tag(z),
                                _ptr(norm_weight, "norm_weight", torch.float32), ntok, H, dv, eps,
-                               _ptr(o, "o"), o_tag, _stream(stream))
+                               _ptr(o, "o", od), o_tag, _stream(stream))
     _check(st, "gdn_output_gate")
+    _keep(stream, *new.made)
     return o
 
 
@@ -496,9 +564,10 @@ def gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv) -> int:
 def gdn_fused_prefill(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, z, norm_weight, *,
                       H, initial_state=None, output_final_state=True, cu_seqlens=None,
                       cu_seqlens_host=None, num_seqs=1, l2_eps=1e-6, rms_eps=1e-6, o=None,
-                      o_dtype=torch.bfloat16, export=False, workspace=None, stream=None):
+                      o_dtype=None, export=False, workspace=None, stream=None):
     """eqs. 6-11 in one call. xq, xk: [ntok,H,128], xv, z: [ntok,H,dv] (bf16/fp32); conv taps
     [H*d,4] fp32; a_raw, b_raw: [ntok,H] fp32; A_log, dt_bias: [H]; norm_weight: [dv].
+    o_dtype: the dtype of o (default: that of a given o, else bf16).
     Returns (o, final_state) or, with export=True, (o, final_state, dict(q, k, v, g, beta, y))."""
     ntok = xq.shape[0]
     dk, dv = xq.shape[-1], xv.shape[-1]
@@ -519,22 +588,22 @@ def gdn_fused_prefill(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, z, n
     _shape("initial_state", initial_state, num_seqs, H, dk, dv)
     _shape("o", o, ntok, H, dv)
     _packing(cu_seqlens, cu_seqlens_host, num_seqs)
+    o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else GDN_BF16)
+    od = _tag_dtype(o_tag)
+    _dtype("o", o, od)
+    new = _Alloc(dev)
     if o is None:
-        o = torch.empty((ntok, H, dv), dtype=_tag_dtype(_tag(o_dtype)), device=dev)
-    final_state = (torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
-                   if output_final_state else None)
+        o = new((ntok, H, dv), od)
+    final_state = new((num_seqs, H, dk, dv), torch.float32) if output_final_state else None
     ex = {}
     if export:
         bf = torch.bfloat16
-        ex = dict(q=torch.empty((ntok, H, dk), dtype=bf, device=dev),
-                  k=torch.empty((ntok, H, dk), dtype=bf, device=dev),
-                  v=torch.empty((ntok, H, dv), dtype=bf, device=dev),
-                  g=torch.empty((ntok, H), dtype=torch.float32, device=dev),
-                  beta=torch.empty((ntok, H), dtype=torch.float32, device=dev),
-                  y=torch.empty((ntok, H, dv), dtype=bf, device=dev))
+        ex = dict(q=new((ntok, H, dk), bf), k=new((ntok, H, dk), bf), v=new((ntok, H, dv), bf),
+                  g=new((ntok, H), torch.float32), beta=new((ntok, H), torch.float32),
+                  y=new((ntok, H, dv), bf))
     need = gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = new(max(need, 1), torch.uint8)
     host_cu = None
     if cu_seqlens_host is not None:
         host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
@@ -547,11 +616,12 @@ def gdn_fused_prefill(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, z, n
         _ptr(initial_state, "initial_state", f32), _ptr(final_state, "final_state", f32),
         _ptr(cu_seqlens, "cu_seqlens", torch.int32),
         ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
-        _ptr(o, "o"), _dtype_tag(o), _ptr(ex.get("q"), "q"), _ptr(ex.get("k"), "k"),
+        _ptr(o, "o", od), o_tag, _ptr(ex.get("q"), "q"), _ptr(ex.get("k"), "k"),
         _ptr(ex.get("v"), "v"), _ptr(ex.get("g"), "g"), _ptr(ex.get("beta"), "beta"),
         _ptr(ex.get("y"), "y"), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_fused_prefill")
+    _keep(stream, *new.made)
     return (o, final_state, ex) if export else (o, final_state)
 
 
@@ -580,18 +650,22 @@ def gdn_fused_decode(xq, xk, xv, wq, wk, wv, conv_state, a_raw, b_raw, A_log, dt
     _shape("norm_weight", norm_weight, dv)
     _shape("o", o, N, H, dv)
     o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else x_tag)
+    od = _tag_dtype(o_tag)
+    _dtype("o", o, od)
+    new = _Alloc(xq.device)
     if o is None:
-        o = torch.empty((N, H, dv), dtype=_tag_dtype(o_tag), device=xq.device)
-    y = torch.empty_like(o) if want_y else None
+        o = new((N, H, dv), od)
+    y = new((N, H, dv), od) if want_y else None
     f32 = torch.float32
     st = lib().gdn_fused_decode(
         _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), x_tag, _ptr(wq, "wq", f32),
         _ptr(wk, "wk", f32), _ptr(wv, "wv", f32), 4, _ptr(conv_state, "conv_state", xq.dtype),
         _ptr(a_raw, "a_raw", f32), _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32),
         _ptr(dt_bias, "dt_bias", f32), l2_eps, _ptr(state, "state", f32), _ptr(z, "z"),
-        _ptr(norm_weight, "norm_weight", f32), rms_eps, N, H, dk, dv, _ptr(o, "o"), o_tag,
-        _ptr(y, "y"), _stream(stream))
+        _ptr(norm_weight, "norm_weight", f32), rms_eps, N, H, dk, dv, _ptr(o, "o", od), o_tag,
+        _ptr(y, "y", od), _stream(stream))
     _check(st, "gdn_fused_decode")
+    _keep(stream, *new.made)
     return (o, y) if want_y else o
 
 
@@ -627,13 +701,16 @@ def gdn_fused_decode_multi(xq, xk, xv, wq, wk, wv, conv_state_in, a_raw, b_raw, 
     if step_states is not True:
         _shape("step_states", step_states, N, T, H, dk, dv)
     o_tag = _tag(o_dtype) if o_dtype is not None else (_dtype_tag(o) if o is not None else x_tag)
+    od = _tag_dtype(o_tag)
+    _dtype("o", o, od)
+    new = _Alloc(xq.device)
     if o is None:
-        o = torch.empty((N, T, H, dv), dtype=_tag_dtype(o_tag), device=xq.device)
-    y = torch.empty_like(o) if want_y else None
+        o = new((N, T, H, dv), od)
+    y = new((N, T, H, dv), od) if want_y else None
     if conv_state_out is None:
         conv_state_out = conv_state_in
     if step_states is True:
-        step_states = torch.empty((N, T, H, dk, dv), dtype=torch.float32, device=xq.device)
+        step_states = new((N, T, H, dk, dv), torch.float32)
     f32 = torch.float32
     st = lib().gdn_fused_decode_multi(
         _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(xv, "xv"), x_tag, _ptr(wq, "wq", f32),
@@ -641,9 +718,10 @@ def gdn_fused_decode_multi(xq, xk, xv, wq, wk, wv, conv_state_in, a_raw, b_raw, 
         _ptr(conv_state_out, "conv_state_out", xq.dtype), _ptr(a_raw, "a_raw", f32),
         _ptr(b_raw, "b_raw", f32), _ptr(A_log, "A_log", f32), _ptr(dt_bias, "dt_bias", f32),
         l2_eps, _ptr(state, "state", f32), _ptr(z, "z"), _ptr(norm_weight, "norm_weight", f32),
-        rms_eps, N, T, H, dk, dv, _ptr(o, "o"), o_tag, _ptr(y, "y"),
+        rms_eps, N, T, H, dk, dv, _ptr(o, "o", od), o_tag, _ptr(y, "y", od),
         _ptr(step_states, "step_states", f32), _stream(stream))
     _check(st, "gdn_fused_decode_multi")
+    _keep(stream, *new.made)
     return o, y, step_states
 
 

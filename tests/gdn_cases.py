@@ -19,8 +19,8 @@ RMS_EPS = 1e-6
 # an elementwise bound on the bf16-input path.
 TOL_REL = {False: 1e-4, True: 5e-3}        # keyed by "bf16 path"
 TOL_ABS = 2e-2
-BF16_HALF_ULP_REL = 2.0 ** -8              # RNE rounding bound of a bf16-stored output
-BF16_ULP_REL = 2.0 ** -7                   # one bf16 ulp, relative (bottom of a binade)
+U_BF16 = 2.0 ** -8                         # unit roundoff of bf16 (8 significant bits, RNE)
+BF16_HALF_ULP_REL = U_BF16                 # rounding bound of a bf16-stored output
 
 
 # ----------------------------------------------------------------------------- host <-> device
@@ -58,15 +58,35 @@ def state_rel_errors(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.linalg.norm(x - y, axis=1) / np.maximum(np.linalg.norm(y, axis=1), 1e-30)
 
 
+def o_allowance(o_ref, o_qkv, y_bf16):
+    """Elementwise allowance of the output gate's o beyond the bar (2e-2 plus o's own bf16
+    rounding), against the plain fp64 oracle o_ref. It is derived from the bf16 storage of the
+    pipeline's intermediates, before any comparison:
+      * y stored in bf16 before the gate (y_bf16): each element of a (token, head) row moves by
+        at most u = 2^-8 relative, so the row's RMS moves by at most u as well (its square is a
+        weighted mean of the elements' factors), and o_j = c_j y_j / rms(y) moves by at most
+        (1+u)/(1-u) - 1 = 2u/(1-u) relative;
+      * q, k, v stored in bf16 between the preprocess and the prefill: their effect on o is
+        |o_qkv - o_ref|, where o_qkv is the oracle's own o with its q, k, v rounded to bf16
+        (y left unrounded). It is computed by the oracle alone, exactly, with no GPU value.
+    The RMSNorm maps each row to unit RMS, so in rows where y is small next to the terms that
+    cancel in it (the first tokens of a sequence) the q, k, v storage shows up in o at full
+    size; elsewhere this term is small."""
+    a = np.abs(o_qkv - o_ref)
+    if y_bf16:
+        a = a + 2.0 * U_BF16 / (1.0 - U_BF16) * np.abs(o_ref)
+    return a
+
+
+def max_abs(got, ref) -> float:
+    return float(np.abs(got - ref).max()) if np.size(ref) else 0.0
+
+
 def assert_close(name, got, ref, bf16_path, stored_bf16=False, cu=None, H=None, state=False,
-                 ref_elem=None, inherits_bf16_input=False):
+                 allowance=None):
     """The parity bar: max slice relative L2 <= TOL_REL; on the bf16 path also
-    |got - ref| <= 2e-2 (+ the output's own bf16 rounding if it is stored in bf16).
-    ref_elem, when given, is the reference of the elementwise check (the oracle with the
-    pipeline's bf16 storage of intermediates modelled). inherits_bf16_input marks an output
-    whose elements scale a bf16-stored input elementwise (the output gate's o = c_j y_j):
-    both sides round their own y to bf16, and two roundings of slightly different values
-    can land one ulp apart, which o inherits as up to 2^-7 of |o|."""
+    |got - ref| <= 2e-2 (+ the output's own bf16 rounding if it is stored in bf16, + an
+    elementwise allowance derived beforehand from the arithmetic, e.g. o_allowance)."""
     if state:
         errs = state_rel_errors(got, ref)
     else:
@@ -75,10 +95,10 @@ def assert_close(name, got, ref, bf16_path, stored_bf16=False, cu=None, H=None, 
     tol = TOL_REL[bf16_path]
     assert worst <= tol, f"{name}: max slice rel L2 {worst:.3e} > {tol:.0e}"
     if bf16_path:
-        r = ref if ref_elem is None else ref_elem
+        r = ref
         bound = TOL_ABS + (BF16_HALF_ULP_REL * np.abs(r) if stored_bf16 else 0.0)
-        if inherits_bf16_input:
-            bound = bound + BF16_ULP_REL * np.abs(r)
+        if allowance is not None:
+            bound = bound + allowance
         excess = np.abs(got - r) - bound
         if not np.all(excess <= 0):
             i = np.unravel_index(np.argmax(excess), excess.shape)
@@ -103,13 +123,17 @@ def subset(inp: dict, seqs=None, heads=None) -> dict:
         if seqs else np.zeros(0, np.int64)
     new_cu = np.concatenate([[0], np.cumsum([cu[s + 1] - cu[s] for s in seqs])]).astype(np.int32)
     out = dict(cu=new_cu, H=len(heads), tok=tok, seqs=seqs, heads=heads)
+    every_token = len(tok) == sh.ntok and np.array_equal(tok, np.arange(sh.ntok))
+
+    def pick(a):                                 # slice first, widen the slice only
+        return a[:, heads] if every_token else a[tok][:, heads]
     for key in ("q", "k", "v", "xq", "xk", "xv", "z"):
         if key in inp:
-            a = inp[key][tok][:, heads]          # slice first, widen the slice only
+            a = pick(inp[key])
             out[key] = gi.as_f64(a, a.dtype == np.uint16)
     for key in ("a_raw", "b_raw"):
         if key in inp:
-            out[key] = inp[key][tok][:, heads].astype(np.float64)
+            out[key] = pick(inp[key]).astype(np.float64)
     for key in ("A_log", "dt_bias"):
         out[key] = inp[key].astype(np.float64)[heads]
     for key, d in (("wq", sh.dk), ("wk", sh.dk), ("wv", sh.dv)):
@@ -126,7 +150,8 @@ def subset(inp: dict, seqs=None, heads=None) -> dict:
 def oracle_run(sub: dict, nthreads=None, storage_bf16=False, y_bf16=True) -> dict:
     """The oracle's token mixer on a subset: eqs. 6-10 (if pre-conv streams), 1-4, 11.
     storage_bf16 rounds the intermediates the bf16 pipeline stores (q, k, v after the
-    preprocess, y before the output gate) to bf16, in the oracle's own arithmetic."""
+    preprocess, and y before the output gate when y_bf16) to bf16, in the oracle's own
+    arithmetic; the o of such a run with y_bf16=False is o_allowance's o_qkv."""
     H = sub["H"]
     res = {}
     if "xq" in sub:
@@ -258,8 +283,14 @@ def check_prefill_sampled(inp, res, seqs, heads, y_bf16):
     rep["ST"] = assert_close("ST", gpu_state_slice(res["ST"], seqs, heads), ref["ST"], sh.bf16,
                              state=True)
     if "o" in res:
-        st = oracle_run(sub, storage_bf16=True, y_bf16=y_bf16)
-        rep["o"] = assert_close("o", gpu_slice(res["o"], tok, heads), ref["o"], True,
-                                stored_bf16=True, cu=cu, H=H, ref_elem=st["o"],
-                                inherits_bf16_input=y_bf16)
+        rep["o"], rep["o_max_abs"] = check_o(gpu_slice(res["o"], tok, heads), sub, ref, y_bf16)
     print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in rep.items()}, flush=True)
+
+
+def check_o(got, sub, ref, y_bf16):
+    """o against the plain fp64 oracle, to the bar plus o_allowance. Returns (max slice rel L2,
+    raw max |o - o_ref|)."""
+    qkv = oracle_run(sub, storage_bf16=True, y_bf16=False)
+    err = assert_close("o", got, ref["o"], True, stored_bf16=True, cu=sub["cu"], H=sub["H"],
+                       allowance=o_allowance(ref["o"], qkv["o"], y_bf16))
+    return err, max_abs(got, ref["o"])

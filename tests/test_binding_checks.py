@@ -96,3 +96,50 @@ def test_fused_entry_point_shapes():
             _t(N, T, H), _t(N, H), hv, hv, st, xm, _t(d))
     _raises("conv_state_out has shape", gdn.gdn_fused_decode_multi, xm, xm, xm, w, w, w, hist,
             _t(N, T, H), _t(N, T, H), hv, hv, st, xm, _t(d), conv_state_out=hist[:2])
+
+
+def test_output_dtype_must_match_the_requested_dtype():
+    """A caller-provided output whose dtype differs from the dtype the call writes (an explicit
+    y_dtype / o_dtype / out_dtype, or the default) is refused: the kernel would write elements
+    of the other size into it."""
+    n, H, d = 64, 2, 128
+    q = k = v = _t(n, H, d, dtype=bf)
+    g, beta = _t(n, H), _t(n, H)
+    _raises("y must be torch.float32", gdn.gdn_chunk_prefill, q, k, v, g, beta,
+            y=_t(n, H, d, dtype=bf), y_dtype=f32)
+    _raises("y must be torch.bfloat16", gdn.gdn_chunk_prefill, q, k, v, g, beta,
+            y=_t(n, H, d), y_dtype=bf)
+    _raises("final_state must be torch.float32", gdn.gdn_chunk_prefill, q, k, v, g, beta,
+            final_state=_t(1, H, d, d, dtype=bf))
+    _raises("y must be torch.float32", gdn.gdn_kda_chunk_prefill, q, k, v, _t(n, H, d), beta,
+            y=_t(n, H, d, dtype=bf), y_dtype=f32)
+    N, T = 4, 2
+    xd = _t(N, H, d, dtype=bf)
+    _raises("y must be torch.float32", gdn.gdn_decode_step, xd, xd, xd, _t(N, H), _t(N, H),
+            _t(N, H, d, d), y=xd, y_dtype=f32)
+    xm = _t(N, T, H, d, dtype=bf)
+    _raises("y must be torch.float32", gdn.gdn_decode_multi, xm, xm, xm, _t(N, T, H),
+            _t(N, T, H), _t(N, H, d, d), y=xm, y_dtype=f32)
+    _raises("o must be torch.float32", gdn.gdn_output_gate, _t(n, H, d, dtype=bf),
+            _t(n, H, d, dtype=bf), _t(d), o=_t(n, H, d, dtype=bf), o_dtype=f32)
+    x = _t(n, H, d, dtype=bf)
+    w = _t(H * d, 4)
+    hv = _t(H)
+    for name in ("q", "k", "v"):
+        outs = {name: _t(n, H, d, dtype=bf)}
+        _raises(f"{name} must be torch.float32", gdn.gdn_preprocess, x, x, x, w, w, w, g, beta,
+                hv, hv, H=H, out_dtype=f32, outs=outs)
+        _raises(f"{name} must be torch.float32", gdn.gdn_preprocess_stateful, x, x, x, w, w, w,
+                g, beta, hv, hv, H=H, out_dtype=f32, outs=outs)
+    _raises("g must be torch.float32", gdn.gdn_preprocess, x, x, x, w, w, w, g, beta, hv, hv,
+            H=H, outs={"g": _t(n, H, dtype=bf)})
+    _raises("o must be torch.float32", gdn.gdn_fused_prefill, x, x, x, w, w, w, g, beta, hv, hv,
+            x, _t(d), H=H, o=_t(n, H, d, dtype=bf), o_dtype=f32)
+    hist = _t(N, 3, H * 3 * d, dtype=bf)
+    _raises("o must be torch.float32", gdn.gdn_fused_decode, xd, xd, xd, w, w, w, hist,
+            _t(N, H), _t(N, H), hv, hv, _t(N, H, d, d), xd, _t(d), o=xd, o_dtype=f32)
+    _raises("o must be torch.float32", gdn.gdn_fused_decode_multi, xm, xm, xm, w, w, w, hist,
+            _t(N, T, H), _t(N, T, H), hv, hv, _t(N, H, d, d), xm, _t(d), o=xm, o_dtype=f32)
+    # a given output of the default dtype passes these checks (next: not on the device)
+    _raises("must be a device tensor", gdn.gdn_chunk_prefill, q, k, v, g, beta,
+            y=_t(n, H, d, dtype=bf))

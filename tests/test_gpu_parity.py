@@ -16,7 +16,7 @@ def _announce(msg):
     sys.stdout.flush()
 
 
-def _compare_prefill(inp, res, ref, sub, y_bf16, ref_st=None):
+def _compare_prefill(inp, res, ref, sub, y_bf16):
     sh = inp["shape"]
     bf = sh.bf16
     tok, heads, seqs = sub["tok"], sub["heads"], sub["seqs"]
@@ -36,13 +36,10 @@ def _compare_prefill(inp, res, ref, sub, y_bf16, ref_st=None):
         report["ST"] = C.assert_close("ST", C.gpu_state_slice(res["ST"], seqs, heads), ref["ST"], bf,
                                       state=True)
     if "o" in res:
-        # RMSNorm rescales each (token, head) row of y to unit RMS, so in rows where y is
-        # small (first tokens of a sequence) the bf16 storage rounding of q, k, v is amplified;
-        # the elementwise check therefore models that storage in the oracle.
-        report["o"] = C.assert_close("o", C.gpu_slice(res["o"], tok, heads), ref["o"], True,
-                                     stored_bf16=True, cu=cu, H=H,
-                                     ref_elem=None if ref_st is None else ref_st["o"],
-                                     inherits_bf16_input=y_bf16)
+        # against the plain oracle; the allowance for the pipeline's bf16 storage of q, k, v
+        # and y is derived in gdn_cases.o_allowance
+        report["o"], report["o_max_abs"] = C.check_o(C.gpu_slice(res["o"], tok, heads), sub,
+                                                     ref, y_bf16)
     print("  max slice rel L2:", {k: f"{v:.2e}" for k, v in report.items()}, flush=True)
 
 
@@ -71,8 +68,7 @@ def test_prefill_pipeline_parity(gpu, workload, ov, ydt):
     res = C.gpu_run(inp, y_dtype=ydt)
     sub = C.subset(inp)
     ref = C.oracle_run(sub)
-    ref_st = C.oracle_run(sub, storage_bf16=True, y_bf16=(ydt == "bf16")) if "z" in sub else None
-    _compare_prefill(inp, res, ref, sub, ydt == "bf16", ref_st)
+    _compare_prefill(inp, res, ref, sub, ydt == "bf16")
 
 
 @pytest.mark.parametrize("ov,ydt", [(dict(N=8, H=2, steps=6), "f32"),
