@@ -63,6 +63,8 @@ def lib():
         L.gdn_chunk_prefill.restype = _i
         L.gdn_chunk_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                         _i, _i, _i, _vp, _i, _vp, ctypes.c_size_t, _vp]
+        L.gdn_chunk_prefill_noalloc.restype = _i
+        L.gdn_chunk_prefill_noalloc.argtypes = L.gdn_chunk_prefill.argtypes[:17] + [_vp]
         L.gdn_chunk_backward_workspace_size.restype = ctypes.c_size_t
         L.gdn_chunk_backward_workspace_size.argtypes = [_i, _i, _i, _i, _i]
         L.gdn_chunk_backward.restype = _i
@@ -374,6 +376,42 @@ def gdn_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_chunk_prefill")
     _keep(stream, *new.made)
+    return y, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20      # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
+
+
+def gdn_chunk_prefill_noalloc(q, k, v, g, beta, *, y, initial_state=None, final_state=None,
+                              cu_seqlens=None, cu_seqlens_host=None, num_seqs=1, stream=None):
+    """gdn_chunk_prefill without a workspace: the library uses its own scratch array (one per
+    GPU, NOALLOC_SCRATCH_BYTES). Allocates nothing, here or in the library, so the caller
+    passes y [ntok,H,dv] (bf16 or fp32: its dtype is y_dtype) and final_state (or None: not
+    written). Calls that overlap in time on one GPU share the array and race.
+    Returns (y, final_state)."""
+    ntok, H, dk = q.shape
+    dv = v.shape[-1]
+    _shape("k", k, ntok, H, dk)
+    _shape("v", v, ntok, H, dv)
+    _same_dtype("q", q, k=k, v=v)
+    _shape("g", g, ntok, H)
+    _shape("beta", beta, ntok, H)
+    _shape("initial_state", initial_state, num_seqs, H, dk, dv)
+    _shape("final_state", final_state, num_seqs, H, dk, dv)
+    _shape("y", y, ntok, H, dv)
+    _dtype("final_state", final_state, torch.float32)
+    _packing(cu_seqlens, cu_seqlens_host, num_seqs)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+    f32 = torch.float32
+    st = lib().gdn_chunk_prefill_noalloc(
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _dtype_tag(q), _ptr(g, "g", f32),
+        _ptr(beta, "beta", f32), _ptr(initial_state, "initial_state", f32),
+        _ptr(final_state, "final_state", f32), _ptr(cu_seqlens, "cu_seqlens", torch.int32),
+        ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
+        _ptr(y, "y"), _dtype_tag(y), _stream(stream))
+    _check(st, "gdn_chunk_prefill_noalloc")
     return y, final_state
 
 
@@ -726,7 +764,8 @@ def gdn_fused_decode_multi(xq, xk, xv, wq, wk, wv, conv_state_in, a_raw, b_raw, 
 
 
 __all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_preprocess_stateful",
-           "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_chunk_backward",
+           "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_chunk_prefill_noalloc",
+           "NOALLOC_SCRATCH_BYTES", "gdn_chunk_backward",
            "gdn_chunk_backward_workspace_size", "gdn_kda_chunk_prefill", "gdn_decode_step",
            "gdn_decode_multi", "gdn_output_gate", "gdn_fused_prefill",
            "gdn_fused_prefill_workspace_size", "gdn_fused_decode", "gdn_fused_decode_multi"]

@@ -223,11 +223,17 @@ size_t gdn_chunk_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, i
     return use_matrix_path(in_dtype, dk) ? gdn::chunk_bf16_workspace(ntok, num_seqs, H) : 0;
 }
 
-int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype, const float* g,
-                      const float* beta, const float* initial_state, float* final_state,
-                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
-                      int ntok, int H, int dk, int dv, void* y, int y_dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_chunk_prefill and its allocation-free variant: validation and dispatch, given the
+// workspace (for the variant, the library's scratch array; ws_limit its size, else 0).
+int chunk_prefill_impl(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                       const float* beta, const float* initial_state, float* final_state,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
+                       int ntok, int H, int dk, int dv, void* y, int y_dtype, void* workspace,
+                       size_t workspace_bytes, bool noalloc, void* stream, const char* name) {
     GDN_REQUIRE(valid_dtype(in_dtype) && valid_dtype(y_dtype), GDN_ERR_DTYPE,
                 "in_dtype/y_dtype must be GDN_F32 or GDN_BF16");
     GDN_REQUIRE(H >= 1 && valid_dim(dk) && valid_dim(dv), GDN_ERR_SHAPE,
@@ -242,6 +248,17 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
     if (st) return st;
     GDN_EXTENTS(ntok, H, dk > dv ? dk : dv, num_seqs, (long long)H * dk * dv);
     const size_t need = gdn_chunk_prefill_workspace_size(ntok, num_seqs, H, dk, dv, in_dtype);
+    if (noalloc) {
+        GDN_REQUIRE(need <= GDN_NOALLOC_SCRATCH_BYTES, GDN_ERR_WORKSPACE,
+                    "%s: these sizes need %zu bytes of workspace, more than the %zu bytes of the "
+                    "library's scratch array (use gdn_chunk_prefill with a workspace)",
+                    name, need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+        if (need > 0) {
+            const hipError_t e = gdn::noalloc_scratch(&workspace);
+            if (e != hipSuccess) return hip_status(e, name);
+            workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+        }
+    }
     GDN_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr), GDN_ERR_WORKSPACE,
                 "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
     GDN_OPT_PTR(workspace);
@@ -255,9 +272,32 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
     a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.dk = dk; a.dv = dv;
     a.y = y; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (use_matrix_path(in_dtype, dk))
-        return hip_status(gdn::launch_chunk_bf16(a, s), "gdn_chunk_prefill");
-    return hip_status(gdn::launch_chunk_fp32(a, s), "gdn_chunk_prefill");
+    if (use_matrix_path(in_dtype, dk)) return hip_status(gdn::launch_chunk_bf16(a, s), name);
+    return hip_status(gdn::launch_chunk_fp32(a, s), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype, const float* g,
+                      const float* beta, const float* initial_state, float* final_state,
+                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
+                      int ntok, int H, int dk, int dv, void* y, int y_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    return chunk_prefill_impl(q, k, v, in_dtype, g, beta, initial_state, final_state, cu_seqlens,
+                              cu_seqlens_host, num_seqs, ntok, H, dk, dv, y, y_dtype, workspace,
+                              workspace_bytes, false, stream, "gdn_chunk_prefill");
+}
+
+int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, int in_dtype,
+                              const float* g, const float* beta, const float* initial_state,
+                              float* final_state, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H,
+                              int dk, int dv, void* y, int y_dtype, void* stream) {
+    return chunk_prefill_impl(q, k, v, in_dtype, g, beta, initial_state, final_state, cu_seqlens,
+                              cu_seqlens_host, num_seqs, ntok, H, dk, dv, y, y_dtype, nullptr, 0,
+                              true, stream, "gdn_chunk_prefill_noalloc");
 }
 
 size_t gdn_chunk_backward_workspace_size(int ntok, int num_seqs, int H, int dk, int dv) {

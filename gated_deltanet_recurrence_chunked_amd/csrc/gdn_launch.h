@@ -77,6 +77,10 @@ struct ChunkArgs {
 // all-fp32 chunked path (vector ALU)
 hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t s);
 
+// The device address of this GPU's library-owned scratch array (GDN_NOALLOC_SCRATCH_BYTES,
+// gdn_noalloc.hip), looked up on the first call per device; it never allocates.
+hipError_t noalloc_scratch(void** ptr);
+
 // bf16 matrix-core chunked path (dk = 128): per-chunk T/P kernel + sequential scan kernel
 size_t chunk_bf16_workspace(int ntok, int num_seqs, int H);
 // The fused front end: q, k, v (bf16, written to out[]) and the gates computed from the

@@ -16,7 +16,9 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library never
- *     allocates, frees or retains device memory and keeps no mutable global state.
+ *     allocates, frees or retains device memory and keeps no mutable global state, with
+ *     one exception: gdn_chunk_prefill_noalloc uses a scratch array of the library's own
+ *     (below).
  *   - Layouts are dense, row-major and token-major over packed sequences:
  *       q, k [ntok, H, dk]; v, y, z, o [ntok, H, dv]; g, beta, a_raw, b_raw [ntok, H];
  *       states [num_seqs, H, dk, dv] (fp32); per-head vectors [H]; norm weight [dv].
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -158,6 +160,31 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, int in_dtype,
                       const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
                       int dv, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* Size of the library's scratch array behind gdn_chunk_prefill_noalloc (one per GPU). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * gdn_chunk_prefill_noalloc - gdn_chunk_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes the same arguments minus the workspace and computes the same result
+ * (the same kernels); in place of the workspace it uses a scratch array of
+ * GDN_NOALLOC_SCRATCH_BYTES compiled into the library, one per GPU, which that GPU holds from
+ * the first call on it until the process ends. It calls no hipMalloc, hipFree or other
+ * allocating routine (the first call on a device only looks the array's address up).
+ *   - Sizes whose workspace (gdn_chunk_prefill_workspace_size) exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_WORKSPACE before anything is enqueued
+ *     (B = 4, H = 16, T = 4096 needs about 71 MB and fits; H = 32, T = 65536 does not).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ *     (nothing in it needs to start at zero). Calls that overlap in time on one GPU (on
+ *     different streams, or from different threads) therefore race and give undefined
+ *     results: order them, e.g. on one stream.
+ */
+int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, int in_dtype,
+                              const float* g, const float* beta, const float* initial_state,
+                              float* final_state, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H,
+                              int dk, int dv, void* y, int y_dtype, void* stream);
 
 /* Bytes of device workspace gdn_chunk_backward needs for these sizes. */
 size_t gdn_chunk_backward_workspace_size(int ntok, int num_seqs, int H, int dk, int dv);

@@ -215,3 +215,22 @@ def test_fused_decode_multi_validation(L):
     st = call(st=F + 64)                      # step states over the state
     assert st == 2 and b"step_states" in L.gdn_last_error()
     assert call(xt=3) == 3
+
+
+def test_noalloc_prefill_refuses_sizes_beyond_its_scratch(L):
+    """gdn_chunk_prefill_noalloc checks the workspace these sizes need against the library's
+    scratch array on the host, before anything touches the device."""
+    import gated_deltanet_recurrence_chunked_amd as g
+    need = L.gdn_chunk_prefill_workspace_size(65536, 1, 32, 128, 128, 1)
+    assert need > g.NOALLOC_SCRATCH_BYTES
+    st = L.gdn_chunk_prefill_noalloc(FAKE, FAKE, FAKE, 1, FAKE, FAKE, None, None, None, None, 1,
+                                     65536, 32, 128, 128, FAKE, 1, None)
+    assert st == 6
+    assert b"scratch array" in L.gdn_last_error()
+    header = open(HEADER).read()
+    assert f"#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in header
+    assert g.NOALLOC_SCRATCH_BYTES == 128 << 20
+    # the same validation as gdn_chunk_prefill comes first
+    st = L.gdn_chunk_prefill_noalloc(None, FAKE, FAKE, 1, FAKE, FAKE, None, None, None, None, 1,
+                                     128, 2, 128, 128, FAKE, 1, None)
+    assert st == 1
