@@ -101,6 +101,8 @@ def lib():
                                              _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                              ctypes.c_float, _i, _i, _i, _i, _i, _vp, _i, _vp,
                                              _vp, _vp]
+        L.gdn_mb_stream.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+        L.gdn_mb_mfma_bf16.argtypes = [_vp, _i, _i, _vp]
         _lib = L
     return _lib
 
@@ -595,6 +597,27 @@ def gdn_output_gate(y, z, norm_weight, *, eps=1e-6, o=None, o_dtype=None, stream
     return o
 
 
+def gdn_mb_stream(src, dst, *, stream=None):
+    """Measurement aid: copies src into dst (the same tensor for the in-place stream) with
+    16-byte nontemporal loads and stores. Both are contiguous device tensors of equal byte
+    size, a multiple of 16."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise GdnError("src and dst must have the same size in bytes")
+    st = lib().gdn_mb_stream(_ptr(src, "src"), _ptr(dst, "dst"), nbytes, _stream(stream))
+    _check(st, "gdn_mb_stream")
+
+
+def gdn_mb_mfma_bf16(sink, iters, *, stream=None):
+    """Measurement aid: sink.numel() workgroups of 4 waves, each wave issuing iters rounds of
+    four independent 32x32x16 bf16 matrix-core products. Returns the flops of the call."""
+    _dtype("sink", sink, torch.float32)
+    wg = sink.numel()
+    st = lib().gdn_mb_mfma_bf16(_ptr(sink, "sink"), wg, int(iters), _stream(stream))
+    _check(st, "gdn_mb_mfma_bf16")
+    return wg * 4 * int(iters) * 4 * 32768
+
+
 def gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv) -> int:
     return int(lib().gdn_fused_prefill_workspace_size(ntok, num_seqs, H, dk, dv))
 
@@ -768,4 +791,5 @@ __all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_prep
            "NOALLOC_SCRATCH_BYTES", "gdn_chunk_backward",
            "gdn_chunk_backward_workspace_size", "gdn_kda_chunk_prefill", "gdn_decode_step",
            "gdn_decode_multi", "gdn_output_gate", "gdn_fused_prefill",
-           "gdn_fused_prefill_workspace_size", "gdn_fused_decode", "gdn_fused_decode_multi"]
+           "gdn_fused_prefill_workspace_size", "gdn_fused_decode", "gdn_fused_decode_multi",
+           "gdn_mb_stream", "gdn_mb_mfma_bf16"]

@@ -616,4 +616,26 @@ int gdn_output_gate(const void* y, int y_dtype, const void* z, int z_dtype, cons
                       "gdn_output_gate");
 }
 
+int gdn_mb_stream(const void* src, void* dst, size_t bytes, void* stream) {
+    GDN_REQUIRE(bytes % 16 == 0, GDN_ERR_SHAPE, "bytes must be a multiple of 16 (got %zu)", bytes);
+    if (bytes > 0) {
+        GDN_PTR(src);
+        GDN_PTR(dst);
+        const char* a0 = static_cast<const char*>(src);
+        const char* b0 = static_cast<const char*>(dst);
+        GDN_REQUIRE(a0 == b0 || a0 + bytes <= b0 || b0 + bytes <= a0, GDN_ERR_SHAPE,
+                    "src and dst must be the same buffer or not overlap");
+    }
+    return hip_status(gdn::launch_mb_stream(src, dst, bytes, static_cast<hipStream_t>(stream)),
+                      "gdn_mb_stream");
+}
+
+int gdn_mb_mfma_bf16(float* sink, int workgroups, int iters, void* stream) {
+    GDN_REQUIRE(workgroups >= 0 && iters >= 1, GDN_ERR_SHAPE,
+                "need workgroups >= 0 and iters >= 1 (got %d, %d)", workgroups, iters);
+    if (workgroups > 0) GDN_SPTR(sink);
+    return hip_status(gdn::launch_mb_mfma(sink, workgroups, iters, static_cast<hipStream_t>(stream)),
+                      "gdn_mb_mfma_bf16");
+}
+
 }  // extern "C"

@@ -81,6 +81,10 @@ hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t s);
 // gdn_noalloc.hip), looked up on the first call per device; it never allocates.
 hipError_t noalloc_scratch(void** ptr);
 
+// measurement aids (microbench.hip)
+hipError_t launch_mb_stream(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_mb_mfma(float* sink, int workgroups, int iters, hipStream_t s);
+
 // bf16 matrix-core chunked path (dk = 128): per-chunk T/P kernel + sequential scan kernel
 size_t chunk_bf16_workspace(int ntok, int num_seqs, int H);
 // The fused front end: q, k, v (bf16, written to out[]) and the gates computed from the

@@ -1,11 +1,15 @@
 """Turns rocprofv3 CSV output into the short text summaries kept under profiles/.
 
   kernels  KTRACE_DIR OUT.txt "COMMAND"
-      per-kernel calls / average / min / max duration from <KTRACE_DIR>/*kernel_stats.csv
+      per (kernel, grid size) calls / average / median / min / max duration from
+      <KTRACE_DIR>/*kernel_trace.csv
   traffic  FETCH_DIR WRITE_DIR OUT.json "COMMAND"
-      FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the chunked-prefill kernels, scaled by
-      what the same counters read for the plain 1 GiB device copy the benchmark runs with
-      --calibrate-copy (the factor turns counter KiB into bytes that cross HBM)
+      FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of every library kernel, scaled by what the
+      same counters read for the 1 GiB measurement copy the benchmark runs (the factor turns
+      counter KiB into bytes that cross HBM)
+  mfma     PMC_DIR OUT.json "COMMAND"
+      bf16 / fp32 matrix-core flops and matrix-core busy share per dispatch of every library
+      kernel
 
 Usage: python -m gated_deltanet_recurrence_chunked_amd.rocprof_summary kernels ...
 """
@@ -24,7 +28,7 @@ COPY_BYTES = 1 << 30
 PREFILL_KERNELS = ("chunk_prep_kernel", "chunk_scan_kernel", "chunk_table_kernel")
 
 
-PREFILL_SOURCES = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h", "gdn_launch.h")
+PREFILL_SOURCES = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h")
 
 
 def prefill_source_sha() -> str:
@@ -35,6 +39,16 @@ def prefill_source_sha() -> str:
         with open(os.path.join(PKG, "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def source_shas() -> dict:
+    """Hash of every library source file: a counter figure of a kernel is void once the file
+    that holds it (or a header it includes) changes."""
+    out = {}
+    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        with open(path, "rb") as f:
+            out[os.path.basename(path)] = hashlib.sha256(f.read()).hexdigest()[:16]
+    return out
 
 
 def _one(pattern: str) -> str:
@@ -50,50 +64,111 @@ def short(name: str) -> str:
 
 
 def kernels(ktrace_dir: str, out: str, command: str) -> None:
-    path = _one(os.path.join(ktrace_dir, "**", "*kernel_stats.csv"))
-    rows = list(csv.DictReader(open(path)))
-    lines = [f"# rocprofv3 --kernel-trace --stats summary", f"# command: {command}", "",
-             f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
-    for r in rows:
-        lines.append(f"{short(r['Name'])[:70]:70s} {int(r['Calls']):6d} "
-                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
-                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    """Per (kernel, grid) duration statistics from the kernel trace: one line per workload a
+    kernel ran, so launches of different sizes are not averaged together."""
+    path = _one(os.path.join(ktrace_dir, "**", "*kernel_trace.csv"))
+    per = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        per[(r["Kernel_Name"], grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in per.values())
+    lines = ["# rocprofv3 --kernel-trace summary, per kernel and grid size (threads)",
+             f"# command: {command}", "",
+             f"{'kernel':64s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} "
+             f"{'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for (name, grid), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        lines.append(f"{short(name)[:64]:64s} {grid:9d} {len(v):6d} {sum(v) / len(v):9.2f} "
+                     f"{v[len(v) // 2]:9.2f} {v[0]:9.2f} {v[-1]:9.2f} {100 * sum(v) / total:6.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
 def _counter(dir_: str, counter: str):
+    """Counter values per dispatch, keyed by kernel name and grid size (one workload each)."""
     path = _one(os.path.join(dir_, "**", "*counter_collection.csv"))
     per = defaultdict(list)
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] == counter:
-            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            per[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
     return per
 
 
+def _key(k) -> str:
+    name, grid = k
+    return f"{short(name)} [grid {grid}]"
+
+
+def _library_kernel(name: str) -> bool:
+    """Kernels of libgdn (torch's own kernels and the runtime's blits are left out)."""
+    sk = short(name)
+    return not (sk.startswith("at::") or sk.startswith("__amd") or "at::native" in name)
+
+
 def traffic(fetch_dir: str, write_dir: str, out: str, command: str) -> None:
-    res = {"command": command, "kernel_source_sha256": prefill_source_sha(), "kernels": {}}
+    """FETCH_SIZE and WRITE_SIZE per dispatch of every library kernel, in bytes: the counters'
+    KiB scaled by what they read for the 1 GiB measurement copy (stream_kernel, 1 GiB read and
+    1 GiB written per dispatch)."""
+    res = {"command": command, "kernel_source_sha256": prefill_source_sha(),
+           "source_sha256": source_shas(), "kernels": {}}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _counter(d, counter)
-        copies = [max(v) for k, v in per.items() if "copyBuffer" in k or "copy" in k.lower()]
+        copies = [max(v) for k, v in per.items() if "stream_kernel" in k[0]]
         if not copies:
-            raise SystemExit(f"no copy kernel among {list(per)}")
+            raise SystemExit(f"no stream_kernel dispatch among {list(per)}")
         copy_kib = max(copies)
         factor = (COPY_BYTES / 1024.0) / copy_kib
         res[f"copy_{counter}_kib"] = copy_kib
         res[f"{counter}_factor"] = factor
         for k, v in per.items():
-            sk = short(k)
-            if any(p in sk for p in PREFILL_KERNELS):
-                e = res["kernels"].setdefault(sk, {})
-                e[f"{counter}_kib_per_dispatch"] = sum(v) / len(v)
-                e[f"{counter}_bytes"] = sum(v) / len(v) * 1024.0 * factor
+            if not _library_kernel(k[0]) or "stream_kernel" in k[0]:
+                continue
+            e = res["kernels"].setdefault(_key(k), {"dispatches": len(v)})
+            e[f"{counter}_kib_per_dispatch"] = sum(v) / len(v)
+            e[f"{counter}_bytes"] = sum(v) / len(v) * 1024.0 * factor
     total = 0.0
     for sk, e in res["kernels"].items():
         e["bytes"] = e.get("FETCH_SIZE_bytes", 0.0) + e.get("WRITE_SIZE_bytes", 0.0)
-        total += e["bytes"]
+        if any(p in sk for p in PREFILL_KERNELS):
+            total += e["bytes"]
     res["gdn_chunk_prefill_bytes_per_call"] = total
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+XCC_NUM = 8        # GRBM_GUI_ACTIVE is summed over the 8 XCDs in the counter file
+SIMD_NUM = 1024    # 256 CUs x 4 SIMDs
+
+
+def mfma(pmc_dir: str, out: str, command: str) -> None:
+    """Matrix-core counters per dispatch of every library kernel:
+      flops_bf16 / flops_f32  SQ_INSTS_VALU_MFMA_MOPS_{BF16,F32} x 512 (the counters count
+                              multiply-add work in units of 512 flops);
+      mfma_busy_frac          SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE / XCDs) x SIMDs,
+                              the share of SIMD-cycles the matrix cores were busy."""
+    res = {"command": command, "kernel_source_sha256": prefill_source_sha(),
+           "source_sha256": source_shas(), "kernels": {}}
+    cnt = {c: _counter(pmc_dir, c) for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                                "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                                                "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")}
+    names = set()
+    for per in cnt.values():
+        names.update(k for k in per if _library_kernel(k[0]))
+    total = 0.0
+    for k in sorted(names):
+        avg = {c: (sum(per[k]) / len(per[k]) if per.get(k) else 0.0) for c, per in cnt.items()}
+        gui = avg["GRBM_GUI_ACTIVE"] / XCC_NUM
+        e = {"dispatches": len(cnt["GRBM_GUI_ACTIVE"].get(k, [])),
+             "flops_bf16": avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+             "flops_f32": avg["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512.0,
+             "gui_active_cycles": gui,
+             "mfma_busy_frac": (avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM)) if gui else None}
+        res["kernels"][_key(k)] = e
+        if any(p in short(k[0]) for p in PREFILL_KERNELS):
+            total += e["flops_bf16"] + e["flops_f32"]
+    res["gdn_chunk_prefill_mfma_flops_per_call"] = total
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
@@ -104,6 +179,8 @@ if __name__ == "__main__":
         kernels(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 6 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
+        mfma(sys.argv[2], sys.argv[3], sys.argv[4])
     else:
         print(__doc__)
         sys.exit(2)

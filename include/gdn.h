@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
     GDN_OK = 0,
@@ -370,6 +370,28 @@ int gdn_fused_decode_multi(const void* xq, const void* xk, const void* xv, int x
                            float l2_eps, float* state, const void* z, const float* norm_weight,
                            float rms_eps, int N, int T, int H, int dk, int dv, void* o,
                            int o_dtype, void* y, float* step_states, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Measurement aids (not operations of the layer). They measure, on the device the library
+ * runs on, the two ceilings its roofline figures are read against: the HBM bandwidth of the
+ * streaming access pattern and the bf16 matrix-core issue rate. Same conventions as above
+ * (device pointers owned by the caller, asynchronous on `stream`, gdn_status on invalid
+ * arguments).
+ *
+ * gdn_mb_stream - copies `bytes` bytes from src to dst with 16-byte nontemporal loads and
+ *   stores, every byte read once and written once. src == dst is allowed and gives the
+ *   in-place read-modify-write stream (the decode state's pattern); otherwise the two
+ *   ranges must not overlap (GDN_ERR_SHAPE). bytes must be a multiple of 16 and both
+ *   pointers 16-byte aligned.
+ *
+ * gdn_mb_mfma_bf16 - `workgroups` workgroups of 4 waves; every wave issues `iters` rounds of
+ *   four independent v_mfma_f32_32x32x16_bf16 (32768 flops each), so one call performs
+ *   workgroups * 4 * iters * 4 * 32768 flops. sink: [workgroups] fp32, one value per
+ *   workgroup (a sum of its results, written so the work cannot be elided). workgroups >= 0,
+ *   iters >= 1.
+ */
+int gdn_mb_stream(const void* src, void* dst, size_t bytes, void* stream);
+int gdn_mb_mfma_bf16(float* sink, int workgroups, int iters, void* stream);
 
 #ifdef __cplusplus
 }

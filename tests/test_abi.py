@@ -234,3 +234,14 @@ def test_noalloc_prefill_refuses_sizes_beyond_its_scratch(L):
     st = L.gdn_chunk_prefill_noalloc(None, FAKE, FAKE, 1, FAKE, FAKE, None, None, None, None, 1,
                                      128, 2, 128, 128, FAKE, 1, None)
     assert st == 1
+
+
+def test_measurement_aid_validation(L):
+    assert L.gdn_mb_stream(FAKE, FAKE + 4096, 17, None) == 2          # not a multiple of 16
+    assert L.gdn_mb_stream(None, FAKE, 16, None) == 1
+    assert L.gdn_mb_stream(MIS, FAKE + 4096, 16, None) == 5
+    assert L.gdn_mb_stream(FAKE, FAKE + 16, 64, None) == 2           # partial overlap
+    assert L.gdn_last_error().startswith(b"src and dst must be the same buffer")
+    assert L.gdn_mb_mfma_bf16(FAKE, -1, 1, None) == 2
+    assert L.gdn_mb_mfma_bf16(FAKE, 1, 0, None) == 2
+    assert L.gdn_mb_mfma_bf16(None, 1, 1, None) == 1
