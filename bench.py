@@ -548,6 +548,18 @@ def bench_varlen(torch, gdn, gi, dev, tm):
     t_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in kt]))
     t_pf = float(np.mean([e[1].elapsed_time(e[2]) for e in kt]))
     t_og = float(np.mean([e[2].elapsed_time(e[3]) for e in kt]))
+    # the same token mixer through the fused entry point (at this many (sequence, head) pairs
+    # the output gate runs in the scan's epilogue)
+    wsf = torch.empty(gdn.gdn_fused_prefill_workspace_size(ntok, nseq, H, dk, dv),
+                      dtype=torch.uint8, device=dev)
+
+    def fstep(i):
+        gdn.gdn_fused_prefill(xq, xk, xv, wq, wk, wv, a_raw, b_raw, A_log, dt_bias, z, nw, H=H,
+                              initial_state=S0, cu_seqlens=cu, cu_seqlens_host=cu_host,
+                              num_seqs=nseq, o=o, workspace=wsf)
+    fstep(0)
+    fms = tm.region(fstep, n)
+    del wsf
     b, f = prefill_algorithmic(H, dk, dv, ntok, nseq, True, True)
     res = {"workload": f"varlen pipeline: {nseq} packed sequences (seeded log-uniform lengths in "
                        f"[128, 32768], {ntok} tokens), H=16 d=128, bf16, per-sequence S0 and S_T",
@@ -558,9 +570,12 @@ def bench_varlen(torch, gdn, gi, dev, tm):
                           "gdn_output_gate": round(t_og * 1e3, 1)},
            "prefill_hbm_frac": round(b / (t_pf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "prefill_mfma_frac": round(f / (t_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-           "longest_sequence": int(max(sh.lengths))}
+           "longest_sequence": int(max(sh.lengths)),
+           "fused_us_per_step": round(fms * 1e3, 1),
+           "fused_Mtok_s": round(ntok / (fms * 1e-3) / 1e6, 2),
+           "fused_vs_separate_kernels": round(ms / fms, 3)}
     log(f"[bench] varlen pipeline {ms * 1e3:.1f} us/step = {res['Mtok_s']} Mtok/s "
-        f"(prefill {t_pf * 1e3:.1f} us)")
+        f"(prefill {t_pf * 1e3:.1f} us); fused {fms * 1e3:.1f} us/step ({ms / fms:.2f}x)")
     del xq, xk, xv, z, outs, y, o, ws, S0, ST, a_raw, b_raw
     torch.cuda.empty_cache()
     return res

@@ -321,137 +321,6 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     prep_chunk_head(a, chunk, h, t0, n, gv, bv, sA, sG, sB);
 }
 
-// ------------------------------------------------------------------ fused front end
-// eqs. (6)-(10) of the notes for one chunk of HPW heads, then each head's T and P (one wave
-// per head), in one workgroup: conv (width 4, zero input before the sequence start) -> SiLU
-// -> L2Norm for q and k, conv -> SiLU for v, the gates beta = sigmoid(b), g = -e^A
-// softplus(a + dt_bias). q, k, v leave in bf16 (the scan reads them) with plain stores, so the
-// T/P stage that follows the barrier reads q and k back from L2, not HBM.
-// Stream layout: a thread owns 8 adjacent channels (one 16-byte bf16 store) of a strip of
-// D/8 consecutive rows; the D/8 threads of one (row, head) are adjacent lanes, so the L2Norm
-// is an in-register shuffle reduction. The 3 rows before a strip are its conv window.
-// A thread's rows of one stream come in P pieces of RP consecutive rows, each with the 3 rows
-// before it as its conv window: issue() puts a piece's loads in flight, run() computes and
-// stores it. Two pieces are in flight at a time (the next one loads while this one runs).
-template <int HPW, int D, typename Tin>
-struct FrontPiece {
-    static constexpr int G = HPW * D / 8;              // channel groups of the head group
-    static constexpr int RS = kC * G / (HPW * kWave);  // rows per thread per stream (D / 8)
-    static constexpr int P = sizeof(Tin) == 2 ? 2 : 4; // pieces per stream
-    static constexpr int RP = RS / P;                  // rows per piece
-    typename Vec8<Tin>::Raw raw[RP + 3];               // rows r0-3 .. r0+RP-1
-
-    __device__ __forceinline__ static int first_row(int part) {
-        return (threadIdx.x / G) * RS + part * RP;
-    }
-
-    __device__ __forceinline__ void issue(const FrontArgs& f, int role, int part, int t0, int n,
-                                          int seq_lo, int h0, int H) {
-        const int r0 = first_row(part), c = h0 * D + (threadIdx.x % G) * 8;
-        const Tin* x = static_cast<const Tin*>(f.x[role]);
-        // addresses clamped into the chunk's sequence: rows before its start are zeroed in
-        // run(), rows past n are not stored
-#pragma unroll
-        for (int j = 0; j < RP + 3; ++j) {
-            const int t = min(max(t0 + r0 - 3 + j, seq_lo), t0 + n - 1);
-            raw[j] = Vec8<Tin>::template load_raw<true>(x + (size_t)t * H * D + c);
-        }
-    }
-
-    __device__ __forceinline__ void run(const FrontArgs& f, int role, int part, int t0, int n,
-                                        int seq_lo, int h0, int H) const {
-        const int r0 = first_row(part), c = h0 * D + (threadIdx.x % G) * 8;
-        uint16_t* out = f.out[role];
-        float w[8][4];
-        {
-            const float4* wp = reinterpret_cast<const float4*>(f.w[role] + (size_t)c * 4);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 t = wp[i];
-                w[i][0] = t.x; w[i][1] = t.y; w[i][2] = t.z; w[i][3] = t.w;
-            }
-        }
-        float win[3][8];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            Vec8<Tin>::unpack(raw[j], win[j]);
-            if (t0 + r0 - 3 + j < seq_lo)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) win[j][i] = 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < RP; ++j) {
-            float xi[8], act[8], ss = 0.f;
-            Vec8<Tin>::unpack(raw[j + 3], xi);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                act[i] = siluf_(conv4(w[i][0], w[i][1], w[i][2], w[i][3], win[0][i], win[1][i],
-                                      win[2][i], xi[i]));
-                ss = __builtin_fmaf(act[i], act[i], ss);
-            }
-            if (role < 2) {
-                ss = group_sum<D / 8>(ss);
-                const float inv = frsq(ss + f.l2_eps);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) act[i] *= inv;
-            }
-            if (r0 + j < n) Vec8<uint16_t>::store(out + (size_t)(t0 + r0 + j) * H * D + c, act);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                win[0][i] = win[1][i];
-                win[1][i] = win[2][i];
-                win[2][i] = xi[i];
-            }
-        }
-    }
-};
-
-template <int HPW, int DV, typename Tin>
-__global__ void __launch_bounds__(HPW * kWave, 2) chunk_front_kernel(DevArgs a, FrontArgs f) {
-    __shared__ __attribute__((aligned(16))) float sA[HPW][kC * kStrA];
-    __shared__ __attribute__((aligned(16))) float sG[HPW][kC], sB[HPW][kC];
-    const int chunk = blockIdx.x, h0 = blockIdx.y * HPW;
-    int seq, t0, n;
-    if (!chunk_of(a, chunk, seq, t0, n)) return;
-    const int seq_lo = a.cu ? a.cu[seq] : seq * a.L, H = a.H;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, h = h0 + wave;
-    const size_t e = (size_t)(t0 + min(lane, n - 1)) * H + h;
-    const float ar = f.a_raw[e], br = f.b_raw[e];
-    {
-        // pieces in order q0..q(P-1), k0..k(P-1), v0..; buffers x0/x1 alternate (P is even)
-        using PK = FrontPiece<HPW, kDK, Tin>;
-        using PV = FrontPiece<HPW, DV, Tin>;
-        constexpr int NQK = 2 * PK::P;
-        PK x0, x1;
-        PV y0, y1;
-        x0.issue(f, 0, 0, t0, n, seq_lo, h0, H);
-#pragma unroll
-        for (int i = 0; i < NQK; i += 2) {
-            x1.issue(f, (i + 1) / PK::P, (i + 1) % PK::P, t0, n, seq_lo, h0, H);
-            x0.run(f, i / PK::P, i % PK::P, t0, n, seq_lo, h0, H);
-            if (i + 2 < NQK) x0.issue(f, (i + 2) / PK::P, (i + 2) % PK::P, t0, n, seq_lo, h0, H);
-            else y0.issue(f, 2, 0, t0, n, seq_lo, h0, H);
-            x1.run(f, (i + 1) / PK::P, (i + 1) % PK::P, t0, n, seq_lo, h0, H);
-        }
-#pragma unroll
-        for (int i = 0; i < PV::P; i += 2) {
-            y1.issue(f, 2, i + 1, t0, n, seq_lo, h0, H);
-            y0.run(f, 2, i, t0, n, seq_lo, h0, H);
-            if (i + 2 < PV::P) y0.issue(f, 2, i + 2, t0, n, seq_lo, h0, H);
-            y1.run(f, 2, i + 1, t0, n, seq_lo, h0, H);
-        }
-    }
-    // gates: wave = head of the group, lane = row (rows >= n repeat row n-1, as the prep expects)
-    const float gv = gate_g(f.A_log[h], ar, f.dt_bias[h]);
-    const float bv = gate_beta(br);
-    if (f.g_out && lane < n) {
-        f.g_out[e] = gv;
-        f.beta_out[e] = bv;
-    }
-    __syncthreads();   // the chunk's q, k rows of every head are written (and in L2)
-    prep_chunk_head(a, chunk, h, t0, n, gv, bv, sA[wave], sG[wave], sB[wave]);
-}
-
 // ------------------------------------------------------------------ sequential chunk scan
 // One 4-wave workgroup per (sequence, head, 32-column slice of d_v), one wave per SIMD:
 //   waves 0-1 ("chain" waves) carry the recurrence of one 16-column slice each,
@@ -975,29 +844,386 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ full-row scan
+// One workgroup per (sequence, head) holding all 128 d_v columns: 8 waves, wave w runs the
+// chain above for columns 16w .. 16w + 15 and also forms their output, Y = gamma Q S + P U
+// (as the output wave above does, from the same operands in the same order). Every wave loads
+// an eighth of the next chunk's tiles (K, V, Q, T, P and the gate rows) straight into LDS at
+// the start of a step. With all the columns of a token's y in one workgroup, the gated
+// zero-centred RMSNorm of eq. (11) (o = sigmoid(z) (1 + w) y / rms(y) over the d_v columns)
+// runs in the scan's epilogue: the waves exchange their per-token sums of y^2 in LDS and
+// chunk c's o is formed at the start of step c + 1, after the barrier both need anyway, so y
+// need not leave the chip. Two waves share a SIMD and hide each other's latency: a CU does
+// about 3.5 times the chunk-columns per unit time of the sliced scan, but holds one (sequence,
+// head), so the launcher takes this kernel when the pairs fill the chip.
+constexpr int kWideWaves = 8;
+constexpr int kWideThreads = kWideWaves * kWave;
+constexpr int kWOffK = 0;                    // [64][128] bf16, 16-byte units swizzled per row
+constexpr int kWOffV = kWOffK + kC * kDK;    // [64][128], the same
+constexpr int kWOffQ = kWOffV + kC * kDK;    // [64][128], the same
+constexpr int kWOffT = kWOffQ + kC * kDK;    // [64][64], the same
+constexpr int kWOffP = kWOffT + kC * kC;     // [64][64], the same
+constexpr int kWOffG = kWOffP + kC * kC;     // beta | gamma | gamma_C / gamma (+ 256 bytes)
+constexpr int kWSlot = kWOffG + 512;
+
+struct GateDev {
+    const void* z;          // [ntok, H, 128]
+    const float* w;         // [128] zero-centred RMSNorm weight
+    void* o;                // [ntok, H, 128]
+    float eps;
+};
+
+template <typename Ty, bool kGate, typename Tz, typename To>
+__global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a, GateDev gd_) {
+    // The two slots are separate arrays and each half of the 2-unrolled chunk loop names its
+    // slots statically: the compiler then sees that the direct loads into one slot cannot alias
+    // the reads of the other, and inserts no wait for the loads in flight before those reads
+    // (with one array and a computed slot it waits for all of them at the first LDS read).
+    __shared__ __attribute__((aligned(16))) uint16_t ring0[kWSlot];
+    __shared__ __attribute__((aligned(16))) uint16_t ring1[kWSlot];
+    __shared__ float ssq[kGate ? 2 : 1][kWideWaves][kC];   // per-wave sums of y^2 per token
+
+    const int pair = blockIdx.x;
+    if (pair >= a.num_seqs * a.H) return;
+    const int rank = pair / a.H, h = pair % a.H;
+    const int seq = a.order ? a.order[rank] : rank;
+    int lo, hi, cbase;
+    if (a.cu) {
+        lo = a.cu[seq];
+        hi = a.cu[seq + 1];
+        cbase = a.chunk_start[seq];
+    } else {
+        lo = seq * a.L;
+        hi = lo + a.L;
+        cbase = seq * ((a.L + kC - 1) / kC);
+    }
+    const int nchunks = (hi - lo + kC - 1) / kC;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15, g = lane >> 4;
+    const int j0w = 16 * wave;
+    constexpr int DV = 128;
+
+    // ---- this wave's share of a chunk's tiles, loaded straight into `slot`
+    auto load_chunk = [&](int ck, uint16_t* slot) __attribute__((always_inline)) {
+        const int t0 = lo + ck * kC, n = min(kC, hi - t0);
+        const size_t ch = (size_t)(cbase + ck) * a.H + h;
+        // [64][128] rows of K, V and Q: 16 one-kilobyte pieces each, two per wave
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int i = 2 * wave + j;
+            const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
+            const size_t src = ((size_t)(t0 + min(row, n - 1)) * a.H + h) * kDK + u * 8;
+            dma16(a.k + src, slot + kWOffK + i * 512);
+            dma16(a.v + src, slot + kWOffV + i * 512);
+            dma16(a.q + src, slot + kWOffQ + i * 512);
+        }
+        // [64][64] T and P: 8 pieces each, one per wave
+        {
+            const int row = 8 * wave + (lane >> 3), u = (lane & 7) ^ swz(row);
+            dma16(a.Tw + ch * kC * kC + row * kC + u * 8, slot + kWOffT + wave * 512);
+            dma16(a.Pw + ch * kC * kC + row * kC + u * 8, slot + kWOffP + wave * 512);
+        }
+        if (wave == 0) dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kWOffG);
+    };
+
+    const size_t sbase = ((size_t)seq * a.H + h) * kDK * DV;
+    f32x4 S[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = f32x4{};
+    if (a.S0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sbase + (size_t)relabel(t, 4 * g + i) * DV + j0w + c16];
+    }
+    bf16x8 Sb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Sb[s] = to_bf16x8(S[2 * s], S[2 * s + 1]);
+
+    // per-lane LDS offsets (elements, from a slot) of the fragment reads (as chunk_scan_kernel)
+    int okf[2][2], otf[2][2], okt[2][2], ovf[2], oqf[2], opf[2];
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2) {
+        const int r = relabel(a2, c16);
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            okf[a2][sp] = kWOffK + r * kDK + (((4 * sp + g) ^ swz(r)) << 3);
+            otf[a2][sp] = kWOffT + r * kC + (((4 * sp + g) ^ swz(r)) << 3);
+        }
+    }
+    const int jj = (lane & 15) >> 2, r4 = lane & 3;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int tok = 8 * g + jj + 4 * hf;
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) okt[hf][tp] = kWOffK + tok * kDK + (((4 * tp + r4) ^ swz(tok)) << 3);
+        // V^T at the lane's relabelled tokens: 4 consecutive tokens of column j0w + c16
+        ovf[hf] = kWOffV + tok * kDK + (((2 * wave + (r4 >> 1)) ^ swz(tok)) << 3) + 4 * (r4 & 1);
+    }
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+        oqf[sp] = kWOffQ + c16 * kDK + (((4 * sp + g) ^ swz(c16)) << 3);
+        opf[sp] = kWOffP + c16 * kC + (((4 * sp + g) ^ swz(c16)) << 3);
+    }
+
+    // output: a lane holds y at token 16 rt + c16, columns j0w + 4g .. j0w + 4g + 3
+    const size_t ytok = (size_t)a.H * DV;
+    const size_t ylane = (size_t)h * DV + j0w + 4 * g + (size_t)c16 * ytok;
+    float gain[4];
+    if constexpr (kGate) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gain[i] = 1.0f + gd_.w[j0w + 4 * g + i];
+    }
+    f32x4 YT[4];      // chunk c - 1's y, held across the barrier until it is stored
+    float zv[4][4];   // z at the same positions
+    auto epilogue = [&](int cy) __attribute__((always_inline)) {
+        const int ty = lo + cy * kC, ny = min(kC, hi - ty);
+        const float* part = &ssq[kGate ? (cy & 1) : 0][0][0];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int tk = 16 * rt + c16;
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWideWaves; ++w) tot += part[w * kC + tk];
+            const float inv = frsq(tot * (1.0f / DV) + gd_.eps);
+            float ov[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = sigmoidf_(zv[rt][i]) * (gain[i] * (YT[rt][i] * inv));
+            if (tk < ny) {
+                const size_t off = ylane + (size_t)(ty + 16 * rt) * ytok;
+                if constexpr (sizeof(To) == 2) {
+                    u32x2 o2;
+                    o2.x = pack_bf2(ov[0], ov[1]);
+                    o2.y = pack_bf2(ov[2], ov[3]);
+                    __builtin_nontemporal_store(o2, reinterpret_cast<u32x2*>(static_cast<To*>(gd_.o) + off));
+                } else {
+                    __builtin_nontemporal_store(f32x4{ov[0], ov[1], ov[2], ov[3]},
+                                                reinterpret_cast<f32x4*>(static_cast<To*>(gd_.o) + off));
+                }
+            }
+        }
+    };
+    auto store_y = [&](int cy) __attribute__((always_inline)) {
+        const int ty = lo + cy * kC, ny = min(kC, hi - ty);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if (16 * rt + c16 < ny) {
+                Ty* yp = static_cast<Ty*>(a.y) + ylane + (size_t)(ty + 16 * rt) * ytok;
+                if constexpr (sizeof(Ty) == 2) {
+                    u32x2 o2;
+                    o2.x = pack_bf2(YT[rt][0], YT[rt][1]);
+                    o2.y = pack_bf2(YT[rt][2], YT[rt][3]);
+                    __builtin_nontemporal_store(o2, reinterpret_cast<u32x2*>(yp));
+                } else {
+                    __builtin_nontemporal_store(YT[rt], reinterpret_cast<f32x4*>(yp));
+                }
+            }
+        }
+    };
+    auto load_z = [&](int cz) __attribute__((always_inline)) {
+        const int tz = lo + cz * kC, nz = min(kC, hi - tz);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const Tz* zp = static_cast<const Tz*>(gd_.z) + (size_t)h * DV + j0w + 4 * g +
+                           (size_t)(tz + min(16 * rt + c16, nz - 1)) * ytok;
+            if constexpr (sizeof(Tz) == 2) {
+                const u32x2 zz = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(zp));
+                zv[rt][0] = __uint_as_float(zz.x << 16);
+                zv[rt][1] = __uint_as_float(zz.x & 0xffff0000u);
+                zv[rt][2] = __uint_as_float(zz.y << 16);
+                zv[rt][3] = __uint_as_float(zz.y & 0xffff0000u);
+            } else {
+                const f32x4 zz = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zp));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zv[rt][i] = zz[i];
+            }
+        }
+    };
+
+    if (nchunks > 0) load_chunk(0, ring0);
+    GDN_WAIT_VMCNT(0);
+    lds_barrier();
+    // Chunk c's results leave at the start of step c + 1, before that step's loads: the wait
+    // for the loads at the end of a step (the vector-memory counter counts stores too, in issue
+    // order) then never waits for stores issued in the same step.
+    auto step = [&](int c, const uint16_t* slot, uint16_t* next) __attribute__((always_inline)) {
+        if (c >= 1) {
+            if constexpr (kGate) {
+                epilogue(c - 1);
+                if (a.y) store_y(c - 1);
+            } else {
+                store_y(c - 1);
+            }
+        }
+        if (c + 1 < nchunks) load_chunk(c + 1, next);
+        if constexpr (kGate) load_z(c);
+        const float* sG = reinterpret_cast<const float*>(slot + kWOffG);   // beta | gamma | gamma_C/gamma
+        auto kfrag = [&](int rt, int s) {
+            return frag(slot + okf[rt & 1][s & 1] + (rt >> 1) * 32 * kDK + (s >> 1) * 64);
+        };
+        auto tfrag = [&](int rt, int s) { return frag(slot + otf[rt & 1][s] + (rt >> 1) * 32 * kC); };
+        auto ktr = [&](int t, int s, int hf) {
+            return lds_tr16(slot + okt[hf][(t >> 1) & 1] + s * 32 * kDK + (t >> 2) * 64 + 4 * (t & 1));
+        };
+        auto grow = [&](int which, int rt) {
+            return *reinterpret_cast<const f32x4*>(sG + which * kC + 8 * g + 32 * (rt >> 1) + 4 * (rt & 1));
+        };
+        const float gC = sG[kC + kC - 1];
+
+        // ---- K S and Q S (both against the state at the chunk start)
+        f32x4 KS[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) KS[rt] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 kf[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) kf[rt] = kfrag(rt, s);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) KS[rt] = mfma16(kf[rt], Sb[s], KS[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            YT[rt] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                YT[rt] = mfma16(Sb[s], frag(slot + oqf[s & 1] + rt * 16 * kDK + (s >> 1) * 64), YT[rt]);
+        }
+        GDN_SCHED_FENCE();
+        // ---- R = beta (V - gamma KS), split into bf16 hi + lo
+        f32x4 R[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 bet = grow(0, rt), gam = grow(1, rt);
+            const s16x4 vv = lds_tr16(slot + ovf[rt & 1] + (rt >> 1) * 32 * kDK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R[rt][i] = bet[i] * (bf2f(uint16_t(vv[i])) - gam[i] * KS[rt][i]);
+        }
+        bf16x8 Rh[2], Rl[2];
+        split8(R[0], R[1], Rh[0], Rl[0]);
+        split8(R[2], R[3], Rh[1], Rl[1]);
+        GDN_SCHED_FENCE();
+        // ---- U = T R (T unit lower triangular: token rows < 32 need step 0 only)
+        f32x4 U[4];
+        {
+            bf16x8 tf[4][2];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    if (s2 <= (rt >> 1)) tf[rt][s2] = tfrag(rt, s2);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) U[rt] = f32x4{};
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rh[0], U[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rl[0], U[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rh[1], U[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rl[1], U[rt]);
+        }
+        GDN_SCHED_FENCE();
+        // ---- Y^T = gamma (S^T Q^T) + U^T P^T, the order of the output wave above
+        {
+            bf16x8 Uh[2], Ul[2];
+            split8(U[0], U[1], Uh[0], Ul[0]);
+            split8(U[2], U[3], Uh[1], Ul[1]);
+            const float* sGq = sG;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) YT[rt] *= sGq[kC + 16 * rt + c16];
+            bf16x8 pf[4][2];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    if (s2 <= (rt >> 1)) pf[rt][s2] = frag(slot + opf[s2] + rt * 16 * kC);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Uh[0], pf[rt][0], YT[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) YT[rt] = mfma16(Ul[0], pf[rt][0], YT[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) YT[rt] = mfma16(Uh[1], pf[rt][1], YT[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) YT[rt] = mfma16(Ul[1], pf[rt][1], YT[rt]);
+        }
+        GDN_SCHED_FENCE();
+        // ---- W = diag(gamma_C / gamma) U, split; S = gamma_C S + K^T W
+        bf16x8 Wh[2], Wl[2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] *= grow(2, rt);
+        split8(U[0], U[1], Wh[0], Wl[0]);
+        split8(U[2], U[3], Wh[1], Wl[1]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            S[t] *= gC;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const u32x2 p0 = __builtin_bit_cast(u32x2, ktr(t, s2, 0));
+                const u32x2 p1 = __builtin_bit_cast(u32x2, ktr(t, s2, 1));
+                const u32x4 pk = {p0.x, p0.y, p1.x, p1.y};
+                const bf16x8 ktf = __builtin_bit_cast(bf16x8, pk);
+                S[t] = mfma16(ktf, Wh[s2], S[t]);
+                S[t] = mfma16(ktf, Wl[s2], S[t]);
+            }
+            if (t & 1) Sb[t >> 1] = to_bf16x8(S[t - 1], S[t]);
+        }
+        GDN_SCHED_FENCE();
+        if constexpr (kGate) {
+            // this wave's sums of y^2 over its 16 columns, per token, for the epilogue
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                float ss = YT[rt][0] * YT[rt][0] + YT[rt][1] * YT[rt][1] + YT[rt][2] * YT[rt][2] +
+                           YT[rt][3] * YT[rt][3];
+                ss += __shfl_xor(ss, 16, kWave);
+                ss += __shfl_xor(ss, 32, kWave);
+                if (g == 0) ssq[c & 1][wave][16 * rt + c16] = ss;
+            }
+        }
+        GDN_WAIT_VMCNT(0);
+        lds_barrier();   // the next slot is in, and this slot and the sums may be reused
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, ring0, ring1);
+        if (c + 1 < nchunks) step(c + 1, ring1, ring0);
+    }
+    if (nchunks > 0) {
+        if constexpr (kGate) {
+            epilogue(nchunks - 1);
+            if (a.y) store_y(nchunks - 1);
+        } else {
+            store_y(nchunks - 1);
+        }
+    }
+    if (a.ST) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.ST[sbase + (size_t)relabel(t, 4 * g + i) * DV + j0w + c16] = S[t][i];
+    }
+}
+
 }  // namespace
 
 size_t chunk_bf16_workspace(int ntok, int num_seqs, int H) {
     return ws_layout(ntok, num_seqs, H).total;
 }
 
-template <int HPW, typename Tin>
-static void launch_front(const DevArgs& a, const FrontArgs& f, int nchunks, int dv, hipStream_t s) {
-    const dim3 grid(nchunks, a.H / HPW);
-    if (dv == 128)
-        hipLaunchKernelGGL((chunk_front_kernel<HPW, 128, Tin>), grid, dim3(HPW * kWave), 0, s, a, f);
-    else
-        hipLaunchKernelGGL((chunk_front_kernel<HPW, 64, Tin>), grid, dim3(HPW * kWave), 0, s, a, f);
+// The full-row scan needs a (sequence, head) per CU to pay: below that the sliced scan's four
+// workgroups per pair spread one pair's columns over four CUs, which is faster when CUs are
+// left over.
+constexpr int kWideMinPairs = 256;
+bool use_wide_scan(int pairs, int dv) { return dv == 128 && pairs >= kWideMinPairs; }
+
+template <typename Ty, bool kGate, typename Tz, typename To>
+static void launch_wide(const DevArgs& a, const GateDev& gd, int pairs, hipStream_t s) {
+    hipLaunchKernelGGL((chunk_scan_wide_kernel<Ty, kGate, Tz, To>), dim3(pairs), dim3(kWideThreads), 0,
+                       s, a, gd);
 }
 
-template <typename Tin>
-static void launch_front_h(const DevArgs& a, const FrontArgs& f, int nchunks, int dv, hipStream_t s) {
-    if (a.H % 4 == 0) launch_front<4, Tin>(a, f, nchunks, dv, s);
-    else if (a.H % 2 == 0) launch_front<2, Tin>(a, f, nchunks, dv, s);
-    else launch_front<1, Tin>(a, f, nchunks, dv, s);
-}
-
-hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const FrontArgs* front) {
+hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* gate) {
     const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
     char* ws = static_cast<char*>(c.workspace);
     DevArgs a;
@@ -1016,19 +1242,39 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const FrontArgs*
     a.y_bf16 = c.y_bf16;
     if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
-    if (nchunks > 0 && front && front->in_bf16)
-        launch_front_h<uint16_t>(a, *front, nchunks, c.dv, s);
-    else if (nchunks > 0 && front)
-        launch_front_h<float>(a, *front, nchunks, c.dv, s);
-    else if (nchunks > 0)
+    if (nchunks > 0)
         hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
-    const int nsl = c.dv / kSl;
     const int pairs = c.num_seqs * c.H;
+    if (use_wide_scan(pairs, c.dv)) {
+        GateDev gd{};
+        if (gate) {
+            gd.z = gate->z; gd.w = gate->w; gd.o = gate->o; gd.eps = gate->eps;
+            a.y = gate->y_export;   // nullable: y is not stored unless exported
+            const int key = (gate->z_bf16 << 1) | gate->o_bf16;
+            switch (key) {
+                case 0: launch_wide<uint16_t, true, float, float>(a, gd, pairs, s); break;
+                case 1: launch_wide<uint16_t, true, float, uint16_t>(a, gd, pairs, s); break;
+                case 2: launch_wide<uint16_t, true, uint16_t, float>(a, gd, pairs, s); break;
+                default: launch_wide<uint16_t, true, uint16_t, uint16_t>(a, gd, pairs, s); break;
+            }
+            return hipGetLastError();
+        }
+        if (c.y_bf16) launch_wide<uint16_t, false, uint16_t, uint16_t>(a, gd, pairs, s);
+        else launch_wide<float, false, uint16_t, uint16_t>(a, gd, pairs, s);
+        return hipGetLastError();
+    }
+    const int nsl = c.dv / kSl;
     const int blocks = (pairs + 7) / 8 * 8 * nsl;
     if (c.y_bf16)
         hipLaunchKernelGGL(chunk_scan_kernel<uint16_t>, dim3(blocks), dim3(kScanThreads), 0, s, a);
     else
         hipLaunchKernelGGL(chunk_scan_kernel<float>, dim3(blocks), dim3(kScanThreads), 0, s, a);
+    if (gate) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_output_gate(c.y, c.y_bf16, gate->z, gate->z_bf16, gate->w, c.ntok, c.H, c.dv,
+                                  gate->eps, gate->o, gate->o_bf16, s);
+    }
     return hipGetLastError();
 }
 

@@ -429,7 +429,7 @@ size_t gdn_fused_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, i
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t rows = (size_t)ntok * H;
     return up(gdn::chunk_bf16_workspace(ntok, num_seqs, H)) + 2 * up(rows * dk * 2) +
-           2 * up(rows * dv * 2);
+           2 * up(rows * dv * 2) + 2 * up(rows * sizeof(float));
 }
 
 int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,
@@ -467,14 +467,16 @@ int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtyp
                 "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
     GDN_OPT_PTR(workspace);
 
-    // workspace: [prefill tiles | q | k | v | y]; exported intermediates replace their slot
+    // workspace: [prefill tiles | q | k | v | y | g | beta]; exported intermediates replace
+    // their slot
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t rows = (size_t)ntok * H;
     char* ws = static_cast<char*>(workspace);
     size_t off = up(gdn::chunk_bf16_workspace(ntok, num_seqs, H));
-    void* slot[4];
-    const size_t bytes[4] = {rows * dk * 2, rows * dk * 2, rows * dv * 2, rows * dv * 2};
-    for (int i = 0; i < 4; ++i) {
+    void* slot[6];
+    const size_t bytes[6] = {rows * dk * 2, rows * dk * 2, rows * dv * 2, rows * dv * 2,
+                             rows * sizeof(float), rows * sizeof(float)};
+    for (int i = 0; i < 6; ++i) {
         slot[i] = ws + off;
         off += up(bytes[i]);
     }
@@ -482,32 +484,44 @@ int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtyp
     void* kb = k ? k : slot[1];
     void* vb = v ? v : slot[2];
     void* yb = y ? y : slot[3];
+    float* gb = g ? g : static_cast<float*>(slot[4]);
+    float* bb = beta ? beta : static_cast<float*>(slot[5]);
+    hipStream_t s = static_cast<hipStream_t>(stream);
 
-    gdn::FrontArgs f;
-    f.x[0] = xq; f.x[1] = xk; f.x[2] = xv;
-    f.in_bf16 = x_dtype == GDN_BF16;
-    f.w[0] = wq; f.w[1] = wk; f.w[2] = wv;
-    f.out[0] = static_cast<uint16_t*>(qb);
-    f.out[1] = static_cast<uint16_t*>(kb);
-    f.out[2] = static_cast<uint16_t*>(vb);
-    f.a_raw = a_raw; f.b_raw = b_raw; f.A_log = A_log; f.dt_bias = dt_bias;
-    f.g_out = g; f.beta_out = beta;
-    f.l2_eps = l2_eps;
+    // eqs. (6)-(10): the preprocess kernel (bf16 q, k, v), exactly as gdn_preprocess
+    gdn::PreprocessArgs p;
+    p.x[0] = xq; p.x[1] = xk; p.x[2] = xv;
+    p.w[0] = wq; p.w[1] = wk; p.w[2] = wv;
+    p.out[0] = qb; p.out[1] = kb; p.out[2] = vb;
+    p.d[0] = dk; p.d[1] = dk; p.d[2] = dv;
+    p.in_bf16 = x_dtype == GDN_BF16;
+    p.out_bf16 = 1;
+    p.a_raw = a_raw; p.b_raw = b_raw; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.g = gb; p.beta = bb;
+    p.cu = cu_seqlens;
+    p.num_seqs = num_seqs; p.ntok = ntok; p.H = H; p.l2_eps = l2_eps;
+    p.hin = nullptr; p.hout = nullptr; p.hC = 0;
+    if (ntok > 0) {
+        const hipError_t e = gdn::launch_preprocess(p, s);
+        if (e != hipSuccess) return hip_status(e, "gdn_fused_prefill");
+    }
 
+    // eqs. (1)-(5) and eq. (11): the chunked prefill with the gate applied to its y (inside
+    // the scan when the full-row scan runs)
     gdn::ChunkArgs a;
     a.q = qb; a.k = kb; a.v = vb;
     a.in_bf16 = 1;
     a.y_bf16 = 1;
-    a.g = nullptr; a.beta = nullptr; a.S0 = initial_state; a.ST = final_state;
+    a.g = gb; a.beta = bb; a.S0 = initial_state; a.ST = final_state;
     a.cu = cu_seqlens;
     a.num_seqs = num_seqs; a.ntok = ntok; a.H = H; a.dk = dk; a.dv = dv;
     a.y = yb; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = gdn::launch_chunk_bf16(a, s, &f);
-    if (e != hipSuccess) return hip_status(e, "gdn_fused_prefill");
-    return hip_status(gdn::launch_output_gate(yb, 1, z, z_dtype == GDN_BF16, norm_weight, ntok, H,
-                                              dv, rms_eps, o, o_dtype == GDN_BF16, s),
-                      "gdn_fused_prefill");
+    gdn::GateArgs ga;
+    ga.z = z; ga.z_bf16 = z_dtype == GDN_BF16;
+    ga.w = norm_weight; ga.eps = rms_eps;
+    ga.o = o; ga.o_bf16 = o_dtype == GDN_BF16;
+    ga.y_export = y;
+    return hip_status(gdn::launch_chunk_bf16(a, s, &ga), "gdn_fused_prefill");
 }
 
 int gdn_fused_decode(const void* xq, const void* xk, const void* xv, int x_dtype, const float* wq,

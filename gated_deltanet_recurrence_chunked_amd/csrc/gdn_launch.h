@@ -87,18 +87,19 @@ hipError_t launch_mb_mfma(float* sink, int workgroups, int iters, hipStream_t s)
 
 // bf16 matrix-core chunked path (dk = 128): per-chunk T/P kernel + sequential scan kernel
 size_t chunk_bf16_workspace(int ntok, int num_seqs, int H);
-// The fused front end: q, k, v (bf16, written to out[]) and the gates computed from the
-// projected streams inside the per-chunk T/P kernel (zero conv history at sequence starts).
-struct FrontArgs {
-    const void* x[3];          // xq, xk, xv [ntok, H, d]
-    int in_bf16;               // x dtype
-    const float* w[3];         // conv taps [H*d, 4]
-    uint16_t* out[3];          // q, k, v [ntok, H, d] bf16 (the ChunkArgs q, k, v)
-    const float *a_raw, *b_raw, *A_log, *dt_bias;
-    float *g_out, *beta_out;   // nullable (both or neither)
-    float l2_eps;
+// The gated output of eq. (11) applied to the prefill's y (the fused prefill): inside the scan
+// when the full-row scan runs, else by the output-gate kernel after it (reading ChunkArgs::y).
+struct GateArgs {
+    const void* z;        // [ntok, H, dv]
+    int z_bf16;
+    const float* w;       // [dv]
+    float eps;
+    void* o;              // [ntok, H, dv]
+    int o_bf16;
+    void* y_export;       // nullable: y (bf16) is also stored here when the scan applies the gate
 };
-hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s, const FrontArgs* front = nullptr);
+bool use_wide_scan(int pairs, int dv);
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s, const GateArgs* gate = nullptr);
 
 // backward of the chunked gated delta rule (fp32 vector ALU)
 struct ChunkBwdArgs {
