@@ -361,21 +361,33 @@ def main():
         gen = torch.Generator(device=dev).manual_seed(1)
         gk = -torch.clamp(torch.exp(torch.randn((ntok, H, dk), generator=gen, device=dev) - 2.0),
                           max=5.0)
-        ws_k = torch.empty(int(gdn.lib().gdn_kda_chunk_prefill_workspace_size(ntok, nseq, H, dk)),
+        ws_k = torch.empty(int(gdn.lib().gdn_kda_chunk_prefill_bounded_workspace_size(ntok, nseq, H)),
+                           dtype=torch.uint8, device=dev)
+        ws_f = torch.empty(int(gdn.lib().gdn_kda_chunk_prefill_workspace_size(ntok, nseq, H, dk)),
                            dtype=torch.uint8, device=dev)
 
-        def kstep_(i):
+        def kstep_(i):   # log-decays in [-5, 0): the bf16 matrix-core path
+            gdn.gdn_kda_chunk_prefill_bounded(outs["q"], outs["k"], outs["v"], gk, outs["beta"],
+                                              num_seqs=nseq, y=y, workspace=ws_k,
+                                              output_final_state=False)
+
+        def fstep_(i):   # the same call on the fp32 path (any log-decay <= 0)
             gdn.gdn_kda_chunk_prefill(outs["q"], outs["k"], outs["v"], gk, outs["beta"],
-                                      num_seqs=nseq, y=y, workspace=ws_k, output_final_state=False)
+                                      num_seqs=nseq, y=y, workspace=ws_f, output_final_state=False)
         for i in range(3):
             kstep_(i)
+            fstep_(i)
         kms = tm.region(kstep_, 10)
-        kda = {"workload": "gdn_kda_chunk_prefill at B=4 H=16 T=4096 d=128 (bf16 q, k, v, y; "
-                           "per-channel fp32 log-decays in [-5, 0))",
+        fms_ = tm.region(fstep_, 5)
+        kda = {"workload": "gdn_kda_chunk_prefill_bounded at B=4 H=16 T=4096 d=128 (bf16 q, k, v, "
+                           "y; per-channel fp32 log-decays in [-5, 0))",
                "calls": 10, "us_per_call": round(kms * 1e3, 1),
                "Mtok_s": round(ntok / (kms * 1e-3) / 1e6, 2),
-               "vs_scalar_decay_prefill": round(kms / t_pf, 2)}
-        log(f"[bench] per-channel-decay prefill {kms * 1e3:.1f} us/call ({kda['Mtok_s']} Mtok/s)")
+               "vs_scalar_decay_prefill": round(kms / t_pf, 2),
+               "fp32_path_us_per_call": round(fms_ * 1e3, 1)}
+        log(f"[bench] per-channel-decay prefill {kms * 1e3:.1f} us/call ({kda['Mtok_s']} Mtok/s); "
+            f"fp32 path {fms_ * 1e3:.1f} us/call")
+        del ws_f
         del gk, ws_k
 
     del sets, outs, y, ws, base

@@ -101,6 +101,9 @@ def lib():
                                              _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                              ctypes.c_float, _i, _i, _i, _i, _i, _vp, _i, _vp,
                                              _vp, _vp]
+        L.gdn_kda_chunk_prefill_bounded_workspace_size.restype = ctypes.c_size_t
+        L.gdn_kda_chunk_prefill_bounded_workspace_size.argtypes = [_i, _i, _i]
+        L.gdn_kda_chunk_prefill_bounded.argtypes = L.gdn_kda_chunk_prefill.argtypes
         L.gdn_mb_stream.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
         L.gdn_mb_mfma_bf16.argtypes = [_vp, _i, _i, _vp]
         _lib = L
@@ -465,13 +468,8 @@ def gdn_chunk_backward(q, k, v, g, beta, dy, *, initial_state=None, dfinal_state
     return out
 
 
-def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
-                          cu_seqlens=None, cu_seqlens_host=None, num_seqs=1, y=None, y_dtype=None,
-                          workspace=None, output_final_state=True, stream=None):
-    """Per-channel-decay delta rule. q,k: [ntok,H,dk], v: [ntok,H,dv] (bf16/fp32);
-    g: [ntok,H,dk] fp32 log-decays; beta: [ntok,H] fp32; final_state: None (allocated when
-    output_final_state) or [num_seqs,H,dk,dv] fp32, which may be initial_state (updated in
-    place). Returns (y, final_state)."""
+def _kda(bounded, q, k, v, g, beta, initial_state, final_state, cu_seqlens, cu_seqlens_host,
+         num_seqs, y, y_dtype, workspace, output_final_state, stream):
     ntok, H, dk = q.shape
     dv = v.shape[-1]
     in_tag = _dtype_tag(q)
@@ -494,23 +492,48 @@ def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=N
         y = new((ntok, H, dv), yd)
     if final_state is None and output_final_state:
         final_state = new((num_seqs, H, dk, dv), torch.float32)
-    need = int(lib().gdn_kda_chunk_prefill_workspace_size(ntok, num_seqs, H, dk))
+    name = "gdn_kda_chunk_prefill_bounded" if bounded else "gdn_kda_chunk_prefill"
+    if bounded:
+        need = int(lib().gdn_kda_chunk_prefill_bounded_workspace_size(ntok, num_seqs, H))
+    else:
+        need = int(lib().gdn_kda_chunk_prefill_workspace_size(ntok, num_seqs, H, dk))
     if workspace is None:
         workspace = new(max(need, 1), torch.uint8)
     host_cu = None
     if cu_seqlens_host is not None:
         host_cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
     f32 = torch.float32
-    st = lib().gdn_kda_chunk_prefill(
+    st = getattr(lib(), name)(
         _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), in_tag, _ptr(g, "g", f32), _ptr(beta, "beta", f32),
         _ptr(initial_state, "initial_state", f32), _ptr(final_state, "final_state", f32),
         _ptr(cu_seqlens, "cu_seqlens", torch.int32),
         ctypes.cast(host_cu, _vp) if host_cu is not None else None, num_seqs, ntok, H, dk, dv,
         _ptr(y, "y", yd), y_tag, _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "gdn_kda_chunk_prefill")
+    _check(st, name)
     _keep(stream, *new.made)
     return y, final_state
+
+
+def gdn_kda_chunk_prefill(q, k, v, g, beta, *, initial_state=None, final_state=None,
+                          cu_seqlens=None, cu_seqlens_host=None, num_seqs=1, y=None, y_dtype=None,
+                          workspace=None, output_final_state=True, stream=None):
+    """Per-channel-decay delta rule. q,k: [ntok,H,dk], v: [ntok,H,dv] (bf16/fp32);
+    g: [ntok,H,dk] fp32 log-decays; beta: [ntok,H] fp32; final_state: None (allocated when
+    output_final_state) or [num_seqs,H,dk,dv] fp32, which may be initial_state (updated in
+    place). Returns (y, final_state)."""
+    return _kda(False, q, k, v, g, beta, initial_state, final_state, cu_seqlens, cu_seqlens_host,
+                num_seqs, y, y_dtype, workspace, output_final_state, stream)
+
+
+def gdn_kda_chunk_prefill_bounded(q, k, v, g, beta, *, initial_state=None, final_state=None,
+                                  cu_seqlens=None, cu_seqlens_host=None, num_seqs=1, y=None,
+                                  y_dtype=None, workspace=None, output_final_state=True,
+                                  stream=None):
+    """gdn_kda_chunk_prefill for log-decays -5 <= g <= 0 on the bf16 matrix cores: q, k, v bf16,
+    dk = dv = 128. Returns (y, final_state)."""
+    return _kda(True, q, k, v, g, beta, initial_state, final_state, cu_seqlens, cu_seqlens_host,
+                num_seqs, y, y_dtype, workspace, output_final_state, stream)
 
 
 def gdn_decode_step(q, k, v, g, beta, state, *, y=None, y_dtype=None, stream=None):
@@ -792,4 +815,4 @@ __all__ = ["GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_preprocess", "gdn_prep
            "gdn_chunk_backward_workspace_size", "gdn_kda_chunk_prefill", "gdn_decode_step",
            "gdn_decode_multi", "gdn_output_gate", "gdn_fused_prefill",
            "gdn_fused_prefill_workspace_size", "gdn_fused_decode", "gdn_fused_decode_multi",
-           "gdn_mb_stream", "gdn_mb_mfma_bf16"]
+           "gdn_mb_stream", "gdn_mb_mfma_bf16", "gdn_kda_chunk_prefill_bounded"]

@@ -86,6 +86,10 @@ struct DevArgs {
     int32_t* order;             // [num_seqs] longest first (varlen)
     uint16_t *Tw, *Pw;          // [max_chunks][H][64][64] bf16
     float* Gw;                  // [max_chunks][H][3][64]: beta, gamma = e^G, gamma_C / gamma
+                                // (per-channel decay: beta [64] | e^{Gc_C} [128])
+    uint16_t* Xw;               // per-channel decay only: [max_chunks][H][3][64][128] bf16
+                                // Kg = K o e^{Gc}, Kc = K o e^{Gc_C - Gc}, Qg = Q o e^{Gc}
+    const float* gk;            // per-channel decay only: log-decays [ntok][H][128]
     int num_seqs, ntok, H, dv, L;  // L: equal length (when cu == NULL)
     int y_bf16;
 };
@@ -844,6 +848,183 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ per-channel decay: prep
+// The per-channel-decay variant (the delta rule with Diag(alpha_t) over the key channels, as
+// in the Kimi Delta Attention entry the reading notes compare GDN with): row c of the state
+// decays by alpha_t[c] = e^{g_t[c]}. Inside a chunk, with Gc[r][c] the running sum of g over
+// the chunk's tokens,
+//   A[r,i] = beta_r sum_c k_r[c] k_i[c] e^{Gc[r][c]-Gc[i][c]} (i < r),  T = (I + A)^{-1}
+//   P[r,i] = sum_c q_r[c] k_i[c] e^{Gc[r][c]-Gc[i][c]}          (i <= r)
+//   U = T (beta o (V - Kg S)),  Y = Qg S + P U,  S' = e^{Gc[C]} o S + Kc^T U
+// with Kg = K o e^{Gc}, Qg = Q o e^{Gc}, Kc = K o e^{Gc[C] - Gc} (exponents <= 0).
+// This path takes the lower bound of that family's log-decay, g >= -5, to put A and P on the
+// bf16 matrix cores: for a 16-token row block a with first row m, e^{Gc_r - Gc_i} =
+// e^{Gc_r - Gc_m} e^{Gc_m - Gc_i}. The first factor lies in [e^-80, 1] (16 tokens of at most
+// 5 each); the second is <= 1 for i in earlier blocks and in [1, e^80] inside block a, so
+// every scaled operand stays far inside the bf16 / fp32 range and each 16x16 block of A and
+// P is one product of scaled K, Q rows over the 128 channels (v_mfma_f32_16x16x32_bf16).
+// One 256-thread workgroup per (chunk, head) writes Kg, Kc, Qg, T and P in bf16, and
+// beta | e^{Gc[C]} for the scan.
+constexpr int kKdaPrepThreads = 256;
+constexpr int kGsStr = kDK + 4;   // row stride (floats) of the running log-decays in LDS
+
+__global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_bf16_kernel(DevArgs a) {
+    __shared__ __attribute__((aligned(16))) float Gs[kC * kGsStr];
+    __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
+    __shared__ __attribute__((aligned(16))) uint16_t sP[kC * kC];
+    __shared__ float sB[kC];
+    const int chunk = blockIdx.x, h = blockIdx.y;
+    int seq, t0, n;
+    if (!chunk_of(a, chunk, seq, t0, n)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const size_t ch = (size_t)chunk * a.H + h;
+    const size_t rowH = (size_t)a.H * kDK;   // elements between consecutive tokens of q, k, g
+
+    // log-decays of the chunk's rows (rows >= n decay by nothing) and beta
+    for (int u = tid; u < kC * kDK / 4; u += kKdaPrepThreads) {
+        const int r = u / (kDK / 4), c4 = (u % (kDK / 4)) * 4;
+        f32x4p gv = {0.f, 0.f, 0.f, 0.f};
+        if (r < n) gv = *reinterpret_cast<const f32x4p*>(a.gk + (size_t)(t0 + r) * rowH + (size_t)h * kDK + c4);
+        *reinterpret_cast<f32x4p*>(&Gs[r * kGsStr + c4]) = gv;
+    }
+    if (tid < kC) sB[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * a.H + h] : 0.f;
+    for (int e = tid; e < kC * kStrA; e += kKdaPrepThreads) sA[e] = 0.f;
+    __syncthreads();
+    {   // running sums down the tokens: thread (half, channel) sums its 32 rows in registers,
+        // then the second half adds the first half's total
+        const int c = tid & (kDK - 1), r0 = (tid >> 7) * (kC / 2);
+        float v[kC / 2];
+#pragma unroll
+        for (int r = 0; r < kC / 2; ++r) v[r] = Gs[(r0 + r) * kGsStr + c];
+#pragma unroll
+        for (int r = 1; r < kC / 2; ++r) v[r] += v[r - 1];
+#pragma unroll
+        for (int r = 0; r < kC / 2; ++r) Gs[(r0 + r) * kGsStr + c] = v[r];
+        __syncthreads();
+        if (r0) {
+            const float base = Gs[(kC / 2 - 1) * kGsStr + c];
+#pragma unroll
+            for (int r = 0; r < kC / 2; ++r) Gs[(r0 + r) * kGsStr + c] = v[r] + base;
+        }
+    }
+    __syncthreads();
+
+    // Kg, Kc, Qg rows (8 channels, one 16-byte store each; rows >= n are zero)
+    auto row8 = [&](const uint16_t* x, int r, int c0) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (r < n) w = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * rowH + (size_t)h * kDK + c0);
+        return w;
+    };
+    auto bfv = [](const u32x4& w, int j) {
+        const uint32_t x = w[j >> 1];
+        return __uint_as_float((j & 1) ? (x & 0xffff0000u) : (x << 16));
+    };
+    uint16_t* xw = a.Xw + ch * 3 * kC * kDK;
+    constexpr int kUnits = kC * kDK / 8 / kKdaPrepThreads;   // 16-byte units per thread
+    u32x4 kws[kUnits], qws[kUnits];
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+        const int u = tid + j * kKdaPrepThreads, r = u / (kDK / 8), c0 = (u % (kDK / 8)) * 8;
+        kws[j] = row8(a.k, r, c0);
+        qws[j] = row8(a.q, r, c0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < kUnits; ++jj) {
+        const int u = tid + jj * kKdaPrepThreads;
+        const int r = u / (kDK / 8), c0 = (u % (kDK / 8)) * 8;
+        const u32x4 kw = kws[jj], qw = qws[jj];
+        float kg[8], kc[8], qg[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float G = Gs[r * kGsStr + c0 + j], GC = Gs[(kC - 1) * kGsStr + c0 + j];
+            const float e = fexp(G), ec = fexp(GC - G);
+            kg[j] = bfv(kw, j) * e;
+            qg[j] = bfv(qw, j) * e;
+            kc[j] = bfv(kw, j) * ec;
+        }
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf2(kg[2 * j], kg[2 * j + 1]);
+        *reinterpret_cast<u32x4*>(xw + r * kDK + c0) = o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf2(kc[2 * j], kc[2 * j + 1]);
+        *reinterpret_cast<u32x4*>(xw + kC * kDK + r * kDK + c0) = o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf2(qg[2 * j], qg[2 * j + 1]);
+        *reinterpret_cast<u32x4*>(xw + 2 * kC * kDK + r * kDK + c0) = o;
+    }
+    float* gw = a.Gw + ch * 3 * kC;   // beta | e^{Gc[C]}
+    if (tid < kC) gw[tid] = sB[tid];
+    else if (tid < kC + kDK) gw[tid] = fexp(Gs[(kC - 1) * kGsStr + tid - kC]);
+
+    // the ten lower 16x16 blocks (row block ra >= column block rb) of A and P; wave w takes
+    // blocks w, w + 4, w + 8 of the list (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+    for (int bi = wave; bi < 10; bi += kKdaPrepThreads / kWave) {
+        const int ra = bi < 1 ? 0 : (bi < 3 ? 1 : (bi < 6 ? 2 : 3));
+        const int rb = bi - ra * (ra + 1) / 2;
+        const int m = 16 * ra, rl = 16 * ra + c16, rr = 16 * rb + c16;
+        f32x4 cA = {0.f, 0.f, 0.f, 0.f}, cP = {0.f, 0.f, 0.f, 0.f};
+        u32x4 kls[kDK / 32], qls[kDK / 32], krs[kDK / 32];
+#pragma unroll
+        for (int s2 = 0; s2 < kDK / 32; ++s2) {
+            const int c0 = 32 * s2 + 8 * g;
+            kls[s2] = row8(a.k, rl, c0);
+            qls[s2] = row8(a.q, rl, c0);
+            krs[s2] = row8(a.k, rr, c0);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < kDK / 32; ++s2) {
+            const int c0 = 32 * s2 + 8 * g;
+            const u32x4 kl = kls[s2], ql = qls[s2], kr = krs[s2];
+            float lk[8], lq[8], rk[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float gm = Gs[m * kGsStr + c0 + j];
+                const float el = fexp(Gs[rl * kGsStr + c0 + j] - gm);
+                const float er = fexp(gm - Gs[rr * kGsStr + c0 + j]);
+                lk[j] = bfv(kl, j) * el;
+                lq[j] = bfv(ql, j) * el;
+                rk[j] = bfv(kr, j) * er;
+            }
+            u32x4 wl, wq, wr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                wl[j] = pack_bf2(lk[2 * j], lk[2 * j + 1]);
+                wq[j] = pack_bf2(lq[2 * j], lq[2 * j + 1]);
+                wr[j] = pack_bf2(rk[2 * j], rk[2 * j + 1]);
+            }
+            const bf16x8 fr = __builtin_bit_cast(bf16x8, wr);
+            cA = mfma16(__builtin_bit_cast(bf16x8, wl), fr, cA);
+            cP = mfma16(__builtin_bit_cast(bf16x8, wq), fr, cP);
+        }
+        // accumulator element i: row 16 ra + 4g + i, column 16 rb + c16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ra + 4 * g + i, c = 16 * rb + c16;
+            sA[r * kStrA + c] = c < r ? sB[r] * cA[i] : 0.f;
+            sP[r * kC + c] = c <= r ? uint16_t(pack_bf2(cP[i], 0.f) & 0xffffu) : uint16_t(0);
+        }
+    }
+    // the blocks above the diagonal of P are zero
+    for (int e = tid; e < kC * kC; e += kKdaPrepThreads) {
+        const int r = e / kC, c = e % kC;
+        if ((c >> 4) > (r >> 4)) sP[e] = 0;
+    }
+    __syncthreads();
+    if (wave == 0) unit_lower_inverse64<kStrA, true>(sA);
+    __syncthreads();
+    const size_t tile = ch * kC * kC;
+    for (int u = tid; u < kC * kC / 8; u += kKdaPrepThreads) {   // T and P, 8 elements per store
+        const int r = u / (kC / 8), c0 = (u % (kC / 8)) * 8;
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf2(sA[r * kStrA + c0 + 2 * j], sA[r * kStrA + c0 + 2 * j + 1]);
+        *reinterpret_cast<u32x4*>(a.Tw + tile + r * kC + c0) = o;
+        *reinterpret_cast<u32x4*>(a.Pw + tile + r * kC + c0) = *reinterpret_cast<const u32x4*>(&sP[r * kC + c0]);
+    }
+}
+
 // ------------------------------------------------------------------ full-row scan
 // One workgroup per (sequence, head) holding all 128 d_v columns: 8 waves, wave w runs the
 // chain above for columns 16w .. 16w + 15 and also forms their output, Y = gamma Q S + P U
@@ -857,7 +1038,6 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
 // about 3.5 times the chunk-columns per unit time of the sliced scan, but holds one (sequence,
 // head), so the launcher takes this kernel when the pairs fill the chip.
 constexpr int kWideWaves = 8;
-constexpr int kWideThreads = kWideWaves * kWave;
 constexpr int kWOffK = 0;                    // [64][128] bf16, 16-byte units swizzled per row
 constexpr int kWOffV = kWOffK + kC * kDK;    // [64][128], the same
 constexpr int kWOffQ = kWOffV + kC * kDK;    // [64][128], the same
@@ -873,8 +1053,19 @@ struct GateDev {
     float eps;
 };
 
-template <typename Ty, bool kGate, typename Tz, typename To>
-__global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a, GateDev gd_) {
+// kKda: the per-channel-decay variant (see kda_prep_bf16_kernel). The ring slots then hold Kg
+// (for K S), Kc (for the update, in V's place) and Qg, the gate rows are beta | e^{Gc[C]},
+// V comes from global memory into registers (the end-of-step wait covers it), the state decays
+// per row, and there are no scalar gamma factors.
+// kWv: waves per workgroup (16 columns each). 8 gives the full row (the only form that can
+// apply the gate); 4 or 2 split a (sequence, head) over 2 or 4 workgroups that each load the
+// chunk's whole tiles (the same bytes from HBM, shared in L2: a pair's workgroups are 8 apart
+// in the grid, so on one XCD), for calls with too few pairs to fill the chip.
+template <typename Ty, bool kGate, typename Tz, typename To, bool kKda, int kWv>
+__global__ void __launch_bounds__(kWv * kWave) chunk_scan_wide_kernel(DevArgs a, GateDev gd_) {
+    static_assert(kWv == 8 || kWv == 4 || kWv == 2, "waves per workgroup");
+    static_assert(!kGate || kWv == 8, "the gate needs every column of a row");
+    constexpr int kNsl = kWideWaves / kWv;   // workgroups per (sequence, head)
     // The two slots are separate arrays and each half of the 2-unrolled chunk loop names its
     // slots statically: the compiler then sees that the direct loads into one slot cannot alias
     // the reads of the other, and inserts no wait for the loads in flight before those reads
@@ -883,7 +1074,11 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
     __shared__ __attribute__((aligned(16))) uint16_t ring1[kWSlot];
     __shared__ float ssq[kGate ? 2 : 1][kWideWaves][kC];   // per-wave sums of y^2 per token
 
-    const int pair = blockIdx.x;
+    // block -> (pair, slice): the slices of one pair are 8 blocks apart
+    const int b = blockIdx.x;
+    const int group = b / (8 * kNsl), within = b % (8 * kNsl);
+    const int slice = within >> 3;
+    const int pair = group * 8 + (within & 7);
     if (pair >= a.num_seqs * a.H) return;
     const int rank = pair / a.H, h = pair % a.H;
     const int seq = a.order ? a.order[rank] : rank;
@@ -901,28 +1096,38 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c16 = lane & 15, g = lane >> 4;
-    const int j0w = 16 * wave;
+    const int j0w = slice * kWv * 16 + 16 * wave;
     constexpr int DV = 128;
 
     // ---- this wave's share of a chunk's tiles, loaded straight into `slot`
     auto load_chunk = [&](int ck, uint16_t* slot) __attribute__((always_inline)) {
         const int t0 = lo + ck * kC, n = min(kC, hi - t0);
         const size_t ch = (size_t)(cbase + ck) * a.H + h;
-        // [64][128] rows of K, V and Q: 16 one-kilobyte pieces each, two per wave
+        // [64][128] rows of K, V and Q (Kg, Kc and Qg): 16 one-kilobyte pieces each, 16 / kWv
+        // per wave
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int i = 2 * wave + j;
+        for (int j = 0; j < 16 / kWv; ++j) {
+            const int i = (16 / kWv) * wave + j;
             const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
-            const size_t src = ((size_t)(t0 + min(row, n - 1)) * a.H + h) * kDK + u * 8;
-            dma16(a.k + src, slot + kWOffK + i * 512);
-            dma16(a.v + src, slot + kWOffV + i * 512);
-            dma16(a.q + src, slot + kWOffQ + i * 512);
+            if constexpr (kKda) {
+                const uint16_t* xs = a.Xw + ch * 3 * kC * kDK + row * kDK + u * 8;
+                dma16(xs, slot + kWOffK + i * 512);
+                dma16(xs + kC * kDK, slot + kWOffV + i * 512);
+                dma16(xs + 2 * kC * kDK, slot + kWOffQ + i * 512);
+            } else {
+                const size_t src = ((size_t)(t0 + min(row, n - 1)) * a.H + h) * kDK + u * 8;
+                dma16(a.k + src, slot + kWOffK + i * 512);
+                dma16(a.v + src, slot + kWOffV + i * 512);
+                dma16(a.q + src, slot + kWOffQ + i * 512);
+            }
         }
-        // [64][64] T and P: 8 pieces each, one per wave
-        {
-            const int row = 8 * wave + (lane >> 3), u = (lane & 7) ^ swz(row);
-            dma16(a.Tw + ch * kC * kC + row * kC + u * 8, slot + kWOffT + wave * 512);
-            dma16(a.Pw + ch * kC * kC + row * kC + u * 8, slot + kWOffP + wave * 512);
+        // [64][64] T and P: 8 pieces each, 8 / kWv per wave
+#pragma unroll
+        for (int j = 0; j < 8 / kWv; ++j) {
+            const int i = (8 / kWv) * wave + j;
+            const int row = 8 * i + (lane >> 3), u = (lane & 7) ^ swz(row);
+            dma16(a.Tw + ch * kC * kC + row * kC + u * 8, slot + kWOffT + i * 512);
+            dma16(a.Pw + ch * kC * kC + row * kC + u * 8, slot + kWOffP + i * 512);
         }
         if (wave == 0) dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kWOffG);
     };
@@ -956,8 +1161,9 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         const int tok = 8 * g + jj + 4 * hf;
+        constexpr int kOffKT = kKda ? kWOffV : kWOffK;   // K^T of the update (Kc^T)
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) okt[hf][tp] = kWOffK + tok * kDK + (((4 * tp + r4) ^ swz(tok)) << 3);
+        for (int tp = 0; tp < 2; ++tp) okt[hf][tp] = kOffKT + tok * kDK + (((4 * tp + r4) ^ swz(tok)) << 3);
         // V^T at the lane's relabelled tokens: 4 consecutive tokens of column j0w + c16
         ovf[hf] = kWOffV + tok * kDK + (((2 * wave + (r4 >> 1)) ^ swz(tok)) << 3) + 4 * (r4 & 1);
     }
@@ -1041,7 +1247,22 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
         }
     };
 
+    // per-channel decay: V at the lane's relabelled tokens, column j0w + c16, from global
+    // memory one chunk ahead (ragged rows repeat the last row; their beta is zero)
+    uint16_t vcur[16], vnext[16];
+    auto fetch_v = [&](int ck) __attribute__((always_inline)) {
+        const int t0 = lo + ck * kC, n = min(kC, hi - t0);
+        const uint16_t* vb = a.v + (size_t)h * DV + j0w + c16;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vnext[4 * rt + i] = vb[(size_t)(t0 + min(relabel(rt, 4 * g + i), n - 1)) * a.H * DV];
+    };
     if (nchunks > 0) load_chunk(0, ring0);
+    if constexpr (kKda) {
+        if (nchunks > 0) fetch_v(0);
+    }
     GDN_WAIT_VMCNT(0);
     lds_barrier();
     // Chunk c's results leave at the start of step c + 1, before that step's loads: the wait
@@ -1057,6 +1278,11 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
             }
         }
         if (c + 1 < nchunks) load_chunk(c + 1, next);
+        if constexpr (kKda) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vcur[i] = vnext[i];
+            if (c + 1 < nchunks) fetch_v(c + 1);
+        }
         if constexpr (kGate) load_z(c);
         const float* sG = reinterpret_cast<const float*>(slot + kWOffG);   // beta | gamma | gamma_C/gamma
         auto kfrag = [&](int rt, int s) {
@@ -1069,7 +1295,7 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
         auto grow = [&](int which, int rt) {
             return *reinterpret_cast<const f32x4*>(sG + which * kC + 8 * g + 32 * (rt >> 1) + 4 * (rt & 1));
         };
-        const float gC = sG[kC + kC - 1];
+        const float gC = kKda ? 1.f : sG[kC + kC - 1];
 
         // ---- K S and Q S (both against the state at the chunk start)
         f32x4 KS[4];
@@ -1095,10 +1321,16 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
         f32x4 R[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const f32x4 bet = grow(0, rt), gam = grow(1, rt);
-            const s16x4 vv = lds_tr16(slot + ovf[rt & 1] + (rt >> 1) * 32 * kDK);
+            const f32x4 bet = grow(0, rt);
+            if constexpr (kKda) {   // R = beta (V - Kg S)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R[rt][i] = bet[i] * (bf2f(uint16_t(vv[i])) - gam[i] * KS[rt][i]);
+                for (int i = 0; i < 4; ++i) R[rt][i] = bet[i] * (bf2f(vcur[4 * rt + i]) - KS[rt][i]);
+            } else {
+                const f32x4 gam = grow(1, rt);
+                const s16x4 vv = lds_tr16(slot + ovf[rt & 1] + (rt >> 1) * 32 * kDK);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) R[rt][i] = bet[i] * (bf2f(uint16_t(vv[i])) - gam[i] * KS[rt][i]);
+            }
         }
         bf16x8 Rh[2], Rl[2];
         split8(R[0], R[1], Rh[0], Rl[0]);
@@ -1130,9 +1362,10 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
             bf16x8 Uh[2], Ul[2];
             split8(U[0], U[1], Uh[0], Ul[0]);
             split8(U[2], U[3], Uh[1], Ul[1]);
-            const float* sGq = sG;
+            if constexpr (!kKda) {   // gamma (S^T Q^T); Qg carries the decay already
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) YT[rt] *= sGq[kC + 16 * rt + c16];
+                for (int rt = 0; rt < 4; ++rt) YT[rt] *= sG[kC + 16 * rt + c16];
+            }
             bf16x8 pf[4][2];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
@@ -1151,13 +1384,18 @@ __global__ void __launch_bounds__(kWideThreads) chunk_scan_wide_kernel(DevArgs a
         GDN_SCHED_FENCE();
         // ---- W = diag(gamma_C / gamma) U, split; S = gamma_C S + K^T W
         bf16x8 Wh[2], Wl[2];
+        if constexpr (!kKda) {   // Kc carries the per-channel decay to the chunk end
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) U[rt] *= grow(2, rt);
+            for (int rt = 0; rt < 4; ++rt) U[rt] *= grow(2, rt);
+        }
         split8(U[0], U[1], Wh[0], Wl[0]);
         split8(U[2], U[3], Wh[1], Wl[1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            S[t] *= gC;
+            if constexpr (kKda)   // e^{Gc[C]} at the tile's d_k rows relabel(t, 4g + i)
+                S[t] *= *reinterpret_cast<const f32x4*>(sG + kC + 32 * (t >> 1) + 8 * g + 4 * (t & 1));
+            else
+                S[t] *= gC;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const u32x2 p0 = __builtin_bit_cast(u32x2, ktr(t, s2, 0));
@@ -1217,14 +1455,14 @@ size_t chunk_bf16_workspace(int ntok, int num_seqs, int H) {
 constexpr int kWideMinPairs = 256;
 bool use_wide_scan(int pairs, int dv) { return dv == 128 && pairs >= kWideMinPairs; }
 
-template <typename Ty, bool kGate, typename Tz, typename To>
+template <typename Ty, bool kGate, typename Tz, typename To, bool kKda = false, int kWv = 8>
 static void launch_wide(const DevArgs& a, const GateDev& gd, int pairs, hipStream_t s) {
-    hipLaunchKernelGGL((chunk_scan_wide_kernel<Ty, kGate, Tz, To>), dim3(pairs), dim3(kWideThreads), 0,
-                       s, a, gd);
+    const int nsl = kWideWaves / kWv;
+    hipLaunchKernelGGL((chunk_scan_wide_kernel<Ty, kGate, Tz, To, kKda, kWv>),
+                       dim3((pairs + 7) / 8 * 8 * nsl), dim3(kWv * kWave), 0, s, a, gd);
 }
 
-hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* gate) {
-    const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
+static DevArgs dev_args(const ChunkArgs& c, const Layout& L) {
     char* ws = static_cast<char*>(c.workspace);
     DevArgs a;
     a.q = static_cast<const uint16_t*>(c.q);
@@ -1237,9 +1475,17 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
     a.Tw = reinterpret_cast<uint16_t*>(ws + L.T);
     a.Pw = reinterpret_cast<uint16_t*>(ws + L.P);
     a.Gw = reinterpret_cast<float*>(ws + L.Gt);
+    a.Xw = nullptr;
+    a.gk = nullptr;
     a.num_seqs = c.num_seqs; a.ntok = c.ntok; a.H = c.H; a.dv = c.dv;
     a.L = c.cu ? 0 : c.ntok / c.num_seqs;
     a.y_bf16 = c.y_bf16;
+    return a;
+}
+
+hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* gate) {
+    const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
+    DevArgs a = dev_args(c, L);
     if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
     if (nchunks > 0)
@@ -1275,6 +1521,37 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
         return launch_output_gate(c.y, c.y_bf16, gate->z, gate->z_bf16, gate->w, c.ntok, c.H, c.dv,
                                   gate->eps, gate->o, gate->o_bf16, s);
     }
+    return hipGetLastError();
+}
+
+// the per-channel-decay path with log-decays >= -5 (bf16 q, k, v; dk = dv = 128): the
+// chunked prefill's tiles plus the Kg, Kc, Qg operand tiles
+size_t kda_bf16_workspace(int ntok, int num_seqs, int H) {
+    const Layout L = ws_layout(ntok, num_seqs, H);
+    return L.total + align256((size_t)L.max_chunks * H * 3 * kC * kDK * sizeof(uint16_t));
+}
+
+hipError_t launch_kda_bf16(const ChunkArgs& c, const float* gk, hipStream_t s) {
+    const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
+    DevArgs a = dev_args(c, L);
+    a.Xw = reinterpret_cast<uint16_t*>(static_cast<char*>(c.workspace) + L.total);
+    a.gk = gk;
+    if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
+    if (nchunks > 0)
+        hipLaunchKernelGGL(kda_prep_bf16_kernel, dim3(nchunks, c.H), dim3(kKdaPrepThreads), 0, s, a);
+    const int pairs = c.num_seqs * c.H;
+    const GateDev gd{};
+    // enough workgroups to cover the chip: the full row when the pairs alone do, else a pair
+    // split over 2 or 4 workgroups
+    auto go = [&](auto ty) {
+        using Ty = decltype(ty);
+        if (pairs >= kWideMinPairs) launch_wide<Ty, false, uint16_t, uint16_t, true, 8>(a, gd, pairs, s);
+        else if (2 * pairs >= kWideMinPairs) launch_wide<Ty, false, uint16_t, uint16_t, true, 4>(a, gd, pairs, s);
+        else launch_wide<Ty, false, uint16_t, uint16_t, true, 2>(a, gd, pairs, s);
+    };
+    if (c.y_bf16) go(uint16_t{});
+    else go(float{});
     return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ struct GateArgs {
     void* y_export;       // nullable: y (bf16) is also stored here when the scan applies the gate
 };
 bool use_wide_scan(int pairs, int dv);
+// per-channel-decay prefill with log-decays >= -5 on the bf16 matrix cores (dk = dv = 128);
+// gk: log-decays [ntok, H, 128]; ChunkArgs::g unused
+size_t kda_bf16_workspace(int ntok, int num_seqs, int H);
+hipError_t launch_kda_bf16(const ChunkArgs& a, const float* gk, hipStream_t s);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s, const GateArgs* gate = nullptr);
 
 // backward of the chunked gated delta rule (fp32 vector ALU)

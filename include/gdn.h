@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
     GDN_OK = 0,
@@ -234,6 +234,29 @@ int gdn_kda_chunk_prefill(const void* q, const void* k, const void* v, int in_dt
                           const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H, int dk,
                           int dv, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Bytes of device workspace gdn_kda_chunk_prefill_bounded needs for these sizes. */
+size_t gdn_kda_chunk_prefill_bounded_workspace_size(int ntok, int num_seqs, int H);
+
+/*
+ * gdn_kda_chunk_prefill_bounded - the per-channel-decay prefill of gdn_kda_chunk_prefill for
+ * log-decays bounded below by -5 (the lower bound of the Kimi Delta Attention gate named
+ * in the reading notes' related-work comparison, section "与已归档相关工作的对比"), on the
+ * bf16 matrix cores: within 16 tokens the decay spans at most e^80, so the per-channel
+ * decays fold into bf16 operands of dense products. fp32 accumulation and an fp32 state.
+ *
+ *   Arguments as gdn_kda_chunk_prefill, with in_dtype GDN_BF16, dk = dv = 128, and
+ *   g: [ntok, H, 128] fp32 log-decays with -5 <= g <= 0, 16-byte aligned. Entries below -5
+ *   are outside this path (a 16-token block could then overflow the scaled operands): use
+ *   gdn_kda_chunk_prefill for them.
+ *   workspace: at least gdn_kda_chunk_prefill_bounded_workspace_size(...) bytes.
+ */
+int gdn_kda_chunk_prefill_bounded(const void* q, const void* k, const void* v, int in_dtype,
+                                  const float* g, const float* beta, const float* initial_state,
+                                  float* final_state, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int num_seqs, int ntok, int H,
+                                  int dk, int dv, void* y, int y_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * gdn_decode_step - one token per sequence through eqs. (1)-(4), state updated in place:

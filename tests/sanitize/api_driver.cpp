@@ -98,6 +98,20 @@ int main() {
     EXPECT(gdn_kda_chunk_prefill(P(1), P(2), P(3), BF, F(4), F(5), F(6), F(7), cud, cu.data(),
                                  nseq, ntok, H, dk, dv, P(8), BF, P(9), wk, nullptr), 0);
 
+    const size_t wkb = gdn_kda_chunk_prefill_bounded_workspace_size(ntok, nseq, H);
+    EXPECT(gdn_kda_chunk_prefill_bounded(P(1), P(2), P(3), BF, F(4), F(5), F(6), F(7), cud,
+                                         cu.data(), nseq, ntok, H, dk, dv, P(8), BF, P(9), wkb,
+                                         nullptr), 0);
+    EXPECT(gdn_kda_chunk_prefill_bounded(P(1), P(2), P(3), FP, F(4), F(5), F(6), F(7), cud,
+                                         cu.data(), nseq, ntok, H, dk, dv, P(8), BF, P(9), wkb,
+                                         nullptr), GDN_ERR_DTYPE);
+    EXPECT(gdn_kda_chunk_prefill_bounded(P(1), P(2), P(3), BF, F(4), F(5), F(6), F(7), cud,
+                                         cu.data(), nseq, ntok, H, 64, dv, P(8), BF, P(9), wkb,
+                                         nullptr), GDN_ERR_SHAPE);
+    EXPECT(gdn_kda_chunk_prefill_bounded(P(1), P(2), P(3), BF, static_cast<const float*>(MIS),
+                                         F(5), F(6), F(7), cud, cu.data(), nseq, ntok, H, dk, dv,
+                                         P(8), BF, P(9), wkb, nullptr), GDN_ERR_ALIGN);
+
     // decode
     EXPECT(gdn_decode_step(P(1), P(2), P(3), BF, F(4), F(5), F(6), N, H, dk, dv, P(7), BF,
                            nullptr), 0);

@@ -31,6 +31,7 @@ hipError_t launch_decode_multi(const void*, const void*, const void*, int, const
 hipError_t launch_chunk_fp32(const ChunkArgs&, hipStream_t) { return reached(); }
 hipError_t launch_chunk_bf16(const ChunkArgs&, hipStream_t, const GateArgs*) { return reached(); }
 hipError_t launch_chunk_bwd(const ChunkBwdArgs&, hipStream_t) { return reached(); }
+hipError_t launch_kda_bf16(const ChunkArgs&, const float*, hipStream_t) { return reached(); }
 hipError_t launch_chunk_kda(const ChunkKdaArgs&, hipStream_t) { return reached(); }
 hipError_t launch_mb_stream(const void*, void*, size_t, hipStream_t) { return reached(); }
 hipError_t launch_mb_mfma(float*, int, int, hipStream_t) { return reached(); }
@@ -46,6 +47,9 @@ size_t chunk_bf16_workspace(int ntok, int num_seqs, int H) {
 }
 size_t chunk_bwd_workspace(int ntok, int num_seqs, int H, int dk, int dv) {
     return ((size_t)ntok / 64 + num_seqs + 1) * H * ((size_t)dk * dv * 4 + 65536);
+}
+size_t kda_bf16_workspace(int ntok, int num_seqs, int H) {
+    return ((size_t)ntok / 64 + num_seqs + 1) * H * 66560;
 }
 size_t chunk_kda_workspace(int ntok, int num_seqs, int H, int dk) {
     return ((size_t)ntok / 64 + num_seqs + 1) * H * ((size_t)dk * 512 + 16384);

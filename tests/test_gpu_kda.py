@@ -22,7 +22,7 @@ def _f32(a):
     return C.dev(np.ascontiguousarray(a, dtype=np.float32))
 
 
-def _case(inp, g, bf16, y_dtype, seqs=None, heads=None):
+def _case(inp, g, bf16, y_dtype, seqs=None, heads=None, bounded=False):
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
     sh = inp["shape"]
@@ -33,7 +33,8 @@ def _case(inp, g, bf16, y_dtype, seqs=None, heads=None):
                                           _f32(inp["dt_bias"]), H=H)
     cu_d = None if sh.equal_lengths else C.dev(cu)
     S0 = inp.get("S0")
-    y, ST = gdn.gdn_kda_chunk_prefill(q, k, v, _f32(g), beta,
+    run = gdn.gdn_kda_chunk_prefill_bounded if bounded else gdn.gdn_kda_chunk_prefill
+    y, ST = run(q, k, v, _f32(g), beta,
                                       initial_state=None if S0 is None else _f32(S0),
                                       cu_seqlens=cu_d, cu_seqlens_host=None if cu_d is None else cu,
                                       num_seqs=sh.num_seqs, y_dtype=y_dtype)
@@ -46,9 +47,11 @@ def _case(inp, g, bf16, y_dtype, seqs=None, heads=None):
     y_ref, S_ref = oracle.kda_recurrence(sub["q"], sub["k"], sub["v"], al, be, sub.get("S0"),
                                          sub["cu"])
     y_bf16 = y_dtype == "bf16"
-    ey = C.assert_close("y", C.gpu_slice(y, sub["tok"], heads), y_ref, y_bf16,
+    # the bounded path computes on the bf16 matrix cores: the bf16 bar whatever y's dtype
+    ey = C.assert_close("y", C.gpu_slice(y, sub["tok"], heads), y_ref, y_bf16 or bounded,
                         stored_bf16=y_bf16, cu=sub["cu"], H=len(heads))
-    es = C.assert_close("S_T", C.gpu_state_slice(ST, seqs, heads), S_ref, False, state=True)
+    # the fp32 path holds S_T to the fp32 bar; the bf16 matrix-core path to the bf16 one
+    es = C.assert_close("S_T", C.gpu_state_slice(ST, seqs, heads), S_ref, bounded, state=True)
     print(f"  max slice rel L2: y {ey:.2e}, S_T {es:.2e}", flush=True)
 
 
@@ -113,3 +116,39 @@ def test_kda_many_sequences(gpu):
     inp["S0"] = gi.make_inputs(gi.LONG_CONTEXT, seed=13, B=len(L), H=2, T=1, d=64)["S0"]
     g = gi.kda_log_decay_draw(13, inp["shape"].ntok, 2, 64)
     _case(inp, g, False, "f32", seqs=C.sampled_seqs(L, 13))
+
+
+# ----------------------------------------------------------------------------- bounded decays
+# gdn_kda_chunk_prefill_bounded: log-decays in [-5, 0] on the bf16 matrix cores (bf16 q, k, v,
+# d = 128), held to the bf16 bar.
+BOUNDED = [
+    (gi.LONG_CONTEXT, dict(H=2, T=1000), "bf16"),                               # S0, bf16 y
+    (gi.LONG_CONTEXT, dict(B=2, H=3, T=200), "f32"),                            # ragged last chunk
+    (gi.LONG_CONTEXT, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130]), "bf16"),  # packed
+    (gi.LONG_CONTEXT, dict(B=64, H=4, T=130), "bf16"),                          # 256 pairs
+]
+
+
+@pytest.mark.parametrize("workload,ov,ydt", BOUNDED, ids=[f"{gi.TAGS[w]}-{o}-{y}" for w, o, y in BOUNDED])
+def test_kda_bounded(gpu, workload, ov, ydt):
+    _announce(f"kda bounded (bf16 matrix cores) {gi.TAGS[workload]} {ov} y={ydt}")
+    inp = gi.make_inputs(workload, seed=14, **ov)
+    g = gi.kda_log_decay_draw(14, inp["shape"].ntok, inp["shape"].H, 128)
+    assert g.min() >= -5.0
+    _case(inp, g, bf16=True, y_dtype=ydt, bounded=True)
+
+
+def test_kda_bounded_at_the_bound(gpu):
+    """Every log-decay at the bound (-5 per token, 80 over a 16-token block): the scaled
+    operands reach e^80 and e^-80 and stay finite; the result still meets the bf16 bar."""
+    _announce("kda bounded with every log-decay = -5, B=2 H=2 T=300")
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=15, B=2, H=2, T=300)
+    g = np.full((inp["shape"].ntok, 2, 128), -5.0, dtype=np.float32)
+    _case(inp, g, bf16=True, y_dtype="f32", bounded=True)
+
+
+def test_kda_bounded_b4_h16_t4096_sampled(gpu):
+    _announce("kda bounded at B=4 H=16 T=4096 d=128, sampled slices")
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=11, B=4, H=16, T=4096)
+    g = gi.kda_log_decay_draw(11, 4 * 4096, 16, 128)
+    _case(inp, g, bf16=True, y_dtype="bf16", seqs=[0, 3], heads=[0, 5, 15], bounded=True)
