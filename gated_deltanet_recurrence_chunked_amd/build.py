@@ -30,6 +30,7 @@ FLAGS = [
 # for every element that the fp32 -> bf16 hi/lo splits and the gate scalings touch.
 EXTRA = {
     "chunk_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "chunk_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

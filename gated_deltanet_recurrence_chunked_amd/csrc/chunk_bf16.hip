@@ -25,6 +25,7 @@
 #include "gdn_device.h"
 #include "gdn_inverse.h"
 #include "gdn_launch.h"
+#include "gdn_mfma.h"
 
 namespace gdn {
 
@@ -39,18 +40,6 @@ constexpr int kStrC = kC + 8;         // LDS row stride (elements) of [*, 64] bf
 constexpr int kStrA = kC + 4;         // LDS row stride of the fp32 A matrix
 constexpr int kMaxSorted = 1024;      // longest-first ordering up to this many sequences
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
-}
 
 // accumulator element i of lane l -> tile row
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
@@ -90,6 +79,8 @@ struct DevArgs {
     uint16_t* Xw;               // per-channel decay only: [max_chunks][H][3][64][128] bf16
                                 // Kg = K o e^{Gc}, Kc = K o e^{Gc_C - Gc}, Qg = Q o e^{Gc}
     const float* gk;            // per-channel decay only: log-decays [ntok][H][128]
+    uint16_t* Sst;              // states-only scan: bf16 state entering each chunk,
+                                // [max_chunks][H][d_v][d_k] (S^T, d_k contiguous)
     int num_seqs, ntok, H, dv, L;  // L: equal length (when cu == NULL)
     int y_bf16;
 };
@@ -369,86 +360,10 @@ constexpr int kQOffP = kQOffQ + kC * kDK;
 constexpr int kQOffG = kQOffP + kC * kC;      // 3 x 64 floats (+ 256 bytes of padding)
 constexpr int kQPSlot = kQOffG + 512;
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 16-byte unit swizzle of LDS row `row`: distinct for the 8 rows {0..7} and for {0-3, 8-11}
-// (+ any multiple of 4), and spreads the 4 consecutive rows of a transposing read.
-__device__ __forceinline__ int swz(int row) {
-    return (((row & 1) << 2) | ((row >> 1) & 3)) ^ (((row >> 3) & 1) << 1);
-}
-
-// tile row r of tile t (2s + a) of a relabelled dimension -> index 32s + 8(r/4) + 4a + r%4
-__device__ __forceinline__ int relabel(int t, int r) {
-    return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
-}
-
-__device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
-}
-
-// two fp32 accumulator quads -> bf16 hi and lo operand fragments (8 values each)
-__device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, bf16x8& hi, bf16x8& lo) {
-    u32x4 h, l;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float a0 = e < 2 ? x0[2 * e] : x1[2 * e - 4];
-        const float a1 = e < 2 ? x0[2 * e + 1] : x1[2 * e - 3];
-        const uint32_t hp = pack_bf2(a0, a1);
-        h[e] = hp;
-        l[e] = pack_bf2(a0 - __uint_as_float(hp << 16), a1 - __uint_as_float(hp & 0xffff0000u));
-    }
-    hi = __builtin_bit_cast(bf16x8, h);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
-
-// two fp32 accumulator quads -> one bf16 operand fragment (8 values)
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& x0, const f32x4& x1) {
-    const u32x4 h = {pack_bf2(x0[0], x0[1]), pack_bf2(x0[2], x0[3]), pack_bf2(x1[0], x1[1]),
-                     pack_bf2(x1[2], x1[3])};
-    return __builtin_bit_cast(bf16x8, h);
-}
-
-__device__ __forceinline__ void dma16(const void* src, uint16_t* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
-}
-
-// Workgroup barrier that orders LDS accesses only (global loads and stores stay in flight).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// The output waves' side of that barrier. Their direct loads into the ring are tracked by the
-// vector-memory counter, which they wait on explicitly (for the chunk they owe) before it, so
-// the chunk just issued stays in flight across it (a fence would wait for it too); their own
-// LDS reads are complete at the barrier (lgkmcnt), and the memory clobber keeps the compiler
-// from moving LDS accesses across it.
-__device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// keeps the instruction scheduler from moving anything across this point (reads issued before
-// it stay ahead of the MFMAs after it)
-#define GDN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// Interleaving request for the scheduling region it closes: nm times {one MFMA, up to nv VALU
-// instructions, up to nd LDS reads}.
-#define GDN_IGLP(nm, nv, nd)                                  \
-    _Pragma("unroll") for (int i_ = 0; i_ < (nm); ++i_) {     \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    \
-        __builtin_amdgcn_sched_group_barrier(0x002, (nv), 0); \
-        __builtin_amdgcn_sched_group_barrier(0x100, (nd), 0); \
-    }
-
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
-#define GDN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
-
-template <typename Ty>
+// kStates: the backward's forward sweep. The chain stores the bf16 state operand entering every
+// chunk (Sst) and nothing else: no Q, P loads, no output wave work, no y.
+template <typename Ty, bool kStates = false>
 __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ring[kRing * kSlot];      // the chain's tiles
     __shared__ __attribute__((aligned(16))) uint16_t qpbuf[2 * kQPSlot];     // the output wave's tiles
@@ -546,7 +461,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         dma_barrier();
         for (int c = 0; c <= nchunks; ++c) {
             if (c + 1 < nchunks) chain_tiles(c + 1);
-            if (c < nchunks) output_tiles(c);
+            if (!kStates && c < nchunks) output_tiles(c);
             GDN_WAIT_VMCNT(0);
             dma_barrier();
         }
@@ -637,7 +552,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         // filled and the output slot the loader filled during step c - 1
         lds_barrier();   // chunk 0 in the ring
         for (int c = 0; c <= nchunks; ++c) {
-            if (c >= 1) output(c - 1);
+            if (!kStates && c >= 1) output(c - 1);
             lds_barrier();
         }
         return;
@@ -692,6 +607,12 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         const uint16_t* slot = ring + (c % kRing) * kSlot;
         const float* sG = reinterpret_cast<const float*>(slot + kOffG);   // beta | gamma | gamma_C/gamma
         u32x4* xb = xbuf[c & 1][wave];
+        if constexpr (kStates) {   // Sb[s] holds d_k rows 32s + 8g .. + 7 of column j0w + c16
+            uint16_t* st = a.Sst + ((size_t)(cbase + c) * a.H + h) * kDK * kDK +
+                           (size_t)(j0w + c16) * kDK + 8 * g;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(st + 32 * s) = Sb[s];
+        }
         auto kfrag = [&](int rt, int s) {   // A of K S: K[relabel(rt, c16)][32s + 8g ..]
             return frag(slot + okf[rt & 1][s & 1] + (rt >> 1) * 32 * kDK + (s >> 1) * 64);
         };
@@ -728,8 +649,10 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) KS[rt] = f32x4{};
         mma_k(0);
+        if constexpr (!kStates) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xb[s * 64 + lane] = __builtin_bit_cast(u32x4, Sb[s]);
+            for (int s = 0; s < 4; ++s) xb[s * 64 + lane] = __builtin_bit_cast(u32x4, Sb[s]);
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) S[t] *= gC;
         load_k(2);
@@ -803,8 +726,10 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         GDN_SCHED_FENCE();
         // ---- U to the output waves | W = diag(gamma_C / gamma) U and its split |
         //      K^T fragments of tiles 4-5
+        if constexpr (!kStates) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) xb[(4 + rt) * 64 + lane] = __builtin_bit_cast(u32x4, U[rt]);
+            for (int rt = 0; rt < 4; ++rt) xb[(4 + rt) * 64 + lane] = __builtin_bit_cast(u32x4, U[rt]);
+        }
         bf16x8 Wh[2], Wl[2];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) U[rt] *= gd[rt];
@@ -1477,6 +1402,7 @@ static DevArgs dev_args(const ChunkArgs& c, const Layout& L) {
     a.Gw = reinterpret_cast<float*>(ws + L.Gt);
     a.Xw = nullptr;
     a.gk = nullptr;
+    a.Sst = nullptr;
     a.num_seqs = c.num_seqs; a.ntok = c.ntok; a.H = c.H; a.dv = c.dv;
     a.L = c.cu ? 0 : c.ntok / c.num_seqs;
     a.y_bf16 = c.y_bf16;
@@ -1521,6 +1447,35 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
         return launch_output_gate(c.y, c.y_bf16, gate->z, gate->z_bf16, gate->w, c.ntok, c.H, c.dv,
                                   gate->eps, gate->o, gate->o_bf16, s);
     }
+    return hipGetLastError();
+}
+
+ChunkTiles chunk_bf16_tiles(void* workspace, int ntok, int num_seqs, int H) {
+    const Layout L = ws_layout(ntok, num_seqs, H);
+    char* ws = static_cast<char*>(workspace);
+    ChunkTiles t;
+    t.chunk_start = reinterpret_cast<int32_t*>(ws + L.cs);
+    t.order = reinterpret_cast<int32_t*>(ws + L.ord);
+    t.T = reinterpret_cast<uint16_t*>(ws + L.T);
+    t.P = reinterpret_cast<uint16_t*>(ws + L.P);
+    t.Gw = reinterpret_cast<float*>(ws + L.Gt);
+    t.max_chunks = L.max_chunks;
+    return t;
+}
+
+hipError_t launch_chunk_bf16_states(const ChunkArgs& c, uint16_t* Sst, hipStream_t s) {
+    const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
+    DevArgs a = dev_args(c, L);
+    a.Sst = Sst;
+    a.y = nullptr;
+    a.ST = nullptr;
+    if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
+    if (nchunks > 0)
+        hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
+    const int pairs = c.num_seqs * c.H;
+    const int blocks = (pairs + 7) / 8 * 8 * (c.dv / kSl);
+    hipLaunchKernelGGL((chunk_scan_kernel<uint16_t, true>), dim3(blocks), dim3(kScanThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@
 //   finish per (chunk, head): sums the slices' shares and adds the A and P terms.
 // Columns of dv are independent in the state recursion (as in the forward), which is what the
 // slices use; the terms that mix columns are sums over them, so slice shares add up.
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_inverse.h"
 #include "gdn_launch.h"
@@ -779,7 +781,10 @@ __global__ void __launch_bounds__(256) copy_or_zero_kernel(float4* dst, const fl
 }  // namespace
 
 size_t chunk_bwd_workspace(int ntok, int num_seqs, int H, int dk, int dv) {
-    return bwd_layout(ntok, num_seqs, H, dk, dv).total;
+    // room for either path: the bf16 one is taken by bf16 q, k, v, dy at dk = dv = 128
+    const size_t f32 = bwd_layout(ntok, num_seqs, H, dk, dv).total;
+    if (dk != 128 || dv != 128) return f32;
+    return std::max(f32, chunk_bwd_bf16_workspace(ntok, num_seqs, H));
 }
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
@@ -811,6 +816,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& c, hipStream_t s) {
         }
         return hipGetLastError();
     }
+    if (use_bwd_bf16(c)) return launch_chunk_bwd_bf16(c, s);
 #define GDN_BWD(DK, TI, TD)                                                                     \
     do {                                                                                        \
         constexpr int SL = scan_cols<TI>();                                                     \

@@ -105,7 +105,21 @@ size_t kda_bf16_workspace(int ntok, int num_seqs, int H);
 hipError_t launch_kda_bf16(const ChunkArgs& a, const float* gk, hipStream_t s);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s, const GateArgs* gate = nullptr);
 
-// backward of the chunked gated delta rule (fp32 vector ALU)
+// The bf16 path's per-chunk tiles inside its workspace (the layout launch_chunk_bf16 uses).
+struct ChunkTiles {
+    int32_t* chunk_start;   // [num_seqs + 1] first packed chunk of each sequence (varlen)
+    int32_t* order;         // [num_seqs] sequences longest first (varlen)
+    uint16_t *T, *P;        // [max_chunks][H][64][64] bf16
+    float* Gw;              // [max_chunks][H][3][64]: beta, gamma = e^G, gamma_C / gamma
+    int max_chunks;
+};
+ChunkTiles chunk_bf16_tiles(void* workspace, int ntok, int num_seqs, int H);
+// The backward's forward sweep on the bf16 path (dk = dv = 128): the chunk table, T and P per
+// chunk, and the state entering every chunk as bf16 S^T [max_chunks][H][dv][dk] in Sst; no y.
+hipError_t launch_chunk_bf16_states(const ChunkArgs& a, uint16_t* Sst, hipStream_t s);
+
+// backward of the chunked gated delta rule: bf16 q, k, v, dy with dk = dv = 128 on the bf16
+// matrix cores (chunk_bwd_bf16.hip), everything else in fp32 (chunk_bwd.hip)
 struct ChunkBwdArgs {
     const void *q, *k, *v, *dy;
     int in_bf16, dy_bf16;
@@ -117,6 +131,9 @@ struct ChunkBwdArgs {
 };
 size_t chunk_bwd_workspace(int ntok, int num_seqs, int H, int dk, int dv);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t s);
+bool use_bwd_bf16(const ChunkBwdArgs& a);
+size_t chunk_bwd_bf16_workspace(int ntok, int num_seqs, int H);
+hipError_t launch_chunk_bwd_bf16(const ChunkBwdArgs& a, hipStream_t s);
 
 // per-channel-decay (KDA-style) chunked forward (fp32 vector ALU)
 struct ChunkKdaArgs {

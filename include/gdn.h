@@ -194,8 +194,13 @@ size_t gdn_chunk_backward_workspace_size(int ntok, int num_seqs, int H, int dk, 
  * dL/dS_T, the gradients with respect to q, k, v, g (= log alpha), beta and S0 of
  * eqs. (1)-(4) (section 2.1.1; the reading notes' "Kernel 效率" cites backward speedups
  * for chunked GDN kernels, and their section 3.1 trains the decay and beta projections
- * with AdamW). Computed chunkwise (C = 64) in fp32: a forward sweep stores the state at
- * every chunk start in the workspace, a reverse sweep carries dS back through the chunks.
+ * with AdamW). Computed chunkwise (C = 64): a forward sweep stores the state at every chunk
+ * start in the workspace, a reverse sweep carries dS back through the chunks and stores it
+ * per chunk, and a per-chunk pass forms the gradients.
+ *   - in_dtype and dy_dtype GDN_BF16 with dk = dv = 128: products on the bf16 matrix cores
+ *     with fp32 accumulation, fp32 operands entering as hi + lo bf16 pairs where the
+ *     gradients need them (relative L2 error per (sequence, head) about 1e-3);
+ *   - any other combination: fp32 throughout (about 1e-6).
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, num_seqs, ntok, H, dk, dv:
  *       as gdn_chunk_prefill (the forward's inputs; q, k, v in in_dtype).

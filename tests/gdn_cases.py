@@ -78,6 +78,38 @@ def o_allowance(o_ref, o_qkv, y_bf16):
     return a
 
 
+def assert_close_grad(name, got, ref, cu=None, H=None, state=False):
+    """The bf16 bar applied to a gradient of the bf16 matrix-core backward, against the fp64
+    oracle's gradient: max slice relative L2 <= 5e-3 as for the forward's outputs, and
+    elementwise |got - ref| <= 2e-2 s + 2^-8 |ref|, where s = max(1, RMS of the reference
+    slice). A gradient is not an O(1) quantity like y: the 2e-2 of the forward's bar is taken in
+    units of the slice's own scale once that scale exceeds 1, and 2^-8 |ref| is the relative
+    precision of bf16 operands (the products' inputs are bf16 or hi + lo pairs)."""
+    if state:
+        errs = state_rel_errors(got, ref)
+        n = ref.shape[0] * ref.shape[1]
+        rms = np.sqrt(np.mean(ref.reshape(n, -1) ** 2, axis=1)).reshape(ref.shape[:2] + (1,) * (ref.ndim - 2))
+        scale = np.broadcast_to(np.maximum(1.0, rms), ref.shape)
+    else:
+        errs = slice_rel_errors(got, ref, cu, H)
+        scale = np.ones_like(ref)
+        for lo, hi in zip(cu[:-1], cu[1:]):
+            for h in range(H):
+                x = ref[lo:hi, h]
+                if x.size:
+                    scale[lo:hi, h] = max(1.0, float(np.sqrt(np.mean(x * x))))
+    worst = float(errs.max()) if errs.size else 0.0
+    assert worst <= TOL_REL[True], f"{name}: max slice rel L2 {worst:.3e} > {TOL_REL[True]:.0e}"
+    bound = TOL_ABS * scale + U_BF16 * np.abs(ref)
+    ratio = np.abs(got - ref) / bound
+    if ratio.size and not np.all(ratio <= 1.0):
+        i = np.unravel_index(np.argmax(ratio), ratio.shape)
+        raise AssertionError(f"{name}: elementwise |diff| over the bound at {tuple(int(x) for x in i)}: "
+                             f"got {got[i]:.6g} ref {ref[i]:.6g} bound {bound[i]:.4g}, "
+                             f"{int(np.sum(ratio > 1))} elements over")
+    return worst, float(ratio.max()) if ratio.size else 0.0
+
+
 def max_abs(got, ref) -> float:
     return float(np.abs(got - ref).max()) if np.size(ref) else 0.0
 
