@@ -467,9 +467,17 @@ __device__ __forceinline__ bool chunk_range(const BArgs& a, int chunk, int& t0, 
     return true;
 }
 
+// one DPP rotation of a value within each 16-lane row (VALU, no LDS traffic)
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a row group
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, kWave);
+    x += row_ror<8>(x);
+    x += row_ror<4>(x);
+    x += row_ror<2>(x);
+    x += row_ror<1>(x);
     return x;
 }
 
@@ -499,11 +507,13 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
     uint16_t* const Pl = Tl + kC * kC;
     uint16_t* const dSl = Pl + kC * kC;
 
-    // ---------------- phase 0: tiles into LDS (rows >= n zero), gates
+    // ---------------- phase 0: tiles into LDS (rows >= n zero), gates. The fp32 dS' rows are
+    // read once, in the fragment order phase 2 consumes them (d_k row 16 wave + c16, d_v
+    // columns 32 s + 8 g .. + 7), and stay in registers until then.
+    f32x4 dsv[4][2];
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
         u32x4 rk[2], rq[2], ry[2], rv[2], rs[4], rt_, rp;
-        float4 rd[4][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int u = tid + i * kGradThreads, row = u >> 4, un = u & 15;
@@ -520,9 +530,9 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int u = tid + i * kGradThreads;
             rs[i] = reinterpret_cast<const u32x4*>(a.Sst + ch * kD * kD)[u];
-            const float4* src = reinterpret_cast<const float4*>(a.dSp + ch * kD * kD) + 2 * u;
-            rd[i][0] = src[0];
-            rd[i][1] = src[1];
+            const f32x4* src = reinterpret_cast<const f32x4*>(a.dSp + (ch * kD + 16 * wave + c16) * kD + 32 * i + 8 * g);
+            dsv[i][0] = src[0];
+            dsv[i][1] = src[1];
         }
         if (wave == 0) {
             const float gv = lane < n ? a.g[(size_t)(t0 + lane) * H + h] : 0.f;
@@ -555,11 +565,10 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int u = tid + i * kGradThreads, row = u >> 4, un = u & 15;
-            const int o = row * kD + ((un ^ swz(row)) << 3);
-            *reinterpret_cast<u32x4*>(Sl + o) = rs[i];
-            const u32x4 hv = {pack_bf2(rd[i][0].x, rd[i][0].y), pack_bf2(rd[i][0].z, rd[i][0].w),
-                              pack_bf2(rd[i][1].x, rd[i][1].y), pack_bf2(rd[i][1].z, rd[i][1].w)};
-            *reinterpret_cast<u32x4*>(dSl + o) = hv;
+            *reinterpret_cast<u32x4*>(Sl + row * kD + ((un ^ swz(row)) << 3)) = rs[i];
+            const u32x4 hv = {pack_bf2(dsv[i][0][0], dsv[i][0][1]), pack_bf2(dsv[i][0][2], dsv[i][0][3]),
+                              pack_bf2(dsv[i][1][0], dsv[i][1][1]), pack_bf2(dsv[i][1][2], dsv[i][1][3])};
+            *reinterpret_cast<u32x4*>(dSl + e128(16 * wave + c16, 32 * i + 8 * g)) = hv;
         }
     }
     __syncthreads();
@@ -758,13 +767,11 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             K1[rt] = f32x4{};
         }
         float gc = 0.f;
-        const float* dsrow = a.dSp + (ch * kD + d) * kD;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int k0 = 32 * s + 8 * g;
             const bf16x8 sb = trcol(Sl, k0, 16 * wave);   // S[d][k0 ..] from S^T rows
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(dsrow + k0);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(dsrow + k0 + 4);
+            const f32x4 x0 = dsv[s][0], x1 = dsv[s][1];   // dS'[d][k0 ..]
             bf16x8 dh, dl;
             split8(x0, x1, dh, dl);
             {
