@@ -1339,8 +1339,7 @@ __global__ void __launch_bounds__(kWv * kWave) chunk_scan_wide_kernel(DevArgs a,
             for (int rt = 0; rt < 4; ++rt) {
                 float ss = YT[rt][0] * YT[rt][0] + YT[rt][1] * YT[rt][1] + YT[rt][2] * YT[rt][2] +
                            YT[rt][3] * YT[rt][3];
-                ss += __shfl_xor(ss, 16, kWave);
-                ss += __shfl_xor(ss, 32, kWave);
+                ss = sum_across<16>(ss);
                 if (g == 0) ssq[c & 1][wave][16 * rt + c16] = ss;
             }
         }

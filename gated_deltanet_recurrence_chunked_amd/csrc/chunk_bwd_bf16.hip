@@ -467,19 +467,7 @@ __device__ __forceinline__ bool chunk_range(const BArgs& a, int chunk, int& t0, 
     return true;
 }
 
-// one DPP rotation of a value within each 16-lane row (VALU, no LDS traffic)
-template <int N>
-__device__ __forceinline__ float row_ror(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a row group
-    x += row_ror<8>(x);
-    x += row_ror<4>(x);
-    x += row_ror<2>(x);
-    x += row_ror<1>(x);
-    return x;
-}
+__device__ __forceinline__ float sum16(float x) { return group_sum<16>(x); }   // a 16-lane row
 
 __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Kl[kC * kD], Ql[kC * kD], Yl[kC * kD];
@@ -744,8 +732,7 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             rs_a[i] = sum16(da * ea * KK[i]);
             cs += dd;
         }
-        cs += __shfl_xor(cs, 16, kWave);
-        cs += __shfl_xor(cs, 32, kWave);
+        cs = sum_across<16>(cs);
         if (c16 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -903,8 +890,7 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
         const float dgam = dg1 - sB[r] * dg2;
         float dG = ok ? rs - cs + dgam * gam - dw * wr : 0.f;
         float tot = ok ? dw * wr : 0.f;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) tot += __shfl_xor(tot, o, kWave);
+        tot = group_sum<kWave>(tot);
         if (r == n - 1) dG += gc * sGam[n - 1] + tot;
         // dg = reverse running sum of dG over the chunk
         float acc = dG;

@@ -70,12 +70,10 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     }
     // reduce over the row groups of this wave (lanes TPR apart), then across waves in LDS
 #pragma unroll
-    for (int o = TPR; o < kWave; o <<= 1)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pk[j] += __shfl_xor(pk[j], o, kWave);
-            pq[j] += __shfl_xor(pq[j], o, kWave);
-        }
+    for (int j = 0; j < 4; ++j) {
+        pk[j] = sum_across<TPR>(pk[j]);
+        pq[j] = sum_across<TPR>(pq[j]);
+    }
     if (lane < TPR) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -197,12 +195,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(DecodeFusedAr
         }
     }
 #pragma unroll
-    for (int o = TPR; o < kWave; o <<= 1)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pk[j] += __shfl_xor(pk[j], o, kWave);
-            pq[j] += __shfl_xor(pq[j], o, kWave);
-        }
+    for (int j = 0; j < 4; ++j) {
+        pk[j] = sum_across<TPR>(pk[j]);
+        pq[j] = sum_across<TPR>(pq[j]);
+    }
     if (lane < TPR) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -258,21 +254,21 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(DecodeFusedAr
 // sums). All 2T column reductions run against the one state in registers, so the state is
 // read once and written once however many tokens the step carries. Decays are exp of
 // differences of the running sum (never above 1).
-// One 256-thread workgroup per state (one wave per SIMD; three per CU for T <= 4): a thread
-// holds dk/8 contiguous rows of 4 columns, as the single-token kernel's threads do. Measured
-// against 512-thread workgroups (two per CU), which leave more registers per thread for the
-// per-token arrays: 424-432 against 534 us per step at T = 8, within the run-to-run spread
-// (about 10 us) at T = 2 and 4 (N = 256, H = 32): more workgroups in flight per CU hide more of
-// the state's load latency, even with a few registers spilled at T = 4. Column sums: in registers over a thread's rows,
-// by shuffles over the wave's row groups, then once per (value, column) across the waves in LDS.
-// kDecColSplit > 1 would give each workgroup 1/kDecColSplit of the columns (a column's sums
-// and update need only that column); measured slower at split 2 (the per-workgroup token
-// work is repeated and each workgroup moves half the bytes).
-// The fused variant keeps 512-thread workgroups (two per CU at T <= 4): its front end has
-// 2 dk + dv channels to convolve, one per thread (276 us at T = 4 against 280 with 256).
-template <bool kFused> constexpr int dm_threads() { return kFused ? 512 : 256; }
+// One workgroup per state: 512 threads (two per CU) for T <= 4, 256 (one wave per SIMD) for
+// T = 8, whose per-token arrays need the registers; a thread holds dk / (threads / (dv / 4))
+// contiguous rows of 4 columns, as the single-token kernel's threads do. Measured at N = 256,
+// H = 32 (us per step, 256 / 512 threads): T = 4 219 / 214, T = 8 386 / 501. Column sums: in
+// registers over a thread's rows, across the wave's row groups by VALU lane exchanges, then
+// once per (value, column) across the waves in LDS. kDecColSplit > 1 would give each
+// workgroup 1/kDecColSplit of the columns (a column's sums and update need only that column);
+// measured slower at split 2 (the per-workgroup token work is repeated and each workgroup
+// moves half the bytes). The fused variant uses 512-thread workgroups at every T: its front
+// end has 2 dk + dv channels to convolve, one per thread.
+template <bool kFused, int kMaxDecT> constexpr int dm_threads() {
+    return (kFused || kMaxDecT <= 4) ? 512 : 256;
+}
 template <bool kFused, int kMaxDecT> constexpr int dm_min_waves() {
-    return kMaxDecT <= 4 ? (kFused ? 4 : 3) : 2;
+    return kMaxDecT <= 4 ? 4 : 2;
 }
 constexpr int kDecColSplit = 1;
 
@@ -304,7 +300,7 @@ struct MultiArgs {
 // kMaxDecT (2, 4 or 8) bounds T at compile time: the per-token register arrays are sized by
 // it, so a short step does not pay the registers (and occupancy) of the longest one.
 template <int DK, int DV, int kMaxDecT, typename Tin, typename Tout, bool kFused>
-__global__ void __launch_bounds__(dm_threads<kFused>(), (dm_min_waves<kFused, kMaxDecT>()))
+__global__ void __launch_bounds__((dm_threads<kFused, kMaxDecT>()), (dm_min_waves<kFused, kMaxDecT>()))
 decode_multi_kernel(MultiArgs m) {
     const Tin* __restrict__ q = static_cast<const Tin*>(m.q);
     const Tin* __restrict__ k = static_cast<const Tin*>(m.k);
@@ -315,7 +311,7 @@ decode_multi_kernel(MultiArgs m) {
     const int T = m.T, H = m.H;
     constexpr int DVS = DV / kDecColSplit;       // columns of this workgroup
     constexpr int TPR = DVS / 4;                 // threads per state row
-    constexpr int kDecMultiThreads = dm_threads<kFused>();
+    constexpr int kDecMultiThreads = dm_threads<kFused, kMaxDecT>();
     constexpr int RG = kDecMultiThreads / TPR;   // row groups
     constexpr int RPT = DK / RG;                 // contiguous rows per thread
     constexpr int NW = kDecMultiThreads / kWave;
@@ -504,12 +500,10 @@ decode_multi_kernel(MultiArgs m) {
                     }
             }
 #pragma unroll
-            for (int o = TPR; o < kWave; o <<= 1)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pk[j] += __shfl_xor(pk[j], o, kWave);
-                    pq[j] += __shfl_xor(pq[j], o, kWave);
-                }
+            for (int j = 0; j < 4; ++j) {
+                pk[j] = sum_across<TPR>(pk[j]);
+                pq[j] = sum_across<TPR>(pq[j]);
+            }
             if (lane < TPR) {
                 *reinterpret_cast<floatx4*>(&red[wave][2 * t][cl]) = floatx4{pk[0], pk[1], pk[2], pk[3]};
                 *reinterpret_cast<floatx4*>(&red[wave][2 * t + 1][cl]) = floatx4{pq[0], pq[1], pq[2], pq[3]};
@@ -557,34 +551,35 @@ decode_multi_kernel(MultiArgs m) {
 
     // S_t = e^{G_t} S + sum_{i<=t} e^{G_t-G_i} k_i U_i^T: every step's state when asked for,
     // the last one in place
+    // Four rows at a time, so only a 4 x 4 block of the new state is live beside the old one.
     auto state_at = [&](int t, float* dst) __attribute__((always_inline)) {
         const float gt = expf(Gs[t]);
-        float o[RPT][4];
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
+        for (int rb = 0; rb < RPT; rb += 4) {
+            float o[4][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[r][j] = gt * s[r][j];
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < kMaxDecT; ++i) {
-            if (i <= t) {
-                const float d = Dm[t][i];
+                for (int j = 0; j < 4; ++j) o[r][j] = rb + r < RPT ? gt * s[rb + r][j] : 0.f;
 #pragma unroll
-                for (int r0_ = 0; r0_ < RPT; r0_ += 4) {
+            for (int i = 0; i < kMaxDecT; ++i) {
+                if (i <= t) {
+                    const float d = Dm[t][i];
                     float kr[4];
-                    row4(ks[i], r0_, kr);
+                    row4(ks[i], rb, kr);
 #pragma unroll
-                    for (int r = 0; r < 4 && r0_ + r < RPT; ++r) {
+                    for (int r = 0; r < 4; ++r) {
                         const float dk = d * kr[r];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) o[r0_ + r][j] += dk * U[i][j];
+                        for (int j = 0; j < 4; ++j) o[r][j] += dk * U[i][j];
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            __builtin_nontemporal_store(floatx4{o[r][0], o[r][1], o[r][2], o[r][3]},
-                                        reinterpret_cast<floatx4*>(dst + (size_t)(r0 + r) * DV + c));
+            for (int r = 0; r < 4 && rb + r < RPT; ++r)
+                __builtin_nontemporal_store(floatx4{o[r][0], o[r][1], o[r][2], o[r][3]},
+                                            reinterpret_cast<floatx4*>(dst + (size_t)(r0 + rb + r) * DV + c));
+        }
     };
     if (steps)
         for (int t = 0; t < T; ++t) state_at(t, steps + ((size_t)(n * T + t) * H + h) * DK * DV);
@@ -617,7 +612,7 @@ static void launch_dec_multi_t(const MultiArgs& m, int in_bf16, int out_bf16, in
                                hipStream_t s) {
 #define GDN_DECM(TI, TO)                                                                        \
     hipLaunchKernelGGL((decode_multi_kernel<DK, DV, MT, TI, TO, kFused>),                         \
-                       dim3(heads * kDecColSplit), dim3(dm_threads<kFused>()), 0, s, m)
+                       dim3(heads * kDecColSplit), dim3(dm_threads<kFused, MT>()), 0, s, m)
     if (in_bf16 && out_bf16) GDN_DECM(uint16_t, uint16_t);
     else if (in_bf16) GDN_DECM(uint16_t, float);
     else if (out_bf16) GDN_DECM(float, uint16_t);

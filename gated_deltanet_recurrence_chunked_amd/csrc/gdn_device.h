@@ -170,11 +170,56 @@ __device__ __forceinline__ floatx4 mma_f32_tile(const TA* A, int ar, int ak, con
 }
 
 // --------------------------------------------------------------------------- reductions
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+// Lane exchanges that stay in the VALU (a shuffle through ds_bpermute is an LDS round trip):
+// v_permlane32_swap / v_permlane16_swap (gfx950) exchange the two 32-lane halves / the rows
+// of each 32-lane half, so r[0] + r[1] of a value swapped with itself is x + x[lane ^ 32] /
+// x + x[lane ^ 16] in every lane; DPP row rotations reach the lanes of a 16-lane row.
+template <int o>
+__device__ __forceinline__ float xor_sum(float x) {
+    static_assert(o == 16 || o == 32, "lane distance");
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (o == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+template <int n>
+__device__ __forceinline__ float row_ror(float x) {   // lane l <- lane 16 (l / 16) + (l + n) % 16
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + n, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64), every lane of a group
+// getting the group's sum. The pairing is a butterfly over lane distances width/2 .. 1 (within
+// a 16-lane row, rotating by 8, 4, 2, 1 pairs the same values as distances 8, 4, 2, 1), so the
+// rounding is the same whichever lane exchange carries a step.
 template <int width>
 __device__ __forceinline__ float group_sum(float x) {
+    static_assert(width >= 1 && width <= 64 && (width & (width - 1)) == 0, "width");
+    if constexpr (width == 64) x = xor_sum<32>(x);
+    if constexpr (width >= 32) x = xor_sum<16>(x);
+    if constexpr (width >= 16) {
+        x += row_ror<8>(x);
+        x += row_ror<4>(x);
+        x += row_ror<2>(x);
+        x += row_ror<1>(x);
+    } else {
 #pragma unroll
-    for (int o = width / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+        for (int o = width / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    }
+    return x;
+}
+// x summed over the lanes lane ^ d for d = from, 2 from, .., 32 (from a power of two): the
+// lanes that share lane % from
+template <int from>
+__device__ __forceinline__ float sum_across(float x) {
+    static_assert(from >= 1 && from <= 32 && (from & (from - 1)) == 0, "lane distance");
+#pragma unroll
+    for (int o = from; o < 16; o <<= 1) x += __shfl_xor(x, o, kWave);
+    if constexpr (from <= 16) x = xor_sum<16>(x);
+    x = xor_sum<32>(x);
     return x;
 }
 
