@@ -36,6 +36,13 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     const int c = (tid % TPR) * 4;
     const int rg = tid / TPR;
 
+    // the token's loads first and unconditional (a load under a branch is waited for at the
+    // join, and the counter completes loads in issue order), then the state's
+    const int ek = min(tid, 2 * DK - 1);
+    const Tin kq_in = ((ek < DK ? k : q) + (size_t)head * DK)[ek < DK ? ek : ek - DK];   // raw
+    float vv[4];
+    Vec4<Tin>::load(v + (size_t)head * DV + c, vv);
+    __builtin_amdgcn_sched_barrier(0);
     float* S = state + (size_t)head * DK * DV;
     float s[RPT][4];
 #pragma unroll
@@ -44,10 +51,9 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
             reinterpret_cast<const floatx4*>(S + (size_t)(rg + RG * i) * DV + c));
         s[i][0] = t.x; s[i][1] = t.y; s[i][2] = t.z; s[i][3] = t.w;
     }
-    if (tid < DK) ks[tid] = load1(k + (size_t)head * DK + tid);
-    else if (tid < 2 * DK) qs[tid - DK] = load1(q + (size_t)head * DK + tid - DK);
-    float vv[4];
-    Vec4<Tin>::load(v + (size_t)head * DV + c, vv);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < DK) ks[tid] = load1(&kq_in);
+    else if (tid < 2 * DK) qs[tid - DK] = load1(&kq_in);
     const float a = expf(g[head]);
     const float b = beta[head];
     __syncthreads();
@@ -341,8 +347,9 @@ decode_multi_kernel(MultiArgs m) {
 
     float* S = state + (size_t)head * DK * DV;
     float s[RPT][4];
-    // the state's loads go first (the unfused prologue's loads overlap them); the fused
-    // prologue's registers would not fit beside them, so there they follow it
+    // The state's loads follow the tokens': the token-pair products need only q and k, so they
+    // run while the state is still arriving (the vector-memory counter completes loads in
+    // issue order, so loads issued before the state's can be waited for alone).
     auto load_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -351,25 +358,45 @@ decode_multi_kernel(MultiArgs m) {
             s[i][0] = x.x; s[i][1] = x.y; s[i][2] = x.z; s[i][3] = x.w;
         }
     };
-    if constexpr (!kFused) load_state();
     float vv[kMaxDecT][4];
     if constexpr (!kFused) {
-        for (int i = tid; i < T * DK; i += kDecMultiThreads) {
-            const int t = i / DK, r = i % DK;
-            ks[t][r] = load1(k + tok(t) * DK + r);
-            qs[t][r] = load1(q + tok(t) * DK + r);
+        // every token load is issued before any is used, unconditionally (tokens past T read
+        // token T - 1 and are dropped): a load under a branch is waited for at the join
+        constexpr int KQ = (kMaxDecT * DK + kDecMultiThreads - 1) / kDecMultiThreads;
+        float kr[KQ], qr[KQ], gv[kMaxDecT], bv[kMaxDecT];
+#pragma unroll
+        for (int u = 0; u < KQ; ++u) {
+            const int i = tid + u * kDecMultiThreads, t = min(i / DK, T - 1), r = i % DK;
+            kr[u] = load1(k + tok(t) * DK + r);
+            qr[u] = load1(q + tok(t) * DK + r);
         }
-        float run = 0.f;
 #pragma unroll
         for (int t = 0; t < kMaxDecT; ++t) {
+            const int tc = min(t, T - 1);
+            Vec4<Tin>::load(v + tok(tc) * DV + c, vv[t]);
+            gv[t] = m.g[tok(tc)];
+            bv[t] = m.beta[tok(tc)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_state();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < KQ; ++u) {
+            const int i = tid + u * kDecMultiThreads, t = i / DK, r = i % DK;
             if (t < T) {
-                Vec4<Tin>::load(v + tok(t) * DV + c, vv[t]);
-                run += m.g[tok(t)];
-                if (tid == t) {
-                    Gs[t] = run;
-                    Bs[t] = m.beta[tok(t)];
-                }
+                ks[t][r] = kr[u];
+                qs[t][r] = qr[u];
             }
+        }
+        if (tid == 0) {
+            float run = 0.f;
+#pragma unroll
+            for (int t = 0; t < kMaxDecT; ++t)
+                if (t < T) {
+                    run += gv[t];
+                    Gs[t] = run;
+                    Bs[t] = bv[t];
+                }
         }
         __syncthreads();
     } else {
