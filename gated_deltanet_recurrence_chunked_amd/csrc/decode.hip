@@ -140,6 +140,36 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(DecodeFusedAr
     const int c = (tid % TPR) * 4;
     const int rg = tid / TPR;
 
+    // The token's loads (inputs, conv history and taps, z) are issued first and unconditionally
+    // (channel indices clamped; a load under a branch is waited for at the join), then the
+    // state's: the conv and the L2 norms run while the state is still arriving.
+    constexpr int NCH = 2 * DK + DV;                                  // q | k | v channels
+    constexpr int CPT = (NCH + kDecThreads - 1) / kDecThreads;        // channels per thread
+    Tin* hist = static_cast<Tin*>(f.conv_state) + (size_t)n * 3 * f.hC;
+    Tin xin[CPT], hv[CPT][3];
+    float4 wv[CPT];
+    int hcs[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int ch = min(tid + u * kDecThreads, NCH - 1);
+        const int role = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
+        const int cl = ch - (role == 0 ? 0 : (role == 1 ? DK : 2 * DK));
+        const int d = role < 2 ? DK : DV;
+        const int cs = h * d + cl;                                   // channel in its stream
+        const int hc = (role == 0 ? 0 : (role == 1 ? H * DK : 2 * H * DK)) + cs;
+        hcs[u] = hc;
+        // stream pointers selected from the (scalar) arguments, not indexed per lane
+        const Tin* xs = static_cast<const Tin*>(role == 0 ? f.x[0] : (role == 1 ? f.x[1] : f.x[2]));
+        const float* ws = role == 0 ? f.w[0] : (role == 1 ? f.w[1] : f.w[2]);
+        xin[u] = xs[(size_t)n * H * d + cs];
+        hv[u][0] = hist[hc];
+        hv[u][1] = hist[f.hC + hc];
+        hv[u][2] = hist[2 * f.hC + hc];
+        wv[u] = reinterpret_cast<const float4*>(ws)[cs];
+    }
+    float zv[4];
+    Vec4<Tin>::load(static_cast<const Tin*>(f.z) + (size_t)head * DV + c, zv);
+    __builtin_amdgcn_sched_barrier(0);
     float* S = f.state + (size_t)head * DK * DV;
     float s[RPT][4];
 #pragma unroll
@@ -148,29 +178,27 @@ __global__ void __launch_bounds__(kDecThreads) decode_fused_kernel(DecodeFusedAr
             reinterpret_cast<const floatx4*>(S + (size_t)(rg + RG * i) * DV + c));
         s[i][0] = t.x; s[i][1] = t.y; s[i][2] = t.z; s[i][3] = t.w;
     }
-    float zv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (rg == 0) Vec4<Tin>::load(static_cast<const Tin*>(f.z) + (size_t)head * DV + c, zv);
+    __builtin_amdgcn_sched_barrier(0);
 
     // conv over [history rows 0..2, x]; the history shifts by one token in place (each
     // channel's four values are touched by this thread only)
-    Tin* hist = static_cast<Tin*>(f.conv_state) + (size_t)n * 3 * f.hC;
-    for (int ch = tid; ch < 2 * DK + DV; ch += kDecThreads) {
-        const int role = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
-        const int cl = ch - (role == 0 ? 0 : (role == 1 ? DK : 2 * DK));
-        const int d = role < 2 ? DK : DV;
-        const int cs = h * d + cl;                                   // channel in its stream
-        const int hc = (role == 0 ? 0 : (role == 1 ? H * DK : 2 * H * DK)) + cs;
-        const Tin x = static_cast<const Tin*>(f.x[role])[(size_t)n * H * d + cs];
-        const Tin h0 = hist[hc], h1 = hist[f.hC + hc], h2 = hist[2 * f.hC + hc];
-        const float4 w = reinterpret_cast<const float4*>(f.w[role])[cs];
-        const float u = conv4(w.x, w.y, w.z, w.w, load1(&h0), load1(&h1), load1(&h2), load1(&x));
-        hist[hc] = h1;
-        hist[f.hC + hc] = h2;
-        hist[2 * f.hC + hc] = x;
-        const float act = siluf_(u);
-        if (role == 0) qs[cl] = act;
-        else if (role == 1) ks[cl] = act;
-        else vs[cl] = act;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int ch = tid + u * kDecThreads;
+        if (ch < NCH) {
+            const int role = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
+            const int cl = ch - (role == 0 ? 0 : (role == 1 ? DK : 2 * DK));
+            const float4 w = wv[u];
+            const float cu = conv4(w.x, w.y, w.z, w.w, load1(&hv[u][0]), load1(&hv[u][1]),
+                                   load1(&hv[u][2]), load1(&xin[u]));
+            hist[hcs[u]] = hv[u][1];
+            hist[f.hC + hcs[u]] = hv[u][2];
+            hist[2 * f.hC + hcs[u]] = xin[u];
+            const float act = siluf_(cu);
+            if (role == 0) qs[cl] = act;
+            else if (role == 1) ks[cl] = act;
+            else vs[cl] = act;
+        }
     }
     const float a = expf(gate_g(f.A_log[h], f.a_raw[head], f.dt_bias[h]));
     const float b = gate_beta(f.b_raw[head]);
@@ -400,24 +428,42 @@ decode_multi_kernel(MultiArgs m) {
         }
         __syncthreads();
     } else {
-        // conv over [history rows 0..2, x_0 .. x_{T-1}], one channel (of q | k | v) per thread
+        // conv over [history rows 0..2, x_0 .. x_{T-1}], one channel (of q | k | v) per thread.
+        // Every load of the step's inputs is issued first and unconditionally (indices clamped;
+        // a load under a branch is waited for at the join), then the state's, then the conv
+        // and the gates run while the state arrives.
+        static_assert(2 * DK + DV <= kDecMultiThreads, "one channel per thread");
+        constexpr int ZPT = (kMaxDecT * DV + kDecMultiThreads - 1) / kDecMultiThreads;
         const Tin* hin = static_cast<const Tin*>(m.hin) + (size_t)n * 3 * m.hC;
         Tin* hout = static_cast<Tin*>(m.hout) + (size_t)n * 3 * m.hC;
-        for (int ch = tid; ch < 2 * DK + DV; ch += kDecMultiThreads) {
-            const int role = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
-            const int cl2 = ch - (role == 0 ? 0 : (role == 1 ? DK : 2 * DK));
-            const int d = role < 2 ? DK : DV;
-            const int cs = h * d + cl2;
-            const int hc = (role == 0 ? 0 : (role == 1 ? H * DK : 2 * H * DK)) + cs;
-            const Tin* xs = static_cast<const Tin*>(m.x[role]);
-            const float4 w = reinterpret_cast<const float4*>(m.w[role])[cs];
-            Tin buf[3 + kMaxDecT];   // history then the new inputs, raw
-            buf[0] = hin[hc];
-            buf[1] = hin[m.hC + hc];
-            buf[2] = hin[2 * m.hC + hc];
+        const int ch = min(tid, 2 * DK + DV - 1);
+        const int role = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
+        const int cl2 = ch - (role == 0 ? 0 : (role == 1 ? DK : 2 * DK));
+        const int d = role < 2 ? DK : DV;
+        const int cs = h * d + cl2;
+        const int hc = (role == 0 ? 0 : (role == 1 ? H * DK : 2 * H * DK)) + cs;
+        // stream pointers selected from the (scalar) arguments, not indexed per lane
+        const Tin* xs = static_cast<const Tin*>(role == 0 ? m.x[0] : (role == 1 ? m.x[1] : m.x[2]));
+        const float* ws = role == 0 ? m.w[0] : (role == 1 ? m.w[1] : m.w[2]);
+        const float4 w = reinterpret_cast<const float4*>(ws)[cs];
+        Tin buf[3 + kMaxDecT];   // history then the new inputs, raw
+        buf[0] = hin[hc];
+        buf[1] = hin[m.hC + hc];
+        buf[2] = hin[2 * m.hC + hc];
 #pragma unroll
-            for (int t = 0; t < kMaxDecT; ++t)
-                if (t < T) buf[3 + t] = xs[tok(t) * d + cl2];
+        for (int t = 0; t < kMaxDecT; ++t) buf[3 + t] = xs[tok(min(t, T - 1)) * d + cl2];
+        Tin zr[ZPT];
+#pragma unroll
+        for (int u = 0; u < ZPT; ++u) {
+            const int e = min(tid + u * kDecMultiThreads, T * DV - 1);
+            zr[u] = static_cast<const Tin*>(m.z)[tok(e / DV) * DV + e % DV];
+        }
+        const int tg = min(tid, T - 1);
+        const float ar = m.a_raw[tok(tg)], br = m.b_raw[tok(tg)];
+        __builtin_amdgcn_sched_barrier(0);
+        load_state();
+        __builtin_amdgcn_sched_barrier(0);
+        if (tid < 2 * DK + DV) {
             float* dst = role == 0 ? &qs[0][0] : (role == 1 ? &ks[0][0] : &vs[0][0]);
             const int stride = role < 2 ? DK : DV;
 #pragma unroll
@@ -438,12 +484,13 @@ decode_multi_kernel(MultiArgs m) {
         }
         // gates: thread t forms token t's; z comes in now for the epilogue's output gate
         if (tid < T) {
-            gl[tid] = gate_g(m.A_log[h], m.a_raw[tok(tid)], m.dt_bias[h]);
-            Bs[tid] = gate_beta(m.b_raw[tok(tid)]);
+            gl[tid] = gate_g(m.A_log[h], ar, m.dt_bias[h]);
+            Bs[tid] = gate_beta(br);
         }
-        for (int e = tid; e < T * DV; e += kDecMultiThreads) {
-            const int t = e / DV, j = e % DV;
-            zs[t][j] = load1(static_cast<const Tin*>(m.z) + tok(t) * DV + j);
+#pragma unroll
+        for (int u = 0; u < ZPT; ++u) {
+            const int e = tid + u * kDecMultiThreads;
+            if (e < T * DV) zs[e / DV][e % DV] = load1(&zr[u]);
         }
         __syncthreads();
         if (tid == 0) {
@@ -468,7 +515,6 @@ decode_multi_kernel(MultiArgs m) {
                 ks[t][r] *= ik;
             }
         }
-        load_state();
 #pragma unroll
         for (int t = 0; t < kMaxDecT; ++t)
             if (t < T)
