@@ -116,7 +116,7 @@ def counted_bytes(rec, kernel):
     return max(hits) if hits else None
 
 
-PREFILL_SRC = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h")
+PREFILL_SRC = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h", "gdn_mfma.h")
 
 
 class Timer:

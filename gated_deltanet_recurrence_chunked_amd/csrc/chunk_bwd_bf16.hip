@@ -523,7 +523,10 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             dsv[i][1] = src[1];
         }
         if (wave == 0) {
-            const float gv = lane < n ? a.g[(size_t)(t0 + lane) * H + h] : 0.f;
+            // both gate loads in flight together, unconditionally (row n - 1 past the end)
+            const size_t gr = (size_t)(t0 + min(lane, n - 1)) * H + h;
+            const float graw = a.g[gr], braw = a.beta[gr];
+            const float gv = lane < n ? graw : 0.f;
             float Gr = gv;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
@@ -534,7 +537,7 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             sG[lane] = Gr;
             sGam[lane] = fexp(Gr);
             sW[lane] = lane < n ? fexp(GC - Gr) : 0.f;
-            sB[lane] = lane < n ? a.beta[(size_t)(t0 + lane) * H + h] : 0.f;
+            sB[lane] = lane < n ? braw : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {

@@ -28,7 +28,7 @@ COPY_BYTES = 1 << 30
 PREFILL_KERNELS = ("chunk_prep_kernel", "chunk_scan_kernel", "chunk_table_kernel")
 
 
-PREFILL_SOURCES = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h")
+PREFILL_SOURCES = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h", "gdn_mfma.h")
 
 
 def prefill_source_sha() -> str:
