@@ -25,7 +25,9 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
-PREFILL_KERNELS = ("chunk_prep_kernel", "chunk_scan_kernel", "chunk_table_kernel")
+# the kernels of one gdn_chunk_prefill call (bf16 y; the states-only scan instantiation that the
+# backward runs is another kernel)
+PREFILL_KERNELS = ("chunk_prep_kernel", "chunk_scan_kernel<unsigned short, false>", "chunk_table_kernel")
 
 
 PREFILL_SOURCES = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h", "gdn_mfma.h")
@@ -130,7 +132,7 @@ def traffic(fetch_dir: str, write_dir: str, out: str, command: str) -> None:
     total = 0.0
     for sk, e in res["kernels"].items():
         e["bytes"] = e.get("FETCH_SIZE_bytes", 0.0) + e.get("WRITE_SIZE_bytes", 0.0)
-        if any(p in sk for p in PREFILL_KERNELS):
+        if sk.split(" [grid")[0] in PREFILL_KERNELS:
             total += e["bytes"]
     res["gdn_chunk_prefill_bytes_per_call"] = total
     with open(out, "w") as f:
@@ -166,7 +168,7 @@ def mfma(pmc_dir: str, out: str, command: str) -> None:
              "gui_active_cycles": gui,
              "mfma_busy_frac": (avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM)) if gui else None}
         res["kernels"][_key(k)] = e
-        if any(p in short(k[0]) for p in PREFILL_KERNELS):
+        if short(k[0]) in PREFILL_KERNELS:
             total += e["flops_bf16"] + e["flops_f32"]
     res["gdn_chunk_prefill_mfma_flops_per_call"] = total
     with open(out, "w") as f:
