@@ -270,7 +270,10 @@ output_gate_kernel(const Ty* __restrict__ y, const Tz* __restrict__ z, const flo
             float ov[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) ov[i] = sigmoidf_(zv[u][i]) * (gain[i] * (yv[u][i] * inv));
-            if (u == 0 || r1 < rows) Vec8<To>::template store<true>(o + (u ? off1 : off0), ov);
+            // unconditional: past the last row, row group 1 recomputes row r0 and stores the same
+            // values again (a conditional store lets the compiler sink z's second load under it,
+            // after row group 0's math, which costs a second memory round trip per step)
+            Vec8<To>::template store<true>(o + (u ? off1 : off0), ov);
         }
     }
 }
