@@ -79,7 +79,7 @@ struct DevArgs {
     uint16_t* Xw;               // per-channel decay only: [max_chunks][H][3][64][128] bf16
                                 // Kg = K o e^{Gc}, Kc = K o e^{Gc_C - Gc}, Qg = Q o e^{Gc}
     const float* gk;            // per-channel decay only: log-decays [ntok][H][128]
-    uint16_t* Sst;              // states-only scan: bf16 state entering each chunk,
+    float* Sst;                 // states-only scan: fp32 state entering each chunk,
                                 // [max_chunks][H][d_v][d_k] (S^T, d_k contiguous)
     int num_seqs, ntok, H, dv, L;  // L: equal length (when cu == NULL)
     int y_bf16;
@@ -361,8 +361,8 @@ constexpr int kQOffG = kQOffP + kC * kC;      // 3 x 64 floats (+ 256 bytes of p
 constexpr int kQPSlot = kQOffG + 512;
 
 
-// kStates: the backward's forward sweep. The chain stores the bf16 state operand entering every
-// chunk (Sst) and nothing else: no Q, P loads, no output wave work, no y.
+// kStates: the backward's forward sweep. The chain stores the fp32 state entering every chunk
+// (Sst) and nothing else: no Q, P loads, no output wave work, no y.
 template <typename Ty, bool kStates = false>
 __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ring[kRing * kSlot];      // the chain's tiles
@@ -607,11 +607,11 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         const uint16_t* slot = ring + (c % kRing) * kSlot;
         const float* sG = reinterpret_cast<const float*>(slot + kOffG);   // beta | gamma | gamma_C/gamma
         u32x4* xb = xbuf[c & 1][wave];
-        if constexpr (kStates) {   // Sb[s] holds d_k rows 32s + 8g .. + 7 of column j0w + c16
-            uint16_t* st = a.Sst + ((size_t)(cbase + c) * a.H + h) * kDK * kDK +
-                           (size_t)(j0w + c16) * kDK + 8 * g;
+        if constexpr (kStates) {   // S[2s], S[2s+1] hold d_k rows 32s + 8g .. + 7 of column j0w + c16
+            float* st = a.Sst + ((size_t)(cbase + c) * a.H + h) * kDK * kDK +
+                        (size_t)(j0w + c16) * kDK + 8 * g;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(st + 32 * s) = Sb[s];
+            for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(st + 32 * (t >> 1) + 4 * (t & 1)) = S[t];
         }
         auto kfrag = [&](int rt, int s) {   // A of K S: K[relabel(rt, c16)][32s + 8g ..]
             return frag(slot + okf[rt & 1][s & 1] + (rt >> 1) * 32 * kDK + (s >> 1) * 64);
@@ -1462,7 +1462,7 @@ ChunkTiles chunk_bf16_tiles(void* workspace, int ntok, int num_seqs, int H) {
     return t;
 }
 
-hipError_t launch_chunk_bf16_states(const ChunkArgs& c, uint16_t* Sst, hipStream_t s) {
+hipError_t launch_chunk_bf16_states(const ChunkArgs& c, float* Sst, hipStream_t s) {
     const Layout L = ws_layout(c.ntok, c.num_seqs, c.H);
     DevArgs a = dev_args(c, L);
     a.Sst = Sst;

@@ -15,8 +15,8 @@
 // with E[r,i] = e^{G_r - G_i} and dKK = beta o dA o E, plus the per-token terms of dbeta and dg.
 //
 // Three sweeps instead of per-slice shares of the terms that sum over d_v:
-//   1. the forward scan in its states-only form (chunk_bf16.hip) stores the bf16 state S
-//      entering every chunk, as the forward's own products saw it;
+//   1. the forward scan in its states-only form (chunk_bf16.hip) stores the fp32 state S
+//      entering every chunk;
 //   2. bwd_chain_kernel walks the chunks of each (sequence, head, 32-column slice) backwards
 //      carrying dS in registers (the forward scan's structure with the adjoint products) and
 //      stores the fp32 dS' of every chunk, and dS0;
@@ -24,9 +24,11 @@
 //      S and dS' and forms every gradient of the chunk with all d_v columns at hand.
 // Rounding (chosen with a bf16 emulation of these sweeps against the fp64 gradients): the
 // products whose operands are fp32 take them as hi + lo bf16 pairs (R, dU, E = -(beta gamma) o
-// dR and gamma o dY in the chain; U and dS' in U dS'^T; dR in dR U^T; U in dY U^T; the
-// coefficient matrices dP o E, dKK + dKK^T) except K dS' and dR S^T, which take dS' and dR as
-// single bf16 like the forward takes S.
+// dR and gamma o dY in the chain; in the per-chunk kernel S, dS', U, the coefficient matrices
+// dP o E and dKK + dKK^T, and dR in dR U^T), except dR in dR S^T, single bf16. The chain takes
+// dS single in K dS, as the forward takes S. Short sequences decide it: a one-token sequence's
+// dg and dbeta are single sums that cancel, and single-bf16 S or dS' there costs up to 8% of
+// them.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -46,7 +48,7 @@ struct BArgs {
     const int32_t *chunk_start, *order;     // varlen: first chunk per sequence, longest first
     const uint16_t *T, *P;                  // [chunk-head][64][64] bf16
     const float* Gw;                        // [chunk-head][3][64]: beta, gamma, gamma_C / gamma
-    const uint16_t* Sst;                    // [chunk-head][d_v][d_k] bf16: S entering the chunk
+    const float* Sst;                       // [chunk-head][d_v][d_k] fp32: S entering the chunk
     float* dSp;                             // [chunk-head][d_k][d_v] fp32: dS leaving the chunk
     float *dq, *dk, *dv, *dg, *dbeta, *dS0;
     int num_seqs, ntok, H, L;
@@ -424,16 +426,17 @@ __global__ void __launch_bounds__(kChainThreads) bwd_chain_kernel(BArgs a) {
 
 // ------------------------------------------------------------------ per-chunk gradients
 // One 8-wave workgroup per (chunk, head) with every d_v column, so the terms that sum over d_v
-// are formed whole (no shares to write and add up). LDS holds the chunk's K, Q, dY rows and
-// S^T as bf16 tiles (rows swizzled in 16-byte units as in the scans) plus one 64 KB region
-// reused by the phases:
+// are formed whole (no shares to write and add up). LDS holds the chunk's K, Q, dY rows as bf16
+// tiles (rows swizzled in 16-byte units as in the scans) plus one 64 KB region reused by the
+// phases; S and dS' reach the products from registers, as hi + lo fragments of the fp32 values
+// each lane loads in the order its fragments need:
 //   1. wave w owns d_v columns 16w .. 16w+15 and all 64 tokens (rows relabelled, so each
 //      accumulator is the next product's operand): KS = K S, R, U = T R, dW = K dS',
 //      X = P^T dY, dU, dR = T^T dU; dv leaves; U and dR go to the region as bf16 hi + lo rows;
-//      the region held V, T, P and dS' (bf16, d_k rows) until then;
+//      the region held V, T and P until then;
 //   2. the products over d_v: dA = -(dR U^T), dP = dY U^T with K K^T and Q K^T for the gate
 //      terms (wave w: lower 16x16 tiles w and w + 8), and dY S^T, dR S^T, U dS'^T for the
-//      d_k columns 16w .. 16w+15 (dS' as hi + lo from the fp32 rows the chain stored);
+//      d_k columns 16w .. 16w+15;
 //   3. the coefficient matrices dP o E, (dA o E) beta + its transpose and (dP o E)^T as hi +
 //      lo tiles in the region, their products with K and Q, and dq, dk out; then dbeta and dg
 //      from the per-token sums every phase left in LDS.
@@ -471,8 +474,7 @@ __device__ __forceinline__ float sum16(float x) { return group_sum<16>(x); }   /
 
 __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Kl[kC * kD], Ql[kC * kD], Yl[kC * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t Sl[kD * kD];   // S^T: rows d_v, cols d_k
-    // phase 1: V [64][128] | T [64][64] | P [64][64] | dS' hi [128][128] (rows d_k)
+    // phase 1: V [64][128] | T [64][64] | P [64][64]
     // phase 2: U hi | U lo | dR hi | dR lo, [64][128] each
     // phase 3: dQK hi | lo, M hi | lo, dQK^T hi | lo, [64][64] each
     __shared__ __attribute__((aligned(16))) uint16_t reg[4 * kC * kD];
@@ -493,15 +495,20 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
     uint16_t* const Vl = reg;
     uint16_t* const Tl = reg + kC * kD;
     uint16_t* const Pl = Tl + kC * kC;
-    uint16_t* const dSl = Pl + kC * kC;
+    const float* const Sg = a.Sst + ch * kD * kD;   // S^T [d_v][d_k]
+    const float* const dSg = a.dSp + ch * kD * kD;  // dS' [d_k][d_v]
 
-    // ---------------- phase 0: tiles into LDS (rows >= n zero), gates. The fp32 dS' rows are
-    // read once, in the fragment order phase 2 consumes them (d_k row 16 wave + c16, d_v
-    // columns 32 s + 8 g .. + 7), and stay in registers until then.
-    f32x4 dsv[4][2];
+    // ---------------- phase 0: tiles into LDS (rows >= n zero), gates. S and dS' are read in
+    // the fragment order their products consume them and stay in registers:
+    //   sr  S^T[j][32 s + 8 g .. + 7] (j = 16 wave + c16): B of K S,
+    //   dwv dS'[32 s + 8 g + e][j]: B of K dS',
+    //   dsv dS'[d][32 s + 8 g .. + 7] (d = 16 wave + c16): B of U dS'^T, and dS' of <S, dS'>.
+    const int j = 16 * wave + c16;
+    f32x4 dsv[4][2], sr[4][2];
+    float dwv[4][8];
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
-        u32x4 rk[2], rq[2], ry[2], rv[2], rs[4], rt_, rp;
+        u32x4 rk[2], rq[2], ry[2], rv[2], rt_, rp;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int u = tid + i * kGradThreads, row = u >> 4, un = u & 15;
@@ -516,11 +523,14 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
         rp = reinterpret_cast<const u32x4*>(a.P + ch * kC * kC)[tid];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int u = tid + i * kGradThreads;
-            rs[i] = reinterpret_cast<const u32x4*>(a.Sst + ch * kD * kD)[u];
-            const f32x4* src = reinterpret_cast<const f32x4*>(a.dSp + (ch * kD + 16 * wave + c16) * kD + 32 * i + 8 * g);
+            const f32x4* src = reinterpret_cast<const f32x4*>(dSg + (size_t)j * kD + 32 * i + 8 * g);
             dsv[i][0] = src[0];
             dsv[i][1] = src[1];
+            const f32x4* ss = reinterpret_cast<const f32x4*>(Sg + (size_t)j * kD + 32 * i + 8 * g);
+            sr[i][0] = ss[0];
+            sr[i][1] = ss[1];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dwv[i][e] = dSg[(size_t)(32 * i + 8 * g + e) * kD + j];
         }
         if (wave == 0) {
             // both gate loads in flight together, unconditionally (row n - 1 past the end)
@@ -553,19 +563,10 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             *reinterpret_cast<u32x4*>(Tl + o) = rt_;
             *reinterpret_cast<u32x4*>(Pl + o) = rp;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int u = tid + i * kGradThreads, row = u >> 4, un = u & 15;
-            *reinterpret_cast<u32x4*>(Sl + row * kD + ((un ^ swz(row)) << 3)) = rs[i];
-            const u32x4 hv = {pack_bf2(dsv[i][0][0], dsv[i][0][1]), pack_bf2(dsv[i][0][2], dsv[i][0][3]),
-                              pack_bf2(dsv[i][1][0], dsv[i][1][1]), pack_bf2(dsv[i][1][2], dsv[i][1][3])};
-            *reinterpret_cast<u32x4*>(dSl + e128(16 * wave + c16, 32 * i + 8 * g)) = hv;
-        }
     }
     __syncthreads();
 
     // ---------------- phase 1: columns j = 16 wave + c16, tokens relabelled
-    const int j = 16 * wave + c16;
     auto tokq = [&](int rt) { return 8 * g + 32 * (rt >> 1) + 4 * (rt & 1); };   // the lane's 4 tokens
     auto row4 = [&](const float* v, int rt) { return *reinterpret_cast<const f32x4*>(v + tokq(rt)); };
     auto trcol = [&](const uint16_t* base, int k0, int col0) {
@@ -579,11 +580,13 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
     };
     f32x4 U[4], dR[4];
     {
-        bf16x8 Sb[4], dSb[4];
+        bf16x8 Sh[4], Slo[4], dWh[4], dWl[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            Sb[s] = frag(Sl + e128(j, 32 * s + 8 * g));
-            dSb[s] = trcol(dSl, 32 * s + 8 * g, 16 * wave);
+            split8(sr[s][0], sr[s][1], Sh[s], Slo[s]);
+            const f32x4 x0 = {dwv[s][0], dwv[s][1], dwv[s][2], dwv[s][3]};
+            const f32x4 x1 = {dwv[s][4], dwv[s][5], dwv[s][6], dwv[s][7]};
+            split8(x0, x1, dWh[s], dWl[s]);
         }
         f32x4 KS[4], dW[4];
 #pragma unroll
@@ -596,8 +599,10 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const bf16x8 kf = frag(Kl + e128(relabel(rt, c16), 32 * s + 8 * g));
-                KS[rt] = mfma16(kf, Sb[s], KS[rt]);
-                dW[rt] = mfma16(kf, dSb[s], dW[rt]);
+                KS[rt] = mfma16(kf, Sh[s], KS[rt]);
+                KS[rt] = mfma16(kf, Slo[s], KS[rt]);
+                dW[rt] = mfma16(kf, dWh[s], dW[rt]);
+                dW[rt] = mfma16(kf, dWl[s], dW[rt]);
             }
         // R = beta o (V - gamma o KS); V at the accumulator positions (4 tokens of column j)
         f32x4 R[4], VG[4];
@@ -665,7 +670,14 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             }
         }
     }
-    __syncthreads();   // V, T, P, dS' no longer read: the region takes U and dR
+    // S[d][32 s + 8 g + e] (d = 16 wave + c16) for phase 2: B of dY S^T and dR S^T, and S of
+    // <S, dS'>; loaded now so they arrive during phase 2a
+    float scol[4][8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) scol[s][e] = Sg[(size_t)(32 * s + 8 * g + e) * kD + j];
+    __syncthreads();   // V, T, P no longer read: the region takes U and dR
     {
         uint16_t* const Uh = reg;
         uint16_t* const Ul = reg + kC * kD;
@@ -760,24 +772,22 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int k0 = 32 * s + 8 * g;
-            const bf16x8 sb = trcol(Sl, k0, 16 * wave);   // S[d][k0 ..] from S^T rows
-            const f32x4 x0 = dsv[s][0], x1 = dsv[s][1];   // dS'[d][k0 ..]
-            bf16x8 dh, dl;
+            const f32x4 s0 = {scol[s][0], scol[s][1], scol[s][2], scol[s][3]};   // S[d][k0 ..]
+            const f32x4 s1 = {scol[s][4], scol[s][5], scol[s][6], scol[s][7]};
+            const f32x4 x0 = dsv[s][0], x1 = dsv[s][1];                           // dS'[d][k0 ..]
+            bf16x8 sbh, sbl, dh, dl;
+            split8(s0, s1, sbh, sbl);
             split8(x0, x1, dh, dl);
-            {
-                const u32x4 sv = __builtin_bit_cast(u32x4, sb);
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    gc += __uint_as_float(sv[e] << 16) * x0[2 * e] + __uint_as_float(sv[e] & 0xffff0000u) * x0[2 * e + 1];
-                    gc += __uint_as_float(sv[2 + e] << 16) * x1[2 * e] + __uint_as_float(sv[2 + e] & 0xffff0000u) * x1[2 * e + 1];
-                }
-            }
+            for (int e = 0; e < 4; ++e) gc += s0[e] * x0[e] + s1[e] * x1[e];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int ar = e128(16 * rt + c16, k0);
-                const bf16x8 uh = frag(Uh + ar);
-                Q1[rt] = mfma16(frag(Yl + ar), sb, Q1[rt]);
-                K2[rt] = mfma16(frag(Rh + ar), sb, K2[rt]);
+                const bf16x8 uh = frag(Uh + ar), ya = frag(Yl + ar), ra = frag(Rh + ar);
+                Q1[rt] = mfma16(ya, sbh, Q1[rt]);
+                Q1[rt] = mfma16(ya, sbl, Q1[rt]);
+                K2[rt] = mfma16(ra, sbh, K2[rt]);
+                K2[rt] = mfma16(ra, sbl, K2[rt]);
                 K1[rt] = mfma16(uh, dh, K1[rt]);
                 K1[rt] = mfma16(frag(Ul + ar), dh, K1[rt]);
                 K1[rt] = mfma16(uh, dl, K1[rt]);
@@ -916,11 +926,11 @@ bool use_bwd_bf16(const ChunkBwdArgs& c) {
     return c.in_bf16 && c.dy_bf16 && c.dk == kD && c.dv == kD;
 }
 
-// the forward tiles of the bf16 prefill, then S^T bf16 and dS' fp32 per chunk-head
+// the forward tiles of the bf16 prefill, then S^T and dS' (fp32) per chunk-head
 static size_t bwd_bf16_offsets(int ntok, int num_seqs, int H, size_t& off_S, size_t& off_dS) {
     const size_t ch = (size_t)((ntok + kC - 1) / kC + num_seqs) * H;
     off_S = (chunk_bf16_workspace(ntok, num_seqs, H) + 255) & ~(size_t)255;
-    off_dS = off_S + ((ch * kD * kD * sizeof(uint16_t) + 255) & ~(size_t)255);
+    off_dS = off_S + ((ch * kD * kD * sizeof(float) + 255) & ~(size_t)255);
     return off_dS + ch * kD * kD * sizeof(float);
 }
 
@@ -933,7 +943,7 @@ hipError_t launch_chunk_bwd_bf16(const ChunkBwdArgs& c, hipStream_t s) {
     size_t off_S, off_dS;
     bwd_bf16_offsets(c.ntok, c.num_seqs, c.H, off_S, off_dS);
     char* ws = static_cast<char*>(c.workspace);
-    uint16_t* Sst = reinterpret_cast<uint16_t*>(ws + off_S);
+    float* Sst = reinterpret_cast<float*>(ws + off_S);
     // 1. forward sweep: chunk table, T and P, the state entering every chunk
     ChunkArgs f{};
     f.q = c.q; f.k = c.k; f.v = c.v; f.in_bf16 = 1; f.y_bf16 = 1;

@@ -115,8 +115,8 @@ struct ChunkTiles {
 };
 ChunkTiles chunk_bf16_tiles(void* workspace, int ntok, int num_seqs, int H);
 // The backward's forward sweep on the bf16 path (dk = dv = 128): the chunk table, T and P per
-// chunk, and the state entering every chunk as bf16 S^T [max_chunks][H][dv][dk] in Sst; no y.
-hipError_t launch_chunk_bf16_states(const ChunkArgs& a, uint16_t* Sst, hipStream_t s);
+// chunk, and the state entering every chunk as fp32 S^T [max_chunks][H][dv][dk] in Sst; no y.
+hipError_t launch_chunk_bf16_states(const ChunkArgs& a, float* Sst, hipStream_t s);
 
 // backward of the chunked gated delta rule: bf16 q, k, v, dy with dk = dv = 128 on the bf16
 // matrix cores (chunk_bwd_bf16.hip), everything else in fp32 (chunk_bwd.hip)

@@ -133,3 +133,26 @@ def test_backward_many_sequences(gpu):
     sh = inp["shape"]
     grads = gi.grad_draws(14, sh.ntok, sh.num_seqs, 2, 64, 64)
     _run(inp, grads, bf16_in=False, bf16_dy=False, seqs=C.sampled_seqs(L, 14))
+
+
+def test_backward_bf16_varlen_ragged(gpu):
+    """The bf16 matrix-core backward on packed sequences of ragged lengths (empty, 1 token, one
+    past a chunk, a full chunk), with S0 and dS_T: the chain's longest-first order, the per-chunk
+    kernel's chunk table and the ragged last chunks."""
+    lengths = [70, 1, 129, 0, 64, 200, 65]
+    _announce(f"backward bf16 inputs, lengths {lengths} H=2 d=128, S0, dS_T")
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=15, H=2, lengths=lengths)
+    sh = inp["shape"]
+    grads = gi.grad_draws(15, sh.ntok, sh.num_seqs, sh.H, 128, 128, bf16=True)
+    _run(inp, grads, bf16_in=True, bf16_dy=True)
+
+
+def test_backward_bf16_many_sequences(gpu):
+    """300 short packed sequences (empty ones, 64 and 65 tokens included) through the bf16
+    matrix-core backward, sampled sequences on both sides of 256 (the chunk table's rounds)."""
+    L = C.many_short_lengths(16, 300)
+    _announce("backward bf16 inputs, 300 packed sequences of 0..70 tokens, H=2 d=128, S0, dS_T")
+    inp = gi.make_inputs(gi.LONG_CONTEXT, seed=16, H=2, lengths=L)
+    sh = inp["shape"]
+    grads = gi.grad_draws(16, sh.ntok, sh.num_seqs, sh.H, 128, 128, bf16=True)
+    _run(inp, grads, bf16_in=True, bf16_dy=True, seqs=C.sampled_seqs(L, 16))
