@@ -806,14 +806,35 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_bf16_kernel(DevArgs 
     const size_t ch = (size_t)chunk * a.H + h;
     const size_t rowH = (size_t)a.H * kDK;   // elements between consecutive tokens of q, k, g
 
-    // log-decays of the chunk's rows (rows >= n decay by nothing) and beta
-    for (int u = tid; u < kC * kDK / 4; u += kKdaPrepThreads) {
-        const int r = u / (kDK / 4), c4 = (u % (kDK / 4)) * 4;
-        f32x4p gv = {0.f, 0.f, 0.f, 0.f};
-        if (r < n) gv = *reinterpret_cast<const f32x4p*>(a.gk + (size_t)(t0 + r) * rowH + (size_t)h * kDK + c4);
-        *reinterpret_cast<f32x4p*>(&Gs[r * kGsStr + c4]) = gv;
+    // Every global load of the rows is issued up front and unconditionally (row n - 1 stands in
+    // past the end and is zeroed after): a load under a branch is waited for where it joins.
+    auto row8 = [&](const uint16_t* x, int r, int c0) {   // raw, row clamped
+        return *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + min(r, n - 1)) * rowH + (size_t)h * kDK + c0);
+    };
+    constexpr int kUnits = kC * kDK / 8 / kKdaPrepThreads;   // 16-byte units per thread
+    constexpr int kGUnits = kC * kDK / 4 / kKdaPrepThreads;  // log-decay float4s per thread
+    u32x4 kws[kUnits], qws[kUnits];
+    f32x4p gvs[kGUnits];
+#pragma unroll
+    for (int j = 0; j < kGUnits; ++j) {
+        const int u = tid + j * kKdaPrepThreads, r = u / (kDK / 4), c4 = (u % (kDK / 4)) * 4;
+        gvs[j] = *reinterpret_cast<const f32x4p*>(a.gk + (size_t)(t0 + min(r, n - 1)) * rowH + (size_t)h * kDK + c4);
     }
-    if (tid < kC) sB[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * a.H + h] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+        const int u = tid + j * kKdaPrepThreads, r = u / (kDK / 8), c0 = (u % (kDK / 8)) * 8;
+        kws[j] = row8(a.k, r, c0);
+        qws[j] = row8(a.q, r, c0);
+    }
+    const float braw = a.beta[(size_t)(t0 + min(tid & (kC - 1), n - 1)) * a.H + h];
+    // log-decays of the chunk's rows (rows >= n decay by nothing) and beta
+#pragma unroll
+    for (int j = 0; j < kGUnits; ++j) {
+        const int u = tid + j * kKdaPrepThreads, r = u / (kDK / 4), c4 = (u % (kDK / 4)) * 4;
+        const f32x4p z4 = {0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4p*>(&Gs[r * kGsStr + c4]) = r < n ? gvs[j] : z4;
+    }
+    if (tid < kC) sB[tid] = tid < n ? braw : 0.f;
     for (int e = tid; e < kC * kStrA; e += kKdaPrepThreads) sA[e] = 0.f;
     __syncthreads();
     {   // running sums down the tokens: thread (half, channel) sums its 32 rows in registers,
@@ -836,29 +857,17 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_bf16_kernel(DevArgs 
     __syncthreads();
 
     // Kg, Kc, Qg rows (8 channels, one 16-byte store each; rows >= n are zero)
-    auto row8 = [&](const uint16_t* x, int r, int c0) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (r < n) w = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * rowH + (size_t)h * kDK + c0);
-        return w;
-    };
     auto bfv = [](const u32x4& w, int j) {
         const uint32_t x = w[j >> 1];
         return __uint_as_float((j & 1) ? (x & 0xffff0000u) : (x << 16));
     };
     uint16_t* xw = a.Xw + ch * 3 * kC * kDK;
-    constexpr int kUnits = kC * kDK / 8 / kKdaPrepThreads;   // 16-byte units per thread
-    u32x4 kws[kUnits], qws[kUnits];
-#pragma unroll
-    for (int j = 0; j < kUnits; ++j) {
-        const int u = tid + j * kKdaPrepThreads, r = u / (kDK / 8), c0 = (u % (kDK / 8)) * 8;
-        kws[j] = row8(a.k, r, c0);
-        qws[j] = row8(a.q, r, c0);
-    }
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int jj = 0; jj < kUnits; ++jj) {
         const int u = tid + jj * kKdaPrepThreads;
         const int r = u / (kDK / 8), c0 = (u % (kDK / 8)) * 8;
-        const u32x4 kw = kws[jj], qw = qws[jj];
+        const u32x4 kw = r < n ? kws[jj] : z4, qw = r < n ? qws[jj] : z4;
         float kg[8], kc[8], qg[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -901,7 +910,7 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_bf16_kernel(DevArgs 
 #pragma unroll
         for (int s2 = 0; s2 < kDK / 32; ++s2) {
             const int c0 = 32 * s2 + 8 * g;
-            const u32x4 kl = kls[s2], ql = qls[s2], kr = krs[s2];
+            const u32x4 kl = rl < n ? kls[s2] : z4, ql = rl < n ? qls[s2] : z4, kr = rr < n ? krs[s2] : z4;
             float lk[8], lq[8], rk[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
