@@ -483,48 +483,65 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         auto output = [&](int cy) __attribute__((always_inline)) {
             const uint16_t* slot = qpbuf + (cy & 1) * kQPSlot;
             const float* sGq = reinterpret_cast<const float*>(slot + kQOffG);
-            bf16x8 qf[4][4], pf[4][2];
+            // The two slices' accumulators (8) take turns in every product group, so no product
+            // waits for the result of the one just issued; each accumulator still adds its
+            // terms in the order S^T Q^T (s = 0..3), the gamma scaling, U^T P^T.
+            bf16x8 qf[4][4], pf[4][2], Sb[2][4];
+            f32x4 YT[2][4], U[2][4];
             float gq[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) Sb[sl][s] = __builtin_bit_cast(bf16x8, xbuf[cy & 1][sl][s * 64 + lane]);
                 // rows 16 apart share the swizzle, units 8 apart are 64 elements apart
 #pragma unroll
-                for (int s = 0; s < 4; ++s) qf[rt][s] = frag(slot + oqf[s & 1] + rt * 16 * kDK + (s >> 1) * 64);
+                for (int rt = 0; rt < 4; ++rt) qf[rt][s] = frag(slot + oqf[s & 1] + rt * 16 * kDK + (s >> 1) * 64);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Sb[sl][s], qf[rt][s], YT[sl][rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) U[sl][rt] = __builtin_bit_cast(f32x4, xbuf[cy & 1][sl][(4 + rt) * 64 + lane]);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     if (s <= (rt >> 1)) pf[rt][s] = frag(slot + opf[s] + rt * 16 * kC);
                 gq[rt] = sGq[kC + 16 * rt + c16];
             }
-            f32x4 YT[2][4];
+            bf16x8 Uh[2][2], Ul[2][2];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
-                const u32x4* xb = xbuf[cy & 1][sl];
-                bf16x8 Sb[4];
-                f32x4 U[4];
+                split8(U[sl][0], U[sl][1], Uh[sl][0], Ul[sl][0]);
+                split8(U[sl][2], U[sl][3], Uh[sl][1], Ul[sl][1]);
+            }
 #pragma unroll
-                for (int s = 0; s < 4; ++s) Sb[s] = __builtin_bit_cast(bf16x8, xb[s * 64 + lane]);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) U[rt] = __builtin_bit_cast(f32x4, xb[(4 + rt) * 64 + lane]);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = f32x4{};
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = mfma16(Sb[s], qf[rt][s], YT[sl][rt]);
-                bf16x8 Uh[2], Ul[2];
-                split8(U[0], U[1], Uh[0], Ul[0]);
-                split8(U[2], U[3], Uh[1], Ul[1]);
+            for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) YT[sl][rt] *= gq[rt];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = mfma16(Uh[0], pf[rt][0], YT[sl][rt]);
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = mfma16(Ul[0], pf[rt][0], YT[sl][rt]);
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Uh[sl][0], pf[rt][0], YT[sl][rt]);
 #pragma unroll
-                for (int rt = 2; rt < 4; ++rt) YT[sl][rt] = mfma16(Uh[1], pf[rt][1], YT[sl][rt]);
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int rt = 2; rt < 4; ++rt) YT[sl][rt] = mfma16(Ul[1], pf[rt][1], YT[sl][rt]);
-            }
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Ul[sl][0], pf[rt][0], YT[sl][rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Uh[sl][1], pf[rt][1], YT[sl][rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Ul[sl][1], pf[rt][1], YT[sl][rt]);
             // y is written once and never read here: streaming (nontemporal) stores keep its
             // lines from displacing the q, k, T and P lines the head's other slices still read
             // from the shared L2
@@ -738,28 +755,38 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         load_kt(4);
         load_kt(5);
         GDN_SCHED_FENCE();
-        // ---- S = gamma_C S + K^T W, each finished pair of tiles split for the next chunk |
-        //      K^T fragments of tiles 6-7
-        auto upd = [&](int t) {
+        // ---- S = gamma_C S + K^T W over tiles t0 .. t0 + 3, then their split for the next
+        //      chunk | K^T fragments of tiles 6-7. Each tile adds its four products in the same
+        //      order as before, but the four tiles take turns, so no product waits for the
+        //      result of the one issued just before it (a dependent product stalls its wave for
+        //      the whole matrix-core latency).
+        auto upd4 = [&](int t0) {
+            bf16x8 ktf[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const u32x2 p0 = __builtin_bit_cast(u32x2, kt[t0 + t][s][0]);
+                    const u32x2 p1 = __builtin_bit_cast(u32x2, kt[t0 + t][s][1]);
+                    const u32x4 pk = {p0.x, p0.y, p1.x, p1.y};
+                    ktf[t][s] = __builtin_bit_cast(bf16x8, pk);
+                }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const u32x2 p0 = __builtin_bit_cast(u32x2, kt[t][s][0]);
-                const u32x2 p1 = __builtin_bit_cast(u32x2, kt[t][s][1]);
-                const u32x4 pk = {p0.x, p0.y, p1.x, p1.y};
-                const bf16x8 ktf = __builtin_bit_cast(bf16x8, pk);
-                S[t] = mfma16(ktf, Wh[s], S[t]);
-                S[t] = mfma16(ktf, Wl[s], S[t]);
-            }
-            if (t & 1) Sb[t >> 1] = to_bf16x8(S[t - 1], S[t]);
-        };
 #pragma unroll
-        for (int t = 0; t < 4; ++t) upd(t);
+                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s], Wh[s], S[t0 + t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s], Wl[s], S[t0 + t]);
+            }
+            Sb[t0 >> 1] = to_bf16x8(S[t0], S[t0 + 1]);
+            Sb[(t0 >> 1) + 1] = to_bf16x8(S[t0 + 2], S[t0 + 3]);
+        };
+        upd4(0);
         load_kt(6);
         load_kt(7);
         GDN_IGLP(16, 2, 1);
         GDN_SCHED_FENCE();
-#pragma unroll
-        for (int t = 4; t < 8; ++t) upd(t);
+        upd4(4);
         GDN_IGLP(16, 1, 0);
         GDN_SCHED_FENCE();
         lds_barrier();   // past this barrier the ring slot is refilled and xb is read
@@ -1324,23 +1351,37 @@ __global__ void __launch_bounds__(kWv * kWave) chunk_scan_wide_kernel(DevArgs a,
         }
         split8(U[0], U[1], Wh[0], Wl[0]);
         split8(U[2], U[3], Wh[1], Wl[1]);
+        // four tiles at a time, taking turns (no product waits for the one just before it);
+        // each tile adds its products in the order s2 = 0 hi, lo, s2 = 1 hi, lo
+        auto upd4 = [&](int t0) __attribute__((always_inline)) {
+            bf16x8 ktf[4][2];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if constexpr (kKda)   // e^{Gc[C]} at the tile's d_k rows relabel(t, 4g + i)
-                S[t] *= *reinterpret_cast<const f32x4*>(sG + kC + 32 * (t >> 1) + 8 * g + 4 * (t & 1));
-            else
-                S[t] *= gC;
+            for (int t = 0; t < 4; ++t) {
+                if constexpr (kKda)   // e^{Gc[C]} at the tile's d_k rows relabel(t, 4g + i)
+                    S[t0 + t] *= *reinterpret_cast<const f32x4*>(sG + kC + 32 * ((t0 + t) >> 1) + 8 * g +
+                                                                 4 * (t & 1));
+                else
+                    S[t0 + t] *= gC;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const u32x2 p0 = __builtin_bit_cast(u32x2, ktr(t0 + t, s2, 0));
+                    const u32x2 p1 = __builtin_bit_cast(u32x2, ktr(t0 + t, s2, 1));
+                    const u32x4 pk = {p0.x, p0.y, p1.x, p1.y};
+                    ktf[t][s2] = __builtin_bit_cast(bf16x8, pk);
+                }
+            }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const u32x2 p0 = __builtin_bit_cast(u32x2, ktr(t, s2, 0));
-                const u32x2 p1 = __builtin_bit_cast(u32x2, ktr(t, s2, 1));
-                const u32x4 pk = {p0.x, p0.y, p1.x, p1.y};
-                const bf16x8 ktf = __builtin_bit_cast(bf16x8, pk);
-                S[t] = mfma16(ktf, Wh[s2], S[t]);
-                S[t] = mfma16(ktf, Wl[s2], S[t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s2], Wh[s2], S[t0 + t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s2], Wl[s2], S[t0 + t]);
             }
-            if (t & 1) Sb[t >> 1] = to_bf16x8(S[t - 1], S[t]);
-        }
+            Sb[t0 >> 1] = to_bf16x8(S[t0], S[t0 + 1]);
+            Sb[(t0 >> 1) + 1] = to_bf16x8(S[t0 + 2], S[t0 + 3]);
+        };
+        upd4(0);
+        upd4(4);
         GDN_SCHED_FENCE();
         if constexpr (kGate) {
             // this wave's sums of y^2 over its 16 columns, per token, for the epilogue

@@ -255,22 +255,23 @@ __global__ void __launch_bounds__(kChainThreads) bwd_chain_kernel(BArgs a) {
                     }
                     split8(x0, x1, gh[s], gl[s]);
                 }
+                // products on one accumulator are kept apart by products on the others; each
+                // accumulator adds its terms in the order step 0 (hi, lo), step 1 (hi, lo)
                 f32x4 X[4], Z[8];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    X[rt] = f32x4{};
+                for (int rt = 0; rt < 4; ++rt) X[rt] = f32x4{};
 #pragma unroll
-                    for (int s = 0; s < 2; ++s)
-                        if (s >= (rt >> 1)) X[rt] = mfma16(pt[rt][s], yb[s], X[rt]);
-                }
+                for (int rt = 0; rt < 2; ++rt) X[rt] = mfma16(pt[rt][0], yb[0], X[rt]);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    Z[t] = f32x4{};
+                for (int rt = 3; rt >= 0; --rt) X[rt] = mfma16(pt[rt][1], yb[1], X[rt]);
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        Z[t] = mfma16(qt[t][s], gh[s], Z[t]);
-                        Z[t] = mfma16(qt[t][s], gl[s], Z[t]);
-                    }
+                for (int t = 0; t < 8; ++t) Z[t] = f32x4{};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) Z[t] = mfma16(qt[t][s], gh[s], Z[t]);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) Z[t] = mfma16(qt[t][s], gl[s], Z[t]);
                 }
                 u32x4* xo = dst + sl * kXZ;
 #pragma unroll
@@ -382,17 +383,23 @@ __global__ void __launch_bounds__(kChainThreads) bwd_chain_kernel(BArgs a) {
         split8(dU[0], dU[1], dUh[0], dUl[0]);
         split8(dU[2], dU[3], dUh[1], dUl[1]);
         // ---- dR = T^T dU
+        // tiles 0-1 take steps 0 and 1, tiles 2-3 step 1; per tile: step 0 hi, lo, step 1 hi, lo,
+        // with the tiles taking turns
         f32x4 dR[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            dR[rt] = f32x4{};
+        for (int rt = 0; rt < 4; ++rt) dR[rt] = f32x4{};
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s >= (rt >> 1)) {
-                    dR[rt] = mfma16(tt[rt][s], dUh[s], dR[rt]);
-                    dR[rt] = mfma16(tt[rt][s], dUl[s], dR[rt]);
-                }
-        }
+        for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][0], dUh[0], dR[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) dR[rt] = mfma16(tt[rt][1], dUh[1], dR[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][0], dUl[0], dR[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) dR[rt] = mfma16(tt[rt][1], dUl[1], dR[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][1], dUh[1], dR[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][1], dUl[1], dR[rt]);
         // ---- E = -(beta gamma) o dR and its split; K^T fragments
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) dR[rt] *= -(grow(0, rt) * grow(1, rt));
@@ -401,17 +408,26 @@ __global__ void __launch_bounds__(kChainThreads) bwd_chain_kernel(BArgs a) {
         split8(dR[2], dR[3], Eh[1], El[1]);
         // ---- dS = gamma_C dS + Z + K^T E
         const float gC = sG[kC + kC - 1];
+        // four tiles at a time, taking turns; per tile: step 0 hi, lo, step 1 hi, lo
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const f32x4 Z = __builtin_bit_cast(f32x4, xzb[(4 + t) * kWave + lane]);
-            D[t] = gC * D[t] + Z;
+        for (int t0 = 0; t0 < 8; t0 += 4) {
+            bf16x8 kt[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 Z = __builtin_bit_cast(f32x4, xzb[(4 + t0 + t) * kWave + lane]);
+                D[t0 + t] = gC * D[t0 + t] + Z;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) kt[t][s] = ktr(t0 + t, s);
+            }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const bf16x8 kt = ktr(t, s);
-                D[t] = mfma16(kt, Eh[s], D[t]);
-                D[t] = mfma16(kt, El[s], D[t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) D[t0 + t] = mfma16(kt[t][s], Eh[s], D[t0 + t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) D[t0 + t] = mfma16(kt[t][s], El[s], D[t0 + t]);
             }
-            if (t & 1) Db[t >> 1] = to_bf16x8(D[t - 1], D[t]);
+            Db[t0 >> 1] = to_bf16x8(D[t0], D[t0 + 1]);
+            Db[(t0 >> 1) + 1] = to_bf16x8(D[t0 + 2], D[t0 + 3]);
         }
         lds_barrier();   // past this barrier the ring slot is refilled and xz rewritten
     }
@@ -594,16 +610,25 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             KS[rt] = f32x4{};
             dW[rt] = f32x4{};
         }
+        // Products on one accumulator are kept apart by products on the others (a product that
+        // needs the result of the one just issued waits out the matrix core's latency); every
+        // accumulator adds its terms in the order of the formula (hi, then lo, per step).
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 kf[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) kf[rt] = frag(Kl + e128(relabel(rt, c16), 32 * s + 8 * g));
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                const bf16x8 kf = frag(Kl + e128(relabel(rt, c16), 32 * s + 8 * g));
-                KS[rt] = mfma16(kf, Sh[s], KS[rt]);
-                KS[rt] = mfma16(kf, Slo[s], KS[rt]);
-                dW[rt] = mfma16(kf, dWh[s], dW[rt]);
-                dW[rt] = mfma16(kf, dWl[s], dW[rt]);
+                KS[rt] = mfma16(kf[rt], Sh[s], KS[rt]);
+                dW[rt] = mfma16(kf[rt], dWh[s], dW[rt]);
             }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                KS[rt] = mfma16(kf[rt], Slo[s], KS[rt]);
+                dW[rt] = mfma16(kf[rt], dWl[s], dW[rt]);
+            }
+        }
         // R = beta o (V - gamma o KS); V at the accumulator positions (4 tokens of column j)
         f32x4 R[4], VG[4];
 #pragma unroll
@@ -618,16 +643,23 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
         split8(R[0], R[1], Rh[0], Rl[0]);
         split8(R[2], R[3], Rh[1], Rl[1]);
         // U = T R (T lower triangular: token tiles 0-1 need step 0 only)
+        {
+            bf16x8 tf[4][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            U[rt] = f32x4{};
+            for (int rt = 0; rt < 4; ++rt) {
+                U[rt] = f32x4{};
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s <= (rt >> 1)) {
-                    const bf16x8 tf = frag(Tl + e64(relabel(rt, c16), 32 * s + 8 * g));
-                    U[rt] = mfma16(tf, Rh[s], U[rt]);
-                    U[rt] = mfma16(tf, Rl[s], U[rt]);
-                }
+                for (int s = 0; s < 2; ++s)
+                    if (s <= (rt >> 1)) tf[rt][s] = frag(Tl + e64(relabel(rt, c16), 32 * s + 8 * g));
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rh[0], U[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rl[0], U[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rh[1], U[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rl[1], U[rt]);
         }
         // dU = w o dW + P^T dY (P^T upper triangular)
         bf16x8 yb[2];
@@ -635,26 +667,39 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
         for (int s = 0; s < 2; ++s) yb[s] = trcol(Yl, 32 * s + 8 * g, 16 * wave);
         f32x4 dU[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            dU[rt] = row4(sW, rt) * dW[rt];
+        for (int rt = 0; rt < 4; ++rt) dU[rt] = row4(sW, rt) * dW[rt];
+        // token tiles 0-1 take steps 0 and 1, tiles 2-3 step 1 only (P^T upper triangular)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s >= (rt >> 1)) dU[rt] = mfma16(trrel(Pl, 32 * s + 8 * g, rt), yb[s], dU[rt]);
-        }
+        for (int rt = 0; rt < 2; ++rt) dU[rt] = mfma16(trrel(Pl, 8 * g, rt), yb[0], dU[rt]);
+#pragma unroll
+        for (int rt = 3; rt >= 0; --rt) dU[rt] = mfma16(trrel(Pl, 32 + 8 * g, rt), yb[1], dU[rt]);
         bf16x8 dUh[2], dUl[2];
         split8(dU[0], dU[1], dUh[0], dUl[0]);
         split8(dU[2], dU[3], dUh[1], dUl[1]);
         // dR = T^T dU (upper triangular)
+        {
+            // tiles 0-1: steps 0 and 1, tiles 2-3: step 1 (T^T upper triangular); per tile the
+            // order is step 0 hi, lo, step 1 hi, lo
+            bf16x8 tt[4][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            dR[rt] = f32x4{};
+            for (int rt = 0; rt < 4; ++rt) {
+                dR[rt] = f32x4{};
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s >= (rt >> 1)) {
-                    const bf16x8 tt = trrel(Tl, 32 * s + 8 * g, rt);
-                    dR[rt] = mfma16(tt, dUh[s], dR[rt]);
-                    dR[rt] = mfma16(tt, dUl[s], dR[rt]);
-                }
+                for (int s = 0; s < 2; ++s)
+                    if (s >= (rt >> 1)) tt[rt][s] = trrel(Tl, 32 * s + 8 * g, rt);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][0], dUh[0], dR[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) dR[rt] = mfma16(tt[rt][1], dUh[1], dR[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][0], dUl[0], dR[rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) dR[rt] = mfma16(tt[rt][1], dUl[1], dR[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][1], dUh[1], dR[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) dR[rt] = mfma16(tt[rt][1], dUl[1], dR[rt]);
         }
         // dv = beta o dR; per-token sum of dR o (V - gamma KS) over this wave's columns
         float* dvp = a.dv + ((size_t)t0 * H + h) * kD + j;
@@ -722,13 +767,13 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
         for (int s = 0; s < 4; ++s) {
             const int ar = e128(16 * rt + c16, 32 * s + 8 * g), br = e128(16 * it + c16, 32 * s + 8 * g);
             const bf16x8 uh = frag(Uh + br), ul = frag(Ul + br), kb = frag(Kl + br);
-            dA = mfma16(frag(Rh + ar), uh, dA);
-            dA = mfma16(frag(Rlo + ar), uh, dA);
             const bf16x8 ya = frag(Yl + ar);
+            dA = mfma16(frag(Rh + ar), uh, dA);
             dP = mfma16(ya, uh, dP);
-            dP = mfma16(ya, ul, dP);
             KK = mfma16(frag(Kl + ar), kb, KK);
             QK = mfma16(frag(Ql + ar), kb, QK);
+            dA = mfma16(frag(Rlo + ar), uh, dA);
+            dP = mfma16(ya, ul, dP);
         }
         float rs_d[4], rs_a[4], cs = 0.f;
         const int col = 16 * it + c16;
@@ -780,18 +825,27 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
             split8(x0, x1, dh, dl);
 #pragma unroll
             for (int e = 0; e < 4; ++e) gc += s0[e] * x0[e] + s1[e] * x1[e];
+            // per accumulator: Q1 and K2 hi then lo; K1 uh dh, ul dh, uh dl
+            bf16x8 uh[4], ya[4], ra[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int ar = e128(16 * rt + c16, k0);
-                const bf16x8 uh = frag(Uh + ar), ya = frag(Yl + ar), ra = frag(Rh + ar);
-                Q1[rt] = mfma16(ya, sbh, Q1[rt]);
-                Q1[rt] = mfma16(ya, sbl, Q1[rt]);
-                K2[rt] = mfma16(ra, sbh, K2[rt]);
-                K2[rt] = mfma16(ra, sbl, K2[rt]);
-                K1[rt] = mfma16(uh, dh, K1[rt]);
-                K1[rt] = mfma16(frag(Ul + ar), dh, K1[rt]);
-                K1[rt] = mfma16(uh, dl, K1[rt]);
+                uh[rt] = frag(Uh + ar);
+                ya[rt] = frag(Yl + ar);
+                ra[rt] = frag(Rh + ar);
+                Q1[rt] = mfma16(ya[rt], sbh, Q1[rt]);
+                K2[rt] = mfma16(ra[rt], sbh, K2[rt]);
+                K1[rt] = mfma16(uh[rt], dh, K1[rt]);
             }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Q1[rt] = mfma16(ya[rt], sbl, Q1[rt]);
+                K2[rt] = mfma16(ra[rt], sbl, K2[rt]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) K1[rt] = mfma16(frag(Ul + e128(16 * rt + c16, k0)), dh, K1[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) K1[rt] = mfma16(uh[rt], dl, K1[rt]);
         }
         gc = group_sum<kWave>(gc);
         if (lane == 0) red_gc[wave] = gc;
@@ -853,24 +907,34 @@ __global__ void __launch_bounds__(kGradThreads) bwd_chunk_kernel(BArgs a) {
         }
     }
     __syncthreads();
+    // per accumulator and step: dQK hi, lo; M hi, lo, then dQK^T hi, lo (as the formula reads);
+    // the four token tiles take turns
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int k0 = 32 * s + 8 * g;
+        const bf16x8 kb = trcol(Kl, k0, 16 * wave);
+        const bf16x8 qb = trcol(Ql, k0, 16 * wave);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int ar = e64(16 * rt + c16, k0);
+            if (s <= (rt >> 1)) dQa[rt] = mfma16(frag(QKh + ar), kb, dQa[rt]);   // dQK lower triangular
+            dKa[rt] = mfma16(frag(Mh + ar), kb, dKa[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int ar = e64(16 * rt + c16, k0);
+            if (s <= (rt >> 1)) dQa[rt] = mfma16(frag(QKl + ar), kb, dQa[rt]);
+            dKa[rt] = mfma16(frag(Ml + ar), kb, dKa[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            if (s >= (rt >> 1)) dKa[rt] = mfma16(frag(QTh + e64(16 * rt + c16, k0)), qb, dKa[rt]);   // dQK^T upper
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            if (s >= (rt >> 1)) dKa[rt] = mfma16(frag(QTl + e64(16 * rt + c16, k0)), qb, dKa[rt]);
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int k0 = 32 * s + 8 * g, ar = e64(16 * rt + c16, k0);
-            const bf16x8 kb = trcol(Kl, k0, 16 * wave);
-            const bf16x8 qb = trcol(Ql, k0, 16 * wave);
-            if (s <= (rt >> 1)) {   // dQK lower triangular
-                dQa[rt] = mfma16(frag(QKh + ar), kb, dQa[rt]);
-                dQa[rt] = mfma16(frag(QKl + ar), kb, dQa[rt]);
-            }
-            dKa[rt] = mfma16(frag(Mh + ar), kb, dKa[rt]);
-            dKa[rt] = mfma16(frag(Ml + ar), kb, dKa[rt]);
-            if (s >= (rt >> 1)) {   // dQK^T upper triangular
-                dKa[rt] = mfma16(frag(QTh + ar), qb, dKa[rt]);
-                dKa[rt] = mfma16(frag(QTl + ar), qb, dKa[rt]);
-            }
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * g + i;
