@@ -1370,12 +1370,24 @@ __global__ void __launch_bounds__(kWv * kWave) chunk_scan_wide_kernel(DevArgs a,
                     ktf[t][s2] = __builtin_bit_cast(bf16x8, pk);
                 }
             }
+            if constexpr (kGate) {
+                // tile by tile: with the epilogue's registers live this order measured 2%
+                // faster (the same additions per tile, so the same results)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s2], Wh[s2], S[t0 + t]);
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        S[t0 + t] = mfma16(ktf[t][s2], Wh[s2], S[t0 + t]);
+                        S[t0 + t] = mfma16(ktf[t][s2], Wl[s2], S[t0 + t]);
+                    }
+            } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s2], Wl[s2], S[t0 + t]);
+                for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s2], Wh[s2], S[t0 + t]);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s2], Wl[s2], S[t0 + t]);
+                }
             }
             Sb[t0 >> 1] = to_bf16x8(S[t0], S[t0 + 1]);
             Sb[(t0 >> 1) + 1] = to_bf16x8(S[t0 + 2], S[t0 + 3]);
