@@ -60,7 +60,7 @@ __host__ __device__ inline Layout ws_layout(int ntok, int num_seqs, int H) {
     const size_t tile = (size_t)kC * kC * sizeof(uint16_t);
     L.T = o;   o = align256(o + tile * L.max_chunks * H);
     L.P = o;   o = align256(o + tile * L.max_chunks * H);
-    L.Gt = o;  o = align256(o + sizeof(float) * 3 * kC * (size_t)L.max_chunks * H);
+    L.Gt = o;  o = align256(o + sizeof(float) * kGateRows * kC * (size_t)L.max_chunks * H);
     L.total = o;
     return L;
 }
@@ -188,9 +188,11 @@ __device__ __forceinline__ void store_tile_bf16(const float* src, uint16_t* dst,
     }
 }
 
-// T, P and the gate rows of one (chunk, head), by one wave. (gv, bv) are g and beta of row
-// min(lane, n-1). sA, sG, sB are the wave's own LDS; the barriers inside are workgroup-wide,
-// so in a workgroup of several waves every wave calls this together (one head each).
+// T, P (kP) and the gate rows of one (chunk, head), by one wave. (gv, bv) are g and beta of
+// row min(lane, n-1). sA, sG, sB are the wave's own LDS; the barriers inside are
+// workgroup-wide, so in a workgroup of several waves every wave calls this together (one head
+// each). Without kP, Q is not read and P not formed (the sliced scan forms P itself).
+template <bool kP>
 __device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int h, int t0, int n,
                                                 float gv, float bv, float* sA, float* sG,
                                                 float* sB) {
@@ -207,12 +209,14 @@ __device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int
     for (int kk = 0; kk < 8; ++kk) {
         fk0[kk] = *reinterpret_cast<const u32x4*>(k0p + kk * 16);
         fk1[kk] = *reinterpret_cast<const u32x4*>(k1p + kk * 16);
-        fq0[kk] = *reinterpret_cast<const u32x4*>(q0p + kk * 16);
-        fq1[kk] = *reinterpret_cast<const u32x4*>(q1p + kk * 16);
+        if constexpr (kP) {
+            fq0[kk] = *reinterpret_cast<const u32x4*>(q0p + kk * 16);
+            fq1[kk] = *reinterpret_cast<const u32x4*>(q1p + kk * 16);
+        }
     }
     {
         // running sum G of g over the chunk (rows >= n add nothing), and the chunk's beta,
-        // gamma_r = e^{G_r} and gamma_C / gamma_r for the scan
+        // gamma_r = e^{G_r}, gamma_C / gamma_r and G_r for the scan
         float Gr = lane < n ? gv : 0.f;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
@@ -221,10 +225,11 @@ __device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int
         }
         const float GC = __shfl(Gr, kC - 1, kWave);
         const float br = lane < n ? bv : 0.f;
-        float* gw = a.Gw + ((size_t)chunk * a.H + h) * 3 * kC;
+        float* gw = a.Gw + ((size_t)chunk * a.H + h) * kGateRows * kC;
         gw[lane] = br;
         gw[kC + lane] = fexp(Gr);
         gw[2 * kC + lane] = fexp(GC - Gr);
+        gw[3 * kC + lane] = Gr;
         sG[lane] = Gr;
         sB[lane] = br;
     }
@@ -242,14 +247,16 @@ __device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int
     for (int kk = 0; kk < kDK / 16; ++kk) {
         const bf16x8 k0 = __builtin_bit_cast(bf16x8, v0 ? fk0[kk] : z);
         const bf16x8 k1 = __builtin_bit_cast(bf16x8, v1 ? fk1[kk] : z);
-        const bf16x8 q0 = __builtin_bit_cast(bf16x8, v0 ? fq0[kk] : z);
-        const bf16x8 q1 = __builtin_bit_cast(bf16x8, v1 ? fq1[kk] : z);
         ckk[0] = mfma(k0, k0, ckk[0]);
         ckk[1] = mfma(k1, k0, ckk[1]);
         ckk[2] = mfma(k1, k1, ckk[2]);
-        cqk[0] = mfma(q0, k0, cqk[0]);
-        cqk[1] = mfma(q1, k0, cqk[1]);
-        cqk[2] = mfma(q1, k1, cqk[2]);
+        if constexpr (kP) {
+            const bf16x8 q0 = __builtin_bit_cast(bf16x8, v0 ? fq0[kk] : z);
+            const bf16x8 q1 = __builtin_bit_cast(bf16x8, v1 ? fq1[kk] : z);
+            cqk[0] = mfma(q0, k0, cqk[0]);
+            cqk[1] = mfma(q1, k0, cqk[1]);
+            cqk[2] = mfma(q1, k1, cqk[2]);
+        }
     }
     __syncthreads();   // gates visible
 
@@ -278,7 +285,7 @@ __device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int
                 const int r = 32 * rb + 8 * q + 4 * (lane >> 5) + e;
                 const float dec = c <= r ? fexp(Grow[rb][q][e] - Gcol[cb]) : 0.f;
                 sA[r * kStrA + c] = c < r ? Brow[rb][q][e] * dec * ckk[t][i] : 0.f;
-                cqk[t][i] *= dec;
+                if constexpr (kP) cqk[t][i] *= dec;
             }
         }
         // the upper-right block of A is zero
@@ -292,6 +299,7 @@ __device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int
     const int c = lane & 31;
     const size_t tile = ((size_t)chunk * a.H + h) * kC * kC;
     store_tile_bf16(sA, a.Tw + tile, lane);
+    if constexpr (!kP) return;
     __syncthreads();   // T read out: P takes its place
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
@@ -305,6 +313,7 @@ __device__ __forceinline__ void prep_chunk_head(const DevArgs& a, int chunk, int
     store_tile_bf16(sA, a.Pw + tile, lane);
 }
 
+template <bool kP>
 __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) float sA[kC * kStrA];
     __shared__ __attribute__((aligned(16))) float sG[kC], sB[kC];
@@ -313,7 +322,7 @@ __global__ void __launch_bounds__(kPrepThreads, 2) chunk_prep_kernel(DevArgs a) 
     if (!chunk_of(a, chunk, seq, t0, n)) return;
     float gv, bv;
     fetch_gates(a, t0, n, h, gv, bv);
-    prep_chunk_head(a, chunk, h, t0, n, gv, bv, sA, sG, sB);
+    prep_chunk_head<kP>(a, chunk, h, t0, n, gv, bv, sA, sG, sB);
 }
 
 // ------------------------------------------------------------------ sequential chunk scan
@@ -352,21 +361,30 @@ constexpr int kRing = 2;
 constexpr int kOffK = 0;                      // ring slot layout, in bf16 elements
 constexpr int kOffT = kOffK + kC * kDK;
 constexpr int kOffV = kOffT + kC * kC;
-constexpr int kOffG = kOffV + kC * kSl;       // 3 x 64 floats (+ 256 bytes of padding)
+constexpr int kOffG = kOffV + kC * kSl;       // kGateRows x 64 floats
 constexpr int kSlot = kOffG + 512;
 
 constexpr int kQOffQ = 0;                     // output slot layout, in bf16 elements
 constexpr int kQOffP = kQOffQ + kC * kDK;
-constexpr int kQOffG = kQOffP + kC * kC;      // 3 x 64 floats (+ 256 bytes of padding)
+constexpr int kQOffG = kQOffP + kC * kC;      // kGateRows x 64 floats
 constexpr int kQPSlot = kQOffG + 512;
+// kPS (P formed in the scan): three slots of the Q tile and the gate rows, then two P tiles
+constexpr int kQGSlot = kC * kDK + 512;
+constexpr int kPSOffP = 3 * kQGSlot;
+constexpr int kPSBuf = kPSOffP + 2 * kC * kC;
 
 
 // kStates: the backward's forward sweep. The chain stores the fp32 state entering every chunk
 // (Sst) and nothing else: no Q, P loads, no output wave work, no y.
-template <typename Ty, bool kStates = false>
-__global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
+// kPS: P = (Q K^T) o e^{G_r - G_i} (i <= r) is formed here, from the Q tile and the K tile
+// already in LDS, instead of being read from the prep's tiles: the prep then reads no Q and
+// writes no P. An eighth wave (wave 7, which shares the loader's SIMD; waves 4-6 only keep the
+// barrier count) forms chunk c's P during step c into a P slot the output wave reads in step
+// c + 1; Q now arrives one step earlier and stays two more, so it takes three slots.
+template <typename Ty, bool kStates = false, bool kPS = false>
+__global__ void __launch_bounds__(kPS ? 2 * kScanThreads : kScanThreads) chunk_scan_kernel(DevArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ring[kRing * kSlot];      // the chain's tiles
-    __shared__ __attribute__((aligned(16))) uint16_t qpbuf[2 * kQPSlot];     // the output wave's tiles
+    __shared__ __attribute__((aligned(16))) uint16_t qpbuf[kPS ? kPSBuf : 2 * kQPSlot];   // the output wave's
     // chain -> output exchange: [chunk parity][slice][8 x 64 lanes x 16 bytes]; rows 0-3 hold
     // the bf16 state fragments of contraction steps 0-3, rows 4-7 the fp32 U tiles
     __shared__ __attribute__((aligned(16))) u32x4 xbuf[2][2][8 * 64];
@@ -396,6 +414,76 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
     const int j0 = slice * kSl;
     const int c16 = lane & 15, g = lane >> 4;
 
+    if constexpr (kPS) {
+        if (wave == 7) {
+            // ================= P wave (on the loader's SIMD): step c forms chunk c's P from the
+            // Q and K tiles the loader brought in during step c - 1, into P slot c % 2, as the
+            // swizzled row-major bf16 tile the prep would have written. Tile (rt, it) is formed transposed, A = K rows, B = Q rows, so
+            // lane (c16, g) holds P[16 rt + c16][16 it + 4g .. + 3]: one 8-byte LDS store.
+            auto form_p = [&](int ck) __attribute__((always_inline)) {
+                const int n = min(kC, hi - (lo + ck * kC));
+                const uint16_t* qs = qpbuf + (ck % 3) * kQGSlot;
+                const uint16_t* ks = ring + (ck & 1) * kSlot + kOffK;
+                const float* Gs = reinterpret_cast<const float*>(qs + kC * kDK) + 3 * kC;   // G
+                uint16_t* ps = qpbuf + kPSOffP + (ck & 1) * kC * kC;
+                const int swc = swz(c16);
+                bf16x8 kf[4][4], qf[4][4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int o = (16 * t + c16) * kDK + (((4 * (s & 1) + g) ^ swc) << 3) + (s >> 1) * 64;
+                        kf[t][s] = frag(ks + o);
+                        qf[t][s] = frag(qs + o);
+                    }
+                constexpr int kRt[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+                constexpr int kIt[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+                f32x4 acc[10];
+#pragma unroll
+                for (int t = 0; t < 10; ++t) acc[t] = f32x4{};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int t = 0; t < 10; ++t) acc[t] = mfma16(kf[kIt[t]][s], qf[kRt[t]][s], acc[t]);
+                float gr[4];
+                f32x4 gc[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    gr[t] = Gs[16 * t + c16];
+                    gc[t] = *reinterpret_cast<const f32x4*>(Gs + 16 * t + 4 * g);
+                }
+                auto put = [&](int rt, int it, u32x2 v) __attribute__((always_inline)) {
+                    *reinterpret_cast<u32x2*>(ps + (16 * rt + c16) * kC + (((2 * it + (g >> 1)) ^ swc) << 3) +
+                                              4 * (g & 1)) = v;
+                };
+#pragma unroll
+                for (int t = 0; t < 10; ++t) {
+                    const int rt = kRt[t], it = kIt[t], r = 16 * rt + c16;
+                    float pv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int col = 16 * it + 4 * g + e;
+                        pv[e] = (col <= r && col < n) ? acc[t][e] * fexp(gr[rt] - gc[it][e]) : 0.f;
+                    }
+                    put(rt, it, u32x2{pack_bf2(pv[0], pv[1]), pack_bf2(pv[2], pv[3])});
+                }
+                // tiles above the diagonal that the output wave's fragments still cover
+                put(0, 1, u32x2{0u, 0u});
+                put(2, 3, u32x2{0u, 0u});
+            };
+            lds_barrier();   // chunk 0's tiles in
+            for (int c = 0; c <= nchunks; ++c) {
+                if (c < nchunks) form_p(c);
+                lds_barrier();
+            }
+            return;
+        }
+        if (wave >= 4) {   // waves 4-6 only keep the barrier count (they exist so that wave 7
+            lds_barrier();  // shares the loader's SIMD)
+            for (int c = 0; c <= nchunks; ++c) lds_barrier();
+            return;
+        }
+    }
     if (wave == 3) {
         // ================= loader wave
         // Step c refills ring slot (c + 1) % 2 with chunk c + 1's K, T, V slice and gate rows
@@ -446,7 +534,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
                 dma16(vb + o, slot + kOffV + i * 512);
             }
             tile64(a.Tw + ch * kC * kC, slot + kOffT);
-            dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kOffG);
+            dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kOffG);
         };
         auto output_tiles = [&](int ck) __attribute__((always_inline)) {
             const int t0 = lo + ck * kC, n = min(kC, hi - t0);
@@ -454,14 +542,32 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
             uint16_t* slot = qpbuf + (ck & 1) * kQPSlot;
             rows128(a.q, t0, n, slot + kQOffQ);
             tile64(a.Pw + ch * kC * kC, slot + kQOffP);
-            dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kQOffG);
+            dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kQOffG);
         };
-        if (nchunks > 0) chain_tiles(0);
+        // kPS: Q and the gate rows of chunk ck into Q slot ck % 3
+        auto q_tiles = [&](int ck) __attribute__((always_inline)) {
+            const int t0 = lo + ck * kC, n = min(kC, hi - t0);
+            const size_t ch = (size_t)(cbase + ck) * a.H + h;
+            uint16_t* slot = qpbuf + (ck % 3) * kQGSlot;
+            rows128(a.q, t0, n, slot);
+            dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kC * kDK);
+        };
+        if (nchunks > 0) {
+            chain_tiles(0);
+            if constexpr (kPS) q_tiles(0);
+        }
         GDN_WAIT_VMCNT(0);
         dma_barrier();
         for (int c = 0; c <= nchunks; ++c) {
-            if (c + 1 < nchunks) chain_tiles(c + 1);
-            if (!kStates && c < nchunks) output_tiles(c);
+            if constexpr (kPS) {
+                if (c + 1 < nchunks) {
+                    chain_tiles(c + 1);
+                    q_tiles(c + 1);
+                }
+            } else {
+                if (c + 1 < nchunks) chain_tiles(c + 1);
+                if (!kStates && c < nchunks) output_tiles(c);
+            }
             GDN_WAIT_VMCNT(0);
             dma_barrier();
         }
@@ -472,17 +578,18 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
         // Y^T = gamma (S^T Q^T) + U^T P^T: S^T and U^T are the chain's operand fragments (lane
         // (c, g): d_v row c, contraction indices 32s + 8g ..), Q and P the B operands with
         // natural token columns; a lane holds 4 adjacent d_v of token 16 rt + c16 of y.
-        int oqf[2], opf[2];
+        int oqf[2], opf[2];   // from the Q tile's and the P tile's start
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
-            oqf[sp] = kQOffQ + c16 * kDK + (((4 * sp + g) ^ swz(c16)) << 3);
-            opf[sp] = kQOffP + c16 * kC + (((4 * sp + g) ^ swz(c16)) << 3);
+            oqf[sp] = c16 * kDK + (((4 * sp + g) ^ swz(c16)) << 3);
+            opf[sp] = c16 * kC + (((4 * sp + g) ^ swz(c16)) << 3);
         }
         const size_t ytok = (size_t)a.H * a.dv;   // elements between consecutive tokens of y
         Ty* const ylane = static_cast<Ty*>(a.y) + (size_t)h * a.dv + j0 + 4 * g + (size_t)c16 * ytok;
         auto output = [&](int cy) __attribute__((always_inline)) {
-            const uint16_t* slot = qpbuf + (cy & 1) * kQPSlot;
-            const float* sGq = reinterpret_cast<const float*>(slot + kQOffG);
+            const uint16_t* slot = kPS ? qpbuf + (cy % 3) * kQGSlot : qpbuf + (cy & 1) * kQPSlot + kQOffQ;
+            const uint16_t* pslot = kPS ? qpbuf + kPSOffP + (cy & 1) * kC * kC : slot - kQOffQ + kQOffP;
+            const float* sGq = reinterpret_cast<const float*>(kPS ? slot + kC * kDK : slot - kQOffQ + kQOffG);
             // The two slices' accumulators (8) take turns in every product group, so no product
             // waits for the result of the one just issued; each accumulator still adds its
             // terms in the order S^T Q^T (s = 0..3), the gamma scaling, U^T P^T.
@@ -513,7 +620,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(DevArgs a) {
                 for (int sl = 0; sl < 2; ++sl) U[sl][rt] = __builtin_bit_cast(f32x4, xbuf[cy & 1][sl][(4 + rt) * 64 + lane]);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    if (s <= (rt >> 1)) pf[rt][s] = frag(slot + opf[s] + rt * 16 * kC);
+                    if (s <= (rt >> 1)) pf[rt][s] = frag(pslot + opf[s] + rt * 16 * kC);
                 gq[rt] = sGq[kC + 16 * rt + c16];
             }
             bf16x8 Uh[2][2], Ul[2][2];
@@ -915,7 +1022,7 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_bf16_kernel(DevArgs 
         for (int j = 0; j < 4; ++j) o[j] = pack_bf2(qg[2 * j], qg[2 * j + 1]);
         *reinterpret_cast<u32x4*>(xw + 2 * kC * kDK + r * kDK + c0) = o;
     }
-    float* gw = a.Gw + ch * 3 * kC;   // beta | e^{Gc[C]}
+    float* gw = a.Gw + ch * kGateRows * kC;   // beta | e^{Gc[C]}
     if (tid < kC) gw[tid] = sB[tid];
     else if (tid < kC + kDK) gw[tid] = fexp(Gs[(kC - 1) * kGsStr + tid - kC]);
 
@@ -1004,7 +1111,7 @@ constexpr int kWOffV = kWOffK + kC * kDK;    // [64][128], the same
 constexpr int kWOffQ = kWOffV + kC * kDK;    // [64][128], the same
 constexpr int kWOffT = kWOffQ + kC * kDK;    // [64][64], the same
 constexpr int kWOffP = kWOffT + kC * kC;     // [64][64], the same
-constexpr int kWOffG = kWOffP + kC * kC;     // beta | gamma | gamma_C / gamma (+ 256 bytes)
+constexpr int kWOffG = kWOffP + kC * kC;     // beta | gamma | gamma_C / gamma | G
 constexpr int kWSlot = kWOffG + 512;
 
 struct GateDev {
@@ -1090,7 +1197,7 @@ __global__ void __launch_bounds__(kWv * kWave) chunk_scan_wide_kernel(DevArgs a,
             dma16(a.Tw + ch * kC * kC + row * kC + u * 8, slot + kWOffT + i * 512);
             dma16(a.Pw + ch * kC * kC + row * kC + u * 8, slot + kWOffP + i * 512);
         }
-        if (wave == 0) dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kWOffG);
+        if (wave == 0) dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kWOffG);
     };
 
     const size_t sbase = ((size_t)seq * a.H + h) * kDK * DV;
@@ -1475,10 +1582,16 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
     DevArgs a = dev_args(c, L);
     if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
-    if (nchunks > 0)
-        hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
     const int pairs = c.num_seqs * c.H;
-    if (use_wide_scan(pairs, c.dv)) {
+    const bool wide = use_wide_scan(pairs, c.dv);
+    // the sliced scan forms P itself (kPS): its prep writes T and the gate rows only
+    if (nchunks > 0) {
+        if (wide)
+            hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
+    }
+    if (wide) {
         GateDev gd{};
         if (gate) {
             gd.z = gate->z; gd.w = gate->w; gd.o = gate->o; gd.eps = gate->eps;
@@ -1499,9 +1612,9 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
     const int nsl = c.dv / kSl;
     const int blocks = (pairs + 7) / 8 * 8 * nsl;
     if (c.y_bf16)
-        hipLaunchKernelGGL(chunk_scan_kernel<uint16_t>, dim3(blocks), dim3(kScanThreads), 0, s, a);
+        hipLaunchKernelGGL((chunk_scan_kernel<uint16_t, false, true>), dim3(blocks), dim3(2 * kScanThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(chunk_scan_kernel<float>, dim3(blocks), dim3(kScanThreads), 0, s, a);
+        hipLaunchKernelGGL((chunk_scan_kernel<float, false, true>), dim3(blocks), dim3(2 * kScanThreads), 0, s, a);
     if (gate) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1533,7 +1646,7 @@ hipError_t launch_chunk_bf16_states(const ChunkArgs& c, float* Sst, hipStream_t 
     if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
     if (nchunks > 0)
-        hipLaunchKernelGGL(chunk_prep_kernel, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
+        hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
     const int pairs = c.num_seqs * c.H;
     const int blocks = (pairs + 7) / 8 * 8 * (c.dv / kSl);
     hipLaunchKernelGGL((chunk_scan_kernel<uint16_t, true>), dim3(blocks), dim3(kScanThreads), 0, s, a);

@@ -93,7 +93,7 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint16_t* p0, const uint16_t* p1
 constexpr int kChainThreads = 256;
 constexpr int kOffK = 0;                     // chain ring slot, in bf16 elements
 constexpr int kOffT = kOffK + kC * kD;
-constexpr int kOffG = kOffT + kC * kC;       // 3 x 64 floats (+ 256 bytes of padding)
+constexpr int kOffG = kOffT + kC * kC;       // kGateRows x 64 floats
 constexpr int kSlot = kOffG + 512;
 constexpr int kHOffQ = 0;                    // helper slot
 constexpr int kHOffP = kHOffQ + kC * kD;
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kChainThreads) bwd_chain_kernel(BArgs a) {
             uint16_t* slot = ring + (m & 1) * kSlot;
             rows128(a.k, t0, n, slot + kOffK);
             tile64(a.T + ch * kC * kC, slot + kOffT);
-            dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kOffG);
+            dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kOffG);
         };
         auto helper_tiles = [&](int m) __attribute__((always_inline)) {
             const int c = nch - 1 - m, t0 = lo + c * kC, n = min(kC, hi - t0);
@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(kChainThreads) bwd_chain_kernel(BArgs a) {
                 const int row = 16 * i + (lane >> 2);
                 dma16(yb + (min(row, n - 1) * a.H + h) * kD + j0 + (lane & 3) * 8, slot + kHOffY + i * 512);
             }
-            dma16(a.Gw + ch * 3 * kC + (lane % 48) * 4, slot + kHOffG);
+            dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kHOffG);
         };
         for (int m = -2; m < nch; ++m) {
             if (m == -2) {

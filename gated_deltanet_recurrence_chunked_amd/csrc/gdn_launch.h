@@ -105,12 +105,17 @@ size_t kda_bf16_workspace(int ntok, int num_seqs, int H);
 hipError_t launch_kda_bf16(const ChunkArgs& a, const float* gk, hipStream_t s);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s, const GateArgs* gate = nullptr);
 
+// Gate rows the bf16 path keeps per (chunk, head), 64 floats each: beta, gamma = e^G,
+// gamma_C / gamma and G (the running sum of g over the chunk); the per-channel-decay path puts
+// beta and e^{Gc[C]} (128 values) in the first three.
+constexpr int kGateRows = 4;
+
 // The bf16 path's per-chunk tiles inside its workspace (the layout launch_chunk_bf16 uses).
 struct ChunkTiles {
     int32_t* chunk_start;   // [num_seqs + 1] first packed chunk of each sequence (varlen)
     int32_t* order;         // [num_seqs] sequences longest first (varlen)
     uint16_t *T, *P;        // [max_chunks][H][64][64] bf16
-    float* Gw;              // [max_chunks][H][3][64]: beta, gamma = e^G, gamma_C / gamma
+    float* Gw;              // [max_chunks][H][kGateRows][64]: beta, gamma = e^G, gamma_C / gamma, G
     int max_chunks;
 };
 ChunkTiles chunk_bf16_tiles(void* workspace, int ntok, int num_seqs, int H);
