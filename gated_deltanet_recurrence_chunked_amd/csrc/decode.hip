@@ -8,6 +8,8 @@
 // once and written once, in place. One 256-thread workgroup owns one state; a thread owns
 // 4 adjacent columns (one 16-byte access) of dk/RG rows, so every wave reads whole
 // contiguous rows. The state stays in registers between the two reductions and the write.
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -112,6 +114,153 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         __builtin_nontemporal_store(t, reinterpret_cast<floatx4*>(S + (size_t)(rg + RG * i) * DV + c));
     }
     if (rg == 0) Vec4<Tout>::store(y + (size_t)head * DV + c, yo);
+}
+
+// ----------------------------------------------------------------------------------------
+// Persistent form of the single-token step for d_k = d_v = 128, the shape of the serving
+// workloads: one 1024-thread workgroup per CU, each walking heads blockIdx.x, + gridDim.x, ...
+// with the next head's state and token loads issued before the current head's reductions and
+// stores, so a CU's state reads keep streaming while the previous head is reduced and written
+// back (8,192 heads: 186 us per step against 190 for one workgroup per head). A thread owns 4
+// columns of 4 consecutive rows (one address, the rows at immediate offsets). Same arithmetic
+// as decode_kernel per element; the partial sums over the state rows are grouped differently
+// (per thread, then per wave, then over the 16 waves in order), so results can differ from it
+// in the last bits. Two 512-thread workgroups per CU measured 196 us, and a third head in
+// flight (registers spilled) 193 us.
+constexpr int kPipeThreads = 1024;
+constexpr int kPipePerCU = 1;
+constexpr int kPipeWavesPerSimd = kPipeThreads / 256 * kPipePerCU;
+
+// workgroup barrier ordering LDS accesses only: the next head's global loads stay in flight
+__device__ __forceinline__ void pipe_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(kPipeWavesPerSimd, kPipeWavesPerSimd)))
+decode_pipe_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+                   const float* __restrict__ g, const float* __restrict__ beta, float* state,
+                   Tout* __restrict__ y, int heads) {
+    constexpr int DK = 128, DV = 128;
+    constexpr int TPR = DV / 4;               // threads per state row (4 columns each)
+    constexpr int RG = kPipeThreads / TPR;    // row groups
+    constexpr int RPT = DK / RG;              // rows per thread
+    constexpr int NW = kPipeThreads / kWave;
+    __shared__ float ks[2][DK], qs[2][DK];
+    __shared__ float red[2][NW][2][DV];   // per-wave partial S^T k, S^T q
+    __shared__ float fin[2][2][DV];       // their sums over the waves
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int c = (tid % TPR) * 4;
+    const int rg = tid / TPR;
+    const int ek = min(tid, 2 * DK - 1);   // threads 0..255: one element of k (then q)
+
+    struct Head {
+        float s[RPT][4];
+        float vv[4];
+        Tin kq;
+        float g, b;
+    };
+    // all of a head's loads, issued together and unconditionally
+    auto load = [&](int head, Head& H) __attribute__((always_inline)) {
+        H.kq = ((ek < DK ? k : q) + (size_t)head * DK)[ek < DK ? ek : ek - DK];
+        Vec4<Tin>::load(v + (size_t)head * DV + c, H.vv);
+        H.g = g[head];
+        H.b = beta[head];
+        const float* S = state + (size_t)head * DK * DV;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const floatx4 t = __builtin_nontemporal_load(
+                reinterpret_cast<const floatx4*>(S + (size_t)(RPT * rg + i) * DV + c));
+            H.s[i][0] = t.x; H.s[i][1] = t.y; H.s[i][2] = t.z; H.s[i][3] = t.w;
+        }
+    };
+    // the step for one head whose loads were issued earlier; p selects the LDS buffers
+    auto process = [&](int head, int p, const Head& H) __attribute__((always_inline)) {
+        if (tid < DK) ks[p][tid] = load1(&H.kq);
+        else if (tid < 2 * DK) qs[p][tid - DK] = load1(&H.kq);
+        const float a = expf(H.g);
+        const float b = H.b;
+        pipe_barrier();
+        float kq = 0.f;
+#pragma unroll
+        for (int i = lane; i < DK; i += kWave) kq += ks[p][i] * qs[p][i];
+        kq = group_sum<kWave>(kq);
+        float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float kr = ks[p][RPT * rg + i], qr = qs[p][RPT * rg + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pk[j] += H.s[i][j] * kr;
+                pq[j] += H.s[i][j] * qr;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pk[j] = sum_across<TPR>(pk[j]);
+            pq[j] = sum_across<TPR>(pq[j]);
+        }
+        if (lane < TPR) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                red[p][wave][0][c + j] = pk[j];
+                red[p][wave][1][c + j] = pq[j];
+            }
+        }
+        pipe_barrier();
+        if (tid < 2 * DV) {   // one (column, S^T k | S^T q) sum per thread, waves in order
+            const int col = tid % DV, which = tid / DV;
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += red[p][w][which][col];
+            fin[p][which][col] = t;
+        }
+        pipe_barrier();
+        float e[4], yo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float sk = fin[p][0][c + j], sq = fin[p][1][c + j];
+            e[j] = H.vv[j] - a * sk;
+            yo[j] = a * sq + b * kq * e[j];
+        }
+        float* S = state + (size_t)head * DK * DV;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float bk = b * ks[p][RPT * rg + i];
+            floatx4 t;
+            t.x = a * H.s[i][0] + bk * e[0];
+            t.y = a * H.s[i][1] + bk * e[1];
+            t.z = a * H.s[i][2] + bk * e[2];
+            t.w = a * H.s[i][3] + bk * e[3];
+            __builtin_nontemporal_store(t, reinterpret_cast<floatx4*>(S + (size_t)(RPT * rg + i) * DV + c));
+        }
+        if (rg == 0) Vec4<Tout>::store(y + (size_t)head * DV + c, yo);
+    };
+
+    const int G = gridDim.x;
+    const int h0 = blockIdx.x;
+    if (h0 >= heads) return;
+    const int n = (heads - h0 + G - 1) / G;
+    Head A, B;
+    load(h0, A);
+    int j = 0;
+    for (; j + 2 < n; j += 2) {
+        load(h0 + (j + 1) * G, B);
+        process(h0 + j * G, 0, A);
+        load(h0 + (j + 2) * G, A);
+        process(h0 + (j + 1) * G, 1, B);
+    }
+    if (j + 1 < n) {
+        load(h0 + (j + 1) * G, B);
+        process(h0 + j * G, 0, A);
+        process(h0 + (j + 1) * G, 1, B);
+    } else {
+        process(h0 + j * G, 0, A);
+    }
 }
 
 // ----------------------------------------------------------------------------------------
@@ -711,10 +860,36 @@ static void launch_dec_multi_shape(const MultiArgs& m, int in_bf16, int out_bf16
     else launch_dec_multi<64, 64, kFused>(m, in_bf16, out_bf16, heads, s);
 }
 
+// compute units of the current device (cached per device)
+static int device_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 template <int DK, int DV>
 static void launch_dec(const void* q, const void* k, const void* v, int in_bf16, const float* g,
                        const float* beta, float* state, int heads, void* y, int y_bf16,
                        hipStream_t s) {
+    if constexpr (DK == 128 && DV == 128) {
+        const int grid = std::min(heads, kPipePerCU * device_cus());
+#define GDN_DECP(TI, TO)                                                                          \
+    hipLaunchKernelGGL((decode_pipe_kernel<TI, TO>), dim3(grid), dim3(kPipeThreads), 0, s,        \
+                       static_cast<const TI*>(q), static_cast<const TI*>(k),                      \
+                       static_cast<const TI*>(v), g, beta, state, static_cast<TO*>(y), heads)
+        if (in_bf16 && y_bf16) GDN_DECP(uint16_t, uint16_t);
+        else if (in_bf16) GDN_DECP(uint16_t, float);
+        else if (y_bf16) GDN_DECP(float, uint16_t);
+        else GDN_DECP(float, float);
+#undef GDN_DECP
+        return;
+    }
 #define GDN_DEC(TI, TO)                                                                        \
     hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO>), dim3(heads), dim3(kDecThreads), 0, s,  \
                        static_cast<const TI*>(q), static_cast<const TI*>(k),                   \
