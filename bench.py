@@ -650,7 +650,7 @@ def bench_decode(torch, gdn, gi, dev, tm, d, args):
               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
               "bytes_per_step": state_bytes + tok_bytes}
     rec = counter_record(TRAFFIC_RECORD, ("decode.hip", "gdn_device.h"))
-    cb = counted_bytes(rec, "decode_kernel<")
+    cb = counted_bytes(rec, "decode_pipe_kernel<")
     if cb is not None:
         decode["counted_bytes"] = int(cb)
         decode["counted_GBs"] = round(cb / (dms * 1e-3) / 1e9, 1)
