@@ -288,7 +288,7 @@ def main():
         if cb is not None:
             kernels[name]["counted_bytes"] = int(cb)
             kernels[name]["counted_GBs"] = round(cb / (t_ms * 1e-3) / 1e9, 1)
-    roofline = {"kernel": "gdn_chunk_prefill (chunk_prep_kernel + chunk_scan_kernel)",
+    roofline = {"kernel": "gdn_chunk_prefill (chunk_prep_kernel + chunk_scan_fwd_kernel)",
                 "bound": "hbm", "achieved": round(pf_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pf_gbs / HBM_PEAK_GBS, 4),
                 "traffic": (int(traffic_rec["gdn_chunk_prefill_bytes_per_call"])

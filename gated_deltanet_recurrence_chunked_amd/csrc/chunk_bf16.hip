@@ -14,8 +14,11 @@
 // single bf16 operand, like q, k and the chunk-local T and P.
 // T and P depend on the chunk's q, k, g, beta only, so they are produced for every chunk at
 // once by chunk_prep_kernel (massively parallel: KK^T and QK^T on MFMA, the 64x64 unit
-// lower-triangular inverse by fp32 forward substitution and 32x32 fp32 MFMA blocks).
-// chunk_scan_kernel then walks the chunks of each (sequence, head) in order. The columns of
+// lower-triangular inverse by fp32 forward substitution and 32x32 fp32 MFMA blocks; the
+// sliced forward scans form P themselves). A scan kernel then walks the chunks of each
+// (sequence, head) in order: chunk_scan_fwd_kernel (tiles two chunks ahead) or
+// chunk_scan_kernel for the forward prefill below 256 pairs, chunk_scan_kernel for the
+// backward's states-only sweep, chunk_scan_wide_kernel from 256 pairs. The columns of
 // S, V, U and Y are independent, so a scan workgroup owns a 32-column slice of d_v: 4
 // workgroups per head at d_v = 128, mapped to the same XCD so the shared q, k, T, P tiles are
 // fetched from HBM once and hit that XCD's L2.
@@ -907,6 +910,483 @@ __global__ void __launch_bounds__(kPS ? 2 * kScanThreads : kScanThreads) chunk_s
     }
 }
 
+// ------------------------------------------------------------------ forward scan, tiles two ahead
+// The forward form of the sliced scan above (P formed in the scan), with every tile a step needs
+// arriving two chunks ahead instead of one: a chunk's loads from HBM take about as long as a step,
+// so with one chunk of lead the step waited on them. The LDS holds three chunks of K, the V slice
+// and the gate rows (ring), three Q tiles and two P tiles; T leaves the LDS: each chain wave loads
+// its six T fragments straight from the workspace into registers, one chunk ahead (two buffers
+// of them spill). The output
+// wave forms chunk c's S^T Q^T in step c (from the state operand the chain left before step c's
+// barrier), so a Q tile is read in the step of its chunk only, and finishes it in step c + 1
+// (gamma, U^T P^T, store). Per accumulator the products are the sliced scan's, in its order.
+constexpr int kFSlot = kC * kDK + kC * kSl + 512;   // K | V slice | gate rows (bf16 elements)
+constexpr int kFOffV = kC * kDK;
+constexpr int kFOffG = kFOffV + kC * kSl;
+constexpr size_t kFwdMaxTBytes = size_t(128) << 20;   // T tiles of one call, see the launcher
+
+template <typename Ty>
+__global__ void __launch_bounds__(2 * kScanThreads) chunk_scan_fwd_kernel(DevArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t ring[3 * kFSlot];
+    __shared__ __attribute__((aligned(16))) uint16_t qbuf[3 * kC * kDK];
+    __shared__ __attribute__((aligned(16))) uint16_t pbuf[2 * kC * kC];
+    // [chunk parity][slice][8 x 64 lanes x 16 bytes]: rows 0-3 the bf16 state operand entering
+    // the chunk (written by the chain before the step's barrier), rows 4-7 the chunk's fp32 U
+    __shared__ __attribute__((aligned(16))) u32x4 xbuf[2][2][8 * 64];
+
+    const int nsl = a.dv / kSl;
+    const int b = blockIdx.x;
+    const int group = b / (8 * nsl), within = b % (8 * nsl);
+    const int slice = within >> 3;
+    const int pair = group * 8 + (within & 7);
+    if (pair >= a.num_seqs * a.H) return;
+    const int rank = pair / a.H, h = pair % a.H;
+    const int seq = a.order ? a.order[rank] : rank;
+    int lo, hi, cbase;
+    if (a.cu) {
+        lo = a.cu[seq];
+        hi = a.cu[seq + 1];
+        cbase = a.chunk_start[seq];
+    } else {
+        lo = seq * a.L;
+        hi = lo + a.L;
+        cbase = seq * ((a.L + kC - 1) / kC);
+    }
+    const int nchunks = (hi - lo + kC - 1) / kC;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j0 = slice * kSl;
+    const int c16 = lane & 15, g = lane >> 4;
+
+    if (wave == 7) {
+        // ================= P wave: step c forms chunk c's P into P slot c % 2 (as chunk_scan_kernel)
+        auto form_p = [&](int ck) __attribute__((always_inline)) {
+            const int n = min(kC, hi - (lo + ck * kC));
+            const uint16_t* qs = qbuf + (ck % 3) * kC * kDK;
+            const uint16_t* ks = ring + (ck % 3) * kFSlot;
+            const float* Gs = reinterpret_cast<const float*>(ks + kFOffG) + 3 * kC;   // G
+            uint16_t* ps = pbuf + (ck & 1) * kC * kC;
+            const int swc = swz(c16);
+            bf16x8 kf[4][4], qf[4][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int o = (16 * t + c16) * kDK + (((4 * (s & 1) + g) ^ swc) << 3) + (s >> 1) * 64;
+                    kf[t][s] = frag(ks + o);
+                    qf[t][s] = frag(qs + o);
+                }
+            constexpr int kRt[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+            constexpr int kIt[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+            f32x4 acc[10];
+#pragma unroll
+            for (int t = 0; t < 10; ++t) acc[t] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int t = 0; t < 10; ++t) acc[t] = mfma16(kf[kIt[t]][s], qf[kRt[t]][s], acc[t]);
+            float gr[4];
+            f32x4 gc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                gr[t] = Gs[16 * t + c16];
+                gc[t] = *reinterpret_cast<const f32x4*>(Gs + 16 * t + 4 * g);
+            }
+            auto put = [&](int rt, int it, u32x2 v) __attribute__((always_inline)) {
+                *reinterpret_cast<u32x2*>(ps + (16 * rt + c16) * kC + (((2 * it + (g >> 1)) ^ swc) << 3) +
+                                          4 * (g & 1)) = v;
+            };
+#pragma unroll
+            for (int t = 0; t < 10; ++t) {
+                const int rt = kRt[t], it = kIt[t], r = 16 * rt + c16;
+                float pv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = 16 * it + 4 * g + e;
+                    pv[e] = (col <= r && col < n) ? acc[t][e] * fexp(gr[rt] - gc[it][e]) : 0.f;
+                }
+                put(rt, it, u32x2{pack_bf2(pv[0], pv[1]), pack_bf2(pv[2], pv[3])});
+            }
+            put(0, 1, u32x2{0u, 0u});
+            put(2, 3, u32x2{0u, 0u});
+        };
+        lds_barrier();   // chunk 0's tiles in
+        for (int c = 0; c <= nchunks; ++c) {
+            if (c < nchunks) form_p(c);
+            lds_barrier();
+        }
+        return;
+    }
+    if (wave >= 4) {   // waves 4-6 only keep the barrier count (so that wave 7 shares wave 3's SIMD)
+        lds_barrier();
+        for (int c = 0; c <= nchunks; ++c) lds_barrier();
+        return;
+    }
+    if (wave == 3) {
+        // ================= loader: step c fills ring slot and Q slot (c + 2) % 3 with chunk c + 2
+        // (they held chunk c - 1, finished before this step's barrier), then waits for chunk
+        // c + 1's loads (issued a step earlier) before the barrier.
+        int offk[16], offv[4];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
+            offk[i] = (row * a.H + h) * kDK + u * 8;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) offv[i] = ((16 * i + (lane >> 2)) * a.H + h) * a.dv + j0 + (lane & 3) * 8;
+        auto rows128 = [&](const uint16_t* x, int t0, int n, uint16_t* dst) __attribute__((always_inline)) {
+            const uint16_t* xb = x + (size_t)t0 * a.H * kDK;
+            if (n == kC) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dma16(xb + offk[i], dst + i * 512);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = 4 * i + (lane >> 4), u = (lane & 15) ^ swz(row);
+                    dma16(xb + (min(row, n - 1) * a.H + h) * kDK + u * 8, dst + i * 512);
+                }
+            }
+        };
+        // 37 loads per lane per chunk: K 16, V 4, gate rows 1, Q 16
+        auto chunk_tiles = [&](int ck) __attribute__((always_inline)) {
+            const int t0 = lo + ck * kC, n = min(kC, hi - t0);
+            const size_t ch = (size_t)(cbase + ck) * a.H + h;
+            uint16_t* slot = ring + (ck % 3) * kFSlot;
+            rows128(a.k, t0, n, slot);
+            const uint16_t* vb = a.v + (size_t)t0 * a.H * a.dv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * i + (lane >> 2);
+                const int o = n == kC ? offv[i] : (min(row, n - 1) * a.H + h) * a.dv + j0 + (lane & 3) * 8;
+                dma16(vb + o, slot + kFOffV + i * 512);
+            }
+            dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kFOffG);
+            rows128(a.q, t0, n, qbuf + (ck % 3) * kC * kDK);
+        };
+        if (nchunks > 0) chunk_tiles(0);
+        if (nchunks > 1) {
+            chunk_tiles(1);
+            GDN_WAIT_VMCNT(37);
+        } else {
+            GDN_WAIT_VMCNT(0);
+        }
+        dma_barrier();
+        for (int c = 0; c <= nchunks; ++c) {
+            if (c + 2 < nchunks) {
+                chunk_tiles(c + 2);
+                GDN_WAIT_VMCNT(37);
+            } else {
+                GDN_WAIT_VMCNT(0);
+            }
+            dma_barrier();
+        }
+        return;
+    }
+    if (wave == 2) {
+        // ================= output wave: step c starts chunk c (gamma-free S^T Q^T of both
+        // slices) and finishes chunk c - 1 (gamma, U^T P^T, y)
+        int oqf[2], opf[2];
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            oqf[sp] = c16 * kDK + (((4 * sp + g) ^ swz(c16)) << 3);
+            opf[sp] = c16 * kC + (((4 * sp + g) ^ swz(c16)) << 3);
+        }
+        const size_t ytok = (size_t)a.H * a.dv;
+        Ty* const ylane = static_cast<Ty*>(a.y) + (size_t)h * a.dv + j0 + 4 * g + (size_t)c16 * ytok;
+        f32x4 YT[2][4];   // the chunk started in the previous step
+        float gq[4];      // its gamma at the lane's 4 tokens
+        auto finish = [&](int cy) __attribute__((always_inline)) {
+            const uint16_t* pslot = pbuf + (cy & 1) * kC * kC;
+            bf16x8 pf[4][2];
+            f32x4 U[2][4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) U[sl][rt] = __builtin_bit_cast(f32x4, xbuf[cy & 1][sl][(4 + rt) * 64 + lane]);
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s <= (rt >> 1)) pf[rt][s] = frag(pslot + opf[s] + rt * 16 * kC);
+            }
+            bf16x8 Uh[2][2], Ul[2][2];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                split8(U[sl][0], U[sl][1], Uh[sl][0], Ul[sl][0]);
+                split8(U[sl][2], U[sl][3], Uh[sl][1], Ul[sl][1]);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] *= gq[rt];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Uh[sl][0], pf[rt][0], YT[sl][rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Ul[sl][0], pf[rt][0], YT[sl][rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Uh[sl][1], pf[rt][1], YT[sl][rt]);
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Ul[sl][1], pf[rt][1], YT[sl][rt]);
+            const int ty = lo + cy * kC, ny = min(kC, hi - ty);
+            Ty* const yc = ylane + (size_t)ty * ytok;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (16 * rt + c16 < ny) {
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) {
+                        Ty* yp = yc + (size_t)(16 * rt) * ytok + 16 * sl;
+                        if constexpr (sizeof(Ty) == 2) {
+                            u32x2 o;
+                            o.x = pack_bf2(YT[sl][rt][0], YT[sl][rt][1]);
+                            o.y = pack_bf2(YT[sl][rt][2], YT[sl][rt][3]);
+                            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(yp));
+                        } else {
+                            __builtin_nontemporal_store(YT[sl][rt], reinterpret_cast<f32x4*>(yp));
+                        }
+                    }
+                }
+            }
+        };
+        auto start = [&](int cs) __attribute__((always_inline)) {
+            const uint16_t* qs = qbuf + (cs % 3) * kC * kDK;
+            const float* sGq = reinterpret_cast<const float*>(ring + (cs % 3) * kFSlot + kFOffG);
+            bf16x8 qf[4][4], Sb[2][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) Sb[sl][s] = __builtin_bit_cast(bf16x8, xbuf[cs & 1][sl][s * 64 + lane]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) qf[rt][s] = frag(qs + oqf[s & 1] + rt * 16 * kDK + (s >> 1) * 64);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) gq[rt] = sGq[kC + 16 * rt + c16];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) YT[sl][rt] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) YT[sl][rt] = mfma16(Sb[sl][s], qf[rt][s], YT[sl][rt]);
+        };
+        lds_barrier();   // chunk 0's tiles and state operand in
+        for (int c = 0; c <= nchunks; ++c) {
+            if (c >= 1) finish(c - 1);
+            GDN_SCHED_FENCE();
+            if (c < nchunks) start(c);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ================= chain waves: d_v columns j0w .. j0w + 15 (as chunk_scan_kernel's chain)
+    const int j0w = j0 + 16 * wave;
+    const size_t sbase = ((size_t)seq * a.H + h) * kDK * a.dv;
+    f32x4 S[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = f32x4{};
+    if (a.S0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[t][i] = a.S0[sbase + (size_t)relabel(t, 4 * g + i) * a.dv + j0w + c16];
+    }
+    bf16x8 Sb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        Sb[s] = to_bf16x8(S[2 * s], S[2 * s + 1]);
+        xbuf[0][wave][s * 64 + lane] = __builtin_bit_cast(u32x4, Sb[s]);
+    }
+    int okf[2][2], okt[2][2], otg[2][2];
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2) {
+        const int r = relabel(a2, c16);
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            okf[a2][sp] = r * kDK + (((4 * sp + g) ^ swz(r)) << 3);
+            otg[a2][sp] = r * kC + 8 * (4 * sp + g);   // T row r, unit 4 sp + g, in the workspace
+        }
+    }
+    const int jj = (lane & 15) >> 2, r4 = lane & 3;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int tok = 8 * g + jj + 4 * hf;
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) okt[hf][tp] = tok * kDK + (((4 * tp + r4) ^ swz(tok)) << 3);
+    }
+    const int ov = kFOffV + (8 * g + jj) * kSl + 16 * wave + 4 * r4;
+    // T fragments [row tile][step] of chunk ck (clamped to the last chunk) from the workspace
+    auto load_t = [&](int ck, bf16x8 (&tf)[4][2]) __attribute__((always_inline)) {
+        const size_t ch = (size_t)(cbase + min(ck, nchunks - 1)) * a.H + h;
+        const uint16_t* tb = a.Tw + ch * kC * kC;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (s <= (rt >> 1)) tf[rt][s] = frag(tb + otg[rt & 1][s] + (rt >> 1) * 32 * kC);
+    };
+
+    auto step = [&](int c, bf16x8 (&tf)[4][2]) __attribute__((always_inline)) {
+        const uint16_t* slot = ring + (c % 3) * kFSlot;
+        const float* sG = reinterpret_cast<const float*>(slot + kFOffG);   // beta | gamma | gamma_C/gamma
+        auto kfrag = [&](int rt, int s) {
+            return frag(slot + okf[rt & 1][s & 1] + (rt >> 1) * 32 * kDK + (s >> 1) * 64);
+        };
+        auto ktr = [&](int t, int s, int hf) {
+            return lds_tr16(slot + okt[hf][(t >> 1) & 1] + s * 32 * kDK + (t >> 2) * 64 + 4 * (t & 1));
+        };
+        auto grow = [&](int which, int rt) {
+            return *reinterpret_cast<const f32x4*>(sG + which * kC + 8 * g + 32 * (rt >> 1) + 4 * (rt & 1));
+        };
+        bf16x8 kf[4][4];
+        f32x4 KS[4];
+        auto mma_k = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) KS[rt] = mfma16(kf[s][rt], Sb[s], KS[rt]);
+        };
+        auto load_k = [&](int s) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) kf[s][rt] = kfrag(rt, s);
+        };
+        load_k(0);
+        load_k(1);
+        const float gC = sG[kC + kC - 1];
+        GDN_SCHED_FENCE();
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) KS[rt] = f32x4{};
+        mma_k(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t] *= gC;
+        load_k(2);
+        load_k(3);
+        GDN_IGLP(4, 4, 2);
+        GDN_SCHED_FENCE();
+        f32x4 bet[4], gam[4];
+        s16x4 vv[4];
+        mma_k(1);
+#pragma unroll
+        for (int t = 4; t < 8; ++t) S[t] *= gC;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            bet[rt] = grow(0, rt);
+            gam[rt] = grow(1, rt);
+            vv[rt] = lds_tr16(slot + ov + (32 * (rt >> 1) + 4 * (rt & 1)) * kSl);
+        }
+        GDN_IGLP(4, 4, 3);
+        GDN_SCHED_FENCE();
+        f32x4 gd[4];
+        mma_k(2);
+        mma_k(3);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) gd[rt] = grow(2, rt);
+        GDN_IGLP(8, 1, 1);
+        GDN_SCHED_FENCE();
+        s16x4 kt[8][2][2];
+        auto load_kt = [&](int t) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) kt[t][s][hf] = ktr(t, s, hf);
+        };
+        f32x4 R[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                R[rt][i] = bet[rt][i] * (bf2f(uint16_t(vv[rt][i])) - gam[rt][i] * KS[rt][i]);
+        bf16x8 Rh[2], Rl[2];
+        split8(R[0], R[1], Rh[0], Rl[0]);
+        split8(R[2], R[3], Rh[1], Rl[1]);
+        load_kt(0);
+        load_kt(1);
+        GDN_SCHED_FENCE();
+        f32x4 U[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = f32x4{};
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rh[0], U[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16(tf[rt][0], Rl[0], U[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rh[1], U[rt]);
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) U[rt] = mfma16(tf[rt][1], Rl[1], U[rt]);
+        load_kt(2);
+        load_kt(3);
+        GDN_IGLP(12, 1, 1);
+        GDN_SCHED_FENCE();
+        // T of chunk c + 1 into the registers just used (in flight for a step; the prep wrote
+        // it just before this kernel, and the launcher takes this kernel when the call's T
+        // tiles fit well inside the Infinity Cache)
+        load_t(c + 1, tf);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) xbuf[c & 1][wave][(4 + rt) * 64 + lane] = __builtin_bit_cast(u32x4, U[rt]);
+        bf16x8 Wh[2], Wl[2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] *= gd[rt];
+        split8(U[0], U[1], Wh[0], Wl[0]);
+        split8(U[2], U[3], Wh[1], Wl[1]);
+        load_kt(4);
+        load_kt(5);
+        GDN_SCHED_FENCE();
+        auto upd4 = [&](int t0) {
+            bf16x8 ktf[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const u32x2 p0 = __builtin_bit_cast(u32x2, kt[t0 + t][s][0]);
+                    const u32x2 p1 = __builtin_bit_cast(u32x2, kt[t0 + t][s][1]);
+                    const u32x4 pk = {p0.x, p0.y, p1.x, p1.y};
+                    ktf[t][s] = __builtin_bit_cast(bf16x8, pk);
+                }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s], Wh[s], S[t0 + t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[t0 + t] = mfma16(ktf[t][s], Wl[s], S[t0 + t]);
+            }
+            Sb[t0 >> 1] = to_bf16x8(S[t0], S[t0 + 1]);
+            Sb[(t0 >> 1) + 1] = to_bf16x8(S[t0 + 2], S[t0 + 3]);
+        };
+        upd4(0);
+        load_kt(6);
+        load_kt(7);
+        GDN_IGLP(16, 2, 1);
+        GDN_SCHED_FENCE();
+        upd4(4);
+        GDN_IGLP(16, 1, 0);
+        GDN_SCHED_FENCE();
+        // the next chunk's state operand, for the output wave (it starts that chunk next step)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xbuf[(c + 1) & 1][wave][s * 64 + lane] = __builtin_bit_cast(u32x4, Sb[s]);
+        lds_barrier();   // past this barrier the ring slot is refilled and the exchange read
+    };
+
+    bf16x8 tf[4][2];
+    if (nchunks > 0) load_t(0, tf);
+    lds_barrier();   // chunks 0 (and 1) in the ring, the state operand in the exchange buffer
+    for (int c = 0; c < nchunks; ++c) step(c, tf);
+    GDN_WAIT_VMCNT(0);   // the last step's T loads (of no chunk still to come) land before exit
+    lds_barrier();   // the output wave finishes the last chunk
+    if (a.ST) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.ST[sbase + (size_t)relabel(t, 4 * g + i) * a.dv + j0w + c16] = S[t][i];
+    }
+}
+
 // ------------------------------------------------------------------ per-channel decay: prep
 // The per-channel-decay variant (the delta rule with Diag(alpha_t) over the key channels, as
 // in the Kimi Delta Attention entry the reading notes compare GDN with): row c of the state
@@ -1611,10 +2091,20 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
     }
     const int nsl = c.dv / kSl;
     const int blocks = (pairs + 7) / 8 * 8 * nsl;
-    if (c.y_bf16)
+    // Tiles two chunks ahead pay while the chain's one-chunk-ahead T reads hit the Infinity
+    // Cache (256 MB): B=4 H=16 T=4096 (34 MB of T) 104 vs 108 us per scan; B=1 H=32 T=65536
+    // (268 MB of T) 1626 vs 1584 us. Larger calls keep the one-chunk-ahead scan.
+    const bool two_ahead = (size_t)nchunks * c.H * kC * kC * sizeof(uint16_t) <= kFwdMaxTBytes;
+    if (two_ahead) {
+        if (c.y_bf16)
+            hipLaunchKernelGGL((chunk_scan_fwd_kernel<uint16_t>), dim3(blocks), dim3(2 * kScanThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((chunk_scan_fwd_kernel<float>), dim3(blocks), dim3(2 * kScanThreads), 0, s, a);
+    } else if (c.y_bf16) {
         hipLaunchKernelGGL((chunk_scan_kernel<uint16_t, false, true>), dim3(blocks), dim3(2 * kScanThreads), 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((chunk_scan_kernel<float, false, true>), dim3(blocks), dim3(2 * kScanThreads), 0, s, a);
+    }
     if (gate) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -27,7 +27,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 # the kernels of one gdn_chunk_prefill call (bf16 y; the states-only scan instantiation that the
 # backward runs is another kernel)
-PREFILL_KERNELS = ("chunk_prep_kernel<false>", "chunk_scan_kernel<unsigned short, false, true>", "chunk_table_kernel")
+PREFILL_KERNELS = ("chunk_prep_kernel<false>", "chunk_scan_fwd_kernel<unsigned short>",
+                   "chunk_scan_kernel<unsigned short, false, true>", "chunk_table_kernel")
 
 
 PREFILL_SOURCES = ("chunk_bf16.hip", "gdn_device.h", "gdn_inverse.h", "gdn_mfma.h")
