@@ -102,6 +102,10 @@ DECODE_CASES = [
     (5, 3, 64, 128, False, False, 4),
     (4, 2, 128, 64, True, False, 3),
     (3, 1, 64, 64, False, True, 6),
+    # around the persistent kernel's grid (one workgroup per compute unit, 256 on MI355X): one
+    # head more than workgroups, and some workgroups with an odd, others an even head count
+    (257, 1, 128, 128, True, True, 2),
+    (769, 1, 128, 128, False, False, 2),
 ]
 
 
