@@ -386,7 +386,9 @@ constexpr int kPSBuf = kPSOffP + 2 * kC * kC;
 // c + 1; Q now arrives one step earlier and stays two more, so it takes three slots.
 template <typename Ty, bool kStates = false, bool kPS = false>
 __global__ void __launch_bounds__(kPS ? 2 * kScanThreads : kScanThreads) chunk_scan_kernel(DevArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t ring[kRing * kSlot];      // the chain's tiles
+    // the states-only sweep has the LDS for a third ring slot: its tiles arrive two chunks ahead
+    constexpr int kR = kStates ? 3 : kRing;
+    __shared__ __attribute__((aligned(16))) uint16_t ring[kR * kSlot];      // the chain's tiles
     __shared__ __attribute__((aligned(16))) uint16_t qpbuf[kPS ? kPSBuf : 2 * kQPSlot];   // the output wave's
     // chain -> output exchange: [chunk parity][slice][8 x 64 lanes x 16 bytes]; rows 0-3 hold
     // the bf16 state fragments of contraction steps 0-3, rows 4-7 the fp32 U tiles
@@ -527,7 +529,7 @@ __global__ void __launch_bounds__(kPS ? 2 * kScanThreads : kScanThreads) chunk_s
         auto chain_tiles = [&](int ck) __attribute__((always_inline)) {
             const int t0 = lo + ck * kC, n = min(kC, hi - t0);
             const size_t ch = (size_t)(cbase + ck) * a.H + h;   // chunk-head index
-            uint16_t* slot = ring + (ck & 1) * kSlot;
+            uint16_t* slot = ring + (ck % kR) * kSlot;
             rows128(a.k, t0, n, slot + kOffK);
             const uint16_t* vb = a.v + (size_t)t0 * a.H * a.dv;
 #pragma unroll
@@ -555,6 +557,28 @@ __global__ void __launch_bounds__(kPS ? 2 * kScanThreads : kScanThreads) chunk_s
             rows128(a.q, t0, n, slot);
             dma16(a.Gw + ch * kGateRows * kC + lane * 4, slot + kC * kDK);
         };
+        if constexpr (kStates) {
+            // chunks c + 2 are loaded in step c (29 loads per lane: K 16, V 4, T 8, gate rows 1);
+            // the wait before the barrier is for chunk c + 1, issued a step earlier
+            if (nchunks > 0) chain_tiles(0);
+            if (nchunks > 1) {
+                chain_tiles(1);
+                GDN_WAIT_VMCNT(29);
+            } else {
+                GDN_WAIT_VMCNT(0);
+            }
+            dma_barrier();
+            for (int c = 0; c <= nchunks; ++c) {
+                if (c + 2 < nchunks) {
+                    chain_tiles(c + 2);
+                    GDN_WAIT_VMCNT(29);
+                } else {
+                    GDN_WAIT_VMCNT(0);
+                }
+                dma_barrier();
+            }
+            return;
+        }
         if (nchunks > 0) {
             chain_tiles(0);
             if constexpr (kPS) q_tiles(0);
@@ -731,7 +755,7 @@ __global__ void __launch_bounds__(kPS ? 2 * kScanThreads : kScanThreads) chunk_s
             lds_barrier();
             break;
         }
-        const uint16_t* slot = ring + (c % kRing) * kSlot;
+        const uint16_t* slot = ring + (c % kR) * kSlot;
         const float* sG = reinterpret_cast<const float*>(slot + kOffG);   // beta | gamma | gamma_C/gamma
         u32x4* xb = xbuf[c & 1][wave];
         if constexpr (kStates) {   // S[2s], S[2s+1] hold d_k rows 32s + 8g .. + 7 of column j0w + c16
