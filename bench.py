@@ -309,8 +309,8 @@ def main():
 
     # the same token mixer through the fused entry point (one call: the preprocess kernel, the
     # chunked prefill, and the gated RMSNorm, which runs in the scan's epilogue only where the
-    # full-row scan runs; below 256 (sequence, head) pairs it launches the same kernels as the
-    # separate calls). The clock drifts over a run, so the ratio comes from rounds that time
+    # full-row scan runs, from 256 (sequence, head) pairs of equal length; here it launches the
+    # same kernels as the separate calls). The clock drifts over a run, so the ratio comes from rounds that time
     # the fused call and the separate calls in turn (median of each).
     ws_f = torch.empty(gdn.gdn_fused_prefill_workspace_size(ntok, nseq, H, dk, dv),
                        dtype=torch.uint8, device=dev)
@@ -577,8 +577,8 @@ def bench_varlen(torch, gdn, gi, dev, tm):
     t_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in kt]))
     t_pf = float(np.mean([e[1].elapsed_time(e[2]) for e in kt]))
     t_og = float(np.mean([e[2].elapsed_time(e[3]) for e in kt]))
-    # the same token mixer through the fused entry point (at this many (sequence, head) pairs
-    # the output gate runs in the scan's epilogue)
+    # the same token mixer through the fused entry point (packed sequences of unequal lengths
+    # take the sliced scan and the output-gate kernel, as the separate calls do)
     wsf = torch.empty(gdn.gdn_fused_prefill_workspace_size(ntok, nseq, H, dk, dv),
                       dtype=torch.uint8, device=dev)
 

@@ -17,8 +17,9 @@
 // lower-triangular inverse by fp32 forward substitution and 32x32 fp32 MFMA blocks; the
 // sliced forward scans form P themselves). A scan kernel then walks the chunks of each
 // (sequence, head) in order: chunk_scan_fwd_kernel (tiles two chunks ahead) or
-// chunk_scan_kernel for the forward prefill below 256 pairs, chunk_scan_kernel for the
-// backward's states-only sweep, chunk_scan_wide_kernel from 256 pairs. The columns of
+// chunk_scan_kernel for the forward prefill, chunk_scan_kernel for the backward's
+// states-only sweep, chunk_scan_wide_kernel for the per-channel-decay prefill and for the
+// prefill with the output gate in its epilogue (256 or more equal-length pairs). The columns of
 // S, V, U and Y are independent, so a scan workgroup owns a 32-column slice of d_v: 4
 // workgroups per head at d_v = 128, mapped to the same XCD so the shared q, k, T, P tiles are
 // fetched from HBM once and hit that XCD's L2.
@@ -2048,9 +2049,17 @@ size_t chunk_bf16_workspace(int ntok, int num_seqs, int H) {
 
 // The full-row scan needs a (sequence, head) per CU to pay: below that the sliced scan's four
 // workgroups per pair spread one pair's columns over four CUs, which is faster when CUs are
-// left over.
+// left over. Without the output gate the sliced scan (which forms P itself, so its prep writes
+// no P) is as fast or faster at every pair count measured: 256 pairs (B=8 H=32 T=4096) 0.62 vs
+// 0.62 ms per prefill, 1,024 pairs (B=16 H=64 T=4096) 2.15 vs 2.33 ms, 64 packed sequences of
+// log-uniform lengths at H=16 2.69 vs 3.31 ms. With the gate in its epilogue the full-row scan
+// saves the output-gate kernel's pass over y: 0.99 vs 1.08 ms (256 uniform pairs, gate
+// included), 3.88 vs 4.01 ms (1,024), while the packed sequences above still favour the sliced
+// scan and the separate gate (5.08 vs 5.34 ms).
 constexpr int kWideMinPairs = 256;
-bool use_wide_scan(int pairs, int dv) { return dv == 128 && pairs >= kWideMinPairs; }
+static bool use_wide_scan(int pairs, int dv, bool gated, bool packed) {
+    return gated && !packed && dv == 128 && pairs >= kWideMinPairs;
+}
 
 template <typename Ty, bool kGate, typename Tz, typename To, bool kKda = false, int kWv = 8>
 static void launch_wide(const DevArgs& a, const GateDev& gd, int pairs, hipStream_t s) {
@@ -2087,7 +2096,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
     if (c.cu) hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
     const int nchunks = c.cu ? L.max_chunks : c.num_seqs * ((a.L + kC - 1) / kC);
     const int pairs = c.num_seqs * c.H;
-    const bool wide = use_wide_scan(pairs, c.dv);
+    const bool wide = use_wide_scan(pairs, c.dv, gate != nullptr, c.cu != nullptr);
     // the sliced scan forms P itself (kPS): its prep writes T and the gate rows only
     if (nchunks > 0) {
         if (wide)
@@ -2095,22 +2104,17 @@ hipError_t launch_chunk_bf16(const ChunkArgs& c, hipStream_t s, const GateArgs* 
         else
             hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3(nchunks, c.H), dim3(kPrepThreads), 0, s, a);
     }
-    if (wide) {
+    if (wide) {   // only with the gate: it runs in the scan's epilogue
         GateDev gd{};
-        if (gate) {
-            gd.z = gate->z; gd.w = gate->w; gd.o = gate->o; gd.eps = gate->eps;
-            a.y = gate->y_export;   // nullable: y is not stored unless exported
-            const int key = (gate->z_bf16 << 1) | gate->o_bf16;
-            switch (key) {
-                case 0: launch_wide<uint16_t, true, float, float>(a, gd, pairs, s); break;
-                case 1: launch_wide<uint16_t, true, float, uint16_t>(a, gd, pairs, s); break;
-                case 2: launch_wide<uint16_t, true, uint16_t, float>(a, gd, pairs, s); break;
-                default: launch_wide<uint16_t, true, uint16_t, uint16_t>(a, gd, pairs, s); break;
-            }
-            return hipGetLastError();
+        gd.z = gate->z; gd.w = gate->w; gd.o = gate->o; gd.eps = gate->eps;
+        a.y = gate->y_export;   // nullable: y is not stored unless exported
+        const int key = (gate->z_bf16 << 1) | gate->o_bf16;
+        switch (key) {
+            case 0: launch_wide<uint16_t, true, float, float>(a, gd, pairs, s); break;
+            case 1: launch_wide<uint16_t, true, float, uint16_t>(a, gd, pairs, s); break;
+            case 2: launch_wide<uint16_t, true, uint16_t, float>(a, gd, pairs, s); break;
+            default: launch_wide<uint16_t, true, uint16_t, uint16_t>(a, gd, pairs, s); break;
         }
-        if (c.y_bf16) launch_wide<uint16_t, false, uint16_t, uint16_t>(a, gd, pairs, s);
-        else launch_wide<float, false, uint16_t, uint16_t>(a, gd, pairs, s);
         return hipGetLastError();
     }
     const int nsl = c.dv / kSl;

@@ -88,7 +88,8 @@ hipError_t launch_mb_mfma(float* sink, int workgroups, int iters, hipStream_t s)
 // bf16 matrix-core chunked path (dk = 128): per-chunk T/P kernel + sequential scan kernel
 size_t chunk_bf16_workspace(int ntok, int num_seqs, int H);
 // The gated output of eq. (11) applied to the prefill's y (the fused prefill): inside the scan
-// when the full-row scan runs, else by the output-gate kernel after it (reading ChunkArgs::y).
+// when the full-row scan runs (256 or more (sequence, head) pairs of equal length, d_v = 128),
+// else by the output-gate kernel after it (reading ChunkArgs::y).
 struct GateArgs {
     const void* z;        // [ntok, H, dv]
     int z_bf16;
@@ -98,7 +99,6 @@ struct GateArgs {
     int o_bf16;
     void* y_export;       // nullable: y (bf16) is also stored here when the scan applies the gate
 };
-bool use_wide_scan(int pairs, int dv);
 // per-channel-decay prefill with log-decays >= -5 on the bf16 matrix cores (dk = dv = 128);
 // gk: log-decays [ntok, H, 128]; ChunkArgs::g unused
 size_t kda_bf16_workspace(int ntok, int num_seqs, int H);

@@ -336,9 +336,10 @@ size_t gdn_fused_prefill_workspace_size(int ntok, int num_seqs, int H, int dk, i
  *       concurrent calls.
  * dk must be 128 (the bf16 matrix-core path: q, k, v are bf16 between the kernels).
  * q, k, v, g, beta, y and the final state equal gdn_preprocess -> gdn_chunk_prefill with bf16
- * q, k, v, y. With 256 or more (sequence, head) pairs and dv = 128 the gate of eq. (11) runs
- * inside the scan on the fp32 y (y never leaves the chip unless exported), so o may differ in
- * its last bits from gdn_output_gate applied to the bf16 y; otherwise o equals it.
+ * q, k, v, y. With 256 or more (sequence, head) pairs, dv = 128 and no cu_seqlens (equal
+ * lengths) the gate of eq. (11) runs inside the scan on the fp32 y (y never leaves the chip
+ * unless exported), so o may differ in its last bits from gdn_output_gate applied to the bf16
+ * y; otherwise o equals it.
  */
 int gdn_fused_prefill(const void* xq, const void* xk, const void* xv, int x_dtype,
                       const float* wq, const float* wk, const float* wv, int conv_k,

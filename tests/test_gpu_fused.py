@@ -65,7 +65,8 @@ PREFILL_CASES = [
     (gi.PREFILL, dict(B=2, H=2, T=150, dv=64)),                               # two heads, dv = 64
     (gi.VARLEN, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130])),      # empty/short seqs, S0
     (gi.VARLEN, dict(H=4, nseq=5, lmax=600)),
-    # 256 or more (sequence, head) pairs: the gate runs in the full-row scan's epilogue
+    # 256 or more (sequence, head) pairs of equal length: the gate runs in the full-row scan's
+    # epilogue; packed sequences of unequal lengths take the sliced scan and the gate kernel
     (gi.PREFILL, dict(B=64, H=4, T=200)),
     (gi.VARLEN, dict(H=8, nseq=40, lmax=400)),
 ]
@@ -73,7 +74,7 @@ PREFILL_CASES = [
 
 def _gate_in_scan(inp):
     sh = inp["shape"]
-    return sh.num_seqs * sh.H >= 256 and sh.dv == 128
+    return sh.equal_lengths and sh.num_seqs * sh.H >= 256 and sh.dv == 128
 
 
 @pytest.mark.parametrize("workload,ov", PREFILL_CASES,

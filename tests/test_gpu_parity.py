@@ -57,7 +57,8 @@ CASES = [
     (gi.LONG_CONTEXT, dict(H=3, T=330, dv=64), "f32"),
     (gi.VARLEN, dict(H=2, lengths=[0, 1, 3, 63, 64, 65, 200, 0, 130]), "f32"),
     (gi.VARLEN, dict(H=2, nseq=5, lmax=600), "bf16"),
-    # 256 or more (sequence, head) pairs: the full-row scan (all 128 d_v columns per workgroup)
+    # 256 or more (sequence, head) pairs: the sliced scan's largest grids (the full-row scan runs
+    # these only with the output gate in the fused prefill)
     (gi.PREFILL, dict(B=64, H=4, T=200), "bf16"),
     (gi.PREFILL, dict(B=64, H=4, T=260), "f32"),
     (gi.VARLEN, dict(H=8, nseq=40, lmax=400), "bf16"),
@@ -172,24 +173,21 @@ def test_prefill_final_state_in_place(gpu, bf16):
 
 
 def test_full_row_scan_equals_sliced_scan(gpu):
-    """The full-row scan (taken for 256 or more (sequence, head) pairs) forms every product of
-    the sliced scan from the same operands in the same order, so one call over 256 pairs equals,
-    bit for bit, four calls over 64 pairs each (the sliced scan) on the same data."""
+    """The full-row scan (all 128 d_v columns per workgroup; the fused prefill takes it, with the
+    output gate in its epilogue, for 256 or more (sequence, head) pairs of equal length) forms
+    every product of the sliced scan that gdn_chunk_prefill runs from the same operands in the
+    same order, so the y and final state the fused call exports equal, bit for bit,
+    gdn_chunk_prefill's on the exported q, k, v, g, beta and the same S0."""
     import torch
     import gated_deltanet_recurrence_chunked_amd as gdn
-    _announce("full-row scan (B=64 H=4, 256 pairs) against the sliced scan (4 x B=16)")
+    _announce("full-row scan (fused prefill, B=64 H=4, 256 pairs, S0) against the sliced scan")
     inp = gi.make_inputs(gi.PREFILL, seed=5, B=64, H=4, T=200)
-    res = C.gpu_run(inp, y_dtype="bf16")
-    q, k, v, g, beta = (res[x] for x in ("q", "k", "v", "g", "beta"))
-    S0 = torch.randn((64, 4, 128, 128), device="cuda",
-                     generator=torch.Generator("cuda").manual_seed(5)) * 0.1
-    y_all, st_all = gdn.gdn_chunk_prefill(q, k, v, g, beta, initial_state=S0, num_seqs=64)
-    T = 200
-    for b in range(4):
-        sl = slice(b * 16 * T, (b + 1) * 16 * T)
-        y_b, st_b = gdn.gdn_chunk_prefill(q[sl], k[sl], v[sl], g[sl], beta[sl],
-                                          initial_state=S0[16 * b:16 * (b + 1)].contiguous(),
-                                          num_seqs=16)
-        assert torch.equal(y_b, y_all[sl]), f"y of batch {b} differs"
-        assert torch.equal(st_b, st_all[16 * b:16 * (b + 1)]), f"final state of batch {b} differs"
-    print("  256-pair call equals four 64-pair calls bit for bit", flush=True)
+    inp["S0"] = np.random.default_rng(5).standard_normal((64, 4, 128, 128)) * 0.1
+    fused = C.gpu_run_fused(inp)
+    y, st = gdn.gdn_chunk_prefill(fused["q"], fused["k"], fused["v"], fused["g"], fused["beta"],
+                                  initial_state=C.dev(inp["S0"].astype(np.float32)),
+                                  num_seqs=64, y_dtype="bf16")
+    torch.cuda.synchronize()
+    assert y.dtype == fused["y"].dtype and torch.equal(y, fused["y"]), "y differs"
+    assert torch.equal(st, fused["ST"]), "final state differs"
+    print("  full-row scan's y and S_T equal the sliced scan's bit for bit", flush=True)
